@@ -1,0 +1,157 @@
+/*
+ * tgs.h -- C ABI of the MI355X (gfx950) error-feedback top-k gradient
+ * sparsifier.
+ *
+ * The operations come from these web pages (cited by title and section):
+ *   [EF]    arxivdaily listing for arXiv 2004.05298, entry "Sparsified SGD with
+ *           Memory": top-k compression with the accumulated error kept in
+ *           memory and added back before the next compression.
+ *   [CONV]  same listing, entry "The Convergence of Sparsified Gradient
+ *           Methods": sort by magnitude, send a subset, accumulate the rest
+ *           locally.
+ *   [SORT]  same listing, entry "Empirical Analysis on Top-k Gradient
+ *           Sparsification for Distributed Deep Learning in a Supercomputing
+ *           Environment": gradient sorting on the GPU is what makes top-k slow.
+ *   [HT]    same listing, entry "Rethinking gradient sparsification as total
+ *           error minimization": hard-threshold sparsifier (k set by a constant
+ *           threshold) with error feedback.
+ *   [GTOPK] nubint review "A Distributed Synchronous SGD Algorithm with Global
+ *           Top-k Sparsification for Low Bandwidth Networks", ABSTRACT and
+ *           Method: global top-k of the largest |values| over P workers by an
+ *           O(log P)-round tournament; only the selected indices survive.
+ *
+ * Conventions shared by every entry point
+ *   - Array arguments are DEVICE pointers owned by the caller; the library
+ *     keeps no pointer after the call returns and allocates no device memory.
+ *   - Calls are asynchronous on `stream` (0 = the null stream); nothing waits
+ *     for the device except tgs_check_device_error().
+ *   - Only 4-byte alignment is required.  Inputs whose grad/residual
+ *     pointers differ in alignment modulo 16 bytes take a slower scalar path.
+ *   - n is at most 2^31 - 1, so every index fits in int32.  Indices are
+ *     relative to the pointers passed.
+ *   - `workspace` is caller-owned device memory of at least the size the
+ *     matching *_workspace_bytes() query returns.  One workspace serves one
+ *     call at a time; calls that share a workspace must be ordered (same
+ *     stream).  Correctness never depends on its previous contents; a
+ *     zero-filled workspace lets the very first call take the fast path.
+ *   - Magnitude order: key(x) = bits(x) & 0x7FFFFFFF as an unsigned integer.
+ *     This matches |x| for every non-NaN value, ranks NaN above infinity and
+ *     makes -0 and +0 equal.  Among equal keys the lower index comes first.
+ *   - acc = residual + grad is one binary32 add, rounded to nearest even,
+ *     never fused and never flushed to zero.
+ *   - On a negative status nothing has been enqueued and the outputs are
+ *     untouched; tgs_last_error() describes the reason.
+ */
+#ifndef TGS_H
+#define TGS_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t tgs_status;
+#define TGS_OK 0
+#define TGS_EINVAL (-1)     /* bad size, null pointer, overlapping buffers, bad lambda */
+#define TGS_EWORKSPACE (-2) /* workspace smaller than the query returned             */
+#define TGS_EHIP (-3)       /* a HIP launch failed; see tgs_last_error()              */
+#define TGS_EDEVICE (-4)    /* a kernel flagged bad input (tgs_check_device_error)    */
+
+/* Bytes of workspace tgs_topk_ef_step needs for this (n, k).  0 if the sizes
+   are invalid. */
+size_t tgs_topk_workspace_bytes(int64_t n, int64_t k);
+
+/*
+ * Error-feedback top-k step ([EF], [CONV]; the selection replaces the full
+ * sort that [SORT] identifies as the bottleneck).
+ *   grad      [n] float32, read only.
+ *   residual  [n] float32, in/out: on entry the accumulated error, on exit
+ *             acc with the selected entries set to +0.0f.
+ *   k         0 <= k <= n entries are selected: the first k of all n indices
+ *             ordered by (key(acc) descending, index ascending).
+ *   out_idx   [k] int32, out: the selected indices in that order.
+ *   out_val   [k] float32, out: acc at out_idx, bit for bit.
+ * grad must not overlap residual or the outputs; the outputs must not overlap
+ * each other or residual.  k == 0 only writes residual = acc.
+ */
+tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64_t n, int64_t k,
+                            int32_t* out_idx, float* out_val, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace tgs_threshold_ef_step needs for this n (0 if invalid). */
+size_t tgs_threshold_workspace_bytes(int64_t n);
+
+/*
+ * Hard-threshold step with error feedback ([HT]).
+ *   An entry qualifies when key(acc_i) >= key((float)lambda); lambda must be a
+ *   non-negative, non-NaN number.
+ *   out_idx/out_val [capacity]: the first min(count, capacity) qualifying
+ *             entries (i, acc_i) in ascending index order.
+ *   d_count   device int64, out: the total number of qualifying entries
+ *             (which may exceed capacity).
+ *   residual  in/out: +0.0f at every emitted index, acc everywhere else
+ *             (qualifying entries beyond the capacity keep acc).
+ */
+tgs_status tgs_threshold_ef_step(const float* grad, float* residual, int64_t n, float lambda,
+                                 int32_t* out_idx, float* out_val, int64_t capacity,
+                                 int64_t* d_count, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+/* Bytes of workspace tgs_gtopk_merge needs (0 if the sizes are invalid). */
+size_t tgs_gtopk_workspace_bytes(int32_t P, int64_t k, int64_t n);
+
+/*
+ * gTop-k tournament of P workers' sparse sets on one GPU ([GTOPK]).
+ *   idx [P][k] int32, val [P][k] float32: worker p's k pairs, any order;
+ *             indices must be distinct within a row and inside [0, n).
+ *   Round r = 0, 1, ... while 2^r < P: slot s (s a multiple of 2^(r+1))
+ *   absorbs slot s + 2^r when that slot exists: the union by index, values of
+ *   a shared index added in binary32, keeps its first k entries by (key desc,
+ *   index asc).  A slot without a partner passes through.
+ *   out_idx/out_val [k]: slot 0 after the last round, in (key desc, index
+ *             asc) order.
+ *   out_mask [P][k] uint8: 1 where idx[p][j] is one of out_idx, else 0.
+ * Rows that break the index precondition set a device error word; check it
+ * with tgs_check_device_error (the outputs are then unspecified).
+ */
+tgs_status tgs_gtopk_merge(const int32_t* idx, const float* val, int32_t P, int64_t k, int64_t n,
+                           int32_t* out_idx, float* out_val, uint8_t* out_mask, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/* Waits for `stream`, then reads the error word a previous call left in
+   `workspace` (TGS_OK or TGS_EDEVICE).  Works for all three workspaces. */
+tgs_status tgs_check_device_error(const void* workspace, hipStream_t stream);
+
+/* Static text for a status code. */
+const char* tgs_status_string(tgs_status s);
+
+/* Thread-local description of the last failure on the calling thread ("" if
+   none). */
+const char* tgs_last_error(void);
+
+/*
+ * Test and profiling controls (process-wide; not thread-safe against
+ * concurrent calls).
+ *   TGS_OPT_TOPK_PATH   0 = automatic, 1 = always the exact general path,
+ *                       2 = fast path with a sample plan that cannot hold
+ *                       (exercises the on-device fallback).
+ *   TGS_OPT_MAIN_GRID   0 = automatic, else the number of workgroups of the
+ *                       streaming pass (results must not depend on it).
+ */
+#define TGS_OPT_TOPK_PATH 1
+#define TGS_OPT_MAIN_GRID 2
+tgs_status tgs_set_option(int32_t option, int64_t value);
+
+/* One-shot profiling hook: the next tgs_topk_ef_step or
+   tgs_threshold_ef_step call records `start` right before and `stop` right
+   after its streaming pass, on its stream.  Pass null events to clear. */
+tgs_status tgs_profile_next_call(hipEvent_t start, hipEvent_t stop);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TGS_H */

@@ -1,0 +1,285 @@
+"""MI355X-native error-feedback top-k gradient sparsifier.
+
+Thin ctypes binding over ``libtgs.so`` (C ABI declared in ``include/tgs.h``).
+This module only marshals arguments: every step of the three operations runs
+in the library's HIP kernels.  PyTorch supplies device memory and streams.
+
+Operations (cited by page title and section):
+
+* ``topk_ef_step``      -- error-feedback top-k (arxivdaily listing for arXiv
+  2004.05298, entries "Sparsified SGD with Memory" and "The Convergence of
+  Sparsified Gradient Methods").
+* ``threshold_ef_step`` -- hard-threshold sparsifier with error feedback (same
+  listing, entry "Rethinking gradient sparsification as total error
+  minimization").
+* ``gtopk_merge``       -- the gTop-k tournament (nubint review "A Distributed
+  Synchronous SGD Algorithm with Global Top-k Sparsification for Low Bandwidth
+  Networks", ABSTRACT and Method).
+
+There is no fallback: if ``libtgs.so`` is missing or cannot be loaded, every
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtgs.so")
+
+TGS_OK = 0
+TGS_EINVAL = -1
+TGS_EWORKSPACE = -2
+TGS_EHIP = -3
+TGS_EDEVICE = -4
+
+OPT_TOPK_PATH = 1
+OPT_MAIN_GRID = 2
+
+_STATUS_EXC = {TGS_EINVAL: ValueError, TGS_EWORKSPACE: MemoryError}
+
+
+class TgsError(RuntimeError):
+    """Raised for TGS_EHIP and TGS_EDEVICE."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                "libtgs.so not found at %s; build it with "
+                "`python -m top_gradient_sparsification_amd.build`" % LIB_PATH)
+        # torch is imported first, so the library binds to torch's HIP runtime
+        # (same soname) and torch streams are valid handles for it.
+        lib = ctypes.CDLL(LIB_PATH)
+        i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+        lib.tgs_topk_workspace_bytes.argtypes = [i64, i64]
+        lib.tgs_topk_workspace_bytes.restype = sz
+        lib.tgs_topk_ef_step.argtypes = [vp, vp, i64, i64, vp, vp, vp, sz, vp]
+        lib.tgs_topk_ef_step.restype = i32
+        lib.tgs_threshold_workspace_bytes.argtypes = [i64]
+        lib.tgs_threshold_workspace_bytes.restype = sz
+        lib.tgs_threshold_ef_step.argtypes = [vp, vp, i64, ctypes.c_float, vp, vp, i64, vp, vp, sz, vp]
+        lib.tgs_threshold_ef_step.restype = i32
+        lib.tgs_gtopk_workspace_bytes.argtypes = [i32, i64, i64]
+        lib.tgs_gtopk_workspace_bytes.restype = sz
+        lib.tgs_gtopk_merge.argtypes = [vp, vp, i32, i64, i64, vp, vp, vp, vp, sz, vp]
+        lib.tgs_gtopk_merge.restype = i32
+        lib.tgs_check_device_error.argtypes = [vp, vp]
+        lib.tgs_check_device_error.restype = i32
+        lib.tgs_status_string.argtypes = [i32]
+        lib.tgs_status_string.restype = ctypes.c_char_p
+        lib.tgs_last_error.argtypes = []
+        lib.tgs_last_error.restype = ctypes.c_char_p
+        lib.tgs_set_option.argtypes = [i32, i64]
+        lib.tgs_set_option.restype = i32
+        lib.tgs_profile_next_call.argtypes = [vp, vp]
+        lib.tgs_profile_next_call.restype = i32
+        _lib = lib
+    return _lib
+
+
+def library():
+    """The loaded ctypes library (raises if it is missing)."""
+    return _load()
+
+
+def _check(status: int, what: str):
+    if status == TGS_OK:
+        return
+    lib = _load()
+    msg = "%s: %s (%s)" % (what, lib.tgs_status_string(status).decode(), lib.tgs_last_error().decode())
+    raise _STATUS_EXC.get(status, TgsError)(msg) if status in _STATUS_EXC else TgsError(status, msg)
+
+
+def _stream_handle(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t) -> int | None:
+    return t.data_ptr() if t is not None and t.numel() > 0 else None
+
+
+def _require(t, dtype, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_cuda:
+        raise TypeError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+# --------------------------------------------------------------- workspaces --
+_ws_cache: dict = {}
+_ws_lock = threading.Lock()
+
+
+def workspace(kind: str, nbytes: int, device) -> torch.Tensor:
+    """A zero-initialised uint8 device buffer of at least ``nbytes``, cached per
+    (device, current stream, kind).  Calls that share it are ordered on that
+    stream."""
+    dev = torch.device(device)
+    key = (dev.index, _stream_handle(dev), kind)
+    with _ws_lock:
+        buf = _ws_cache.get(key)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
+            _ws_cache[key] = buf
+        return buf
+
+
+# --------------------------------------------------------------- operations --
+def topk_workspace_bytes(n: int, k: int) -> int:
+    return int(_load().tgs_topk_workspace_bytes(n, k))
+
+
+def topk_ef_step(grad: torch.Tensor, residual: torch.Tensor, k: int, out_idx=None, out_val=None,
+                 ws: torch.Tensor | None = None):
+    """One error-feedback top-k step on the GPU.
+
+    ``residual`` (float32, same length as ``grad``) is updated in place to
+    ``acc`` with the selected entries zeroed, where ``acc = residual + grad``.
+    Returns ``(idx int32[k], val float32[k])`` in (|acc| desc, index asc) order.
+    """
+    _require(grad, torch.float32, "grad")
+    _require(residual, torch.float32, "residual")
+    n = grad.numel()
+    if residual.numel() != n or residual.device != grad.device:
+        raise ValueError("grad and residual must have the same length and device")
+    k = int(k)
+    dev = grad.device
+    if out_idx is None:
+        out_idx = torch.empty(k, dtype=torch.int32, device=dev)
+    if out_val is None:
+        out_val = torch.empty(k, dtype=torch.float32, device=dev)
+    _require(out_idx, torch.int32, "out_idx")
+    _require(out_val, torch.float32, "out_val")
+    if out_idx.numel() < k or out_val.numel() < k:
+        raise ValueError("outputs hold fewer than k entries")
+    lib = _load()
+    need = lib.tgs_topk_workspace_bytes(n, k)
+    if need == 0:
+        raise ValueError("invalid sizes n=%d k=%d" % (n, k))
+    if ws is None:
+        ws = workspace("topk", need, dev)
+    st = lib.tgs_topk_ef_step(_ptr(grad), _ptr(residual), n, k, _ptr(out_idx), _ptr(out_val), ws.data_ptr(),
+                              ws.numel(), _stream_handle(dev))
+    _check(st, "tgs_topk_ef_step")
+    return out_idx[:k], out_val[:k]
+
+
+def threshold_workspace_bytes(n: int) -> int:
+    return int(_load().tgs_threshold_workspace_bytes(n))
+
+
+def threshold_ef_step(grad: torch.Tensor, residual: torch.Tensor, lam: float, capacity: int,
+                      out_idx=None, out_val=None, count=None, ws: torch.Tensor | None = None):
+    """One hard-threshold step on the GPU.
+
+    Returns ``(idx int32[capacity], val float32[capacity], count int64[1])``:
+    the first ``min(count, capacity)`` entries of idx/val are the qualifying
+    entries in ascending index order; ``count`` (a device tensor) is the total
+    number of qualifying entries.
+    """
+    _require(grad, torch.float32, "grad")
+    _require(residual, torch.float32, "residual")
+    n = grad.numel()
+    if residual.numel() != n or residual.device != grad.device:
+        raise ValueError("grad and residual must have the same length and device")
+    dev = grad.device
+    capacity = int(capacity)
+    if out_idx is None:
+        out_idx = torch.empty(max(capacity, 0), dtype=torch.int32, device=dev)
+    if out_val is None:
+        out_val = torch.empty(max(capacity, 0), dtype=torch.float32, device=dev)
+    if count is None:
+        count = torch.empty(1, dtype=torch.int64, device=dev)
+    lib = _load()
+    need = lib.tgs_threshold_workspace_bytes(n)
+    if need == 0:
+        raise ValueError("invalid size n=%d" % n)
+    if ws is None:
+        ws = workspace("threshold", need, dev)
+    st = lib.tgs_threshold_ef_step(_ptr(grad), _ptr(residual), n, ctypes.c_float(lam), _ptr(out_idx),
+                                   _ptr(out_val), capacity, count.data_ptr(), ws.data_ptr(), ws.numel(),
+                                   _stream_handle(dev))
+    _check(st, "tgs_threshold_ef_step")
+    return out_idx, out_val, count
+
+
+def gtopk_workspace_bytes(P: int, k: int, n: int) -> int:
+    return int(_load().tgs_gtopk_workspace_bytes(P, k, n))
+
+
+def gtopk_merge(idx: torch.Tensor, val: torch.Tensor, n: int, ws: torch.Tensor | None = None,
+                check: bool = True):
+    """gTop-k tournament of the P rows of ``idx``/``val`` (shape [P, k]).
+
+    Returns ``(gidx int32[k], gval float32[k], mask uint8[P, k])``.  With
+    ``check`` the call waits for the device and raises if a row broke the
+    index precondition (distinct indices inside [0, n))."""
+    _require(idx, torch.int32, "idx")
+    _require(val, torch.float32, "val")
+    if idx.dim() != 2 or idx.shape != val.shape:
+        raise ValueError("idx and val must both have shape [P, k]")
+    P, k = idx.shape
+    dev = idx.device
+    out_idx = torch.empty(k, dtype=torch.int32, device=dev)
+    out_val = torch.empty(k, dtype=torch.float32, device=dev)
+    mask = torch.empty((P, k), dtype=torch.uint8, device=dev)
+    lib = _load()
+    need = lib.tgs_gtopk_workspace_bytes(P, k, n)
+    if need == 0:
+        raise ValueError("invalid sizes P=%d k=%d n=%d" % (P, k, n))
+    if ws is None:
+        ws = workspace("gtopk", need, dev)
+    st = lib.tgs_gtopk_merge(_ptr(idx), _ptr(val), P, k, n, _ptr(out_idx), _ptr(out_val), _ptr(mask),
+                             ws.data_ptr(), ws.numel(), _stream_handle(dev))
+    _check(st, "tgs_gtopk_merge")
+    if check:
+        _check(lib.tgs_check_device_error(ws.data_ptr(), _stream_handle(dev)), "tgs_gtopk_merge (device)")
+    return out_idx, out_val, mask
+
+
+def check_device_error(ws: torch.Tensor):
+    """Waits for the current stream and raises if a kernel flagged bad input."""
+    lib = _load()
+    _check(lib.tgs_check_device_error(ws.data_ptr(), _stream_handle(ws.device)), "tgs_check_device_error")
+
+
+def set_option(option: int, value: int):
+    _check(_load().tgs_set_option(option, value), "tgs_set_option")
+
+
+def profile_next_call(start_event, stop_event):
+    """The next topk/threshold call records these torch.cuda.Events around its
+    streaming pass (on its stream)."""
+    lib = _load()
+    s = start_event.cuda_event if start_event is not None else None
+    e = stop_event.cuda_event if stop_event is not None else None
+    _check(lib.tgs_profile_next_call(s, e), "tgs_profile_next_call")
+
+
+__all__ = [
+    "topk_ef_step", "threshold_ef_step", "gtopk_merge", "topk_workspace_bytes", "threshold_workspace_bytes",
+    "gtopk_workspace_bytes", "check_device_error", "set_option", "profile_next_call", "library", "workspace",
+    "TgsError", "OPT_TOPK_PATH", "OPT_MAIN_GRID", "LIB_PATH",
+]

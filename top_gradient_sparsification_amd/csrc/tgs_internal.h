@@ -1,0 +1,173 @@
+// Internal helpers shared by the gfx950 kernels of the sparsifier library.
+//
+// Magnitude key (all kernels): key(x) = bits(x) & 0x7FFFFFFF, compared as an
+// unsigned integer.  For every non-NaN float this orders like |x|; NaN ranks
+// above infinity; -0 and +0 are equal.  Ties go to the lower index, so the
+// rank order of (index, value) pairs is the ascending order of
+//     rank_key = (0x7FFFFFFF - key) << 32 | index.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tgs.h"
+
+namespace tgs {
+
+typedef uint32_t u32;
+typedef uint64_t u64;
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- keys ----
+__device__ __forceinline__ u32 key_of_bits(u32 b) { return b & 0x7FFFFFFFu; }
+__device__ __forceinline__ u32 key_of(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
+__device__ __forceinline__ u64 rank_key(u32 bits, u32 idx) {
+  return ((u64)(0x7FFFFFFFu - key_of_bits(bits)) << 32) | (u64)idx;
+}
+
+// A selected entry: index and the raw bits of its value.
+struct Pair {
+  int32_t idx;
+  u32 bits;
+};
+// Sorts after every real entry (real indices are below 2^31).
+__device__ __forceinline__ Pair pair_sentinel() { return Pair{-1, 0u}; }
+__device__ __forceinline__ u64 pair_rank(const Pair& p) { return rank_key(p.bits, (u32)p.idx); }
+
+// -------------------------------------------------------- wave helpers ----
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+__device__ __forceinline__ u64 ballot(bool p) { return __ballot(p); }
+// number of set bits of `mask` in lanes below this one
+__device__ __forceinline__ u32 lanes_below(u64 mask) {
+  return __builtin_amdgcn_mbcnt_hi((u32)(mask >> 32), __builtin_amdgcn_mbcnt_lo((u32)mask, 0u));
+}
+
+// ------------------------------------------------ device-scope atomics ----
+__device__ __forceinline__ u32 ld_agent(const u32* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(u32* p, u32 v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ u32 add_agent_acqrel(u32* p, u32 v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ u32 add_agent_relaxed(u32* p, u32 v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// -------------------------------------------------- block-wide scans ----
+// Exclusive prefix sum of one u32 per thread over the block; `total` gets the
+// block sum.  `lds` needs one u32 per wave (+1).  Every thread must call it.
+template <int NT>
+__device__ __forceinline__ u32 block_exclusive_sum(u32 v, u32* lds, u32& total) {
+  constexpr int NW = NT / kWave;
+  const int lane = lane_id();
+  const int w = threadIdx.x / kWave;
+  // inclusive scan inside the wave with shuffles
+  u32 x = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    u32 y = __shfl_up(x, d, kWave);
+    if (lane >= d) x += y;
+  }
+  if (lane == kWave - 1) lds[w] = x;
+  __syncthreads();
+  u32 wave_off = 0, sum = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    u32 t = lds[i];
+    if (i < w) wave_off += t;
+    sum += t;
+  }
+  __syncthreads();
+  total = sum;
+  return wave_off + x - v;
+}
+
+// ------------------------------------------- LDS bitonic sort of Pairs ----
+// Sorts a[0..N) ascending by pair_rank; N is a power of two, entries past the
+// live ones must hold pair_sentinel().  All NT threads of the block call it.
+template <int NT>
+__device__ void lds_bitonic_sort(Pair* a, int N) {
+  for (int size = 2; size <= N; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < (N >> 1); i += NT) {
+        int lo = 2 * i - (i & (stride - 1));
+        int hi = lo + stride;
+        bool up = (lo & size) == 0;
+        Pair x = a[lo], y = a[hi];
+        bool swap = up ? (pair_rank(x) > pair_rank(y)) : (pair_rank(x) < pair_rank(y));
+        if (swap) {
+          a[lo] = y;
+          a[hi] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// ---------------------------------------------------- grid barrier ----
+// For kernels whose whole grid is resident at once (grid no larger than one
+// workgroup per compute unit).  Arrivals go to `count`; the last arrival
+// resets it and bumps `gen`, which the others poll.  A bounded spin turns a
+// missing workgroup into an error (flag bit in *err, `abort` set) instead of
+// a hang; after an abort every barrier returns at once.
+struct GridBar {
+  u32* count;  // zero before the kernel starts
+  u32* gen;    // any value
+  u32* abort;  // zero before the kernel starts
+  u32* err;    // device error word
+};
+
+constexpr u32 kErrBarrierTimeout = 1u << 1;
+constexpr u32 kErrBadMergeInput = 1u << 0;
+
+__device__ __forceinline__ bool grid_sync(const GridBar& gb) {
+  __shared__ u32 s_ok;
+  // Release: every wave waits for its own global stores and writes back its
+  // L2 before the workgroup arrives (one wave's fence does not cover the
+  // stores other waves still have in flight).
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    u32 ok = 1;
+    if (ld_agent(gb.abort) != 0) {
+      ok = 0;
+    } else {
+      u32 g0 = ld_agent(gb.gen);
+      u32 t = add_agent_acqrel(gb.count, 1u);
+      if (t == gridDim.x - 1) {
+        st_agent(gb.count, 0u);
+        __threadfence();
+        add_agent_acqrel(gb.gen, 1u);
+      } else {
+        u32 spins = 0;
+        while (ld_agent(gb.gen) == g0) {
+          __builtin_amdgcn_s_sleep(2);
+          if (++spins > (1u << 23)) {
+            atomicOr(gb.err, kErrBarrierTimeout);
+            st_agent(gb.abort, 1u);
+            ok = 0;
+            break;
+          }
+          if ((spins & 1023u) == 0 && ld_agent(gb.abort) != 0) {
+            ok = 0;
+            break;
+          }
+        }
+      }
+    }
+    s_ok = ok;
+  }
+  __syncthreads();
+  // Acquire: every wave drops stale cached lines before reading what other
+  // workgroups wrote.
+  __threadfence();
+  return s_ok != 0;
+}
+
+}  // namespace tgs

@@ -1,0 +1,331 @@
+// Hard-threshold sparsifier with error feedback on gfx950.
+//
+// Method (arxivdaily listing for arXiv 2004.05298, entry "Rethinking gradient
+// sparsification as total error minimization"): the hard-threshold variant of
+// top-k, where the number of entries sent is whatever a constant threshold
+// lets through, run with error feedback.
+//
+// Two launches, no global atomics:
+//   k_thr_pass  each workgroup streams its contiguous chunk once: acc =
+//               residual + grad, residual <- acc (non-temporal), qualifying
+//               entries (key(acc) >= key(lambda)) are counted and the first
+//               `stash_cap` of them are kept, in index order, in the
+//               workgroup's stash; the count goes to cnt[wg].
+//   k_thr_emit  each workgroup adds up the counts of the workgroups before it
+//               (its output offset), copies its stash to the output while the
+//               position is below `capacity` and zeroes those residual entries.
+//               A workgroup whose stash overflowed rescans its chunk of acc
+//               (now in residual) instead.  The last workgroup writes the
+//               total count.
+// The output is in ascending index order: chunks are contiguous and in
+// workgroup order, and inside a chunk entries are ranked by (tile, wave, lane,
+// component), which is index order.
+#include <algorithm>
+#include <climits>
+
+#include "tgs_host.h"
+#include "tgs_internal.h"
+
+namespace tgs {
+
+constexpr int kThrThreads = 256;
+constexpr int kThrWaves = kThrThreads / kWave;
+constexpr int kThrMaxBlocks = 2048;
+
+struct ThrArgs {
+  const float* grad;
+  float* residual;
+  int64_t n;
+  int64_t head;  // scalar elements before the 16-byte aligned part (vector mode)
+  int64_t nv;    // float4 vectors (0 in scalar mode)
+  bool vec;
+  u32 klam;
+  u32* cnt;      // [G]
+  Pair* stash;   // [G][stash_cap]
+  int64_t stash_cap;
+  int32_t* out_idx;
+  float* out_val;
+  int64_t capacity;
+  int64_t* d_count;
+  u32* err;      // device error word (cleared by k_thr_pass)
+};
+
+// Walks this workgroup's chunk in index order.  For each tile, `load(i, bits[4],
+// idx[4], nval)` fills up to 4 values of thread slot i; qualifying entries get
+// consecutive ranks starting at `rank0`, and `put(rank, idx, bits)` is called
+// for each.  Returns the number of qualifying entries in the chunk.
+template <class Load, class Put>
+__device__ int64_t ordered_walk(const ThrArgs& a, Load load, Put put, u32 (*s_wt)[kThrWaves]) {
+  const int tid = threadIdx.x;
+  const int w = tid / kWave;
+  const int G = gridDim.x;
+  int64_t running = 0;
+  int par = 0;
+  // chunk in "slots": a slot is one float4 (vector mode) or one float (scalar)
+  const int64_t units = a.vec ? a.nv : a.n;
+  const int64_t per = (units + G - 1) / G;
+  const int64_t ub = std::min<int64_t>(units, (int64_t)blockIdx.x * per);
+  const int64_t ue = std::min<int64_t>(units, ub + per);
+  // vector mode: head elements belong to workgroup 0 (before its chunk) and the
+  // tail to the last workgroup (after its chunk); both run as one extra tile.
+  const bool has_head = a.vec && blockIdx.x == 0 && a.head > 0;
+  const bool has_tail = a.vec && blockIdx.x == G - 1 && a.head + 4 * a.nv < a.n;
+  const int64_t tail0 = a.head + 4 * a.nv;
+  const int64_t ntiles_main = (ue - ub + kThrThreads - 1) / kThrThreads;
+  const int64_t tail_tiles = has_tail ? (a.n - tail0 + 4 * kThrThreads - 1) / (4 * kThrThreads) : 0;
+  const int64_t ntiles = (has_head ? 1 : 0) + ntiles_main + tail_tiles;
+  for (int64_t t = 0; t < ntiles; ++t) {
+    u32 bits[4] = {0, 0, 0, 0};
+    int64_t idx[4] = {0, 0, 0, 0};
+    int nval = 0;
+    int64_t tt = t;
+    int kind = 1;  // 0 head, 1 main, 2 tail
+    if (has_head) {
+      if (tt == 0) kind = 0;
+      else tt -= 1;
+    }
+    if (kind == 1 && tt >= ntiles_main) {
+      kind = 2;
+      tt -= ntiles_main;
+    }
+    if (kind == 0) {
+      if (tid < a.head) {
+        idx[0] = tid;
+        nval = 1;
+        load(-1, idx, bits, nval);
+      }
+    } else if (kind == 1) {
+      int64_t i = ub + tt * kThrThreads + tid;
+      if (i < ue) {
+        if (a.vec) {
+          int64_t e = a.head + 4 * i;
+          idx[0] = e;
+          idx[1] = e + 1;
+          idx[2] = e + 2;
+          idx[3] = e + 3;
+          nval = 4;
+        } else {
+          idx[0] = i;
+          nval = 1;
+        }
+        load(i, idx, bits, nval);
+      }
+    } else {
+      // tail: up to 4 scalar elements per thread, in index order
+      int64_t base = tail0 + tt * 4 * kThrThreads + 4 * (int64_t)tid;
+      for (int c = 0; c < 4; ++c)
+        if (base + c < a.n) {
+          idx[c] = base + c;
+          nval = c + 1;
+        }
+      if (nval) load(-2, idx, bits, nval);
+    }
+    bool q[4];
+    u32 mine = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      q[c] = c < nval && key_of_bits(bits[c]) >= a.klam;
+      mine += q[c];
+    }
+    u32 below = 0, wtot = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      u64 m = ballot(q[c]);
+      below += lanes_below(m);
+      wtot += (u32)__popcll(m);
+    }
+    if (lane_id() == 0) s_wt[par][w] = wtot;
+    __syncthreads();
+    u32 woff = 0, ttot = 0;
+#pragma unroll
+    for (int ww = 0; ww < kThrWaves; ++ww) {
+      u32 v = s_wt[par][ww];
+      if (ww < w) woff += v;
+      ttot += v;
+    }
+    if (mine) {
+      int64_t r = running + woff + below;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (q[c]) put(r++, idx[c], bits[c]);
+    }
+    running += ttot;
+    par ^= 1;
+  }
+  return running;
+}
+
+__global__ __launch_bounds__(kThrThreads) void k_thr_pass(ThrArgs a) {
+  __shared__ u32 s_wt[2][kThrWaves];
+  const float* __restrict__ g = a.grad;
+  float* __restrict__ r = a.residual;
+  const v4f* __restrict__ gv = (const v4f*)(g + a.head);
+  v4f* __restrict__ rv = (v4f*)(r + a.head);
+  Pair* stash = a.stash + (int64_t)blockIdx.x * a.stash_cap;
+  const int64_t cap = a.stash_cap;
+  auto load = [&](int64_t i, const int64_t* idx, u32* bits, int nval) {
+    if (i >= 0 && a.vec) {
+      v4f x = __builtin_nontemporal_load(rv + i) + __builtin_nontemporal_load(gv + i);
+      __builtin_nontemporal_store(x, rv + i);
+      bits[0] = __float_as_uint(x.x);
+      bits[1] = __float_as_uint(x.y);
+      bits[2] = __float_as_uint(x.z);
+      bits[3] = __float_as_uint(x.w);
+    } else {
+      for (int c = 0; c < nval; ++c) {
+        float x = r[idx[c]] + g[idx[c]];
+        r[idx[c]] = x;
+        bits[c] = __float_as_uint(x);
+      }
+    }
+  };
+  auto put = [&](int64_t rank, int64_t idx, u32 bits) {
+    if (rank < cap) stash[rank] = Pair{(int32_t)idx, bits};
+  };
+  int64_t total = ordered_walk(a, load, put, s_wt);
+  if (threadIdx.x == 0) {
+    a.cnt[blockIdx.x] = (u32)total;
+    if (blockIdx.x == 0) *a.err = 0u;
+  }
+}
+
+__global__ __launch_bounds__(kThrThreads) void k_thr_emit(ThrArgs a) {
+  __shared__ u32 s_wt[2][kThrWaves];
+  __shared__ u32 s_scan[kThrWaves + 1];
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  u32 before = 0;
+  for (int i = tid; i < b; i += kThrThreads) before += a.cnt[i];
+  u32 prefix_u;
+  block_exclusive_sum<kThrThreads>(before, s_scan, prefix_u);
+  const int64_t prefix = prefix_u;
+  const int64_t mine = a.cnt[b];
+  if (b == gridDim.x - 1 && tid == 0) *a.d_count = prefix + mine;
+  if (prefix >= a.capacity || mine == 0) return;
+  const int64_t take = std::min<int64_t>(mine, a.capacity - prefix);
+  if (mine <= a.stash_cap) {
+    const Pair* stash = a.stash + (int64_t)b * a.stash_cap;
+    for (int64_t j = tid; j < take; j += kThrThreads) {
+      Pair e = stash[j];
+      a.out_idx[prefix + j] = e.idx;
+      a.out_val[prefix + j] = __uint_as_float(e.bits);
+      if (e.idx >= 0 && (int64_t)e.idx < a.n) a.residual[e.idx] = 0.0f;
+    }
+    return;
+  }
+  // the stash overflowed: rescan acc (held in residual) in index order
+  const float* r = a.residual;
+  const v4f* rv = (const v4f*)(r + a.head);
+  auto load = [&](int64_t i, const int64_t* idx, u32* bits, int nval) {
+    if (i >= 0 && a.vec) {
+      v4f x = rv[i];
+      bits[0] = __float_as_uint(x.x);
+      bits[1] = __float_as_uint(x.y);
+      bits[2] = __float_as_uint(x.z);
+      bits[3] = __float_as_uint(x.w);
+    } else {
+      for (int c = 0; c < nval; ++c) bits[c] = __float_as_uint(r[idx[c]]);
+    }
+  };
+  float* rw = a.residual;
+  auto put = [&](int64_t rank, int64_t idx, u32 bits) {
+    if (rank < take) {
+      a.out_idx[prefix + rank] = (int32_t)idx;
+      a.out_val[prefix + rank] = __uint_as_float(bits);
+      rw[idx] = 0.0f;
+    }
+  };
+  ordered_walk(a, load, put, s_wt);
+}
+
+__global__ void k_store_zero_count(int64_t* d_count) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) *d_count = 0;
+}
+
+struct ThrLayout {
+  int G;
+  int64_t stash_cap;
+  size_t cnt, stash, total;
+};
+
+static ThrLayout thr_layout(int64_t n) {
+  ThrLayout L{};
+  int64_t units = (n + 3) / 4;
+  int64_t want = (units + kThrThreads - 1) / kThrThreads;
+  L.G = (int)std::max<int64_t>(1, std::min<int64_t>(kThrMaxBlocks, want));
+  // one workgroup covers at most ceil(n / G) + 3 elements (head/tail shifts);
+  // the stash keeps up to 1/64 of them (at least 256)
+  int64_t per = (n + L.G - 1) / L.G + 8;
+  L.stash_cap = std::max<int64_t>(256, (per + 63) / 64);
+  L.cnt = 256;  // after a 256-byte header whose first word is the error word
+  size_t cnt_bytes = (((size_t)L.G * 4) + 255) & ~(size_t)255;
+  L.stash = L.cnt + cnt_bytes;
+  L.total = L.stash + (size_t)L.G * (size_t)L.stash_cap * sizeof(Pair);
+  return L;
+}
+
+}  // namespace tgs
+
+using namespace tgs;
+
+extern "C" size_t tgs_threshold_workspace_bytes(int64_t n) {
+  if (n < 0 || n > INT32_MAX) return 0;
+  return thr_layout(n).total;
+}
+
+extern "C" tgs_status tgs_threshold_ef_step(const float* grad, float* residual, int64_t n, float lambda,
+                                            int32_t* out_idx, float* out_val, int64_t capacity,
+                                            int64_t* d_count, void* workspace, size_t workspace_bytes,
+                                            hipStream_t stream) {
+  if (n < 0 || n > INT32_MAX) return fail(TGS_EINVAL, "threshold_ef_step: n=%lld outside [0, 2^31-1]", (long long)n);
+  if (!(lambda >= 0.0f)) return fail(TGS_EINVAL, "threshold_ef_step: lambda must be >= 0 and not NaN");
+  if (capacity < 0) return fail(TGS_EINVAL, "threshold_ef_step: capacity < 0");
+  if (!d_count || !workspace) return fail(TGS_EINVAL, "threshold_ef_step: null d_count/workspace");
+  if (n > 0 && (!grad || !residual)) return fail(TGS_EINVAL, "threshold_ef_step: null grad/residual");
+  if (capacity > 0 && (!out_idx || !out_val)) return fail(TGS_EINVAL, "threshold_ef_step: null outputs");
+  for (const void* p : {(const void*)grad, (const void*)residual, (const void*)out_idx, (const void*)out_val})
+    if (((uintptr_t)p & 3u) != 0) return fail(TGS_EINVAL, "threshold_ef_step: pointer not 4-byte aligned");
+  if (((uintptr_t)d_count & 7u) != 0) return fail(TGS_EINVAL, "threshold_ef_step: d_count not 8-byte aligned");
+  const size_t nb4 = (size_t)n * 4, cb4 = (size_t)capacity * 4;
+  if (overlaps(grad, nb4, residual, nb4) || overlaps(grad, nb4, out_idx, cb4) || overlaps(grad, nb4, out_val, cb4) ||
+      overlaps(residual, nb4, out_idx, cb4) || overlaps(residual, nb4, out_val, cb4) ||
+      overlaps(out_idx, cb4, out_val, cb4) || overlaps(d_count, 8, residual, nb4) ||
+      overlaps(d_count, 8, out_idx, cb4) || overlaps(d_count, 8, out_val, cb4) || overlaps(d_count, 8, grad, nb4))
+    return fail(TGS_EINVAL, "threshold_ef_step: overlapping buffers");
+  const ThrLayout L = thr_layout(n);
+  if (workspace_bytes < L.total)
+    return fail(TGS_EWORKSPACE, "threshold_ef_step: workspace %zu bytes, need %zu", workspace_bytes, L.total);
+  if (n == 0) {
+    hipLaunchKernelGGL(k_store_zero_count, dim3(1), dim3(64), 0, stream, d_count);
+  } else {
+    char* ws = (char*)workspace;
+    ThrArgs a{};
+    a.grad = grad;
+    a.residual = residual;
+    a.n = n;
+    a.vec = (((uintptr_t)grad) & 15u) == (((uintptr_t)residual) & 15u);
+    if (a.vec) {
+      int64_t head = (int64_t)(((16u - (((uintptr_t)residual) & 15u)) & 15u) / 4u);
+      a.head = std::min<int64_t>(head, n);
+      a.nv = (n - a.head) / 4;
+    }
+    a.klam = __builtin_bit_cast(uint32_t, lambda) & 0x7FFFFFFFu;
+    a.cnt = (u32*)(ws + L.cnt);
+    a.stash = (Pair*)(ws + L.stash);
+    a.stash_cap = L.stash_cap;
+    a.out_idx = out_idx;
+    a.out_val = out_val;
+    a.capacity = capacity;
+    a.d_count = d_count;
+    a.err = (u32*)ws;
+    hipEvent_t ev0, ev1;
+    take_profile_events(&ev0, &ev1);
+    if (ev0) (void)hipEventRecord(ev0, stream);
+    hipLaunchKernelGGL(k_thr_pass, dim3(L.G), dim3(kThrThreads), 0, stream, a);
+    if (ev1) (void)hipEventRecord(ev1, stream);
+    hipLaunchKernelGGL(k_thr_emit, dim3(L.G), dim3(kThrThreads), 0, stream, a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TGS_EHIP, "threshold_ef_step: launch failed: %s", hipGetErrorString(e));
+  return TGS_OK;
+}

@@ -144,3 +144,28 @@ def gtopk_sets(P: int = 32, k: int = 25_600, n: int = 25_600_000, hot: int = 51_
         idx[p] = row.astype(np.int32)
         val[p] = v32
     return idx, val
+
+
+def mixture_gpu(n: int, sigma: float, p_out: float, b_out: float, seed: tuple, device="cuda",
+                out=None, chunk: int = 1 << 26):
+    """Same mixture as `mixture`, drawn on the GPU with torch's seeded Philox
+    generator (float64 draws rounded to float32), for sizes where host
+    generation would take minutes.  Laplace(0, b) is drawn by inverting its
+    CDF from a uniform in (0, 1).  Returns a float32 torch tensor on `device`."""
+    import torch
+    s = 0
+    for part in seed:
+        s = (s * 1_000_003 + int(part) + 1) % (2 ** 61 - 1)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(s)
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=device)
+    for lo in range(0, n, chunk):
+        m = min(chunk, n - lo)
+        x = torch.randn(m, dtype=torch.float64, device=device, generator=gen) * sigma
+        hit = torch.rand(m, dtype=torch.float64, device=device, generator=gen) < p_out
+        u = torch.rand(m, dtype=torch.float64, device=device, generator=gen) - 0.5
+        lap = -b_out * torch.sign(u) * torch.log1p(-2.0 * u.abs())
+        out[lo:lo + m] = torch.where(hit, lap, x).to(torch.float32)
+        del x, hit, u, lap
+    return out

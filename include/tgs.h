@@ -150,6 +150,10 @@ tgs_status tgs_set_option(int32_t option, int64_t value);
    after its streaming pass, on its stream.  Pass null events to clear. */
 tgs_status tgs_profile_next_call(hipEvent_t start, hipEvent_t stop);
 
+/* Milliseconds between two events recorded through tgs_profile_next_call
+   (waits for `stop`).  TGS_EHIP if either has not completed. */
+tgs_status tgs_profile_elapsed_ms(hipEvent_t start, hipEvent_t stop, float* ms);
+
 #ifdef __cplusplus
 }
 #endif

@@ -91,6 +91,8 @@ def _load():
         lib.tgs_set_option.restype = i32
         lib.tgs_profile_next_call.argtypes = [vp, vp]
         lib.tgs_profile_next_call.restype = i32
+        lib.tgs_profile_elapsed_ms.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_float)]
+        lib.tgs_profile_elapsed_ms.restype = i32
         _lib = lib
     return _lib
 
@@ -186,6 +188,38 @@ def topk_ef_step(grad: torch.Tensor, residual: torch.Tensor, k: int, out_idx=Non
     return out_idx[:k], out_val[:k]
 
 
+class TopkStep:
+    """A prepared top-k step for repeated calls on tensors of one shape.
+
+    Holds the outputs, the workspace and the stream, so a call costs one C-ABI
+    call plus pointer reads: for training loops that sparsify the same buffer
+    every iteration.  The library still validates every call."""
+
+    def __init__(self, n: int, k: int, device="cuda", stream=None):
+        lib = _load()
+        self.n, self.k = int(n), int(k)
+        self.device = torch.device(device)
+        need = lib.tgs_topk_workspace_bytes(self.n, self.k)
+        if need == 0:
+            raise ValueError("invalid sizes n=%d k=%d" % (n, k))
+        self.ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
+        self.out_idx = torch.empty(self.k, dtype=torch.int32, device=self.device)
+        self.out_val = torch.empty(self.k, dtype=torch.float32, device=self.device)
+        self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
+        self._fn = lib.tgs_topk_ef_step
+        self._args = (self.out_idx.data_ptr() if self.k else None, self.out_val.data_ptr() if self.k else None,
+                      self.ws.data_ptr(), self.ws.numel(), self.stream.cuda_stream)
+
+    def __call__(self, grad: torch.Tensor, residual: torch.Tensor):
+        if grad.numel() != self.n or residual.numel() != self.n:
+            raise ValueError("this step is prepared for n=%d" % self.n)
+        oi, ov, wp, wn, st = self._args
+        status = self._fn(grad.data_ptr(), residual.data_ptr(), self.n, self.k, oi, ov, wp, wn, st)
+        if status:
+            _check(status, "tgs_topk_ef_step")
+        return self.out_idx, self.out_val
+
+
 def threshold_workspace_bytes(n: int) -> int:
     return int(_load().tgs_threshold_workspace_bytes(n))
 
@@ -273,13 +307,25 @@ def profile_next_call(start_event, stop_event):
     """The next topk/threshold call records these torch.cuda.Events around its
     streaming pass (on its stream)."""
     lib = _load()
+    for ev in (start_event, stop_event):
+        if ev is not None and not ev.cuda_event:
+            ev.record()  # torch creates the HIP event lazily, on its first record
     s = start_event.cuda_event if start_event is not None else None
     e = stop_event.cuda_event if stop_event is not None else None
     _check(lib.tgs_profile_next_call(s, e), "tgs_profile_next_call")
 
 
+def profile_elapsed_ms(start_event, stop_event) -> float:
+    """Milliseconds between two events recorded by the library."""
+    ms = ctypes.c_float()
+    _check(_load().tgs_profile_elapsed_ms(start_event.cuda_event, stop_event.cuda_event, ctypes.byref(ms)),
+           "tgs_profile_elapsed_ms")
+    return ms.value
+
+
 __all__ = [
-    "topk_ef_step", "threshold_ef_step", "gtopk_merge", "topk_workspace_bytes", "threshold_workspace_bytes",
-    "gtopk_workspace_bytes", "check_device_error", "set_option", "profile_next_call", "library", "workspace",
+    "TopkStep", "topk_ef_step", "threshold_ef_step", "gtopk_merge", "topk_workspace_bytes", "threshold_workspace_bytes",
+    "gtopk_workspace_bytes", "check_device_error", "set_option", "profile_next_call", "profile_elapsed_ms",
+    "library", "workspace",
     "TgsError", "OPT_TOPK_PATH", "OPT_MAIN_GRID", "LIB_PATH",
 ]

@@ -95,6 +95,14 @@ extern "C" tgs_status tgs_profile_next_call(hipEvent_t start, hipEvent_t stop) {
   return TGS_OK;
 }
 
+extern "C" tgs_status tgs_profile_elapsed_ms(hipEvent_t start, hipEvent_t stop, float* ms) {
+  if (!start || !stop || !ms) return fail(TGS_EINVAL, "profile_elapsed_ms: null argument");
+  hipError_t e = hipEventSynchronize(stop);
+  if (e == hipSuccess) e = hipEventElapsedTime(ms, start, stop);
+  if (e != hipSuccess) return fail(TGS_EHIP, "profile_elapsed_ms: %s", hipGetErrorString(e));
+  return TGS_OK;
+}
+
 extern "C" tgs_status tgs_check_device_error(const void* workspace, hipStream_t stream) {
   if (!workspace) return fail(TGS_EINVAL, "check_device_error: null workspace");
   hipError_t e = hipStreamSynchronize(stream);

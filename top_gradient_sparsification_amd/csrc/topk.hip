@@ -7,7 +7,7 @@
 // Analysis on Top-k Gradient Sparsification ..." names gradient sorting as the
 // GPU bottleneck, so nothing here sorts more than the selected entries.
 //
-// Fast path (four launches, one pass over the data):
+// Fast path (three launches, one pass over the data):
 //   k_sample    reads ~1% of grad+residual in 64-element chunks, builds a
 //               13-bit histogram of key >> 18 and, in its last workgroup, turns
 //               it into a plan: a guess T_guess with about 1.4k keys above it
@@ -20,13 +20,14 @@
 //               counts, a validity verdict, the bucket gathered into LDS and
 //               bitonic-sorted by (key desc, index asc); entries whose global
 //               rank is below k are written out and their residual zeroed.
-//   k_general   exits at once when the verdict holds; otherwise runs the exact
+//               When the verdict fails, the same 64 workgroups run the exact
 //               general path below on acc (now in residual).
 // The result never depends on the guess: the fast path's output is used only
 // when every candidate was kept, at least k keys reached T_guess and every
 // bucket holding a rank below k fit in LDS.  Otherwise the exact path runs.
 //
-// General path (k_general, one workgroup per compute unit, grid barriers):
+// General path (grid barriers, every workgroup resident): used as the fallback
+// inside k_finish, and on its own (k_general) where no fast path applies:
 //   radix select of the k-th key over 11/11/9-bit digits, counts per
 //   workgroup, ordered compaction of the selected entries in ascending index
 //   order (ties at the k-th key resolved by index), a stable LSD radix sort of
@@ -44,15 +45,22 @@ namespace tgs {
 constexpr int kSampleChunk = 64;           // contiguous elements per sample chunk
 constexpr int kHistShift = 18;             // sample histogram bin = key >> 18
 constexpr int kHistBins = 1 << (31 - kHistShift);  // 8192
-constexpr int kSampleThreads = 256;
+constexpr int kSampleThreads = 1024;
 constexpr int kSampleBlocks = 64;
+constexpr int kSampleUnroll = 8;          // chunks whose loads one wave issues together
+constexpr int kSampleKeyCap = 5120;       // sample keys one workgroup keeps (80 chunks)
+constexpr int kListPerBlock = 160;        // top sample keys one workgroup may publish
+constexpr int kListCap = kSampleBlocks * kListPerBlock;  // 10240
+constexpr int64_t kMaxChunks = (int64_t)kSampleBlocks * (kSampleKeyCap / 64);
+constexpr int kRankBinCap = 256;          // bins up to this size are ranked by counting
 constexpr int kMaxBuckets = 64;
-constexpr int kSlot = 16;                  // entries per (workgroup, bucket)
+constexpr int kSlot = 15;                  // entries per (workgroup, bucket); a count >= 16 means overflow
 constexpr int kMaxMainBlocks = 2048;
 constexpr int kMainThreads = 256;
-constexpr int kMainU = 1;                  // float4 per thread per tile
+constexpr int kMainU = 4;                  // float4 per thread per tile
 constexpr int kFinishThreads = 1024;
 constexpr int kFinishCap = 4096;           // entries one finish workgroup sorts
+constexpr int kSubBins = 2048;             // key sub-ranges of a bucket in the finish sort
 constexpr int kGenBlocks = 256;
 constexpr int kGenThreads = 512;
 constexpr int64_t kFastMinN = 1 << 16;
@@ -70,7 +78,11 @@ struct TopkCtl {
   u32 err;        // device error word: offset 0 of every workspace
   u32 ticket;     // k_sample arrivals
   u32 verdict;    // 1 when k_finish produced the whole output
-  u32 pad0[61];
+  u32 fallbacks;  // calls whose plan did not hold (never reset by the library)
+  u32 why;        // OR of the reasons plans failed: 1 plan, 2 slot overflow,
+                  // 4 bucket over capacity, 8 fewer than k candidates
+  u32 pad_lc;
+  u32 pad0[58];
   Plan plan;
 };
 
@@ -86,7 +98,7 @@ static_assert(sizeof(TopkCtl) <= 4096, "control block too large");
 
 // Workspace layout (every region 256-byte aligned).
 struct TopkLayout {
-  size_t ctl, shist, ghist, gcnt, lsd_cnt, lsd_pre, lsd_tot, cnt, slots, bufA, bufB, total;
+  size_t ctl, shist, slist, ghist, gcnt, lsd_cnt, lsd_pre, lsd_tot, cnt, slots, bufA, bufB, total;
   bool fast_possible;
 };
 
@@ -107,6 +119,7 @@ static TopkLayout topk_layout(int64_t n, int64_t k) {
   L.fast_possible = fast_eligible(n, k);
   L.ctl = take(4096);
   L.shist = take(sizeof(u32) * kHistBins);
+  L.slist = take(sizeof(u32) * (kListCap + kSampleBlocks));
   L.ghist = take(sizeof(GenState));
   L.gcnt = take(sizeof(u32) * 2 * kGenBlocks);
   L.lsd_cnt = take(sizeof(u32) * 256 * kGenBlocks);
@@ -124,6 +137,7 @@ static TopkLayout topk_layout(int64_t n, int64_t k) {
 struct SampleParams {
   int64_t n;
   int64_t chunks;       // number of 64-element chunks sampled
+  int64_t stride;       // chunk c starts at c * stride (stride = n / chunks >= 512)
   u32 c_target;         // sample count that must lie above T_guess
   u32 bucket_samples;   // expected sample count per bucket
   u32 break_plan;       // test hook: publish a plan that cannot hold
@@ -143,7 +157,9 @@ static SampleParams sample_params(int64_t n, int64_t k) {
   int64_t chunks = (int64_t)std::ceil(m / kSampleChunk);
   chunks = std::max<int64_t>(chunks, kSampleBlocks);
   chunks = std::min<int64_t>(chunks, n / (8 * kSampleChunk));
+  chunks = std::min<int64_t>(chunks, kMaxChunks);
   sp.chunks = std::max<int64_t>(chunks, 1);
+  sp.stride = n / sp.chunks;
   double m_real = (double)sp.chunks * kSampleChunk;
   sp.c_target = (u32)std::max(1.0, std::ceil(tau * m_real / (double)n));
   sp.bucket_samples = (u32)std::max(1.0, std::ceil(bucket_elems * m_real / (double)n));
@@ -151,65 +167,174 @@ static SampleParams sample_params(int64_t n, int64_t k) {
 }
 
 // ----------------------------------------------------------- k_sample ----
+// One wave per sampled chunk (64 consecutive elements at c * stride); each
+// wave issues the loads of up to kSampleUnroll chunks before using any, and
+// the workgroup keeps every sample key in LDS.  Each workgroup publishes the
+// top of its 13-bit histogram (bins down to where its own count from the top
+// reaches 8x its share of c_target, +32) and the sample keys in those bins.
+// Everything published goes through returning device atomics, so no cache
+// write-back fences are needed; the last workgroup to arrive (relaxed
+// ticket) builds the plan:
+//   - T_guess = the c_target-th largest sample key, and bucket boundaries =
+//     the (j+1)*bucket_samples-th largest, found exactly: the published keys
+//     are grouped by bin (offsets from the histogram's suffix sums) and the
+//     keys of each bin that holds a wanted rank are ranked by counting;
+//   - where that is not possible (inconsistent counts, a bin larger than
+//     kExactBinCap) the key is interpolated inside its bin.
+// The plan is only a guess: k_finish checks that it held before using it.
 __global__ __launch_bounds__(kSampleThreads) void k_sample(const float* __restrict__ grad,
                                                            const float* __restrict__ residual,
                                                            SampleParams sp, u32* __restrict__ shist,
-                                                           TopkCtl* __restrict__ ctl) {
-  __shared__ u32 s_h[kHistBins];  // 32 KB
-  __shared__ u32 s_last;
-  __shared__ u32 s_scan[kSampleThreads / kWave + 1];
-  __shared__ u32 s_bT;
+                                                           u32* __restrict__ slist, TopkCtl* __restrict__ ctl) {
+  constexpr int NT = kSampleThreads;
+  constexpr int per = kHistBins / NT;  // bins per thread, top first
+  constexpr u32 kNoKey = 0xFFFFFFFFu;
+  __shared__ u32 s_h[kHistBins];        // 32 KB histogram, then suffix sums
+  __shared__ u32 s_keys[kListCap];      // 40 KB sample keys; last workgroup: the published list
+  __shared__ u32 s_cur[kHistBins];      // 32 KB last workgroup: group cursors, then bin flags
+  __shared__ u32 s_grp[kListCap];       // 40 KB last workgroup: the list grouped by bin
+  __shared__ u32 s_scan[NT / kWave + 1];
+  __shared__ u32 s_tkey[kMaxBuckets + 1];  // wanted keys: [0] T_guess, [1+j] boundary j
+  __shared__ u32 s_last, s_floor, s_bT, s_exact;
   const int tid = threadIdx.x;
-  for (int i = tid; i < kHistBins; i += kSampleThreads) s_h[i] = 0;
+  for (int i = tid; i < kHistBins; i += NT) s_h[i] = 0;
+  for (int i = tid; i < kSampleKeyCap; i += NT) s_keys[i] = kNoKey;
+  if (tid == 0) s_floor = kHistBins;
   __syncthreads();
 
   const int lane = lane_id();
-  const int waves = kSampleThreads / kWave;
+  constexpr int waves = NT / kWave;
+  const int w = tid / kWave;
   const int64_t wstride = (int64_t)gridDim.x * waves;
-  for (int64_t c = (int64_t)blockIdx.x * waves + tid / kWave; c < sp.chunks; c += wstride) {
-    int64_t start = c * sp.n / sp.chunks;
-    int64_t i = start + lane;
-    if (lane < kSampleChunk && i < sp.n) {
-      float a = residual[i] + grad[i];
-      atomicAdd(&s_h[key_of(a) >> kHistShift], 1u);
+  const int64_t first = (int64_t)blockIdx.x * waves + w;
+  for (int64_t t0 = 0; first + t0 * wstride < sp.chunks; t0 += kSampleUnroll) {
+    float gg[kSampleUnroll], rr[kSampleUnroll];
+    bool ok[kSampleUnroll];
+#pragma unroll
+    for (int j = 0; j < kSampleUnroll; ++j) {
+      const int64_t c = first + (t0 + j) * wstride;
+      const int64_t i = c * sp.stride + lane;
+      ok[j] = c < sp.chunks && i < sp.n;
+      gg[j] = ok[j] ? grad[i] : 0.0f;
+      rr[j] = ok[j] ? residual[i] : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < kSampleUnroll; ++j) {
+      if (!ok[j]) continue;
+      const u32 key = key_of(rr[j] + gg[j]);
+      atomicAdd(&s_h[key >> kHistShift], 1u);
+      const int64_t slot = ((t0 + j) * waves + w) * kWave + lane;
+      if (slot < kSampleKeyCap) s_keys[slot] = key;
     }
   }
   __syncthreads();
-  for (int i = tid; i < kHistBins; i += kSampleThreads) {
-    u32 v = s_h[i];
-    if (v) add_agent_relaxed(&shist[i], v);
+  // Publish the top of this workgroup's histogram -- bins down to where its
+  // own count from the top reaches 8x its share of c_target (+32) -- and the
+  // sample keys in those bins (at most kListPerBlock, in this workgroup's own
+  // region of the list; its count goes to slist[kListCap + block]).  All of it
+  // uses returning device atomics, issued together and awaited once.
+  {
+    const int hi = kHistBins - per * tid;
+    u32 own = 0;
+#pragma unroll
+    for (int q = 1; q <= per; ++q) own += s_h[hi - q];
+    u32 total;
+    const u32 above = block_exclusive_sum<NT>(own, s_scan, total);
+    const u32 want = 8u * ((sp.c_target + gridDim.x - 1) / gridDim.x) + 32u;
+    u32 run = above;
+    int lowest = kHistBins;
+    for (int q = 1; q <= per; ++q) {
+      if (run >= want) break;  // bins below this one are not needed
+      lowest = hi - q;
+      run += s_h[hi - q];
+    }
+    if (lowest < kHistBins) atomicMin(&s_floor, (u32)lowest);
   }
-  __threadfence();
   __syncthreads();
-  if (tid == 0) s_last = (add_agent_acqrel(&ctl->ticket, 1u) == gridDim.x - 1);
+  {
+    const u32 floor_bin = s_floor;
+    u32 mine = 0;
+    for (int i = tid; i < kSampleKeyCap; i += NT) {
+      const u32 key = s_keys[i];
+      mine += key != kNoKey && (key >> kHistShift) >= floor_bin;
+    }
+    u32 count;
+    u32 pos = block_exclusive_sum<NT>(mine, s_scan, count);
+    u32 sink = 0;
+    // histogram bins >= floor_bin
+    for (int b = kHistBins - 1 - tid; b >= (int)floor_bin; b -= NT) {
+      const u32 v = s_h[b];
+      if (v) sink += add_agent_relaxed(&shist[b], v);
+    }
+    // keys in those bins
+    u32* region = slist + (int64_t)blockIdx.x * kListPerBlock;
+    for (int i = tid; i < kSampleKeyCap; i += NT) {
+      const u32 key = s_keys[i];
+      if (key != kNoKey && (key >> kHistShift) >= floor_bin) {
+        if (pos < (u32)kListPerBlock)
+          sink += __hip_atomic_exchange(&region[pos], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ++pos;
+      }
+    }
+    if (tid == 0) sink += __hip_atomic_exchange(&slist[kListCap + blockIdx.x], count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (sink == 0x12345678u) s_scan[0] = sink;  // keeps the returned values live
+  }
+  __syncthreads();
+  if (tid == 0) s_last = (add_agent_relaxed(&ctl->ticket, 1u) == gridDim.x - 1);
   __syncthreads();
   if (!s_last) return;
 
-  // ---- last workgroup: histogram -> plan ----
-  __threadfence();
-  for (int i = tid; i < kHistBins; i += kSampleThreads) s_h[i] = ld_agent(&shist[i]);
+  // ---- last workgroup: histogram + published keys -> plan ----
+  {
+    u32 v[per];
+#pragma unroll
+    for (int j = 0; j < per; ++j) v[j] = ld_agent(&shist[tid + j * NT]);
+#pragma unroll
+    for (int j = 0; j < per; ++j) s_h[tid + j * NT] = v[j];
+  }
+  // offsets of the published regions (one lane of wave 0 per workgroup);
+  // K = all published keys, or ~0 if a workgroup had more than its region holds
+  static_assert(kSampleBlocks == kWave, "one lane per sampling workgroup");
+  __shared__ u32 s_cnt[kSampleBlocks + 1];
+  if (tid < kWave) {
+    const u32 c = ld_agent(&slist[kListCap + tid]);
+    const u32 cc = std::min(c, (u32)kListPerBlock);
+    u32 x = cc;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const u32 y = __shfl_up(x, d, kWave);
+      if (tid >= d) x += y;
+    }
+    s_cnt[tid] = x - cc;
+    const bool trunc = ballot(c > (u32)kListPerBlock) != 0;
+    if (tid == kWave - 1) s_cnt[kSampleBlocks] = trunc ? 0xFFFFFFFFu : x;
+  }
   __syncthreads();
-  // suffix sums: thread t owns the 32 bins [8192-32(t+1), 8192-32t) (top first)
-  constexpr int per = kHistBins / kSampleThreads;  // 32
-  const int hi = kHistBins - per * tid;            // exclusive upper bin
+  const u32 K = s_cnt[kSampleBlocks];
+  const int hi = kHistBins - per * tid;  // thread t owns bins [hi - per, hi), top first
   u32 own = 0;
-  for (int b = hi - 1; b >= hi - per; --b) own += s_h[b];
+#pragma unroll
+  for (int q = 1; q <= per; ++q) own += s_h[hi - q];
   u32 total;
-  u32 above = block_exclusive_sum<kSampleThreads>(own, s_scan, total);
+  u32 above = block_exclusive_sum<NT>(own, s_scan, total);
   // convert s_h into inclusive suffix sums cum[b] = sum_{b' >= b} h[b']
   {
     u32 run = above;
-    for (int b = hi - 1; b >= hi - per; --b) {
-      run += s_h[b];
-      s_h[b] = run;
+#pragma unroll
+    for (int q = 1; q <= per; ++q) {
+      run += s_h[hi - q];
+      s_h[hi - q] = run;
     }
   }
-  if (tid == 0) s_bT = 0xFFFFFFFFu;
+  if (tid == 0) {
+    s_bT = 0xFFFFFFFFu;
+    s_exact = (K == total && K <= (u32)kListCap) ? 1u : 0u;  // K = ~0 if a region was truncated
+  }
   __syncthreads();
   // b_T = the largest bin with cum[b_T] >= c_target (cum is non-increasing in b)
-  for (int b = hi - 1; b >= hi - per; --b) {
-    if (s_h[b] >= sp.c_target) {
-      atomicMax((int*)&s_bT, b);  // s_bT starts at -1 as int
+  for (int q = 1; q <= per; ++q) {
+    if (s_h[hi - q] >= sp.c_target) {
+      atomicMax((int*)&s_bT, hi - q);  // s_bT starts at -1 as int
       break;
     }
   }
@@ -226,23 +351,176 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const float* __restri
     }
     return;
   }
-  const u32 cT = s_h[bT];
-  u32 nb = (cT + sp.bucket_samples - 1) / sp.bucket_samples;
-  nb = std::max(1u, std::min(nb, (u32)kMaxBuckets));
-  // boundary j (j < nb-1): the largest bin b with cum[b] >= (j+1)*bucket_samples
-  if (tid < (int)nb - 1) {
-    u32 q = (u32)(tid + 1) * sp.bucket_samples;
-    int lo = bT, hi2 = kHistBins - 1;  // answer in [bT, 8191]; cum[bT] >= q holds
+  auto bin_of_rank = [&](u32 q) -> int {  // largest b with cum[b] >= q (cum[0] >= q)
+    int lo = 0, hi2 = kHistBins - 1;
     while (lo < hi2) {
       int mid = (lo + hi2 + 1) >> 1;
       if (s_h[mid] >= q) lo = mid;
       else hi2 = mid - 1;
     }
-    plan->lo[tid] = (u32)lo << kHistShift;
+    return lo;
+  };
+  auto cum_above = [&](int b) -> u32 { return b + 1 < kHistBins ? s_h[b + 1] : 0u; };
+  // wanted ranks: [0] c_target, [1+j] (j+1)*bucket_samples for j < nb-1
+  u32 nb = (sp.c_target + sp.bucket_samples - 1) / sp.bucket_samples;
+  nb = std::max(1u, std::min(nb, (u32)kMaxBuckets));
+  const int ntarget = (int)nb;  // T_guess + nb-1 boundaries
+  // default: interpolation inside the bin (used where no exact key is found)
+  if (tid < ntarget) {
+    const u32 q = tid == 0 ? sp.c_target : (u32)tid * sp.bucket_samples;
+    const int b = bin_of_rank(q);
+    const u32 above_b = cum_above(b);
+    const u32 h = s_h[b] - above_b;  // >= q - above_b >= 1
+    const u32 f = q - above_b;
+    const u32 off = (u32)((((u64)f << kHistShift) + h - 1) / h);  // in [1, 2^18]
+    s_tkey[tid] = (((u32)b + 1u) << kHistShift) - off;
+  }
+  for (int i = tid; i < kHistBins; i += NT) s_cur[i] = 0;
+  for (int i = tid; i < kListCap; i += NT) s_grp[i] = kNoKey;
+  __syncthreads();
+  if (s_exact) {
+    // flag the bins that hold a wanted rank: 1 = small (rank by counting),
+    // 2 = large (second-level histogram)
+    if (tid < ntarget) {
+      const u32 q = tid == 0 ? sp.c_target : (u32)tid * sp.bucket_samples;
+      const int b = bin_of_rank(q);
+      atomicMax(&s_cur[b], s_h[b] - cum_above(b) <= (u32)kRankBinCap ? 1u : 2u);
+    }
+    {  // wave w copies regions w, w + 16, ...: every load issued before any use
+      constexpr int kPerWave = kSampleBlocks / (NT / kWave);
+      constexpr int kRows = (kListPerBlock + kWave - 1) / kWave;
+      u32 v[kPerWave][kRows];
+#pragma unroll
+      for (int r = 0; r < kPerWave; ++r) {
+        const int b2 = w + r * (NT / kWave);
+        const u32 c = (b2 + 1 < kSampleBlocks ? s_cnt[b2 + 1] : K) - s_cnt[b2];
+#pragma unroll
+        for (int j = 0; j < kRows; ++j) {
+          const u32 i = (u32)(lane + j * kWave);
+          v[r][j] = i < c ? ld_agent(&slist[b2 * kListPerBlock + i]) : kNoKey;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < kPerWave; ++r) {
+        const int b2 = w + r * (NT / kWave);
+        const u32 o = s_cnt[b2];
+        const u32 c = (b2 + 1 < kSampleBlocks ? s_cnt[b2 + 1] : K) - o;
+#pragma unroll
+        for (int j = 0; j < kRows; ++j) {
+          const u32 i = (u32)(lane + j * kWave);
+          if (i < c) s_keys[o + i] = v[r][j];
+        }
+      }
+    }
+    __syncthreads();
+    // large flagged bins, listed once each (few: the pile-ups).  Targets in
+    // rank order are q_1 < ... < q_{nb-1} <= q_0 = c_target, so their bins do
+    // not increase; a target lists its bin when the previous one's differs.
+    __shared__ u32 s_fat[kMaxBuckets + 1];
+    __shared__ u32 s_nfat;
+    if (tid == 0) s_nfat = 0;
+    __syncthreads();
+    if (tid < ntarget) {
+      const int order = tid == 0 ? ntarget - 1 : tid - 1;  // position in rank order
+      const u32 q = tid == 0 ? sp.c_target : (u32)tid * sp.bucket_samples;
+      const int b = bin_of_rank(q);
+      int bprev = -1;
+      if (order > 0) {
+        const u32 qp = (u32)order * sp.bucket_samples;  // the target just before in rank order
+        bprev = bin_of_rank(qp);
+      }
+      if (s_cur[b] == 2u && b != bprev) s_fat[atomicAdd(&s_nfat, 1u)] = (u32)b;
+    }
+    __syncthreads();  // s_cur is rewritten below
+    // small flagged bins: group their keys (group of bin b starts at cum[b+1])
+    for (int i = tid; i < kHistBins; i += NT) s_cur[i] = s_cur[i] == 1u ? (cum_above(i) | 0x80000000u) : 0u;
+    __syncthreads();
+    for (u32 i = tid; i < K; i += NT) {
+      const u32 key = s_keys[i];
+      const u32 b = key >> kHistShift;
+      if (s_cur[b] & 0x80000000u) {
+        const u32 pos = (atomicAdd(&s_cur[b], 1u) & 0x7FFFFFFFu);
+        if (pos < (u32)kListCap) s_grp[pos] = key;
+      }
+    }
+    __syncthreads();
+    // rank each grouped key inside its bin (ties broken by position); a key of
+    // global rank q-1 (0-based, from the top) is the wanted key for rank q
+    for (u32 i = tid; i < K; i += NT) {
+      const u32 x = s_grp[i];
+      if (x == kNoKey) continue;
+      const int b = (int)(x >> kHistShift);
+      const u32 g0 = cum_above(b), g1 = s_h[b];
+      u32 r = 0;
+      for (u32 t = g0; t < g1; ++t) {
+        const u32 y = s_grp[t];
+        r += (y > x) || (y == x && t < i);
+      }
+      const u32 rank1 = g0 + r + 1;  // 1-based rank of x among all samples
+      if (rank1 == sp.c_target) s_tkey[0] = x;
+      if (rank1 % sp.bucket_samples == 0) {
+        const u32 jj = rank1 / sp.bucket_samples;
+        if (jj >= 1 && jj < nb) s_tkey[jj] = x;
+      }
+    }
+    __syncthreads();
+    // large bins: histogram of key bits [17:5] (8192 sub-bins of 32 keys) over
+    // the bin's keys; a wanted key is the lower edge of the sub-bin where the
+    // count from the top reaches its rank (never above the exact key)
+    constexpr int kSubShift = 5;
+    constexpr int kSubN = 1 << (kHistShift - kSubShift);  // 8192
+    u32* sub = s_grp;  // free again
+    for (u32 f = 0; f < s_nfat; ++f) {
+      const u32 fb = s_fat[f];
+      for (int i = tid; i < kSubN; i += NT) sub[i] = 0;
+      __syncthreads();
+      for (u32 i = tid; i < K; i += NT) {
+        const u32 key = s_keys[i];
+        if ((key >> kHistShift) == fb) atomicAdd(&sub[(key >> kSubShift) & (kSubN - 1)], 1u);
+      }
+      __syncthreads();
+      const int shi = kSubN - per * tid;  // thread t owns sub-bins [shi - per, shi), top first
+      u32 sown = 0;
+#pragma unroll
+      for (int q2 = 1; q2 <= per; ++q2) sown += sub[shi - q2];
+      u32 stot;
+      const u32 sabove = block_exclusive_sum<NT>(sown, s_scan, stot);
+      {
+        u32 run = sabove;
+#pragma unroll
+        for (int q2 = 1; q2 <= per; ++q2) {
+          run += sub[shi - q2];
+          sub[shi - q2] = run;  // suffix sums inside the bin
+        }
+      }
+      __syncthreads();
+      if (tid < ntarget) {
+        const u32 q = tid == 0 ? sp.c_target : (u32)tid * sp.bucket_samples;
+        if ((u32)bin_of_rank(q) == fb) {
+          const u32 want = q - cum_above((int)fb);  // rank inside the bin, 1-based
+          int lo = 0, hi2 = kSubN - 1;              // largest sub-bin with suffix >= want
+          while (lo < hi2) {
+            int mid = (lo + hi2 + 1) >> 1;
+            if (sub[mid] >= want) lo = mid;
+            else hi2 = mid - 1;
+          }
+          s_tkey[tid] = (fb << kHistShift) | ((u32)lo << kSubShift);
+        }
+      }
+      __syncthreads();
+    }
   }
   if (tid == 0) {
-    plan->lo[nb - 1] = (u32)bT << kHistShift;
-    plan->t_guess = (u32)bT << kHistShift;
+    const u32 tg = s_tkey[0];
+    u32 prev = 0xFFFFFFFFu;
+    for (int j = 0; j + 1 < (int)nb; ++j) {
+      u32 v = std::max(s_tkey[1 + j], tg);
+      v = std::min(v, prev);
+      plan->lo[j] = v;
+      prev = v;
+    }
+    plan->lo[nb - 1] = tg;
+    plan->t_guess = tg;
     plan->nbuckets = nb;
     plan->valid = 1;
   }
@@ -319,10 +597,11 @@ __global__ __launch_bounds__(kMainThreads) void k_ef_main(MainArgs a) {
     }
     const v4f* __restrict__ gv = (const v4f*)(g + a.head);
     v4f* __restrict__ rv = (v4f*)(r + a.head);
-    const int64_t per = (a.nv + gridDim.x - 1) / gridDim.x;
-    const int64_t vb = (int64_t)blockIdx.x * per;
-    const int64_t ve = std::min<int64_t>(a.nv, vb + per);
-    for (int64_t base = vb; base < ve; base += kMainThreads * kMainU) {
+    // tiles of kMainThreads * kMainU vectors, dealt round-robin to the
+    // workgroups so that the whole grid sweeps the arrays front to back
+    constexpr int64_t tile = (int64_t)kMainThreads * kMainU;
+    const int64_t ve = a.nv;
+    for (int64_t base = (int64_t)blockIdx.x * tile; base < ve; base += (int64_t)gridDim.x * tile) {
       v4f gg[kMainU], rr[kMainU];
 #pragma unroll
       for (int u = 0; u < kMainU; ++u) {
@@ -363,10 +642,7 @@ __global__ __launch_bounds__(kMainThreads) void k_ef_main(MainArgs a) {
       }
     }
   } else {
-    const int64_t per = (a.n + gridDim.x - 1) / gridDim.x;
-    const int64_t eb = (int64_t)blockIdx.x * per;
-    const int64_t ee = std::min<int64_t>(a.n, eb + per);
-    for (int64_t i = eb + tid; i < ee; i += kMainThreads) {
+    for (int64_t i = (int64_t)blockIdx.x * kMainThreads + tid; i < a.n; i += (int64_t)gridDim.x * kMainThreads) {
       float acc = r[i] + g[i];
       r[i] = acc;
       main_emit<SPEC>(i, __float_as_uint(acc), tg, nb, s_lo, s_cnt, a.slots);
@@ -376,132 +652,6 @@ __global__ __launch_bounds__(kMainThreads) void k_ef_main(MainArgs a) {
     __syncthreads();
     if (tid < kMaxBuckets)
       a.cnt[(int64_t)blockIdx.x * kMaxBuckets + tid] = (unsigned char)std::min(s_cnt[tid], 255u);
-  }
-}
-
-// ---------------------------------------------------------- k_finish ----
-struct FinishArgs {
-  const Plan* plan;
-  const unsigned char* cnt;
-  const Pair* slots;
-  int G1;
-  int64_t n;
-  int64_t k;
-  int32_t* out_idx;
-  float* out_val;
-  float* residual;
-  TopkCtl* ctl;
-  u32* shist;
-};
-
-__global__ __launch_bounds__(kFinishThreads) void k_finish(FinishArgs a) {
-  __shared__ Pair s_a[kFinishCap];         // 32 KB
-  __shared__ u32 s_rows[kMaxMainBlocks];   // (row << 8) | count for this bucket
-  __shared__ u32 s_tot[kMaxBuckets];
-  __shared__ u32 s_lo[kMaxBuckets];
-  __shared__ u32 s_nrows, s_ovf, s_pos;
-  __shared__ u32 s_ok, s_nb;
-  __shared__ int64_t s_start, s_mytot;
-  const int tid = threadIdx.x;
-  const int j = blockIdx.x;
-  if (tid < kMaxBuckets) {
-    s_tot[tid] = 0;
-    s_lo[tid] = a.plan->lo[tid];
-  }
-  if (tid == 0) {
-    s_nrows = 0;
-    s_ovf = 0;
-    s_pos = 0;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    u32 nb = a.plan->nbuckets;
-    bool ok = a.plan->valid == 1 && nb >= 1 && nb <= (u32)kMaxBuckets;
-    if (ok) {
-      for (u32 i = 1; i < nb; ++i) ok = ok && s_lo[i] <= s_lo[i - 1];
-      ok = ok && s_lo[nb - 1] == a.plan->t_guess;
-    }
-    s_ok = ok;
-    s_nb = ok ? nb : 1;
-  }
-  // slot counts: G1 rows of 64 bytes, read as 16 words per row; thread t always
-  // sees word t % 16 of a row, i.e. buckets 4*(t%16) .. 4*(t%16)+3
-  const u32* cw = (const u32*)a.cnt;
-  const int q = tid & 15;
-  u32 acc4[4] = {0, 0, 0, 0};
-  u32 ovf = 0;
-  for (int w = tid; w < a.G1 * 16; w += kFinishThreads) {
-    u32 x = cw[w];
-    int row = w >> 4;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      u32 v = (x >> (8 * c)) & 0xFFu;
-      acc4[c] += v;
-      ovf |= (v > (u32)kSlot);
-      if (v && 4 * q + c == j) {
-        u32 p = atomicAdd(&s_nrows, 1u);
-        s_rows[p] = ((u32)row << 8) | v;
-      }
-    }
-  }
-  // reduce over lanes sharing q (lanes q, q+16, q+32, q+48 of each wave)
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    u32 v = acc4[c];
-    v += __shfl_xor(v, 16, kWave);
-    v += __shfl_xor(v, 32, kWave);
-    if ((lane_id() & 48) == 0 && v) atomicAdd(&s_tot[4 * q + c], v);
-  }
-  if (ovf) atomicOr(&s_ovf, 1u);
-  __syncthreads();
-  if (tid == 0) {
-    bool valid = s_ok && !s_ovf;
-    int64_t start = 0, mystart = 0, mytot = 0;
-    for (int i = 0; i < kMaxBuckets; ++i) {
-      int64_t t = s_tot[i];
-      if (i >= (int)s_nb) {
-        valid = valid && t == 0;
-        continue;
-      }
-      if (start < a.k && t > kFinishCap) valid = false;
-      if (i == j) {
-        mystart = start;
-        mytot = t;
-      }
-      start += t;
-    }
-    if (start < a.k) valid = false;
-    s_ok = valid;
-    s_start = mystart;
-    s_mytot = (j < (int)s_nb) ? mytot : 0;
-    if (j == 0) a.ctl->verdict = valid ? 1u : 0u;
-  }
-  __syncthreads();
-  const int64_t mystart = s_start, mytot = s_mytot;
-  if (s_ok && mytot > 0 && mystart < a.k) {
-    int N = 1;
-    while (N < mytot) N <<= 1;
-    for (int i = (int)mytot + tid; i < N; i += kFinishThreads) s_a[i] = pair_sentinel();
-    for (u32 rI = tid; rI < s_nrows; rI += kFinishThreads) {
-      u32 rc = s_rows[rI];
-      u32 row = rc >> 8, c = rc & 0xFFu;
-      u32 base = atomicAdd(&s_pos, c);
-      const Pair* src = a.slots + ((int64_t)row * kMaxBuckets + j) * kSlot;
-      for (u32 e = 0; e < c && base + e < (u32)kFinishCap; ++e) s_a[base + e] = src[e];
-    }
-    __syncthreads();
-    lds_bitonic_sort<kFinishThreads>(s_a, N);
-    const int64_t take = std::min<int64_t>(mytot, a.k - mystart);
-    for (int64_t p = tid; p < take; p += kFinishThreads) {
-      Pair e = s_a[p];
-      a.out_idx[mystart + p] = e.idx;
-      a.out_val[mystart + p] = __uint_as_float(e.bits);
-      if (e.idx >= 0 && (int64_t)e.idx < a.n) a.residual[e.idx] = 0.0f;
-    }
-  }
-  if (j == 0) {
-    for (int i = tid; i < kHistBins; i += kFinishThreads) a.shist[i] = 0u;
-    if (tid == 0) a.ctl->ticket = 0u;
   }
 }
 
@@ -520,8 +670,6 @@ struct GenArgs {
   Pair* bufA;
   Pair* bufB;
   GridBar bar;
-  const u32* verdict;
-  int mode;  // 0: run only when *verdict == 0; 1: always run
 };
 
 // Sum over the block of one value per thread.
@@ -532,8 +680,10 @@ __device__ __forceinline__ u32 block_sum(u32 v, u32* lds) {
   return total;
 }
 
-__global__ __launch_bounds__(kGenThreads) void k_general(GenArgs a) {
-  constexpr int NT = kGenThreads;
+// The exact general path.  Every workgroup of the grid must be resident at
+// once (grid barriers); NT is the workgroup size.
+template <int NT>
+__device__ void general_path(const GenArgs& a) {
   constexpr int NW = NT / kWave;
   __shared__ u32 s_hist[2048];
   __shared__ u32 s_wcnt[NW][256];
@@ -541,7 +691,6 @@ __global__ __launch_bounds__(kGenThreads) void k_general(GenArgs a) {
   __shared__ u32 s_run[256];
   __shared__ u32 s_scan[NW + 1];
   __shared__ u32 s_found[4];
-  if (a.mode == 0 && *a.verdict == 1u) return;
   const int tid = threadIdx.x;
   const int G = gridDim.x;
   const int b = blockIdx.x;
@@ -757,6 +906,234 @@ __global__ __launch_bounds__(kGenThreads) void k_general(GenArgs a) {
   }
 }
 
+__global__ __launch_bounds__(kGenThreads) void k_general(GenArgs a) { general_path<kGenThreads>(a); }
+
+// ---------------------------------------------------------- k_finish ----
+struct FinishArgs {
+  const Plan* plan;
+  const unsigned char* cnt;
+  const Pair* slots;
+  int G1;
+  int64_t n;
+  int64_t k;
+  int32_t* out_idx;
+  float* out_val;
+  float* residual;
+  TopkCtl* ctl;
+  u32* shist;
+  GenArgs gen;  // fallback: the exact general path on this kernel's grid
+};
+
+__global__ __launch_bounds__(kFinishThreads) void k_finish(FinishArgs a) {
+  constexpr int NT = kFinishThreads;
+  constexpr int NW = NT / kWave;
+  __shared__ Pair s_a[kFinishCap];         // 32 KB: the bucket as gathered
+  __shared__ Pair s_b[kFinishCap];         // 32 KB: grouped by key sub-range
+  __shared__ u32 s_sub_cnt[kSubBins];      // 8 KB
+  __shared__ u32 s_sub_off[kSubBins];      // 8 KB
+  __shared__ u32 s_scan[NW + 1];
+  __shared__ u32 s_rows[kMaxMainBlocks];   // (row << 8) | count for this bucket
+  __shared__ u32 s_part[NW][kMaxBuckets];  // per-wave bucket totals
+  __shared__ u32 s_lo[kMaxBuckets];
+  __shared__ u32 s_nrows, s_ovf, s_pos, s_kmin, s_kmax;
+  __shared__ u32 s_ok;
+  __shared__ int64_t s_start, s_mytot;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int w = tid / kWave;
+  const int j = blockIdx.x;
+  if (tid < kMaxBuckets) s_lo[tid] = a.plan->lo[tid];
+  if (tid == 0) {
+    s_nrows = 0;
+    s_ovf = 0;
+    s_pos = 0;
+    s_kmin = 0xFFFFFFFFu;
+    s_kmax = 0;
+  }
+  // Slot counts: G1 rows of 64 bytes (one per bucket), read as 16 words per
+  // row.  Thread t always sees word q = t % 16 of a row (buckets 4q .. 4q+3)
+  // and adds the four byte counts as two pairs of 16-bit lanes.
+  const u32* cw = (const u32*)a.cnt;
+  const int q = tid & 15;
+  constexpr int kWordsPerThread = kMaxMainBlocks * kMaxBuckets / 4 / NT;
+  const int nwords = a.G1 * (kMaxBuckets / 4);
+  u32 xw[kWordsPerThread];
+#pragma unroll
+  for (int i = 0; i < kWordsPerThread; ++i) {  // all loads in flight at once
+    const int wd = tid + i * NT;
+    xw[i] = wd < nwords ? cw[wd] : 0u;
+  }
+  __syncthreads();
+  u32 even = 0, odd = 0, ovf = 0;
+  const bool mine = q == (j >> 2);
+  const int myb = j & 3;
+#pragma unroll
+  for (int i = 0; i < kWordsPerThread; ++i) {
+    const u32 x = xw[i];
+    even += x & 0x00FF00FFu;
+    odd += (x >> 8) & 0x00FF00FFu;
+    ovf |= x & 0xF0F0F0F0u;  // a count >= 16 = kSlot + 1: the slot overflowed
+    if (mine) {
+      const u32 v = (x >> (8 * myb)) & 0xFFu;
+      if (v) {
+        u32 p = atomicAdd(&s_nrows, 1u);
+        s_rows[p] = ((u32)((tid + i * NT) >> 4) << 8) | v;
+      }
+    }
+  }
+  // reduce over the lanes of a wave that share q (q, q+16, q+32, q+48)
+  even += __shfl_xor(even, 16, kWave);
+  even += __shfl_xor(even, 32, kWave);
+  odd += __shfl_xor(odd, 16, kWave);
+  odd += __shfl_xor(odd, 32, kWave);
+  if (lane < 16) {
+    s_part[w][4 * q + 0] = even & 0xFFFFu;
+    s_part[w][4 * q + 1] = odd & 0xFFFFu;
+    s_part[w][4 * q + 2] = even >> 16;
+    s_part[w][4 * q + 3] = odd >> 16;
+  }
+  if (ovf) atomicOr(&s_ovf, 1u);
+  __syncthreads();
+  // Verdict and bucket offsets, in wave 0 (lane i = bucket i).
+  if (w == 0) {
+    u32 t = 0;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) t += s_part[ww][lane];
+    const u32 nb = a.plan->nbuckets;
+    bool plan_ok = a.plan->valid == 1 && nb >= 1 && nb <= (u32)kMaxBuckets;
+    if (plan_ok) {
+      const u32 lo_i = s_lo[lane];
+      const u32 lo_prev = lane > 0 ? s_lo[lane - 1] : 0xFFFFFFFFu;
+      const bool mono = (u32)lane >= nb || (u32)lane == 0 || lo_i <= lo_prev;
+      plan_ok = ballot(!mono) == 0 && s_lo[nb - 1] == a.plan->t_guess;
+    }
+    u32 x = t;  // inclusive scan of the totals over buckets 0..63
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      u32 y = __shfl_up(x, d, kWave);
+      if (lane >= d) x += y;
+    }
+    const int64_t start = (int64_t)(x - t), all = __shfl(x, kWave - 1, kWave);
+    const bool live = (u32)lane < nb;
+    const bool bad = (!live && t != 0) || (live && start < a.k && t > (u32)kFinishCap);
+    const bool valid = plan_ok && !s_ovf && ballot(bad) == 0 && all >= a.k;
+    const u32 why = (plan_ok ? 0u : 1u) | (s_ovf ? 2u : 0u) | (ballot(bad) != 0 ? 4u : 0u) | (all >= a.k ? 0u : 8u);
+    if (lane == j) {
+      s_start = start;
+      s_mytot = live ? t : 0;
+    }
+    if (lane == 0) {
+      s_ok = valid;
+      if (j == 0) {
+        a.ctl->verdict = valid ? 1u : 0u;
+        if (!valid) {
+          a.ctl->fallbacks += 1u;
+          a.ctl->why |= why;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (!s_ok) {
+    // the plan did not hold: every workgroup of this grid runs the exact path
+    // (they all computed the same verdict from the same counts)
+    general_path<NT>(a.gen);
+    if (j == 0) {
+      for (int i = tid; i < kHistBins; i += NT) a.shist[i] = 0u;
+      if (tid == 0) {
+        a.ctl->ticket = 0u;
+      }
+    }
+    return;
+  }
+  const int64_t mystart = s_start, mytot = s_mytot;
+  if (mytot > 0 && mystart < a.k) {
+    const int m = (int)mytot;
+    for (int i = tid; i < kSubBins; i += NT) s_sub_cnt[i] = 0;
+    for (u32 rI = tid; rI < s_nrows; rI += NT) {
+      u32 rc = s_rows[rI];
+      u32 row = rc >> 8, c = rc & 0xFFu;
+      u32 base = atomicAdd(&s_pos, c);
+      const Pair* src = a.slots + ((int64_t)row * kMaxBuckets + j) * kSlot;
+      Pair e8[kSlot];
+#pragma unroll
+      for (int e = 0; e < kSlot; ++e) e8[e] = (u32)e < c ? src[e] : pair_sentinel();
+      u32 kmin = 0xFFFFFFFFu, kmax = 0;
+#pragma unroll
+      for (int e = 0; e < kSlot; ++e)
+        if ((u32)e < c && base + e < (u32)kFinishCap) {
+          s_a[base + e] = e8[e];
+          const u32 kk = key_of_bits(e8[e].bits);
+          kmin = std::min(kmin, kk);
+          kmax = std::max(kmax, kk);
+        }
+      if (c) {
+        atomicMin(&s_kmin, kmin);
+        atomicMax(&s_kmax, kmax);
+      }
+    }
+    __syncthreads();
+    // Split [kmin, kmax] into kSubBins equal key sub-ranges, numbered from the
+    // top (descending key), and group the entries by sub-range (counting
+    // sort).  Inside a sub-range an entry's place is the number of entries of
+    // that sub-range that rank before it; ranks are unique (indices differ).
+    const u32 kmin = s_kmin;
+    const u32 span = s_kmax - kmin + 1u;  // >= 1
+    const int bits = span <= 1 ? 0 : 32 - __clz(span - 1);
+    const int sh = bits > 11 ? bits - 11 : 0;  // kSubBins = 2^11
+    auto sub_of = [&](const Pair& e) -> u32 {
+      const u32 d = (key_of_bits(e.bits) - kmin) >> sh;
+      return (u32)(kSubBins - 1) - (d < (u32)kSubBins ? d : (u32)(kSubBins - 1));
+    };
+    for (int i = tid; i < m; i += NT) atomicAdd(&s_sub_cnt[sub_of(s_a[i])], 1u);
+    __syncthreads();
+    {
+      constexpr int per = kSubBins / NT;  // 2 consecutive sub-ranges per thread
+      u32 v[per], own = 0;
+#pragma unroll
+      for (int q2 = 0; q2 < per; ++q2) {
+        v[q2] = s_sub_cnt[tid * per + q2];
+        own += v[q2];
+      }
+      u32 tot;
+      u32 ex = block_exclusive_sum<NT>(own, s_scan, tot);
+#pragma unroll
+      for (int q2 = 0; q2 < per; ++q2) {
+        s_sub_off[tid * per + q2] = ex;
+        s_sub_cnt[tid * per + q2] = ex;  // becomes the fill cursor
+        ex += v[q2];
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < m; i += NT) {
+      Pair e = s_a[i];
+      s_b[atomicAdd(&s_sub_cnt[sub_of(e)], 1u)] = e;
+    }
+    __syncthreads();
+    const int64_t take = std::min<int64_t>(mytot, a.k - mystart);
+    for (int i = tid; i < m; i += NT) {
+      const Pair e = s_b[i];
+      const u32 sb = sub_of(e);
+      const u32 s0 = s_sub_off[sb], s1 = s_sub_cnt[sb];  // the cursor ended at the range's end
+      const u64 re = pair_rank(e);
+      u32 r = 0;
+      for (u32 t = s0; t < s1; ++t) r += pair_rank(s_b[t]) < re;
+      const int64_t p = (int64_t)(s0 + r);
+      if (p < take) {
+        a.out_idx[mystart + p] = e.idx;
+        a.out_val[mystart + p] = __uint_as_float(e.bits);
+        if (e.idx >= 0 && (int64_t)e.idx < a.n) a.residual[e.idx] = 0.0f;
+      }
+    }
+  }
+  if (j == 0) {
+    for (int i = tid; i < kHistBins; i += NT) a.shist[i] = 0u;
+    if (tid == 0) {
+      a.ctl->ticket = 0u;
+    }
+  }
+}
+
 }  // namespace tgs
 
 // ==================================================================== host ==
@@ -824,7 +1201,7 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
     SampleParams sp = sample_params(n, k);
     sp.break_plan = path == 2 ? 1u : 0u;
     hipLaunchKernelGGL(k_sample, dim3(kSampleBlocks), dim3(kSampleThreads), 0, stream, grad, residual, sp,
-                       (u32*)(ws + L.shist), ctl);
+                       (u32*)(ws + L.shist), (u32*)(ws + L.slist), ctl);
   }
   if (ev0) (void)hipEventRecord(ev0, stream);
   if (fast) {
@@ -837,21 +1214,6 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
   if (ev1) (void)hipEventRecord(ev1, stream);
 
   if (k > 0) {
-    if (fast) {
-      FinishArgs fa{};
-      fa.plan = &ctl->plan;
-      fa.cnt = ma.cnt;
-      fa.slots = ma.slots;
-      fa.G1 = G1;
-      fa.n = n;
-      fa.k = k;
-      fa.out_idx = out_idx;
-      fa.out_val = out_val;
-      fa.residual = residual;
-      fa.ctl = ctl;
-      fa.shist = (u32*)(ws + L.shist);
-      hipLaunchKernelGGL(k_finish, dim3(kMaxBuckets), dim3(kFinishThreads), 0, stream, fa);
-    }
     GenArgs ga{};
     ga.acc = residual;
     ga.residual = residual;
@@ -870,20 +1232,37 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
     ga.bar.gen = &gs->bar_gen;
     ga.bar.abort = &gs->bar_abort;
     ga.bar.err = &ctl->err;
-    ga.verdict = &ctl->verdict;
-    ga.mode = fast ? 0 : 1;
-    // every workgroup of k_general must be resident at once (grid barriers):
-    // at most one per compute unit per occupancy slot, and never above kGenBlocks
-    static int occ = 0;
-    if (occ == 0) {
-      int o = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, k_general, kGenThreads, 0) != hipSuccess || o < 1) o = 1;
-      occ = o;
+    if (fast) {
+      FinishArgs fa{};
+      fa.plan = &ctl->plan;
+      fa.cnt = ma.cnt;
+      fa.slots = ma.slots;
+      fa.G1 = G1;
+      fa.n = n;
+      fa.k = k;
+      fa.out_idx = out_idx;
+      fa.out_val = out_val;
+      fa.residual = residual;
+      fa.ctl = ctl;
+      fa.shist = (u32*)(ws + L.shist);
+      fa.gen = ga;
+      // kMaxBuckets workgroups of kFinishThreads: far below one per compute
+      // unit, so all are resident for the fallback's grid barriers
+      hipLaunchKernelGGL(k_finish, dim3(kMaxBuckets), dim3(kFinishThreads), 0, stream, fa);
+    } else {
+      // every workgroup of k_general must be resident at once (grid barriers):
+      // at most one per compute unit per occupancy slot, and never above kGenBlocks
+      static int occ = 0;
+      if (occ == 0) {
+        int o = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, k_general, kGenThreads, 0) != hipSuccess || o < 1) o = 1;
+        occ = o;
+      }
+      const int cus = device_cu_count();
+      if (cus <= 0) return fail(TGS_EHIP, "topk_ef_step: cannot read the compute-unit count");
+      const int G = std::max(1, std::min(kGenBlocks, cus * occ));
+      hipLaunchKernelGGL(k_general, dim3(G), dim3(kGenThreads), 0, stream, ga);
     }
-    const int cus = device_cu_count();
-    if (cus <= 0) return fail(TGS_EHIP, "topk_ef_step: cannot read the compute-unit count");
-    const int G = std::max(1, std::min(kGenBlocks, cus * occ));
-    hipLaunchKernelGGL(k_general, dim3(G), dim3(kGenThreads), 0, stream, ga);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TGS_EHIP, "topk_ef_step: launch failed: %s", hipGetErrorString(e));

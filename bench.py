@@ -41,9 +41,34 @@ def parse():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--traffic", type=str, default=None,
-                    help="JSON file with measured HBM bytes per k_ef_main launch (from the rocprofv3 counters)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="before the steps, copy a 256 MiB buffer three times (a plain copy kernel of known "
+                         "size, for scaling the FETCH_SIZE/WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+# HBM bytes per k_ef_main launch from two rocprofv3 --pmc runs of this script
+# (FETCH_SIZE, then WRITE_SIZE), each scaled by what the same counter read for
+# the 256 MiB copy of --copy-calibration.  Valid only for the streaming-pass
+# source they were taken on: `source_sha256` is the hash of csrc/topk.hip then.
+MEASURED_TRAFFIC = {
+    "source_sha256": "db00ee30b428f29c20b4044aeeeae395bfad21c89b1f502209bcab6278a52513",
+    # FETCH_SIZE 100,042.5 KiB x (262,144 / 131,083.5: the copy's true read over its counter)
+    "fetch_bytes": 204_869_065,
+    # WRITE_SIZE 101,168.7 KiB x 1.0 (the copy's counter read exactly 262,144 KiB)
+    "write_bytes": 103_596_749,
+}
+
+
+def traffic_per_launch():
+    import hashlib
+    if not MEASURED_TRAFFIC:
+        return None
+    src = os.path.join(ROOT, "top_gradient_sparsification_amd", "csrc", "topk.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if sha != MEASURED_TRAFFIC["source_sha256"]:
+        return None  # the kernel changed since the counters were taken
+    return MEASURED_TRAFFIC["fetch_bytes"] + MEASURED_TRAFFIC["write_bytes"]
 
 
 def main():
@@ -68,6 +93,13 @@ def main():
     resid = [torch.zeros(N, dtype=torch.float32, device=dev) for _ in range(sets)]
     run = tgs.TopkStep(N, k, dev)
     ws = run.ws
+    if args.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step(t):
         run(grads[(t + t // pool) % pool], resid[t % sets])
@@ -106,9 +138,7 @@ def main():
     gbps_step = bytes_step / (ms_per_step * 1e-3) / 1e9
     gbps_main = bytes_main / (main_avg_ms * 1e-3) / 1e9
 
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        traffic = json.load(open(args.traffic)).get("bytes_per_launch")
+    traffic = traffic_per_launch()
 
     cpu = None
     if not args.no_cpu_baseline:

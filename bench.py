@@ -15,8 +15,9 @@ them from HBM, and each residual buffer meets all sixteen gradients before one
 repeats.  The W warm-up steps give every residual buffer its error-feedback
 history (W = 20 -> 5 steps each).
 
-Prints one JSON line.  `roofline` covers the dominant kernel (the streaming
-pass k_ef_main), timed per launch with HIP events on the stream it runs on;
+Prints one JSON line.  `roofline` covers the dominant kernel, k_step (the
+whole fused step: 12n + 8k algorithmic bytes per launch), timed per launch
+with HIP events recorded by the library on the stream it launches on;
 `cpu_baseline` is the plain C oracle on one host core on the same workload.
 """
 from __future__ import annotations
@@ -47,7 +48,7 @@ def parse():
     return ap.parse_args()
 
 
-# HBM bytes per k_ef_main launch from two rocprofv3 --pmc runs of this script
+# HBM bytes per k_step launch from two rocprofv3 --pmc runs of this script
 # (FETCH_SIZE, then WRITE_SIZE), each scaled by what the same counter read for
 # the 256 MiB copy of --copy-calibration.  Valid only for the streaming-pass
 # source they were taken on: `source_sha256` is the hash of csrc/topk.hip then.
@@ -110,9 +111,10 @@ def main():
     torch.cuda.synchronize()
     tgs.check_device_error(ws)
     fb0 = int(ws[12:16].view(torch.int32).item())  # calls whose sampled plan did not hold
+    rs0 = int(ws[20:24].view(torch.int32).item())  # workgroup shares re-read (incomplete local lists)
 
     K = args.steps
-    every = 8  # the streaming pass of every 8th timed step is bracketed by events
+    every = 8  # every 8th timed step is bracketed by events
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(0, K, every)]
     for a, b in ev:  # torch creates the HIP event on its first record
         a.record()
@@ -129,14 +131,14 @@ def main():
     tgs.check_device_error(ws)
     fast = int(ws[8:12].view(torch.int32).item())  # verdict word of the last step
     fallbacks = int(ws[12:16].view(torch.int32).item()) - fb0
+    rescans = int(ws[20:24].view(torch.int32).item()) - rs0
     elapsed = t1 - t0
     ms_per_step = elapsed * 1e3 / K
     main_ms = sorted(tgs.profile_elapsed_ms(a, b) for a, b in ev)
     main_avg_ms = sum(main_ms) / len(main_ms)
     bytes_step = 12.0 * N + 8.0 * k          # read grad + residual, write residual + k pairs
-    bytes_main = 12.0 * N                    # the streaming pass's share
     gbps_step = bytes_step / (ms_per_step * 1e-3) / 1e9
-    gbps_main = bytes_main / (main_avg_ms * 1e-3) / 1e9
+    gbps_main = bytes_step / (main_avg_ms * 1e-3) / 1e9
 
     traffic = traffic_per_launch()
 
@@ -178,13 +180,14 @@ def main():
         "roofline_frac_step": gbps_step / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "achieved": gbps_main, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": gbps_main / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": "k_ef_main", "bytes_per_launch": bytes_main,
+                     "kernel": "k_step", "bytes_per_launch": bytes_step,
                      "avg_launch_us": main_avg_ms * 1e3, "median_launch_us": main_ms[len(main_ms) // 2] * 1e3,
                      "launches_timed": len(main_ms)},
         "cpu_baseline": cpu,
         "last_step_fast_path": bool(fast == 1),
         "timed_steps_on_exact_fallback": fallbacks,
         "fallback_reasons": int(ws[16:20].view(torch.int32).item()),
+        "timed_share_rescans": rescans,
     }
     print(json.dumps(rec))
 

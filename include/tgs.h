@@ -32,8 +32,11 @@
  *   - `workspace` is caller-owned device memory of at least the size the
  *     matching *_workspace_bytes() query returns.  One workspace serves one
  *     call at a time; calls that share a workspace must be ordered (same
- *     stream).  Correctness never depends on its previous contents; a
- *     zero-filled workspace lets the very first call take the fast path.
+ *     stream).  Its first 8 KB carry synchronisation counters from one call
+ *     to the next (every call leaves them at zero): a new workspace must be
+ *     zero-filled, and the caller must not write to it between calls.  Any
+ *     of the three operations may use a workspace after any other.  The rest
+ *     is scratch.
  *   - Magnitude order: key(x) = bits(x) & 0x7FFFFFFF as an unsigned integer.
  *     This matches |x| for every non-NaN value, ranks NaN above infinity and
  *     makes -0 and +0 equal.  Among equal keys the lower index comes first.
@@ -66,7 +69,9 @@ size_t tgs_topk_workspace_bytes(int64_t n, int64_t k);
 
 /*
  * Error-feedback top-k step ([EF], [CONV]; the selection replaces the full
- * sort that [SORT] identifies as the bottleneck).
+ * sort that [SORT] identifies as the bottleneck).  For k up to ~48k (and
+ * n >= 2^18) it is one kernel launch that reads grad and residual once; other
+ * sizes take an exact radix-select path.  Both give the same result.
  *   grad      [n] float32, read only.
  *   residual  [n] float32, in/out: on entry the accumulated error, on exit
  *             acc with the selected entries set to +0.0f.
@@ -139,15 +144,18 @@ const char* tgs_last_error(void);
  *                       2 = fast path with a sample plan that cannot hold
  *                       (exercises the on-device fallback).
  *   TGS_OPT_MAIN_GRID   0 = automatic, else the number of workgroups of the
- *                       streaming pass (results must not depend on it).
+ *                       streaming launch, capped at what can be resident;
+ *                       below 65 the exact path runs (results must not
+ *                       depend on it).
  */
 #define TGS_OPT_TOPK_PATH 1
 #define TGS_OPT_MAIN_GRID 2
 tgs_status tgs_set_option(int32_t option, int64_t value);
 
-/* One-shot profiling hook: the next tgs_topk_ef_step or
-   tgs_threshold_ef_step call records `start` right before and `stop` right
-   after its streaming pass, on its stream.  Pass null events to clear. */
+/* One-shot profiling hook: the next tgs_topk_ef_step call records `start`
+   right before its first launch and `stop` right after its last (the whole
+   step); the next tgs_threshold_ef_step call brackets its streaming pass.
+   Both on the call's stream.  Pass null events to clear. */
 tgs_status tgs_profile_next_call(hipEvent_t start, hipEvent_t stop);
 
 /* Milliseconds between two events recorded through tgs_profile_next_call

@@ -144,7 +144,7 @@ def test_misaligned_slices(tgs_gpu, off_g, off_r):
         assert np.all(host(rb[:off_r]) == 0) and np.all(host(rb[off_r + n:]) == 0)
 
 
-@pytest.mark.parametrize("grid", [1, 7, 256, 2048])
+@pytest.mark.parametrize("grid", [1, 7, 64, 65, 100, 256, 2048])
 def test_results_do_not_depend_on_grid(tgs_gpu, grid):
     rng = np.random.default_rng(5)
     n = 2_000_000

@@ -336,7 +336,7 @@ static GtLayout gt_layout(int64_t P, int64_t k) {
   GtLayout L{};
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   size_t pk = sizeof(Pair) * (size_t)P * (size_t)std::max<int64_t>(k, 1);
-  L.slots = 256;
+  L.slots = kWorkspaceHeader;  // after the header whose first word is the error word
   L.tmp = L.slots + al(pk);
   L.M = L.tmp + al(pk);
   L.f0 = L.M + al(pk);  // (P/2) merges x 2k entries <= P*k

@@ -20,6 +20,12 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
+// Every workspace starts with this header; its first word is the device error
+// word.  The top-k step keeps its control block (counters that are zero
+// between calls) here; the other operations touch only the error word, so a
+// workspace can move between operations without clearing it.
+constexpr size_t kWorkspaceHeader = 8192;
+
 // ---------------------------------------------------------------- keys ----
 __device__ __forceinline__ u32 key_of_bits(u32 b) { return b & 0x7FFFFFFFu; }
 __device__ __forceinline__ u32 key_of(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
@@ -57,6 +63,54 @@ __device__ __forceinline__ u32 add_agent_acqrel(u32* p, u32 v) {
 __device__ __forceinline__ u32 add_agent_relaxed(u32* p, u32 v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ u32 xchg_agent(u32* p, u32 v) {
+  return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ u64 ld_agent64(const u64* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ u64 add_agent64(u64* p, u64 v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ u64 xchg_agent64(u64* p, u64 v) {
+  return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ u32 or_agent(u32* p, u32 v) {
+  return __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------- wave scans (DPP) ----
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
+// row broadcasts (no LDS traffic).  Every lane of the wave must be active.
+__device__ __forceinline__ u32 wave_inclusive_sum(u32 x) {
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
+// Sum, maximum and minimum over the wave, returned to every lane.
+__device__ __forceinline__ u32 wave_sum(u32 x) { return __builtin_amdgcn_readlane(wave_inclusive_sum(x), 63); }
+__device__ __forceinline__ u32 wave_max(u32 x) {
+  x = max(x, (u32)__builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, false));
+  x = max(x, (u32)__builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, false));
+  x = max(x, (u32)__builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, false));
+  x = max(x, (u32)__builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, false));
+  x = max(x, (u32)__builtin_amdgcn_update_dpp(0u, x, 0x142, 0xa, 0xf, false));
+  x = max(x, (u32)__builtin_amdgcn_update_dpp(0u, x, 0x143, 0xc, 0xf, false));
+  return __builtin_amdgcn_readlane(x, 63);
+}
+__device__ __forceinline__ u32 wave_min(u32 x) {
+  x = min(x, (u32)__builtin_amdgcn_update_dpp(0xFFFFFFFFu, x, 0x111, 0xf, 0xf, false));
+  x = min(x, (u32)__builtin_amdgcn_update_dpp(0xFFFFFFFFu, x, 0x112, 0xf, 0xf, false));
+  x = min(x, (u32)__builtin_amdgcn_update_dpp(0xFFFFFFFFu, x, 0x114, 0xf, 0xf, false));
+  x = min(x, (u32)__builtin_amdgcn_update_dpp(0xFFFFFFFFu, x, 0x118, 0xf, 0xf, false));
+  x = min(x, (u32)__builtin_amdgcn_update_dpp(0xFFFFFFFFu, x, 0x142, 0xa, 0xf, false));
+  x = min(x, (u32)__builtin_amdgcn_update_dpp(0xFFFFFFFFu, x, 0x143, 0xc, 0xf, false));
+  return __builtin_amdgcn_readlane(x, 63);
+}
 
 // -------------------------------------------------- block-wide scans ----
 // Exclusive prefix sum of one u32 per thread over the block; `total` gets the
@@ -66,19 +120,13 @@ __device__ __forceinline__ u32 block_exclusive_sum(u32 v, u32* lds, u32& total) 
   constexpr int NW = NT / kWave;
   const int lane = lane_id();
   const int w = threadIdx.x / kWave;
-  // inclusive scan inside the wave with shuffles
-  u32 x = v;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    u32 y = __shfl_up(x, d, kWave);
-    if (lane >= d) x += y;
-  }
+  const u32 x = wave_inclusive_sum(v);
   if (lane == kWave - 1) lds[w] = x;
   __syncthreads();
   u32 wave_off = 0, sum = 0;
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
-    u32 t = lds[i];
+    const u32 t = lds[i];
     if (i < w) wave_off += t;
     sum += t;
   }
@@ -87,40 +135,18 @@ __device__ __forceinline__ u32 block_exclusive_sum(u32 v, u32* lds, u32& total) 
   return wave_off + x - v;
 }
 
-// ------------------------------------------- LDS bitonic sort of Pairs ----
-// Sorts a[0..N) ascending by pair_rank; N is a power of two, entries past the
-// live ones must hold pair_sentinel().  All NT threads of the block call it.
-template <int NT>
-__device__ void lds_bitonic_sort(Pair* a, int N) {
-  for (int size = 2; size <= N; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < (N >> 1); i += NT) {
-        int lo = 2 * i - (i & (stride - 1));
-        int hi = lo + stride;
-        bool up = (lo & size) == 0;
-        Pair x = a[lo], y = a[hi];
-        bool swap = up ? (pair_rank(x) > pair_rank(y)) : (pair_rank(x) < pair_rank(y));
-        if (swap) {
-          a[lo] = y;
-          a[hi] = x;
-        }
-      }
-      __syncthreads();
-    }
-  }
-}
-
 // ---------------------------------------------------- grid barrier ----
-// For kernels whose whole grid is resident at once (grid no larger than one
-// workgroup per compute unit).  Arrivals go to `count`; the last arrival
-// resets it and bumps `gen`, which the others poll.  A bounded spin turns a
-// missing workgroup into an error (flag bit in *err, `abort` set) instead of
-// a hang; after an abort every barrier returns at once.
+// For the `nwg` workgroups 0 .. nwg-1 of a kernel whose whole grid is resident
+// at once.  Arrivals go to `count`; the last arrival resets it and bumps
+// `gen`, which the others poll.  A bounded spin turns a missing workgroup into
+// an error (flag bit in *err, `abort` set) instead of a hang; after an abort
+// every barrier returns at once.
 struct GridBar {
   u32* count;  // zero before the kernel starts
   u32* gen;    // any value
   u32* abort;  // zero before the kernel starts
   u32* err;    // device error word
+  u32 nwg;     // participating workgroups
 };
 
 constexpr u32 kErrBarrierTimeout = 1u << 1;
@@ -140,7 +166,7 @@ __device__ __forceinline__ bool grid_sync(const GridBar& gb) {
     } else {
       u32 g0 = ld_agent(gb.gen);
       u32 t = add_agent_acqrel(gb.count, 1u);
-      if (t == gridDim.x - 1) {
+      if (t == gb.nwg - 1) {
         st_agent(gb.count, 0u);
         __threadfence();
         add_agent_acqrel(gb.gen, 1u);

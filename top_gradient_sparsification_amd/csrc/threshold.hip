@@ -257,7 +257,7 @@ static ThrLayout thr_layout(int64_t n) {
   // the stash keeps up to 1/64 of them (at least 256)
   int64_t per = (n + L.G - 1) / L.G + 8;
   L.stash_cap = std::max<int64_t>(256, (per + 63) / 64);
-  L.cnt = 256;  // after a 256-byte header whose first word is the error word
+  L.cnt = kWorkspaceHeader;  // after the header whose first word is the error word
   size_t cnt_bytes = (((size_t)L.G * 4) + 255) & ~(size_t)255;
   L.stash = L.cnt + cnt_bytes;
   L.total = L.stash + (size_t)L.G * (size_t)L.stash_cap * sizeof(Pair);

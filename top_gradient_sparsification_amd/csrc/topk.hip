@@ -5,29 +5,42 @@
 // accumulated error to the gradient, send the k entries of largest magnitude,
 // keep everything else as the new error.  The listing's entry "Empirical
 // Analysis on Top-k Gradient Sparsification ..." names gradient sorting as the
-// GPU bottleneck, so nothing here sorts more than the selected entries.
+// GPU bottleneck, so nothing here sorts more than the candidates.
 //
-// Fast path (three launches, one pass over the data):
-//   k_sample    reads ~1% of grad+residual in 64-element chunks, builds a
-//               13-bit histogram of key >> 18 and, in its last workgroup, turns
-//               it into a plan: a guess T_guess with about 1.4k keys above it
-//               and up to 64 key ranges ("buckets") of ~1k expected entries.
-//   k_ef_main   the only pass over the data: acc = residual + grad, residual <-
-//               acc (non-temporal), and every key >= T_guess is stored as
-//               (index, bits) in a fixed slot of (workgroup, bucket): no global
-//               atomics, no ordering between workgroups.
-//   k_finish    one workgroup per bucket: totals and prefix from the slot
-//               counts, a validity verdict, the bucket gathered into LDS and
-//               bitonic-sorted by (key desc, index asc); entries whose global
-//               rank is below k are written out and their residual zeroed.
-//               When the verdict fails, the same 64 workgroups run the exact
-//               general path below on acc (now in residual).
-// The result never depends on the guess: the fast path's output is used only
-// when every candidate was kept, at least k keys reached T_guess and every
-// bucket holding a rank below k fit in LDS.  Otherwise the exact path runs.
+// Fast path: ONE launch, k_step, one workgroup of 1024 threads per compute
+// unit, every workgroup resident.  Workgroup 0 plans; workgroups 1..G-1 each
+// stream one contiguous share of the vector; workgroups 0..63 finish.
+//   sample   every workgroup reads ~1/G of a ~1% sample (64-element chunks
+//            spread over the whole vector) into a 12-bit LDS histogram of
+//            key >> 19.  It publishes its top sample keys (device atomics) and
+//            derives its own local threshold T_loc, a sample quantile several
+//            times below the k-th key.
+//   plan     workgroup 0 gathers the published keys and ranks them exactly:
+//            T_guess (about 1.4k entries expected above it) and up to 64
+//            bucket boundaries between T_guess and the top.  It publishes
+//            the plan while the others stream.
+//   stream   acc = residual + grad, one pass.  Entries with key < T_loc go
+//            straight back to residual (non-temporal float4 stores); the
+//            others are kept in an LDS list and their residual is left for
+//            later.  Nothing waits for the plan here.
+//   publish  at the end of its share a workgroup reads the plan, writes
+//            back the list entries below T_guess, sorts the rest (the
+//            candidates) by bucket and publishes them with device atomics.
+//   finish   finisher f waits for every workgroup, adds up the bucket counts,
+//            checks that the plan held (at least k candidates, every bucket
+//            that holds a rank below k fits in LDS, nothing overflowed),
+//            gathers bucket f, orders it by (key desc, index asc), writes the
+//            entries of rank < k to the output and every candidate's residual
+//            (+0 for the selected, acc for the rest).
+// No residual word is written by two workgroups and everything one
+// workgroup reads from another goes through device-scope atomics, so the
+// fast path needs no cache write-back fences.
 //
-// General path (grid barriers, every workgroup resident): used as the fallback
-// inside k_finish, and on its own (k_general) where no fast path applies:
+// When the plan did not hold, every workgroup writes back the acc of what it
+// published, fences, and the whole grid runs the exact general path below.
+//
+// General path (grid barriers; the fast path's fallback, and a launch of its
+// own, k_general, where the fast path does not apply):
 //   radix select of the k-th key over 11/11/9-bit digits, counts per
 //   workgroup, ordered compaction of the selected entries in ascending index
 //   order (ties at the k-th key resolved by index), a stable LSD radix sort of
@@ -42,73 +55,89 @@
 namespace tgs {
 
 // --------------------------------------------------------------- sizes ----
-constexpr int kSampleChunk = 64;           // contiguous elements per sample chunk
-constexpr int kHistShift = 18;             // sample histogram bin = key >> 18
-constexpr int kHistBins = 1 << (31 - kHistShift);  // 8192
-constexpr int kSampleThreads = 1024;
-constexpr int kSampleBlocks = 64;
-constexpr int kSampleUnroll = 8;          // chunks whose loads one wave issues together
-constexpr int kSampleKeyCap = 5120;       // sample keys one workgroup keeps (80 chunks)
-constexpr int kListPerBlock = 160;        // top sample keys one workgroup may publish
-constexpr int kListCap = kSampleBlocks * kListPerBlock;  // 10240
-constexpr int64_t kMaxChunks = (int64_t)kSampleBlocks * (kSampleKeyCap / 64);
-constexpr int kRankBinCap = 256;          // bins up to this size are ranked by counting
-constexpr int kMaxBuckets = 64;
-constexpr int kSlot = 15;                  // entries per (workgroup, bucket); a count >= 16 means overflow
-constexpr int kMaxMainBlocks = 2048;
-constexpr int kMainThreads = 256;
-constexpr int kMainU = 4;                  // float4 per thread per tile
-constexpr int kFinishThreads = 1024;
-constexpr int kFinishCap = 4096;           // entries one finish workgroup sorts
-constexpr int kSubBins = 2048;             // key sub-ranges of a bucket in the finish sort
-constexpr int kGenBlocks = 256;
+constexpr int kStepThreads = 1024;
+constexpr int kStepWaves = kStepThreads / kWave;    // 16
+constexpr int kMaxStepBlocks = 256;
+constexpr int kMaxBuckets = 64;                     // also the number of finishers
+constexpr int kHistShift = 19;                      // sample histogram bin = key >> 19
+constexpr int kHistBins = 1 << (31 - kHistShift);   // 4096
+constexpr int kSampleChunk = 64;                    // contiguous elements per sample chunk
+constexpr int kSampleRounds = 2;                    // chunks per wave at most
+constexpr int kSampleKeyCap = kSampleRounds * kStepThreads;  // sample keys per workgroup
+constexpr int kPubCap = 40;                         // sample keys one workgroup may publish
+constexpr int kPlanCap = kPubCap * kMaxStepBlocks;  // 10240
+constexpr int kRankBinCap = 256;                    // bins up to this size are ranked by counting
+constexpr int kListCap = 8192;                      // local list of one workgroup (LDS)
+constexpr int kRegionCap = 4096;                    // candidates one workgroup may publish
+constexpr int kFinishCap = 4096;                    // bucket entries a finisher orders in LDS
+constexpr int kSubBins = 2048;
+constexpr int kRawWords = 28672;                    // 112 KB of LDS shared by the phases
+constexpr int kMaxPairs = 256;                      // row pairs one workgroup remembers (for a re-read)
+constexpr int64_t kFastMinN = (int64_t)kMaxStepBlocks * kStepWaves * kSampleRounds * kSampleChunk;  // 2^19
+constexpr u32 kSpinLimit = 1u << 18;
+// plain pass + standalone general path
+constexpr int kAccThreads = 256;
+constexpr int kAccU = 4;
+constexpr int kMaxAccBlocks = 2048;
 constexpr int kGenThreads = 512;
-constexpr int64_t kFastMinN = 1 << 16;
-constexpr int64_t kFastMaxK = 48 * 1024;
+constexpr int kGenBlocks = 256;
+constexpr int kMaxGenWG = 256;  // workgroups of either general-path launch
 
+// reasons a plan did not hold (StepCtl::why)
+constexpr u32 kWhyPlan = 1u, kWhyBucket = 4u, kWhyFew = 8u, kWhyRegion = 16u, kWhyList = 32u, kWhyWait = 64u;
+
+// ------------------------------------------------------------- state ----
 struct Plan {
-  u32 valid;
-  u32 t_guess;
-  u32 nbuckets;
+  u32 valid;     // 1 when the plan below was built
+  u32 t_guess;   // candidates are the keys >= t_guess
+  u32 nbuckets;  // 1..kMaxBuckets
   u32 pad;
-  u32 lo[kMaxBuckets];  // bucket j holds keys in [lo[j], lo[j-1]); lo[-1] = 2^31
+  u32 lo[kMaxBuckets];  // bucket j holds keys in [lo[j], lo[j-1]); lo[nbuckets-1] == t_guess
 };
 
-struct TopkCtl {
-  u32 err;        // device error word: offset 0 of every workspace
-  u32 ticket;     // k_sample arrivals
-  u32 verdict;    // 1 when k_finish produced the whole output
-  u32 fallbacks;  // calls whose plan did not hold (never reset by the library)
-  u32 why;        // OR of the reasons plans failed: 1 plan, 2 slot overflow,
-                  // 4 bucket over capacity, 8 fewer than k candidates
-  u32 pad_lc;
-  u32 pad0[58];
+struct alignas(128) Counter {  // one cache line each
+  u64 v;
+  u64 pad[15];
+};
+
+// Start of every top-k workspace.  The counters are zero between calls: the
+// last workgroup to leave a k_step launch clears them.
+struct StepCtl {
+  u32 err;        // device error word (offset 0 of every workspace)
+  u32 pad0;
+  u32 verdict;    // 1 when the last fast-path call's plan held
+  u32 fallbacks;  // fast-path calls whose plan did not hold (never reset)
+  u32 why;        // OR of kWhy* reasons over those calls (never reset)
+  u32 rescans;    // workgroup shares re-read because their list was incomplete (never reset)
+  u32 pad1[58];
+  Counter samp_grp[8], samp_all;
+  Counter main_grp[8], main_all;
+  Counter exit_grp[8], exit_all;
+  Counter rows_grp[8];   // row pairs handed out per group of streaming workgroups
+  Counter plan_flag;     // 1 once the plan is published
+  Counter last_rank;     // 1 + the rank key of the k-th entry, once known
+  Counter verdict_flag;  // 1 = the plan held, 2 = run the exact path
+  Counter bad;           // low word: OR of kWhy* failures seen by the streaming workgroups
   Plan plan;
 };
+static_assert(sizeof(StepCtl) <= kWorkspaceHeader, "control block exceeds the workspace header");
 
-// State of the general path; k_ef_main's workgroup 0 clears it every call.
+// State of the general path (zero when it starts).
 struct GenState {
   u32 hist[3][2048];
   u32 bar_count;
   u32 bar_abort;
   u32 bar_gen;
-  u32 pad[61];
 };
-static_assert(sizeof(TopkCtl) <= 4096, "control block too large");
 
-// Workspace layout (every region 256-byte aligned).
 struct TopkLayout {
-  size_t ctl, shist, slist, ghist, gcnt, lsd_cnt, lsd_pre, lsd_tot, cnt, slots, bufA, bufB, total;
-  bool fast_possible;
+  size_t ctl, gstate, gcnt, lsd_cnt, lsd_pre, lsd_tot, bufA, bufB, pub, rcnt, region, total;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-static bool fast_eligible(int64_t n, int64_t k) {
-  return k > 0 && n >= kFastMinN && k <= kFastMaxK && k * 8 <= n;
-}
-
 static TopkLayout topk_layout(int64_t n, int64_t k) {
+  (void)n;
   TopkLayout L{};
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -116,542 +145,62 @@ static TopkLayout topk_layout(int64_t n, int64_t k) {
     off = align256(off + bytes);
     return o;
   };
-  L.fast_possible = fast_eligible(n, k);
-  L.ctl = take(4096);
-  L.shist = take(sizeof(u32) * kHistBins);
-  L.slist = take(sizeof(u32) * (kListCap + kSampleBlocks));
-  L.ghist = take(sizeof(GenState));
-  L.gcnt = take(sizeof(u32) * 2 * kGenBlocks);
-  L.lsd_cnt = take(sizeof(u32) * 256 * kGenBlocks);
-  L.lsd_pre = take(sizeof(u32) * 256 * kGenBlocks);
+  L.ctl = take(kWorkspaceHeader);
+  L.gstate = take(sizeof(GenState));
+  L.gcnt = take(sizeof(u32) * 2 * kMaxGenWG);
+  L.lsd_cnt = take(sizeof(u32) * 256 * kMaxGenWG);
+  L.lsd_pre = take(sizeof(u32) * 256 * kMaxGenWG);
   L.lsd_tot = take(sizeof(u32) * 256);
-  L.cnt = take(L.fast_possible ? (size_t)kMaxMainBlocks * kMaxBuckets : 0);
-  L.slots = take(L.fast_possible ? sizeof(Pair) * kMaxMainBlocks * kMaxBuckets * kSlot : 0);
   L.bufA = take(sizeof(Pair) * (size_t)std::max<int64_t>(k, 1));
   L.bufB = take(sizeof(Pair) * (size_t)std::max<int64_t>(k, 1));
+  L.pub = take(sizeof(u32) * ((size_t)kPlanCap + kMaxStepBlocks));
+  L.rcnt = take(sizeof(u32) * (size_t)kMaxStepBlocks * (kMaxBuckets / 2));
+  L.region = take(sizeof(Pair) * (size_t)kMaxStepBlocks * kRegionCap);
   L.total = off;
   return L;
 }
 
-// Sampling parameters derived from (n, k) on the host.
-struct SampleParams {
-  int64_t n;
-  int64_t chunks;       // number of 64-element chunks sampled
-  int64_t stride;       // chunk c starts at c * stride (stride = n / chunks >= 512)
-  u32 c_target;         // sample count that must lie above T_guess
-  u32 bucket_samples;   // expected sample count per bucket
-  u32 break_plan;       // test hook: publish a plan that cannot hold
-};
+// ------------------------------------------------------ phase counters ----
+// A phase completes when every workgroup of the grid has arrived.  Arrivals
+// are counted per group of workgroups (blockIdx % 8, each counter on its own
+// cache line) and the last arrival of a group bumps the phase counter, so
+// no single address takes more than G/8 + 8 atomics.  Counters start at zero.
+__device__ __forceinline__ int phase_groups(int G) { return G < 8 ? G : 8; }
 
-static SampleParams sample_params(int64_t n, int64_t k) {
-  SampleParams sp{};
-  sp.n = n;
-  double tau = std::max(1.4 * (double)k, (double)k + 8192.0);  // candidates aimed for
-  double alpha = tau / (double)k;
-  double eps = 1.0 - 1.0 / alpha;                 // relative slack below tau
-  double need_stat = 25.0 / (eps * eps);          // ~5 sigma of Poisson noise
-  double bucket_elems = std::max(512.0, 1.2 * (double)k / 56.0);
-  double nb_needed = std::ceil(1.1 * (double)k / bucket_elems);
-  double c = std::max({need_stat, 8.0 * nb_needed, 64.0});
-  double m = c * (double)n / tau;                 // sample elements
-  int64_t chunks = (int64_t)std::ceil(m / kSampleChunk);
-  chunks = std::max<int64_t>(chunks, kSampleBlocks);
-  chunks = std::min<int64_t>(chunks, n / (8 * kSampleChunk));
-  chunks = std::min<int64_t>(chunks, kMaxChunks);
-  sp.chunks = std::max<int64_t>(chunks, 1);
-  sp.stride = n / sp.chunks;
-  double m_real = (double)sp.chunks * kSampleChunk;
-  sp.c_target = (u32)std::max(1.0, std::ceil(tau * m_real / (double)n));
-  sp.bucket_samples = (u32)std::max(1.0, std::ceil(bucket_elems * m_real / (double)n));
-  return sp;
+// Thread 0 only.  True when this arrival completed the phase.
+__device__ __forceinline__ bool phase_arrive(Counter* grp, Counter* all, int G) {
+  const int ng = phase_groups(G);
+  const int x = (int)blockIdx.x % ng;
+  const u64 per = (u64)((G - 1 - x) / ng + 1);
+  if (add_agent64(&grp[x].v, 1) + 1 != per) return false;
+  return add_agent64(&all->v, 1) + 1 == (u64)ng;
 }
 
-// ----------------------------------------------------------- k_sample ----
-// One wave per sampled chunk (64 consecutive elements at c * stride); each
-// wave issues the loads of up to kSampleUnroll chunks before using any, and
-// the workgroup keeps every sample key in LDS.  Each workgroup publishes the
-// top of its 13-bit histogram (bins down to where its own count from the top
-// reaches 8x its share of c_target, +32) and the sample keys in those bins.
-// Everything published goes through returning device atomics, so no cache
-// write-back fences are needed; the last workgroup to arrive (relaxed
-// ticket) builds the plan:
-//   - T_guess = the c_target-th largest sample key, and bucket boundaries =
-//     the (j+1)*bucket_samples-th largest, found exactly: the published keys
-//     are grouped by bin (offsets from the histogram's suffix sums) and the
-//     keys of each bin that holds a wanted rank are ranked by counting;
-//   - where that is not possible (inconsistent counts, a bin larger than
-//     kExactBinCap) the key is interpolated inside its bin.
-// The plan is only a guess: k_finish checks that it held before using it.
-__global__ __launch_bounds__(kSampleThreads) void k_sample(const float* __restrict__ grad,
-                                                           const float* __restrict__ residual,
-                                                           SampleParams sp, u32* __restrict__ shist,
-                                                           u32* __restrict__ slist, TopkCtl* __restrict__ ctl) {
-  constexpr int NT = kSampleThreads;
-  constexpr int per = kHistBins / NT;  // bins per thread, top first
-  constexpr u32 kNoKey = 0xFFFFFFFFu;
-  __shared__ u32 s_h[kHistBins];        // 32 KB histogram, then suffix sums
-  __shared__ u32 s_keys[kListCap];      // 40 KB sample keys; last workgroup: the published list
-  __shared__ u32 s_cur[kHistBins];      // 32 KB last workgroup: group cursors, then bin flags
-  __shared__ u32 s_grp[kListCap];       // 40 KB last workgroup: the list grouped by bin
-  __shared__ u32 s_scan[NT / kWave + 1];
-  __shared__ u32 s_tkey[kMaxBuckets + 1];  // wanted keys: [0] T_guess, [1+j] boundary j
-  __shared__ u32 s_last, s_floor, s_bT, s_exact;
-  const int tid = threadIdx.x;
-  for (int i = tid; i < kHistBins; i += NT) s_h[i] = 0;
-  for (int i = tid; i < kSampleKeyCap; i += NT) s_keys[i] = kNoKey;
-  if (tid == 0) s_floor = kHistBins;
-  __syncthreads();
-
-  const int lane = lane_id();
-  constexpr int waves = NT / kWave;
-  const int w = tid / kWave;
-  const int64_t wstride = (int64_t)gridDim.x * waves;
-  const int64_t first = (int64_t)blockIdx.x * waves + w;
-  for (int64_t t0 = 0; first + t0 * wstride < sp.chunks; t0 += kSampleUnroll) {
-    float gg[kSampleUnroll], rr[kSampleUnroll];
-    bool ok[kSampleUnroll];
-#pragma unroll
-    for (int j = 0; j < kSampleUnroll; ++j) {
-      const int64_t c = first + (t0 + j) * wstride;
-      const int64_t i = c * sp.stride + lane;
-      ok[j] = c < sp.chunks && i < sp.n;
-      gg[j] = ok[j] ? grad[i] : 0.0f;
-      rr[j] = ok[j] ? residual[i] : 0.0f;
-    }
-#pragma unroll
-    for (int j = 0; j < kSampleUnroll; ++j) {
-      if (!ok[j]) continue;
-      const u32 key = key_of(rr[j] + gg[j]);
-      atomicAdd(&s_h[key >> kHistShift], 1u);
-      const int64_t slot = ((t0 + j) * waves + w) * kWave + lane;
-      if (slot < kSampleKeyCap) s_keys[slot] = key;
+// Thread 0 only.  Bounded wait for the phase; a timeout sets an error bit.
+__device__ __forceinline__ bool phase_wait(const Counter* all, int G, u32* err) {
+  const u64 target = (u64)phase_groups(G);
+  u32 spins = 0;
+  while (ld_agent64(&all->v) < target) {
+    __builtin_amdgcn_s_sleep(2);
+    if (++spins > kSpinLimit) {
+      atomicOr(err, kErrBarrierTimeout);
+      return false;
     }
   }
-  __syncthreads();
-  // Publish the top of this workgroup's histogram -- bins down to where its
-  // own count from the top reaches 8x its share of c_target (+32) -- and the
-  // sample keys in those bins (at most kListPerBlock, in this workgroup's own
-  // region of the list; its count goes to slist[kListCap + block]).  All of it
-  // uses returning device atomics, issued together and awaited once.
-  {
-    const int hi = kHistBins - per * tid;
-    u32 own = 0;
-#pragma unroll
-    for (int q = 1; q <= per; ++q) own += s_h[hi - q];
-    u32 total;
-    const u32 above = block_exclusive_sum<NT>(own, s_scan, total);
-    const u32 want = 8u * ((sp.c_target + gridDim.x - 1) / gridDim.x) + 32u;
-    u32 run = above;
-    int lowest = kHistBins;
-    for (int q = 1; q <= per; ++q) {
-      if (run >= want) break;  // bins below this one are not needed
-      lowest = hi - q;
-      run += s_h[hi - q];
-    }
-    if (lowest < kHistBins) atomicMin(&s_floor, (u32)lowest);
-  }
-  __syncthreads();
-  {
-    const u32 floor_bin = s_floor;
-    u32 mine = 0;
-    for (int i = tid; i < kSampleKeyCap; i += NT) {
-      const u32 key = s_keys[i];
-      mine += key != kNoKey && (key >> kHistShift) >= floor_bin;
-    }
-    u32 count;
-    u32 pos = block_exclusive_sum<NT>(mine, s_scan, count);
-    u32 sink = 0;
-    // histogram bins >= floor_bin
-    for (int b = kHistBins - 1 - tid; b >= (int)floor_bin; b -= NT) {
-      const u32 v = s_h[b];
-      if (v) sink += add_agent_relaxed(&shist[b], v);
-    }
-    // keys in those bins
-    u32* region = slist + (int64_t)blockIdx.x * kListPerBlock;
-    for (int i = tid; i < kSampleKeyCap; i += NT) {
-      const u32 key = s_keys[i];
-      if (key != kNoKey && (key >> kHistShift) >= floor_bin) {
-        if (pos < (u32)kListPerBlock)
-          sink += __hip_atomic_exchange(&region[pos], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ++pos;
-      }
-    }
-    if (tid == 0) sink += __hip_atomic_exchange(&slist[kListCap + blockIdx.x], count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (sink == 0x12345678u) s_scan[0] = sink;  // keeps the returned values live
-  }
-  __syncthreads();
-  if (tid == 0) s_last = (add_agent_relaxed(&ctl->ticket, 1u) == gridDim.x - 1);
-  __syncthreads();
-  if (!s_last) return;
-
-  // ---- last workgroup: histogram + published keys -> plan ----
-  {
-    u32 v[per];
-#pragma unroll
-    for (int j = 0; j < per; ++j) v[j] = ld_agent(&shist[tid + j * NT]);
-#pragma unroll
-    for (int j = 0; j < per; ++j) s_h[tid + j * NT] = v[j];
-  }
-  // offsets of the published regions (one lane of wave 0 per workgroup);
-  // K = all published keys, or ~0 if a workgroup had more than its region holds
-  static_assert(kSampleBlocks == kWave, "one lane per sampling workgroup");
-  __shared__ u32 s_cnt[kSampleBlocks + 1];
-  if (tid < kWave) {
-    const u32 c = ld_agent(&slist[kListCap + tid]);
-    const u32 cc = std::min(c, (u32)kListPerBlock);
-    u32 x = cc;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-      const u32 y = __shfl_up(x, d, kWave);
-      if (tid >= d) x += y;
-    }
-    s_cnt[tid] = x - cc;
-    const bool trunc = ballot(c > (u32)kListPerBlock) != 0;
-    if (tid == kWave - 1) s_cnt[kSampleBlocks] = trunc ? 0xFFFFFFFFu : x;
-  }
-  __syncthreads();
-  const u32 K = s_cnt[kSampleBlocks];
-  const int hi = kHistBins - per * tid;  // thread t owns bins [hi - per, hi), top first
-  u32 own = 0;
-#pragma unroll
-  for (int q = 1; q <= per; ++q) own += s_h[hi - q];
-  u32 total;
-  u32 above = block_exclusive_sum<NT>(own, s_scan, total);
-  // convert s_h into inclusive suffix sums cum[b] = sum_{b' >= b} h[b']
-  {
-    u32 run = above;
-#pragma unroll
-    for (int q = 1; q <= per; ++q) {
-      run += s_h[hi - q];
-      s_h[hi - q] = run;
-    }
-  }
-  if (tid == 0) {
-    s_bT = 0xFFFFFFFFu;
-    s_exact = (K == total && K <= (u32)kListCap) ? 1u : 0u;  // K = ~0 if a region was truncated
-  }
-  __syncthreads();
-  // b_T = the largest bin with cum[b_T] >= c_target (cum is non-increasing in b)
-  for (int q = 1; q <= per; ++q) {
-    if (s_h[hi - q] >= sp.c_target) {
-      atomicMax((int*)&s_bT, hi - q);  // s_bT starts at -1 as int
-      break;
-    }
-  }
-  __syncthreads();
-  const int bT = (int)s_bT;
-  Plan* plan = &ctl->plan;
-  if (bT < 0 || sp.break_plan) {
-    if (tid == 0) {
-      plan->valid = 1;
-      plan->nbuckets = 1;
-      plan->t_guess = sp.break_plan ? 0x7FFFFFFFu : 0xFFFFFFFFu;
-      plan->lo[0] = plan->t_guess;
-      if (!sp.break_plan) plan->valid = 0;
-    }
-    return;
-  }
-  auto bin_of_rank = [&](u32 q) -> int {  // largest b with cum[b] >= q (cum[0] >= q)
-    int lo = 0, hi2 = kHistBins - 1;
-    while (lo < hi2) {
-      int mid = (lo + hi2 + 1) >> 1;
-      if (s_h[mid] >= q) lo = mid;
-      else hi2 = mid - 1;
-    }
-    return lo;
-  };
-  auto cum_above = [&](int b) -> u32 { return b + 1 < kHistBins ? s_h[b + 1] : 0u; };
-  // wanted ranks: [0] c_target, [1+j] (j+1)*bucket_samples for j < nb-1
-  u32 nb = (sp.c_target + sp.bucket_samples - 1) / sp.bucket_samples;
-  nb = std::max(1u, std::min(nb, (u32)kMaxBuckets));
-  const int ntarget = (int)nb;  // T_guess + nb-1 boundaries
-  // default: interpolation inside the bin (used where no exact key is found)
-  if (tid < ntarget) {
-    const u32 q = tid == 0 ? sp.c_target : (u32)tid * sp.bucket_samples;
-    const int b = bin_of_rank(q);
-    const u32 above_b = cum_above(b);
-    const u32 h = s_h[b] - above_b;  // >= q - above_b >= 1
-    const u32 f = q - above_b;
-    const u32 off = (u32)((((u64)f << kHistShift) + h - 1) / h);  // in [1, 2^18]
-    s_tkey[tid] = (((u32)b + 1u) << kHistShift) - off;
-  }
-  for (int i = tid; i < kHistBins; i += NT) s_cur[i] = 0;
-  for (int i = tid; i < kListCap; i += NT) s_grp[i] = kNoKey;
-  __syncthreads();
-  if (s_exact) {
-    // flag the bins that hold a wanted rank: 1 = small (rank by counting),
-    // 2 = large (second-level histogram)
-    if (tid < ntarget) {
-      const u32 q = tid == 0 ? sp.c_target : (u32)tid * sp.bucket_samples;
-      const int b = bin_of_rank(q);
-      atomicMax(&s_cur[b], s_h[b] - cum_above(b) <= (u32)kRankBinCap ? 1u : 2u);
-    }
-    {  // wave w copies regions w, w + 16, ...: every load issued before any use
-      constexpr int kPerWave = kSampleBlocks / (NT / kWave);
-      constexpr int kRows = (kListPerBlock + kWave - 1) / kWave;
-      u32 v[kPerWave][kRows];
-#pragma unroll
-      for (int r = 0; r < kPerWave; ++r) {
-        const int b2 = w + r * (NT / kWave);
-        const u32 c = (b2 + 1 < kSampleBlocks ? s_cnt[b2 + 1] : K) - s_cnt[b2];
-#pragma unroll
-        for (int j = 0; j < kRows; ++j) {
-          const u32 i = (u32)(lane + j * kWave);
-          v[r][j] = i < c ? ld_agent(&slist[b2 * kListPerBlock + i]) : kNoKey;
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < kPerWave; ++r) {
-        const int b2 = w + r * (NT / kWave);
-        const u32 o = s_cnt[b2];
-        const u32 c = (b2 + 1 < kSampleBlocks ? s_cnt[b2 + 1] : K) - o;
-#pragma unroll
-        for (int j = 0; j < kRows; ++j) {
-          const u32 i = (u32)(lane + j * kWave);
-          if (i < c) s_keys[o + i] = v[r][j];
-        }
-      }
-    }
-    __syncthreads();
-    // large flagged bins, listed once each (few: the pile-ups).  Targets in
-    // rank order are q_1 < ... < q_{nb-1} <= q_0 = c_target, so their bins do
-    // not increase; a target lists its bin when the previous one's differs.
-    __shared__ u32 s_fat[kMaxBuckets + 1];
-    __shared__ u32 s_nfat;
-    if (tid == 0) s_nfat = 0;
-    __syncthreads();
-    if (tid < ntarget) {
-      const int order = tid == 0 ? ntarget - 1 : tid - 1;  // position in rank order
-      const u32 q = tid == 0 ? sp.c_target : (u32)tid * sp.bucket_samples;
-      const int b = bin_of_rank(q);
-      int bprev = -1;
-      if (order > 0) {
-        const u32 qp = (u32)order * sp.bucket_samples;  // the target just before in rank order
-        bprev = bin_of_rank(qp);
-      }
-      if (s_cur[b] == 2u && b != bprev) s_fat[atomicAdd(&s_nfat, 1u)] = (u32)b;
-    }
-    __syncthreads();  // s_cur is rewritten below
-    // small flagged bins: group their keys (group of bin b starts at cum[b+1])
-    for (int i = tid; i < kHistBins; i += NT) s_cur[i] = s_cur[i] == 1u ? (cum_above(i) | 0x80000000u) : 0u;
-    __syncthreads();
-    for (u32 i = tid; i < K; i += NT) {
-      const u32 key = s_keys[i];
-      const u32 b = key >> kHistShift;
-      if (s_cur[b] & 0x80000000u) {
-        const u32 pos = (atomicAdd(&s_cur[b], 1u) & 0x7FFFFFFFu);
-        if (pos < (u32)kListCap) s_grp[pos] = key;
-      }
-    }
-    __syncthreads();
-    // rank each grouped key inside its bin (ties broken by position); a key of
-    // global rank q-1 (0-based, from the top) is the wanted key for rank q
-    for (u32 i = tid; i < K; i += NT) {
-      const u32 x = s_grp[i];
-      if (x == kNoKey) continue;
-      const int b = (int)(x >> kHistShift);
-      const u32 g0 = cum_above(b), g1 = s_h[b];
-      u32 r = 0;
-      for (u32 t = g0; t < g1; ++t) {
-        const u32 y = s_grp[t];
-        r += (y > x) || (y == x && t < i);
-      }
-      const u32 rank1 = g0 + r + 1;  // 1-based rank of x among all samples
-      if (rank1 == sp.c_target) s_tkey[0] = x;
-      if (rank1 % sp.bucket_samples == 0) {
-        const u32 jj = rank1 / sp.bucket_samples;
-        if (jj >= 1 && jj < nb) s_tkey[jj] = x;
-      }
-    }
-    __syncthreads();
-    // large bins: histogram of key bits [17:5] (8192 sub-bins of 32 keys) over
-    // the bin's keys; a wanted key is the lower edge of the sub-bin where the
-    // count from the top reaches its rank (never above the exact key)
-    constexpr int kSubShift = 5;
-    constexpr int kSubN = 1 << (kHistShift - kSubShift);  // 8192
-    u32* sub = s_grp;  // free again
-    for (u32 f = 0; f < s_nfat; ++f) {
-      const u32 fb = s_fat[f];
-      for (int i = tid; i < kSubN; i += NT) sub[i] = 0;
-      __syncthreads();
-      for (u32 i = tid; i < K; i += NT) {
-        const u32 key = s_keys[i];
-        if ((key >> kHistShift) == fb) atomicAdd(&sub[(key >> kSubShift) & (kSubN - 1)], 1u);
-      }
-      __syncthreads();
-      const int shi = kSubN - per * tid;  // thread t owns sub-bins [shi - per, shi), top first
-      u32 sown = 0;
-#pragma unroll
-      for (int q2 = 1; q2 <= per; ++q2) sown += sub[shi - q2];
-      u32 stot;
-      const u32 sabove = block_exclusive_sum<NT>(sown, s_scan, stot);
-      {
-        u32 run = sabove;
-#pragma unroll
-        for (int q2 = 1; q2 <= per; ++q2) {
-          run += sub[shi - q2];
-          sub[shi - q2] = run;  // suffix sums inside the bin
-        }
-      }
-      __syncthreads();
-      if (tid < ntarget) {
-        const u32 q = tid == 0 ? sp.c_target : (u32)tid * sp.bucket_samples;
-        if ((u32)bin_of_rank(q) == fb) {
-          const u32 want = q - cum_above((int)fb);  // rank inside the bin, 1-based
-          int lo = 0, hi2 = kSubN - 1;              // largest sub-bin with suffix >= want
-          while (lo < hi2) {
-            int mid = (lo + hi2 + 1) >> 1;
-            if (sub[mid] >= want) lo = mid;
-            else hi2 = mid - 1;
-          }
-          s_tkey[tid] = (fb << kHistShift) | ((u32)lo << kSubShift);
-        }
-      }
-      __syncthreads();
-    }
-  }
-  if (tid == 0) {
-    const u32 tg = s_tkey[0];
-    u32 prev = 0xFFFFFFFFu;
-    for (int j = 0; j + 1 < (int)nb; ++j) {
-      u32 v = std::max(s_tkey[1 + j], tg);
-      v = std::min(v, prev);
-      plan->lo[j] = v;
-      prev = v;
-    }
-    plan->lo[nb - 1] = tg;
-    plan->t_guess = tg;
-    plan->nbuckets = nb;
-    plan->valid = 1;
-  }
+  return true;
 }
 
-// --------------------------------------------------------- k_ef_main ----
-struct MainArgs {
-  const float* grad;
-  float* residual;
-  int64_t n;
-  int64_t head;  // scalar elements before the 16-byte aligned part
-  int64_t nv;    // float4 vectors in the aligned part (0 = scalar mode)
-  const Plan* plan;
-  unsigned char* cnt;  // [G][kMaxBuckets]
-  Pair* slots;         // [G][kMaxBuckets][kSlot]
-  u32* zero_ptr;       // general-path state cleared by workgroup 0
-  int zero_words;
-  u32* err;            // device error word, cleared by workgroup 0
-};
-
-template <bool SPEC>
-__device__ __forceinline__ void main_emit(int64_t idx, u32 bits, u32 tg, int nb, const u32* s_lo,
-                                          u32* s_cnt, Pair* slots) {
-  if (!SPEC) return;
-  u32 key = key_of_bits(bits);
-  if (key < tg) return;
-  int lo = 0, hi = nb;  // bucket = #{i < nb : lo[i] > key}
-  while (lo < hi) {
-    int mid = (lo + hi) >> 1;
-    if (s_lo[mid] > key) lo = mid + 1;
-    else hi = mid;
-  }
-  int j = lo < nb ? lo : nb - 1;
-  u32 pos = atomicAdd(&s_cnt[j], 1u);
-  if (pos < (u32)kSlot) slots[((int64_t)blockIdx.x * kMaxBuckets + j) * kSlot + pos] = Pair{(int32_t)idx, bits};
-}
-
-template <bool SPEC, bool VEC>
-__global__ __launch_bounds__(kMainThreads) void k_ef_main(MainArgs a) {
-  __shared__ u32 s_lo[kMaxBuckets];
-  __shared__ u32 s_cnt[kMaxBuckets];
-  __shared__ u32 s_meta[2];
-  const int tid = threadIdx.x;
-  u32 tg = 0xFFFFFFFFu;
-  int nb = 1;
-  if (SPEC) {
-    if (tid < kMaxBuckets) {
-      s_cnt[tid] = 0;
-      s_lo[tid] = a.plan->lo[tid];
+// Thread 0 only.  Bounded wait for a nonzero flag; 0 on timeout.
+__device__ __forceinline__ u32 flag_wait(const Counter* flag, u32* err) {
+  u32 spins = 0;
+  for (;;) {
+    const u64 v = ld_agent64(&flag->v);
+    if (v != 0) return (u32)v;
+    __builtin_amdgcn_s_sleep(2);
+    if (++spins > kSpinLimit) {
+      atomicOr(err, kErrBarrierTimeout);
+      return 0;
     }
-    if (tid == 0) {
-      u32 v = a.plan->valid, b = a.plan->nbuckets;
-      bool ok = (v == 1) && b >= 1 && b <= (u32)kMaxBuckets;
-      s_meta[0] = ok ? a.plan->t_guess : 0xFFFFFFFFu;
-      s_meta[1] = ok ? b : 1u;
-    }
-    __syncthreads();
-    tg = s_meta[0];
-    nb = (int)s_meta[1];
-  }
-  if (blockIdx.x == 0) {
-    for (int i = tid; i < a.zero_words; i += kMainThreads) a.zero_ptr[i] = 0u;
-    if (tid == 0) *a.err = 0u;
-  }
-
-  const float* __restrict__ g = a.grad;
-  float* __restrict__ r = a.residual;
-  if (VEC) {
-    // scalar head (workgroup 0), then this workgroup's contiguous vector range
-    if (blockIdx.x == 0 && tid < a.head) {
-      float acc = r[tid] + g[tid];
-      r[tid] = acc;
-      main_emit<SPEC>(tid, __float_as_uint(acc), tg, nb, s_lo, s_cnt, a.slots);
-    }
-    const v4f* __restrict__ gv = (const v4f*)(g + a.head);
-    v4f* __restrict__ rv = (v4f*)(r + a.head);
-    // tiles of kMainThreads * kMainU vectors, dealt round-robin to the
-    // workgroups so that the whole grid sweeps the arrays front to back
-    constexpr int64_t tile = (int64_t)kMainThreads * kMainU;
-    const int64_t ve = a.nv;
-    for (int64_t base = (int64_t)blockIdx.x * tile; base < ve; base += (int64_t)gridDim.x * tile) {
-      v4f gg[kMainU], rr[kMainU];
-#pragma unroll
-      for (int u = 0; u < kMainU; ++u) {
-        int64_t i = base + u * kMainThreads + tid;
-        if (i < ve) {
-          gg[u] = __builtin_nontemporal_load(gv + i);
-          rr[u] = __builtin_nontemporal_load(rv + i);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kMainU; ++u) {
-        int64_t i = base + u * kMainThreads + tid;
-        if (i < ve) {
-          v4f acc = rr[u] + gg[u];
-          __builtin_nontemporal_store(acc, rv + i);
-          if (SPEC) {
-            u32 b0 = __float_as_uint(acc.x), b1 = __float_as_uint(acc.y);
-            u32 b2 = __float_as_uint(acc.z), b3 = __float_as_uint(acc.w);
-            u32 kmax = std::max(std::max(key_of_bits(b0), key_of_bits(b1)),
-                                std::max(key_of_bits(b2), key_of_bits(b3)));
-            if (kmax >= tg) {
-              int64_t e = a.head + 4 * i;
-              main_emit<SPEC>(e + 0, b0, tg, nb, s_lo, s_cnt, a.slots);
-              main_emit<SPEC>(e + 1, b1, tg, nb, s_lo, s_cnt, a.slots);
-              main_emit<SPEC>(e + 2, b2, tg, nb, s_lo, s_cnt, a.slots);
-              main_emit<SPEC>(e + 3, b3, tg, nb, s_lo, s_cnt, a.slots);
-            }
-          }
-        }
-      }
-    }
-    // scalar tail (last workgroup)
-    if (blockIdx.x == gridDim.x - 1) {
-      for (int64_t i = a.head + 4 * a.nv + tid; i < a.n; i += kMainThreads) {
-        float acc = r[i] + g[i];
-        r[i] = acc;
-        main_emit<SPEC>(i, __float_as_uint(acc), tg, nb, s_lo, s_cnt, a.slots);
-      }
-    }
-  } else {
-    for (int64_t i = (int64_t)blockIdx.x * kMainThreads + tid; i < a.n; i += (int64_t)gridDim.x * kMainThreads) {
-      float acc = r[i] + g[i];
-      r[i] = acc;
-      main_emit<SPEC>(i, __float_as_uint(acc), tg, nb, s_lo, s_cnt, a.slots);
-    }
-  }
-  if (SPEC) {
-    __syncthreads();
-    if (tid < kMaxBuckets)
-      a.cnt[(int64_t)blockIdx.x * kMaxBuckets + tid] = (unsigned char)std::min(s_cnt[tid], 255u);
   }
 }
 
@@ -680,10 +229,11 @@ __device__ __forceinline__ u32 block_sum(u32 v, u32* lds) {
   return total;
 }
 
-// The exact general path.  Every workgroup of the grid must be resident at
-// once (grid barriers); NT is the workgroup size.
+// The exact general path, run by workgroups 0 .. a.bar.nwg-1, which must all
+// be resident at once (grid barriers); NT is the workgroup size.  acc is read
+// from residual, which every participant must be able to see.
 template <int NT>
-__device__ void general_path(const GenArgs& a) {
+__device__ __forceinline__ void general_path(const GenArgs& a) {
   constexpr int NW = NT / kWave;
   __shared__ u32 s_hist[2048];
   __shared__ u32 s_wcnt[NW][256];
@@ -692,7 +242,7 @@ __device__ void general_path(const GenArgs& a) {
   __shared__ u32 s_scan[NW + 1];
   __shared__ u32 s_found[4];
   const int tid = threadIdx.x;
-  const int G = gridDim.x;
+  const int G = (int)a.bar.nwg;
   const int b = blockIdx.x;
   const int64_t per = (a.n + G - 1) / G;
   const int64_t cb = std::min<int64_t>(a.n, (int64_t)b * per);
@@ -906,231 +456,1037 @@ __device__ void general_path(const GenArgs& a) {
   }
 }
 
-__global__ __launch_bounds__(kGenThreads) void k_general(GenArgs a) { general_path<kGenThreads>(a); }
 
-// ---------------------------------------------------------- k_finish ----
-struct FinishArgs {
-  const Plan* plan;
-  const unsigned char* cnt;
-  const Pair* slots;
-  int G1;
-  int64_t n;
-  int64_t k;
-  int32_t* out_idx;
-  float* out_val;
+// ---------------------------------------------------------- k_acc_pass ----
+// acc = residual + grad written back to residual; the general path then runs
+// on it.  Workgroup 0 clears the general-path state and the error word.
+struct AccArgs {
+  const float* grad;
   float* residual;
-  TopkCtl* ctl;
-  u32* shist;
-  GenArgs gen;  // fallback: the exact general path on this kernel's grid
+  int64_t n;
+  int64_t head;  // scalar elements before the 16-byte aligned part
+  int64_t nv;    // float4 vectors in the aligned part
+  u32* zero_ptr;
+  int zero_words;
+  u32* err;
 };
 
-__global__ __launch_bounds__(kFinishThreads) void k_finish(FinishArgs a) {
-  constexpr int NT = kFinishThreads;
-  constexpr int NW = NT / kWave;
-  __shared__ Pair s_a[kFinishCap];         // 32 KB: the bucket as gathered
-  __shared__ Pair s_b[kFinishCap];         // 32 KB: grouped by key sub-range
-  __shared__ u32 s_sub_cnt[kSubBins];      // 8 KB
-  __shared__ u32 s_sub_off[kSubBins];      // 8 KB
-  __shared__ u32 s_scan[NW + 1];
-  __shared__ u32 s_rows[kMaxMainBlocks];   // (row << 8) | count for this bucket
-  __shared__ u32 s_part[NW][kMaxBuckets];  // per-wave bucket totals
+template <bool VEC>
+__global__ __launch_bounds__(kAccThreads) void k_acc_pass(AccArgs a) {
+  const int tid = threadIdx.x;
+  if (blockIdx.x == 0) {
+    for (int i = tid; i < a.zero_words; i += kAccThreads) a.zero_ptr[i] = 0u;
+    if (tid == 0) *a.err = 0u;
+  }
+  const float* __restrict__ g = a.grad;
+  float* __restrict__ r = a.residual;
+  if (VEC) {
+    if (blockIdx.x == 0 && tid < a.head) r[tid] = r[tid] + g[tid];
+    const v4f* __restrict__ gv = (const v4f*)(g + a.head);
+    v4f* __restrict__ rv = (v4f*)(r + a.head);
+    constexpr int64_t tile = (int64_t)kAccThreads * kAccU;
+    for (int64_t base = (int64_t)blockIdx.x * tile; base < a.nv; base += (int64_t)gridDim.x * tile) {
+      v4f gg[kAccU], rr[kAccU];
+#pragma unroll
+      for (int u = 0; u < kAccU; ++u) {
+        const int64_t i = base + u * kAccThreads + tid;
+        if (i < a.nv) {
+          gg[u] = __builtin_nontemporal_load(gv + i);
+          rr[u] = __builtin_nontemporal_load(rv + i);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kAccU; ++u) {
+        const int64_t i = base + u * kAccThreads + tid;
+        if (i < a.nv) __builtin_nontemporal_store(rr[u] + gg[u], rv + i);
+      }
+    }
+    if (blockIdx.x == gridDim.x - 1)
+      for (int64_t i = a.head + 4 * a.nv + tid; i < a.n; i += kAccThreads) r[i] = r[i] + g[i];
+  } else {
+    for (int64_t i = (int64_t)blockIdx.x * kAccThreads + tid; i < a.n; i += (int64_t)gridDim.x * kAccThreads)
+      r[i] = r[i] + g[i];
+  }
+}
+
+__global__ __launch_bounds__(kGenThreads) void k_general(GenArgs a) { general_path<kGenThreads>(a); }
+
+// ------------------------------------------------------------- k_step ----
+struct StepArgs {
+  const float* grad;
+  float* residual;
+  int64_t n, k;
+  int64_t head, nv;  // aligned mode: head scalars, then nv float4 (from residual + head)
+  int vec;           // 0: scalar mode (grad and residual differ in 16-byte alignment)
+  int32_t* out_idx;
+  float* out_val;
+  int64_t chunks, stride;        // sample chunk c covers [c * stride, c * stride + 64)
+  u32 c_target, bucket_samples;  // plan: sample ranks of T_guess and of the bucket edges
+  u32 pub_want;                  // sample keys each workgroup publishes at least
+  u32 loc_q16;                   // T_loc: rank fraction of the local sample, in 1/65536
+  u32 break_plan;                // test hook: publish a plan that cannot hold
+  StepCtl* ctl;
+  u32* pub;      // [kMaxStepBlocks][kPubCap] keys, then [kMaxStepBlocks] count | floor << 16
+  u32* rcnt;     // [kMaxStepBlocks][kMaxBuckets / 2] bucket counts, two u16 per word
+  Pair* region;  // [kMaxStepBlocks][kRegionCap] published candidates, by bucket
+  u32* gstate;   // the general path's state, cleared by workgroup 0
+  int gstate_words;
+  GenArgs gen;   // the exact path on this grid
+};
+
+__device__ __forceinline__ u64 pack_pair(const Pair& p) { return (u64)(u32)p.idx | ((u64)p.bits << 32); }
+__device__ __forceinline__ Pair unpack_pair(u64 v) { return Pair{(int32_t)(u32)v, (u32)(v >> 32)}; }
+
+// bucket of a candidate key: #{j < nb : lo[j] > key}, at most nb - 1
+__device__ __forceinline__ int bucket_of(u32 key, const u32* lo, int nb) {
+  int l = 0, h = nb;
+  while (l < h) {
+    const int mid = (l + h) >> 1;
+    if (lo[mid] > key) l = mid + 1;
+    else h = mid;
+  }
+  return l < nb ? l : nb - 1;
+}
+
+// Keeps (idx, bits) in the workgroup's list (its acc is in residual
+// already); a full list is marked incomplete.
+__device__ __forceinline__ void list_keep(Pair* s_list, u32* s_nlist, u32* s_ovf, int64_t idx, u32 bits) {
+  const u32 pos = atomicAdd(s_nlist, 1u);
+  if (pos < (u32)kListCap) s_list[pos] = Pair{(int32_t)idx, bits};
+  else *s_ovf = 1u;
+}
+
+// Publishes a plan (all threads of workgroup 0): words with returning device
+// atomics, then the flag once they are all done.
+__device__ __forceinline__ void publish_plan(StepCtl* ctl, u32 valid, u32 tg, u32 nb, const u32* lo, u32* s_scan) {
+  const int tid = threadIdx.x;
+  u32 sink = 0;
+  if (tid < kMaxBuckets) sink += xchg_agent(&ctl->plan.lo[tid], lo[tid]);
+  if (tid == kMaxBuckets) sink += xchg_agent(&ctl->plan.t_guess, tg);
+  if (tid == kMaxBuckets + 1) sink += xchg_agent(&ctl->plan.nbuckets, nb);
+  if (tid == kMaxBuckets + 2) sink += xchg_agent(&ctl->plan.valid, valid);
+  if (sink == 0x12345678u) s_scan[kStepWaves] = sink;  // keeps the returned values live
+  __syncthreads();
+  if (tid == 0) xchg_agent64(&ctl->plan_flag.v, 1u);
+}
+
+// Workgroup 0: the published sample keys -> plan.
+//   T_guess = the c_target-th largest sample key; bucket edge j = the
+//   (j+1)*bucket_samples-th largest.  The keys are grouped by 12-bit bin
+//   (offsets from the suffix sums of their histogram); a bin that holds a
+//   wanted rank is ranked by counting when small, or by a histogram of key
+//   bits [18:6] when large (its lower sub-bin edge, never above the key).
+//   The ranks are exact when no workgroup truncated its keys and the
+//   T_guess bin lies at or above every workgroup's floor bin (all bins from
+//   the highest floor up were published in full); otherwise the plan is
+//   still a valid guess.
+__device__ __forceinline__ void step_plan(const StepArgs& a, u32* s_raw, u32* s_scan) {
+  constexpr int NT = kStepThreads;
+  constexpr int NW = kStepWaves;
+  constexpr int per = kHistBins / NT;  // 4 bins per thread, top first
+  constexpr u32 kNoKey = 0xFFFFFFFFu;
+  u32* s_h = s_raw;                     // [kHistBins] histogram, then suffix sums
+  u32* s_cur = s_raw + kHistBins;       // [kHistBins] bin flags, then group cursors
+  u32* s_keys = s_raw + 2 * kHistBins;  // [kPlanCap] the published keys
+  u32* s_grp = s_keys + kPlanCap;       // [kPlanCap] grouped by bin, then a sub-histogram
+  __shared__ u32 s_off[kMaxStepBlocks + 1];
+  __shared__ u32 s_tkey[kMaxBuckets + 1];  // [0] T_guess, [1+j] edge j
   __shared__ u32 s_lo[kMaxBuckets];
-  __shared__ u32 s_nrows, s_ovf, s_pos, s_kmin, s_kmax;
-  __shared__ u32 s_ok;
+  __shared__ u32 s_fat[kMaxBuckets + 1];
+  __shared__ u32 s_nfat, s_trunc, s_maxfloor, s_bT, s_ok;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int w = tid / kWave;
+  const int G = gridDim.x;
+  StepCtl* ctl = a.ctl;
+  if (tid == 0) {
+    s_ok = phase_wait(&ctl->samp_all, G, &ctl->err) ? 1u : 0u;
+    s_trunc = 0;
+    s_maxfloor = 0;
+    s_bT = 0xFFFFFFFFu;
+    s_nfat = 0;
+  }
+  for (int i = tid; i < kHistBins; i += NT) {
+    s_h[i] = 0;
+    s_cur[i] = 0;
+  }
+  for (int i = tid; i < kPlanCap; i += NT) s_grp[i] = kNoKey;
+  __syncthreads();
+  u32 c = 0;
+  if (tid < G) {
+    const u32 v = ld_agent(&a.pub[kPlanCap + tid]);
+    c = v & 0xFFFFu;
+    if (c > (u32)kPubCap) atomicOr(&s_trunc, 1u);
+    atomicMax(&s_maxfloor, v >> 16);
+  }
+  u32 K;
+  const u32 off = block_exclusive_sum<NT>(std::min(c, (u32)kPubCap), s_scan, K);
+  if (tid < G) s_off[tid] = off;
+  if (tid == 0) s_off[G] = K;
+  __syncthreads();
+  {  // wave w loads workgroups w, w + 16, ...: all its loads in flight at once
+    constexpr int kPerWave = kMaxStepBlocks / NW;
+    u32 v[kPerWave];
+#pragma unroll
+    for (int r = 0; r < kPerWave; ++r) {
+      const int wg = w + r * NW;
+      const u32 cnt = wg < G ? s_off[wg + 1] - s_off[wg] : 0u;
+      v[r] = (u32)lane < cnt ? ld_agent(&a.pub[wg * kPubCap + lane]) : kNoKey;
+    }
+#pragma unroll
+    for (int r = 0; r < kPerWave; ++r) {
+      const int wg = w + r * NW;
+      const u32 cnt = wg < G ? s_off[wg + 1] - s_off[wg] : 0u;
+      if ((u32)lane < cnt) {
+        s_keys[s_off[wg] + lane] = v[r];
+        atomicAdd(&s_h[v[r] >> kHistShift], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  const int hi = kHistBins - per * tid;  // thread t owns bins [hi - per, hi)
+  {
+    u32 own = 0;
+#pragma unroll
+    for (int q = 1; q <= per; ++q) own += s_h[hi - q];
+    u32 total;
+    u32 run = block_exclusive_sum<NT>(own, s_scan, total);
+#pragma unroll
+    for (int q = 1; q <= per; ++q) {  // inclusive suffix sums cum[b] = sum_{b' >= b} h[b']
+      run += s_h[hi - q];
+      s_h[hi - q] = run;
+    }
+  }
+  __syncthreads();
+  for (int q = 1; q <= per; ++q) {  // b_T = the largest bin with cum[b_T] >= c_target
+    if (s_h[hi - q] >= a.c_target) {
+      atomicMax((int*)&s_bT, hi - q);  // starts at -1 as int
+      break;
+    }
+  }
+  __syncthreads();
+  const int bT = (int)s_bT;
+  u32 nb = (a.c_target + a.bucket_samples - 1) / a.bucket_samples;
+  nb = std::max(1u, std::min(nb, (u32)kMaxBuckets));
+  if (bT < 0 || !s_ok || a.break_plan) {
+    // no plan (T_guess above every key), or the test hook's plan: a
+    // threshold no finite key reaches
+    const u32 tg = a.break_plan ? 0x7FFFFFFFu : 0xFFFFFFFFu;
+    if (tid < kMaxBuckets) s_lo[tid] = tid == 0 ? tg : 0u;
+    __syncthreads();
+    publish_plan(ctl, a.break_plan ? 1u : 0u, tg, 1u, s_lo, s_scan);
+    return;
+  }
+  auto bin_of_rank = [&](u32 q) -> int {  // largest b with cum[b] >= q
+    int lo = 0, hi2 = kHistBins - 1;
+    while (lo < hi2) {
+      const int mid = (lo + hi2 + 1) >> 1;
+      if (s_h[mid] >= q) lo = mid;
+      else hi2 = mid - 1;
+    }
+    return lo;
+  };
+  auto cum_above = [&](int b) -> u32 { return b + 1 < kHistBins ? s_h[b + 1] : 0u; };
+  const int ntarget = (int)nb;  // wanted ranks: [0] c_target, [j] j * bucket_samples for 1 <= j < nb
+  auto rank_of = [&](int t) -> u32 { return t == 0 ? a.c_target : (u32)t * a.bucket_samples; };
+  if (tid < ntarget) {  // default: interpolation inside the bin
+    const u32 q = rank_of(tid);
+    const int b = bin_of_rank(q);
+    const u32 above_b = cum_above(b);
+    const u32 h = s_h[b] - above_b;  // >= q - above_b >= 1
+    const u32 f = q - above_b;
+    const u32 offk = (u32)((((u64)f << kHistShift) + h - 1) / h);  // in [1, 2^19]
+    s_tkey[tid] = (((u32)b + 1u) << kHistShift) - offk;
+  }
+  __syncthreads();
+  const bool exact = !s_trunc && bT >= (int)s_maxfloor;
+  if (exact) {
+    // flag the bins that hold a wanted rank: 1 = small, 2 = large
+    if (tid < ntarget) {
+      const int b = bin_of_rank(rank_of(tid));
+      atomicMax(&s_cur[b], s_h[b] - cum_above(b) <= (u32)kRankBinCap ? 1u : 2u);
+    }
+    __syncthreads();
+    // large flagged bins, listed once each.  In rank order the targets are
+    // t = 1 .. nb-1, then t = 0 (c_target is the largest rank); their bins do
+    // not increase, so a target lists its bin when its predecessor's differs.
+    if (tid < ntarget) {
+      const int order = tid == 0 ? ntarget - 1 : tid - 1;
+      const int b = bin_of_rank(rank_of(tid));
+      const int bprev = order > 0 ? bin_of_rank((u32)order * a.bucket_samples) : -1;
+      if (s_cur[b] == 2u && b != bprev) s_fat[atomicAdd(&s_nfat, 1u)] = (u32)b;
+    }
+    __syncthreads();  // s_cur is rewritten below
+    // small flagged bins: group their keys (the group of bin b starts at cum[b+1])
+    for (int i = tid; i < kHistBins; i += NT) s_cur[i] = s_cur[i] == 1u ? (cum_above(i) | 0x80000000u) : 0u;
+    __syncthreads();
+    for (u32 i = tid; i < K; i += NT) {
+      const u32 key = s_keys[i];
+      const u32 b = key >> kHistShift;
+      if (s_cur[b] & 0x80000000u) {
+        const u32 pos = atomicAdd(&s_cur[b], 1u) & 0x7FFFFFFFu;
+        if (pos < (u32)kPlanCap) s_grp[pos] = key;
+      }
+    }
+    __syncthreads();
+    // rank each grouped key inside its bin (ties broken by position); the key
+    // of 1-based rank q is the wanted key for rank q
+    for (u32 i = tid; i < K; i += NT) {
+      const u32 x = s_grp[i];
+      if (x == kNoKey) continue;
+      const int b = (int)(x >> kHistShift);
+      const u32 g0 = cum_above(b), g1 = s_h[b];
+      u32 r = 0;
+      for (u32 t = g0; t < g1; ++t) {
+        const u32 y = s_grp[t];
+        r += (y > x) || (y == x && t < i);
+      }
+      const u32 rank1 = g0 + r + 1;
+      if (rank1 == a.c_target) s_tkey[0] = x;
+      if (rank1 % a.bucket_samples == 0) {
+        const u32 jj = rank1 / a.bucket_samples;
+        if (jj >= 1 && jj < nb) s_tkey[jj] = x;
+      }
+    }
+    __syncthreads();
+    // large bins: histogram of key bits [18:6] (8192 sub-bins of 64 keys)
+    constexpr int kSubShift = 6;
+    constexpr int kSubN = 1 << (kHistShift - kSubShift);
+    constexpr int per2 = kSubN / NT;
+    u32* sub = s_grp;  // free again
+    for (u32 fi = 0; fi < s_nfat; ++fi) {
+      const u32 fb = s_fat[fi];
+      for (int i = tid; i < kSubN; i += NT) sub[i] = 0;
+      __syncthreads();
+      for (u32 i = tid; i < K; i += NT) {
+        const u32 key = s_keys[i];
+        if ((key >> kHistShift) == fb) atomicAdd(&sub[(key >> kSubShift) & (kSubN - 1)], 1u);
+      }
+      __syncthreads();
+      const int shi = kSubN - per2 * tid;
+      u32 sown = 0;
+#pragma unroll
+      for (int q2 = 1; q2 <= per2; ++q2) sown += sub[shi - q2];
+      u32 stot;
+      u32 srun = block_exclusive_sum<NT>(sown, s_scan, stot);
+#pragma unroll
+      for (int q2 = 1; q2 <= per2; ++q2) {
+        srun += sub[shi - q2];
+        sub[shi - q2] = srun;
+      }
+      __syncthreads();
+      if (tid < ntarget) {
+        const u32 q = rank_of(tid);
+        if ((u32)bin_of_rank(q) == fb) {
+          const u32 want = q - cum_above((int)fb);  // 1-based rank inside the bin
+          int lo = 0, hi2 = kSubN - 1;              // largest sub-bin with suffix >= want
+          while (lo < hi2) {
+            const int mid = (lo + hi2 + 1) >> 1;
+            if (sub[mid] >= want) lo = mid;
+            else hi2 = mid - 1;
+          }
+          s_tkey[tid] = (fb << kHistShift) | ((u32)lo << kSubShift);
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (tid == 0) {  // monotone edges, each at least T_guess
+    const u32 tg = s_tkey[0];
+    u32 prev = 0xFFFFFFFFu;
+    for (int j = 0; j < kMaxBuckets; ++j) {
+      u32 v = 0;
+      if (j + 1 < (int)nb) {
+        v = std::min(std::max(s_tkey[1 + j], tg), prev);
+        prev = v;
+      } else if (j + 1 == (int)nb) {
+        v = tg;
+      }
+      s_lo[j] = v;
+    }
+  }
+  __syncthreads();
+  publish_plan(ctl, 1u, s_lo[nb - 1], nb, s_lo, s_scan);
+}
+
+// Finisher f (workgroups 0..63), once every workgroup has published: the
+// verdict, then bucket f.  Returns false when the plan did not hold.
+__device__ __forceinline__ bool step_finish(const StepArgs& a, u32* s_raw, u32* s_scan) {
+  constexpr int NT = kStepThreads;
+  constexpr int NW = kStepWaves;
+  Pair* s_a = (Pair*)s_raw;                     // [kFinishCap] the bucket as gathered
+  Pair* s_b = (Pair*)(s_raw + 2 * kFinishCap);  // [kFinishCap] grouped by key sub-range
+  u32* s_sub_cnt = s_raw + 4 * kFinishCap;      // [kSubBins]
+  u32* s_sub_off = s_sub_cnt + kSubBins;        // [kSubBins]
+  u32* s_rows = s_sub_off + kSubBins;           // [2][kMaxStepBlocks]: row, offset | count << 16
+  u32* s_part = s_rows + 2 * kMaxStepBlocks;    // [NW][kMaxBuckets] partial bucket totals
+  static_assert(4 * kFinishCap + 2 * kSubBins + 2 * kMaxStepBlocks + NW * kMaxBuckets <= kRawWords, "LDS");
+  __shared__ u32 s_plo[kMaxBuckets];
+  __shared__ u32 s_phdr[3];
+  __shared__ u32 s_nrows, s_kmin, s_kmax, s_ok, s_wait, s_seen;
+  __shared__ u32 s_rpre[kMaxStepBlocks + 1];
   __shared__ int64_t s_start, s_mytot;
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int w = tid / kWave;
-  const int j = blockIdx.x;
-  if (tid < kMaxBuckets) s_lo[tid] = a.plan->lo[tid];
+  const int f = blockIdx.x;
+  const int G = gridDim.x;
+  StepCtl* ctl = a.ctl;
+  __syncthreads();  // s_raw changes role
+  // The plan is final before any workgroup publishes (every streaming
+  // workgroup waited for it), so it is read while waiting for the others.
+  if (tid < kMaxBuckets) s_plo[tid] = ld_agent(&ctl->plan.lo[tid]);
+  if (tid == kMaxBuckets) s_phdr[0] = ld_agent(&ctl->plan.t_guess);
+  if (tid == kMaxBuckets + 1) s_phdr[1] = ld_agent(&ctl->plan.nbuckets);
+  if (tid == kMaxBuckets + 2) s_phdr[2] = ld_agent(&ctl->plan.valid);
   if (tid == 0) {
+    s_wait = phase_wait(&ctl->main_all, G, &ctl->err) ? 1u : 0u;
     s_nrows = 0;
-    s_ovf = 0;
-    s_pos = 0;
     s_kmin = 0xFFFFFFFFu;
     s_kmax = 0;
   }
-  // Slot counts: G1 rows of 64 bytes (one per bucket), read as 16 words per
-  // row.  Thread t always sees word q = t % 16 of a row (buckets 4q .. 4q+3)
-  // and adds the four byte counts as two pairs of 16-bit lanes.
-  const u32* cw = (const u32*)a.cnt;
-  const int q = tid & 15;
-  constexpr int kWordsPerThread = kMaxMainBlocks * kMaxBuckets / 4 / NT;
-  const int nwords = a.G1 * (kMaxBuckets / 4);
-  u32 xw[kWordsPerThread];
+  __syncthreads();
+  // Bucket counts: G rows of 32 words (two u16 counts each; row 0, the
+  // planner, publishes nothing), read coalesced into an LDS matrix (it lives
+  // where the sorted bucket goes later).  Then thread (bucket j, part p) adds
+  // rows p, p + 16, ... of column j, and thread r (one per row) finds where
+  // row r's entries of bucket f start and how many there are.
+  constexpr int kWords = kMaxBuckets / 2;
+  constexpr int kIters = kMaxStepBlocks * kWords / NT;
+  u32* s_cm = (u32*)s_b;  // [kMaxStepBlocks][kWords]
+  static_assert(kMaxStepBlocks * kWords <= 2 * kFinishCap, "count matrix fits where s_b goes");
+  const int nwords = G * kWords;
+  {
+    u32 xw[kIters];
 #pragma unroll
-  for (int i = 0; i < kWordsPerThread; ++i) {  // all loads in flight at once
-    const int wd = tid + i * NT;
-    xw[i] = wd < nwords ? cw[wd] : 0u;
+    for (int it = 0; it < kIters; ++it) {
+      const int wd = tid + it * NT;
+      xw[it] = (wd >= kWords && wd < nwords) ? ld_agent(&a.rcnt[wd]) : 0u;
+    }
+    if (tid == 0) s_seen = ld_agent((const u32*)&ctl->bad.v);
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) s_cm[tid + it * NT] = xw[it];
   }
   __syncthreads();
-  u32 even = 0, odd = 0, ovf = 0;
-  const bool mine = q == (j >> 2);
-  const int myb = j & 3;
-#pragma unroll
-  for (int i = 0; i < kWordsPerThread; ++i) {
-    const u32 x = xw[i];
-    even += x & 0x00FF00FFu;
-    odd += (x >> 8) & 0x00FF00FFu;
-    ovf |= x & 0xF0F0F0F0u;  // a count >= 16 = kSlot + 1: the slot overflowed
-    if (mine) {
-      const u32 v = (x >> (8 * myb)) & 0xFFu;
-      if (v) {
-        u32 p = atomicAdd(&s_nrows, 1u);
-        s_rows[p] = ((u32)((tid + i * NT) >> 4) << 8) | v;
+  {
+    const int j = tid & (kMaxBuckets - 1), part = tid / kMaxBuckets;  // 16 parts
+    u32 sum = 0;
+    for (int row = part; row < G; row += NT / kMaxBuckets) {
+      const u32 x = s_cm[row * kWords + (j >> 1)];
+      sum += (j & 1) ? (x >> 16) : (x & 0xFFFFu);
+    }
+    s_part[part * kMaxBuckets + j] = sum;
+    if (tid < G) {
+      const int row = tid;
+      u32 pre = 0;
+      for (int q2 = 0; q2 < (f >> 1); ++q2) {
+        const u32 x = s_cm[row * kWords + q2];
+        pre += (x & 0xFFFFu) + (x >> 16);
+      }
+      const u32 x = s_cm[row * kWords + (f >> 1)];
+      if (f & 1) pre += x & 0xFFFFu;
+      const u32 cf = (f & 1) ? (x >> 16) : (x & 0xFFFFu);
+      if (cf != 0) {
+        const u32 p = atomicAdd(&s_nrows, 1u);
+        s_rows[p] = (u32)row;
+        s_rows[kMaxStepBlocks + p] = pre | (cf << 16);
       }
     }
   }
-  // reduce over the lanes of a wave that share q (q, q+16, q+32, q+48)
-  even += __shfl_xor(even, 16, kWave);
-  even += __shfl_xor(even, 32, kWave);
-  odd += __shfl_xor(odd, 16, kWave);
-  odd += __shfl_xor(odd, 32, kWave);
-  if (lane < 16) {
-    s_part[w][4 * q + 0] = even & 0xFFFFu;
-    s_part[w][4 * q + 1] = odd & 0xFFFFu;
-    s_part[w][4 * q + 2] = even >> 16;
-    s_part[w][4 * q + 3] = odd >> 16;
-  }
-  if (ovf) atomicOr(&s_ovf, 1u);
   __syncthreads();
-  // Verdict and bucket offsets, in wave 0 (lane i = bucket i).
+  // verdict and bucket offsets in wave 0 (lane i = bucket i)
   if (w == 0) {
     u32 t = 0;
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) t += s_part[ww][lane];
-    const u32 nb = a.plan->nbuckets;
-    bool plan_ok = a.plan->valid == 1 && nb >= 1 && nb <= (u32)kMaxBuckets;
+    for (int ww = 0; ww < NW; ++ww) t += s_part[ww * kMaxBuckets + lane];
+    const u32 nb = s_phdr[1];
+    bool plan_ok = s_wait && s_phdr[2] == 1u && nb >= 1 && nb <= (u32)kMaxBuckets;
     if (plan_ok) {
-      const u32 lo_i = s_lo[lane];
-      const u32 lo_prev = lane > 0 ? s_lo[lane - 1] : 0xFFFFFFFFu;
-      const bool mono = (u32)lane >= nb || (u32)lane == 0 || lo_i <= lo_prev;
-      plan_ok = ballot(!mono) == 0 && s_lo[nb - 1] == a.plan->t_guess;
+      const u32 lo_i = s_plo[lane];
+      const u32 lo_prev = lane > 0 ? s_plo[lane - 1] : 0xFFFFFFFFu;
+      const bool mono = (u32)lane >= nb || lane == 0 || lo_i <= lo_prev;
+      plan_ok = ballot(!mono) == 0 && s_plo[nb - 1] == s_phdr[0];
     }
-    u32 x = t;  // inclusive scan of the totals over buckets 0..63
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-      u32 y = __shfl_up(x, d, kWave);
-      if (lane >= d) x += y;
-    }
-    const int64_t start = (int64_t)(x - t), all = __shfl(x, kWave - 1, kWave);
+    const u32 x = wave_inclusive_sum(t);  // over buckets 0..63
+    const int64_t start = (int64_t)(x - t), all = __builtin_amdgcn_readlane(x, kWave - 1);
     const bool live = (u32)lane < nb;
     const bool bad = (!live && t != 0) || (live && start < a.k && t > (u32)kFinishCap);
-    const bool valid = plan_ok && !s_ovf && ballot(bad) == 0 && all >= a.k;
-    const u32 why = (plan_ok ? 0u : 1u) | (s_ovf ? 2u : 0u) | (ballot(bad) != 0 ? 4u : 0u) | (all >= a.k ? 0u : 8u);
-    if (lane == j) {
+    const u32 seen = s_seen;
+    const bool any_bad = ballot(bad) != 0;
+    const bool valid = plan_ok && seen == 0 && !any_bad && all >= a.k;
+    if (lane == f) {
       s_start = start;
       s_mytot = live ? t : 0;
     }
     if (lane == 0) {
-      s_ok = valid;
-      if (j == 0) {
-        a.ctl->verdict = valid ? 1u : 0u;
+      s_ok = valid ? 1u : 0u;
+      if (f == 0) {
+        ctl->verdict = valid ? 1u : 0u;
         if (!valid) {
-          a.ctl->fallbacks += 1u;
-          a.ctl->why |= why;
+          ctl->fallbacks += 1u;
+          ctl->why |= (plan_ok ? 0u : kWhyPlan) | seen | (any_bad ? kWhyBucket : 0u) | (all >= a.k ? 0u : kWhyFew);
         }
+        xchg_agent64(&ctl->verdict_flag.v, valid ? 1u : 2u);
       }
     }
   }
   __syncthreads();
-  if (!s_ok) {
-    // the plan did not hold: every workgroup of this grid runs the exact path
-    // (they all computed the same verdict from the same counts)
-    general_path<NT>(a.gen);
-    if (j == 0) {
-      for (int i = tid; i < kHistBins; i += NT) a.shist[i] = 0u;
-      if (tid == 0) {
-        a.ctl->ticket = 0u;
-      }
-    }
-    return;
-  }
+  if (!s_ok) return false;
   const int64_t mystart = s_start, mytot = s_mytot;
-  if (mytot > 0 && mystart < a.k) {
-    const int m = (int)mytot;
-    for (int i = tid; i < kSubBins; i += NT) s_sub_cnt[i] = 0;
-    for (u32 rI = tid; rI < s_nrows; rI += NT) {
-      u32 rc = s_rows[rI];
-      u32 row = rc >> 8, c = rc & 0xFFu;
-      u32 base = atomicAdd(&s_pos, c);
-      const Pair* src = a.slots + ((int64_t)row * kMaxBuckets + j) * kSlot;
-      Pair e8[kSlot];
+  if (mytot == 0) return true;
+  const u32 nrows = s_nrows;
+  const u64* reg = (const u64*)a.region;
+  if (mystart >= a.k) return true;  // no rank below k here
+  const int m = (int)mytot;  // <= kFinishCap (verdict)
+  for (int i = tid; i < kSubBins; i += NT) s_sub_cnt[i] = 0;
+  {  // where each row's entries go: exclusive prefix over the rows
+    const u32 cnt = (u32)tid < nrows ? s_rows[kMaxStepBlocks + tid] >> 16 : 0u;
+    u32 tot;
+    const u32 ex = block_exclusive_sum<NT>(cnt, s_scan, tot);
+    if ((u32)tid < nrows) s_rpre[tid] = ex;
+    if (tid == 0) s_rpre[nrows] = tot;
+  }
+  __syncthreads();
+  {  // entry i of the bucket: its row by binary search, every load in flight at once
+    constexpr int kPer = kFinishCap / NT;
+    u64 v[kPer];
 #pragma unroll
-      for (int e = 0; e < kSlot; ++e) e8[e] = (u32)e < c ? src[e] : pair_sentinel();
-      u32 kmin = 0xFFFFFFFFu, kmax = 0;
-#pragma unroll
-      for (int e = 0; e < kSlot; ++e)
-        if ((u32)e < c && base + e < (u32)kFinishCap) {
-          s_a[base + e] = e8[e];
-          const u32 kk = key_of_bits(e8[e].bits);
-          kmin = std::min(kmin, kk);
-          kmax = std::max(kmax, kk);
+    for (int q2 = 0; q2 < kPer; ++q2) {
+      const int i = tid + q2 * NT;
+      v[q2] = 0;
+      if (i < m) {
+        int lo = 0, hi = (int)nrows - 1;  // the last row whose prefix is <= i
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (s_rpre[mid] <= (u32)i) lo = mid;
+          else hi = mid - 1;
         }
-      if (c) {
-        atomicMin(&s_kmin, kmin);
-        atomicMax(&s_kmax, kmax);
+        const u32 row = s_rows[lo], off = s_rows[kMaxStepBlocks + lo] & 0xFFFFu;
+        v[q2] = ld_agent64(reg + (int64_t)row * kRegionCap + off + (i - s_rpre[lo]));
       }
     }
-    __syncthreads();
-    // Split [kmin, kmax] into kSubBins equal key sub-ranges, numbered from the
-    // top (descending key), and group the entries by sub-range (counting
-    // sort).  Inside a sub-range an entry's place is the number of entries of
-    // that sub-range that rank before it; ranks are unique (indices differ).
-    const u32 kmin = s_kmin;
-    const u32 span = s_kmax - kmin + 1u;  // >= 1
-    const int bits = span <= 1 ? 0 : 32 - __clz(span - 1);
-    const int sh = bits > 11 ? bits - 11 : 0;  // kSubBins = 2^11
-    auto sub_of = [&](const Pair& e) -> u32 {
-      const u32 d = (key_of_bits(e.bits) - kmin) >> sh;
-      return (u32)(kSubBins - 1) - (d < (u32)kSubBins ? d : (u32)(kSubBins - 1));
-    };
-    for (int i = tid; i < m; i += NT) atomicAdd(&s_sub_cnt[sub_of(s_a[i])], 1u);
-    __syncthreads();
-    {
-      constexpr int per = kSubBins / NT;  // 2 consecutive sub-ranges per thread
-      u32 v[per], own = 0;
+    u32 kmin = 0xFFFFFFFFu, kmax = 0;
 #pragma unroll
-      for (int q2 = 0; q2 < per; ++q2) {
-        v[q2] = s_sub_cnt[tid * per + q2];
-        own += v[q2];
+    for (int q2 = 0; q2 < kPer; ++q2) {
+      const int i = tid + q2 * NT;
+      if (i < m) {
+        const Pair p = unpack_pair(v[q2]);
+        s_a[i] = p;
+        const u32 kk = key_of_bits(p.bits);
+        kmin = std::min(kmin, kk);
+        kmax = std::max(kmax, kk);
       }
-      u32 tot;
-      u32 ex = block_exclusive_sum<NT>(own, s_scan, tot);
+    }
+    kmin = wave_min(kmin);
+    kmax = wave_max(kmax);
+    if (lane == 0) {
+      atomicMin(&s_kmin, kmin);
+      atomicMax(&s_kmax, kmax);
+    }
+  }
+  __syncthreads();
+  // Split [kmin, kmax] into kSubBins equal key sub-ranges numbered from the
+  // top and group the entries by sub-range (counting sort); inside a
+  // sub-range an entry's place is the number of its entries that rank before
+  // it (ranks are unique: indices differ).
+  const u32 kmin = s_kmin;
+  const u32 span = s_kmax - kmin + 1u;
+  const int bits = span <= 1 ? 0 : 32 - __clz(span - 1);
+  const int sh = bits > 11 ? bits - 11 : 0;  // kSubBins = 2^11
+  auto sub_of = [&](const Pair& e) -> u32 {
+    const u32 d = (key_of_bits(e.bits) - kmin) >> sh;
+    return (u32)(kSubBins - 1) - (d < (u32)kSubBins ? d : (u32)(kSubBins - 1));
+  };
+  for (int i = tid; i < m; i += NT) atomicAdd(&s_sub_cnt[sub_of(s_a[i])], 1u);
+  __syncthreads();
+  {
+    constexpr int per = kSubBins / NT;
+    u32 v[per], own = 0;
 #pragma unroll
-      for (int q2 = 0; q2 < per; ++q2) {
-        s_sub_off[tid * per + q2] = ex;
-        s_sub_cnt[tid * per + q2] = ex;  // becomes the fill cursor
-        ex += v[q2];
-      }
+    for (int q2 = 0; q2 < per; ++q2) {
+      v[q2] = s_sub_cnt[tid * per + q2];
+      own += v[q2];
     }
-    __syncthreads();
-    for (int i = tid; i < m; i += NT) {
-      Pair e = s_a[i];
-      s_b[atomicAdd(&s_sub_cnt[sub_of(e)], 1u)] = e;
+    u32 tot;
+    u32 ex = block_exclusive_sum<NT>(own, s_scan, tot);
+#pragma unroll
+    for (int q2 = 0; q2 < per; ++q2) {
+      s_sub_off[tid * per + q2] = ex;
+      s_sub_cnt[tid * per + q2] = ex;  // becomes the fill cursor
+      ex += v[q2];
     }
-    __syncthreads();
-    const int64_t take = std::min<int64_t>(mytot, a.k - mystart);
-    for (int i = tid; i < m; i += NT) {
-      const Pair e = s_b[i];
-      const u32 sb = sub_of(e);
-      const u32 s0 = s_sub_off[sb], s1 = s_sub_cnt[sb];  // the cursor ended at the range's end
-      const u64 re = pair_rank(e);
-      u32 r = 0;
-      for (u32 t = s0; t < s1; ++t) r += pair_rank(s_b[t]) < re;
-      const int64_t p = (int64_t)(s0 + r);
-      if (p < take) {
-        a.out_idx[mystart + p] = e.idx;
-        a.out_val[mystart + p] = __uint_as_float(e.bits);
-        if (e.idx >= 0 && (int64_t)e.idx < a.n) a.residual[e.idx] = 0.0f;
+  }
+  __syncthreads();
+  for (int i = tid; i < m; i += NT) {
+    const Pair e = s_a[i];
+    s_b[atomicAdd(&s_sub_cnt[sub_of(e)], 1u)] = e;
+  }
+  __syncthreads();
+  const int64_t take = std::min<int64_t>(mytot, a.k - mystart);
+  for (int i = tid; i < m; i += NT) {
+    const Pair e = s_b[i];
+    const u32 sb = sub_of(e);
+    const u32 s0 = s_sub_off[sb], s1 = s_sub_cnt[sb];  // the cursor ended at the range's end
+    const u64 re = pair_rank(e);
+    u32 r = 0;
+    for (u32 t = s0; t < s1; ++t) r += pair_rank(s_b[t]) < re;
+    const int64_t p = (int64_t)(s0 + r);
+    if (p < take) {
+      a.out_idx[mystart + p] = e.idx;
+      a.out_val[mystart + p] = __uint_as_float(e.bits);
+    }
+    // the k-th entry: every workgroup zeroes its own entries ranked up to it
+    if (mystart + p == a.k - 1) xchg_agent64(&ctl->last_rank.v, re + 1u);
+  }
+  return true;
+}
+
+__global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
+  constexpr int NT = kStepThreads;
+  constexpr int NW = kStepWaves;
+  constexpr int per = kHistBins / NT;
+  constexpr u32 kNoKey = 0xFFFFFFFFu;
+  __shared__ __align__(16) u32 s_raw[kRawWords];
+  __shared__ u32 s_scan[NW + 1];
+  __shared__ u32 s_lo[kMaxBuckets];
+  __shared__ u32 s_bcnt[kMaxBuckets];
+  __shared__ u32 s_boff[kMaxBuckets];
+  __shared__ u32 s_hdr[3];
+  __shared__ u32 s_nlist, s_ovf, s_npub, s_flag, s_floor, s_tlocbin;
+  __shared__ int64_t s_next[2];        // next row pair (double-buffered), -1 when none is left
+  __shared__ u32 s_pairs[kMaxPairs];  // row pairs this workgroup streamed
+  __shared__ u32 s_npairs;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int w = tid / kWave;
+  const int G = gridDim.x;
+  const int b = blockIdx.x;
+  const int M = G - 1, m = b - 1;  // streaming workgroups and this one's rank among them
+  StepCtl* ctl = a.ctl;
+  float* __restrict__ r = a.residual;
+  const float* __restrict__ g = a.grad;
+  const v4f* __restrict__ gv = (const v4f*)(g + a.head);
+  v4f* __restrict__ rv = (v4f*)(r + a.head);
+  // Aligned mode streams rows of NT float4, two at a time: pair p is rows
+  // 2p and 2p + 1.  Streaming workgroup m takes pair m first, then pairs
+  // handed out at run time (see next_pair), so workgroups on busier parts of
+  // the chip take fewer; the grid still sweeps the arrays front to back.
+  // Scalar mode streams tiles of NT * 8 elements, tile t to workgroup t % M.
+  constexpr int64_t TE = (int64_t)NT * 8;
+  const int64_t nrows = a.vec ? (a.nv + NT - 1) / NT : (a.n + TE - 1) / TE;
+  const int64_t npairs = (nrows + 1) / 2;
+  const int ng = phase_groups(G);
+
+  // sample loads first, then the first two rows, all in flight together
+  float sg[kSampleRounds], sr[kSampleRounds];
+  bool sok[kSampleRounds];
+#pragma unroll
+  for (int j = 0; j < kSampleRounds; ++j) {  // chunk c belongs to workgroup c % G
+    const int64_t c = b + (int64_t)G * (w + NW * j);
+    const int64_t i = c * a.stride + lane;
+    sok[j] = c < a.chunks && i < a.n;
+    sg[j] = sok[j] ? g[i] : 0.0f;
+    sr[j] = sok[j] ? r[i] : 0.0f;
+  }
+  v4f pg[2], pr[2];
+  if (b > 0 && a.vec) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int64_t i = (2 * (int64_t)m + u) * NT + tid;
+      if (i < a.nv) {
+        pg[u] = __builtin_nontemporal_load(gv + i);
+        pr[u] = __builtin_nontemporal_load(rv + i);
       }
     }
   }
-  if (j == 0) {
-    for (int i = tid; i < kHistBins; i += NT) a.shist[i] = 0u;
+
+  // ---------------- sample ----------------
+  u32 psink = 0;  // returned values of the publishing atomics
+  {
+    u32* s_h = s_raw;                 // [kHistBins]
+    u32* s_keys = s_raw + kHistBins;  // [kSampleKeyCap]
+    for (int i = tid; i < kHistBins; i += NT) s_h[i] = 0;
+    for (int i = tid; i < kSampleKeyCap; i += NT) s_keys[i] = kNoKey;
     if (tid == 0) {
-      a.ctl->ticket = 0u;
+      s_floor = 0;
+      s_tlocbin = 0;
+      s_nlist = 0;
+      s_ovf = 0;
+      s_npub = 0;
+      s_npairs = 0;
     }
+    if (b == 0) {  // the exact path's state and the error word start at zero
+      for (int i = tid; i < a.gstate_words; i += NT) psink += xchg_agent(&a.gstate[i], 0u);
+      if (tid == 0) psink += xchg_agent(&ctl->err, 0u);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kSampleRounds; ++j) {
+      if (!sok[j]) continue;
+      const u32 key = key_of(sr[j] + sg[j]);
+      atomicAdd(&s_h[key >> kHistShift], 1u);
+      s_keys[(j * NW + w) * kWave + lane] = key;
+    }
+    __syncthreads();
+    {  // floor bin (at least pub_want keys at or above it) and T_loc's bin
+      const int hi = kHistBins - per * tid;
+      u32 own = 0;
+#pragma unroll
+      for (int q = 1; q <= per; ++q) own += s_h[hi - q];
+      u32 total;
+      u32 run = block_exclusive_sum<NT>(own, s_scan, total);
+      const u32 rl = std::max(1u, (u32)(((u64)total * a.loc_q16) >> 16));
+#pragma unroll
+      for (int q = 1; q <= per; ++q) {
+        const u32 h = s_h[hi - q];
+        if (run < a.pub_want && run + h >= a.pub_want) s_floor = (u32)(hi - q);
+        if (run < rl && run + h >= rl) s_tlocbin = (u32)(hi - q);
+        run += h;
+      }
+    }
+    __syncthreads();
+    {  // publish the keys of bins >= floor (at most kPubCap) and the count
+      const u32 floor_bin = s_floor;
+      u32 mine = 0;
+      for (int i = tid; i < kSampleKeyCap; i += NT) {
+        const u32 key = s_keys[i];
+        mine += key != kNoKey && (key >> kHistShift) >= floor_bin;
+      }
+      u32 count;
+      u32 pos = block_exclusive_sum<NT>(mine, s_scan, count);
+      u32* mine_pub = a.pub + (int64_t)b * kPubCap;
+      for (int i = tid; i < kSampleKeyCap; i += NT) {
+        const u32 key = s_keys[i];
+        if (key != kNoKey && (key >> kHistShift) >= floor_bin) {
+          if (pos < (u32)kPubCap) psink += xchg_agent(&mine_pub[pos], key);
+          ++pos;
+        }
+      }
+      if (tid == 0) psink += xchg_agent(&a.pub[kPlanCap + b], std::min(count, 0xFFFFu) | (floor_bin << 16));
+    }
+    __syncthreads();  // s_raw changes role after this
+  }
+  // Arrival at the sample phase, once this workgroup's published values are
+  // all in (waiting for the atomics' returned values).
+  auto sample_arrive = [&]() {
+    if (psink == 0x12345678u) s_scan[NW] = psink;  // keeps the returned values live
+    __syncthreads();
+    if (tid == 0) phase_arrive(ctl->samp_grp, &ctl->samp_all, G);
+  };
+
+  if (b == 0) {
+    // ---------------- plan ----------------
+    sample_arrive();
+    step_plan(a, s_raw, s_scan);
+    __syncthreads();
+    if (tid == 0) phase_arrive(ctl->main_grp, &ctl->main_all, G);
+  } else {
+    // ---------------- stream ----------------
+    const u32 tloc = s_tlocbin << kHistShift;
+    Pair* s_list = (Pair*)s_raw;                  // [kListCap]
+    Pair* s_pub = (Pair*)(s_raw + 2 * kListCap);  // [kRegionCap]
+    static_assert(2 * kListCap + 2 * kRegionCap <= kRawWords, "LDS");
+    auto keep_scalar = [&](int64_t i) {
+      const float acc = r[i] + g[i];
+      r[i] = acc;
+      const u32 bits = __float_as_uint(acc);
+      if (key_of_bits(bits) >= tloc) list_keep(s_list, &s_nlist, &s_ovf, i, bits);
+    };
+    // One row: acc goes to residual as a float4 (whole lines, never partial);
+    // entries with key >= T_loc are appended to the list at offsets from one
+    // wave-wide prefix sum and one LDS atomic per wave.
+    auto vec_row = [&](int64_t t, const v4f gg, const v4f rr) {
+      const int64_t i = t * NT + tid;
+      const bool in = i < a.nv;
+      const v4f acc = rr + gg;
+      if (in) __builtin_nontemporal_store(acc, rv + i);
+      const u32 b0 = __float_as_uint(acc.x), b1 = __float_as_uint(acc.y);
+      const u32 b2 = __float_as_uint(acc.z), b3 = __float_as_uint(acc.w);
+      const u32 mk = in ? ((u32)(key_of_bits(b0) >= tloc) | ((u32)(key_of_bits(b1) >= tloc) << 1) |
+                           ((u32)(key_of_bits(b2) >= tloc) << 2) | ((u32)(key_of_bits(b3) >= tloc) << 3))
+                        : 0u;
+      if (ballot(mk != 0) == 0) return;  // wave-uniform
+      const u32 cnt = (u32)__popc(mk);
+      const u32 incl = wave_inclusive_sum(cnt);
+      const u32 total = __builtin_amdgcn_readlane(incl, kWave - 1);
+      u32 base = 0;
+      if (lane == 0) base = atomicAdd(&s_nlist, total);
+      base = __builtin_amdgcn_readfirstlane(base);
+      if (mk != 0) {
+        u32 pos = base + incl - cnt;
+        const int64_t e = a.head + 4 * i;
+        const u32 bb[4] = {b0, b1, b2, b3};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (mk & (1u << j)) {
+            if (pos < (u32)kListCap) s_list[pos] = Pair{(int32_t)(e + j), bb[j]};
+            else s_ovf = 1u;  // the list is incomplete
+            ++pos;
+          }
+        }
+      }
+    };
+    if (a.vec) {
+      // Pairs [0, S) are dealt statically: workgroup m takes m, m + M, ...
+      // (no barriers).  Pairs [S, npairs), about a quarter, are handed out
+      // at run time: group x (= b % ng) hands out S + x, S + x + ng, ...
+      // from its counter.  Thread 0 asks for the next pair one iteration
+      // ahead; when its group has none left it looks at every group's
+      // counter and asks the one with the most left.
+      const int64_t S = std::min<int64_t>(npairs, std::max<int64_t>(1, (npairs * 3 / 4) / M) * M);
+      u32 xs = (u32)(b % ng);
+      u64 pend = 0;
+      bool more = npairs > S;
+      auto group_total = [&](u32 x) -> u64 {
+        const int64_t d = npairs - S - (int64_t)x;
+        return d > 0 ? (u64)((d + ng - 1) / ng) : 0u;
+      };
+      auto next_pair = [&]() -> int64_t {  // thread 0: completes the request in flight
+        if (!more) return -1;
+        int64_t p = S + (int64_t)xs + (int64_t)ng * (int64_t)pend;
+        for (int attempt = 0; p >= npairs && attempt < 16; ++attempt) {
+          u64 c[8];
+#pragma unroll
+          for (int x = 0; x < 8; ++x) c[x] = x < ng ? ld_agent64(&ctl->rows_grp[x].v) : 0u;
+          u64 best_left = 0;
+          int best = -1;
+          for (int x = 0; x < ng; ++x) {
+            const u64 tot = group_total((u32)x);
+            const u64 left = tot > c[x] ? tot - c[x] : 0u;
+            if (left > best_left) {
+              best_left = left;
+              best = x;
+            }
+          }
+          if (best < 0) break;
+          xs = (u32)best;
+          pend = add_agent64(&ctl->rows_grp[xs].v, 1u);
+          p = S + (int64_t)xs + (int64_t)ng * (int64_t)pend;
+        }
+        if (p >= npairs) {
+          more = false;
+          return -1;
+        }
+        return p;
+      };
+      if (m < S) {
+        vec_row(2 * (int64_t)m, pg[0], pr[0]);
+        vec_row(2 * (int64_t)m + 1, pg[1], pr[1]);
+      }
+      sample_arrive();
+      for (int64_t p = (int64_t)m + M; p < S; p += M) {
+        v4f gg[2], rr[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int64_t i = (2 * p + u) * NT + tid;
+          if (i < a.nv) {
+            gg[u] = __builtin_nontemporal_load(gv + i);
+            rr[u] = __builtin_nontemporal_load(rv + i);
+          }
+        }
+        vec_row(2 * p, gg[0], rr[0]);
+        vec_row(2 * p + 1, gg[1], rr[1]);
+      }
+      if (tid == 0 && more) pend = add_agent64(&ctl->rows_grp[xs].v, 1u);
+      for (int it = 0;; ++it) {
+        if (tid == 0) s_next[it & 1] = next_pair();
+        __syncthreads();
+        const int64_t p = s_next[it & 1];
+        if (p < 0) break;
+        if (tid == 0) {
+          if (more) pend = add_agent64(&ctl->rows_grp[xs].v, 1u);  // the one after
+          if (s_npairs < (u32)kMaxPairs) s_pairs[s_npairs] = (u32)p;
+          ++s_npairs;
+        }
+        v4f gg[2], rr[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int64_t i = (2 * p + u) * NT + tid;
+          if (i < a.nv) {
+            gg[u] = __builtin_nontemporal_load(gv + i);
+            rr[u] = __builtin_nontemporal_load(rv + i);
+          }
+        }
+        vec_row(2 * p, gg[0], rr[0]);
+        vec_row(2 * p + 1, gg[1], rr[1]);
+      }
+      if (m == 0 && tid < a.head) keep_scalar(tid);
+      if (m == M - 1)
+        for (int64_t i = a.head + 4 * a.nv + tid; i < a.n; i += NT) keep_scalar(i);
+    } else {
+      sample_arrive();
+      constexpr int kU = 8;
+      for (int64_t t = m; t < nrows; t += M) {
+        float gg[kU], rr[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int64_t i = t * TE + u * NT + tid;
+          if (i < a.n) {
+            gg[u] = g[i];
+            rr[u] = r[i];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int64_t i = t * TE + u * NT + tid;
+          if (i < a.n) {
+            const float acc = rr[u] + gg[u];
+            r[i] = acc;
+            const u32 bits = __float_as_uint(acc);
+            if (key_of_bits(bits) >= tloc) list_keep(s_list, &s_nlist, &s_ovf, i, bits);
+          }
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---------------- publish ----------------
+    if (tid == 0) s_flag = flag_wait(&ctl->plan_flag, &ctl->err);
+    __syncthreads();
+    if (tid < kMaxBuckets) s_lo[tid] = ld_agent(&ctl->plan.lo[tid]);
+    if (tid == kMaxBuckets) s_hdr[0] = ld_agent(&ctl->plan.t_guess);
+    if (tid == kMaxBuckets + 1) s_hdr[1] = ld_agent(&ctl->plan.nbuckets);
+    if (tid == kMaxBuckets + 2) s_hdr[2] = ld_agent(&ctl->plan.valid);
+    if (tid < kMaxBuckets) s_bcnt[tid] = 0;
+    __syncthreads();
+    const bool plan_ok = s_flag != 0 && s_hdr[2] == 1u && s_hdr[1] >= 1 && s_hdr[1] <= (u32)kMaxBuckets;
+    const u32 tg = plan_ok ? s_hdr[0] : 0xFFFFFFFFu;
+    const int nb = plan_ok ? (int)s_hdr[1] : 1;
+    u32 fail = s_flag != 0 ? 0u : kWhyWait;
+    if ((s_ovf || tloc > tg) && plan_ok) {
+      // The list may miss keys >= T_guess (it overflowed, or T_loc lies
+      // above T_guess).  This workgroup's rows of residual hold acc; after a
+      // fence (so no stale cached line is read) they are re-read for the keys
+      // >= T_guess.
+      __threadfence();
+      __syncthreads();
+      if (tid == 0) {
+        s_nlist = 0;
+        s_ovf = 0;
+        atomicAdd(&ctl->rescans, 1u);
+      }
+      __syncthreads();
+      auto rescan = [&](int64_t lo, int64_t hi) {
+        for (int64_t i = lo + tid; i < hi; i += NT) {
+          const u32 bits = __float_as_uint(r[i]);
+          if (key_of_bits(bits) >= tg) list_keep(s_list, &s_nlist, &s_ovf, i, bits);
+        }
+      };
+      if (a.vec) {
+        const int64_t S = std::min<int64_t>(npairs, std::max<int64_t>(1, (npairs * 3 / 4) / M) * M);
+        auto rescan_pair = [&](int64_t p) {
+          rescan(a.head + 4 * 2 * p * NT, a.head + 4 * std::min<int64_t>(a.nv, (2 * p + 2) * NT));
+        };
+        for (int64_t p = m; p < S; p += M) rescan_pair(p);
+        const u32 np = std::min(s_npairs, (u32)kMaxPairs);
+        for (u32 q = 0; q < np; ++q) rescan_pair((int64_t)s_pairs[q]);
+        if (s_npairs > (u32)kMaxPairs) atomicOr(&s_ovf, 1u);  // rows not remembered: cannot re-read
+      } else {
+        for (int64_t t = m; t < nrows; t += M) rescan(t * TE, std::min<int64_t>(a.n, (t + 1) * TE));
+      }
+      if (a.vec && m == 0) rescan(0, a.head);
+      if (a.vec && m == M - 1) rescan(a.head + 4 * a.nv, a.n);
+      __syncthreads();
+      if (s_ovf) fail |= kWhyList;  // more keys >= T_guess than the list holds
+    }
+    const u32 nl = std::min(s_nlist, (u32)kListCap);
+    for (u32 i = tid; i < nl; i += NT) {
+      const u32 key = key_of_bits(s_list[i].bits);
+      if (key >= tg) atomicAdd(&s_bcnt[bucket_of(key, s_lo, nb)], 1u);
+    }
+    __syncthreads();
+    if (w == 0) {  // bucket offsets
+      const u32 v = s_bcnt[lane];
+      const u32 x = wave_inclusive_sum(v);
+      s_boff[lane] = x - v;
+      if (lane == kWave - 1) s_npub = x;
+    }
+    __syncthreads();
+    const u32 C = s_npub;
+    u32 sink = 0;
+    if (C <= (u32)kRegionCap && !(fail & kWhyList)) {
+      for (u32 i = tid; i < nl; i += NT) {
+        const Pair e = s_list[i];
+        const u32 key = key_of_bits(e.bits);
+        if (key >= tg) s_pub[atomicAdd(&s_boff[bucket_of(key, s_lo, nb)], 1u)] = e;
+      }
+      __syncthreads();
+      u64* dst = (u64*)(a.region + (int64_t)b * kRegionCap);
+      for (u32 i = tid; i < C; i += NT) sink += (u32)xchg_agent64(dst + i, pack_pair(s_pub[i]));
+      if (tid < kMaxBuckets / 2)
+        sink += xchg_agent(&a.rcnt[b * (kMaxBuckets / 2) + tid], s_bcnt[2 * tid] | (s_bcnt[2 * tid + 1] << 16));
+    } else {
+      // cannot publish: the plan fails
+      if (tid < kMaxBuckets / 2) sink += xchg_agent(&a.rcnt[b * (kMaxBuckets / 2) + tid], 0u);
+      fail |= kWhyRegion;
+      __syncthreads();
+      if (tid == 0) s_npub = 0;
+    }
+    if (tid == 0 && fail) sink += or_agent((u32*)&ctl->bad.v, fail);
+    if (sink == 0x12345678u) s_scan[NW] = sink;  // keeps the returned values live
+    __syncthreads();
+    if (tid == 0) phase_arrive(ctl->main_grp, &ctl->main_all, G);
+  }
+
+  // ---------------- finish ----------------
+  u32 verdict;
+  if (b < kMaxBuckets) {
+    verdict = step_finish(a, s_raw, s_scan) ? 1u : 2u;
+  } else {
+    if (tid == 0) s_flag = flag_wait(&ctl->verdict_flag, &ctl->err);
+    __syncthreads();
+    verdict = s_flag;
+  }
+  if (verdict == 1u) {
+    // The selected entries are those ranked up to the k-th; each streaming
+    // workgroup zeroes the ones it published (it wrote their acc itself, so
+    // its two stores to a word stay in order).
+    if (b > 0) {
+      __shared__ u64 s_last;
+      if (tid == 0) {
+        u32 spins = 0;
+        u64 v;
+        while ((v = ld_agent64(&ctl->last_rank.v)) == 0) {
+          __builtin_amdgcn_s_sleep(2);
+          if (++spins > kSpinLimit) {
+            atomicOr(&ctl->err, kErrBarrierTimeout);
+            break;
+          }
+        }
+        s_last = v - 1u;  // ~0 after a time-out: nothing is zeroed
+      }
+      __syncthreads();
+      const u64 last = s_last;
+      const u32 npub = s_npub;
+      const u64* mine = (const u64*)(a.region + (int64_t)b * kRegionCap);
+      for (u32 i = tid; i < npub; i += NT) {
+        const Pair p = b >= kMaxBuckets ? ((const Pair*)(s_raw + 2 * kListCap))[i] : unpack_pair(ld_agent64(mine + i));
+        if (pair_rank(p) <= last) r[p.idx] = 0.0f;
+      }
+    }
+  } else {
+    // The plan did not hold: residual holds acc everywhere, and the whole
+    // grid runs the exact path (grid_sync fences first, so every
+    // workgroup's residual stores are visible to all).
+    if (grid_sync(a.gen.bar)) general_path<NT>(a.gen);
+  }
+
+  // ---------------- exit: the last workgroup clears the counters ----------------
+  __syncthreads();
+  if (tid == 0 && phase_arrive(ctl->exit_grp, &ctl->exit_all, G)) {
+    for (int i = 0; i < 8; ++i) {
+      xchg_agent64(&ctl->samp_grp[i].v, 0u);
+      xchg_agent64(&ctl->main_grp[i].v, 0u);
+      xchg_agent64(&ctl->exit_grp[i].v, 0u);
+      xchg_agent64(&ctl->rows_grp[i].v, 0u);
+    }
+    xchg_agent64(&ctl->samp_all.v, 0u);
+    xchg_agent64(&ctl->main_all.v, 0u);
+    xchg_agent64(&ctl->exit_all.v, 0u);
+    xchg_agent64(&ctl->plan_flag.v, 0u);
+    xchg_agent64(&ctl->last_rank.v, 0u);
+    xchg_agent64(&ctl->verdict_flag.v, 0u);
+    xchg_agent64(&ctl->bad.v, 0u);
   }
 }
 
@@ -1138,6 +1494,61 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(FinishArgs a) {
 
 // ==================================================================== host ==
 using namespace tgs;
+
+namespace {
+
+// Workgroups k_step may use on the current device: one per compute unit (its
+// LDS allows no more), never above kMaxStepBlocks.  0 if unknown.
+int step_capacity() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_step, kStepThreads, 0) != hipSuccess) occ = 0;
+    const int cus = device_cu_count();
+    cache[dev] = std::max(0, std::min(kMaxStepBlocks, occ * cus));
+    if (cache[dev] == 0) cache[dev] = -1;
+  }
+  return cache[dev] > 0 ? cache[dev] : 0;
+}
+
+// Sampling and sizing of the fast path for (n, k) on G workgroups; false when
+// the fast path does not apply.
+bool step_params(int64_t n, int64_t k, int G, StepArgs& a) {
+  if (k < 1 || n < kFastMinN || G < kMaxBuckets + 1 || G > kMaxStepBlocks) return false;
+  const int M = G - 1;
+  const double kd = (double)k, nd = (double)n;
+  const double tau = std::max(1.4 * kd, kd + 8192.0);  // candidates aimed for
+  const double eps = 1.0 - kd / tau;                   // relative slack below tau
+  const double need_stat = 25.0 / (eps * eps);         // ~5 sigma of Poisson noise
+  const double bucket_elems = std::max(512.0, 1.2 * kd / 56.0);
+  if (bucket_elems > kFinishCap / 4) return false;
+  const double nb_needed = std::ceil(1.1 * kd / bucket_elems);
+  const double c = std::max({need_stat, 8.0 * nb_needed, 64.0});
+  const double m = c * nd / tau;  // sample elements
+  int64_t chunks = (int64_t)std::ceil(m / kSampleChunk);
+  chunks = std::max<int64_t>(chunks, 4 * (int64_t)G);  // every workgroup samples at least 4 chunks
+  chunks = std::min<int64_t>(chunks, (int64_t)G * kStepWaves * kSampleRounds);
+  chunks = std::min<int64_t>(chunks, n / kSampleChunk);
+  if (chunks < 4 * (int64_t)G) return false;
+  a.chunks = chunks;
+  a.stride = n / chunks;  // >= 64: chunks never overlap
+  const double m_real = (double)chunks * kSampleChunk;
+  a.c_target = (u32)std::max(1.0, std::ceil(tau * m_real / nd));
+  a.bucket_samples = (u32)std::max(1.0, std::ceil(bucket_elems * m_real / nd));
+  a.pub_want = 8u * ((a.c_target + G - 1) / G) + 8u;
+  if (a.pub_want + 8 > (u32)kPubCap) return false;
+  // T_loc: a local-sample quantile with about 1024 (and at least 4x the
+  // expected candidate count) of a share's entries above it
+  const double share = nd / M;
+  const double f_loc = std::min(1.0, std::max(1024.0 / share, 4.0 * tau / nd));
+  if (f_loc * share > kListCap / 4 || tau / M > kRegionCap / 4) return false;
+  a.loc_q16 = (u32)std::min(65535.0, std::ceil(f_loc * 65536.0));
+  return true;
+}
+
+}  // namespace
 
 extern "C" size_t tgs_topk_workspace_bytes(int64_t n, int64_t k) {
   if (n < 0 || n > INT32_MAX || k < 0 || k > n) return 0;
@@ -1164,94 +1575,86 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
     return fail(TGS_EWORKSPACE, "topk_ef_step: workspace %zu bytes, need %zu", workspace_bytes, L.total);
   if (n == 0) return TGS_OK;
   char* ws = (char*)workspace;
-  TopkCtl* ctl = (TopkCtl*)(ws + L.ctl);
+  StepCtl* ctl = (StepCtl*)(ws + L.ctl);
+  GenState* gs = (GenState*)(ws + L.gstate);
 
   const int path = (int)get_option(TGS_OPT_TOPK_PATH);
-  const bool fast = path != 1 && L.fast_possible;
-
-  MainArgs ma{};
-  ma.grad = grad;
-  ma.residual = residual;
-  ma.n = n;
+  const int64_t gopt = get_option(TGS_OPT_MAIN_GRID);
   const bool vec = (((uintptr_t)grad) & 15u) == (((uintptr_t)residual) & 15u);
+  int64_t head = 0, nv = 0;
   if (vec) {
-    int64_t head = (int64_t)(((16u - (((uintptr_t)residual) & 15u)) & 15u) / 4u);
-    head = std::min<int64_t>(head, n);
-    ma.head = head;
-    ma.nv = (n - head) / 4;
+    head = std::min<int64_t>(n, (int64_t)(((16u - (((uintptr_t)residual) & 15u)) & 15u) / 4u));
+    nv = (n - head) / 4;
   }
-  ma.plan = &ctl->plan;
-  ma.cnt = (unsigned char*)(ws + L.cnt);
-  ma.slots = (Pair*)(ws + L.slots);
-  // general-path state: its histograms and the grid-barrier words
-  GenState* gs = (GenState*)(ws + L.ghist);
-  ma.zero_ptr = (u32*)gs;
-  ma.zero_words = (int)(sizeof(GenState) / sizeof(u32));
-  ma.err = &ctl->err;
-  int64_t units = vec ? ma.nv : n;
-  int64_t want = (units + kMainThreads * kMainU * (vec ? 1 : 4) - 1) / (kMainThreads * kMainU * (vec ? 1 : 4));
-  int G1 = (int)std::max<int64_t>(1, std::min<int64_t>(kMaxMainBlocks, want));
-  int64_t gopt = get_option(TGS_OPT_MAIN_GRID);
-  if (gopt > 0) G1 = (int)std::min<int64_t>(gopt, kMaxMainBlocks);
+
+  GenArgs ga{};
+  ga.acc = residual;
+  ga.residual = residual;
+  ga.n = n;
+  ga.k = k;
+  ga.out_idx = out_idx;
+  ga.out_val = out_val;
+  ga.ghist = &gs->hist[0][0];
+  ga.gcnt = (u32*)(ws + L.gcnt);
+  ga.lsd_cnt = (u32*)(ws + L.lsd_cnt);
+  ga.lsd_pre = (u32*)(ws + L.lsd_pre);
+  ga.lsd_tot = (u32*)(ws + L.lsd_tot);
+  ga.bufA = (Pair*)(ws + L.bufA);
+  ga.bufB = (Pair*)(ws + L.bufB);
+  ga.bar.count = &gs->bar_count;
+  ga.bar.gen = &gs->bar_gen;
+  ga.bar.abort = &gs->bar_abort;
+  ga.bar.err = &ctl->err;
+
+  StepArgs sa{};
+  int G = 0;
+  if (path != 1) {
+    const int cap = step_capacity();
+    G = gopt > 0 ? (int)std::min<int64_t>(gopt, cap) : cap;
+    if (!step_params(n, k, G, sa)) G = 0;
+  }
 
   hipEvent_t ev0, ev1;
   take_profile_events(&ev0, &ev1);
-
-  if (fast) {
-    SampleParams sp = sample_params(n, k);
-    sp.break_plan = path == 2 ? 1u : 0u;
-    hipLaunchKernelGGL(k_sample, dim3(kSampleBlocks), dim3(kSampleThreads), 0, stream, grad, residual, sp,
-                       (u32*)(ws + L.shist), (u32*)(ws + L.slist), ctl);
-  }
   if (ev0) (void)hipEventRecord(ev0, stream);
-  if (fast) {
-    if (vec) hipLaunchKernelGGL((k_ef_main<true, true>), dim3(G1), dim3(kMainThreads), 0, stream, ma);
-    else hipLaunchKernelGGL((k_ef_main<true, false>), dim3(G1), dim3(kMainThreads), 0, stream, ma);
+  if (G > 0) {
+    sa.grad = grad;
+    sa.residual = residual;
+    sa.n = n;
+    sa.k = k;
+    sa.head = head;
+    sa.nv = nv;
+    sa.vec = vec ? 1 : 0;
+    sa.out_idx = out_idx;
+    sa.out_val = out_val;
+    sa.break_plan = path == 2 ? 1u : 0u;
+    sa.ctl = ctl;
+    sa.pub = (u32*)(ws + L.pub);
+    sa.rcnt = (u32*)(ws + L.rcnt);
+    sa.region = (Pair*)(ws + L.region);
+    sa.gstate = (u32*)gs;
+    sa.gstate_words = (int)(sizeof(GenState) / sizeof(u32));
+    sa.gen = ga;
+    sa.gen.bar.nwg = (u32)G;
+    hipLaunchKernelGGL(k_step, dim3(G), dim3(kStepThreads), 0, stream, sa);
   } else {
-    if (vec) hipLaunchKernelGGL((k_ef_main<false, true>), dim3(G1), dim3(kMainThreads), 0, stream, ma);
-    else hipLaunchKernelGGL((k_ef_main<false, false>), dim3(G1), dim3(kMainThreads), 0, stream, ma);
-  }
-  if (ev1) (void)hipEventRecord(ev1, stream);
-
-  if (k > 0) {
-    GenArgs ga{};
-    ga.acc = residual;
-    ga.residual = residual;
-    ga.n = n;
-    ga.k = k;
-    ga.out_idx = out_idx;
-    ga.out_val = out_val;
-    ga.ghist = &gs->hist[0][0];
-    ga.gcnt = (u32*)(ws + L.gcnt);
-    ga.lsd_cnt = (u32*)(ws + L.lsd_cnt);
-    ga.lsd_pre = (u32*)(ws + L.lsd_pre);
-    ga.lsd_tot = (u32*)(ws + L.lsd_tot);
-    ga.bufA = (Pair*)(ws + L.bufA);
-    ga.bufB = (Pair*)(ws + L.bufB);
-    ga.bar.count = &gs->bar_count;
-    ga.bar.gen = &gs->bar_gen;
-    ga.bar.abort = &gs->bar_abort;
-    ga.bar.err = &ctl->err;
-    if (fast) {
-      FinishArgs fa{};
-      fa.plan = &ctl->plan;
-      fa.cnt = ma.cnt;
-      fa.slots = ma.slots;
-      fa.G1 = G1;
-      fa.n = n;
-      fa.k = k;
-      fa.out_idx = out_idx;
-      fa.out_val = out_val;
-      fa.residual = residual;
-      fa.ctl = ctl;
-      fa.shist = (u32*)(ws + L.shist);
-      fa.gen = ga;
-      // kMaxBuckets workgroups of kFinishThreads: far below one per compute
-      // unit, so all are resident for the fallback's grid barriers
-      hipLaunchKernelGGL(k_finish, dim3(kMaxBuckets), dim3(kFinishThreads), 0, stream, fa);
-    } else {
-      // every workgroup of k_general must be resident at once (grid barriers):
-      // at most one per compute unit per occupancy slot, and never above kGenBlocks
+    AccArgs aa{};
+    aa.grad = grad;
+    aa.residual = residual;
+    aa.n = n;
+    aa.head = head;
+    aa.nv = nv;
+    aa.zero_ptr = (u32*)gs;
+    aa.zero_words = (int)(sizeof(GenState) / sizeof(u32));
+    aa.err = &ctl->err;
+    const int64_t units = vec ? nv : n;
+    const int64_t per = (int64_t)kAccThreads * kAccU * (vec ? 1 : 4);
+    int G1 = (int)std::max<int64_t>(1, std::min<int64_t>(kMaxAccBlocks, (units + per - 1) / per));
+    if (gopt > 0) G1 = (int)std::min<int64_t>(gopt, kMaxAccBlocks);
+    if (vec) hipLaunchKernelGGL(k_acc_pass<true>, dim3(G1), dim3(kAccThreads), 0, stream, aa);
+    else hipLaunchKernelGGL(k_acc_pass<false>, dim3(G1), dim3(kAccThreads), 0, stream, aa);
+    if (k > 0) {
+      // every workgroup of k_general must be resident at once (grid barriers)
       static int occ = 0;
       if (occ == 0) {
         int o = 0;
@@ -1260,10 +1663,12 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
       }
       const int cus = device_cu_count();
       if (cus <= 0) return fail(TGS_EHIP, "topk_ef_step: cannot read the compute-unit count");
-      const int G = std::max(1, std::min(kGenBlocks, cus * occ));
-      hipLaunchKernelGGL(k_general, dim3(G), dim3(kGenThreads), 0, stream, ga);
+      const int G2 = std::max(1, std::min(kGenBlocks, cus * occ));
+      ga.bar.nwg = (u32)G2;
+      hipLaunchKernelGGL(k_general, dim3(G2), dim3(kGenThreads), 0, stream, ga);
     }
   }
+  if (ev1) (void)hipEventRecord(ev1, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TGS_EHIP, "topk_ef_step: launch failed: %s", hipGetErrorString(e));
   return TGS_OK;

@@ -91,6 +91,16 @@ __device__ __forceinline__ u32 wave_inclusive_sum(u32 x) {
   x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
   return x;
 }
+// Inclusive prefix minimum over the 64 lanes (same pattern, identity ~0).
+__device__ __forceinline__ u32 wave_inclusive_min(u32 x) {
+  x = min(x, (u32)__builtin_amdgcn_update_dpp(0xFFFFFFFFu, x, 0x111, 0xf, 0xf, false));
+  x = min(x, (u32)__builtin_amdgcn_update_dpp(0xFFFFFFFFu, x, 0x112, 0xf, 0xf, false));
+  x = min(x, (u32)__builtin_amdgcn_update_dpp(0xFFFFFFFFu, x, 0x114, 0xf, 0xf, false));
+  x = min(x, (u32)__builtin_amdgcn_update_dpp(0xFFFFFFFFu, x, 0x118, 0xf, 0xf, false));
+  x = min(x, (u32)__builtin_amdgcn_update_dpp(0xFFFFFFFFu, x, 0x142, 0xa, 0xf, false));
+  x = min(x, (u32)__builtin_amdgcn_update_dpp(0xFFFFFFFFu, x, 0x143, 0xc, 0xf, false));
+  return x;
+}
 // Sum, maximum and minimum over the wave, returned to every lane.
 __device__ __forceinline__ u32 wave_sum(u32 x) { return __builtin_amdgcn_readlane(wave_inclusive_sum(x), 63); }
 __device__ __forceinline__ u32 wave_max(u32 x) {

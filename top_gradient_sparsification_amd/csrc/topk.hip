@@ -66,7 +66,6 @@ constexpr int kSampleRounds = 2;                    // chunks per wave at most
 constexpr int kSampleKeyCap = kSampleRounds * kStepThreads;  // sample keys per workgroup
 constexpr int kPubCap = 40;                         // sample keys one workgroup may publish
 constexpr int kPlanCap = kPubCap * kMaxStepBlocks;  // 10240
-constexpr int kRankBinCap = 256;                    // bins up to this size are ranked by counting
 constexpr int kListCap = 8192;                      // local list of one workgroup (LDS)
 constexpr int kRegionCap = 4096;                    // candidates one workgroup may publish
 constexpr int kFinishCap = 4096;                    // bucket entries a finisher orders in LDS
@@ -572,28 +571,29 @@ __device__ __forceinline__ void publish_plan(StepCtl* ctl, u32 valid, u32 tg, u3
 
 // Workgroup 0: the published sample keys -> plan.
 //   T_guess = the c_target-th largest sample key; bucket edge j = the
-//   (j+1)*bucket_samples-th largest.  The keys are grouped by 12-bit bin
-//   (offsets from the suffix sums of their histogram); a bin that holds a
-//   wanted rank is ranked by counting when small, or by a histogram of key
-//   bits [18:6] when large (its lower sub-bin edge, never above the key).
-//   The ranks are exact when no workgroup truncated its keys and the
-//   T_guess bin lies at or above every workgroup's floor bin (all bins from
-//   the highest floor up were published in full); otherwise the plan is
-//   still a valid guess.
+//   (j+1)*bucket_samples-th largest.  A 12-bit histogram of the keys gives
+//   b_T, the bin of the c_target-th key, and a radix select inside that bin
+//   (10 + 9 more bits) gives T_guess itself.  The keys >= T_guess -- about
+//   c_target of them; error feedback piles entries up just below the last
+//   threshold, so the bin b_T itself can be large -- are then ranked exactly
+//   (a counting sort by sub-range of the key, then counting inside each).  This
+//   is exact when b_T lies at or above every workgroup's floor (all bins
+//   from the highest floor up were published in full); otherwise the keys
+//   are interpolated inside their bins.  The plan is a guess either way.
 __device__ __forceinline__ void step_plan(const StepArgs& a, u32* s_raw, u32* s_scan) {
   constexpr int NT = kStepThreads;
   constexpr int NW = kStepWaves;
   constexpr int per = kHistBins / NT;  // 4 bins per thread, top first
+  constexpr int kTopCap = 4096;        // keys of bins >= b_T ranked exactly
   constexpr u32 kNoKey = 0xFFFFFFFFu;
-  u32* s_h = s_raw;                     // [kHistBins] histogram, then suffix sums
-  u32* s_cur = s_raw + kHistBins;       // [kHistBins] bin flags, then group cursors
-  u32* s_keys = s_raw + 2 * kHistBins;  // [kPlanCap] the published keys
-  u32* s_grp = s_keys + kPlanCap;       // [kPlanCap] grouped by bin, then a sub-histogram
+  u32* s_h = s_raw;                    // [kHistBins] histogram, then suffix sums
+  u32* s_keys = s_raw + kHistBins;     // [kPlanCap] the published keys
+  u32* s_top = s_keys + kPlanCap;      // [kTopCap] keys of bins >= b_T
+  static_assert(kHistBins + kPlanCap + kTopCap <= kRawWords, "LDS");
   __shared__ u32 s_off[kMaxStepBlocks + 1];
   __shared__ u32 s_tkey[kMaxBuckets + 1];  // [0] T_guess, [1+j] edge j
   __shared__ u32 s_lo[kMaxBuckets];
-  __shared__ u32 s_fat[kMaxBuckets + 1];
-  __shared__ u32 s_nfat, s_trunc, s_maxfloor, s_bT, s_ok;
+  __shared__ u32 s_maxfloor, s_bT, s_ok, s_ntop, s_kmax;
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int w = tid / kWave;
@@ -601,23 +601,18 @@ __device__ __forceinline__ void step_plan(const StepArgs& a, u32* s_raw, u32* s_
   StepCtl* ctl = a.ctl;
   if (tid == 0) {
     s_ok = phase_wait(&ctl->samp_all, G, &ctl->err) ? 1u : 0u;
-    s_trunc = 0;
     s_maxfloor = 0;
+    s_kmax = 0;
     s_bT = 0xFFFFFFFFu;
-    s_nfat = 0;
+    s_ntop = 0;
   }
-  for (int i = tid; i < kHistBins; i += NT) {
-    s_h[i] = 0;
-    s_cur[i] = 0;
-  }
-  for (int i = tid; i < kPlanCap; i += NT) s_grp[i] = kNoKey;
+  for (int i = tid; i < kHistBins; i += NT) s_h[i] = 0;
   __syncthreads();
   u32 c = 0;
-  if (tid < G) {
+  if (tid < G) {  // a workgroup that left keys out is complete from floor + 1 up
     const u32 v = ld_agent(&a.pub[kPlanCap + tid]);
     c = v & 0xFFFFu;
-    if (c > (u32)kPubCap) atomicOr(&s_trunc, 1u);
-    atomicMax(&s_maxfloor, v >> 16);
+    atomicMax(&s_maxfloor, (v >> 16) + (c > (u32)kPubCap ? 1u : 0u));
   }
   u32 K;
   const u32 off = block_exclusive_sum<NT>(std::min(c, (u32)kPubCap), s_scan, K);
@@ -653,15 +648,10 @@ __device__ __forceinline__ void step_plan(const StepArgs& a, u32* s_raw, u32* s_
     u32 run = block_exclusive_sum<NT>(own, s_scan, total);
 #pragma unroll
     for (int q = 1; q <= per; ++q) {  // inclusive suffix sums cum[b] = sum_{b' >= b} h[b']
-      run += s_h[hi - q];
+      const u32 h = s_h[hi - q];
+      if (run < a.c_target && run + h >= a.c_target) s_bT = (u32)(hi - q);  // b_T: where cum reaches c_target
+      run += h;
       s_h[hi - q] = run;
-    }
-  }
-  __syncthreads();
-  for (int q = 1; q <= per; ++q) {  // b_T = the largest bin with cum[b_T] >= c_target
-    if (s_h[hi - q] >= a.c_target) {
-      atomicMax((int*)&s_bT, hi - q);  // starts at -1 as int
-      break;
     }
   }
   __syncthreads();
@@ -677,133 +667,145 @@ __device__ __forceinline__ void step_plan(const StepArgs& a, u32* s_raw, u32* s_
     publish_plan(ctl, a.break_plan ? 1u : 0u, tg, 1u, s_lo, s_scan);
     return;
   }
-  auto bin_of_rank = [&](u32 q) -> int {  // largest b with cum[b] >= q
-    int lo = 0, hi2 = kHistBins - 1;
+  const int ntarget = (int)nb;  // wanted ranks: [0] c_target, [j] j * bucket_samples for 1 <= j < nb
+  auto rank_of = [&](int t) -> u32 { return t == 0 ? a.c_target : (u32)t * a.bucket_samples; };
+  if (tid < ntarget) {  // default: interpolation inside the bin of each wanted rank
+    const u32 q = rank_of(tid);
+    int lo = 0, hi2 = kHistBins - 1;  // largest b with cum[b] >= q
     while (lo < hi2) {
       const int mid = (lo + hi2 + 1) >> 1;
       if (s_h[mid] >= q) lo = mid;
       else hi2 = mid - 1;
     }
-    return lo;
-  };
-  auto cum_above = [&](int b) -> u32 { return b + 1 < kHistBins ? s_h[b + 1] : 0u; };
-  const int ntarget = (int)nb;  // wanted ranks: [0] c_target, [j] j * bucket_samples for 1 <= j < nb
-  auto rank_of = [&](int t) -> u32 { return t == 0 ? a.c_target : (u32)t * a.bucket_samples; };
-  if (tid < ntarget) {  // default: interpolation inside the bin
-    const u32 q = rank_of(tid);
-    const int b = bin_of_rank(q);
-    const u32 above_b = cum_above(b);
-    const u32 h = s_h[b] - above_b;  // >= q - above_b >= 1
+    const u32 above_b = lo + 1 < kHistBins ? s_h[lo + 1] : 0u;
+    const u32 h = s_h[lo] - above_b;  // >= q - above_b >= 1
     const u32 f = q - above_b;
     const u32 offk = (u32)((((u64)f << kHistShift) + h - 1) / h);  // in [1, 2^19]
-    s_tkey[tid] = (((u32)b + 1u) << kHistShift) - offk;
+    s_tkey[tid] = (((u32)lo + 1u) << kHistShift) - offk;
   }
-  __syncthreads();
-  const bool exact = !s_trunc && bT >= (int)s_maxfloor;
+  const bool exact = bT >= (int)s_maxfloor;
   if (exact) {
-    // flag the bins that hold a wanted rank: 1 = small, 2 = large
-    if (tid < ntarget) {
-      const int b = bin_of_rank(rank_of(tid));
-      atomicMax(&s_cur[b], s_h[b] - cum_above(b) <= (u32)kRankBinCap ? 1u : 2u);
-    }
-    __syncthreads();
-    // large flagged bins, listed once each.  In rank order the targets are
-    // t = 1 .. nb-1, then t = 0 (c_target is the largest rank); their bins do
-    // not increase, so a target lists its bin when its predecessor's differs.
-    if (tid < ntarget) {
-      const int order = tid == 0 ? ntarget - 1 : tid - 1;
-      const int b = bin_of_rank(rank_of(tid));
-      const int bprev = order > 0 ? bin_of_rank((u32)order * a.bucket_samples) : -1;
-      if (s_cur[b] == 2u && b != bprev) s_fat[atomicAdd(&s_nfat, 1u)] = (u32)b;
-    }
-    __syncthreads();  // s_cur is rewritten below
-    // small flagged bins: group their keys (the group of bin b starts at cum[b+1])
-    for (int i = tid; i < kHistBins; i += NT) s_cur[i] = s_cur[i] == 1u ? (cum_above(i) | 0x80000000u) : 0u;
-    __syncthreads();
-    for (u32 i = tid; i < K; i += NT) {
-      const u32 key = s_keys[i];
-      const u32 b = key >> kHistShift;
-      if (s_cur[b] & 0x80000000u) {
-        const u32 pos = atomicAdd(&s_cur[b], 1u) & 0x7FFFFFFFu;
-        if (pos < (u32)kPlanCap) s_grp[pos] = key;
-      }
-    }
-    __syncthreads();
-    // rank each grouped key inside its bin (ties broken by position); the key
-    // of 1-based rank q is the wanted key for rank q
-    for (u32 i = tid; i < K; i += NT) {
-      const u32 x = s_grp[i];
-      if (x == kNoKey) continue;
-      const int b = (int)(x >> kHistShift);
-      const u32 g0 = cum_above(b), g1 = s_h[b];
-      u32 r = 0;
-      for (u32 t = g0; t < g1; ++t) {
-        const u32 y = s_grp[t];
-        r += (y > x) || (y == x && t < i);
-      }
-      const u32 rank1 = g0 + r + 1;
-      if (rank1 == a.c_target) s_tkey[0] = x;
-      if (rank1 % a.bucket_samples == 0) {
-        const u32 jj = rank1 / a.bucket_samples;
-        if (jj >= 1 && jj < nb) s_tkey[jj] = x;
-      }
-    }
-    __syncthreads();
-    // large bins: histogram of key bits [18:6] (8192 sub-bins of 64 keys)
-    constexpr int kSubShift = 6;
-    constexpr int kSubN = 1 << (kHistShift - kSubShift);
-    constexpr int per2 = kSubN / NT;
-    u32* sub = s_grp;  // free again
-    for (u32 fi = 0; fi < s_nfat; ++fi) {
-      const u32 fb = s_fat[fi];
-      for (int i = tid; i < kSubN; i += NT) sub[i] = 0;
+    // T_guess exactly: radix select of the c_target-th key inside bin b_T
+    // over key bits [18:9] then [8:0] (their histograms go in s_top).
+    const u32 cum_above_bT = bT + 1 < kHistBins ? s_h[bT + 1] : 0u;
+    u32 need = a.c_target - cum_above_bT;  // 1-based rank inside bin b_T
+    u32 prefix = (u32)bT;                    // the key's bits chosen so far
+    int shift = kHistShift;
+    const int widths[2] = {10, 9};
+    for (int L = 0; L < 2; ++L) {
+      const int wd = widths[L];
+      const int nbins = 1 << wd;
+      shift -= wd;
+      __syncthreads();  // s_h (or the last level's histogram) is still being read
+      for (int i = tid; i < nbins; i += NT) s_top[i] = 0;
       __syncthreads();
       for (u32 i = tid; i < K; i += NT) {
         const u32 key = s_keys[i];
-        if ((key >> kHistShift) == fb) atomicAdd(&sub[(key >> kSubShift) & (kSubN - 1)], 1u);
+        if ((key >> (shift + wd)) == prefix) atomicAdd(&s_top[(key >> shift) & (nbins - 1)], 1u);
       }
       __syncthreads();
-      const int shi = kSubN - per2 * tid;
-      u32 sown = 0;
+      // suffix counts from the top bin down; thread t owns bin nbins - 1 - t
+      const u32 hcount = tid < nbins ? s_top[nbins - 1 - tid] : 0u;
+      u32 tot;
+      const u32 above = block_exclusive_sum<NT>(hcount, s_scan, tot);
+      if (tid < nbins && above < need && above + hcount >= need) {
+        s_bT = (u32)(nbins - 1 - tid);  // the digit (s_bT is free again)
+        s_ntop = above;
+      }
+      __syncthreads();
+      prefix = (prefix << wd) | s_bT;
+      need -= s_ntop;
+    }
+    const u32 tg = prefix;  // the c_target-th largest sample key
+    __syncthreads();
+    // the keys >= T_guess (c_target of them, more with ties), ranked exactly
+    if (tid == 0) {
+      s_tkey[0] = tg;
+      s_ntop = 0;
+    }
+    __syncthreads();
+    for (u32 i = tid; i < K; i += NT) {
+      const u32 key = s_keys[i];
+      if (key >= tg) {
+        const u32 pos = atomicAdd(&s_ntop, 1u);
+        if (pos < (u32)kTopCap) s_top[pos] = key;
+      }
+    }
+    __syncthreads();
+    // Rank them: counting sort by 2048 sub-ranges of key - T_guess from the
+    // top (the key bits are close to log2 |value|, so the sub-ranges stay
+    // small even for a long tail), then each key's place inside its sub-range
+    // by counting.  The key of 1-based rank q lands in s_final[q - 1].
+    const u32 ntop = std::min(s_ntop, (u32)kTopCap);
+    u32* s_sub = s_h;                  // [kSubBins] counts, then fill cursors
+    u32* s_subo = s_h + kSubBins;      // [kSubBins] starts
+    u32* s_sorted = s_keys;            // [ntop] grouped by sub-range
+    u32* s_final = s_keys + kTopCap;   // [ntop] in rank order
+    static_assert(2 * kSubBins <= kHistBins && 2 * kTopCap <= kPlanCap, "LDS");
+    {
+      u32 km = 0;
+      for (u32 i = tid; i < ntop; i += NT) km = std::max(km, s_top[i]);
+      km = wave_max(km);
+      if (lane == 0) atomicMax(&s_kmax, km);
+      for (int i = tid; i < kSubBins; i += NT) s_sub[i] = 0;
+    }
+    __syncthreads();
+    const u32 span = s_kmax - tg + 1u;  // >= 1
+    const int sbits = span <= 1 ? 0 : 32 - __clz(span - 1);
+    const int ssh = sbits > 11 ? sbits - 11 : 0;  // kSubBins = 2^11
+    auto sub_of = [&](u32 x) -> u32 {
+      const u32 d = (x - tg) >> ssh;
+      return (u32)(kSubBins - 1) - (d < (u32)kSubBins ? d : (u32)(kSubBins - 1));
+    };
+    for (u32 i = tid; i < ntop; i += NT) atomicAdd(&s_sub[sub_of(s_top[i])], 1u);
+    __syncthreads();
+    {
+      constexpr int sper = kSubBins / NT;
+      u32 v[sper], own = 0;
 #pragma unroll
-      for (int q2 = 1; q2 <= per2; ++q2) sown += sub[shi - q2];
-      u32 stot;
-      u32 srun = block_exclusive_sum<NT>(sown, s_scan, stot);
+      for (int q2 = 0; q2 < sper; ++q2) {
+        v[q2] = s_sub[tid * sper + q2];
+        own += v[q2];
+      }
+      u32 tot;
+      u32 ex = block_exclusive_sum<NT>(own, s_scan, tot);
 #pragma unroll
-      for (int q2 = 1; q2 <= per2; ++q2) {
-        srun += sub[shi - q2];
-        sub[shi - q2] = srun;
+      for (int q2 = 0; q2 < sper; ++q2) {
+        s_subo[tid * sper + q2] = ex;
+        s_sub[tid * sper + q2] = ex;  // becomes the fill cursor
+        ex += v[q2];
       }
-      __syncthreads();
-      if (tid < ntarget) {
-        const u32 q = rank_of(tid);
-        if ((u32)bin_of_rank(q) == fb) {
-          const u32 want = q - cum_above((int)fb);  // 1-based rank inside the bin
-          int lo = 0, hi2 = kSubN - 1;              // largest sub-bin with suffix >= want
-          while (lo < hi2) {
-            const int mid = (lo + hi2 + 1) >> 1;
-            if (sub[mid] >= want) lo = mid;
-            else hi2 = mid - 1;
-          }
-          s_tkey[tid] = (fb << kHistShift) | ((u32)lo << kSubShift);
-        }
+    }
+    __syncthreads();
+    for (u32 i = tid; i < ntop; i += NT) {
+      const u32 x = s_top[i];
+      s_sorted[atomicAdd(&s_sub[sub_of(x)], 1u)] = x;
+    }
+    __syncthreads();
+    for (u32 i = tid; i < ntop; i += NT) {
+      const u32 x = s_sorted[i];
+      const u32 sb = sub_of(x);
+      const u32 s0 = s_subo[sb], s1 = s_sub[sb];  // the cursor ended at the range's end
+      u32 r = 0;
+      for (u32 t = s0; t < s1; ++t) {
+        const u32 y = s_sorted[t];
+        r += (y > x) | ((y == x) & (t < i));
       }
-      __syncthreads();
+      s_final[s0 + r] = x;
+    }
+    __syncthreads();
+    if (tid >= 1 && tid < (int)nb) {
+      const u32 q = (u32)tid * a.bucket_samples;  // 1-based rank of edge tid - 1
+      if (q <= ntop) s_tkey[tid] = s_final[q - 1];
     }
   }
-  if (tid == 0) {  // monotone edges, each at least T_guess
+  __syncthreads();  // every wanted key is in s_tkey
+  if (w == 0) {  // monotone edges, each at least T_guess (a prefix minimum over lanes)
     const u32 tg = s_tkey[0];
-    u32 prev = 0xFFFFFFFFu;
-    for (int j = 0; j < kMaxBuckets; ++j) {
-      u32 v = 0;
-      if (j + 1 < (int)nb) {
-        v = std::min(std::max(s_tkey[1 + j], tg), prev);
-        prev = v;
-      } else if (j + 1 == (int)nb) {
-        v = tg;
-      }
-      s_lo[j] = v;
-    }
+    const u32 j = (u32)lane;
+    const u32 x = j + 1 < nb ? std::max(s_tkey[1 + j], tg) : 0xFFFFFFFFu;
+    const u32 v = wave_inclusive_min(x);  // every lane takes part
+    s_lo[j] = j + 1 < nb ? v : (j + 1 == nb ? tg : 0u);
   }
   __syncthreads();
   publish_plan(ctl, 1u, s_lo[nb - 1], nb, s_lo, s_scan);
@@ -1056,6 +1058,8 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
   __shared__ int64_t s_next[2];        // next row pair (double-buffered), -1 when none is left
   __shared__ u32 s_pairs[kMaxPairs];  // row pairs this workgroup streamed
   __shared__ u32 s_npairs;
+  __shared__ u32 s_pstate[2];      // plan polling state, by iteration parity
+  __shared__ bool s_plan_in_lds;
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int w = tid / kWave;
@@ -1088,23 +1092,31 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
     sg[j] = sok[j] ? g[i] : 0.0f;
     sr[j] = sok[j] ? r[i] : 0.0f;
   }
-  v4f pg[2], pr[2];
-  if (b > 0 && a.vec) {
+  // two row-pair buffers: A = pair m, B = pair m + M (loads issued now)
+  v4f ag[2], ar[2], bg[2], br[2];
+  auto load_pair = [&](int64_t p, v4f* gg, v4f* rr) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int64_t i = (2 * (int64_t)m + u) * NT + tid;
+      const int64_t i = (2 * p + u) * NT + tid;
       if (i < a.nv) {
-        pg[u] = __builtin_nontemporal_load(gv + i);
-        pr[u] = __builtin_nontemporal_load(rv + i);
+        gg[u] = __builtin_nontemporal_load(gv + i);
+        rr[u] = __builtin_nontemporal_load(rv + i);
       }
     }
+  };
+  if (b > 0 && a.vec) {
+    load_pair(m, ag, ar);
+    load_pair((int64_t)m + M, bg, br);
   }
 
   // ---------------- sample ----------------
   u32 psink = 0;  // returned values of the publishing atomics
+  // The sample keys stay past the list and staging areas (the list fills
+  // while they are published); the histogram is done with before streaming.
+  u32* s_keys = s_raw + 2 * kListCap + 2 * kRegionCap;  // [kSampleKeyCap]
+  static_assert(2 * kListCap + 2 * kRegionCap + kSampleKeyCap <= kRawWords, "LDS");
   {
-    u32* s_h = s_raw;                 // [kHistBins]
-    u32* s_keys = s_raw + kHistBins;  // [kSampleKeyCap]
+    u32* s_h = s_raw;  // [kHistBins]
     for (int i = tid; i < kHistBins; i += NT) s_h[i] = 0;
     for (int i = tid; i < kSampleKeyCap; i += NT) s_keys[i] = kNoKey;
     if (tid == 0) {
@@ -1114,6 +1126,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
       s_ovf = 0;
       s_npub = 0;
       s_npairs = 0;
+      s_plan_in_lds = false;
     }
     if (b == 0) {  // the exact path's state and the error word start at zero
       for (int i = tid; i < a.gstate_words; i += NT) psink += xchg_agent(&a.gstate[i], 0u);
@@ -1145,27 +1158,41 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
       }
     }
     __syncthreads();
-    {  // publish the keys of bins >= floor (at most kPubCap) and the count
-      const u32 floor_bin = s_floor;
-      u32 mine = 0;
-      for (int i = tid; i < kSampleKeyCap; i += NT) {
-        const u32 key = s_keys[i];
-        mine += key != kNoKey && (key >> kHistShift) >= floor_bin;
-      }
-      u32 count;
-      u32 pos = block_exclusive_sum<NT>(mine, s_scan, count);
-      u32* mine_pub = a.pub + (int64_t)b * kPubCap;
-      for (int i = tid; i < kSampleKeyCap; i += NT) {
-        const u32 key = s_keys[i];
-        if (key != kNoKey && (key >> kHistShift) >= floor_bin) {
-          if (pos < (u32)kPubCap) psink += xchg_agent(&mine_pub[pos], key);
-          ++pos;
-        }
-      }
-      if (tid == 0) psink += xchg_agent(&a.pub[kPlanCap + b], std::min(count, 0xFFFFu) | (floor_bin << 16));
-    }
-    __syncthreads();  // s_raw changes role after this
   }
+  // Publishes the sample keys of bins >= floor and their count: first those
+  // of bins above the floor bin (fewer than pub_want, so they always fit),
+  // then those of the floor bin while kPubCap allows.  A workgroup that had
+  // to leave some out is complete from floor + 1 up.  The atomics' returned
+  // values are awaited by sample_arrive.
+  auto sample_publish = [&]() {
+    const u32 floor_bin = s_floor;
+    u32 mine = 0;  // keys above the floor bin (low half) and in it (high half)
+    for (int i = tid; i < kSampleKeyCap; i += NT) {
+      const u32 key = s_keys[i];
+      if (key != kNoKey) {
+        const u32 bin = key >> kHistShift;
+        mine += bin > floor_bin ? 1u : bin == floor_bin ? 0x10000u : 0u;
+      }
+    }
+    u32 count;
+    const u32 pos = block_exclusive_sum<NT>(mine, s_scan, count);
+    const u32 above = count & 0xFFFFu;
+    u32 pos_hi = pos & 0xFFFFu, pos_eq = above + (pos >> 16);
+    u32* mine_pub = a.pub + (int64_t)b * kPubCap;
+    for (int i = tid; i < kSampleKeyCap; i += NT) {
+      const u32 key = s_keys[i];
+      if (key == kNoKey) continue;
+      const u32 bin = key >> kHistShift;
+      if (bin > floor_bin) {
+        psink += xchg_agent(&mine_pub[pos_hi++], key);
+      } else if (bin == floor_bin) {
+        if (pos_eq < (u32)kPubCap) psink += xchg_agent(&mine_pub[pos_eq], key);
+        ++pos_eq;
+      }
+    }
+    const u32 total = above + (count >> 16);
+    if (tid == 0) psink += xchg_agent(&a.pub[kPlanCap + b], std::min(total, 0xFFFFu) | (floor_bin << 16));
+  };
   // Arrival at the sample phase, once this workgroup's published values are
   // all in (waiting for the atomics' returned values).
   auto sample_arrive = [&]() {
@@ -1176,6 +1203,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
 
   if (b == 0) {
     // ---------------- plan ----------------
+    sample_publish();
     sample_arrive();
     step_plan(a, s_raw, s_scan);
     __syncthreads();
@@ -1269,35 +1297,57 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
         }
         return p;
       };
+      // static pairs m, m + M, ...: buffer A holds one, B the next, and the
+      // loads of the pair after go out before a buffer is processed
       if (m < S) {
-        vec_row(2 * (int64_t)m, pg[0], pr[0]);
-        vec_row(2 * (int64_t)m + 1, pg[1], pr[1]);
+        vec_row(2 * (int64_t)m, ag[0], ar[0]);
+        vec_row(2 * (int64_t)m + 1, ag[1], ar[1]);
       }
-      sample_arrive();
-      for (int64_t p = (int64_t)m + M; p < S; p += M) {
-        v4f gg[2], rr[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int64_t i = (2 * p + u) * NT + tid;
-          if (i < a.nv) {
-            gg[u] = __builtin_nontemporal_load(gv + i);
-            rr[u] = __builtin_nontemporal_load(rv + i);
-          }
+      sample_publish();
+      bool arrived = false;
+      for (int64_t p = (int64_t)m + M; p < S; p += 2 * (int64_t)M) {
+        if (p + M < S) load_pair(p + M, ag, ar);
+        vec_row(2 * p, bg[0], br[0]);
+        vec_row(2 * p + 1, bg[1], br[1]);
+        if (!arrived) {
+          sample_arrive();
+          arrived = true;
         }
-        vec_row(2 * p, gg[0], rr[0]);
-        vec_row(2 * p + 1, gg[1], rr[1]);
+        if (p + M >= S) break;
+        if (p + 2 * (int64_t)M < S) load_pair(p + 2 * (int64_t)M, bg, br);
+        vec_row(2 * (p + M), ag[0], ar[0]);
+        vec_row(2 * (p + M) + 1, ag[1], ar[1]);
       }
-      if (tid == 0 && more) pend = add_agent64(&ctl->rows_grp[xs].v, 1u);
+      if (!arrived) sample_arrive();
+      // The plan is usually published while the dynamic pairs stream: thread
+      // 0 polls its flag once per pair (state 1 = seen), and the iteration
+      // after, threads 0..66 load it into LDS (state 2 = in LDS).  The state
+      // is double-buffered by iteration parity like s_next.
+      if (tid == 0) {
+        if (more) pend = add_agent64(&ctl->rows_grp[xs].v, 1u);
+        s_pstate[0] = 0;
+      }
       for (int it = 0;; ++it) {
         if (tid == 0) s_next[it & 1] = next_pair();
         __syncthreads();
         const int64_t p = s_next[it & 1];
-        if (p < 0) break;
+        const u32 pst = s_pstate[it & 1];
+        if (p < 0) {
+          s_plan_in_lds = pst == 2u;
+          break;
+        }
+        u64 pf = 0;
         if (tid == 0) {
           if (more) pend = add_agent64(&ctl->rows_grp[xs].v, 1u);  // the one after
+          if (pst == 0) pf = ld_agent64(&ctl->plan_flag.v);
           if (s_npairs < (u32)kMaxPairs) s_pairs[s_npairs] = (u32)p;
           ++s_npairs;
         }
+        u32 pw = 0;
+        if (pst == 1u && tid < kMaxBuckets + 3)
+          pw = ld_agent(tid < kMaxBuckets ? &ctl->plan.lo[tid] : tid == kMaxBuckets ? &ctl->plan.t_guess
+                                                               : tid == kMaxBuckets + 1 ? &ctl->plan.nbuckets
+                                                                                        : &ctl->plan.valid);
         v4f gg[2], rr[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -1309,11 +1359,17 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
         }
         vec_row(2 * p, gg[0], rr[0]);
         vec_row(2 * p + 1, gg[1], rr[1]);
+        if (pst == 1u && tid < kMaxBuckets + 3) {
+          if (tid < kMaxBuckets) s_lo[tid] = pw;
+          else s_hdr[tid - kMaxBuckets] = pw;
+        }
+        if (tid == 0) s_pstate[(it + 1) & 1] = pst == 0u ? (pf != 0 ? 1u : 0u) : 2u;
       }
       if (m == 0 && tid < a.head) keep_scalar(tid);
       if (m == M - 1)
         for (int64_t i = a.head + 4 * a.nv + tid; i < a.n; i += NT) keep_scalar(i);
     } else {
+      sample_publish();
       sample_arrive();
       constexpr int kU = 8;
       for (int64_t t = m; t < nrows; t += M) {
@@ -1341,12 +1397,16 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
     __syncthreads();
 
     // ---------------- publish ----------------
-    if (tid == 0) s_flag = flag_wait(&ctl->plan_flag, &ctl->err);
-    __syncthreads();
-    if (tid < kMaxBuckets) s_lo[tid] = ld_agent(&ctl->plan.lo[tid]);
-    if (tid == kMaxBuckets) s_hdr[0] = ld_agent(&ctl->plan.t_guess);
-    if (tid == kMaxBuckets + 1) s_hdr[1] = ld_agent(&ctl->plan.nbuckets);
-    if (tid == kMaxBuckets + 2) s_hdr[2] = ld_agent(&ctl->plan.valid);
+    if (!s_plan_in_lds) {
+      if (tid == 0) s_flag = flag_wait(&ctl->plan_flag, &ctl->err);
+      __syncthreads();
+      if (tid < kMaxBuckets) s_lo[tid] = ld_agent(&ctl->plan.lo[tid]);
+      if (tid == kMaxBuckets) s_hdr[0] = ld_agent(&ctl->plan.t_guess);
+      if (tid == kMaxBuckets + 1) s_hdr[1] = ld_agent(&ctl->plan.nbuckets);
+      if (tid == kMaxBuckets + 2) s_hdr[2] = ld_agent(&ctl->plan.valid);
+    } else if (tid == 0) {
+      s_flag = 1;
+    }
     if (tid < kMaxBuckets) s_bcnt[tid] = 0;
     __syncthreads();
     const bool plan_ok = s_flag != 0 && s_hdr[2] == 1u && s_hdr[1] >= 1 && s_hdr[1] <= (u32)kMaxBuckets;

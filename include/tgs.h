@@ -142,7 +142,13 @@ const char* tgs_last_error(void);
  * concurrent calls).
  *   TGS_OPT_TOPK_PATH   0 = automatic, 1 = always the exact general path,
  *                       2 = fast path with a sample plan that cannot hold
- *                       (exercises the on-device fallback).
+ *                       (exercises the on-device fallback),
+ *                       3 = fast path whose workgroups keep no local list
+ *                       while streaming (every workgroup re-reads its rows),
+ *                       4 = fast path whose workgroups keep every entry in
+ *                       their local list (it overflows; they re-read),
+ *                       5 = fast path whose workgroups may publish only one
+ *                       candidate each (the plan fails; on-device fallback).
  *   TGS_OPT_MAIN_GRID   0 = automatic, else the number of workgroups of the
  *                       streaming launch, capped at what can be resident;
  *                       below 65 the exact path runs (results must not

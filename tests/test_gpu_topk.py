@@ -97,11 +97,14 @@ def test_fast_path_sizes(tgs_gpu, n, ks, dist):
         assert_topk_equal(gpu_topk(tgs_gpu, grad, res, k), oracle_topk(grad, res, k), "n=%d k=%d %s" % (n, k, dist))
 
 
-@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("path", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("dist", ["normal", "ties", "special"])
 def test_forced_general_and_fallback(tgs_gpu, path, dist):
-    """path 1: the exact general path only; path 2: fast path whose plan cannot
-    hold, so the on-device fallback produces the result."""
+    """path 1: the exact general path only; 2: fast path whose plan cannot
+    hold, so the on-device fallback produces the result; 3 and 4: fast path
+    whose streaming workgroups must re-read their rows (no local list, or an
+    overflowing one); 5: fast path whose workgroups cannot publish their
+    candidates (fallback)."""
     tgs_gpu.set_option(tgs_gpu.OPT_TOPK_PATH, path)
     rng = np.random.default_rng(31 + path)
     n = 1_000_003
@@ -246,3 +249,61 @@ def test_large_transformer_sized_invariants(tgs_gpu, residual_kind):
     acc = res_h + grad_h
     del grad_h, res_h
     check_topk_invariants(acc, r_after, idx_h, val_h, k)
+
+
+def _ctl(ws):
+    """(verdict, fallbacks, why, rescans) words at the start of a top-k workspace."""
+    w = host(ws[:24].view(torch.int32))
+    return int(w[2]), int(w[3]), int(w[4]), int(w[5])
+
+
+@pytest.mark.parametrize("path,route", [(0, "fast"), (3, "reread"), (4, "reread"), (2, "fallback"), (5, "fallback")])
+def test_fast_path_routes(tgs_gpu, path, route):
+    """Each route through the single-launch step: the plan holds; workgroups
+    re-read their rows (no list / overflowing list); the plan fails and the
+    exact path runs on the same launch.  Results always match the oracle."""
+    rng = np.random.default_rng(17)
+    n, k = 4_000_000, 4000  # shares of ~15.7K entries: more than a local list holds when T_loc = 0
+    grad, res = make("mixture", n, rng)
+    exp = oracle_topk(grad, res, k)
+    tgs_gpu.set_option(tgs_gpu.OPT_TOPK_PATH, path)
+    g, r = gpu(grad), gpu(res)
+    ws = torch.zeros(tgs_gpu.topk_workspace_bytes(n, k), dtype=torch.uint8, device="cuda")
+    idx, val = tgs_gpu.topk_ef_step(g, r, k, ws=ws)
+    tgs_gpu.check_device_error(ws)
+    assert_topk_equal((host(idx), host(val), host(r)), exp, "path=%d" % path)
+    verdict, fallbacks, why, rescans = _ctl(ws)
+    if route == "fast":
+        assert verdict == 1 and fallbacks == 0 and rescans == 0
+    elif route == "reread":
+        assert verdict == 1 and fallbacks == 0 and rescans > 0
+    else:
+        assert verdict == 0 and fallbacks == 1 and why != 0
+
+
+def test_workspace_shared_by_all_operations(tgs_gpu):
+    """One zero-filled buffer serves top-k, threshold and gTop-k calls in turn
+    (each operation leaves the top-k counters clean), with grids that change
+    from one top-k call to the next."""
+    rng = np.random.default_rng(23)
+    n, k = 1_500_000, 1500
+    need = max(tgs_gpu.topk_workspace_bytes(n, k), tgs_gpu.threshold_workspace_bytes(n),
+               tgs_gpu.gtopk_workspace_bytes(4, 512, n))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    r_gpu = torch.zeros(n, dtype=torch.float32, device="cuda")
+    r_cpu = np.zeros(n, np.float32)
+    for step, grid in enumerate([0, 100, 0, 256, 80, 0]):
+        tgs_gpu.set_option(tgs_gpu.OPT_MAIN_GRID, grid)
+        grad = rng.standard_normal(n).astype(np.float32)
+        idx, val = tgs_gpu.topk_ef_step(gpu(grad), r_gpu, k, ws=ws)
+        tgs_gpu.check_device_error(ws)
+        ei, ev = oracle.topk_ef_step(grad, r_cpu, k)
+        assert_topk_equal((host(idx), host(val), host(r_gpu)), (ei, ev, r_cpu), "step %d grid %d" % (step, grid))
+        if step % 2 == 0:  # another operation on the same buffer in between
+            g2 = rng.standard_normal(n).astype(np.float32)
+            r2 = torch.zeros(n, dtype=torch.float32, device="cuda")
+            tgs_gpu.threshold_ef_step(gpu(g2), r2, 2.5, 4096, ws=ws)
+            tgs_gpu.check_device_error(ws)
+            gi, gv = workloads.gtopk_sets(P=4, k=512, n=n, hot=1024)
+            tgs_gpu.gtopk_merge(gpu(gi), gpu(gv), n, ws=ws)
+            tgs_gpu.check_device_error(ws)

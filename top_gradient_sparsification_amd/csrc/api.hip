@@ -2,7 +2,9 @@
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
+#include <map>
 #include <mutex>
+#include <utility>
 
 #include "tgs_host.h"
 
@@ -46,6 +48,28 @@ int device_cu_count() {
   return v;
 }
 
+// Launch parity per (device, workspace): which of the top-k control block's
+// two counter sets the next fast-path launch on that workspace uses.
+static std::mutex g_parity_mu;
+static std::map<std::pair<int, uintptr_t>, uint32_t> g_parity;
+
+static std::pair<int, uintptr_t> parity_key(const void* workspace) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  return {dev, (uintptr_t)workspace};
+}
+
+uint32_t launch_parity(const void* workspace) {
+  std::lock_guard<std::mutex> lk(g_parity_mu);
+  auto it = g_parity.find(parity_key(workspace));
+  return it == g_parity.end() ? 0u : it->second;
+}
+
+void advance_parity(const void* workspace) {
+  std::lock_guard<std::mutex> lk(g_parity_mu);
+  g_parity[parity_key(workspace)] ^= 1u;
+}
+
 static std::mutex g_prof_mu;
 static hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
 
@@ -76,7 +100,7 @@ extern "C" const char* tgs_last_error(void) { return t_last_error; }
 extern "C" tgs_status tgs_set_option(int32_t option, int64_t value) {
   switch (option) {
     case TGS_OPT_TOPK_PATH:
-      if (value < 0 || value > 2) return fail(TGS_EINVAL, "TGS_OPT_TOPK_PATH takes 0, 1 or 2");
+      if (value < 0 || value > 5) return fail(TGS_EINVAL, "TGS_OPT_TOPK_PATH takes 0 .. 5");
       g_opt_path.store(value);
       return TGS_OK;
     case TGS_OPT_MAIN_GRID:

@@ -21,6 +21,13 @@ int64_t get_option(int32_t option);
 // Compute units of the current device (cached per device; 0 on failure).
 int device_cu_count();
 
+// Which of the top-k control block's two counter sets the next fast-path
+// launch on `workspace` (current device) uses; advance_parity flips it after a
+// launch went out.  A workspace the library has not seen starts at 0 (both
+// sets of a zero-filled workspace are clean).
+uint32_t launch_parity(const void* workspace);
+void advance_parity(const void* workspace);
+
 // Hands out (and clears) the events set by tgs_profile_next_call; null when
 // none are pending.
 void take_profile_events(hipEvent_t* start, hipEvent_t* stop);

@@ -21,10 +21,10 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 
 // Every workspace starts with this header; its first word is the device error
-// word.  The top-k step keeps its control block (counters that are zero
-// between calls) here; the other operations touch only the error word, so a
+// word.  The top-k step keeps its control block (two sets of counters used by
+// alternate calls) here; the other operations touch only the error word, so a
 // workspace can move between operations without clearing it.
-constexpr size_t kWorkspaceHeader = 8192;
+constexpr size_t kWorkspaceHeader = 32768;
 
 // ---------------------------------------------------------------- keys ----
 __device__ __forceinline__ u32 key_of_bits(u32 b) { return b & 0x7FFFFFFFu; }

@@ -99,8 +99,31 @@ struct alignas(128) Counter {  // one cache line each
   u64 pad[15];
 };
 
-// Start of every top-k workspace.  The counters are zero between calls: the
-// last workgroup to leave a k_step launch clears them.
+// The counters one k_step launch synchronises with; zero when it starts.
+// Flags many workgroups wait on are written to 8 lines and each workgroup
+// polls the one of its group (blockIdx % 8): same-address accesses serialise
+// at the memory, and a few hundred pollers on one line would slow down
+// everything else that goes there.
+struct StepSet {
+  Counter samp_grp[8], samp_all;  // sample phase arrivals (workgroup 0 polls samp_all)
+  Counter main_grp[8], main_all;  // streaming workgroups published
+  Counter main_go[8];             // 1 once main_all is complete
+  Counter rows_grp[8];            // row pairs handed out per group of streaming workgroups
+  Counter plan_flag[8];           // 1 once the plan is published
+  Counter last_rank[8];           // 1 + the rank key of the k-th entry, once known
+  Counter verdict_flag[8];        // 1 = the plan held, 2 = run the exact path
+  Counter bad;                    // low word: OR of kWhy* failures seen by the streaming workgroups
+};
+
+// Thread 0 only: sets all 8 copies of a replicated flag (no wait).
+__device__ __forceinline__ void flag_set(Counter* f, u64 v) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) xchg_agent64(&f[i].v, v);
+}
+
+// Start of every top-k workspace.  Launches alternate between the two
+// counter sets (the host passes the parity); workgroup 0 of each launch
+// clears the set the next launch uses, which no one else touches meanwhile.
 struct StepCtl {
   u32 err;        // device error word (offset 0 of every workspace)
   u32 pad0;
@@ -109,14 +132,7 @@ struct StepCtl {
   u32 why;        // OR of kWhy* reasons over those calls (never reset)
   u32 rescans;    // workgroup shares re-read because their list was incomplete (never reset)
   u32 pad1[58];
-  Counter samp_grp[8], samp_all;
-  Counter main_grp[8], main_all;
-  Counter exit_grp[8], exit_all;
-  Counter rows_grp[8];   // row pairs handed out per group of streaming workgroups
-  Counter plan_flag;     // 1 once the plan is published
-  Counter last_rank;     // 1 + the rank key of the k-th entry, once known
-  Counter verdict_flag;  // 1 = the plan held, 2 = run the exact path
-  Counter bad;           // low word: OR of kWhy* failures seen by the streaming workgroups
+  StepSet set[2];
   Plan plan;
 };
 static_assert(sizeof(StepCtl) <= kWorkspaceHeader, "control block exceeds the workspace header");
@@ -524,6 +540,9 @@ struct StepArgs {
   u32 pub_want;                  // sample keys each workgroup publishes at least
   u32 loc_q16;                   // T_loc: rank fraction of the local sample, in 1/65536
   u32 break_plan;                // test hook: publish a plan that cannot hold
+  u32 loc_mode;                  // test hook: 1 = T_loc above every key, 2 = T_loc = 0
+  u32 region_cap;                // candidates one workgroup may publish (kRegionCap; less to test)
+  u32 parity;                    // which counter set this launch uses
   StepCtl* ctl;
   u32* pub;      // [kMaxStepBlocks][kPubCap] keys, then [kMaxStepBlocks] count | floor << 16
   u32* rcnt;     // [kMaxStepBlocks][kMaxBuckets / 2] bucket counts, two u16 per word
@@ -557,7 +576,8 @@ __device__ __forceinline__ void list_keep(Pair* s_list, u32* s_nlist, u32* s_ovf
 
 // Publishes a plan (all threads of workgroup 0): words with returning device
 // atomics, then the flag once they are all done.
-__device__ __forceinline__ void publish_plan(StepCtl* ctl, u32 valid, u32 tg, u32 nb, const u32* lo, u32* s_scan) {
+__device__ __forceinline__ void publish_plan(StepCtl* ctl, StepSet* cs, u32 valid, u32 tg, u32 nb, const u32* lo,
+                                             u32* s_scan) {
   const int tid = threadIdx.x;
   u32 sink = 0;
   if (tid < kMaxBuckets) sink += xchg_agent(&ctl->plan.lo[tid], lo[tid]);
@@ -566,7 +586,7 @@ __device__ __forceinline__ void publish_plan(StepCtl* ctl, u32 valid, u32 tg, u3
   if (tid == kMaxBuckets + 2) sink += xchg_agent(&ctl->plan.valid, valid);
   if (sink == 0x12345678u) s_scan[kStepWaves] = sink;  // keeps the returned values live
   __syncthreads();
-  if (tid == 0) xchg_agent64(&ctl->plan_flag.v, 1u);
+  if (tid == 0) flag_set(cs->plan_flag, 1u);
 }
 
 // Workgroup 0: the published sample keys -> plan.
@@ -599,8 +619,9 @@ __device__ __forceinline__ void step_plan(const StepArgs& a, u32* s_raw, u32* s_
   const int w = tid / kWave;
   const int G = gridDim.x;
   StepCtl* ctl = a.ctl;
+  StepSet* cs = &ctl->set[a.parity];
   if (tid == 0) {
-    s_ok = phase_wait(&ctl->samp_all, G, &ctl->err) ? 1u : 0u;
+    s_ok = phase_wait(&cs->samp_all, G, &ctl->err) ? 1u : 0u;
     s_maxfloor = 0;
     s_kmax = 0;
     s_bT = 0xFFFFFFFFu;
@@ -664,7 +685,7 @@ __device__ __forceinline__ void step_plan(const StepArgs& a, u32* s_raw, u32* s_
     const u32 tg = a.break_plan ? 0x7FFFFFFFu : 0xFFFFFFFFu;
     if (tid < kMaxBuckets) s_lo[tid] = tid == 0 ? tg : 0u;
     __syncthreads();
-    publish_plan(ctl, a.break_plan ? 1u : 0u, tg, 1u, s_lo, s_scan);
+    publish_plan(ctl, cs, a.break_plan ? 1u : 0u, tg, 1u, s_lo, s_scan);
     return;
   }
   const int ntarget = (int)nb;  // wanted ranks: [0] c_target, [j] j * bucket_samples for 1 <= j < nb
@@ -808,7 +829,7 @@ __device__ __forceinline__ void step_plan(const StepArgs& a, u32* s_raw, u32* s_
     s_lo[j] = j + 1 < nb ? v : (j + 1 == nb ? tg : 0u);
   }
   __syncthreads();
-  publish_plan(ctl, 1u, s_lo[nb - 1], nb, s_lo, s_scan);
+  publish_plan(ctl, cs, 1u, s_lo[nb - 1], nb, s_lo, s_scan);
 }
 
 // Finisher f (workgroups 0..63), once every workgroup has published: the
@@ -834,6 +855,7 @@ __device__ __forceinline__ bool step_finish(const StepArgs& a, u32* s_raw, u32* 
   const int f = blockIdx.x;
   const int G = gridDim.x;
   StepCtl* ctl = a.ctl;
+  StepSet* cs = &ctl->set[a.parity];
   __syncthreads();  // s_raw changes role
   // The plan is final before any workgroup publishes (every streaming
   // workgroup waited for it), so it is read while waiting for the others.
@@ -842,7 +864,7 @@ __device__ __forceinline__ bool step_finish(const StepArgs& a, u32* s_raw, u32* 
   if (tid == kMaxBuckets + 1) s_phdr[1] = ld_agent(&ctl->plan.nbuckets);
   if (tid == kMaxBuckets + 2) s_phdr[2] = ld_agent(&ctl->plan.valid);
   if (tid == 0) {
-    s_wait = phase_wait(&ctl->main_all, G, &ctl->err) ? 1u : 0u;
+    s_wait = flag_wait(&cs->main_go[blockIdx.x & 7], &ctl->err) != 0 ? 1u : 0u;
     s_nrows = 0;
     s_kmin = 0xFFFFFFFFu;
     s_kmax = 0;
@@ -865,7 +887,7 @@ __device__ __forceinline__ bool step_finish(const StepArgs& a, u32* s_raw, u32* 
       const int wd = tid + it * NT;
       xw[it] = (wd >= kWords && wd < nwords) ? ld_agent(&a.rcnt[wd]) : 0u;
     }
-    if (tid == 0) s_seen = ld_agent((const u32*)&ctl->bad.v);
+    if (tid == 0) s_seen = ld_agent((const u32*)&cs->bad.v);
 #pragma unroll
     for (int it = 0; it < kIters; ++it) s_cm[tid + it * NT] = xw[it];
   }
@@ -928,7 +950,7 @@ __device__ __forceinline__ bool step_finish(const StepArgs& a, u32* s_raw, u32* 
           ctl->fallbacks += 1u;
           ctl->why |= (plan_ok ? 0u : kWhyPlan) | seen | (any_bad ? kWhyBucket : 0u) | (all >= a.k ? 0u : kWhyFew);
         }
-        xchg_agent64(&ctl->verdict_flag.v, valid ? 1u : 2u);
+        flag_set(cs->verdict_flag, valid ? 1u : 2u);
       }
     }
   }
@@ -1038,7 +1060,7 @@ __device__ __forceinline__ bool step_finish(const StepArgs& a, u32* s_raw, u32* 
       a.out_val[mystart + p] = __uint_as_float(e.bits);
     }
     // the k-th entry: every workgroup zeroes its own entries ranked up to it
-    if (mystart + p == a.k - 1) xchg_agent64(&ctl->last_rank.v, re + 1u);
+    if (mystart + p == a.k - 1) flag_set(cs->last_rank, re + 1u);
   }
   return true;
 }
@@ -1067,6 +1089,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
   const int b = blockIdx.x;
   const int M = G - 1, m = b - 1;  // streaming workgroups and this one's rank among them
   StepCtl* ctl = a.ctl;
+  StepSet* cs = &ctl->set[a.parity];
   float* __restrict__ r = a.residual;
   const float* __restrict__ g = a.grad;
   const v4f* __restrict__ gv = (const v4f*)(g + a.head);
@@ -1128,9 +1151,13 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
       s_npairs = 0;
       s_plan_in_lds = false;
     }
-    if (b == 0) {  // the exact path's state and the error word start at zero
+    if (b == 0) {  // the exact path's state and the error word start at zero; the
+                   // other counter set is cleared for the next launch
       for (int i = tid; i < a.gstate_words; i += NT) psink += xchg_agent(&a.gstate[i], 0u);
       if (tid == 0) psink += xchg_agent(&ctl->err, 0u);
+      constexpr int kSetWords = (int)(sizeof(StepSet) / sizeof(Counter));
+      Counter* other = (Counter*)&ctl->set[a.parity ^ 1u];
+      if (tid < kSetWords) psink += (u32)xchg_agent64(&other[tid].v, 0u);
     }
     __syncthreads();
 #pragma unroll
@@ -1198,7 +1225,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
   auto sample_arrive = [&]() {
     if (psink == 0x12345678u) s_scan[NW] = psink;  // keeps the returned values live
     __syncthreads();
-    if (tid == 0) phase_arrive(ctl->samp_grp, &ctl->samp_all, G);
+    if (tid == 0) phase_arrive(cs->samp_grp, &cs->samp_all, G);
   };
 
   if (b == 0) {
@@ -1207,10 +1234,10 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
     sample_arrive();
     step_plan(a, s_raw, s_scan);
     __syncthreads();
-    if (tid == 0) phase_arrive(ctl->main_grp, &ctl->main_all, G);
+    if (tid == 0 && phase_arrive(cs->main_grp, &cs->main_all, G)) flag_set(cs->main_go, 1u);
   } else {
     // ---------------- stream ----------------
-    const u32 tloc = s_tlocbin << kHistShift;
+    const u32 tloc = a.loc_mode == 1u ? 0x7FFFFFFFu : a.loc_mode == 2u ? 0u : s_tlocbin << kHistShift;
     Pair* s_list = (Pair*)s_raw;                  // [kListCap]
     Pair* s_pub = (Pair*)(s_raw + 2 * kListCap);  // [kRegionCap]
     static_assert(2 * kListCap + 2 * kRegionCap <= kRawWords, "LDS");
@@ -1275,7 +1302,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
         for (int attempt = 0; p >= npairs && attempt < 16; ++attempt) {
           u64 c[8];
 #pragma unroll
-          for (int x = 0; x < 8; ++x) c[x] = x < ng ? ld_agent64(&ctl->rows_grp[x].v) : 0u;
+          for (int x = 0; x < 8; ++x) c[x] = x < ng ? ld_agent64(&cs->rows_grp[x].v) : 0u;
           u64 best_left = 0;
           int best = -1;
           for (int x = 0; x < ng; ++x) {
@@ -1288,7 +1315,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
           }
           if (best < 0) break;
           xs = (u32)best;
-          pend = add_agent64(&ctl->rows_grp[xs].v, 1u);
+          pend = add_agent64(&cs->rows_grp[xs].v, 1u);
           p = S + (int64_t)xs + (int64_t)ng * (int64_t)pend;
         }
         if (p >= npairs) {
@@ -1324,7 +1351,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
       // after, threads 0..66 load it into LDS (state 2 = in LDS).  The state
       // is double-buffered by iteration parity like s_next.
       if (tid == 0) {
-        if (more) pend = add_agent64(&ctl->rows_grp[xs].v, 1u);
+        if (more) pend = add_agent64(&cs->rows_grp[xs].v, 1u);
         s_pstate[0] = 0;
       }
       for (int it = 0;; ++it) {
@@ -1338,8 +1365,8 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
         }
         u64 pf = 0;
         if (tid == 0) {
-          if (more) pend = add_agent64(&ctl->rows_grp[xs].v, 1u);  // the one after
-          if (pst == 0) pf = ld_agent64(&ctl->plan_flag.v);
+          if (more) pend = add_agent64(&cs->rows_grp[xs].v, 1u);  // the one after
+          if (pst == 0) pf = ld_agent64(&cs->plan_flag[blockIdx.x & 7].v);
           if (s_npairs < (u32)kMaxPairs) s_pairs[s_npairs] = (u32)p;
           ++s_npairs;
         }
@@ -1398,7 +1425,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
 
     // ---------------- publish ----------------
     if (!s_plan_in_lds) {
-      if (tid == 0) s_flag = flag_wait(&ctl->plan_flag, &ctl->err);
+      if (tid == 0) s_flag = flag_wait(&cs->plan_flag[blockIdx.x & 7], &ctl->err);
       __syncthreads();
       if (tid < kMaxBuckets) s_lo[tid] = ld_agent(&ctl->plan.lo[tid]);
       if (tid == kMaxBuckets) s_hdr[0] = ld_agent(&ctl->plan.t_guess);
@@ -1464,7 +1491,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
     __syncthreads();
     const u32 C = s_npub;
     u32 sink = 0;
-    if (C <= (u32)kRegionCap && !(fail & kWhyList)) {
+    if (C <= a.region_cap && !(fail & kWhyList)) {
       for (u32 i = tid; i < nl; i += NT) {
         const Pair e = s_list[i];
         const u32 key = key_of_bits(e.bits);
@@ -1482,10 +1509,10 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
       __syncthreads();
       if (tid == 0) s_npub = 0;
     }
-    if (tid == 0 && fail) sink += or_agent((u32*)&ctl->bad.v, fail);
+    if (tid == 0 && fail) sink += or_agent((u32*)&cs->bad.v, fail);
     if (sink == 0x12345678u) s_scan[NW] = sink;  // keeps the returned values live
     __syncthreads();
-    if (tid == 0) phase_arrive(ctl->main_grp, &ctl->main_all, G);
+    if (tid == 0 && phase_arrive(cs->main_grp, &cs->main_all, G)) flag_set(cs->main_go, 1u);
   }
 
   // ---------------- finish ----------------
@@ -1493,7 +1520,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
   if (b < kMaxBuckets) {
     verdict = step_finish(a, s_raw, s_scan) ? 1u : 2u;
   } else {
-    if (tid == 0) s_flag = flag_wait(&ctl->verdict_flag, &ctl->err);
+    if (tid == 0) s_flag = flag_wait(&cs->verdict_flag[blockIdx.x & 7], &ctl->err);
     __syncthreads();
     verdict = s_flag;
   }
@@ -1506,7 +1533,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
       if (tid == 0) {
         u32 spins = 0;
         u64 v;
-        while ((v = ld_agent64(&ctl->last_rank.v)) == 0) {
+        while ((v = ld_agent64(&cs->last_rank[blockIdx.x & 7].v)) == 0) {
           __builtin_amdgcn_s_sleep(2);
           if (++spins > kSpinLimit) {
             atomicOr(&ctl->err, kErrBarrierTimeout);
@@ -1531,23 +1558,6 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
     if (grid_sync(a.gen.bar)) general_path<NT>(a.gen);
   }
 
-  // ---------------- exit: the last workgroup clears the counters ----------------
-  __syncthreads();
-  if (tid == 0 && phase_arrive(ctl->exit_grp, &ctl->exit_all, G)) {
-    for (int i = 0; i < 8; ++i) {
-      xchg_agent64(&ctl->samp_grp[i].v, 0u);
-      xchg_agent64(&ctl->main_grp[i].v, 0u);
-      xchg_agent64(&ctl->exit_grp[i].v, 0u);
-      xchg_agent64(&ctl->rows_grp[i].v, 0u);
-    }
-    xchg_agent64(&ctl->samp_all.v, 0u);
-    xchg_agent64(&ctl->main_all.v, 0u);
-    xchg_agent64(&ctl->exit_all.v, 0u);
-    xchg_agent64(&ctl->plan_flag.v, 0u);
-    xchg_agent64(&ctl->last_rank.v, 0u);
-    xchg_agent64(&ctl->verdict_flag.v, 0u);
-    xchg_agent64(&ctl->bad.v, 0u);
-  }
 }
 
 }  // namespace tgs
@@ -1688,6 +1698,9 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
     sa.out_idx = out_idx;
     sa.out_val = out_val;
     sa.break_plan = path == 2 ? 1u : 0u;
+    sa.loc_mode = path == 3 ? 1u : path == 4 ? 2u : 0u;
+    sa.region_cap = path == 5 ? 1u : (u32)kRegionCap;
+    sa.parity = launch_parity(workspace);
     sa.ctl = ctl;
     sa.pub = (u32*)(ws + L.pub);
     sa.rcnt = (u32*)(ws + L.rcnt);
@@ -1697,6 +1710,7 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
     sa.gen = ga;
     sa.gen.bar.nwg = (u32)G;
     hipLaunchKernelGGL(k_step, dim3(G), dim3(kStepThreads), 0, stream, sa);
+    if (hipPeekAtLastError() == hipSuccess) advance_parity(workspace);
   } else {
     AccArgs aa{};
     aa.grad = grad;

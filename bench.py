@@ -50,14 +50,14 @@ def parse():
 
 # HBM bytes per k_step launch from two rocprofv3 --pmc runs of this script
 # (FETCH_SIZE, then WRITE_SIZE), each scaled by what the same counter read for
-# the 256 MiB copy of --copy-calibration.  Valid only for the streaming-pass
+# the 256 MiB copy of --copy-calibration.  Valid only for the k_step
 # source they were taken on: `source_sha256` is the hash of csrc/topk.hip then.
 MEASURED_TRAFFIC = {
-    "source_sha256": "db00ee30b428f29c20b4044aeeeae395bfad21c89b1f502209bcab6278a52513",
-    # FETCH_SIZE 100,042.5 KiB x (262,144 / 131,083.5: the copy's true read over its counter)
-    "fetch_bytes": 204_869_065,
-    # WRITE_SIZE 101,168.7 KiB x 1.0 (the copy's counter read exactly 262,144 KiB)
-    "write_bytes": 103_596_749,
+    "source_sha256": "18e74f5749af09601fc723f31d2de7475b37dc2e484c67cffedf235ce9eb2f16",
+    # FETCH_SIZE 102,637.6 KiB x (262,144 / 131,083.5: the copy's true read over its counter)
+    "fetch_bytes": 210_183_415,
+    # WRITE_SIZE 101,850.8 KiB x 1.0 (the copy's counter read exactly 262,144 KiB)
+    "write_bytes": 104_295_168,
 }
 
 

@@ -9,7 +9,7 @@
 //
 // Fast path: ONE launch, k_step, one workgroup of 1024 threads per compute
 // unit, every workgroup resident.  Workgroup 0 plans; workgroups 1..G-1 each
-// stream one contiguous share of the vector; workgroups 0..63 finish.
+// stream their share of the vector; workgroups 0..63 finish.
 //   sample   every workgroup reads ~1/G of a ~1% sample (64-element chunks
 //            spread over the whole vector) into a 12-bit LDS histogram of
 //            key >> 19.  It publishes its top sample keys (device atomics) and
@@ -19,25 +19,34 @@
 //            T_guess (about 1.4k entries expected above it) and up to 64
 //            bucket boundaries between T_guess and the top.  It publishes
 //            the plan while the others stream.
-//   stream   acc = residual + grad, one pass.  Entries with key < T_loc go
-//            straight back to residual (non-temporal float4 stores); the
-//            others are kept in an LDS list and their residual is left for
-//            later.  Nothing waits for the plan here.
-//   publish  at the end of its share a workgroup reads the plan, writes
-//            back the list entries below T_guess, sorts the rest (the
-//            candidates) by bucket and publishes them with device atomics.
+//   stream   acc = residual + grad, one pass over rows of 1024 float4, two
+//            rows at a time.  About three quarters of the row pairs are dealt
+//            out statically, the rest are handed out at run time from eight
+//            counters (so workgroups that started late or run slow take
+//            fewer).  Every acc goes back to residual as a whole float4
+//            (non-temporal; partial lines would cost far more), and entries
+//            with key >= T_loc are also appended to an LDS list.  Nothing
+//            waits for the plan here.
+//   publish  at the end of its share a workgroup reads the plan, keeps the
+//            list entries with key >= T_guess (the candidates), groups them
+//            by bucket and publishes them and their per-bucket counts with
+//            device atomics.  A workgroup whose list overflowed, or whose
+//            T_loc lay above T_guess, first re-reads its own rows of residual.
 //   finish   finisher f waits for every workgroup, adds up the bucket counts,
 //            checks that the plan held (at least k candidates, every bucket
 //            that holds a rank below k fits in LDS, nothing overflowed),
-//            gathers bucket f, orders it by (key desc, index asc), writes the
-//            entries of rank < k to the output and every candidate's residual
-//            (+0 for the selected, acc for the rest).
+//            gathers bucket f, orders it by (key desc, index asc) and writes
+//            the entries of rank < k to the output.  The finisher that holds
+//            rank k-1 publishes its composite key R.
+//   zero     each streaming workgroup sets to +0 the residual of those of its
+//            own candidates whose composite key is <= R.  It wrote their acc
+//            itself, so its own two stores reach memory in order.
 // No residual word is written by two workgroups and everything one
 // workgroup reads from another goes through device-scope atomics, so the
 // fast path needs no cache write-back fences.
 //
-// When the plan did not hold, every workgroup writes back the acc of what it
-// published, fences, and the whole grid runs the exact general path below.
+// When the plan did not hold, residual already holds acc everywhere: the
+// grid fences, meets at a barrier and runs the exact general path below.
 //
 // General path (grid barriers; the fast path's fallback, and a launch of its
 // own, k_general, where the fast path does not apply):

@@ -148,7 +148,10 @@ const char* tgs_last_error(void);
  *                       4 = fast path whose workgroups keep every entry in
  *                       their local list (it overflows; they re-read),
  *                       5 = fast path whose workgroups may publish only one
- *                       candidate each (the plan fails; on-device fallback).
+ *                       candidate each (the plan fails; on-device fallback),
+ *                       6 = fast path with one fixed slot per bucket and
+ *                       workgroup (nearly every candidate goes through the
+ *                       overflow area).
  *   TGS_OPT_MAIN_GRID   0 = automatic, else the number of workgroups of the
  *                       streaming launch, capped at what can be resident;
  *                       below 65 the exact path runs (results must not

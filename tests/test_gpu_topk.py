@@ -97,14 +97,15 @@ def test_fast_path_sizes(tgs_gpu, n, ks, dist):
         assert_topk_equal(gpu_topk(tgs_gpu, grad, res, k), oracle_topk(grad, res, k), "n=%d k=%d %s" % (n, k, dist))
 
 
-@pytest.mark.parametrize("path", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("path", [1, 2, 3, 4, 5, 6])
 @pytest.mark.parametrize("dist", ["normal", "ties", "special"])
 def test_forced_general_and_fallback(tgs_gpu, path, dist):
     """path 1: the exact general path only; 2: fast path whose plan cannot
     hold, so the on-device fallback produces the result; 3 and 4: fast path
     whose streaming workgroups must re-read their rows (no local list, or an
     overflowing one); 5: fast path whose workgroups cannot publish their
-    candidates (fallback)."""
+    candidates (fallback); 6: fast path with one slot per bucket and
+    workgroup (candidates go through the overflow area)."""
     tgs_gpu.set_option(tgs_gpu.OPT_TOPK_PATH, path)
     rng = np.random.default_rng(31 + path)
     n = 1_000_003
@@ -257,9 +258,11 @@ def _ctl(ws):
     return int(w[2]), int(w[3]), int(w[4]), int(w[5])
 
 
-@pytest.mark.parametrize("path,route", [(0, "fast"), (3, "reread"), (4, "reread"), (2, "fallback"), (5, "fallback")])
+@pytest.mark.parametrize("path,route", [(0, "fast"), (6, "fast"), (3, "reread"), (4, "reread"), (2, "fallback"),
+                                        (5, "fallback")])
 def test_fast_path_routes(tgs_gpu, path, route):
-    """Each route through the single-launch step: the plan holds; workgroups
+    """Each route through the single-launch step: the plan holds (with the
+    usual slots, or with one slot so that candidates overflow); workgroups
     re-read their rows (no list / overflowing list); the plan fails and the
     exact path runs on the same launch.  Results always match the oracle."""
     rng = np.random.default_rng(17)

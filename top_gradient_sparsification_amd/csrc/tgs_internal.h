@@ -78,6 +78,24 @@ __device__ __forceinline__ u64 xchg_agent64(u64* p, u64 v) {
 __device__ __forceinline__ u32 or_agent(u32* p, u32 v) {
   return __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void st_agent_f32(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// A float4 store made at device scope (written through to where every XCD
+// sees it, as the device-scope atomics are), with the streaming hint: a raw
+// buffer store with the sc1 and nt cache-policy bits.  `base` must be the same
+// in every lane of the wave; lanes whose byte offset lies at or beyond
+// `nbytes` store nothing.  Once a wave has waited for its stores to complete
+// (s_waitcnt vmcnt(0)), a store another workgroup makes to the same address
+// after hearing from it through a device-scope atomic lands later.
+constexpr int kPolicyNtSc1 = 2 | 16;  // cache-policy bits: nt = 2, sc1 = 16
+__device__ __forceinline__ void st_agent_v4_nt(v4f* base, u32 nbytes, u32 off, v4f v) {
+  typedef u32 v4u __attribute__((ext_vector_type(4)));
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)nbytes, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), rs, (int)off, 0, kPolicyNtSc1);
+}
+// Waits until every memory access this wave issued has completed.
+__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
 // ------------------------------------------------- wave scans (DPP) ----
 // Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and

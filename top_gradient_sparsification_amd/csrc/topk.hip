@@ -76,7 +76,8 @@ constexpr int kSampleKeyCap = kSampleRounds * kStepThreads;  // sample keys per 
 constexpr int kPubCap = 40;                         // sample keys one workgroup may publish
 constexpr int kPlanCap = kPubCap * kMaxStepBlocks;  // 10240
 constexpr int kListCap = 8192;                      // local list of one workgroup (LDS)
-constexpr int kRegionCap = 4096;                    // candidates one workgroup may publish
+constexpr int kSlotTotal = 4096;                    // slots of one bucket over all workgroups (G * S)
+constexpr int kOvfCap = 4096;                       // candidates one workgroup may put past its slots
 constexpr int kFinishCap = 4096;                    // bucket entries a finisher orders in LDS
 constexpr int kSubBins = 2048;
 constexpr int kRawWords = 28672;                    // 112 KB of LDS shared by the phases
@@ -119,7 +120,6 @@ struct StepSet {
   Counter main_go[8];             // 1 once main_all is complete
   Counter rows_grp[8];            // row pairs handed out per group of streaming workgroups
   Counter plan_flag[8];           // 1 once the plan is published
-  Counter last_rank[8];           // 1 + the rank key of the k-th entry, once known
   Counter verdict_flag[8];        // 1 = the plan held, 2 = run the exact path
   Counter bad;                    // low word: OR of kWhy* failures seen by the streaming workgroups
 };
@@ -155,7 +155,7 @@ struct GenState {
 };
 
 struct TopkLayout {
-  size_t ctl, gstate, gcnt, lsd_cnt, lsd_pre, lsd_tot, bufA, bufB, pub, rcnt, region, total;
+  size_t ctl, gstate, gcnt, lsd_cnt, lsd_pre, lsd_tot, bufA, bufB, pub, rcnt, slots, ovf, total;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -179,7 +179,8 @@ static TopkLayout topk_layout(int64_t n, int64_t k) {
   L.bufB = take(sizeof(Pair) * (size_t)std::max<int64_t>(k, 1));
   L.pub = take(sizeof(u32) * ((size_t)kPlanCap + kMaxStepBlocks));
   L.rcnt = take(sizeof(u32) * (size_t)kMaxStepBlocks * (kMaxBuckets / 2));
-  L.region = take(sizeof(Pair) * (size_t)kMaxStepBlocks * kRegionCap);
+  L.slots = take(sizeof(Pair) * (size_t)kMaxBuckets * kSlotTotal);
+  L.ovf = take(sizeof(Pair) * (size_t)kMaxStepBlocks * kOvfCap);
   L.total = off;
   return L;
 }
@@ -550,12 +551,14 @@ struct StepArgs {
   u32 loc_q16;                   // T_loc: rank fraction of the local sample, in 1/65536
   u32 break_plan;                // test hook: publish a plan that cannot hold
   u32 loc_mode;                  // test hook: 1 = T_loc above every key, 2 = T_loc = 0
-  u32 region_cap;                // candidates one workgroup may publish (kRegionCap; less to test)
+  u32 region_cap;                // candidates one workgroup may publish (no limit; less to test)
+  u32 slot_log;                  // each workgroup has S = 2^slot_log slots per bucket
   u32 parity;                    // which counter set this launch uses
   StepCtl* ctl;
   u32* pub;      // [kMaxStepBlocks][kPubCap] keys, then [kMaxStepBlocks] count | floor << 16
   u32* rcnt;     // [kMaxStepBlocks][kMaxBuckets / 2] bucket counts, two u16 per word
-  Pair* region;  // [kMaxStepBlocks][kRegionCap] published candidates, by bucket
+  u64* slots;    // [kMaxBuckets][G][S] candidates (packed pairs): bucket j's first S of workgroup b
+  u64* ovf;      // [kMaxStepBlocks][kOvfCap] the rest of workgroup b's candidates, by bucket
   u32* gstate;   // the general path's state, cleared by workgroup 0
   int gstate_words;
   GenArgs gen;   // the exact path on this grid
@@ -846,23 +849,29 @@ __device__ __forceinline__ void step_plan(const StepArgs& a, u32* s_raw, u32* s_
 __device__ __forceinline__ bool step_finish(const StepArgs& a, u32* s_raw, u32* s_scan) {
   constexpr int NT = kStepThreads;
   constexpr int NW = kStepWaves;
-  Pair* s_a = (Pair*)s_raw;                     // [kFinishCap] the bucket as gathered
-  Pair* s_b = (Pair*)(s_raw + 2 * kFinishCap);  // [kFinishCap] grouped by key sub-range
-  u32* s_sub_cnt = s_raw + 4 * kFinishCap;      // [kSubBins]
-  u32* s_sub_off = s_sub_cnt + kSubBins;        // [kSubBins]
-  u32* s_rows = s_sub_off + kSubBins;           // [2][kMaxStepBlocks]: row, offset | count << 16
-  u32* s_part = s_rows + 2 * kMaxStepBlocks;    // [NW][kMaxBuckets] partial bucket totals
-  static_assert(4 * kFinishCap + 2 * kSubBins + 2 * kMaxStepBlocks + NW * kMaxBuckets <= kRawWords, "LDS");
+  constexpr int kWords = kMaxBuckets / 2;                // count words per workgroup (two u16)
+  constexpr int kCmStride = kWords + 1;                  // LDS row pitch: a column has no bank conflicts
+  constexpr int kIters = kMaxStepBlocks * kWords / NT;   // count words per thread
+  constexpr int kSlotIters = kSlotTotal / NT;            // slots per thread
+  Pair* s_a = (Pair*)s_raw;                      // [kFinishCap] the bucket, as gathered
+  Pair* s_b = (Pair*)(s_raw + 2 * kFinishCap);   // [kFinishCap] grouped by key sub-range
+  u32* s_sub_cnt = s_raw + 4 * kFinishCap;       // [kSubBins]
+  u32* s_sub_off = s_sub_cnt + kSubBins;         // [kSubBins]
+  u32* s_part = s_sub_off + kSubBins;            // [NW][kMaxBuckets] partial bucket totals
+  u32* s_cm = (u32*)s_b;                         // [G][kCmStride] the counts, until the sort
+  static_assert(4 * kFinishCap + 2 * kSubBins + NW * kMaxBuckets <= kRawWords, "LDS");
+  static_assert(kMaxStepBlocks * kCmStride <= 2 * kFinishCap + kSubBins, "counts end before s_sub_off");
   __shared__ u32 s_plo[kMaxBuckets];
   __shared__ u32 s_phdr[3];
-  __shared__ u32 s_nrows, s_kmin, s_kmax, s_ok, s_wait, s_seen;
-  __shared__ u32 s_rpre[kMaxStepBlocks + 1];
+  __shared__ u32 s_kmin, s_kmax, s_ok, s_wait, s_seen;
+  __shared__ u32 s_rpre[kMaxStepBlocks];  // where workgroup b's entries of bucket f start in s_a
   __shared__ int64_t s_start, s_mytot;
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int w = tid / kWave;
   const int f = blockIdx.x;
   const int G = gridDim.x;
+  const u32 slog = a.slot_log, S = 1u << slog;
   StepCtl* ctl = a.ctl;
   StepSet* cs = &ctl->set[a.parity];
   __syncthreads();  // s_raw changes role
@@ -874,59 +883,51 @@ __device__ __forceinline__ bool step_finish(const StepArgs& a, u32* s_raw, u32* 
   if (tid == kMaxBuckets + 2) s_phdr[2] = ld_agent(&ctl->plan.valid);
   if (tid == 0) {
     s_wait = flag_wait(&cs->main_go[blockIdx.x & 7], &ctl->err) != 0 ? 1u : 0u;
-    s_nrows = 0;
     s_kmin = 0xFFFFFFFFu;
     s_kmax = 0;
   }
   __syncthreads();
-  // Bucket counts: G rows of 32 words (two u16 counts each; row 0, the
-  // planner, publishes nothing), read coalesced into an LDS matrix (it lives
-  // where the sorted bucket goes later).  Then thread (bucket j, part p) adds
-  // rows p, p + 16, ... of column j, and thread r (one per row) finds where
-  // row r's entries of bucket f start and how many there are.
-  constexpr int kWords = kMaxBuckets / 2;
-  constexpr int kIters = kMaxStepBlocks * kWords / NT;
-  u32* s_cm = (u32*)s_b;  // [kMaxStepBlocks][kWords]
-  static_assert(kMaxStepBlocks * kWords <= 2 * kFinishCap, "count matrix fits where s_b goes");
-  const int nwords = G * kWords;
+  // One round trip: the count matrix (G rows of 32 words, two u16 counts
+  // each; row 0, the planner, publishes nothing) and bucket f's slots.
+  const int nslots = G << slog;  // <= kSlotTotal
+  u64 sv[kSlotIters];
   {
+    const u64* mine = a.slots + ((int64_t)f << slog) * G;
     u32 xw[kIters];
 #pragma unroll
     for (int it = 0; it < kIters; ++it) {
       const int wd = tid + it * NT;
-      xw[it] = (wd >= kWords && wd < nwords) ? ld_agent(&a.rcnt[wd]) : 0u;
+      xw[it] = (wd >= kWords && wd < G * kWords) ? ld_agent(&a.rcnt[wd]) : 0u;
+    }
+#pragma unroll
+    for (int q = 0; q < kSlotIters; ++q) {
+      const int i = tid + q * NT;
+      sv[q] = i < nslots ? ld_agent64(mine + i) : 0u;
     }
     if (tid == 0) s_seen = ld_agent((const u32*)&cs->bad.v);
 #pragma unroll
-    for (int it = 0; it < kIters; ++it) s_cm[tid + it * NT] = xw[it];
+    for (int it = 0; it < kIters; ++it) {
+      const int wd = tid + it * NT;
+      s_cm[(wd / kWords) * kCmStride + wd % kWords] = xw[it];
+    }
   }
   __syncthreads();
-  {
-    const int j = tid & (kMaxBuckets - 1), part = tid / kMaxBuckets;  // 16 parts
+  auto count_of = [&](int row, int j) -> u32 {
+    const u32 x = s_cm[row * kCmStride + (j >> 1)];
+    return (j & 1) ? (x >> 16) : (x & 0xFFFFu);
+  };
+  {  // thread (bucket j, part p) adds rows p, p + 16, ... of column j
+    const int j = tid & (kMaxBuckets - 1), part = tid / kMaxBuckets;
     u32 sum = 0;
-    for (int row = part; row < G; row += NT / kMaxBuckets) {
-      const u32 x = s_cm[row * kWords + (j >> 1)];
-      sum += (j & 1) ? (x >> 16) : (x & 0xFFFFu);
-    }
+    for (int row = part; row < G; row += NT / kMaxBuckets) sum += count_of(row, j);
     s_part[part * kMaxBuckets + j] = sum;
-    if (tid < G) {
-      const int row = tid;
-      u32 pre = 0;
-      for (int q2 = 0; q2 < (f >> 1); ++q2) {
-        const u32 x = s_cm[row * kWords + q2];
-        pre += (x & 0xFFFFu) + (x >> 16);
-      }
-      const u32 x = s_cm[row * kWords + (f >> 1)];
-      if (f & 1) pre += x & 0xFFFFu;
-      const u32 cf = (f & 1) ? (x >> 16) : (x & 0xFFFFu);
-      if (cf != 0) {
-        const u32 p = atomicAdd(&s_nrows, 1u);
-        s_rows[p] = (u32)row;
-        s_rows[kMaxStepBlocks + p] = pre | (cf << 16);
-      }
-    }
   }
-  __syncthreads();
+  {  // where each workgroup's entries of bucket f go: exclusive prefix over the rows
+    const u32 cnt = tid < G ? count_of(tid, f) : 0u;
+    u32 tot;
+    const u32 ex = block_exclusive_sum<NT>(cnt, s_scan, tot);  // its barriers publish s_part too
+    if (tid < G) s_rpre[tid] = ex;
+  }
   // verdict and bucket offsets in wave 0 (lane i = bucket i)
   if (w == 0) {
     u32 t = 0;
@@ -966,48 +967,35 @@ __device__ __forceinline__ bool step_finish(const StepArgs& a, u32* s_raw, u32* 
   __syncthreads();
   if (!s_ok) return false;
   const int64_t mystart = s_start, mytot = s_mytot;
-  if (mytot == 0) return true;
-  const u32 nrows = s_nrows;
-  const u64* reg = (const u64*)a.region;
-  if (mystart >= a.k) return true;  // no rank below k here
+  if (mytot == 0 || mystart >= a.k) return true;  // no rank below k here
   const int m = (int)mytot;  // <= kFinishCap (verdict)
-  for (int i = tid; i < kSubBins; i += NT) s_sub_cnt[i] = 0;
-  {  // where each row's entries go: exclusive prefix over the rows
-    const u32 cnt = (u32)tid < nrows ? s_rows[kMaxStepBlocks + tid] >> 16 : 0u;
-    u32 tot;
-    const u32 ex = block_exclusive_sum<NT>(cnt, s_scan, tot);
-    if ((u32)tid < nrows) s_rpre[tid] = ex;
-    if (tid == 0) s_rpre[nrows] = tot;
-  }
-  __syncthreads();
-  {  // entry i of the bucket: its row by binary search, every load in flight at once
-    constexpr int kPer = kFinishCap / NT;
-    u64 v[kPer];
+  {  // gather: the slots in hand, then (rarely) entries past a workgroup's S slots
+    u32 kmin = 0xFFFFFFFFu, kmax = 0;
+    auto take_entry = [&](const Pair& p, u32 at) {
+      s_a[at] = p;
+      const u32 kk = key_of_bits(p.bits);
+      kmin = std::min(kmin, kk);
+      kmax = std::max(kmax, kk);
+    };
 #pragma unroll
-    for (int q2 = 0; q2 < kPer; ++q2) {
-      const int i = tid + q2 * NT;
-      v[q2] = 0;
-      if (i < m) {
-        int lo = 0, hi = (int)nrows - 1;  // the last row whose prefix is <= i
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (s_rpre[mid] <= (u32)i) lo = mid;
-          else hi = mid - 1;
-        }
-        const u32 row = s_rows[lo], off = s_rows[kMaxStepBlocks + lo] & 0xFFFFu;
-        v[q2] = ld_agent64(reg + (int64_t)row * kRegionCap + off + (i - s_rpre[lo]));
+    for (int q = 0; q < kSlotIters; ++q) {
+      const int i = tid + q * NT;
+      if (i < nslots) {
+        const int row = i >> slog;
+        const u32 sl = (u32)i & (S - 1u);
+        if (sl < count_of(row, f)) take_entry(unpack_pair(sv[q]), s_rpre[row] + sl);
       }
     }
-    u32 kmin = 0xFFFFFFFFu, kmax = 0;
-#pragma unroll
-    for (int q2 = 0; q2 < kPer; ++q2) {
-      const int i = tid + q2 * NT;
-      if (i < m) {
-        const Pair p = unpack_pair(v[q2]);
-        s_a[i] = p;
-        const u32 kk = key_of_bits(p.bits);
-        kmin = std::min(kmin, kk);
-        kmax = std::max(kmax, kk);
+    if (tid < G) {
+      const u32 cnt = count_of(tid, f);
+      if (cnt > S) {  // workgroup tid put entries of bucket f in its overflow area
+        u32 off = 0;  // its overflow entries of buckets 0..f-1
+        for (int j = 0; j < f; ++j) {
+          const u32 c = count_of(tid, j);
+          off += c > S ? c - S : 0u;
+        }
+        const u64* src = a.ovf + (int64_t)tid * kOvfCap + off;
+        for (u32 sl = S; sl < cnt; ++sl) take_entry(unpack_pair(ld_agent64(src + (sl - S))), s_rpre[tid] + sl);
       }
     }
     kmin = wave_min(kmin);
@@ -1017,6 +1005,8 @@ __device__ __forceinline__ bool step_finish(const StepArgs& a, u32* s_raw, u32* 
       atomicMax(&s_kmax, kmax);
     }
   }
+  __syncthreads();  // the counts are no longer needed: s_sub_cnt may overwrite them
+  for (int i = tid; i < kSubBins; i += NT) s_sub_cnt[i] = 0;
   __syncthreads();
   // Split [kmin, kmax] into kSubBins equal key sub-ranges numbered from the
   // top and group the entries by sub-range (counting sort); inside a
@@ -1055,6 +1045,9 @@ __device__ __forceinline__ bool step_finish(const StepArgs& a, u32* s_raw, u32* 
     s_b[atomicAdd(&s_sub_cnt[sub_of(e)], 1u)] = e;
   }
   __syncthreads();
+  // Entries of rank < k: to the output, and their residual to +0.  Every
+  // streaming workgroup's acc stores completed at device scope before it
+  // arrived, so these stores land after them.
   const int64_t take = std::min<int64_t>(mytot, a.k - mystart);
   for (int i = tid; i < m; i += NT) {
     const Pair e = s_b[i];
@@ -1067,9 +1060,8 @@ __device__ __forceinline__ bool step_finish(const StepArgs& a, u32* s_raw, u32* 
     if (p < take) {
       a.out_idx[mystart + p] = e.idx;
       a.out_val[mystart + p] = __uint_as_float(e.bits);
+      st_agent_f32(a.residual + e.idx, 0.0f);
     }
-    // the k-th entry: every workgroup zeroes its own entries ranked up to it
-    if (mystart + p == a.k - 1) flag_set(cs->last_rank, re + 1u);
   }
   return true;
 }
@@ -1085,7 +1077,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
   __shared__ u32 s_bcnt[kMaxBuckets];
   __shared__ u32 s_boff[kMaxBuckets];
   __shared__ u32 s_hdr[3];
-  __shared__ u32 s_nlist, s_ovf, s_npub, s_flag, s_floor, s_tlocbin;
+  __shared__ u32 s_nlist, s_ovf, s_npub, s_novf, s_flag, s_floor, s_tlocbin;
   __shared__ int64_t s_next[2];        // next row pair (double-buffered), -1 when none is left
   __shared__ u32 s_pairs[kMaxPairs];  // row pairs this workgroup streamed
   __shared__ u32 s_npairs;
@@ -1145,8 +1137,8 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
   u32 psink = 0;  // returned values of the publishing atomics
   // The sample keys stay past the list and staging areas (the list fills
   // while they are published); the histogram is done with before streaming.
-  u32* s_keys = s_raw + 2 * kListCap + 2 * kRegionCap;  // [kSampleKeyCap]
-  static_assert(2 * kListCap + 2 * kRegionCap + kSampleKeyCap <= kRawWords, "LDS");
+  u32* s_keys = s_raw + 2 * kListCap + 2 * kOvfCap;  // [kSampleKeyCap]
+  static_assert(2 * kListCap + 2 * kOvfCap + kSampleKeyCap <= kRawWords, "LDS");
   {
     u32* s_h = s_raw;  // [kHistBins]
     for (int i = tid; i < kHistBins; i += NT) s_h[i] = 0;
@@ -1157,6 +1149,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
       s_nlist = 0;
       s_ovf = 0;
       s_npub = 0;
+      s_novf = 0;
       s_npairs = 0;
       s_plan_in_lds = false;
     }
@@ -1247,12 +1240,10 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
   } else {
     // ---------------- stream ----------------
     const u32 tloc = a.loc_mode == 1u ? 0x7FFFFFFFu : a.loc_mode == 2u ? 0u : s_tlocbin << kHistShift;
-    Pair* s_list = (Pair*)s_raw;                  // [kListCap]
-    Pair* s_pub = (Pair*)(s_raw + 2 * kListCap);  // [kRegionCap]
-    static_assert(2 * kListCap + 2 * kRegionCap <= kRawWords, "LDS");
+    Pair* s_list = (Pair*)s_raw;  // [kListCap]
     auto keep_scalar = [&](int64_t i) {
       const float acc = r[i] + g[i];
-      r[i] = acc;
+      st_agent_f32(r + i, acc);
       const u32 bits = __float_as_uint(acc);
       if (key_of_bits(bits) >= tloc) list_keep(s_list, &s_nlist, &s_ovf, i, bits);
     };
@@ -1260,10 +1251,11 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
     // entries with key >= T_loc are appended to the list at offsets from one
     // wave-wide prefix sum and one LDS atomic per wave.
     auto vec_row = [&](int64_t t, const v4f gg, const v4f rr) {
-      const int64_t i = t * NT + tid;
+      const int64_t row0 = (int64_t)__builtin_amdgcn_readfirstlane((int)t) * NT;  // t is the same in every lane
+      const int64_t i = row0 + tid;
       const bool in = i < a.nv;
       const v4f acc = rr + gg;
-      if (in) __builtin_nontemporal_store(acc, rv + i);
+      if (in) st_agent_v4_nt(rv + row0, (u32)std::min<int64_t>(NT, a.nv - row0) * 16u, (u32)tid * 16u, acc);
       const u32 b0 = __float_as_uint(acc.x), b1 = __float_as_uint(acc.y);
       const u32 b2 = __float_as_uint(acc.z), b3 = __float_as_uint(acc.w);
       const u32 mk = in ? ((u32)(key_of_bits(b0) >= tloc) | ((u32)(key_of_bits(b1) >= tloc) << 1) |
@@ -1423,7 +1415,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
           const int64_t i = t * TE + u * NT + tid;
           if (i < a.n) {
             const float acc = rr[u] + gg[u];
-            r[i] = acc;
+            st_agent_f32(r + i, acc);
             const u32 bits = __float_as_uint(acc);
             if (key_of_bits(bits) >= tloc) list_keep(s_list, &s_nlist, &s_ovf, i, bits);
           }
@@ -1486,40 +1478,63 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
       if (s_ovf) fail |= kWhyList;  // more keys >= T_guess than the list holds
     }
     const u32 nl = std::min(s_nlist, (u32)kListCap);
-    for (u32 i = tid; i < nl; i += NT) {
-      const u32 key = key_of_bits(s_list[i].bits);
-      if (key >= tg) atomicAdd(&s_bcnt[bucket_of(key, s_lo, nb)], 1u);
-    }
-    __syncthreads();
-    if (w == 0) {  // bucket offsets
-      const u32 v = s_bcnt[lane];
-      const u32 x = wave_inclusive_sum(v);
-      s_boff[lane] = x - v;
-      if (lane == kWave - 1) s_npub = x;
-    }
-    __syncthreads();
-    const u32 C = s_npub;
+    const u32 slog = a.slot_log, S = 1u << slog;
+    Pair* s_ovl = (Pair*)(s_raw + 2 * kListCap);     // [kOvfCap] candidates past their S slots
+    u32* s_ovt = s_raw + 2 * kListCap + 2 * kOvfCap;  // [kOvfCap] bucket << 16 | place past S
+    static_assert(2 * kListCap + 3 * kOvfCap <= kRawWords, "LDS");
     u32 sink = 0;
-    if (C <= a.region_cap && !(fail & kWhyList)) {
+    // One pass over the list: a candidate (key >= T_guess) takes the next
+    // place of its bucket; places below S are this workgroup's slots of the
+    // bucket and are written now, the rest wait here for the overflow area.
+    if (!(fail & kWhyList)) {
+      u64* const slots = a.slots;
       for (u32 i = tid; i < nl; i += NT) {
         const Pair e = s_list[i];
         const u32 key = key_of_bits(e.bits);
-        if (key >= tg) s_pub[atomicAdd(&s_boff[bucket_of(key, s_lo, nb)], 1u)] = e;
+        if (key < tg) continue;
+        const int j = bucket_of(key, s_lo, nb);
+        const u32 pos = atomicAdd(&s_bcnt[j], 1u);
+        if (pos < S) {
+          sink += (u32)xchg_agent64(slots + (((int64_t)j * G + b) << slog) + pos, pack_pair(e));
+        } else {
+          const u32 q = atomicAdd(&s_novf, 1u);
+          if (q < (u32)kOvfCap) {
+            s_ovl[q] = e;
+            s_ovt[q] = ((u32)j << 16) | (pos - S);
+          }
+        }
       }
-      __syncthreads();
-      u64* dst = (u64*)(a.region + (int64_t)b * kRegionCap);
-      for (u32 i = tid; i < C; i += NT) sink += (u32)xchg_agent64(dst + i, pack_pair(s_pub[i]));
+    }
+    __syncthreads();
+    if (w == 0) {  // candidates, and where each bucket's overflow starts
+      const u32 c = s_bcnt[lane];
+      const u32 over = c > S ? c - S : 0u;
+      const u32 xo = wave_inclusive_sum(over);
+      s_boff[lane] = xo - over;
+      const u32 xc = wave_inclusive_sum(c);
+      if (lane == kWave - 1) s_npub = xc;
+    }
+    __syncthreads();
+    const u32 C = s_npub, novf = s_novf;
+    if (C > a.region_cap || novf > (u32)kOvfCap) fail |= kWhyRegion;
+    if (!fail) {
+      u64* const dst = a.ovf + (int64_t)b * kOvfCap;
+      for (u32 q = tid; q < novf; q += NT) {
+        const u32 t = s_ovt[q];
+        sink += (u32)xchg_agent64(dst + s_boff[t >> 16] + (t & 0xFFFFu), pack_pair(s_ovl[q]));
+      }
       if (tid < kMaxBuckets / 2)
         sink += xchg_agent(&a.rcnt[b * (kMaxBuckets / 2) + tid], s_bcnt[2 * tid] | (s_bcnt[2 * tid + 1] << 16));
     } else {
       // cannot publish: the plan fails
       if (tid < kMaxBuckets / 2) sink += xchg_agent(&a.rcnt[b * (kMaxBuckets / 2) + tid], 0u);
-      fail |= kWhyRegion;
-      __syncthreads();
-      if (tid == 0) s_npub = 0;
+      if (tid == 0) sink += or_agent((u32*)&cs->bad.v, fail);
     }
-    if (tid == 0 && fail) sink += or_agent((u32*)&cs->bad.v, fail);
     if (sink == 0x12345678u) s_scan[NW] = sink;  // keeps the returned values live
+    // Every store of this workgroup -- acc included -- has completed at
+    // device scope before it arrives: after the verdict the finishers zero
+    // the selected entries of residual, and those stores must land later.
+    wait_all_memory();
     __syncthreads();
     if (tid == 0 && phase_arrive(cs->main_grp, &cs->main_all, G)) flag_set(cs->main_go, 1u);
   }
@@ -1533,40 +1548,12 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
     __syncthreads();
     verdict = s_flag;
   }
-  if (verdict == 1u) {
-    // The selected entries are those ranked up to the k-th; each streaming
-    // workgroup zeroes the ones it published (it wrote their acc itself, so
-    // its two stores to a word stay in order).
-    if (b > 0) {
-      __shared__ u64 s_last;
-      if (tid == 0) {
-        u32 spins = 0;
-        u64 v;
-        while ((v = ld_agent64(&cs->last_rank[blockIdx.x & 7].v)) == 0) {
-          __builtin_amdgcn_s_sleep(2);
-          if (++spins > kSpinLimit) {
-            atomicOr(&ctl->err, kErrBarrierTimeout);
-            break;
-          }
-        }
-        s_last = v - 1u;  // ~0 after a time-out: nothing is zeroed
-      }
-      __syncthreads();
-      const u64 last = s_last;
-      const u32 npub = s_npub;
-      const u64* mine = (const u64*)(a.region + (int64_t)b * kRegionCap);
-      for (u32 i = tid; i < npub; i += NT) {
-        const Pair p = b >= kMaxBuckets ? ((const Pair*)(s_raw + 2 * kListCap))[i] : unpack_pair(ld_agent64(mine + i));
-        if (pair_rank(p) <= last) r[p.idx] = 0.0f;
-      }
-    }
-  } else {
+  if (verdict != 1u) {
     // The plan did not hold: residual holds acc everywhere, and the whole
     // grid runs the exact path (grid_sync fences first, so every
     // workgroup's residual stores are visible to all).
     if (grid_sync(a.gen.bar)) general_path<NT>(a.gen);
   }
-
 }
 
 }  // namespace tgs
@@ -1622,7 +1609,7 @@ bool step_params(int64_t n, int64_t k, int G, StepArgs& a) {
   // expected candidate count) of a share's entries above it
   const double share = nd / M;
   const double f_loc = std::min(1.0, std::max(1024.0 / share, 4.0 * tau / nd));
-  if (f_loc * share > kListCap / 4 || tau / M > kRegionCap / 4) return false;
+  if (f_loc * share > kListCap / 4 || tau / M > kOvfCap / 4) return false;
   a.loc_q16 = (u32)std::min(65535.0, std::ceil(f_loc * 65536.0));
   return true;
 }
@@ -1708,12 +1695,18 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
     sa.out_val = out_val;
     sa.break_plan = path == 2 ? 1u : 0u;
     sa.loc_mode = path == 3 ? 1u : path == 4 ? 2u : 0u;
-    sa.region_cap = path == 5 ? 1u : (u32)kRegionCap;
+    sa.region_cap = path == 5 ? 1u : 0xFFFFFFFFu;
+    // S = 2^slot_log slots per (bucket, workgroup), the most that keeps a
+    // bucket's G * S slots within kSlotTotal (path 6: one slot, so nearly
+    // every candidate goes to the overflow area)
+    sa.slot_log = 0;
+    while (path != 6 && ((int64_t)G << (sa.slot_log + 1)) <= kSlotTotal) ++sa.slot_log;
     sa.parity = launch_parity(workspace);
     sa.ctl = ctl;
     sa.pub = (u32*)(ws + L.pub);
     sa.rcnt = (u32*)(ws + L.rcnt);
-    sa.region = (Pair*)(ws + L.region);
+    sa.slots = (u64*)(ws + L.slots);
+    sa.ovf = (u64*)(ws + L.ovf);
     sa.gstate = (u32*)gs;
     sa.gstate_words = (int)(sizeof(GenState) / sizeof(u32));
     sa.gen = ga;

@@ -16,9 +16,12 @@ repeats.  The W warm-up steps give every residual buffer its error-feedback
 history (W = 20 -> 5 steps each).
 
 Prints one JSON line.  `roofline` covers the dominant kernel, k_step (the
-whole fused step: 12n + 8k algorithmic bytes per launch), timed per launch
-with HIP events recorded by the library on the stream it launches on;
-`cpu_baseline` is the plain C oracle on one host core on the same workload.
+whole fused step, one launch: 12n + 8k algorithmic bytes per launch), timed
+with HIP events on the stream it is launched on, recorded around spans of 8
+back-to-back launches: the average launch period, gaps between launches
+included, without an event pair around every launch (which adds a few
+microseconds of its own); `cpu_baseline` is the plain C oracle on one host core
+on the same workload.
 """
 from __future__ import annotations
 
@@ -114,18 +117,20 @@ def main():
     rs0 = int(ws[20:24].view(torch.int32).item())  # workgroup shares re-read (incomplete local lists)
 
     K = args.steps
-    every = 8  # every 8th timed step is bracketed by events
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(0, K, every)]
-    for a, b in ev:  # torch creates the HIP event on its first record
-        a.record()
-        b.record()
+    span = 8  # launches between two events
+    nspan = max(1, K // span)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nspan + 1)]
+    for e in ev:  # torch creates the HIP event on its first record
+        e.record(run.stream)
     print("bench: timing %d steps" % K, file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        if i % every == 0:
-            tgs.profile_next_call(*ev[i // every])
+        if i % span == 0 and i // span < nspan:
+            ev[i // span].record(run.stream)
         step(args.warmup + i)
+        if i + 1 == nspan * span:
+            ev[nspan].record(run.stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     tgs.check_device_error(ws)
@@ -134,7 +139,7 @@ def main():
     rescans = int(ws[20:24].view(torch.int32).item()) - rs0
     elapsed = t1 - t0
     ms_per_step = elapsed * 1e3 / K
-    main_ms = sorted(tgs.profile_elapsed_ms(a, b) for a, b in ev)
+    main_ms = sorted(ev[j].elapsed_time(ev[j + 1]) / span for j in range(nspan))  # per launch
     main_avg_ms = sum(main_ms) / len(main_ms)
     bytes_step = 12.0 * N + 8.0 * k          # read grad + residual, write residual + k pairs
     gbps_step = bytes_step / (ms_per_step * 1e-3) / 1e9
@@ -182,7 +187,7 @@ def main():
                      "frac": gbps_main / HBM_PEAK_GBPS, "traffic": traffic,
                      "kernel": "k_step", "bytes_per_launch": bytes_step,
                      "avg_launch_us": main_avg_ms * 1e3, "median_launch_us": main_ms[len(main_ms) // 2] * 1e3,
-                     "launches_timed": len(main_ms)},
+                     "launches_timed": nspan * span, "timing": "HIP events around spans of %d launches" % span},
         "cpu_baseline": cpu,
         "last_step_fast_path": bool(fast == 1),
         "timed_steps_on_exact_fallback": fallbacks,

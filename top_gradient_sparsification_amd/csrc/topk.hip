@@ -586,17 +586,16 @@ __device__ __forceinline__ void list_keep(Pair* s_list, u32* s_nlist, u32* s_ovf
   else *s_ovf = 1u;
 }
 
-// Publishes a plan (all threads of workgroup 0): words with returning device
-// atomics, then the flag once they are all done.
-__device__ __forceinline__ void publish_plan(StepCtl* ctl, StepSet* cs, u32 valid, u32 tg, u32 nb, const u32* lo,
-                                             u32* s_scan) {
+// Publishes a plan (all threads of workgroup 0): the words with device-scope
+// stores, then the flag once they have all completed (a streaming workgroup
+// that sees the flag must read this plan and no older one).
+__device__ __forceinline__ void publish_plan(StepCtl* ctl, StepSet* cs, u32 valid, u32 tg, u32 nb, const u32* lo) {
   const int tid = threadIdx.x;
-  u32 sink = 0;
-  if (tid < kMaxBuckets) sink += xchg_agent(&ctl->plan.lo[tid], lo[tid]);
-  if (tid == kMaxBuckets) sink += xchg_agent(&ctl->plan.t_guess, tg);
-  if (tid == kMaxBuckets + 1) sink += xchg_agent(&ctl->plan.nbuckets, nb);
-  if (tid == kMaxBuckets + 2) sink += xchg_agent(&ctl->plan.valid, valid);
-  if (sink == 0x12345678u) s_scan[kStepWaves] = sink;  // keeps the returned values live
+  if (tid < kMaxBuckets) st_agent(&ctl->plan.lo[tid], lo[tid]);
+  if (tid == kMaxBuckets) st_agent(&ctl->plan.t_guess, tg);
+  if (tid == kMaxBuckets + 1) st_agent(&ctl->plan.nbuckets, nb);
+  if (tid == kMaxBuckets + 2) st_agent(&ctl->plan.valid, valid);
+  wait_all_memory();
   __syncthreads();
   if (tid == 0) flag_set(cs->plan_flag, 1u);
 }
@@ -697,7 +696,7 @@ __device__ __forceinline__ void step_plan(const StepArgs& a, u32* s_raw, u32* s_
     const u32 tg = a.break_plan ? 0x7FFFFFFFu : 0xFFFFFFFFu;
     if (tid < kMaxBuckets) s_lo[tid] = tid == 0 ? tg : 0u;
     __syncthreads();
-    publish_plan(ctl, cs, a.break_plan ? 1u : 0u, tg, 1u, s_lo, s_scan);
+    publish_plan(ctl, cs, a.break_plan ? 1u : 0u, tg, 1u, s_lo);
     return;
   }
   const int ntarget = (int)nb;  // wanted ranks: [0] c_target, [j] j * bucket_samples for 1 <= j < nb
@@ -841,7 +840,7 @@ __device__ __forceinline__ void step_plan(const StepArgs& a, u32* s_raw, u32* s_
     s_lo[j] = j + 1 < nb ? v : (j + 1 == nb ? tg : 0u);
   }
   __syncthreads();
-  publish_plan(ctl, cs, 1u, s_lo[nb - 1], nb, s_lo, s_scan);
+  publish_plan(ctl, cs, 1u, s_lo[nb - 1], nb, s_lo);
 }
 
 // Finisher f (workgroups 0..63), once every workgroup has published: the
@@ -917,16 +916,18 @@ __device__ __forceinline__ bool step_finish(const StepArgs& a, u32* s_raw, u32* 
     return (j & 1) ? (x >> 16) : (x & 0xFFFFu);
   };
   {  // thread (bucket j, part p) adds rows p, p + 16, ... of column j
+    constexpr int kParts = NT / kMaxBuckets;  // 16
     const int j = tid & (kMaxBuckets - 1), part = tid / kMaxBuckets;
     u32 sum = 0;
-    for (int row = part; row < G; row += NT / kMaxBuckets) sum += count_of(row, j);
+#pragma unroll
+    for (int q = 0; q < kMaxStepBlocks / kParts; ++q) sum += count_of(part + q * kParts, j);  // rows >= G hold 0
     s_part[part * kMaxBuckets + j] = sum;
   }
   {  // where each workgroup's entries of bucket f go: exclusive prefix over the rows
     const u32 cnt = tid < G ? count_of(tid, f) : 0u;
     u32 tot;
     const u32 ex = block_exclusive_sum<NT>(cnt, s_scan, tot);  // its barriers publish s_part too
-    if (tid < G) s_rpre[tid] = ex;
+    if (tid < kMaxStepBlocks) s_rpre[tid] = ex;  // rows >= G: read, never used
   }
   // verdict and bucket offsets in wave 0 (lane i = bucket i)
   if (w == 0) {
@@ -977,14 +978,18 @@ __device__ __forceinline__ bool step_finish(const StepArgs& a, u32* s_raw, u32* 
       kmin = std::min(kmin, kk);
       kmax = std::max(kmax, kk);
     };
+    u32 cq[kSlotIters], pq[kSlotIters];  // all LDS reads first, then the writes
+#pragma unroll
+    for (int q = 0; q < kSlotIters; ++q) {
+      const int row = std::min((tid + q * NT) >> slog, kMaxStepBlocks - 1);
+      cq[q] = count_of(row, f);
+      pq[q] = s_rpre[row];
+    }
 #pragma unroll
     for (int q = 0; q < kSlotIters; ++q) {
       const int i = tid + q * NT;
-      if (i < nslots) {
-        const int row = i >> slog;
-        const u32 sl = (u32)i & (S - 1u);
-        if (sl < count_of(row, f)) take_entry(unpack_pair(sv[q]), s_rpre[row] + sl);
-      }
+      const u32 sl = (u32)i & (S - 1u);
+      if (i < nslots && sl < cq[q]) take_entry(unpack_pair(sv[q]), pq[q] + sl);
     }
     if (tid < G) {
       const u32 cnt = count_of(tid, f);
@@ -1078,6 +1083,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
   __shared__ u32 s_boff[kMaxBuckets];
   __shared__ u32 s_hdr[3];
   __shared__ u32 s_nlist, s_ovf, s_npub, s_novf, s_flag, s_floor, s_tlocbin;
+  __shared__ u32 s_cursor, s_snap[2];  // list entries filed into slots so far; this iteration's range
   __shared__ int64_t s_next[2];        // next row pair (double-buffered), -1 when none is left
   __shared__ u32 s_pairs[kMaxPairs];  // row pairs this workgroup streamed
   __shared__ u32 s_npairs;
@@ -1134,7 +1140,6 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
   }
 
   // ---------------- sample ----------------
-  u32 psink = 0;  // returned values of the publishing atomics
   // The sample keys stay past the list and staging areas (the list fills
   // while they are published); the histogram is done with before streaming.
   u32* s_keys = s_raw + 2 * kListCap + 2 * kOvfCap;  // [kSampleKeyCap]
@@ -1143,6 +1148,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
     u32* s_h = s_raw;  // [kHistBins]
     for (int i = tid; i < kHistBins; i += NT) s_h[i] = 0;
     for (int i = tid; i < kSampleKeyCap; i += NT) s_keys[i] = kNoKey;
+    if (tid < kMaxBuckets) s_bcnt[tid] = 0;
     if (tid == 0) {
       s_floor = 0;
       s_tlocbin = 0;
@@ -1150,16 +1156,17 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
       s_ovf = 0;
       s_npub = 0;
       s_novf = 0;
+      s_cursor = 0;
       s_npairs = 0;
       s_plan_in_lds = false;
     }
     if (b == 0) {  // the exact path's state and the error word start at zero; the
                    // other counter set is cleared for the next launch
-      for (int i = tid; i < a.gstate_words; i += NT) psink += xchg_agent(&a.gstate[i], 0u);
-      if (tid == 0) psink += xchg_agent(&ctl->err, 0u);
+      for (int i = tid; i < a.gstate_words; i += NT) st_agent(&a.gstate[i], 0u);
+      if (tid == 0) st_agent(&ctl->err, 0u);
       constexpr int kSetWords = (int)(sizeof(StepSet) / sizeof(Counter));
       Counter* other = (Counter*)&ctl->set[a.parity ^ 1u];
-      if (tid < kSetWords) psink += (u32)xchg_agent64(&other[tid].v, 0u);
+      if (tid < kSetWords) st_agent64(&other[tid].v, 0u);
     }
     __syncthreads();
 #pragma unroll
@@ -1191,8 +1198,10 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
   // Publishes the sample keys of bins >= floor and their count: first those
   // of bins above the floor bin (fewer than pub_want, so they always fit),
   // then those of the floor bin while kPubCap allows.  A workgroup that had
-  // to leave some out is complete from floor + 1 up.  The atomics' returned
-  // values are awaited by sample_arrive.
+  // to leave some out is complete from floor + 1 up.  Nothing waits for
+  // these stores: workgroup 0 reads them only after every workgroup has
+  // arrived, microseconds later, and the keys only shape the plan, which is a
+  // guess -- whatever it holds, the verdict makes the result exact.
   auto sample_publish = [&]() {
     const u32 floor_bin = s_floor;
     u32 mine = 0;  // keys above the floor bin (low half) and in it (high half)
@@ -1213,19 +1222,18 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
       if (key == kNoKey) continue;
       const u32 bin = key >> kHistShift;
       if (bin > floor_bin) {
-        psink += xchg_agent(&mine_pub[pos_hi++], key);
+        st_agent(&mine_pub[pos_hi++], key);
       } else if (bin == floor_bin) {
-        if (pos_eq < (u32)kPubCap) psink += xchg_agent(&mine_pub[pos_eq], key);
+        if (pos_eq < (u32)kPubCap) st_agent(&mine_pub[pos_eq], key);
         ++pos_eq;
       }
     }
     const u32 total = above + (count >> 16);
-    if (tid == 0) psink += xchg_agent(&a.pub[kPlanCap + b], std::min(total, 0xFFFFu) | (floor_bin << 16));
+    if (tid == 0) st_agent(&a.pub[kPlanCap + b], std::min(total, 0xFFFFu) | (floor_bin << 16));
   };
   // Arrival at the sample phase, once this workgroup's published values are
   // all in (waiting for the atomics' returned values).
   auto sample_arrive = [&]() {
-    if (psink == 0x12345678u) s_scan[NW] = psink;  // keeps the returned values live
     __syncthreads();
     if (tid == 0) phase_arrive(cs->samp_grp, &cs->samp_all, G);
   };
@@ -1240,7 +1248,34 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
   } else {
     // ---------------- stream ----------------
     const u32 tloc = a.loc_mode == 1u ? 0x7FFFFFFFu : a.loc_mode == 2u ? 0u : s_tlocbin << kHistShift;
-    Pair* s_list = (Pair*)s_raw;  // [kListCap]
+    Pair* s_list = (Pair*)s_raw;                      // [kListCap]
+    Pair* s_ovl = (Pair*)(s_raw + 2 * kListCap);     // [kOvfCap] candidates past their S slots
+    u32* s_ovt = s_raw + 2 * kListCap + 2 * kOvfCap;  // [kOvfCap] bucket << 16 | place past S
+    static_assert(2 * kListCap + 3 * kOvfCap <= kRawWords, "LDS");
+    const u32 slog = a.slot_log, S = 1u << slog;
+    // Files list entries [lo, hi) under a plan: a candidate (key >= T_guess)
+    // takes the next place of its bucket; places below S are this
+    // workgroup's slots of the bucket and are written at once, the rest wait
+    // here for the overflow area.
+    auto file_range = [&](u32 lo, u32 hi, u32 tg, int nb) {
+      u64* const slots = a.slots;
+      for (u32 i = lo + tid; i < hi; i += NT) {
+        const Pair e = s_list[i];
+        const u32 key = key_of_bits(e.bits);
+        if (key < tg) continue;
+        const int j = bucket_of(key, s_lo, nb);
+        const u32 pos = atomicAdd(&s_bcnt[j], 1u);
+        if (pos < S) {
+          st_agent64(slots + (((int64_t)j * G + b) << slog) + pos, pack_pair(e));
+        } else {
+          const u32 q = atomicAdd(&s_novf, 1u);
+          if (q < (u32)kOvfCap) {
+            s_ovl[q] = e;
+            s_ovt[q] = ((u32)j << 16) | (pos - S);
+          }
+        }
+      }
+    };
     auto keep_scalar = [&](int64_t i) {
       const float acc = r[i] + g[i];
       st_agent_f32(r + i, acc);
@@ -1385,6 +1420,20 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
             rr[u] = __builtin_nontemporal_load(rv + i);
           }
         }
+        if (pst == 2u) {
+          // The plan is in LDS: while this pair's loads are in flight, file
+          // the entries the list gained since the last filing (no wave
+          // appends before the barrier below: the one above ended the last
+          // pair's appends).
+          if (tid == 0) {
+            s_snap[0] = s_cursor;
+            s_snap[1] = std::min(s_nlist, (u32)kListCap);
+            s_cursor = s_snap[1];
+          }
+          __syncthreads();
+          if (s_hdr[2] == 1u && s_hdr[1] >= 1 && s_hdr[1] <= (u32)kMaxBuckets)
+            file_range(s_snap[0], s_snap[1], s_hdr[0], (int)s_hdr[1]);
+        }
         vec_row(2 * p, gg[0], rr[0]);
         vec_row(2 * p + 1, gg[1], rr[1]);
         if (pst == 1u && tid < kMaxBuckets + 3) {
@@ -1435,7 +1484,6 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
     } else if (tid == 0) {
       s_flag = 1;
     }
-    if (tid < kMaxBuckets) s_bcnt[tid] = 0;
     __syncthreads();
     const bool plan_ok = s_flag != 0 && s_hdr[2] == 1u && s_hdr[1] >= 1 && s_hdr[1] <= (u32)kMaxBuckets;
     const u32 tg = plan_ok ? s_hdr[0] : 0xFFFFFFFFu;
@@ -1451,8 +1499,11 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
       if (tid == 0) {
         s_nlist = 0;
         s_ovf = 0;
+        s_cursor = 0;  // what was filed is filed again, from the first place
+        s_novf = 0;
         atomicAdd(&ctl->rescans, 1u);
       }
+      if (tid < kMaxBuckets) s_bcnt[tid] = 0;
       __syncthreads();
       auto rescan = [&](int64_t lo, int64_t hi) {
         for (int64_t i = lo + tid; i < hi; i += NT) {
@@ -1477,34 +1528,10 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
       __syncthreads();
       if (s_ovf) fail |= kWhyList;  // more keys >= T_guess than the list holds
     }
+    // File what the list gained since the last filing (all of it when the
+    // plan arrived after the stream, or after a re-read).
     const u32 nl = std::min(s_nlist, (u32)kListCap);
-    const u32 slog = a.slot_log, S = 1u << slog;
-    Pair* s_ovl = (Pair*)(s_raw + 2 * kListCap);     // [kOvfCap] candidates past their S slots
-    u32* s_ovt = s_raw + 2 * kListCap + 2 * kOvfCap;  // [kOvfCap] bucket << 16 | place past S
-    static_assert(2 * kListCap + 3 * kOvfCap <= kRawWords, "LDS");
-    u32 sink = 0;
-    // One pass over the list: a candidate (key >= T_guess) takes the next
-    // place of its bucket; places below S are this workgroup's slots of the
-    // bucket and are written now, the rest wait here for the overflow area.
-    if (!(fail & kWhyList)) {
-      u64* const slots = a.slots;
-      for (u32 i = tid; i < nl; i += NT) {
-        const Pair e = s_list[i];
-        const u32 key = key_of_bits(e.bits);
-        if (key < tg) continue;
-        const int j = bucket_of(key, s_lo, nb);
-        const u32 pos = atomicAdd(&s_bcnt[j], 1u);
-        if (pos < S) {
-          sink += (u32)xchg_agent64(slots + (((int64_t)j * G + b) << slog) + pos, pack_pair(e));
-        } else {
-          const u32 q = atomicAdd(&s_novf, 1u);
-          if (q < (u32)kOvfCap) {
-            s_ovl[q] = e;
-            s_ovt[q] = ((u32)j << 16) | (pos - S);
-          }
-        }
-      }
-    }
+    if (!(fail & kWhyList)) file_range(s_cursor, nl, tg, nb);
     __syncthreads();
     if (w == 0) {  // candidates, and where each bucket's overflow starts
       const u32 c = s_bcnt[lane];
@@ -1521,19 +1548,19 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
       u64* const dst = a.ovf + (int64_t)b * kOvfCap;
       for (u32 q = tid; q < novf; q += NT) {
         const u32 t = s_ovt[q];
-        sink += (u32)xchg_agent64(dst + s_boff[t >> 16] + (t & 0xFFFFu), pack_pair(s_ovl[q]));
+        st_agent64(dst + s_boff[t >> 16] + (t & 0xFFFFu), pack_pair(s_ovl[q]));
       }
       if (tid < kMaxBuckets / 2)
-        sink += xchg_agent(&a.rcnt[b * (kMaxBuckets / 2) + tid], s_bcnt[2 * tid] | (s_bcnt[2 * tid + 1] << 16));
+        st_agent(&a.rcnt[b * (kMaxBuckets / 2) + tid], s_bcnt[2 * tid] | (s_bcnt[2 * tid + 1] << 16));
     } else {
       // cannot publish: the plan fails
-      if (tid < kMaxBuckets / 2) sink += xchg_agent(&a.rcnt[b * (kMaxBuckets / 2) + tid], 0u);
-      if (tid == 0) sink += or_agent((u32*)&cs->bad.v, fail);
+      if (tid < kMaxBuckets / 2) st_agent(&a.rcnt[b * (kMaxBuckets / 2) + tid], 0u);
+      if (tid == 0) or_agent((u32*)&cs->bad.v, fail);
     }
-    if (sink == 0x12345678u) s_scan[NW] = sink;  // keeps the returned values live
     // Every store of this workgroup -- acc included -- has completed at
-    // device scope before it arrives: after the verdict the finishers zero
-    // the selected entries of residual, and those stores must land later.
+    // device scope before it arrives: the finishers read the slots and counts
+    // after the last arrival, and after the verdict they zero the selected
+    // entries of residual, stores that must land after the acc stores.
     wait_all_memory();
     __syncthreads();
     if (tid == 0 && phase_arrive(cs->main_grp, &cs->main_all, G)) flag_set(cs->main_go, 1u);

@@ -89,7 +89,8 @@ def test_small_sizes_all_k(tgs_gpu, n, dist):
 
 @pytest.mark.parametrize("dist", ["normal", "mixture", "ties"])
 @pytest.mark.parametrize("n,ks", [(65536, [1, 64, 8192]), (100_003, [17, 1000, 12_500]),
-                                  (1 << 20, [1, 1048, 49_152, 131_072]), (3_000_001, [3, 3000, 30_000])])
+                                  (524_365, [2, 524, 5000]), (1 << 20, [1, 1048, 49_152, 131_072]),
+                                  (3_000_001, [3, 3000, 30_000])])
 def test_fast_path_sizes(tgs_gpu, n, ks, dist):
     rng = np.random.default_rng(n + 3 * len(dist))
     grad, res = make(dist, n, rng)

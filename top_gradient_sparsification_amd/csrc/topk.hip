@@ -1083,7 +1083,6 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
   __shared__ u32 s_boff[kMaxBuckets];
   __shared__ u32 s_hdr[3];
   __shared__ u32 s_nlist, s_ovf, s_npub, s_novf, s_flag, s_floor, s_tlocbin;
-  __shared__ u32 s_cursor, s_snap[2];  // list entries filed into slots so far; this iteration's range
   __shared__ int64_t s_next[2];        // next row pair (double-buffered), -1 when none is left
   __shared__ u32 s_pairs[kMaxPairs];  // row pairs this workgroup streamed
   __shared__ u32 s_npairs;
@@ -1156,7 +1155,6 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
       s_ovf = 0;
       s_npub = 0;
       s_novf = 0;
-      s_cursor = 0;
       s_npairs = 0;
       s_plan_in_lds = false;
     }
@@ -1420,20 +1418,6 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
             rr[u] = __builtin_nontemporal_load(rv + i);
           }
         }
-        if (pst == 2u) {
-          // The plan is in LDS: while this pair's loads are in flight, file
-          // the entries the list gained since the last filing (no wave
-          // appends before the barrier below: the one above ended the last
-          // pair's appends).
-          if (tid == 0) {
-            s_snap[0] = s_cursor;
-            s_snap[1] = std::min(s_nlist, (u32)kListCap);
-            s_cursor = s_snap[1];
-          }
-          __syncthreads();
-          if (s_hdr[2] == 1u && s_hdr[1] >= 1 && s_hdr[1] <= (u32)kMaxBuckets)
-            file_range(s_snap[0], s_snap[1], s_hdr[0], (int)s_hdr[1]);
-        }
         vec_row(2 * p, gg[0], rr[0]);
         vec_row(2 * p + 1, gg[1], rr[1]);
         if (pst == 1u && tid < kMaxBuckets + 3) {
@@ -1499,7 +1483,6 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
       if (tid == 0) {
         s_nlist = 0;
         s_ovf = 0;
-        s_cursor = 0;  // what was filed is filed again, from the first place
         s_novf = 0;
         atomicAdd(&ctl->rescans, 1u);
       }
@@ -1528,10 +1511,8 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
       __syncthreads();
       if (s_ovf) fail |= kWhyList;  // more keys >= T_guess than the list holds
     }
-    // File what the list gained since the last filing (all of it when the
-    // plan arrived after the stream, or after a re-read).
     const u32 nl = std::min(s_nlist, (u32)kListCap);
-    if (!(fail & kWhyList)) file_range(s_cursor, nl, tg, nb);
+    if (!(fail & kWhyList)) file_range(0, nl, tg, nb);
     __syncthreads();
     if (w == 0) {  // candidates, and where each bucket's overflow starts
       const u32 c = s_bcnt[lane];

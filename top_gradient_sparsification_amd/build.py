@@ -31,6 +31,7 @@ COMPILE_FLAGS = [
     "-fno-fast-math",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
+    "-Wshadow",
     "-Wno-unused-result",
     "-I" + INCLUDE,
     "-I" + CSRC,

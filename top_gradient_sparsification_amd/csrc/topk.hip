@@ -1109,6 +1109,11 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
   const int64_t nrows = a.vec ? (a.nv + NT - 1) / NT : (a.n + TE - 1) / TE;
   const int64_t npairs = (nrows + 1) / 2;
   const int ng = phase_groups(G);
+  // aligned mode: rows [0, R0) are dealt statically, one at a time: streaming
+  // workgroup m takes rows m, m + M, ...; the pairs of rows after them, about
+  // a quarter, are handed out at run time
+  const int64_t S = std::min<int64_t>(npairs, std::max<int64_t>(1, (npairs * 3 / 4) / M) * M);
+  const int64_t R0 = std::min<int64_t>(nrows, 2 * S);
 
   // sample loads first, then the first two rows, all in flight together
   float sg[kSampleRounds], sr[kSampleRounds];
@@ -1121,21 +1126,18 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
     sg[j] = sok[j] ? g[i] : 0.0f;
     sr[j] = sok[j] ? r[i] : 0.0f;
   }
-  // two row-pair buffers: A = pair m, B = pair m + M (loads issued now)
-  v4f ag[2], ar[2], bg[2], br[2];
-  auto load_pair = [&](int64_t p, v4f* gg, v4f* rr) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int64_t i = (2 * p + u) * NT + tid;
-      if (i < a.nv) {
-        gg[u] = __builtin_nontemporal_load(gv + i);
-        rr[u] = __builtin_nontemporal_load(rv + i);
-      }
+  // two row buffers: A = row m, B = row m + M (loads issued now)
+  v4f ag, ar, bg, br;
+  auto load_row = [&](int64_t t, v4f& gg, v4f& rr) {
+    const int64_t i = t * NT + tid;
+    if (i < a.nv) {
+      gg = __builtin_nontemporal_load(gv + i);
+      rr = __builtin_nontemporal_load(rv + i);
     }
   };
   if (b > 0 && a.vec) {
-    load_pair(m, ag, ar);
-    load_pair((int64_t)m + M, bg, br);
+    if ((int64_t)m < R0) load_row(m, ag, ar);
+    if ((int64_t)m + M < R0) load_row((int64_t)m + M, bg, br);
   }
 
   // ---------------- sample ----------------
@@ -1247,12 +1249,12 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
     // ---------------- stream ----------------
     const u32 tloc = a.loc_mode == 1u ? 0x7FFFFFFFu : a.loc_mode == 2u ? 0u : s_tlocbin << kHistShift;
     Pair* s_list = (Pair*)s_raw;                      // [kListCap]
-    Pair* s_ovl = (Pair*)(s_raw + 2 * kListCap);     // [kOvfCap] candidates past their S slots
-    u32* s_ovt = s_raw + 2 * kListCap + 2 * kOvfCap;  // [kOvfCap] bucket << 16 | place past S
+    Pair* s_ovl = (Pair*)(s_raw + 2 * kListCap);     // [kOvfCap] candidates past their nslot slots
+    u32* s_ovt = s_raw + 2 * kListCap + 2 * kOvfCap;  // [kOvfCap] bucket << 16 | place past nslot
     static_assert(2 * kListCap + 3 * kOvfCap <= kRawWords, "LDS");
-    const u32 slog = a.slot_log, S = 1u << slog;
+    const u32 slog = a.slot_log, nslot = 1u << slog;  // slots per bucket and workgroup
     // Files list entries [lo, hi) under a plan: a candidate (key >= T_guess)
-    // takes the next place of its bucket; places below S are this
+    // takes the next place of its bucket; places below nslot are this
     // workgroup's slots of the bucket and are written at once, the rest wait
     // here for the overflow area.
     auto file_range = [&](u32 lo, u32 hi, u32 tg, int nb) {
@@ -1263,13 +1265,13 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
         if (key < tg) continue;
         const int j = bucket_of(key, s_lo, nb);
         const u32 pos = atomicAdd(&s_bcnt[j], 1u);
-        if (pos < S) {
+        if (pos < nslot) {
           st_agent64(slots + (((int64_t)j * G + b) << slog) + pos, pack_pair(e));
         } else {
           const u32 q = atomicAdd(&s_novf, 1u);
           if (q < (u32)kOvfCap) {
             s_ovl[q] = e;
-            s_ovt[q] = ((u32)j << 16) | (pos - S);
+            s_ovt[q] = ((u32)j << 16) | (pos - nslot);
           }
         }
       }
@@ -1316,13 +1318,12 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
       }
     };
     if (a.vec) {
-      // Pairs [0, S) are dealt statically: workgroup m takes m, m + M, ...
-      // (no barriers).  Pairs [S, npairs), about a quarter, are handed out
+      // Rows [0, R0) are dealt statically (no barriers).  Pairs [S, npairs)
+      // (rows from R0 = 2S on), about a quarter, are handed out
       // at run time: group x (= b % ng) hands out S + x, S + x + ng, ...
       // from its counter.  Thread 0 asks for the next pair one iteration
       // ahead; when its group has none left it looks at every group's
       // counter and asks the one with the most left.
-      const int64_t S = std::min<int64_t>(npairs, std::max<int64_t>(1, (npairs * 3 / 4) / M) * M);
       u32 xs = (u32)(b % ng);
       u64 pend = 0;
       bool more = npairs > S;
@@ -1358,26 +1359,22 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
         }
         return p;
       };
-      // static pairs m, m + M, ...: buffer A holds one, B the next, and the
-      // loads of the pair after go out before a buffer is processed
-      if (m < S) {
-        vec_row(2 * (int64_t)m, ag[0], ar[0]);
-        vec_row(2 * (int64_t)m + 1, ag[1], ar[1]);
-      }
+      // static rows m, m + M, ...: buffer A holds one, B the next, and the
+      // load of the row after goes out before a buffer is processed (two
+      // rows of a workgroup in flight: more would cost the memory system)
+      if ((int64_t)m < R0) vec_row(m, ag, ar);
       sample_publish();
       bool arrived = false;
-      for (int64_t p = (int64_t)m + M; p < S; p += 2 * (int64_t)M) {
-        if (p + M < S) load_pair(p + M, ag, ar);
-        vec_row(2 * p, bg[0], br[0]);
-        vec_row(2 * p + 1, bg[1], br[1]);
+      for (int64_t t = (int64_t)m + M; t < R0; t += 2 * (int64_t)M) {
+        if (t + M < R0) load_row(t + M, ag, ar);
+        vec_row(t, bg, br);
         if (!arrived) {
           sample_arrive();
           arrived = true;
         }
-        if (p + M >= S) break;
-        if (p + 2 * (int64_t)M < S) load_pair(p + 2 * (int64_t)M, bg, br);
-        vec_row(2 * (p + M), ag[0], ar[0]);
-        vec_row(2 * (p + M) + 1, ag[1], ar[1]);
+        if (t + M >= R0) break;
+        if (t + 2 * (int64_t)M < R0) load_row(t + 2 * (int64_t)M, bg, br);
+        vec_row(t + M, ag, ar);
       }
       if (!arrived) sample_arrive();
       // The plan is usually published while the dynamic pairs stream: thread
@@ -1495,13 +1492,12 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
         }
       };
       if (a.vec) {
-        const int64_t S = std::min<int64_t>(npairs, std::max<int64_t>(1, (npairs * 3 / 4) / M) * M);
-        auto rescan_pair = [&](int64_t p) {
-          rescan(a.head + 4 * 2 * p * NT, a.head + 4 * std::min<int64_t>(a.nv, (2 * p + 2) * NT));
+        auto rescan_rows = [&](int64_t t, int64_t nr) {
+          rescan(a.head + 4 * t * NT, a.head + 4 * std::min<int64_t>(a.nv, (t + nr) * NT));
         };
-        for (int64_t p = m; p < S; p += M) rescan_pair(p);
+        for (int64_t t = m; t < R0; t += M) rescan_rows(t, 1);
         const u32 np = std::min(s_npairs, (u32)kMaxPairs);
-        for (u32 q = 0; q < np; ++q) rescan_pair((int64_t)s_pairs[q]);
+        for (u32 q = 0; q < np; ++q) rescan_rows(2 * (int64_t)s_pairs[q], 2);
         if (s_npairs > (u32)kMaxPairs) atomicOr(&s_ovf, 1u);  // rows not remembered: cannot re-read
       } else {
         for (int64_t t = m; t < nrows; t += M) rescan(t * TE, std::min<int64_t>(a.n, (t + 1) * TE));
@@ -1516,7 +1512,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
     __syncthreads();
     if (w == 0) {  // candidates, and where each bucket's overflow starts
       const u32 c = s_bcnt[lane];
-      const u32 over = c > S ? c - S : 0u;
+      const u32 over = c > nslot ? c - nslot : 0u;
       const u32 xo = wave_inclusive_sum(over);
       s_boff[lane] = xo - over;
       const u32 xc = wave_inclusive_sum(c);

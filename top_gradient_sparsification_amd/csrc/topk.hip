@@ -849,17 +849,16 @@ __device__ __forceinline__ bool step_finish(const StepArgs& a, u32* s_raw, u32* 
   constexpr int NT = kStepThreads;
   constexpr int NW = kStepWaves;
   constexpr int kWords = kMaxBuckets / 2;                // count words per workgroup (two u16)
-  constexpr int kCmStride = kWords + 1;                  // LDS row pitch: a column has no bank conflicts
-  constexpr int kIters = kMaxStepBlocks * kWords / NT;   // count words per thread
+  constexpr int kIters = kMaxStepBlocks * kWords / NT;   // count words per thread (all in one column)
   constexpr int kSlotIters = kSlotTotal / NT;            // slots per thread
   Pair* s_a = (Pair*)s_raw;                      // [kFinishCap] the bucket, as gathered
   Pair* s_b = (Pair*)(s_raw + 2 * kFinishCap);   // [kFinishCap] grouped by key sub-range
   u32* s_sub_cnt = s_raw + 4 * kFinishCap;       // [kSubBins]
   u32* s_sub_off = s_sub_cnt + kSubBins;         // [kSubBins]
   u32* s_part = s_sub_off + kSubBins;            // [NW][kMaxBuckets] partial bucket totals
-  u32* s_cm = (u32*)s_b;                         // [G][kCmStride] the counts, until the sort
-  static_assert(4 * kFinishCap + 2 * kSubBins + NW * kMaxBuckets <= kRawWords, "LDS");
-  static_assert(kMaxStepBlocks * kCmStride <= 2 * kFinishCap + kSubBins, "counts end before s_sub_off");
+  u32* s_cf = s_part + NW * kMaxBuckets;         // [kMaxStepBlocks] bucket f's count per workgroup
+  static_assert(4 * kFinishCap + 2 * kSubBins + NW * kMaxBuckets + kMaxStepBlocks <= kRawWords, "LDS");
+  static_assert(NT % kWords == 0, "a thread's count words share one column");
   __shared__ u32 s_plo[kMaxBuckets];
   __shared__ u32 s_phdr[3];
   __shared__ u32 s_kmin, s_kmax, s_ok, s_wait, s_seen;
@@ -880,6 +879,7 @@ __device__ __forceinline__ bool step_finish(const StepArgs& a, u32* s_raw, u32* 
   if (tid == kMaxBuckets) s_phdr[0] = ld_agent(&ctl->plan.t_guess);
   if (tid == kMaxBuckets + 1) s_phdr[1] = ld_agent(&ctl->plan.nbuckets);
   if (tid == kMaxBuckets + 2) s_phdr[2] = ld_agent(&ctl->plan.valid);
+  for (int i = tid; i < kSubBins; i += NT) s_sub_cnt[i] = 0;
   if (tid == 0) {
     s_wait = flag_wait(&cs->main_go[blockIdx.x & 7], &ctl->err) != 0 ? 1u : 0u;
     s_kmin = 0xFFFFFFFFu;
@@ -904,30 +904,34 @@ __device__ __forceinline__ bool step_finish(const StepArgs& a, u32* s_raw, u32* 
       sv[q] = i < nslots ? ld_agent64(mine + i) : 0u;
     }
     if (tid == 0) s_seen = ld_agent((const u32*)&cs->bad.v);
+    // Thread tid holds column c = tid % 32 (buckets 2c, 2c + 1) of rows
+    // tid / 32 + 32 it.  Its sums, plus those of lane +- 32 (same column),
+    // then of the 16 waves, give the bucket totals; the threads of column
+    // f / 2 keep bucket f's count of each row.
+    const int c = tid % kWords;
+    u32 lo = 0, hi = 0;
 #pragma unroll
     for (int it = 0; it < kIters; ++it) {
-      const int wd = tid + it * NT;
-      s_cm[(wd / kWords) * kCmStride + wd % kWords] = xw[it];
+      lo += xw[it] & 0xFFFFu;
+      hi += xw[it] >> 16;
+    }
+    lo += __shfl_xor(lo, kWords);
+    hi += __shfl_xor(hi, kWords);
+    if (lane < kWords) {
+      s_part[w * kMaxBuckets + 2 * c] = lo;
+      s_part[w * kMaxBuckets + 2 * c + 1] = hi;
+    }
+    if (c == (f >> 1)) {
+#pragma unroll
+      for (int it = 0; it < kIters; ++it) s_cf[tid / kWords + it * (NT / kWords)] = (f & 1) ? xw[it] >> 16 : xw[it] & 0xFFFFu;
     }
   }
   __syncthreads();
-  auto count_of = [&](int row, int j) -> u32 {
-    const u32 x = s_cm[row * kCmStride + (j >> 1)];
-    return (j & 1) ? (x >> 16) : (x & 0xFFFFu);
-  };
-  {  // thread (bucket j, part p) adds rows p, p + 16, ... of column j
-    constexpr int kParts = NT / kMaxBuckets;  // 16
-    const int j = tid & (kMaxBuckets - 1), part = tid / kMaxBuckets;
-    u32 sum = 0;
-#pragma unroll
-    for (int q = 0; q < kMaxStepBlocks / kParts; ++q) sum += count_of(part + q * kParts, j);  // rows >= G hold 0
-    s_part[part * kMaxBuckets + j] = sum;
-  }
   {  // where each workgroup's entries of bucket f go: exclusive prefix over the rows
-    const u32 cnt = tid < G ? count_of(tid, f) : 0u;
+    const u32 cnt = tid < kMaxStepBlocks ? s_cf[tid] : 0u;  // rows >= G hold 0
     u32 tot;
-    const u32 ex = block_exclusive_sum<NT>(cnt, s_scan, tot);  // its barriers publish s_part too
-    if (tid < kMaxStepBlocks) s_rpre[tid] = ex;  // rows >= G: read, never used
+    const u32 ex = block_exclusive_sum<NT>(cnt, s_scan, tot);
+    if (tid < kMaxStepBlocks) s_rpre[tid] = ex;
   }
   // verdict and bucket offsets in wave 0 (lane i = bucket i)
   if (w == 0) {
@@ -982,7 +986,7 @@ __device__ __forceinline__ bool step_finish(const StepArgs& a, u32* s_raw, u32* 
 #pragma unroll
     for (int q = 0; q < kSlotIters; ++q) {
       const int row = std::min((tid + q * NT) >> slog, kMaxStepBlocks - 1);
-      cq[q] = count_of(row, f);
+      cq[q] = s_cf[row];
       pq[q] = s_rpre[row];
     }
 #pragma unroll
@@ -992,12 +996,13 @@ __device__ __forceinline__ bool step_finish(const StepArgs& a, u32* s_raw, u32* 
       if (i < nslots && sl < cq[q]) take_entry(unpack_pair(sv[q]), pq[q] + sl);
     }
     if (tid < G) {
-      const u32 cnt = count_of(tid, f);
+      const u32 cnt = s_cf[tid];
       if (cnt > S) {  // workgroup tid put entries of bucket f in its overflow area
-        u32 off = 0;  // its overflow entries of buckets 0..f-1
+        u32 off = 0;  // its overflow entries of buckets 0..f-1 (its counts, read again)
         for (int j = 0; j < f; ++j) {
-          const u32 c = count_of(tid, j);
-          off += c > S ? c - S : 0u;
+          const u32 x = ld_agent(&a.rcnt[tid * kWords + (j >> 1)]);
+          const u32 cj = (j & 1) ? x >> 16 : x & 0xFFFFu;
+          off += cj > S ? cj - S : 0u;
         }
         const u64* src = a.ovf + (int64_t)tid * kOvfCap + off;
         for (u32 sl = S; sl < cnt; ++sl) take_entry(unpack_pair(ld_agent64(src + (sl - S))), s_rpre[tid] + sl);
@@ -1010,8 +1015,6 @@ __device__ __forceinline__ bool step_finish(const StepArgs& a, u32* s_raw, u32* 
       atomicMax(&s_kmax, kmax);
     }
   }
-  __syncthreads();  // the counts are no longer needed: s_sub_cnt may overwrite them
-  for (int i = tid; i < kSubBins; i += NT) s_sub_cnt[i] = 0;
   __syncthreads();
   // Split [kmin, kmax] into kSubBins equal key sub-ranges numbered from the
   // top and group the entries by sub-range (counting sort); inside a

@@ -56,11 +56,11 @@ def parse():
 # the 256 MiB copy of --copy-calibration.  Valid only for the k_step
 # source they were taken on: `source_sha256` is the hash of csrc/topk.hip then.
 MEASURED_TRAFFIC = {
-    "source_sha256": "1c673e3825de3cac1e88701a9377499af93eb01312dec2efeade46d4b5a04793",
-    # FETCH_SIZE 102,637.6 KiB x (262,144 / 131,083.5: the copy's true read over its counter)
-    "fetch_bytes": 210_183_415,
-    # WRITE_SIZE 101,850.8 KiB x 1.0 (the copy's counter read exactly 262,144 KiB)
-    "write_bytes": 104_295_168,
+    "source_sha256": "5222603f03ba9a6c02403537c2e3336e2e8849018db53a84a5d5b053a0a32543",
+    # FETCH_SIZE 103,058.1 KiB x (262,144 / 131,083.5: the copy's true read over its counter)
+    "fetch_bytes": 211_044_472,
+    # WRITE_SIZE 102,284.9 KiB x 1.0 (the copy's counter read exactly 262,144 KiB)
+    "write_bytes": 104_739_737,
 }
 
 

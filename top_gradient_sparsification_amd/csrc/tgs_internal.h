@@ -41,6 +41,8 @@ struct Pair {
 // Sorts after every real entry (real indices are below 2^31).
 __device__ __forceinline__ Pair pair_sentinel() { return Pair{-1, 0u}; }
 __device__ __forceinline__ u64 pair_rank(const Pair& p) { return rank_key(p.bits, (u32)p.idx); }
+__device__ __forceinline__ u64 pack_pair(const Pair& p) { return (u64)(u32)p.idx | ((u64)p.bits << 32); }
+__device__ __forceinline__ Pair unpack_pair(u64 v) { return Pair{(int32_t)(u32)v, (u32)(v >> 32)}; }
 
 // -------------------------------------------------------- wave helpers ----
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
@@ -172,6 +174,13 @@ __device__ __forceinline__ u32 block_exclusive_sum(u32 v, u32* lds, u32& total) 
 // `gen`, which the others poll.  A bounded spin turns a missing workgroup into
 // an error (flag bit in *err, `abort` set) instead of a hang; after an abort
 // every barrier returns at once.
+//
+// There are no cache fences: every wave waits for its own memory operations
+// to complete before its workgroup arrives, so data that crosses workgroups
+// only has to be written and read at device scope (sc1 stores and loads,
+// atomics), which no L2 holds back or serves stale.  (A fence in every
+// workgroup writes back and invalidates L2 each time: tens of microseconds a
+// barrier on this chip.)
 struct GridBar {
   u32* count;  // zero before the kernel starts
   u32* gen;    // any value
@@ -185,10 +194,7 @@ constexpr u32 kErrBadMergeInput = 1u << 0;
 
 __device__ __forceinline__ bool grid_sync(const GridBar& gb) {
   __shared__ u32 s_ok;
-  // Release: every wave waits for its own global stores and writes back its
-  // L2 before the workgroup arrives (one wave's fence does not cover the
-  // stores other waves still have in flight).
-  __threadfence();
+  wait_all_memory();  // every wave: its own stores have completed at device scope
   __syncthreads();
   if (threadIdx.x == 0) {
     u32 ok = 1;
@@ -196,11 +202,11 @@ __device__ __forceinline__ bool grid_sync(const GridBar& gb) {
       ok = 0;
     } else {
       u32 g0 = ld_agent(gb.gen);
-      u32 t = add_agent_acqrel(gb.count, 1u);
+      u32 t = add_agent_relaxed(gb.count, 1u);
       if (t == gb.nwg - 1) {
         st_agent(gb.count, 0u);
-        __threadfence();
-        add_agent_acqrel(gb.gen, 1u);
+        wait_all_memory();  // the reset lands before anyone can arrive at the next barrier
+        add_agent_relaxed(gb.gen, 1u);
       } else {
         u32 spins = 0;
         while (ld_agent(gb.gen) == g0) {
@@ -221,9 +227,6 @@ __device__ __forceinline__ bool grid_sync(const GridBar& gb) {
     s_ok = ok;
   }
   __syncthreads();
-  // Acquire: every wave drops stale cached lines before reading what other
-  // workgroups wrote.
-  __threadfence();
   return s_ok != 0;
 }
 

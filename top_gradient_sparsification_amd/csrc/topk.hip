@@ -288,7 +288,7 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
     for (int i = tid; i < 2048; i += NT) s_hist[i] = 0;
     __syncthreads();
     for (int64_t i = cb + tid; i < ce; i += NT) {
-      u32 key = key_of_bits(accb[i]);
+      u32 key = key_of_bits(ld_agent(accb + i));
       if ((key >> (sh + wd)) == prefix) atomicAdd(&s_hist[(key >> sh) & (nbins - 1)], 1u);
     }
     __syncthreads();
@@ -297,7 +297,7 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
       if (v) add_agent_relaxed(&a.ghist[L * 2048 + i], v);
     }
     if (!grid_sync(a.bar)) return;
-    for (int i = tid; i < (int)nbins; i += NT) s_hist[i] = a.ghist[L * 2048 + i];
+    for (int i = tid; i < (int)nbins; i += NT) s_hist[i] = ld_agent(&a.ghist[L * 2048 + i]);
     __syncthreads();
     // thread t owns bins [nbins - cpt(t+1), nbins - cpt*t), scanning from the top
     const int cpt = (int)nbins / NT > 0 ? (int)nbins / NT : 1;
@@ -347,15 +347,15 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
   // ---------------- per-workgroup counts ----------------
   u32 c_gt = 0, c_eq = 0;
   for (int64_t i = cb + tid; i < ce; i += NT) {
-    u32 key = key_of_bits(accb[i]);
+    u32 key = key_of_bits(ld_agent(accb + i));
     c_gt += (int64_t)key > t_strict;
     c_eq += (r > 0) && key == t_eq;
   }
   c_gt = block_sum<NT>(c_gt, s_scan);
   c_eq = block_sum<NT>(c_eq, s_scan);
   if (tid == 0) {
-    a.gcnt[2 * b] = c_gt;
-    a.gcnt[2 * b + 1] = c_eq;
+    st_agent(&a.gcnt[2 * b], c_gt);
+    st_agent(&a.gcnt[2 * b + 1], c_eq);
   }
   if (!grid_sync(a.bar)) return;
 
@@ -363,8 +363,8 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
   {
     u32 pg = 0, pe = 0;
     for (int i = tid; i < b; i += NT) {
-      pg += a.gcnt[2 * i];
-      pe += a.gcnt[2 * i + 1];
+      pg += ld_agent(&a.gcnt[2 * i]);
+      pe += ld_agent(&a.gcnt[2 * i + 1]);
     }
     pg = block_sum<NT>(pg, s_scan);
     pe = block_sum<NT>(pe, s_scan);
@@ -373,7 +373,7 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
     for (int64_t base = cb; base < ce; base += NT) {
       int64_t i = base + tid;
       bool valid = i < ce;
-      u32 bits = valid ? accb[i] : 0u;
+      u32 bits = valid ? ld_agent(accb + i) : 0u;
       u32 key = key_of_bits(bits);
       bool gt = valid && (int64_t)key > t_strict;
       bool eq = valid && r > 0 && key == t_eq;
@@ -382,7 +382,7 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
       bool sel = gt || (eq && eq_seen + (int64_t)eq_ex < r);
       u32 sel_tot;
       u32 sel_ex = block_exclusive_sum<NT>(sel ? 1u : 0u, s_scan, sel_tot);
-      if (sel && out + sel_ex < a.k) a.bufA[out + sel_ex] = Pair{(int32_t)i, bits};
+      if (sel && out + sel_ex < a.k) st_agent64((u64*)a.bufA + out + sel_ex, pack_pair(Pair{(int32_t)i, bits}));
       out += sel_tot;
       eq_seen += eq_tot;
     }
@@ -401,22 +401,22 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
     for (int i = tid; i < 256; i += NT) s_hist[i] = 0;
     __syncthreads();
     for (int64_t i = sb + tid; i < se; i += NT) {
-      u32 inv = 0x7FFFFFFFu - key_of_bits(src[i].bits);
+      u32 inv = 0x7FFFFFFFu - key_of_bits(unpack_pair(ld_agent64((const u64*)src + i)).bits);
       atomicAdd(&s_hist[(inv >> sh) & 0xFFu], 1u);
     }
     __syncthreads();
-    for (int i = tid; i < 256; i += NT) a.lsd_cnt[b * 256 + i] = s_hist[i];
+    for (int i = tid; i < 256; i += NT) st_agent(&a.lsd_cnt[b * 256 + i], s_hist[i]);
     if (!grid_sync(a.bar)) return;
     // column scans: digit d handled by workgroup d % G
     for (int d = b; d < 256; d += G) {  // G <= NT: one column entry per thread
-      u32 c = tid < G ? a.lsd_cnt[tid * 256 + d] : 0u;
+      u32 c = tid < G ? ld_agent(&a.lsd_cnt[tid * 256 + d]) : 0u;
       u32 colsum;
       u32 ex = block_exclusive_sum<NT>(c, s_scan, colsum);
-      if (tid < G) a.lsd_pre[tid * 256 + d] = ex;
-      if (tid == 0) a.lsd_tot[d] = colsum;
+      if (tid < G) st_agent(&a.lsd_pre[tid * 256 + d], ex);
+      if (tid == 0) st_agent(&a.lsd_tot[d], colsum);
     }
     if (!grid_sync(a.bar)) return;
-    for (int i = tid; i < 256; i += NT) s_hist[i] = a.lsd_tot[i];
+    for (int i = tid; i < 256; i += NT) s_hist[i] = ld_agent(&a.lsd_tot[i]);
     __syncthreads();
     bool identity = false;
     for (int i = 0; i < 256; ++i) identity = identity || ((int64_t)s_hist[i] == a.k);
@@ -428,7 +428,7 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
       u32 t;
       u32 ex = block_exclusive_sum<NT>(v, s_scan, t);
       if (tid < 256) {
-        s_base[tid] = ex + a.lsd_pre[b * 256 + tid];
+        s_base[tid] = ex + ld_agent(&a.lsd_pre[b * 256 + tid]);
         s_run[tid] = 0;
       }
     }
@@ -437,7 +437,7 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
     for (int64_t base = sb; base < se; base += NT) {
       int64_t i = base + tid;
       bool valid = i < se;
-      Pair e = valid ? src[i] : pair_sentinel();
+      Pair e = valid ? unpack_pair(ld_agent64((const u64*)src + i)) : pair_sentinel();
       u32 d = valid ? (((0x7FFFFFFFu - key_of_bits(e.bits)) >> sh) & 0xFFu) : 0u;
       u64 peers = ballot(valid);
 #pragma unroll
@@ -453,7 +453,7 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
         u32 off = 0;
         for (int ww = 0; ww < w; ++ww) off += s_wcnt[ww][d];
         u32 pos = s_base[d] + s_run[d] + off + rank;
-        if ((int64_t)pos < a.k) dst[pos] = e;
+        if ((int64_t)pos < a.k) st_agent64((u64*)dst + pos, pack_pair(e));
       }
       __syncthreads();
       if (tid < 256) {
@@ -474,10 +474,10 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
 
   // ---------------- emit and zero ----------------
   for (int64_t i = sb + tid; i < se; i += NT) {
-    Pair e = src[i];
+    Pair e = unpack_pair(ld_agent64((const u64*)src + i));
     a.out_idx[i] = e.idx;
     a.out_val[i] = __uint_as_float(e.bits);
-    if (e.idx >= 0 && (int64_t)e.idx < a.n) a.residual[e.idx] = 0.0f;
+    if (e.idx >= 0 && (int64_t)e.idx < a.n) st_agent_f32(a.residual + e.idx, 0.0f);
   }
 }
 
@@ -564,8 +564,6 @@ struct StepArgs {
   GenArgs gen;   // the exact path on this grid
 };
 
-__device__ __forceinline__ u64 pack_pair(const Pair& p) { return (u64)(u32)p.idx | ((u64)p.bits << 32); }
-__device__ __forceinline__ Pair unpack_pair(u64 v) { return Pair{(int32_t)(u32)v, (u32)(v >> 32)}; }
 
 // bucket of a candidate key: #{j < nb : lo[j] > key}, at most nb - 1
 __device__ __forceinline__ int bucket_of(u32 key, const u32* lo, int nb) {
@@ -1556,9 +1554,9 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
     verdict = s_flag;
   }
   if (verdict != 1u) {
-    // The plan did not hold: residual holds acc everywhere, and the whole
-    // grid runs the exact path (grid_sync fences first, so every
-    // workgroup's residual stores are visible to all).
+    // The plan did not hold: residual holds acc everywhere (every store of
+    // it was made at device scope), and the whole grid runs the exact path,
+    // which reads it at device scope.
     if (grid_sync(a.gen.bar)) general_path<NT>(a.gen);
   }
 }

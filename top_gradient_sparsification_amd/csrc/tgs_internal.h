@@ -170,21 +170,23 @@ __device__ __forceinline__ u32 block_exclusive_sum(u32 v, u32* lds, u32& total) 
 
 // ---------------------------------------------------- grid barrier ----
 // For the `nwg` workgroups 0 .. nwg-1 of a kernel whose whole grid is resident
-// at once.  Arrivals go to `count`; the last arrival resets it and bumps
-// `gen`, which the others poll.  A bounded spin turns a missing workgroup into
-// an error (flag bit in *err, `abort` set) instead of a hang; after an abort
-// every barrier returns at once.
+// at once.  Workgroup b arrives at the counter of its group (b % 8); the last
+// arrival of a group resets that counter and arrives at the all-counter; the
+// last of those resets it and bumps the generation, kept in 8 copies so that
+// each group of pollers has its own cache line.  A bounded spin turns a
+// missing workgroup into an error (flag bit in *err, `abort` set) instead of
+// a hang; after an abort every barrier returns at once.
 //
-// There are no cache fences: every wave waits for its own memory operations
-// to complete before its workgroup arrives, so data that crosses workgroups
-// only has to be written and read at device scope (sc1 stores and loads,
-// atomics), which no L2 holds back or serves stale.  (A fence in every
-// workgroup writes back and invalidates L2 each time: tens of microseconds a
-// barrier on this chip.)
+// Writes: every wave waits for its own memory operations to complete before
+// its workgroup arrives, and data that crosses workgroups is stored at device
+// scope (sc1 stores, atomics), which no L2 holds back, so no write-back is
+// needed.  Reads: after the barrier the workgroup drops its cached lines
+// (an agent-scope acquire: L1 and L2 invalidate, no write-back), so plain
+// loads then see what the others wrote.
 struct GridBar {
-  u32* count;  // zero before the kernel starts
-  u32* gen;    // any value
-  u32* abort;  // zero before the kernel starts
+  u32* cnt;    // [9][32]: the 8 group counters, then the all-counter, one cache line each; zero at start
+  u32* gen;    // [8][32]: the generation, one copy per line; any value
+  u32* abort;  // zero at start
   u32* err;    // device error word
   u32 nwg;     // participating workgroups
 };
@@ -201,15 +203,25 @@ __device__ __forceinline__ bool grid_sync(const GridBar& gb) {
     if (ld_agent(gb.abort) != 0) {
       ok = 0;
     } else {
-      u32 g0 = ld_agent(gb.gen);
-      u32 t = add_agent_relaxed(gb.count, 1u);
-      if (t == gb.nwg - 1) {
-        st_agent(gb.count, 0u);
-        wait_all_memory();  // the reset lands before anyone can arrive at the next barrier
-        add_agent_relaxed(gb.gen, 1u);
-      } else {
+      const u32 ng = gb.nwg < 8u ? gb.nwg : 8u;
+      const u32 x = blockIdx.x % ng;
+      u32* mygen = gb.gen + 32 * (blockIdx.x & 7u);
+      const u32 g0 = ld_agent(mygen);
+      const u32 per = (gb.nwg - 1u - x) / ng + 1u;
+      bool bumped = false;
+      if (add_agent_relaxed(gb.cnt + 32 * x, 1u) == per - 1u) {  // last of its group
+        st_agent(gb.cnt + 32 * x, 0u);
+        wait_all_memory();  // the reset lands before this group can arrive again
+        if (add_agent_relaxed(gb.cnt + 32 * 8, 1u) == ng - 1u) {  // last of all
+          st_agent(gb.cnt + 32 * 8, 0u);
+          wait_all_memory();
+          for (int i = 0; i < 8; ++i) add_agent_relaxed(gb.gen + 32 * i, 1u);
+          bumped = true;
+        }
+      }
+      if (!bumped) {
         u32 spins = 0;
-        while (ld_agent(gb.gen) == g0) {
+        while (ld_agent(mygen) == g0) {
           __builtin_amdgcn_s_sleep(2);
           if (++spins > (1u << 23)) {
             atomicOr(gb.err, kErrBarrierTimeout);
@@ -226,6 +238,7 @@ __device__ __forceinline__ bool grid_sync(const GridBar& gb) {
     }
     s_ok = ok;
   }
+  if (threadIdx.x < kWave) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   __syncthreads();
   return s_ok != 0;
 }

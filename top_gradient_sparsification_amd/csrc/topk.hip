@@ -149,9 +149,9 @@ static_assert(sizeof(StepCtl) <= kWorkspaceHeader, "control block exceeds the wo
 // State of the general path (zero when it starts).
 struct GenState {
   u32 hist[3][2048];
-  u32 bar_count;
+  u32 bar_cnt[9][32];  // grid barrier counters, one cache line each
+  u32 bar_gen[8][32];  // grid barrier generation, 8 copies
   u32 bar_abort;
-  u32 bar_gen;
 };
 
 struct TopkLayout {
@@ -255,9 +255,10 @@ __device__ __forceinline__ u32 block_sum(u32 v, u32* lds) {
 }
 
 // The exact general path, run by workgroups 0 .. a.bar.nwg-1, which must all
-// be resident at once (grid barriers); NT is the workgroup size.  acc is read
-// from residual, which every participant must be able to see.
-template <int NT>
+// be resident at once (grid barriers); NT is the workgroup size and V the
+// rows of NT entries each pass keeps in flight per tile.  acc is read from
+// residual, which every participant must be able to see.
+template <int NT, int V>
 __device__ __forceinline__ void general_path(const GenArgs& a) {
   constexpr int NW = NT / kWave;
   __shared__ u32 s_hist[2048];
@@ -266,13 +267,28 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
   __shared__ u32 s_run[256];
   __shared__ u32 s_scan[NW + 1];
   __shared__ u32 s_found[4];
+  __shared__ u32 s_rc[V * NW];          // per (row, wave): greater | equal << 16
+  __shared__ u32 s_rtot;
   const int tid = threadIdx.x;
+  const int lane = lane_id();
   const int G = (int)a.bar.nwg;
   const int b = blockIdx.x;
   const int64_t per = (a.n + G - 1) / G;
   const int64_t cb = std::min<int64_t>(a.n, (int64_t)b * per);
   const int64_t ce = std::min<int64_t>(a.n, cb + per);
   const u32* accb = (const u32*)a.acc;
+  // Entry base + j NT + tid of a tile (j < V); past ce, valid is false.  The
+  // loads are unconditional (an index past the end reads entry cb instead),
+  // so all V are in flight before any is used: a load under a branch would
+  // be waited for on its own.
+  auto load_tile = [&](int64_t base, u32* bits, bool* valid) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const int64_t i = base + (int64_t)j * NT + tid;
+      valid[j] = i < ce;
+      bits[j] = accb[valid[j] ? i : cb];
+    }
+  };
 
   // ---------------- radix select of the k-th largest key ----------------
   const int shifts[3] = {20, 9, 0};
@@ -287,9 +303,15 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
     const u32 nbins = 1u << wd;
     for (int i = tid; i < 2048; i += NT) s_hist[i] = 0;
     __syncthreads();
-    for (int64_t i = cb + tid; i < ce; i += NT) {
-      u32 key = key_of_bits(ld_agent(accb + i));
-      if ((key >> (sh + wd)) == prefix) atomicAdd(&s_hist[(key >> sh) & (nbins - 1)], 1u);
+    for (int64_t base = cb; base < ce; base += (int64_t)V * NT) {
+      u32 bits[V];
+      bool valid[V];
+      load_tile(base, bits, valid);
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        const u32 key = key_of_bits(bits[j]);
+        if (valid[j] && (key >> (sh + wd)) == prefix) atomicAdd(&s_hist[(key >> sh) & (nbins - 1)], 1u);
+      }
     }
     __syncthreads();
     for (int i = tid; i < (int)nbins; i += NT) {
@@ -297,7 +319,7 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
       if (v) add_agent_relaxed(&a.ghist[L * 2048 + i], v);
     }
     if (!grid_sync(a.bar)) return;
-    for (int i = tid; i < (int)nbins; i += NT) s_hist[i] = ld_agent(&a.ghist[L * 2048 + i]);
+    for (int i = tid; i < (int)nbins; i += NT) s_hist[i] = a.ghist[L * 2048 + i];
     __syncthreads();
     // thread t owns bins [nbins - cpt(t+1), nbins - cpt*t), scanning from the top
     const int cpt = (int)nbins / NT > 0 ? (int)nbins / NT : 1;
@@ -346,10 +368,16 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
 
   // ---------------- per-workgroup counts ----------------
   u32 c_gt = 0, c_eq = 0;
-  for (int64_t i = cb + tid; i < ce; i += NT) {
-    u32 key = key_of_bits(ld_agent(accb + i));
-    c_gt += (int64_t)key > t_strict;
-    c_eq += (r > 0) && key == t_eq;
+  for (int64_t base = cb; base < ce; base += (int64_t)V * NT) {
+    u32 bits[V];
+    bool valid[V];
+    load_tile(base, bits, valid);
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const u32 key = key_of_bits(bits[j]);
+      c_gt += valid[j] && (int64_t)key > t_strict;
+      c_eq += valid[j] && (r > 0) && key == t_eq;
+    }
   }
   c_gt = block_sum<NT>(c_gt, s_scan);
   c_eq = block_sum<NT>(c_eq, s_scan);
@@ -363,28 +391,66 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
   {
     u32 pg = 0, pe = 0;
     for (int i = tid; i < b; i += NT) {
-      pg += ld_agent(&a.gcnt[2 * i]);
-      pe += ld_agent(&a.gcnt[2 * i + 1]);
+      pg += a.gcnt[2 * i];
+      pe += a.gcnt[2 * i + 1];
     }
     pg = block_sum<NT>(pg, s_scan);
     pe = block_sum<NT>(pe, s_scan);
-    int64_t out = (int64_t)pg + std::min<int64_t>((int64_t)pe, r);
-    int64_t eq_seen = pe;
-    for (int64_t base = cb; base < ce; base += NT) {
-      int64_t i = base + tid;
-      bool valid = i < ce;
-      u32 bits = valid ? ld_agent(accb + i) : 0u;
-      u32 key = key_of_bits(bits);
-      bool gt = valid && (int64_t)key > t_strict;
-      bool eq = valid && r > 0 && key == t_eq;
-      u32 eq_tot;
-      u32 eq_ex = block_exclusive_sum<NT>(eq ? 1u : 0u, s_scan, eq_tot);
-      bool sel = gt || (eq && eq_seen + (int64_t)eq_ex < r);
-      u32 sel_tot;
-      u32 sel_ex = block_exclusive_sum<NT>(sel ? 1u : 0u, s_scan, sel_tot);
-      if (sel && out + sel_ex < a.k) st_agent64((u64*)a.bufA + out + sel_ex, pack_pair(Pair{(int32_t)i, bits}));
-      out += sel_tot;
-      eq_seen += eq_tot;
+    // An entry's place: (greater keys before it) + min(equal keys before
+    // it, r), both counted over the whole vector in index order; it is
+    // selected if its key is greater, or equal with fewer than r equal keys
+    // before it.  Per tile: a ballot per row and wave, one wave's scan over
+    // the V x NW counts, then every entry knows both numbers.
+    int64_t gt_seen = pg, eq_seen = pe;  // over the entries before this tile
+    const int w = tid / kWave;
+    for (int64_t base = cb; base < ce; base += (int64_t)V * NT) {
+      u32 bits[V];
+      bool valid[V];
+      load_tile(base, bits, valid);
+      u32 below[V];  // greater | equal << 16 among the lanes below, per row
+      bool gt[V], eq[V];
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        const u32 key = key_of_bits(bits[j]);
+        gt[j] = valid[j] && (int64_t)key > t_strict;
+        eq[j] = valid[j] && r > 0 && key == t_eq;
+        const u64 bg = ballot(gt[j]), be = ballot(eq[j]);
+        below[j] = lanes_below(bg) | (lanes_below(be) << 16);
+        if (lane == 0) s_rc[j * NW + w] = (u32)__popcll(bg) | ((u32)__popcll(be) << 16);
+      }
+      __syncthreads();
+      if (w == 0) {  // exclusive prefix over (row, wave) in index order
+        constexpr int cpl = V * NW / kWave;  // counts per lane
+        static_assert(V * NW % kWave == 0, "tile counts split evenly over a wave");
+        u32 v[cpl], own = 0;
+#pragma unroll
+        for (int q = 0; q < cpl; ++q) {
+          v[q] = s_rc[lane * cpl + q];
+          own += v[q];
+        }
+        const u32 incl = wave_inclusive_sum(own);
+        u32 ex = incl - own;
+#pragma unroll
+        for (int q = 0; q < cpl; ++q) {
+          s_rc[lane * cpl + q] = ex;
+          ex += v[q];
+        }
+        if (lane == kWave - 1) s_rtot = incl;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        const u32 pre = s_rc[j * NW + w] + below[j];
+        const int64_t gb = gt_seen + (pre & 0xFFFFu), eb = eq_seen + (pre >> 16);
+        const bool sel = gt[j] || (eq[j] && eb < r);
+        const int64_t pos = gb + std::min<int64_t>(eb, r);
+        if (sel && pos < a.k)
+          st_agent64((u64*)a.bufA + pos, pack_pair(Pair{(int32_t)(base + (int64_t)j * NT + tid), bits[j]}));
+      }
+      const u32 tt = s_rtot;
+      gt_seen += tt & 0xFFFFu;
+      eq_seen += tt >> 16;
+      __syncthreads();  // s_rc and s_rtot are rewritten by the next tile
     }
   }
   if (!grid_sync(a.bar)) return;
@@ -400,23 +466,32 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
     const int sh = 8 * pass;
     for (int i = tid; i < 256; i += NT) s_hist[i] = 0;
     __syncthreads();
-    for (int64_t i = sb + tid; i < se; i += NT) {
-      u32 inv = 0x7FFFFFFFu - key_of_bits(unpack_pair(ld_agent64((const u64*)src + i)).bits);
-      atomicAdd(&s_hist[(inv >> sh) & 0xFFu], 1u);
+    for (int64_t base = sb; base < se; base += (int64_t)V * NT) {
+      u64 pv[V];
+#pragma unroll
+      for (int j = 0; j < V; ++j) {  // unconditional loads (see load_tile)
+        const int64_t i = base + (int64_t)j * NT + tid;
+        pv[j] = ((const u64*)src)[i < se ? i : sb];
+      }
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        const u32 inv = 0x7FFFFFFFu - key_of_bits(unpack_pair(pv[j]).bits);
+        if (base + (int64_t)j * NT + tid < se) atomicAdd(&s_hist[(inv >> sh) & 0xFFu], 1u);
+      }
     }
     __syncthreads();
     for (int i = tid; i < 256; i += NT) st_agent(&a.lsd_cnt[b * 256 + i], s_hist[i]);
     if (!grid_sync(a.bar)) return;
     // column scans: digit d handled by workgroup d % G
     for (int d = b; d < 256; d += G) {  // G <= NT: one column entry per thread
-      u32 c = tid < G ? ld_agent(&a.lsd_cnt[tid * 256 + d]) : 0u;
+      u32 c = tid < G ? a.lsd_cnt[tid * 256 + d] : 0u;
       u32 colsum;
       u32 ex = block_exclusive_sum<NT>(c, s_scan, colsum);
       if (tid < G) st_agent(&a.lsd_pre[tid * 256 + d], ex);
       if (tid == 0) st_agent(&a.lsd_tot[d], colsum);
     }
     if (!grid_sync(a.bar)) return;
-    for (int i = tid; i < 256; i += NT) s_hist[i] = ld_agent(&a.lsd_tot[i]);
+    for (int i = tid; i < 256; i += NT) s_hist[i] = a.lsd_tot[i];
     __syncthreads();
     bool identity = false;
     for (int i = 0; i < 256; ++i) identity = identity || ((int64_t)s_hist[i] == a.k);
@@ -428,16 +503,29 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
       u32 t;
       u32 ex = block_exclusive_sum<NT>(v, s_scan, t);
       if (tid < 256) {
-        s_base[tid] = ex + ld_agent(&a.lsd_pre[b * 256 + tid]);
+        s_base[tid] = ex + a.lsd_pre[b * 256 + tid];
         s_run[tid] = 0;
       }
     }
     for (int i = tid; i < NW * 256; i += NT) (&s_wcnt[0][0])[i] = 0;
     __syncthreads();
+    // rows of NT entries, V rows' loads in flight at a time
+    u64 pv[V];
     for (int64_t base = sb; base < se; base += NT) {
+      const int64_t row = (base - sb) / NT;
+      if (row % V == 0) {
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+          const int64_t i = base + (int64_t)j * NT + tid;
+          pv[j] = ((const u64*)src)[i < se ? i : sb];
+        }
+      }
       int64_t i = base + tid;
       bool valid = i < se;
-      Pair e = valid ? unpack_pair(ld_agent64((const u64*)src + i)) : pair_sentinel();
+      u64 cur = pv[0];
+#pragma unroll
+      for (int j = 1; j < V; ++j) cur = (row % V == j) ? pv[j] : cur;
+      Pair e = valid ? unpack_pair(cur) : pair_sentinel();
       u32 d = valid ? (((0x7FFFFFFFu - key_of_bits(e.bits)) >> sh) & 0xFFu) : 0u;
       u64 peers = ballot(valid);
 #pragma unroll
@@ -473,11 +561,22 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
   }
 
   // ---------------- emit and zero ----------------
-  for (int64_t i = sb + tid; i < se; i += NT) {
-    Pair e = unpack_pair(ld_agent64((const u64*)src + i));
-    a.out_idx[i] = e.idx;
-    a.out_val[i] = __uint_as_float(e.bits);
-    if (e.idx >= 0 && (int64_t)e.idx < a.n) st_agent_f32(a.residual + e.idx, 0.0f);
+  for (int64_t base = sb; base < se; base += (int64_t)V * NT) {
+    u64 pv[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const int64_t i = base + (int64_t)j * NT + tid;
+      pv[j] = ((const u64*)src)[i < se ? i : sb];
+    }
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const int64_t i = base + (int64_t)j * NT + tid;
+      if (i >= se) continue;
+      const Pair e = unpack_pair(pv[j]);
+      a.out_idx[i] = e.idx;
+      a.out_val[i] = __uint_as_float(e.bits);
+      if (e.idx >= 0 && (int64_t)e.idx < a.n) st_agent_f32(a.residual + e.idx, 0.0f);
+    }
   }
 }
 
@@ -534,7 +633,7 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_pass(AccArgs a) {
   }
 }
 
-__global__ __launch_bounds__(kGenThreads) void k_general(GenArgs a) { general_path<kGenThreads>(a); }
+__global__ __launch_bounds__(kGenThreads) void k_general(GenArgs a) { general_path<kGenThreads, 16>(a); }
 
 // ------------------------------------------------------------- k_step ----
 struct StepArgs {
@@ -1557,7 +1656,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
     // The plan did not hold: residual holds acc everywhere (every store of
     // it was made at device scope), and the whole grid runs the exact path,
     // which reads it at device scope.
-    if (grid_sync(a.gen.bar)) general_path<NT>(a.gen);
+    if (grid_sync(a.gen.bar)) general_path<NT, 4>(a.gen);  // rarely taken: kept small
   }
 }
 
@@ -1672,8 +1771,8 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
   ga.lsd_tot = (u32*)(ws + L.lsd_tot);
   ga.bufA = (Pair*)(ws + L.bufA);
   ga.bufB = (Pair*)(ws + L.bufB);
-  ga.bar.count = &gs->bar_count;
-  ga.bar.gen = &gs->bar_gen;
+  ga.bar.cnt = &gs->bar_cnt[0][0];
+  ga.bar.gen = &gs->bar_gen[0][0];
   ga.bar.abort = &gs->bar_abort;
   ga.bar.err = &ctl->err;
 

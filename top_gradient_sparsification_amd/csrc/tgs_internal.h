@@ -99,6 +99,20 @@ __device__ __forceinline__ void st_agent_v4_nt(v4f* base, u32 nbytes, u32 off, v
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)nbytes, 0x00020000);
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), rs, (int)off, 0, kPolicyNtSc1);
 }
+// The same uniform value in a scalar register the compiler cannot trace back
+// to where it came from.  Kernel arguments are loaded as wide scalar blocks
+// that stay one register tuple; under register pressure a spilled tuple is
+// reloaded whole (16 registers) wherever any one of its fields is used.
+__device__ __forceinline__ u32 opaque_u32(u32 v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
+template <class T>
+__device__ __forceinline__ T* opaque_ptr(T* p) {
+  u64 v = (u64)p;
+  asm volatile("" : "+s"(v));
+  return (T*)v;
+}
 // Waits until every memory access this wave issued has completed.
 __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
 

@@ -171,7 +171,7 @@ static TopkLayout topk_layout(int64_t n, int64_t k) {
   };
   L.ctl = take(kWorkspaceHeader);
   L.gstate = take(sizeof(GenState));
-  L.gcnt = take(sizeof(u32) * 2 * kMaxGenWG);
+  L.gcnt = take(sizeof(u32) * 2 * kMaxGenWG * (kStepThreads / kWave));  // per (workgroup, wave)
   L.lsd_cnt = take(sizeof(u32) * 256 * kMaxGenWG);
   L.lsd_pre = take(sizeof(u32) * 256 * kMaxGenWG);
   L.lsd_tot = take(sizeof(u32) * 256);
@@ -237,7 +237,7 @@ struct GenArgs {
   int32_t* out_idx;
   float* out_val;
   u32* ghist;    // 3 x 2048, zero on entry
-  u32* gcnt;     // [G][2]
+  u32* gcnt;     // [G][waves][2]
   u32* lsd_cnt;  // [G][256]
   u32* lsd_pre;  // [G][256]
   u32* lsd_tot;  // [256]
@@ -256,9 +256,10 @@ __device__ __forceinline__ u32 block_sum(u32 v, u32* lds) {
 
 // The exact general path, run by workgroups 0 .. a.bar.nwg-1, which must all
 // be resident at once (grid barriers); NT is the workgroup size and V the
-// rows of NT entries each pass keeps in flight per tile.  acc is read from
+// rows of NT entries each pass keeps in flight per tile (kPipe: the next
+// tile's loads go out before a tile is processed).  acc is read from
 // residual, which every participant must be able to see.
-template <int NT, int V>
+template <int NT, int V, bool kPipe>
 __device__ __forceinline__ void general_path(const GenArgs& a) {
   constexpr int NW = NT / kWave;
   __shared__ u32 s_hist[2048];
@@ -267,8 +268,6 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
   __shared__ u32 s_run[256];
   __shared__ u32 s_scan[NW + 1];
   __shared__ u32 s_found[4];
-  __shared__ u32 s_rc[V * NW];          // per (row, wave): greater | equal << 16
-  __shared__ u32 s_rtot;
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int G = (int)a.bar.nwg;
@@ -277,16 +276,44 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
   const int64_t cb = std::min<int64_t>(a.n, (int64_t)b * per);
   const int64_t ce = std::min<int64_t>(a.n, cb + per);
   const u32* accb = (const u32*)a.acc;
-  // Entry base + j NT + tid of a tile (j < V); past ce, valid is false.  The
-  // loads are unconditional (an index past the end reads entry cb instead),
-  // so all V are in flight before any is used: a load under a branch would
-  // be waited for on its own.
-  auto load_tile = [&](int64_t base, u32* bits, bool* valid) {
+  // Entry base + j NT + tid of a tile (j < V); bit j of the returned mask
+  // says whether it lies before ce.  The loads are unconditional (an index
+  // past the end reads entry cb instead), so all V are in flight before any
+  // is used: a load under a branch would be waited for on its own.  Per-entry
+  // flags live in bit masks: bool arrays become wave masks in scalar
+  // registers, which spill.
+  // Offsets are 32-bit and relative to cb (a chunk is below 2^31 entries).
+  const u32* accc = opaque_ptr(accb + cb);
+  const u32 clen = opaque_u32((u32)(ce - cb));
+  auto load_tile = [&](int64_t base, u32* bits) -> u32 {
+    const u32 o0 = (u32)(base - cb) + (u32)tid;
+    u32 vm = 0;
 #pragma unroll
     for (int j = 0; j < V; ++j) {
-      const int64_t i = base + (int64_t)j * NT + tid;
-      valid[j] = i < ce;
-      bits[j] = accb[valid[j] ? i : cb];
+      const u32 o = o0 + (u32)(j * NT);
+      const bool in = o < clen;
+      vm |= (u32)in << j;
+      bits[j] = accc[in ? o : 0u];
+    }
+    return vm;
+  };
+  // body(base, bits, valid) on every tile of [cb, ce) in order; the next
+  // tile's loads are in flight while one is processed (one workgroup per
+  // compute unit needs two tiles in flight to keep HBM busy).
+  auto for_each_tile = [&](auto&& body) {
+    constexpr int64_t TS = (int64_t)V * NT;
+    u32 b0[V], b1[V];
+    if constexpr (kPipe) {
+      u32 v0 = cb < ce ? load_tile(cb, b0) : 0u, v1;
+      for (int64_t base = cb; base < ce; base += 2 * TS) {
+        v1 = load_tile(base + TS, b1);
+        body(base, b0, v0);
+        if (base + TS >= ce) break;
+        v0 = load_tile(base + 2 * TS, b0);
+        body(base + TS, b1, v1);
+      }
+    } else {
+      for (int64_t base = cb; base < ce; base += TS) body(base, b0, load_tile(base, b0));
     }
   };
 
@@ -303,16 +330,13 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
     const u32 nbins = 1u << wd;
     for (int i = tid; i < 2048; i += NT) s_hist[i] = 0;
     __syncthreads();
-    for (int64_t base = cb; base < ce; base += (int64_t)V * NT) {
-      u32 bits[V];
-      bool valid[V];
-      load_tile(base, bits, valid);
+    for_each_tile([&](int64_t, const u32* bits, u32 vm) {
 #pragma unroll
       for (int j = 0; j < V; ++j) {
         const u32 key = key_of_bits(bits[j]);
-        if (valid[j] && (key >> (sh + wd)) == prefix) atomicAdd(&s_hist[(key >> sh) & (nbins - 1)], 1u);
+        if (((vm >> j) & 1u) && (key >> (sh + wd)) == prefix) atomicAdd(&s_hist[(key >> sh) & (nbins - 1)], 1u);
       }
-    }
+    });
     __syncthreads();
     for (int i = tid; i < (int)nbins; i += NT) {
       u32 v = s_hist[i];
@@ -366,92 +390,97 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
     __syncthreads();
   }
 
-  // ---------------- per-workgroup counts ----------------
-  u32 c_gt = 0, c_eq = 0;
-  for (int64_t base = cb; base < ce; base += (int64_t)V * NT) {
-    u32 bits[V];
-    bool valid[V];
-    load_tile(base, bits, valid);
+  // ---------------- per-wave counts ----------------
+  // Wave w owns the contiguous slice [wb, we) of the workgroup's chunk; the
+  // counts and the ordered compaction walk it in rows of 64 entries, V rows
+  // per tile, so the compaction needs no barrier and no LDS.  Counts,
+  // places and indices fit in 32 bits (n < 2^31).
+  const int w = tid / kWave;
+  const u32 wlen = (clen + NW - 1) / NW;
+  const u32 wb = std::min<u32>(clen, (u32)w * wlen), we = std::min<u32>(clen, wb + wlen);
+  auto load_wave_tile = [&](u32 o, u32* bits) -> u32 {
+    u32 vm = 0;
 #pragma unroll
     for (int j = 0; j < V; ++j) {
-      const u32 key = key_of_bits(bits[j]);
-      c_gt += valid[j] && (int64_t)key > t_strict;
-      c_eq += valid[j] && (r > 0) && key == t_eq;
+      const u32 q = o + (u32)(j * kWave + lane);
+      const bool in = q < we;
+      vm |= (u32)in << j;
+      bits[j] = accc[in ? q : 0u];
     }
-  }
-  c_gt = block_sum<NT>(c_gt, s_scan);
-  c_eq = block_sum<NT>(c_eq, s_scan);
-  if (tid == 0) {
-    st_agent(&a.gcnt[2 * b], c_gt);
-    st_agent(&a.gcnt[2 * b + 1], c_eq);
+    return vm;
+  };
+  auto for_each_wave_tile = [&](auto&& body) {
+    constexpr u32 TS = (u32)(V * kWave);
+    u32 b0[V], b1[V];
+    if constexpr (kPipe) {
+      u32 v0 = wb < we ? load_wave_tile(wb, b0) : 0u, v1;
+      for (u32 o = wb; o < we; o += 2 * TS) {
+        v1 = load_wave_tile(o + TS, b1);
+        body(o, b0, v0);
+        if (o + TS >= we) break;
+        v0 = load_wave_tile(o + 2 * TS, b0);
+        body(o + TS, b1, v1);
+      }
+    } else {
+      for (u32 o = wb; o < we; o += TS) body(o, b0, load_wave_tile(o, b0));
+    }
+  };
+  const u32 t_lo = (u32)(t_strict + 1), r32 = (u32)r, k32 = opaque_u32((u32)a.k);
+  {
+    u32 c_gt = 0, c_eq = 0;
+    for_each_wave_tile([&](u32, const u32* bits, u32 vm) {
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        const u32 key = key_of_bits(bits[j]);
+        const bool in = (vm >> j) & 1u;
+        c_gt += in && key >= t_lo;
+        c_eq += in && r32 > 0 && key == t_eq;
+      }
+    });
+    c_gt = wave_sum(c_gt);
+    c_eq = wave_sum(c_eq);
+    if (lane == 0) {
+      st_agent(&a.gcnt[2 * (b * NW + w)], c_gt);
+      st_agent(&a.gcnt[2 * (b * NW + w) + 1], c_eq);
+    }
   }
   if (!grid_sync(a.bar)) return;
 
   // ---------------- ordered compaction (ascending index) ----------------
   {
+    // greater / equal keys in every slice before this wave's, in index order
     u32 pg = 0, pe = 0;
-    for (int i = tid; i < b; i += NT) {
+    for (int i = tid; i < b * NW; i += NT) {
       pg += a.gcnt[2 * i];
       pe += a.gcnt[2 * i + 1];
     }
     pg = block_sum<NT>(pg, s_scan);
     pe = block_sum<NT>(pe, s_scan);
-    // An entry's place: (greater keys before it) + min(equal keys before
-    // it, r), both counted over the whole vector in index order; it is
-    // selected if its key is greater, or equal with fewer than r equal keys
-    // before it.  Per tile: a ballot per row and wave, one wave's scan over
-    // the V x NW counts, then every entry knows both numbers.
-    int64_t gt_seen = pg, eq_seen = pe;  // over the entries before this tile
-    const int w = tid / kWave;
-    for (int64_t base = cb; base < ce; base += (int64_t)V * NT) {
-      u32 bits[V];
-      bool valid[V];
-      load_tile(base, bits, valid);
-      u32 below[V];  // greater | equal << 16 among the lanes below, per row
-      bool gt[V], eq[V];
+    for (int q = 0; q < w; ++q) {
+      pg += a.gcnt[2 * (b * NW + q)];
+      pe += a.gcnt[2 * (b * NW + q) + 1];
+    }
+    // An entry's place: (greater keys before it) + min(equal keys before it,
+    // r); it is selected if its key is greater, or equal with fewer than r
+    // equal keys before it.
+    u32 gt_seen = pg, eq_seen = pe;
+    u64* const outA = opaque_ptr((u64*)a.bufA);
+    const u32 i0 = (u32)cb + (u32)lane;
+    for_each_wave_tile([&](u32 o, const u32* bits, u32 vm) {
 #pragma unroll
       for (int j = 0; j < V; ++j) {
         const u32 key = key_of_bits(bits[j]);
-        gt[j] = valid[j] && (int64_t)key > t_strict;
-        eq[j] = valid[j] && r > 0 && key == t_eq;
-        const u64 bg = ballot(gt[j]), be = ballot(eq[j]);
-        below[j] = lanes_below(bg) | (lanes_below(be) << 16);
-        if (lane == 0) s_rc[j * NW + w] = (u32)__popcll(bg) | ((u32)__popcll(be) << 16);
+        const bool in = (vm >> j) & 1u;
+        const bool g = in && key >= t_lo, e = in && r32 > 0 && key == t_eq;
+        const u64 bg = ballot(g), be = ballot(e);
+        const u32 gb = gt_seen + lanes_below(bg), eb = eq_seen + lanes_below(be);
+        const bool sel = g || (e && eb < r32);
+        const u32 pos = gb + std::min(eb, r32);
+        if (sel && pos < k32) st_agent64(outA + pos, pack_pair(Pair{(int32_t)(i0 + o + (u32)(j * kWave)), bits[j]}));
+        gt_seen += (u32)__popcll(bg);
+        eq_seen += (u32)__popcll(be);
       }
-      __syncthreads();
-      if (w == 0) {  // exclusive prefix over (row, wave) in index order
-        constexpr int cpl = V * NW / kWave;  // counts per lane
-        static_assert(V * NW % kWave == 0, "tile counts split evenly over a wave");
-        u32 v[cpl], own = 0;
-#pragma unroll
-        for (int q = 0; q < cpl; ++q) {
-          v[q] = s_rc[lane * cpl + q];
-          own += v[q];
-        }
-        const u32 incl = wave_inclusive_sum(own);
-        u32 ex = incl - own;
-#pragma unroll
-        for (int q = 0; q < cpl; ++q) {
-          s_rc[lane * cpl + q] = ex;
-          ex += v[q];
-        }
-        if (lane == kWave - 1) s_rtot = incl;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < V; ++j) {
-        const u32 pre = s_rc[j * NW + w] + below[j];
-        const int64_t gb = gt_seen + (pre & 0xFFFFu), eb = eq_seen + (pre >> 16);
-        const bool sel = gt[j] || (eq[j] && eb < r);
-        const int64_t pos = gb + std::min<int64_t>(eb, r);
-        if (sel && pos < a.k)
-          st_agent64((u64*)a.bufA + pos, pack_pair(Pair{(int32_t)(base + (int64_t)j * NT + tid), bits[j]}));
-      }
-      const u32 tt = s_rtot;
-      gt_seen += tt & 0xFFFFu;
-      eq_seen += tt >> 16;
-      __syncthreads();  // s_rc and s_rtot are rewritten by the next tile
-    }
+    });
   }
   if (!grid_sync(a.bar)) return;
 
@@ -461,7 +490,6 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
   const int64_t se = std::min<int64_t>(a.k, sb + per2);
   Pair* src = a.bufA;
   Pair* dst = a.bufB;
-  const int w = tid / kWave;
   for (int pass = 0; pass < 4; ++pass) {
     const int sh = 8 * pass;
     for (int i = tid; i < 256; i += NT) s_hist[i] = 0;
@@ -492,12 +520,11 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
     }
     if (!grid_sync(a.bar)) return;
     for (int i = tid; i < 256; i += NT) s_hist[i] = a.lsd_tot[i];
+    if (tid == 0) s_found[3] = 0;
     __syncthreads();
-    bool identity = false;
-    for (int i = 0; i < 256; ++i) identity = identity || ((int64_t)s_hist[i] == a.k);
-    // every wave must finish reading s_hist before the next pass clears it
+    if (tid < 256 && (int64_t)s_hist[tid] == a.k) s_found[3] = 1;
     __syncthreads();
-    if (identity) continue;  // every key shares this digit: the pass is a no-op
+    if (s_found[3] != 0) continue;  // every key shares this digit: the pass is a no-op
     {
       u32 v = tid < 256 ? s_hist[tid] : 0u;
       u32 t;
@@ -633,7 +660,7 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_pass(AccArgs a) {
   }
 }
 
-__global__ __launch_bounds__(kGenThreads) void k_general(GenArgs a) { general_path<kGenThreads, 16>(a); }
+__global__ __launch_bounds__(kGenThreads) void k_general(GenArgs a) { general_path<kGenThreads, 16, true>(a); }
 
 // ------------------------------------------------------------- k_step ----
 struct StepArgs {
@@ -1656,7 +1683,9 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
     // The plan did not hold: residual holds acc everywhere (every store of
     // it was made at device scope), and the whole grid runs the exact path,
     // which reads it at device scope.
-    if (grid_sync(a.gen.bar)) general_path<NT, 4>(a.gen);  // rarely taken: kept small
+    // rarely taken: one row per tile keeps this copy of the general path small
+    // (a larger one costs the fast path registers and time even unused)
+    if (grid_sync(a.gen.bar)) general_path<NT, 1, false>(a.gen);
   }
 }
 

@@ -91,6 +91,7 @@ constexpr int kMaxAccBlocks = 2048;
 constexpr int kGenThreads = 512;
 constexpr int kGenBlocks = 256;
 constexpr int kMaxGenWG = 256;  // workgroups of either general-path launch
+constexpr int kLsdDigits = 512;  // digits of an LSD pass at most (9 bits)
 
 // reasons a plan did not hold (StepCtl::why)
 constexpr u32 kWhyPlan = 1u, kWhyBucket = 4u, kWhyFew = 8u, kWhyRegion = 16u, kWhyList = 32u, kWhyWait = 64u;
@@ -172,9 +173,9 @@ static TopkLayout topk_layout(int64_t n, int64_t k) {
   L.ctl = take(kWorkspaceHeader);
   L.gstate = take(sizeof(GenState));
   L.gcnt = take(sizeof(u32) * 2 * kMaxGenWG * (kStepThreads / kWave));  // per (workgroup, wave)
-  L.lsd_cnt = take(sizeof(u32) * 256 * kMaxGenWG);
-  L.lsd_pre = take(sizeof(u32) * 256 * kMaxGenWG);
-  L.lsd_tot = take(sizeof(u32) * 256);
+  L.lsd_cnt = take(sizeof(u32) * kLsdDigits * kMaxGenWG);
+  L.lsd_pre = take(sizeof(u32) * kLsdDigits * kMaxGenWG);
+  L.lsd_tot = take(sizeof(u32) * kLsdDigits);
   L.bufA = take(sizeof(Pair) * (size_t)std::max<int64_t>(k, 1));
   L.bufB = take(sizeof(Pair) * (size_t)std::max<int64_t>(k, 1));
   L.pub = take(sizeof(u32) * ((size_t)kPlanCap + kMaxStepBlocks));
@@ -238,9 +239,9 @@ struct GenArgs {
   float* out_val;
   u32* ghist;    // 3 x 2048, zero on entry
   u32* gcnt;     // [G][waves][2]
-  u32* lsd_cnt;  // [G][256]
-  u32* lsd_pre;  // [G][256]
-  u32* lsd_tot;  // [256]
+  u32* lsd_cnt;  // [G][digits]
+  u32* lsd_pre;  // [G][digits]
+  u32* lsd_tot;  // [digits]
   Pair* bufA;
   Pair* bufB;
   GridBar bar;
@@ -259,13 +260,15 @@ __device__ __forceinline__ u32 block_sum(u32 v, u32* lds) {
 // rows of NT entries each pass keeps in flight per tile (kPipe: the next
 // tile's loads go out before a tile is processed).  acc is read from
 // residual, which every participant must be able to see.
-template <int NT, int V, bool kPipe>
+template <int NT, int V, bool kPipe, int DB>
 __device__ __forceinline__ void general_path(const GenArgs& a) {
   constexpr int NW = NT / kWave;
+  constexpr int ND = 1 << DB;  // digits of one LSD pass
+  static_assert(ND <= kLsdDigits && ND <= 2048, "LSD digit tables");
   __shared__ u32 s_hist[2048];
-  __shared__ u32 s_wcnt[NW][256];
-  __shared__ u32 s_base[256];
-  __shared__ u32 s_run[256];
+  __shared__ u32 s_wcnt[NW][ND];
+  __shared__ u32 s_base[ND];
+  __shared__ u32 s_run[ND];
   __shared__ u32 s_scan[NW + 1];
   __shared__ u32 s_found[4];
   const int tid = threadIdx.x;
@@ -325,6 +328,7 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
   int64_t t_strict = -1;  // select every key > t_strict ...
   u32 t_eq = 0;           // ... and the first r keys equal to t_eq
   int64_t r = 0;
+  u32 kmax = 0x7FFFFFFFu;  // at least the largest key (top of its level-0 bin)
   for (int L = 0; L < 3; ++L) {
     const int sh = shifts[L], wd = widths[L];
     const u32 nbins = 1u << wd;
@@ -344,7 +348,14 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
     }
     if (!grid_sync(a.bar)) return;
     for (int i = tid; i < (int)nbins; i += NT) s_hist[i] = a.ghist[L * 2048 + i];
+    if (L == 0 && tid == 0) s_found[3] = 0;
     __syncthreads();
+    if (L == 0) {
+      for (int i = tid; i < (int)nbins; i += NT)
+        if (s_hist[i] != 0) atomicMax(&s_found[3], (u32)i);
+      __syncthreads();
+      kmax = (s_found[3] << sh) | ((1u << sh) - 1u);
+    }
     // thread t owns bins [nbins - cpt(t+1), nbins - cpt*t), scanning from the top
     const int cpt = (int)nbins / NT > 0 ? (int)nbins / NT : 1;
     const int top = (int)nbins - cpt * tid;  // exclusive
@@ -485,14 +496,20 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
   if (!grid_sync(a.bar)) return;
 
   // ---------------- stable LSD radix sort by descending key ----------------
+  // Every selected key lies in [kmin, kmax], so all of them agree above the
+  // highest bit where kmin and kmax differ: only the bits below it are
+  // sorted, DB per pass (the inverse key's bits are the key's complemented).
+  const u32 kmin = r > 0 ? t_eq : (u32)(t_strict + 1);
+  const int nbits = kmin == kmax ? 0 : 32 - __clz(kmin ^ kmax);
+  const int npass = (nbits + DB - 1) / DB;
   const int64_t per2 = (a.k + G - 1) / G;
   const int64_t sb = std::min<int64_t>(a.k, (int64_t)b * per2);
   const int64_t se = std::min<int64_t>(a.k, sb + per2);
   Pair* src = a.bufA;
   Pair* dst = a.bufB;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int sh = 8 * pass;
-    for (int i = tid; i < 256; i += NT) s_hist[i] = 0;
+  for (int pass = 0; pass < npass; ++pass) {
+    const int sh = DB * pass;
+    for (int i = tid; i < ND; i += NT) s_hist[i] = 0;
     __syncthreads();
     for (int64_t base = sb; base < se; base += (int64_t)V * NT) {
       u64 pv[V];
@@ -504,37 +521,39 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
 #pragma unroll
       for (int j = 0; j < V; ++j) {
         const u32 inv = 0x7FFFFFFFu - key_of_bits(unpack_pair(pv[j]).bits);
-        if (base + (int64_t)j * NT + tid < se) atomicAdd(&s_hist[(inv >> sh) & 0xFFu], 1u);
+        if (base + (int64_t)j * NT + tid < se) atomicAdd(&s_hist[(inv >> sh) & (ND - 1)], 1u);
       }
     }
     __syncthreads();
-    for (int i = tid; i < 256; i += NT) st_agent(&a.lsd_cnt[b * 256 + i], s_hist[i]);
+    for (int i = tid; i < ND; i += NT) st_agent(&a.lsd_cnt[b * ND + i], s_hist[i]);
     if (!grid_sync(a.bar)) return;
     // column scans: digit d handled by workgroup d % G
-    for (int d = b; d < 256; d += G) {  // G <= NT: one column entry per thread
-      u32 c = tid < G ? a.lsd_cnt[tid * 256 + d] : 0u;
+    for (int d = b; d < ND; d += G) {  // G <= NT: one column entry per thread
+      u32 c = tid < G ? a.lsd_cnt[tid * ND + d] : 0u;
       u32 colsum;
       u32 ex = block_exclusive_sum<NT>(c, s_scan, colsum);
-      if (tid < G) st_agent(&a.lsd_pre[tid * 256 + d], ex);
+      if (tid < G) st_agent(&a.lsd_pre[tid * ND + d], ex);
       if (tid == 0) st_agent(&a.lsd_tot[d], colsum);
     }
     if (!grid_sync(a.bar)) return;
-    for (int i = tid; i < 256; i += NT) s_hist[i] = a.lsd_tot[i];
+    for (int i = tid; i < ND; i += NT) s_hist[i] = a.lsd_tot[i];
     if (tid == 0) s_found[3] = 0;
     __syncthreads();
-    if (tid < 256 && (int64_t)s_hist[tid] == a.k) s_found[3] = 1;
+    for (int i = tid; i < ND; i += NT)
+      if ((int64_t)s_hist[i] == a.k) s_found[3] = 1;
     __syncthreads();
     if (s_found[3] != 0) continue;  // every key shares this digit: the pass is a no-op
+    static_assert(ND <= NT, "one digit per thread in the base scan");
     {
-      u32 v = tid < 256 ? s_hist[tid] : 0u;
+      u32 v = tid < ND ? s_hist[tid] : 0u;
       u32 t;
       u32 ex = block_exclusive_sum<NT>(v, s_scan, t);
-      if (tid < 256) {
-        s_base[tid] = ex + a.lsd_pre[b * 256 + tid];
+      if (tid < ND) {
+        s_base[tid] = ex + a.lsd_pre[b * ND + tid];
         s_run[tid] = 0;
       }
     }
-    for (int i = tid; i < NW * 256; i += NT) (&s_wcnt[0][0])[i] = 0;
+    for (int i = tid; i < NW * ND; i += NT) (&s_wcnt[0][0])[i] = 0;
     __syncthreads();
     // rows of NT entries, V rows' loads in flight at a time
     u64 pv[V];
@@ -553,10 +572,10 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
 #pragma unroll
       for (int j = 1; j < V; ++j) cur = (row % V == j) ? pv[j] : cur;
       Pair e = valid ? unpack_pair(cur) : pair_sentinel();
-      u32 d = valid ? (((0x7FFFFFFFu - key_of_bits(e.bits)) >> sh) & 0xFFu) : 0u;
+      u32 d = valid ? (((0x7FFFFFFFu - key_of_bits(e.bits)) >> sh) & (ND - 1)) : 0u;
       u64 peers = ballot(valid);
 #pragma unroll
-      for (int bit = 0; bit < 8; ++bit) {
+      for (int bit = 0; bit < DB; ++bit) {
         bool on = (d >> bit) & 1u;
         u64 m = ballot(valid && on);
         peers &= on ? m : ~m;
@@ -571,7 +590,7 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
         if ((int64_t)pos < a.k) st_agent64((u64*)dst + pos, pack_pair(e));
       }
       __syncthreads();
-      if (tid < 256) {
+      if (tid < ND) {
         u32 s = 0;
         for (int ww = 0; ww < NW; ++ww) {
           s += s_wcnt[ww][tid];
@@ -660,7 +679,7 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_pass(AccArgs a) {
   }
 }
 
-__global__ __launch_bounds__(kGenThreads) void k_general(GenArgs a) { general_path<kGenThreads, 16, true>(a); }
+__global__ __launch_bounds__(kGenThreads) void k_general(GenArgs a) { general_path<kGenThreads, 16, true, 9>(a); }
 
 // ------------------------------------------------------------- k_step ----
 struct StepArgs {
@@ -1685,7 +1704,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
     // which reads it at device scope.
     // rarely taken: one row per tile keeps this copy of the general path small
     // (a larger one costs the fast path registers and time even unused)
-    if (grid_sync(a.gen.bar)) general_path<NT, 1, false>(a.gen);
+    if (grid_sync(a.gen.bar)) general_path<NT, 1, false, 8>(a.gen);
   }
 }
 

@@ -115,6 +115,28 @@ def test_forced_general_and_fallback(tgs_gpu, path, dist):
         assert_topk_equal(gpu_topk(tgs_gpu, grad, res, k), oracle_topk(grad, res, k), "path=%d k=%d" % (path, k))
 
 
+@pytest.mark.parametrize("layout", ["spread", "clustered", "crowded"])
+def test_general_path_candidate_layouts(tgs_gpu, layout):
+    """The standalone general path copies the entries of the threshold's
+    first-level bin and above into one region per wave and selects among
+    the copies.  Large entries bunched in one index range overflow the
+    regions of the waves that hold them, and a value shared by half the
+    vector is too many to copy at all: both must give the oracle's result
+    through the route over the whole vector."""
+    tgs_gpu.set_option(tgs_gpu.OPT_TOPK_PATH, 1)
+    rng = np.random.default_rng({"spread": 5, "clustered": 6, "crowded": 7}[layout])
+    n = 1_000_003
+    grad = rng.normal(0.0, 1e-3, n).astype(np.float32)
+    res = rng.normal(0.0, 1e-3, n).astype(np.float32)
+    if layout == "clustered":
+        grad[200_000:260_000] = rng.uniform(1.0, 2.0, 60_000).astype(np.float32)
+    if layout == "crowded":
+        grad[rng.random(n) < 0.5] = np.float32(0.5)
+        res[:] = 0.0
+    for k in (1, 1000, 40_000, 70_000):
+        assert_topk_equal(gpu_topk(tgs_gpu, grad, res, k), oracle_topk(grad, res, k), "%s k=%d" % (layout, k))
+
+
 def test_small_config_three_chained_steps(tgs_gpu):
     """n = 1,048,576, N(0,1) gradients, residual from 0, k = 1,048 (0.1%)."""
     n = 1_048_576

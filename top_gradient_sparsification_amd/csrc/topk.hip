@@ -153,11 +153,21 @@ struct GenState {
   u32 bar_cnt[9][32];  // grid barrier counters, one cache line each
   u32 bar_gen[8][32];  // grid barrier generation, 8 copies
   u32 bar_abort;
+  u32 cand_ovf;
 };
 
 struct TopkLayout {
-  size_t ctl, gstate, gcnt, lsd_cnt, lsd_pre, lsd_tot, bufA, bufB, pub, rcnt, slots, ovf, total;
+  size_t ctl, gstate, gcnt, lsd_cnt, lsd_pre, lsd_tot, bufA, bufB, cand, pub, rcnt, slots, ovf, total;
+  u32 cand_cap;
 };
+
+// Pairs one candidate region (one wave of the standalone general path) holds:
+// room for 3 k spread evenly, plus slack.
+static u32 cand_region_cap(int64_t k) {
+  const int64_t regions = (int64_t)kMaxGenWG * (kGenThreads / kWave);
+  const int64_t c = (3 * k + regions - 1) / regions + 64;
+  return (u32)((c + 63) / 64 * 64);
+}
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -178,6 +188,8 @@ static TopkLayout topk_layout(int64_t n, int64_t k) {
   L.lsd_tot = take(sizeof(u32) * kLsdDigits);
   L.bufA = take(sizeof(Pair) * (size_t)std::max<int64_t>(k, 1));
   L.bufB = take(sizeof(Pair) * (size_t)std::max<int64_t>(k, 1));
+  L.cand_cap = cand_region_cap(k);
+  L.cand = take(sizeof(u64) * (size_t)kMaxGenWG * (kGenThreads / kWave) * L.cand_cap);
   L.pub = take(sizeof(u32) * ((size_t)kPlanCap + kMaxStepBlocks));
   L.rcnt = take(sizeof(u32) * (size_t)kMaxStepBlocks * (kMaxBuckets / 2));
   L.slots = take(sizeof(Pair) * (size_t)kMaxBuckets * kSlotTotal);
@@ -245,6 +257,9 @@ struct GenArgs {
   Pair* bufA;
   Pair* bufB;
   GridBar bar;
+  u64* cand;      // candidate regions, cand_cap pairs per (workgroup, wave)
+  u32* cand_ovf;  // set when a region overflows (zero on entry)
+  u32 cand_cap;
 };
 
 // Sum over the block of one value per thread.
@@ -260,7 +275,7 @@ __device__ __forceinline__ u32 block_sum(u32 v, u32* lds) {
 // rows of NT entries each pass keeps in flight per tile (kPipe: the next
 // tile's loads go out before a tile is processed).  acc is read from
 // residual, which every participant must be able to see.
-template <int NT, int V, bool kPipe, int DB>
+template <int NT, int V, bool kPipe, int DB, bool kCand>
 __device__ __forceinline__ void general_path(const GenArgs& a) {
   constexpr int NW = NT / kWave;
   constexpr int ND = 1 << DB;  // digits of one LSD pass
@@ -320,6 +335,71 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
     }
   };
 
+  // Wave w owns the contiguous slice [wb, we) of the workgroup's chunk; the
+  // candidate pass, the counts and the ordered compaction walk it in rows of
+  // 64 entries, V rows per tile, with no barrier and no LDS.  Counts, places
+  // and indices fit in 32 bits (n < 2^31).
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);  // the same in every lane
+  const u32 wlen = (clen + NW - 1) / NW;
+  const u32 wb = std::min<u32>(clen, (u32)w * wlen), we = std::min<u32>(clen, wb + wlen);
+  auto load_wave_tile = [&](u32 o, u32* bits) -> u32 {
+    u32 vm = 0;
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const u32 q = o + (u32)(j * kWave + lane);
+      const bool in = q < we;
+      vm |= (u32)in << j;
+      bits[j] = accc[in ? q : 0u];
+    }
+    return vm;
+  };
+  auto for_each_wave_tile = [&](auto&& body) {
+    constexpr u32 TS = (u32)(V * kWave);
+    u32 b0[V], b1[V];
+    if constexpr (kPipe) {
+      u32 v0 = wb < we ? load_wave_tile(wb, b0) : 0u, v1;
+      for (u32 o = wb; o < we; o += 2 * TS) {
+        v1 = load_wave_tile(o + TS, b1);
+        body(o, b0, v0);
+        if (o + TS >= we) break;
+        v0 = load_wave_tile(o + 2 * TS, b0);
+        body(o + TS, b1, v1);
+      }
+    } else {
+      for (u32 o = wb; o < we; o += TS) body(o, b0, load_wave_tile(o, b0));
+    }
+  };
+  // Candidates (standalone path): this wave's entries of the first-level bins
+  // at and above the threshold bin, in index order, in its own region of
+  // cand_cap pairs.  ccount is the wave's count; use_cand is the same in
+  // every workgroup.
+  bool use_cand = false;
+  u32 ccount = 0;
+  const u64* const creg = kCand ? opaque_ptr(a.cand + (size_t)(b * NW + w) * a.cand_cap) : nullptr;
+  auto load_cand_tile = [&](u32 o, u64* pv) -> u32 {
+    u32 vm = 0;
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const u32 q = o + (u32)(j * kWave + lane);
+      const bool in = q < ccount;
+      vm |= (u32)in << j;
+      pv[j] = creg[in ? q : 0u];
+    }
+    return vm;
+  };
+  auto for_each_cand_tile = [&](auto&& body) {
+    constexpr u32 TS = (u32)(V * kWave);
+    u64 p0[V], p1[V];
+    u32 v0 = ccount > 0 ? load_cand_tile(0, p0) : 0u, v1;
+    for (u32 o = 0; o < ccount; o += 2 * TS) {
+      v1 = load_cand_tile(o + TS, p1);
+      body(p0, v0);
+      if (o + TS >= ccount) break;
+      v0 = load_cand_tile(o + 2 * TS, p0);
+      body(p1, v1);
+    }
+  };
+
   // ---------------- radix select of the k-th largest key ----------------
   const int shifts[3] = {20, 9, 0};
   const int widths[3] = {11, 11, 9};
@@ -334,13 +414,22 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
     const u32 nbins = 1u << wd;
     for (int i = tid; i < 2048; i += NT) s_hist[i] = 0;
     __syncthreads();
-    for_each_tile([&](int64_t, const u32* bits, u32 vm) {
+    auto hist_key = [&](u32 key) {
+      if ((key >> (sh + wd)) == prefix) atomicAdd(&s_hist[(key >> sh) & (nbins - 1)], 1u);
+    };
+    if (kCand && use_cand) {
+      for_each_cand_tile([&](const u64* pv, u32 vm) {
 #pragma unroll
-      for (int j = 0; j < V; ++j) {
-        const u32 key = key_of_bits(bits[j]);
-        if (((vm >> j) & 1u) && (key >> (sh + wd)) == prefix) atomicAdd(&s_hist[(key >> sh) & (nbins - 1)], 1u);
-      }
-    });
+        for (int j = 0; j < V; ++j)
+          if ((vm >> j) & 1u) hist_key(key_of_bits((u32)(pv[j] >> 32)));
+      });
+    } else {
+      for_each_tile([&](int64_t, const u32* bits, u32 vm) {
+#pragma unroll
+        for (int j = 0; j < V; ++j)
+          if ((vm >> j) & 1u) hist_key(key_of_bits(bits[j]));
+      });
+    }
     __syncthreads();
     for (int i = tid; i < (int)nbins; i += NT) {
       u32 v = s_hist[i];
@@ -385,7 +474,8 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
       if (tid == 0) atomicOr(a.bar.err, 1u << 2);
       return;
     }
-    need -= (int64_t)s_found[1];
+    const int64_t n_above = s_found[1];
+    need -= n_above;
     const int64_t h = s_found[2];
     prefix = (prefix << wd) | d;
     if (need == h) {  // the whole digit range is taken: select key >= prefix << sh
@@ -398,56 +488,55 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
       t_eq = prefix;
       r = need;
     }
+    if constexpr (kCand) {
+      // After the first level: copy the entries of bins >= d (n_above + h of
+      // them) out of acc once, and run the rest on the copies -- unless they
+      // would crowd the regions, or one wave's share does not fit.
+      if (L == 0 && (u64)(n_above + h) <= (u64)a.bar.nwg * NW * a.cand_cap * 3 / 4) {
+        const u32 lo = d << sh;
+        u64* const out = (u64*)creg;
+        const u32 i0 = (u32)cb + (u32)lane;
+        u32 cnt = 0;
+        for_each_wave_tile([&](u32 o, const u32* bits, u32 vm) {
+#pragma unroll
+          for (int j = 0; j < V; ++j) {
+            const bool keep = ((vm >> j) & 1u) && key_of_bits(bits[j]) >= lo;
+            const u64 m = ballot(keep);
+            const u32 pos = cnt + lanes_below(m);
+            if (keep && pos < a.cand_cap) out[pos] = pack_pair(Pair{(int32_t)(i0 + o + (u32)(j * kWave)), bits[j]});
+            cnt += (u32)__popcll(m);
+          }
+        });
+        if (cnt > a.cand_cap && lane == 0) st_agent(a.cand_ovf, 1u);
+        ccount = cnt;
+        if (!grid_sync(a.bar)) return;
+        use_cand = ld_agent(a.cand_ovf) == 0u;
+      }
+    }
     __syncthreads();
   }
 
   // ---------------- per-wave counts ----------------
-  // Wave w owns the contiguous slice [wb, we) of the workgroup's chunk; the
-  // counts and the ordered compaction walk it in rows of 64 entries, V rows
-  // per tile, so the compaction needs no barrier and no LDS.  Counts,
-  // places and indices fit in 32 bits (n < 2^31).
-  const int w = tid / kWave;
-  const u32 wlen = (clen + NW - 1) / NW;
-  const u32 wb = std::min<u32>(clen, (u32)w * wlen), we = std::min<u32>(clen, wb + wlen);
-  auto load_wave_tile = [&](u32 o, u32* bits) -> u32 {
-    u32 vm = 0;
-#pragma unroll
-    for (int j = 0; j < V; ++j) {
-      const u32 q = o + (u32)(j * kWave + lane);
-      const bool in = q < we;
-      vm |= (u32)in << j;
-      bits[j] = accc[in ? q : 0u];
-    }
-    return vm;
-  };
-  auto for_each_wave_tile = [&](auto&& body) {
-    constexpr u32 TS = (u32)(V * kWave);
-    u32 b0[V], b1[V];
-    if constexpr (kPipe) {
-      u32 v0 = wb < we ? load_wave_tile(wb, b0) : 0u, v1;
-      for (u32 o = wb; o < we; o += 2 * TS) {
-        v1 = load_wave_tile(o + TS, b1);
-        body(o, b0, v0);
-        if (o + TS >= we) break;
-        v0 = load_wave_tile(o + 2 * TS, b0);
-        body(o + TS, b1, v1);
-      }
-    } else {
-      for (u32 o = wb; o < we; o += TS) body(o, b0, load_wave_tile(o, b0));
-    }
-  };
   const u32 t_lo = (u32)(t_strict + 1), r32 = (u32)r, k32 = opaque_u32((u32)a.k);
   {
     u32 c_gt = 0, c_eq = 0;
-    for_each_wave_tile([&](u32, const u32* bits, u32 vm) {
+    auto count_key = [&](u32 key) {
+      c_gt += key >= t_lo;
+      c_eq += r32 > 0 && key == t_eq;
+    };
+    if (kCand && use_cand) {
+      for_each_cand_tile([&](const u64* pv, u32 vm) {
 #pragma unroll
-      for (int j = 0; j < V; ++j) {
-        const u32 key = key_of_bits(bits[j]);
-        const bool in = (vm >> j) & 1u;
-        c_gt += in && key >= t_lo;
-        c_eq += in && r32 > 0 && key == t_eq;
-      }
-    });
+        for (int j = 0; j < V; ++j)
+          if ((vm >> j) & 1u) count_key(key_of_bits((u32)(pv[j] >> 32)));
+      });
+    } else {
+      for_each_wave_tile([&](u32, const u32* bits, u32 vm) {
+#pragma unroll
+        for (int j = 0; j < V; ++j)
+          if ((vm >> j) & 1u) count_key(key_of_bits(bits[j]));
+      });
+    }
     c_gt = wave_sum(c_gt);
     c_eq = wave_sum(c_eq);
     if (lane == 0) {
@@ -476,22 +565,29 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
     // equal keys before it.
     u32 gt_seen = pg, eq_seen = pe;
     u64* const outA = opaque_ptr((u64*)a.bufA);
-    const u32 i0 = (u32)cb + (u32)lane;
-    for_each_wave_tile([&](u32 o, const u32* bits, u32 vm) {
+    auto place = [&](bool in, u32 key, u64 pair) {
+      const bool g = in && key >= t_lo, e = in && r32 > 0 && key == t_eq;
+      const u64 bg = ballot(g), be = ballot(e);
+      const u32 gb = gt_seen + lanes_below(bg), eb = eq_seen + lanes_below(be);
+      const bool sel = g || (e && eb < r32);
+      const u32 pos = gb + std::min(eb, r32);
+      if (sel && pos < k32) st_agent64(outA + pos, pair);
+      gt_seen += (u32)__popcll(bg);
+      eq_seen += (u32)__popcll(be);
+    };
+    if (kCand && use_cand) {
+      for_each_cand_tile([&](const u64* pv, u32 vm) {
 #pragma unroll
-      for (int j = 0; j < V; ++j) {
-        const u32 key = key_of_bits(bits[j]);
-        const bool in = (vm >> j) & 1u;
-        const bool g = in && key >= t_lo, e = in && r32 > 0 && key == t_eq;
-        const u64 bg = ballot(g), be = ballot(e);
-        const u32 gb = gt_seen + lanes_below(bg), eb = eq_seen + lanes_below(be);
-        const bool sel = g || (e && eb < r32);
-        const u32 pos = gb + std::min(eb, r32);
-        if (sel && pos < k32) st_agent64(outA + pos, pack_pair(Pair{(int32_t)(i0 + o + (u32)(j * kWave)), bits[j]}));
-        gt_seen += (u32)__popcll(bg);
-        eq_seen += (u32)__popcll(be);
-      }
-    });
+        for (int j = 0; j < V; ++j) place((vm >> j) & 1u, key_of_bits((u32)(pv[j] >> 32)), pv[j]);
+      });
+    } else {
+      const u32 i0 = (u32)cb + (u32)lane;
+      for_each_wave_tile([&](u32 o, const u32* bits, u32 vm) {
+#pragma unroll
+        for (int j = 0; j < V; ++j)
+          place((vm >> j) & 1u, key_of_bits(bits[j]), pack_pair(Pair{(int32_t)(i0 + o + (u32)(j * kWave)), bits[j]}));
+      });
+    }
   }
   if (!grid_sync(a.bar)) return;
 
@@ -679,7 +775,7 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_pass(AccArgs a) {
   }
 }
 
-__global__ __launch_bounds__(kGenThreads) void k_general(GenArgs a) { general_path<kGenThreads, 16, true, 9>(a); }
+__global__ __launch_bounds__(kGenThreads) void k_general(GenArgs a) { general_path<kGenThreads, 16, true, 9, true>(a); }
 
 // ------------------------------------------------------------- k_step ----
 struct StepArgs {
@@ -1704,7 +1800,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
     // which reads it at device scope.
     // rarely taken: one row per tile keeps this copy of the general path small
     // (a larger one costs the fast path registers and time even unused)
-    if (grid_sync(a.gen.bar)) general_path<NT, 1, false, 8>(a.gen);
+    if (grid_sync(a.gen.bar)) general_path<NT, 1, false, 8, false>(a.gen);
   }
 }
 
@@ -1819,6 +1915,9 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
   ga.lsd_tot = (u32*)(ws + L.lsd_tot);
   ga.bufA = (Pair*)(ws + L.bufA);
   ga.bufB = (Pair*)(ws + L.bufB);
+  ga.cand = (u64*)(ws + L.cand);
+  ga.cand_cap = L.cand_cap;
+  ga.cand_ovf = &gs->cand_ovf;
   ga.bar.cnt = &gs->bar_cnt[0][0];
   ga.bar.gen = &gs->bar_gen[0][0];
   ga.bar.abort = &gs->bar_abort;

@@ -85,9 +85,8 @@ constexpr int kMaxPairs = 256;                      // row pairs one workgroup r
 constexpr int64_t kFastMinN = (int64_t)kMaxStepBlocks * kStepWaves * kSampleRounds * kSampleChunk;  // 2^19
 constexpr u32 kSpinLimit = 1u << 18;
 // plain pass + standalone general path
-constexpr int kAccThreads = 256;
-constexpr int kAccU = 4;
-constexpr int kMaxAccBlocks = 2048;
+constexpr int kAccThreads = 1024;
+constexpr int kMaxAccBlocks = 256;  // one first-level histogram row each
 constexpr int kGenThreads = 512;
 constexpr int kGenBlocks = 256;
 constexpr int kMaxGenWG = 256;  // workgroups of either general-path launch
@@ -157,7 +156,7 @@ struct GenState {
 };
 
 struct TopkLayout {
-  size_t ctl, gstate, gcnt, lsd_cnt, lsd_pre, lsd_tot, bufA, bufB, cand, pub, rcnt, slots, ovf, total;
+  size_t ctl, gstate, gcnt, lsd_cnt, lsd_pre, lsd_tot, bufA, bufB, cand, hist_rows, pub, rcnt, slots, ovf, total;
   u32 cand_cap;
 };
 
@@ -190,6 +189,7 @@ static TopkLayout topk_layout(int64_t n, int64_t k) {
   L.bufB = take(sizeof(Pair) * (size_t)std::max<int64_t>(k, 1));
   L.cand_cap = cand_region_cap(k);
   L.cand = take(sizeof(u64) * (size_t)kMaxGenWG * (kGenThreads / kWave) * L.cand_cap);
+  L.hist_rows = take(sizeof(u32) * 2048 * (size_t)kMaxAccBlocks);
   L.pub = take(sizeof(u32) * ((size_t)kPlanCap + kMaxStepBlocks));
   L.rcnt = take(sizeof(u32) * (size_t)kMaxStepBlocks * (kMaxBuckets / 2));
   L.slots = take(sizeof(Pair) * (size_t)kMaxBuckets * kSlotTotal);
@@ -260,6 +260,8 @@ struct GenArgs {
   u64* cand;      // candidate regions, cand_cap pairs per (workgroup, wave)
   u32* cand_ovf;  // set when a region overflows (zero on entry)
   u32 cand_cap;
+  u32 acc_rows;          // rows of acc_hist (standalone path)
+  const u32* acc_hist;   // [acc_rows][2048] first-level histograms from the accumulate pass
 };
 
 // Sum over the block of one value per thread.
@@ -414,6 +416,19 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
     const u32 nbins = 1u << wd;
     for (int i = tid; i < 2048; i += NT) s_hist[i] = 0;
     __syncthreads();
+    if (kCand && L == 0) {
+      // the accumulate pass left one histogram row per workgroup: this
+      // workgroup sums the columns of its share of the bins
+      const int per_wg = (2048 + G - 1) / G;
+      const int bin0 = std::min(2048, b * per_wg), nbin = std::min(2048, bin0 + per_wg) - bin0;
+      const int rows = (int)a.acc_rows;
+      for (int q = tid; q < nbin * rows; q += NT) {
+        const u32 v = a.acc_hist[(size_t)(q / nbin) * 2048 + bin0 + q % nbin];
+        if (v) atomicAdd(&s_hist[q % nbin], v);
+      }
+      __syncthreads();
+      for (int i = tid; i < nbin; i += NT) st_agent(&a.ghist[bin0 + i], s_hist[i]);
+    } else {
     auto hist_key = [&](u32 key) {
       if ((key >> (sh + wd)) == prefix) atomicAdd(&s_hist[(key >> sh) & (nbins - 1)], 1u);
     };
@@ -434,6 +449,7 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
     for (int i = tid; i < (int)nbins; i += NT) {
       u32 v = s_hist[i];
       if (v) add_agent_relaxed(&a.ghist[L * 2048 + i], v);
+    }
     }
     if (!grid_sync(a.bar)) return;
     for (int i = tid; i < (int)nbins; i += NT) s_hist[i] = a.ghist[L * 2048 + i];
@@ -735,44 +751,68 @@ struct AccArgs {
   u32* zero_ptr;
   int zero_words;
   u32* err;
+  u32* hist_rows;  // [gridDim.x][2048]: each workgroup's first-level histogram
 };
 
 template <bool VEC>
 __global__ __launch_bounds__(kAccThreads) void k_acc_pass(AccArgs a) {
+  constexpr int NT = kAccThreads;
+  __shared__ u32 s_h[2048];  // first-level histogram of this workgroup's keys (key >> 20)
   const int tid = threadIdx.x;
+  for (int i = tid; i < 2048; i += NT) s_h[i] = 0;
   if (blockIdx.x == 0) {
-    for (int i = tid; i < a.zero_words; i += kAccThreads) a.zero_ptr[i] = 0u;
+    for (int i = tid; i < a.zero_words; i += NT) a.zero_ptr[i] = 0u;
     if (tid == 0) *a.err = 0u;
   }
+  __syncthreads();
   const float* __restrict__ g = a.grad;
   float* __restrict__ r = a.residual;
+  auto add = [&](int64_t i) {
+    const float acc = r[i] + g[i];
+    r[i] = acc;
+    atomicAdd(&s_h[key_of_bits(__float_as_uint(acc)) >> 20], 1u);
+  };
   if (VEC) {
-    if (blockIdx.x == 0 && tid < a.head) r[tid] = r[tid] + g[tid];
+    if (blockIdx.x == 0 && tid < a.head) add(tid);
     const v4f* __restrict__ gv = (const v4f*)(g + a.head);
     v4f* __restrict__ rv = (v4f*)(r + a.head);
-    constexpr int64_t tile = (int64_t)kAccThreads * kAccU;
-    for (int64_t base = (int64_t)blockIdx.x * tile; base < a.nv; base += (int64_t)gridDim.x * tile) {
-      v4f gg[kAccU], rr[kAccU];
-#pragma unroll
-      for (int u = 0; u < kAccU; ++u) {
-        const int64_t i = base + u * kAccThreads + tid;
-        if (i < a.nv) {
-          gg[u] = __builtin_nontemporal_load(gv + i);
-          rr[u] = __builtin_nontemporal_load(rv + i);
-        }
+    // rows of NT float4: row t, then t + G, ...; the next row's loads go out
+    // before a row is processed (two rows of a workgroup in flight)
+    const int64_t nrows = (a.nv + NT - 1) / NT, G = gridDim.x;
+    auto load = [&](int64_t t, v4f& gg, v4f& rr) {
+      const int64_t i = t * NT + tid;
+      if (t < nrows && i < a.nv) {
+        gg = __builtin_nontemporal_load(gv + i);
+        rr = __builtin_nontemporal_load(rv + i);
       }
+    };
+    auto process = [&](int64_t t, const v4f& gg, const v4f& rr) {
+      const int64_t i = t * NT + tid;
+      if (i < a.nv) {
+        const v4f acc = rr + gg;
+        __builtin_nontemporal_store(acc, rv + i);
 #pragma unroll
-      for (int u = 0; u < kAccU; ++u) {
-        const int64_t i = base + u * kAccThreads + tid;
-        if (i < a.nv) __builtin_nontemporal_store(rr[u] + gg[u], rv + i);
+        for (int q = 0; q < 4; ++q) atomicAdd(&s_h[key_of_bits(__float_as_uint(acc[q])) >> 20], 1u);
       }
+    };
+    v4f ga, ra, gb, rb;
+    int64_t t = blockIdx.x;
+    load(t, ga, ra);
+    load(t + G, gb, rb);
+    for (; t < nrows; t += 2 * G) {
+      process(t, ga, ra);
+      load(t + 2 * G, ga, ra);
+      if (t + G >= nrows) break;
+      process(t + G, gb, rb);
+      load(t + 3 * G, gb, rb);
     }
     if (blockIdx.x == gridDim.x - 1)
-      for (int64_t i = a.head + 4 * a.nv + tid; i < a.n; i += kAccThreads) r[i] = r[i] + g[i];
+      for (int64_t i = a.head + 4 * a.nv + tid; i < a.n; i += NT) add(i);
   } else {
-    for (int64_t i = (int64_t)blockIdx.x * kAccThreads + tid; i < a.n; i += (int64_t)gridDim.x * kAccThreads)
-      r[i] = r[i] + g[i];
+    for (int64_t i = (int64_t)blockIdx.x * NT + tid; i < a.n; i += (int64_t)gridDim.x * NT) add(i);
   }
+  __syncthreads();
+  for (int i = tid; i < 2048; i += NT) a.hist_rows[(size_t)blockIdx.x * 2048 + i] = s_h[i];
 }
 
 __global__ __launch_bounds__(kGenThreads) void k_general(GenArgs a) { general_path<kGenThreads, 16, true, 9, true>(a); }
@@ -1975,9 +2015,12 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
     aa.zero_words = (int)(sizeof(GenState) / sizeof(u32));
     aa.err = &ctl->err;
     const int64_t units = vec ? nv : n;
-    const int64_t per = (int64_t)kAccThreads * kAccU * (vec ? 1 : 4);
+    const int64_t per = (int64_t)kAccThreads * (vec ? 2 : 8);
     int G1 = (int)std::max<int64_t>(1, std::min<int64_t>(kMaxAccBlocks, (units + per - 1) / per));
     if (gopt > 0) G1 = (int)std::min<int64_t>(gopt, kMaxAccBlocks);
+    aa.hist_rows = (u32*)(ws + L.hist_rows);
+    ga.acc_hist = aa.hist_rows;
+    ga.acc_rows = (u32)G1;
     if (vec) hipLaunchKernelGGL(k_acc_pass<true>, dim3(G1), dim3(kAccThreads), 0, stream, aa);
     else hipLaunchKernelGGL(k_acc_pass<false>, dim3(G1), dim3(kAccThreads), 0, stream, aa);
     if (k > 0) {

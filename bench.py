@@ -22,6 +22,28 @@ back-to-back launches: the average launch period, gaps between launches
 included, without an event pair around every launch (which adds a few
 microseconds of its own); `cpu_baseline` is the plain C oracle on one host core
 on the same workload.
+
+    python bench.py --workload NAME [--steps K]
+
+times one of the other workloads instead (names below; no cpu_baseline).
+Before every timed call the residual is restored from a copy holding its
+error-feedback history and, for vectors below 200M entries, a 512 MiB buffer
+is written to push the inputs out of the Infinity Cache; an event pair on the
+call's stream times each call.  `roofline` then covers the whole call (every
+kernel of it) against its algorithmic bytes:
+    topk_n25.6M_2%, topk_n25.6M_0.02%   the 25.6M mixture at k = 512,000 / 5,120
+                                        (residual after 5 steps at that density)
+    topk_n138M_0.1%                     138M VGG-16-sized mixture, whole vector,
+                                        k = 138,000 (residual after 2 steps)
+    topk_segments_n138M_0.1%            the same vector as 32 log-uniform
+                                        segments, one call per segment,
+                                        k_s = floor(0.001 size_s)
+    topk_n1.5e9_0.1%                    1.5e9 mixture (0.5% Laplace(0, 0.05)),
+                                        k = 1,500,000 (residual after 2 steps)
+    threshold_n1.5e9                    the same vector, lambda = 4e-3,
+                                        capacity 30M (residual after 1 step)
+    gtopk_P32_k25600                    the merge of 32 sets of 25,600 pairs
+                                        (50% from a hot set of 51,200)
 """
 from __future__ import annotations
 
@@ -39,12 +61,130 @@ N = 25_600_000
 DENSITY = 0.001
 
 
+# the other workloads: (kind, n, density or lambda, mixture (sigma, p_out, b_out), config id, prior steps)
+OTHER = {
+    "topk_n25.6M_2%": ("topk", 25_600_000, 0.02, (1e-3, 0.01, 0.1), 2, 5),
+    "topk_n25.6M_0.02%": ("topk", 25_600_000, 0.0002, (1e-3, 0.01, 0.1), 2, 5),
+    "topk_n138M_0.1%": ("topk", 138_000_000, 0.001, (1e-3, 0.01, 0.1), 3, 2),
+    "topk_segments_n138M_0.1%": ("segments", 138_000_000, 0.001, (1e-3, 0.01, 0.1), 3, 2),
+    "topk_n1.5e9_0.1%": ("topk", 1_500_000_000, 0.001, (1e-3, 0.005, 0.05), 5, 2),
+    "threshold_n1.5e9": ("threshold", 1_500_000_000, 4e-3, (1e-3, 0.005, 0.05), 5, 1),
+    "gtopk_P32_k25600": ("gtopk", 25_600_000, 0.0, None, 4, 0),
+}
+
+
+def run_other(args):
+    """Times one of the other workloads (see the module docstring)."""
+    import numpy as np
+    import torch
+    import top_gradient_sparsification_amd as tgs
+    from top_gradient_sparsification_amd import workloads
+
+    kind, n, par, mix, cfg, prior = OTHER[args.workload]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    flush = torch.empty(128 << 20, dtype=torch.float32, device=dev) if n < 200_000_000 or kind == "gtopk" else None
+    print("bench: preparing %s" % args.workload, file=sys.stderr, flush=True)
+    if kind == "gtopk":
+        P, k = 32, 25_600
+        gi, gv = workloads.gtopk_sets(P=P, k=k, n=n, hot=51_200)
+        ti, tv = torch.from_numpy(gi).to(dev), torch.from_numpy(gv).to(dev)
+        ws = torch.zeros(tgs.gtopk_workspace_bytes(P, k, n), dtype=torch.uint8, device=dev)
+        restore = lambda: None
+        call = lambda: tgs.gtopk_merge(ti, tv, n, ws=ws, check=False)
+        nbytes, elems, what = 8.0 * P * k + 8.0 * k + P * k, P * k, "pairs merged"
+    else:
+        sigma, p_out, b_out = mix
+        grads = [workloads.mixture_gpu(n, sigma, p_out, b_out, (cfg, 200, j), device=dev) for j in range(prior + 1)]
+        resid = torch.zeros(n, dtype=torch.float32, device=dev)
+        if kind == "threshold":
+            cap = 30_000_000
+            oi = torch.empty(cap, dtype=torch.int32, device=dev)
+            ov = torch.empty(cap, dtype=torch.float32, device=dev)
+            cnt = torch.zeros(1, dtype=torch.int64, device=dev)
+            ws = torch.zeros(tgs.threshold_workspace_bytes(n), dtype=torch.uint8, device=dev)
+            one = lambda g: tgs.threshold_ef_step(g, resid, par, cap, out_idx=oi, out_val=ov, count=cnt, ws=ws)
+        elif kind == "segments":
+            sizes = workloads.segments_log_uniform(n)
+            offs = np.concatenate([[0], np.cumsum(sizes)])
+            runs = [tgs.TopkStep(int(sz), workloads.k_for_density(int(sz), par), dev) for sz in sizes]
+
+            def one(g):
+                for j, run in enumerate(runs):
+                    a, b = int(offs[j]), int(offs[j + 1])
+                    run(g[a:b], resid[a:b])
+        else:
+            run = tgs.TopkStep(n, workloads.k_for_density(n, par), dev)
+            one = lambda g: run(g, resid)
+        for j in range(prior):  # the residual's error-feedback history
+            one(grads[j])
+        pristine = resid.clone()
+        g_last = grads[prior]
+        del grads[:prior]
+
+        def restore():
+            resid.copy_(pristine)
+
+        call = lambda: one(g_last)
+        elems, what = n, "gradient elements"
+        if kind == "threshold":
+            one(g_last)
+            torch.cuda.synchronize()
+            c = int(cnt.item())
+            nbytes = 12.0 * n + 8.0 * min(c, cap) + 8.0
+        elif kind == "segments":
+            nbytes = 12.0 * n + 8.0 * sum(workloads.k_for_density(int(sz), par) for sz in sizes)
+        else:
+            nbytes = 12.0 * n + 8.0 * workloads.k_for_density(n, par)
+    for _ in range(3):  # warm-up calls
+        restore()
+        call()
+    torch.cuda.synchronize()
+    K = max(1, args.steps if args.steps != 500 else (20 if n < 1_000_000_000 else 5))
+    times = []
+    print("bench: timing %d calls" % K, file=sys.stderr, flush=True)
+    for _ in range(K):
+        restore()
+        if flush is not None:
+            flush.fill_(1.0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    times.sort()
+    med = times[len(times) // 2]
+    gbps = nbytes / (med * 1e-3) / 1e9
+    rec = {
+        "metric": "%s/sec (GB/s, %% HBM roofline), %s" % (what, args.workload),
+        "value": elems / (med * 1e-3),
+        "unit": "pairs/s" if kind == "gtopk" else "elements/s",
+        "n_gpus": 1, "steps": K, "warmup": 3, "ms_per_step": med,
+        "ms_per_step_min": times[0],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32" if kind != "gtopk" else "f32+i32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "n": n},
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None, "kernel": "whole call (all its kernels)",
+                     "bytes_per_launch": nbytes,
+                     "timing": "HIP event pair per call (median of %d); residual restored and the cache flushed "
+                               "between calls" % K},
+        "cpu_baseline": None,
+    }
+    if kind == "threshold":
+        rec["config"]["count"] = c
+    print(json.dumps(rec))
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="topk_n25.6M_0.1%", choices=sorted(OTHER) + ["topk_n25.6M_0.1%"])
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before the steps, copy a 256 MiB buffer three times (a plain copy kernel of known "
                          "size, for scaling the FETCH_SIZE/WRITE_SIZE counters)")
@@ -56,11 +196,11 @@ def parse():
 # the 256 MiB copy of --copy-calibration.  Valid only for the k_step
 # source they were taken on: `source_sha256` is the hash of csrc/topk.hip then.
 MEASURED_TRAFFIC = {
-    "source_sha256": "5222603f03ba9a6c02403537c2e3336e2e8849018db53a84a5d5b053a0a32543",
-    # FETCH_SIZE 103,058.1 KiB x (262,144 / 131,083.5: the copy's true read over its counter)
-    "fetch_bytes": 211_044_472,
-    # WRITE_SIZE 102,284.9 KiB x 1.0 (the copy's counter read exactly 262,144 KiB)
-    "write_bytes": 104_739_737,
+    "source_sha256": "39ff11c688e371a00df89f7b20012b251a45c526a67a5c54457ca4915c721543",
+    # FETCH_SIZE 103,060.8 KiB x (262,144 / 131,083.5: the copy's true read over its counter)
+    "fetch_bytes": 211049963,
+    # WRITE_SIZE 102,287.7 KiB x 1.0 (the copy's counter read exactly 262,144 KiB)
+    "write_bytes": 104742640,
 }
 
 
@@ -82,6 +222,9 @@ def main():
               "(the per-worker step shards as independent units; see the design notes). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.workload != "topk_n25.6M_0.1%":
+        run_other(args)
+        return
     import numpy as np
     import torch
     import top_gradient_sparsification_amd as tgs

@@ -151,7 +151,19 @@ const char* tgs_last_error(void);
  *                       candidate each (the plan fails; on-device fallback),
  *                       6 = fast path with one fixed slot per bucket and
  *                       workgroup (nearly every candidate goes through the
- *                       overflow area).
+ *                       overflow area),
+ *                       7 = guided general path whose guessed bin is the
+ *                       highest one sampled (the guess fails; the general
+ *                       path reads acc again),
+ *                       8 = guided general path whose candidate regions
+ *                       hold one pair (they overflow; the general path reads
+ *                       acc again),
+ *                       9 = guided general path (the accumulate pass copies
+ *                       out the candidates of a sampled first-level bin)
+ *                       where the fast path would otherwise run.
+ *                       The guided path needs n >= 2^22, grad and residual
+ *                       equally aligned modulo 16 bytes and k > 0; otherwise
+ *                       7-9 run the plain general path.
  *   TGS_OPT_MAIN_GRID   0 = automatic, else the number of workgroups of the
  *                       streaming launch, capped at what can be resident;
  *                       below 65 the exact path runs (results must not

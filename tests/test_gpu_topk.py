@@ -333,3 +333,88 @@ def test_workspace_shared_by_all_operations(tgs_gpu):
             gi, gv = workloads.gtopk_sets(P=4, k=512, n=n, hot=1024)
             tgs_gpu.gtopk_merge(gpu(gi), gpu(gv), n, ws=ws)
             tgs_gpu.check_device_error(ws)
+
+
+def _guided(ws):
+    """(guided_used, guided_missed) words of a top-k workspace."""
+    w = host(ws[:32].view(torch.int32))
+    return int(w[6]), int(w[7])
+
+
+def _guided_step(tgs_gpu, g, r, k):
+    ws = torch.zeros(tgs_gpu.topk_workspace_bytes(g.numel(), k), dtype=torch.uint8, device=g.device)
+    idx, val = tgs_gpu.topk_ef_step(g, r, k, ws=ws)
+    tgs_gpu.check_device_error(ws)
+    return (host(idx), host(val), host(r)), _guided(ws)
+
+
+@pytest.mark.parametrize("dist", ["normal", "mixture", "ties", "special"])
+def test_guided_general_path(tgs_gpu, dist):
+    """Path 9: the accumulate pass copies out the entries of a sampled
+    first-level bin and above while it streams, and the general path selects
+    among the copies (no second read of acc).  n spans 256 chunks of whole
+    rows plus a ragged last chunk and tail."""
+    tgs_gpu.set_option(tgs_gpu.OPT_TOPK_PATH, 9)
+    rng = np.random.default_rng(41)
+    n = 4_200_007
+    grad, res = make(dist, n, rng)
+    for k in (1, 4200, 100_000):
+        got, (used, missed) = _guided_step(tgs_gpu, gpu(grad), gpu(res), k)
+        assert_topk_equal(got, oracle_topk(grad, res, k), "%s k=%d" % (dist, k))
+        assert used + missed == 1
+        if dist in ("normal", "mixture"):
+            assert used == 1, "%s k=%d: the sampled guess should hold" % (dist, k)
+
+
+@pytest.mark.parametrize("path", [7, 8])
+def test_guided_general_path_misses(tgs_gpu, path):
+    """Path 7: the guessed bin is the highest one sampled, above the k-th
+    key's bin; path 8: every candidate region overflows.  Either way the
+    general path reads acc again and must still match the oracle."""
+    tgs_gpu.set_option(tgs_gpu.OPT_TOPK_PATH, path)
+    rng = np.random.default_rng(43 + path)
+    n = 4_194_304 + 4097
+    grad, res = make("mixture", n, rng)
+    for k in (5000, 60_000):
+        got, (used, missed) = _guided_step(tgs_gpu, gpu(grad), gpu(res), k)
+        assert_topk_equal(got, oracle_topk(grad, res, k), "path=%d k=%d" % (path, k))
+        assert (used, missed) == (0, 1)
+
+
+@pytest.mark.parametrize("off", [1, 2, 3])
+def test_guided_general_path_misaligned(tgs_gpu, off):
+    """Equal 4-byte offsets: a scalar head in workgroup 0's chunk, whose
+    candidates must come before those of the first row."""
+    tgs_gpu.set_option(tgs_gpu.OPT_TOPK_PATH, 9)
+    rng = np.random.default_rng(47 + off)
+    n = 4_194_304 + 3 * off
+    grad, res = make("normal", n, rng)
+    # the largest entries sit in the head and the tail
+    grad[:off] = np.float32(100.0)
+    grad[-3:] = np.float32(-100.0)
+    gb = torch.zeros(n + 8, dtype=torch.float32, device="cuda")
+    rb = torch.zeros(n + 8, dtype=torch.float32, device="cuda")
+    gb[off:off + n] = gpu(grad)
+    rb[off:off + n] = gpu(res)
+    k = 20_000
+    got, (used, _) = _guided_step(tgs_gpu, gb[off:off + n], rb[off:off + n], k)
+    assert_topk_equal(got, oracle_topk(grad, res, k), "offset %d" % off)
+    assert used == 1
+    assert np.all(host(rb[:off]) == 0) and np.all(host(rb[off + n:]) == 0)
+
+
+def test_guided_is_the_default_for_large_k(tgs_gpu):
+    """k above what the one-launch step buckets: the guided general path runs
+    by default, over 3 chained EF steps sharing one workspace."""
+    rng = np.random.default_rng(53)
+    n, k = 6_000_000, 120_000
+    r_gpu = torch.zeros(n, dtype=torch.float32, device="cuda")
+    r_cpu = np.zeros(n, np.float32)
+    ws = torch.zeros(tgs_gpu.topk_workspace_bytes(n, k), dtype=torch.uint8, device="cuda")
+    for step in range(3):
+        grad = workloads.mixture(n, 1e-3, 0.01, 0.1, (91, step, 1))
+        idx, val = tgs_gpu.topk_ef_step(gpu(grad), r_gpu, k, ws=ws)
+        tgs_gpu.check_device_error(ws)
+        ei, ev = oracle.topk_ef_step(grad, r_cpu, k)
+        assert_topk_equal((host(idx), host(val), host(r_gpu)), (ei, ev, r_cpu), "step %d" % step)
+    assert _guided(ws) == (3, 0)

@@ -93,6 +93,12 @@ constexpr int kMaxGenWG = 256;  // workgroups of either general-path launch
 constexpr int kLsdDigits = 512;  // digits of an LSD pass at most (9 bits)
 
 // reasons a plan did not hold (StepCtl::why)
+constexpr u32 kNoGuide = 0xFFFFFFFFu;  // guided accumulate pass: keep no candidates
+constexpr int kGuessThreads = 1024;
+constexpr int kGuessBlocks = 256;
+constexpr int kGuessUnroll = 8;  // sample chunks per wave, all loads in flight at once
+constexpr int64_t kGuessMaxChunks = (int64_t)kGuessBlocks * (kGuessThreads / kWave) * kGuessUnroll;
+constexpr int64_t kGuideMinN = (int64_t)1 << 22;  // smaller vectors take the plain accumulate pass
 constexpr u32 kWhyPlan = 1u, kWhyBucket = 4u, kWhyFew = 8u, kWhyRegion = 16u, kWhyList = 32u, kWhyWait = 64u;
 
 // ------------------------------------------------------------- state ----
@@ -140,31 +146,42 @@ struct StepCtl {
   u32 fallbacks;  // fast-path calls whose plan did not hold (never reset)
   u32 why;        // OR of kWhy* reasons over those calls (never reset)
   u32 rescans;    // workgroup shares re-read because their list was incomplete (never reset)
-  u32 pad1[58];
+  u32 guided_used;    // guided general-path calls that selected from the copied candidates (never reset)
+  u32 guided_missed;  // guided calls whose guess or regions did not hold: acc read again (never reset)
+  u32 pad1[56];
   StepSet set[2];
   Plan plan;
+  // guided accumulate pass (standalone general path): k_guess adds its sample
+  // histogram into guide_hist; its last workgroup picks guide_bin and leaves
+  // guide_hist, guide_done and guide_ovf zero for the accumulate pass
+  u32 guide_hist[2048];
+  u32 guide_done;
+  u32 guide_bin;  // candidates are the entries of first-level bins >= guide_bin (kNoGuide: none)
+  u32 guide_ovf;  // set by the accumulate pass when a workgroup's region overflowed
 };
 static_assert(sizeof(StepCtl) <= kWorkspaceHeader, "control block exceeds the workspace header");
+static_assert(kMaxAccBlocks <= kMaxGenWG, "one guided region per general-path workgroup");
 
 // State of the general path (zero when it starts).
 struct GenState {
   u32 hist[3][2048];
-  u32 bar_cnt[9][32];  // grid barrier counters, one cache line each
-  u32 bar_gen[8][32];  // grid barrier generation, 8 copies
+  u32 bar_cnt[9][32];  // grid barrier group counters, one cache line each
+  u32 bar_gen[8][32];  // grid barrier all-counter, 8 copies
   u32 bar_abort;
   u32 cand_ovf;
 };
 
 struct TopkLayout {
-  size_t ctl, gstate, gcnt, lsd_cnt, lsd_pre, lsd_tot, bufA, bufB, cand, hist_rows, pub, rcnt, slots, ovf, total;
+  size_t ctl, gstate, gcnt, lsd_cnt, lsd_pre, lsd_tot, bufA, bufB, cand, hist_rows, guide_cnt, pub, rcnt, slots, ovf, total;
   u32 cand_cap;
 };
 
 // Pairs one candidate region (one wave of the standalone general path) holds:
-// room for 3 k spread evenly, plus slack.
+// room for 4 k spread evenly, plus slack.  The guided accumulate pass fills
+// the regions of one workgroup's waves as a single region.
 static u32 cand_region_cap(int64_t k) {
   const int64_t regions = (int64_t)kMaxGenWG * (kGenThreads / kWave);
-  const int64_t c = (3 * k + regions - 1) / regions + 64;
+  const int64_t c = (4 * k + regions - 1) / regions + 64;
   return (u32)((c + 63) / 64 * 64);
 }
 
@@ -190,6 +207,7 @@ static TopkLayout topk_layout(int64_t n, int64_t k) {
   L.cand_cap = cand_region_cap(k);
   L.cand = take(sizeof(u64) * (size_t)kMaxGenWG * (kGenThreads / kWave) * L.cand_cap);
   L.hist_rows = take(sizeof(u32) * 2048 * (size_t)kMaxAccBlocks);
+  L.guide_cnt = take(sizeof(u32) * (size_t)kMaxAccBlocks);
   L.pub = take(sizeof(u32) * ((size_t)kPlanCap + kMaxStepBlocks));
   L.rcnt = take(sizeof(u32) * (size_t)kMaxStepBlocks * (kMaxBuckets / 2));
   L.slots = take(sizeof(Pair) * (size_t)kMaxBuckets * kSlotTotal);
@@ -262,6 +280,14 @@ struct GenArgs {
   u32 cand_cap;
   u32 acc_rows;          // rows of acc_hist (standalone path)
   const u32* acc_hist;   // [acc_rows][2048] first-level histograms from the accumulate pass
+  // guided accumulate pass (guided != 0; then acc_rows == the grid): workgroup
+  // b's candidates, the entries of first-level bins >= *guide_bin in index
+  // order, fill the regions of its waves as one region of guide_cnt[b] pairs
+  u32 guided;
+  const u32* guide_bin;
+  const u32* guide_ovf;
+  const u32* guide_cnt;
+  u32* guide_stats;  // [2]: guided_used, guided_missed
 };
 
 // Sum over the block of one value per thread.
@@ -377,7 +403,7 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
   // every workgroup.
   bool use_cand = false;
   u32 ccount = 0;
-  const u64* const creg = kCand ? opaque_ptr(a.cand + (size_t)(b * NW + w) * a.cand_cap) : nullptr;
+  const u64* creg = kCand ? opaque_ptr(a.cand + (size_t)(b * NW + w) * a.cand_cap) : nullptr;
   auto load_cand_tile = [&](u32 o, u64* pv) -> u32 {
     u32 vm = 0;
 #pragma unroll
@@ -494,6 +520,25 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
     need -= n_above;
     const int64_t h = s_found[2];
     prefix = (prefix << wd) | d;
+    if constexpr (kCand) {
+      // The guided accumulate pass already copied out every entry of the bins
+      // >= its guessed bin: when that bin is at or below d and no region
+      // overflowed, those copies hold every entry still in play.  Wave w
+      // takes the w-th eighth of its workgroup's region (index order holds).
+      // Every workgroup reads the same words, so all decide alike.
+      if (L == 0 && a.guided) {
+        const u32 gb = *a.guide_bin;
+        if (gb != kNoGuide && gb <= d && *a.guide_ovf == 0u) {
+          const u32 cntb = a.guide_cnt[b];
+          const u32 part = (cntb + NW - 1) / NW;
+          const u32 lo = std::min(cntb, (u32)w * part), hi = std::min(cntb, lo + part);
+          creg = opaque_ptr(a.cand + (size_t)b * NW * a.cand_cap + lo);
+          ccount = hi - lo;
+          use_cand = true;
+        }
+        if (b == 0 && tid == 0) atomicAdd(&a.guide_stats[use_cand ? 0 : 1], 1u);
+      }
+    }
     if (need == h) {  // the whole digit range is taken: select key >= prefix << sh
       t_strict = (int64_t)((u64)prefix << sh) - 1;
       r = 0;
@@ -508,7 +553,7 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
       // After the first level: copy the entries of bins >= d (n_above + h of
       // them) out of acc once, and run the rest on the copies -- unless they
       // would crowd the regions, or one wave's share does not fit.
-      if (L == 0 && (u64)(n_above + h) <= (u64)a.bar.nwg * NW * a.cand_cap * 3 / 4) {
+      if (L == 0 && !use_cand && (u64)(n_above + h) <= (u64)a.bar.nwg * NW * a.cand_cap * 3 / 4) {
         const u32 lo = d << sh;
         u64* const out = (u64*)creg;
         const u32 i0 = (u32)cb + (u32)lane;
@@ -813,6 +858,210 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_pass(AccArgs a) {
   }
   __syncthreads();
   for (int i = tid; i < 2048; i += NT) a.hist_rows[(size_t)blockIdx.x * 2048 + i] = s_h[i];
+}
+
+// ------------------------------------------------------------- k_guess ----
+// Guess of the first-level bin that holds the k-th key, from a sample of
+// chunks of 64 consecutive entries spread over the vector.  The guessed bin
+// is the highest one whose bins and those above it hold at least c_req sample
+// entries, c_req being the expected sample count above the k-th key plus six
+// standard deviations of its Poisson noise: the whole vector then holds at
+// least k entries in those bins except with negligible probability.  A guess
+// whose bins would hold more than s_max sample entries (more candidates than
+// the regions can take) is dropped.  The guess shapes only how much work the
+// later passes do; whether it held is checked against the exact histogram.
+struct GuessArgs {
+  const float* grad;
+  const float* residual;
+  int64_t chunks, stride;  // chunk c covers [c * stride, c * stride + 64); stride >= 64
+  u32 c_req, s_max;
+  StepCtl* ctl;
+};
+
+__global__ __launch_bounds__(kGuessThreads) void k_guess(GuessArgs a) {
+  constexpr int NT = kGuessThreads, NW = NT / kWave;
+  __shared__ u32 s_h[2048];
+  __shared__ u32 s_scan[NW + 1];
+  __shared__ u32 s_last, s_pick;
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  for (int i = tid; i < 2048; i += NT) s_h[i] = 0;
+  __syncthreads();
+  const int64_t W = (int64_t)gridDim.x * NW;
+  const int64_t c0 = (int64_t)blockIdx.x * NW + w;
+  float gq[kGuessUnroll], rq[kGuessUnroll];
+#pragma unroll
+  for (int u = 0; u < kGuessUnroll; ++u) {
+    const int64_t c = c0 + u * W;
+    const int64_t i = (c < a.chunks ? c : 0) * a.stride + lane;
+    gq[u] = a.grad[i];
+    rq[u] = a.residual[i];
+  }
+#pragma unroll
+  for (int u = 0; u < kGuessUnroll; ++u)
+    if (c0 + u * W < a.chunks) atomicAdd(&s_h[key_of(rq[u] + gq[u]) >> 20], 1u);
+  __syncthreads();
+  StepCtl* ctl = a.ctl;
+  for (int i = tid; i < 2048; i += NT)
+    if (s_h[i]) add_agent_relaxed(&ctl->guide_hist[i], s_h[i]);
+  wait_all_memory();
+  __syncthreads();
+  if (tid == 0) s_last = add_agent_acqrel(&ctl->guide_done, 1u) == gridDim.x - 1 ? 1u : 0u;
+  __syncthreads();
+  if (!s_last) return;
+  // last workgroup: every other one has added its histogram
+  static_assert(NT * 2 == 2048, "two bins per thread");
+  const int hi = 2047 - 2 * tid;  // this thread's bins, from the top: hi, hi - 1
+  const u32 h1 = ld_agent(&ctl->guide_hist[hi]), h0 = ld_agent(&ctl->guide_hist[hi - 1]);
+  u32 tot;
+  const u32 above = block_exclusive_sum<NT>(h1 + h0, s_scan, tot);
+  if (tid == 0) s_pick = 0u;  // no bin reaches c_req: every bin
+  __syncthreads();
+  if (above < a.c_req && above + h1 + h0 >= a.c_req) s_pick = above + h1 >= a.c_req ? (u32)hi : (u32)(hi - 1);
+  __syncthreads();
+  const u32 pick = s_pick;
+  // sample entries in the bins >= pick
+  const u32 mine = (u32)hi >= pick ? h1 : 0u, mine0 = (u32)(hi - 1) >= pick ? h0 : 0u;
+  const u32 kept = block_sum<NT>(mine + mine0, s_scan);
+  st_agent(&ctl->guide_hist[hi], 0u);
+  st_agent(&ctl->guide_hist[hi - 1], 0u);
+  if (tid == 0) {
+    st_agent(&ctl->guide_bin, kept <= a.s_max ? pick : kNoGuide);
+    st_agent(&ctl->guide_ovf, 0u);
+    st_agent(&ctl->guide_done, 0u);
+  }
+}
+
+// ------------------------------------------------------- k_acc_guided ----
+// The accumulate pass of the standalone general path, given the guessed bin:
+// acc = residual + grad written back to residual, the first-level histogram
+// of each workgroup, and the candidates -- every entry of the bins >= the
+// guessed bin -- copied into one region per workgroup in index order.
+// Workgroup b streams one contiguous chunk of per_v float4 (whole rows of NT
+// float4; workgroup 0 also takes the scalar head, the last non-empty chunk
+// the scalar tail), so the regions in workgroup order are in index order.
+// Inside a row, a candidate's place is the count of candidates before it:
+// in earlier waves (wave totals in LDS, one barrier per row), in earlier
+// lanes of its wave (DPP scan) and earlier in its own float4.
+struct GuidedArgs {
+  const float* grad;
+  float* residual;
+  int64_t n;
+  int64_t head;   // scalar entries before the 16-byte aligned part
+  int64_t nv;     // float4 vectors in the aligned part
+  int64_t per_v;  // float4 vectors per workgroup chunk, a multiple of the workgroup size
+  u32* zero_ptr;
+  int zero_words;
+  u32* err;
+  u32* hist_rows;  // [gridDim.x][2048]
+  const StepCtl* ctl;  // guide_bin (read), guide_ovf (set on overflow)
+  u32* guide_ovf;
+  u32* guide_cnt;  // [gridDim.x] candidates found (a count above cap means the region overflowed)
+  u64* cand;       // workgroup b's region: cand + b * cap
+  u32 cap;
+};
+
+__global__ __launch_bounds__(kAccThreads) void k_acc_guided(GuidedArgs a) {
+  constexpr int NT = kAccThreads, NW = NT / kWave;
+  __shared__ u32 s_h[2048];
+  __shared__ u32 s_wc[2][NW];
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  for (int i = tid; i < 2048; i += NT) s_h[i] = 0;
+  if (blockIdx.x == 0) {
+    for (int i = tid; i < a.zero_words; i += NT) a.zero_ptr[i] = 0u;
+    if (tid == 0) *a.err = 0u;
+  }
+  const u32 gbin = a.ctl->guide_bin;
+  const bool guide = gbin != kNoGuide;  // the same in every thread
+  __syncthreads();
+  const int b = blockIdx.x;
+  const int64_t v0 = std::min<int64_t>(a.nv, (int64_t)b * a.per_v);
+  const int64_t v1 = std::min<int64_t>(a.nv, v0 + a.per_v);
+  u64* const reg = a.cand + (size_t)b * a.cap;
+  u32 cnt = 0;  // candidates of this workgroup so far (the same in every thread)
+  int par = 0;
+  // Ordered append of this thread's kept entries i0 + q (bit q of m4); every
+  // thread of the workgroup calls it.
+  auto place = [&](u32 m4, int64_t i0, const u32* bq) {
+    const u32 c = (u32)__popc(m4);
+    const u32 incl = wave_inclusive_sum(c);
+    if (lane == kWave - 1) s_wc[par][w] = incl;
+    __syncthreads();
+    u32 off = 0, tot = 0;
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+      const u32 t = s_wc[par][j];
+      off += j < w ? t : 0u;
+      tot += t;
+    }
+    u32 pos = cnt + off + incl - c;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if ((m4 >> q) & 1u) {
+        if (pos < a.cap) reg[pos] = pack_pair(Pair{(int32_t)(i0 + q), bq[q]});
+        ++pos;
+      }
+    cnt += tot;
+    par ^= 1;
+  };
+  float* __restrict__ r = a.residual;
+  const float* __restrict__ g = a.grad;
+  auto scalar = [&](int64_t i, bool in) {  // entry i if `in`; every thread calls it
+    u32 m = 0, bq[4] = {0u, 0u, 0u, 0u};
+    if (in) {
+      const float acc = r[i] + g[i];
+      r[i] = acc;
+      bq[0] = __float_as_uint(acc);
+      const u32 bin = key_of_bits(bq[0]) >> 20;
+      atomicAdd(&s_h[bin], 1u);
+      m = guide && bin >= gbin ? 1u : 0u;
+    }
+    if (guide) place(m, i, bq);
+  };
+  if (b == 0) scalar(tid, tid < a.head);
+  const v4f* __restrict__ gv = (const v4f*)(g + a.head);
+  v4f* __restrict__ rv = (v4f*)(r + a.head);
+  const int64_t nrow = (v1 - v0 + NT - 1) / NT;
+  auto load = [&](int64_t t, v4f& gg, v4f& rr) {
+    const int64_t i = v0 + t * NT + tid;
+    if (t < nrow && i < v1) {
+      gg = __builtin_nontemporal_load(gv + i);
+      rr = __builtin_nontemporal_load(rv + i);
+    }
+  };
+  auto process = [&](int64_t t, const v4f& gg, const v4f& rr) {
+    const int64_t i = v0 + t * NT + tid;
+    u32 m4 = 0, bq[4] = {0u, 0u, 0u, 0u};
+    if (i < v1) {
+      const v4f acc = rr + gg;
+      __builtin_nontemporal_store(acc, rv + i);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        bq[q] = __float_as_uint(acc[q]);
+        const u32 bin = key_of_bits(bq[q]) >> 20;
+        atomicAdd(&s_h[bin], 1u);
+        m4 |= (guide && bin >= gbin ? 1u : 0u) << q;
+      }
+    }
+    if (guide) place(m4, a.head + 4 * i, bq);
+  };
+  v4f ga, ra, gb, rb;
+  load(0, ga, ra);
+  load(1, gb, rb);
+  for (int64_t t = 0; t < nrow; t += 2) {
+    process(t, ga, ra);
+    load(t + 2, ga, ra);
+    if (t + 1 >= nrow) break;
+    process(t + 1, gb, rb);
+    load(t + 3, gb, rb);
+  }
+  const int64_t tail0 = a.head + 4 * a.nv;
+  if (v0 < v1 && v1 == a.nv) scalar(tail0 + tid, tail0 + tid < a.n);
+  __syncthreads();
+  for (int i = tid; i < 2048; i += NT) a.hist_rows[(size_t)b * 2048 + i] = s_h[i];
+  if (tid == 0) {
+    a.guide_cnt[b] = cnt;
+    if (cnt > a.cap) atomicOr(a.guide_ovf, 1u);
+  }
 }
 
 __global__ __launch_bounds__(kGenThreads) void k_general(GenArgs a) { general_path<kGenThreads, 16, true, 9, true>(a); }
@@ -1965,7 +2214,7 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
 
   StepArgs sa{};
   int G = 0;
-  if (path != 1) {
+  if (path != 1 && path < 7) {
     const int cap = step_capacity();
     G = gopt > 0 ? (int)std::min<int64_t>(gopt, cap) : cap;
     if (!step_params(n, k, G, sa)) G = 0;
@@ -2021,8 +2270,7 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
     aa.hist_rows = (u32*)(ws + L.hist_rows);
     ga.acc_hist = aa.hist_rows;
     ga.acc_rows = (u32)G1;
-    if (vec) hipLaunchKernelGGL(k_acc_pass<true>, dim3(G1), dim3(kAccThreads), 0, stream, aa);
-    else hipLaunchKernelGGL(k_acc_pass<false>, dim3(G1), dim3(kAccThreads), 0, stream, aa);
+    int G2 = 0;
     if (k > 0) {
       // every workgroup of k_general must be resident at once (grid barriers)
       static int occ = 0;
@@ -2033,7 +2281,59 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
       }
       const int cus = device_cu_count();
       if (cus <= 0) return fail(TGS_EHIP, "topk_ef_step: cannot read the compute-unit count");
-      const int G2 = std::max(1, std::min(kGenBlocks, cus * occ));
+      G2 = std::max(1, std::min(kGenBlocks, cus * occ));
+    }
+    // The guided accumulate pass copies the candidates out while it streams,
+    // so k_general need not read acc again: it takes one region per
+    // workgroup of k_general, in index order.
+    const bool guided = vec && k > 0 && path != 1 && n >= kGuideMinN && G1 == G2;
+    if (guided) {
+      const int64_t want = (int64_t)std::ceil(2048.0 * (double)n / (double)k);  // ~2048 expected above the k-th key
+      int64_t chunks = (want + kSampleChunk - 1) / kSampleChunk;
+      chunks = std::max<int64_t>(1, std::min<int64_t>({chunks, kGuessMaxChunks, n / (4 * kSampleChunk)}));
+      GuessArgs q{};
+      q.grad = grad;
+      q.residual = residual;
+      q.chunks = chunks;
+      q.stride = n / chunks;
+      const double f = (double)(chunks * kSampleChunk) / (double)n;
+      const double c = (double)k * f;
+      q.c_req = path == 7 ? 1u : (u32)std::min(4.0e9, std::ceil(c + 6.0 * std::sqrt(c) + 8.0));
+      const double room = (double)G1 * (kGenThreads / kWave) * L.cand_cap;
+      q.s_max = (u32)std::min(4.0e9, std::floor(0.6 * room * f));
+      q.ctl = ctl;
+      const int gq = (int)std::min<int64_t>(kGuessBlocks, (chunks + (kGuessThreads / kWave) * kGuessUnroll - 1) /
+                                                              ((kGuessThreads / kWave) * kGuessUnroll));
+      hipLaunchKernelGGL(k_guess, dim3(gq), dim3(kGuessThreads), 0, stream, q);
+      GuidedArgs g{};
+      g.grad = grad;
+      g.residual = residual;
+      g.n = n;
+      g.head = head;
+      g.nv = nv;
+      g.per_v = (nv + G1 - 1) / G1;
+      g.per_v = (g.per_v + kAccThreads - 1) / kAccThreads * kAccThreads;
+      g.zero_ptr = aa.zero_ptr;
+      g.zero_words = aa.zero_words;
+      g.err = aa.err;
+      g.hist_rows = aa.hist_rows;
+      g.ctl = ctl;
+      g.guide_ovf = &ctl->guide_ovf;
+      g.guide_cnt = (u32*)(ws + L.guide_cnt);
+      g.cand = ga.cand;
+      g.cap = path == 8 ? 1u : (u32)(kGenThreads / kWave) * L.cand_cap;
+      hipLaunchKernelGGL(k_acc_guided, dim3(G1), dim3(kAccThreads), 0, stream, g);
+      ga.guided = 1;
+      ga.guide_bin = &ctl->guide_bin;
+      ga.guide_ovf = &ctl->guide_ovf;
+      ga.guide_cnt = g.guide_cnt;
+      ga.guide_stats = &ctl->guided_used;
+    } else if (vec) {
+      hipLaunchKernelGGL(k_acc_pass<true>, dim3(G1), dim3(kAccThreads), 0, stream, aa);
+    } else {
+      hipLaunchKernelGGL(k_acc_pass<false>, dim3(G1), dim3(kAccThreads), 0, stream, aa);
+    }
+    if (k > 0) {
       ga.bar.nwg = (u32)G2;
       hipLaunchKernelGGL(k_general, dim3(G2), dim3(kGenThreads), 0, stream, ga);
     }

@@ -366,15 +366,20 @@ def test_guided_general_path(tgs_gpu, dist):
             assert used == 1, "%s k=%d: the sampled guess should hold" % (dist, k)
 
 
-@pytest.mark.parametrize("path", [7, 8])
+@pytest.mark.parametrize("path", [7, 8, 9])
 def test_guided_general_path_misses(tgs_gpu, path):
     """Path 7: the guessed bin is the highest one sampled, above the k-th
-    key's bin; path 8: every candidate region overflows.  Either way the
-    general path reads acc again and must still match the oracle."""
+    key's bin; path 8: every candidate region overflows; path 9 with 3000
+    entries of one value among the largest: one ranking bucket holds more
+    than it may.  Each time the general path reads acc again and must still
+    match the oracle."""
     tgs_gpu.set_option(tgs_gpu.OPT_TOPK_PATH, path)
     rng = np.random.default_rng(43 + path)
     n = 4_194_304 + 4097
     grad, res = make("mixture", n, rng)
+    if path == 9:
+        grad[rng.choice(n, 3000, replace=False)] = np.float32(0.75)
+        res[:] = 0.0
     for k in (5000, 60_000):
         got, (used, missed) = _guided_step(tgs_gpu, gpu(grad), gpu(res), k)
         assert_topk_equal(got, oracle_topk(grad, res, k), "path=%d k=%d" % (path, k))

@@ -184,12 +184,17 @@ __device__ __forceinline__ u32 block_exclusive_sum(u32 v, u32* lds, u32& total) 
 
 // ---------------------------------------------------- grid barrier ----
 // For the `nwg` workgroups 0 .. nwg-1 of a kernel whose whole grid is resident
-// at once.  Workgroup b arrives at the counter of its group (b % 8); the last
-// arrival of a group resets that counter and arrives at the all-counter; the
-// last of those resets it and bumps the generation, kept in 8 copies so that
-// each group of pollers has its own cache line.  A bounded spin turns a
-// missing workgroup into an error (flag bit in *err, `abort` set) instead of
-// a hang; after an abort every barrier returns at once.
+// at once.  Every counter only grows (all are zero when the kernel starts).
+// Workgroup b arrives at the counter of its group (b % 8).  No workgroup can
+// arrive at barrier e+1 before every workgroup has arrived at barrier e, so
+// the value an arrival returns tells which barrier it is (e = old / per + 1
+// for a group of `per` workgroups) and whether it completes its group.  The
+// last arrival of a group adds one to each of 8 copies of the all-counter
+// (one cache line each, so that each group of pollers has its own), and
+// barrier e is complete once a copy reaches 8 e (or nwg e below 8
+// workgroups).  No reset or generation word sits on the critical path.  A
+// bounded spin turns a missing workgroup into an error (flag bit in *err,
+// `abort` set) instead of a hang; after an abort every barrier returns at once.
 //
 // Writes: every wave waits for its own memory operations to complete before
 // its workgroup arrives, and data that crosses workgroups is stored at device
@@ -198,8 +203,8 @@ __device__ __forceinline__ u32 block_exclusive_sum(u32 v, u32* lds, u32& total) 
 // (an agent-scope acquire: L1 and L2 invalidate, no write-back), so plain
 // loads then see what the others wrote.
 struct GridBar {
-  u32* cnt;    // [9][32]: the 8 group counters, then the all-counter, one cache line each; zero at start
-  u32* gen;    // [8][32]: the generation, one copy per line; any value
+  u32* cnt;    // [9][32]: the 8 group counters, one cache line each; zero at start
+  u32* gen;    // [8][32]: the 8 copies of the all-counter, one per line; zero at start
   u32* abort;  // zero at start
   u32* err;    // device error word
   u32 nwg;     // participating workgroups
@@ -219,34 +224,27 @@ __device__ __forceinline__ bool grid_sync(const GridBar& gb) {
     } else {
       const u32 ng = gb.nwg < 8u ? gb.nwg : 8u;
       const u32 x = blockIdx.x % ng;
-      u32* mygen = gb.gen + 32 * (blockIdx.x & 7u);
-      const u32 g0 = ld_agent(mygen);
       const u32 per = (gb.nwg - 1u - x) / ng + 1u;
-      bool bumped = false;
-      if (add_agent_relaxed(gb.cnt + 32 * x, 1u) == per - 1u) {  // last of its group
-        st_agent(gb.cnt + 32 * x, 0u);
-        wait_all_memory();  // the reset lands before this group can arrive again
-        if (add_agent_relaxed(gb.cnt + 32 * 8, 1u) == ng - 1u) {  // last of all
-          st_agent(gb.cnt + 32 * 8, 0u);
-          wait_all_memory();
-          for (int i = 0; i < 8; ++i) add_agent_relaxed(gb.gen + 32 * i, 1u);
-          bumped = true;
-        }
+      const u32 old = add_agent_relaxed(gb.cnt + 32 * x, 1u);
+      const u32 e = old / per + 1u;
+      if (old + 1u == e * per) {  // last of its group
+#pragma unroll
+        for (int i = 0; i < 8; ++i) (void)add_agent_relaxed(gb.gen + 32 * i, 1u);
       }
-      if (!bumped) {
-        u32 spins = 0;
-        while (ld_agent(mygen) == g0) {
-          __builtin_amdgcn_s_sleep(2);
-          if (++spins > (1u << 23)) {
-            atomicOr(gb.err, kErrBarrierTimeout);
-            st_agent(gb.abort, 1u);
-            ok = 0;
-            break;
-          }
-          if ((spins & 1023u) == 0 && ld_agent(gb.abort) != 0) {
-            ok = 0;
-            break;
-          }
+      const u32* mine = gb.gen + 32 * (blockIdx.x & 7u);
+      const u32 target = e * ng;
+      u32 spins = 0;
+      while ((int)(ld_agent(mine) - target) < 0) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > (1u << 23)) {
+          atomicOr(gb.err, kErrBarrierTimeout);
+          st_agent(gb.abort, 1u);
+          ok = 0;
+          break;
+        }
+        if ((spins & 1023u) == 0 && ld_agent(gb.abort) != 0) {
+          ok = 0;
+          break;
         }
       }
     }

@@ -57,6 +57,7 @@
 #include <algorithm>
 #include <climits>
 #include <cstring>
+#include <type_traits>
 
 #include "tgs_host.h"
 #include "tgs_internal.h"
@@ -94,9 +95,14 @@ constexpr int kLsdDigits = 512;  // digits of an LSD pass at most (9 bits)
 
 // reasons a plan did not hold (StepCtl::why)
 constexpr u32 kNoGuide = 0xFFFFFFFFu;  // guided accumulate pass: keep no candidates
+constexpr u32 kBktMax = 8192;     // buckets of the guided ranking at most
+constexpr u32 kBktCap = 1024;     // entries one bucket may hold
+constexpr u32 kBktBatch = 4096;   // entries a workgroup sorts at once (LDS)
+constexpr u32 kBktRanges = 2048;  // ranges of buckets sorted by one workgroup each, at most
 constexpr int kGuessThreads = 1024;
-constexpr int kGuessBlocks = 256;
+constexpr int kGuessBlocks = 64;
 constexpr int kGuessUnroll = 8;  // sample chunks per wave, all loads in flight at once
+constexpr int kGuessChunk = 4 * kWave;  // entries per sample chunk: one float4 per lane
 constexpr int64_t kGuessMaxChunks = (int64_t)kGuessBlocks * (kGuessThreads / kWave) * kGuessUnroll;
 constexpr int64_t kGuideMinN = (int64_t)1 << 22;  // smaller vectors take the plain accumulate pass
 constexpr u32 kWhyPlan = 1u, kWhyBucket = 4u, kWhyFew = 8u, kWhyRegion = 16u, kWhyList = 32u, kWhyWait = 64u;
@@ -160,7 +166,7 @@ struct StepCtl {
   u32 guide_ovf;  // set by the accumulate pass when a workgroup's region overflowed
 };
 static_assert(sizeof(StepCtl) <= kWorkspaceHeader, "control block exceeds the workspace header");
-static_assert(kMaxAccBlocks <= kMaxGenWG, "one guided region per general-path workgroup");
+static_assert(kMaxAccBlocks <= kMaxGenWG, "guided regions are the general path's");
 
 // State of the general path (zero when it starts).
 struct GenState {
@@ -172,7 +178,8 @@ struct GenState {
 };
 
 struct TopkLayout {
-  size_t ctl, gstate, gcnt, lsd_cnt, lsd_pre, lsd_tot, bufA, bufB, cand, hist_rows, guide_cnt, pub, rcnt, slots, ovf, total;
+  size_t ctl, gstate, gcnt, lsd_cnt, lsd_pre, lsd_tot, bufA, bufB, cand, hist_rows, guide_cnt, bkt_cnt, bkt_cur, bkt_buf,
+      pub, rcnt, slots, ovf, total;
   u32 cand_cap;
 };
 
@@ -207,7 +214,10 @@ static TopkLayout topk_layout(int64_t n, int64_t k) {
   L.cand_cap = cand_region_cap(k);
   L.cand = take(sizeof(u64) * (size_t)kMaxGenWG * (kGenThreads / kWave) * L.cand_cap);
   L.hist_rows = take(sizeof(u32) * 2048 * (size_t)kMaxAccBlocks);
-  L.guide_cnt = take(sizeof(u32) * (size_t)kMaxAccBlocks);
+  L.guide_cnt = take(sizeof(u32) * (size_t)kMaxGenWG);
+  L.bkt_cnt = take(sizeof(u32) * kBktMax);
+  L.bkt_cur = take(sizeof(u32) * kBktMax);
+  L.bkt_buf = take(sizeof(u64) * (size_t)kMaxGenWG * (kGenThreads / kWave) * L.cand_cap);
   L.pub = take(sizeof(u32) * ((size_t)kPlanCap + kMaxStepBlocks));
   L.rcnt = take(sizeof(u32) * (size_t)kMaxStepBlocks * (kMaxBuckets / 2));
   L.slots = take(sizeof(Pair) * (size_t)kMaxBuckets * kSlotTotal);
@@ -280,14 +290,19 @@ struct GenArgs {
   u32 cand_cap;
   u32 acc_rows;          // rows of acc_hist (standalone path)
   const u32* acc_hist;   // [acc_rows][2048] first-level histograms from the accumulate pass
-  // guided accumulate pass (guided != 0; then acc_rows == the grid): workgroup
-  // b's candidates, the entries of first-level bins >= *guide_bin in index
-  // order, fill the regions of its waves as one region of guide_cnt[b] pairs
+  // guided accumulate pass (guided != 0; then acc_rows == the grid): the
+  // entries of first-level bins >= *guide_bin streamed by workgroup b, in no
+  // particular order, fill the regions of its waves as one region of
+  // guide_cnt[b] pairs
   u32 guided;
   const u32* guide_bin;
   const u32* guide_ovf;
   const u32* guide_cnt;
   u32* guide_stats;  // [2]: guided_used, guided_missed
+  // bucket ranking of the guided candidates
+  u32* bkt_cnt;  // [kBktMax] entries per bucket (cleared by this kernel)
+  u32* bkt_cur;  // [kBktMax] places handed out per range of buckets (cleared by this kernel)
+  u64* bkt_buf;  // the candidates, grouped by bucket in bucket order
 };
 
 // Sum over the block of one value per thread.
@@ -319,6 +334,13 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
   const int G = (int)a.bar.nwg;
   const int b = blockIdx.x;
   const int64_t per = (a.n + G - 1) / G;
+  if constexpr (kCand) {
+    if (a.guided)  // zero before the first barrier, used after it
+      for (u32 i = (u32)b * NT + tid; i < kBktMax; i += (u32)G * NT) {
+        st_agent(&a.bkt_cnt[i], 0u);
+        st_agent(&a.bkt_cur[i], 0u);
+      }
+  }
   const int64_t cb = std::min<int64_t>(a.n, (int64_t)b * per);
   const int64_t ce = std::min<int64_t>(a.n, cb + per);
   const u32* accb = (const u32*)a.acc;
@@ -428,6 +450,244 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
     }
   };
 
+  // Guided candidates (any order in the regions): sort every entry of the
+  // first-level bins >= d -- all C of them, the k-th key's bin included --
+  // by (key desc, index asc) and emit the first k.  Each bin's key range is
+  // cut into ceil(count / target) equal buckets, numbered from the top, so
+  // the buckets split the C entries in descending key order:
+  //   1. bucket counts (LDS, then device-scope adds)                | barrier
+  //   2. bucket starts (scan of the counts); the buckets grouped into
+  //      ranges of fewer than kBktBatch entries; places reserved per
+  //      (workgroup, range) and the entries scattered to bkt_buf    | barrier
+  //   3. workgroup b loads ranges b, b + G, ... into LDS; each wave ranks
+  //      whole buckets by counting and writes the entries of place < k.
+  // Returns 1 when done, 0 when a bucket is too large (nothing written; the
+  // caller goes on with the radix select over copies from acc), -1 if a
+  // barrier failed.
+  auto bucket_rank = [&](auto d, auto C) -> int {  // generic: instantiated only where called
+    __shared__ u32 s_bkt[kBktMax];  // counts, then starts
+    __shared__ u64 s_ent[kBktBatch];  // step 3: one range's entries
+    __shared__ u32 s_bbase[2048];   // first bucket of bin j (j >= d)
+    __shared__ u32 s_bnum[2048];    // buckets of bin j
+    __shared__ u32 s_misc[4];
+    __shared__ u32 s_rbeg[kBktRanges];  // first entry of range r
+    __shared__ u32 s_rcnt[kBktRanges];  // this workgroup's entries of range r, then its next place there
+    const u32 target = std::max(32u, (C + (kBktMax - 2048u) - 1u) / (kBktMax - 2048u));
+    // thread t owns bins [2048 - 4 (t + 1), 2048 - 4 t), scanned from the top
+    static_assert(2048 % NT == 0, "bins per thread");
+    constexpr int BPT = 2048 / NT;
+    const int top = 2048 - BPT * tid;
+    u32 own = 0;
+    for (int j = top - 1; j >= top - BPT; --j) {
+      const u32 nb = (u32)j >= d ? (s_hist[j] + target - 1) / target : 0u;
+      s_bnum[j] = nb;
+      own += nb;
+    }
+    u32 nbk;
+    u32 run = block_exclusive_sum<NT>(own, s_scan, nbk);
+    for (int j = top - 1; j >= top - BPT; --j) {
+      s_bbase[j] = run;
+      run += s_bnum[j];
+    }
+    if (nbk > kBktMax) return 0;  // cannot happen: C / target + 2048 bins <= kBktMax
+    for (u32 i = tid; i < nbk; i += NT) s_bkt[i] = 0u;
+    __syncthreads();
+    auto bucket_of_key = [&](u32 key) -> u32 {
+      const u32 j = key >> 20, nb = s_bnum[j];
+      return s_bbase[j] + nb - 1u - (u32)(((u64)(key & 0xFFFFFu) * nb) >> 20);
+    };
+    // 1. counts
+    for_each_cand_tile([&](const u64* pv, u32 vm) {
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        const u32 key = key_of_bits((u32)(pv[j] >> 32));
+        if (((vm >> j) & 1u) && (key >> 20) >= d) atomicAdd(&s_bkt[bucket_of_key(key)], 1u);
+      }
+    });
+    __syncthreads();
+    for (u32 i = tid; i < nbk; i += NT)
+      if (s_bkt[i]) add_agent_relaxed(&a.bkt_cnt[i], s_bkt[i]);
+    if (!grid_sync(a.bar)) return -1;
+    // 2. bucket starts (exclusive scan of the counts; thread t holds buckets
+    // [q0, q1)) into s_bkt; the largest bucket
+    const u32 per_t = (nbk + NT - 1) / NT;
+    const u32 q0 = std::min(nbk, (u32)tid * per_t), q1 = std::min(nbk, q0 + per_t);
+    u32 sum = 0, mx = 0;
+    for (u32 q = q0; q < q1; ++q) {
+      const u32 c = a.bkt_cnt[q];
+      sum += c;
+      mx = std::max(mx, c);
+    }
+    u32 total;
+    const u32 start0 = block_exclusive_sum<NT>(sum, s_scan, total);
+    mx = wave_max(mx);
+    if (tid == 0) s_misc[0] = 0u;
+    __syncthreads();
+    if (lane == 0) atomicMax(&s_misc[0], mx);
+    // Range r holds the buckets that start in [r S, (r+1) S): whole buckets,
+    // fewer than S + kBktCap <= kBktBatch entries, sorted by one workgroup.
+    // Buckets start at most kBktCap apart, so every range holds one.
+    constexpr u32 S = kBktBatch - kBktCap;
+    const u32 D = (C + S - 1) / S;
+    __syncthreads();
+    if (s_misc[0] > kBktCap || total != C || D > kBktRanges) return 0;  // the same in every workgroup
+    for (u32 r = tid; r < D; r += NT) {
+      s_rbeg[r] = C;
+      s_rcnt[r] = 0u;
+    }
+    __syncthreads();
+    {
+      u32 st = start0;
+      for (u32 q = q0; q < q1; ++q) {
+        const u32 c = a.bkt_cnt[q];
+        s_bkt[q] = st;
+        if (st < C) atomicMin(&s_rbeg[st / S], st);  // a range begins at its first bucket
+        st += c;
+      }
+    }
+    __syncthreads();
+    // this workgroup's entries per range, then places reserved per range
+    for_each_cand_tile([&](const u64* pv, u32 vm) {
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        const u32 key = key_of_bits((u32)(pv[j] >> 32));
+        if (((vm >> j) & 1u) && (key >> 20) >= d) atomicAdd(&s_rcnt[s_bkt[bucket_of_key(key)] / S], 1u);
+      }
+    });
+    __syncthreads();
+    for (u32 r = tid; r < D; r += NT) {
+      const u32 c = s_rcnt[r];
+      if (c) s_rcnt[r] = s_rbeg[r] + add_agent_relaxed(&a.bkt_cur[r], c);
+    }
+    __syncthreads();
+    u64* const bout = opaque_ptr(a.bkt_buf);
+    for_each_cand_tile([&](const u64* pv, u32 vm) {
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        const u32 key = key_of_bits((u32)(pv[j] >> 32));
+        if (((vm >> j) & 1u) && (key >> 20) >= d)
+          st_agent64(bout + atomicAdd(&s_rcnt[s_bkt[bucket_of_key(key)] / S], 1u), pv[j]);
+      }
+    });
+    if (!grid_sync(a.bar)) return -1;
+    // 3. workgroup b ranks ranges b, b + G, ...: the entries of range r,
+    // [s_rbeg[r], s_rbeg[r+1]) in bkt_buf, are grouped by bucket into LDS
+    // (counting sort over the range's buckets u0..u1; s_bkt then holds each
+    // bucket's end), and wave w ranks buckets u0 + w, u0 + w + 8, ... by
+    // counting, inside the bucket, the entries with a smaller
+    // (0x7FFFFFFF - key, index).  An entry's place is the range's start plus
+    // its bucket's start in the range plus that count; places below k are
+    // written.
+    static_assert(kBktCap < kBktBatch, "a range holds whole buckets");
+    const u32 kk = (u32)a.k;
+    auto ck = [](u64 p) { return rank_key((u32)(p >> 32), (u32)p); };
+    for (u32 r = (u32)b; r < D; r += (u32)G) {  // the same in every thread
+      const u32 x = s_rbeg[r], y = r + 1 < D ? s_rbeg[r + 1] : C;
+      if (x >= kk) break;
+      if (x >= y) continue;  // cannot happen: every range holds a bucket
+      const u32 m = y - x;
+      // the range's entries in registers (every load in flight at once)
+      constexpr int EPT = kBktBatch / NT;
+      u64 pv[EPT];
+      u32 uq[EPT];
+#pragma unroll
+      for (int j = 0; j < EPT; ++j) {
+        const u32 i = (u32)tid + (u32)j * NT;
+        pv[j] = a.bkt_buf[x + (i < m ? i : 0u)];
+      }
+      u32 umin = 0xFFFFFFFFu, umax = 0u;
+#pragma unroll
+      for (int j = 0; j < EPT; ++j) {
+        uq[j] = bucket_of_key(key_of_bits((u32)(pv[j] >> 32)));
+        if ((u32)tid + (u32)j * NT < m) {
+          umin = std::min(umin, uq[j]);
+          umax = std::max(umax, uq[j]);
+        }
+      }
+      umin = wave_min(umin);
+      umax = wave_max(umax);
+      if (tid == 0) {
+        s_misc[1] = 0xFFFFFFFFu;
+        s_misc[2] = 0u;
+      }
+      __syncthreads();
+      if (lane == 0) {
+        atomicMin(&s_misc[1], umin);
+        atomicMax(&s_misc[2], umax);
+      }
+      __syncthreads();
+      const u32 u0 = s_misc[1], span = s_misc[2] - u0 + 1;  // span <= nbk <= kBktMax
+      for (u32 i = tid; i < span; i += NT) s_bkt[i] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < EPT; ++j)
+        if ((u32)tid + (u32)j * NT < m) atomicAdd(&s_bkt[uq[j] - u0], 1u);
+      __syncthreads();
+      {  // exclusive scan of the span's counts, kBktMax / NT per thread
+        constexpr u32 PT = kBktMax / NT;
+        const u32 i0 = (u32)tid * PT;
+        u32 own_sum = 0;
+        for (u32 i = i0; i < i0 + PT && i < span; ++i) own_sum += s_bkt[i];
+        u32 tot_unused;
+        u32 run2 = block_exclusive_sum<NT>(own_sum, s_scan, tot_unused);
+        for (u32 i = i0; i < i0 + PT && i < span; ++i) {
+          const u32 c = s_bkt[i];
+          s_bkt[i] = run2;
+          run2 += c;
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < EPT; ++j)
+        if ((u32)tid + (u32)j * NT < m) s_ent[atomicAdd(&s_bkt[uq[j] - u0], 1u)] = pv[j];
+      __syncthreads();  // s_bkt[u - u0] is now the end of bucket u in s_ent
+      // Lane l holds entries bs + l + 64 e (e < NE) of a bucket of at most
+      // 64 NE and counts, for all of them at once, the smaller ones among
+      // the bucket's entries, read one at a time (the same LDS address in
+      // every lane).
+      auto rank_bucket = [&](u32 bs, u32 be, auto ne_c) {
+        constexpr int NE = decltype(ne_c)::value;
+        u64 ci[NE];
+        u32 rk[NE];
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+          const u32 i = bs + (u32)lane + (u32)(e * kWave);
+          ci[e] = i < be ? ck(s_ent[i]) : ~0ull;
+          rk[e] = 0;
+        }
+#pragma unroll 4
+        for (u32 j = bs; j < be; ++j) {
+          const u64 cj = ck(s_ent[j]);
+#pragma unroll
+          for (int e = 0; e < NE; ++e) rk[e] += cj < ci[e];
+        }
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+          const u32 i = bs + (u32)lane + (u32)(e * kWave), pos = x + bs + rk[e];
+          if (i < be && pos < kk) {
+            const Pair p = unpack_pair(s_ent[i]);
+            a.out_idx[pos] = p.idx;
+            a.out_val[pos] = __uint_as_float(p.bits);
+            st_agent_f32(a.residual + p.idx, 0.0f);
+          }
+        }
+      };
+      static_assert(kBktCap <= 16 * kWave, "a bucket fits 16 entries per lane");
+      for (u32 v = (u32)w; v < span; v += NW) {  // the same in every lane
+        const u32 bs = v == 0 ? 0u : s_bkt[v - 1], be = s_bkt[v];
+        if (bs >= be || x + bs >= kk) continue;
+        const u32 mb = be - bs;
+        if (mb <= kWave) rank_bucket(bs, be, std::integral_constant<int, 1>{});
+        else if (mb <= 2 * kWave) rank_bucket(bs, be, std::integral_constant<int, 2>{});
+        else if (mb <= 4 * kWave) rank_bucket(bs, be, std::integral_constant<int, 4>{});
+        else if (mb <= 8 * kWave) rank_bucket(bs, be, std::integral_constant<int, 8>{});
+        else rank_bucket(bs, be, std::integral_constant<int, 16>{});
+      }
+      __syncthreads();
+    }
+    return 1;
+  };
+
   // ---------------- radix select of the k-th largest key ----------------
   const int shifts[3] = {20, 9, 0};
   const int widths[3] = {11, 11, 9};
@@ -522,21 +782,28 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
     prefix = (prefix << wd) | d;
     if constexpr (kCand) {
       // The guided accumulate pass already copied out every entry of the bins
-      // >= its guessed bin: when that bin is at or below d and no region
-      // overflowed, those copies hold every entry still in play.  Wave w
-      // takes the w-th eighth of its workgroup's region (index order holds).
-      // Every workgroup reads the same words, so all decide alike.
+      // >= its guessed bin, wave by wave into the regions this kernel's waves
+      // read: when that bin is at or below d and no region overflowed, those
+      // copies hold every entry still in play.  Every workgroup reads the
+      // same words, so all decide alike.
       if (L == 0 && a.guided) {
         const u32 gb = *a.guide_bin;
+        bool ranked = false;
         if (gb != kNoGuide && gb <= d && *a.guide_ovf == 0u) {
           const u32 cntb = a.guide_cnt[b];
           const u32 part = (cntb + NW - 1) / NW;
           const u32 lo = std::min(cntb, (u32)w * part), hi = std::min(cntb, lo + part);
+          const u64* const wave_reg = creg;
           creg = opaque_ptr(a.cand + (size_t)b * NW * a.cand_cap + lo);
           ccount = hi - lo;
-          use_cand = true;
+          const int st = bucket_rank(d, (u32)(n_above + h));
+          if (st < 0) return;
+          ranked = st > 0;
+          creg = wave_reg;  // not ranked: the regions are refilled from acc below
+          ccount = 0;
         }
-        if (b == 0 && tid == 0) atomicAdd(&a.guide_stats[use_cand ? 0 : 1], 1u);
+        if (b == 0 && tid == 0) atomicAdd(&a.guide_stats[ranked ? 0 : 1], 1u);
+        if (ranked) return;
       }
     }
     if (need == h) {  // the whole digit range is taken: select key >= prefix << sh
@@ -862,7 +1129,8 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_pass(AccArgs a) {
 
 // ------------------------------------------------------------- k_guess ----
 // Guess of the first-level bin that holds the k-th key, from a sample of
-// chunks of 64 consecutive entries spread over the vector.  The guessed bin
+// chunks of 256 consecutive entries (one float4 per lane) spread over the
+// 16-byte aligned part of the vector.  The guessed bin
 // is the highest one whose bins and those above it hold at least c_req sample
 // entries, c_req being the expected sample count above the k-th key plus six
 // standard deviations of its Poisson noise: the whole vector then holds at
@@ -871,9 +1139,9 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_pass(AccArgs a) {
 // the regions can take) is dropped.  The guess shapes only how much work the
 // later passes do; whether it held is checked against the exact histogram.
 struct GuessArgs {
-  const float* grad;
-  const float* residual;
-  int64_t chunks, stride;  // chunk c covers [c * stride, c * stride + 64); stride >= 64
+  const v4f* grad;      // the aligned parts (grad + head, residual + head)
+  const v4f* residual;
+  int64_t chunks, stride;  // chunk c covers float4 [c * stride, c * stride + 64); stride >= 64
   u32 c_req, s_max;
   StepCtl* ctl;
 };
@@ -888,17 +1156,21 @@ __global__ __launch_bounds__(kGuessThreads) void k_guess(GuessArgs a) {
   __syncthreads();
   const int64_t W = (int64_t)gridDim.x * NW;
   const int64_t c0 = (int64_t)blockIdx.x * NW + w;
-  float gq[kGuessUnroll], rq[kGuessUnroll];
+  v4f gq[kGuessUnroll], rq[kGuessUnroll];
 #pragma unroll
   for (int u = 0; u < kGuessUnroll; ++u) {
     const int64_t c = c0 + u * W;
     const int64_t i = (c < a.chunks ? c : 0) * a.stride + lane;
-    gq[u] = a.grad[i];
-    rq[u] = a.residual[i];
+    gq[u] = __builtin_nontemporal_load(a.grad + i);
+    rq[u] = __builtin_nontemporal_load(a.residual + i);
   }
 #pragma unroll
   for (int u = 0; u < kGuessUnroll; ++u)
-    if (c0 + u * W < a.chunks) atomicAdd(&s_h[key_of(rq[u] + gq[u]) >> 20], 1u);
+    if (c0 + u * W < a.chunks) {
+      const v4f acc = rq[u] + gq[u];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) atomicAdd(&s_h[key_of(acc[q]) >> 20], 1u);
+    }
   __syncthreads();
   StepCtl* ctl = a.ctl;
   for (int i = tid; i < 2048; i += NT)
@@ -933,39 +1205,37 @@ __global__ __launch_bounds__(kGuessThreads) void k_guess(GuessArgs a) {
 
 // ------------------------------------------------------- k_acc_guided ----
 // The accumulate pass of the standalone general path, given the guessed bin:
-// acc = residual + grad written back to residual, the first-level histogram
-// of each workgroup, and the candidates -- every entry of the bins >= the
-// guessed bin -- copied into one region per workgroup in index order.
-// Workgroup b streams one contiguous chunk of per_v float4 (whole rows of NT
-// float4; workgroup 0 also takes the scalar head, the last non-empty chunk
-// the scalar tail), so the regions in workgroup order are in index order.
-// Inside a row, a candidate's place is the count of candidates before it:
-// in earlier waves (wave totals in LDS, one barrier per row), in earlier
-// lanes of its wave (DPP scan) and earlier in its own float4.
+// acc = residual + grad written back to residual and the first-level
+// histogram of each workgroup, as k_acc_pass does (rows of NT float4 dealt
+// round-robin, two in flight), and the candidates -- every entry of the bins
+// >= the guessed bin -- copied into one region per workgroup, in no
+// particular order: a wave reserves room for a row's candidates with one LDS
+// atomic and places them by a DPP scan over its lanes, so waves never wait
+// for each other.  k_general ranks them by (key desc, index asc) itself.
 struct GuidedArgs {
   const float* grad;
   float* residual;
   int64_t n;
-  int64_t head;   // scalar entries before the 16-byte aligned part
-  int64_t nv;     // float4 vectors in the aligned part
-  int64_t per_v;  // float4 vectors per workgroup chunk, a multiple of the workgroup size
+  int64_t head;  // scalar entries before the 16-byte aligned part
+  int64_t nv;    // float4 vectors in the aligned part
   u32* zero_ptr;
   int zero_words;
   u32* err;
-  u32* hist_rows;  // [gridDim.x][2048]
-  const StepCtl* ctl;  // guide_bin (read), guide_ovf (set on overflow)
-  u32* guide_ovf;
-  u32* guide_cnt;  // [gridDim.x] candidates found (a count above cap means the region overflowed)
-  u64* cand;       // workgroup b's region: cand + b * cap
+  u32* hist_rows;      // [gridDim.x][2048]
+  const StepCtl* ctl;  // guide_bin
+  u32* guide_ovf;      // set when a region overflowed
+  u32* guide_cnt;      // [gridDim.x] candidates each workgroup found (above cap: its region overflowed)
+  u64* cand;           // workgroup b's region: cand + b * cap
   u32 cap;
 };
 
 __global__ __launch_bounds__(kAccThreads) void k_acc_guided(GuidedArgs a) {
-  constexpr int NT = kAccThreads, NW = NT / kWave;
+  constexpr int NT = kAccThreads;
   __shared__ u32 s_h[2048];
-  __shared__ u32 s_wc[2][NW];
-  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  __shared__ u32 s_cnt;
+  const int tid = threadIdx.x, lane = lane_id();
   for (int i = tid; i < 2048; i += NT) s_h[i] = 0;
+  if (tid == 0) s_cnt = 0;
   if (blockIdx.x == 0) {
     for (int i = tid; i < a.zero_words; i += NT) a.zero_ptr[i] = 0u;
     if (tid == 0) *a.err = 0u;
@@ -973,39 +1243,26 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_guided(GuidedArgs a) {
   const u32 gbin = a.ctl->guide_bin;
   const bool guide = gbin != kNoGuide;  // the same in every thread
   __syncthreads();
-  const int b = blockIdx.x;
-  const int64_t v0 = std::min<int64_t>(a.nv, (int64_t)b * a.per_v);
-  const int64_t v1 = std::min<int64_t>(a.nv, v0 + a.per_v);
-  u64* const reg = a.cand + (size_t)b * a.cap;
-  u32 cnt = 0;  // candidates of this workgroup so far (the same in every thread)
-  int par = 0;
-  // Ordered append of this thread's kept entries i0 + q (bit q of m4); every
-  // thread of the workgroup calls it.
+  u64* const reg = a.cand + (size_t)blockIdx.x * a.cap;
+  // this lane's kept entries i0 + j (bit j of m4) go to the region; every
+  // lane of the wave calls it
   auto place = [&](u32 m4, int64_t i0, const u32* bq) {
     const u32 c = (u32)__popc(m4);
+    if (ballot(c != 0u) == 0u) return;
     const u32 incl = wave_inclusive_sum(c);
-    if (lane == kWave - 1) s_wc[par][w] = incl;
-    __syncthreads();
-    u32 off = 0, tot = 0;
+    u32 base = 0;
+    if (lane == kWave - 1) base = atomicAdd(&s_cnt, incl);
+    u32 pos = __builtin_amdgcn_readlane(base, kWave - 1) + incl - c;
 #pragma unroll
-    for (int j = 0; j < NW; ++j) {
-      const u32 t = s_wc[par][j];
-      off += j < w ? t : 0u;
-      tot += t;
-    }
-    u32 pos = cnt + off + incl - c;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if ((m4 >> q) & 1u) {
-        if (pos < a.cap) reg[pos] = pack_pair(Pair{(int32_t)(i0 + q), bq[q]});
+    for (int j = 0; j < 4; ++j)
+      if ((m4 >> j) & 1u) {
+        if (pos < a.cap) reg[pos] = pack_pair(Pair{(int32_t)(i0 + j), bq[j]});
         ++pos;
       }
-    cnt += tot;
-    par ^= 1;
   };
   float* __restrict__ r = a.residual;
   const float* __restrict__ g = a.grad;
-  auto scalar = [&](int64_t i, bool in) {  // entry i if `in`; every thread calls it
+  auto scalar = [&](int64_t i, bool in) {  // entry i if `in`; every lane of the wave calls it
     u32 m = 0, bq[4] = {0u, 0u, 0u, 0u};
     if (in) {
       const float acc = r[i] + g[i];
@@ -1017,49 +1274,53 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_guided(GuidedArgs a) {
     }
     if (guide) place(m, i, bq);
   };
-  if (b == 0) scalar(tid, tid < a.head);
+  if (blockIdx.x == 0 && tid < kWave) scalar(tid, tid < a.head);
   const v4f* __restrict__ gv = (const v4f*)(g + a.head);
   v4f* __restrict__ rv = (v4f*)(r + a.head);
-  const int64_t nrow = (v1 - v0 + NT - 1) / NT;
+  const int64_t nrows = (a.nv + NT - 1) / NT, G = gridDim.x;
   auto load = [&](int64_t t, v4f& gg, v4f& rr) {
-    const int64_t i = v0 + t * NT + tid;
-    if (t < nrow && i < v1) {
+    const int64_t i = t * NT + tid;
+    if (t < nrows && i < a.nv) {
       gg = __builtin_nontemporal_load(gv + i);
       rr = __builtin_nontemporal_load(rv + i);
     }
   };
   auto process = [&](int64_t t, const v4f& gg, const v4f& rr) {
-    const int64_t i = v0 + t * NT + tid;
+    const int64_t i = t * NT + tid;
     u32 m4 = 0, bq[4] = {0u, 0u, 0u, 0u};
-    if (i < v1) {
+    if (i < a.nv) {
       const v4f acc = rr + gg;
       __builtin_nontemporal_store(acc, rv + i);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        bq[q] = __float_as_uint(acc[q]);
-        const u32 bin = key_of_bits(bq[q]) >> 20;
+      for (int e = 0; e < 4; ++e) {
+        bq[e] = __float_as_uint(acc[e]);
+        const u32 bin = key_of_bits(bq[e]) >> 20;
         atomicAdd(&s_h[bin], 1u);
-        m4 |= (guide && bin >= gbin ? 1u : 0u) << q;
+        m4 |= (guide && bin >= gbin ? 1u : 0u) << e;
       }
     }
     if (guide) place(m4, a.head + 4 * i, bq);
   };
   v4f ga, ra, gb, rb;
-  load(0, ga, ra);
-  load(1, gb, rb);
-  for (int64_t t = 0; t < nrow; t += 2) {
+  int64_t t = blockIdx.x;
+  load(t, ga, ra);
+  load(t + G, gb, rb);
+  for (; t < nrows; t += 2 * G) {
     process(t, ga, ra);
-    load(t + 2, ga, ra);
-    if (t + 1 >= nrow) break;
-    process(t + 1, gb, rb);
-    load(t + 3, gb, rb);
+    load(t + 2 * G, ga, ra);
+    if (t + G >= nrows) break;
+    process(t + G, gb, rb);
+    load(t + 3 * G, gb, rb);
   }
-  const int64_t tail0 = a.head + 4 * a.nv;
-  if (v0 < v1 && v1 == a.nv) scalar(tail0 + tid, tail0 + tid < a.n);
+  if (blockIdx.x == gridDim.x - 1 && tid < kWave) {
+    const int64_t i = a.head + 4 * a.nv + tid;
+    scalar(i, i < a.n);
+  }
   __syncthreads();
-  for (int i = tid; i < 2048; i += NT) a.hist_rows[(size_t)b * 2048 + i] = s_h[i];
+  for (int i = tid; i < 2048; i += NT) a.hist_rows[(size_t)blockIdx.x * 2048 + i] = s_h[i];
   if (tid == 0) {
-    a.guide_cnt[b] = cnt;
+    const u32 cnt = s_cnt;
+    a.guide_cnt[blockIdx.x] = cnt;
     if (cnt > a.cap) atomicOr(a.guide_ovf, 1u);
   }
 }
@@ -2288,15 +2549,15 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
     // workgroup of k_general, in index order.
     const bool guided = vec && k > 0 && path != 1 && n >= kGuideMinN && G1 == G2;
     if (guided) {
-      const int64_t want = (int64_t)std::ceil(2048.0 * (double)n / (double)k);  // ~2048 expected above the k-th key
-      int64_t chunks = (want + kSampleChunk - 1) / kSampleChunk;
-      chunks = std::max<int64_t>(1, std::min<int64_t>({chunks, kGuessMaxChunks, n / (4 * kSampleChunk)}));
+      const int64_t want = (int64_t)std::ceil(1024.0 * (double)n / (double)k);  // ~1024 expected above the k-th key
+      int64_t chunks = (want + kGuessChunk - 1) / kGuessChunk;
+      chunks = std::max<int64_t>(1, std::min<int64_t>({chunks, kGuessMaxChunks, nv / kGuessChunk}));  // <= 1/4 of it
       GuessArgs q{};
-      q.grad = grad;
-      q.residual = residual;
+      q.grad = (const v4f*)(grad + head);
+      q.residual = (const v4f*)(residual + head);
       q.chunks = chunks;
-      q.stride = n / chunks;
-      const double f = (double)(chunks * kSampleChunk) / (double)n;
+      q.stride = nv / chunks;
+      const double f = (double)(chunks * kGuessChunk) / (double)n;
       const double c = (double)k * f;
       q.c_req = path == 7 ? 1u : (u32)std::min(4.0e9, std::ceil(c + 6.0 * std::sqrt(c) + 8.0));
       const double room = (double)G1 * (kGenThreads / kWave) * L.cand_cap;
@@ -2311,8 +2572,6 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
       g.n = n;
       g.head = head;
       g.nv = nv;
-      g.per_v = (nv + G1 - 1) / G1;
-      g.per_v = (g.per_v + kAccThreads - 1) / kAccThreads * kAccThreads;
       g.zero_ptr = aa.zero_ptr;
       g.zero_words = aa.zero_words;
       g.err = aa.err;
@@ -2328,6 +2587,9 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
       ga.guide_ovf = &ctl->guide_ovf;
       ga.guide_cnt = g.guide_cnt;
       ga.guide_stats = &ctl->guided_used;
+      ga.bkt_cnt = (u32*)(ws + L.bkt_cnt);
+      ga.bkt_cur = (u32*)(ws + L.bkt_cur);
+      ga.bkt_buf = (u64*)(ws + L.bkt_buf);
     } else if (vec) {
       hipLaunchKernelGGL(k_acc_pass<true>, dim3(G1), dim3(kAccThreads), 0, stream, aa);
     } else {

@@ -84,6 +84,28 @@ def test_stash_overflow_rescan(tgs_gpu):
         assert_thr_equal(gpu_thr(tgs_gpu, grad, res, 0.0, cap), oracle_thr(grad, res, 0.0, cap), "cap=%d" % cap)
 
 
+@pytest.mark.parametrize("layout", ["dense", "clustered"])
+def test_stash_overflow_positive_lambda(tgs_gpu, layout):
+    """lambda > 0 with more qualifying entries than a stash holds: every
+    workgroup (dense: 38% of N(0,1) has |x| >= 0.5) or only those over one
+    index range (clustered) overflow.  The pass has already set the stashed
+    entries' residual to +0, so the rescan must skip them and number the
+    rest from the stash's end, and stashed entries past the capacity must get
+    acc back."""
+    rng = np.random.default_rng(4)
+    n = 2_000_003
+    grad = rng.standard_normal(n).astype(np.float32)
+    res = rng.standard_normal(n).astype(np.float32)
+    lam = 0.5 if layout == "dense" else 4.0
+    if layout == "clustered":
+        grad[700_000:760_000] = rng.uniform(5.0, 6.0, 60_000).astype(np.float32)
+    exp_all = oracle_thr(grad, res, lam, n)
+    c = exp_all[2]
+    for cap in (n, c, c - 1, c // 3, 7, 0):
+        assert_thr_equal(gpu_thr(tgs_gpu, grad, res, lam, cap), oracle_thr(grad, res, lam, cap),
+                         "%s cap=%d" % (layout, cap))
+
+
 @pytest.mark.parametrize("off_g,off_r", [(1, 1), (3, 3), (0, 2)])
 def test_misaligned(tgs_gpu, off_g, off_r):
     rng = np.random.default_rng(10 + off_g + off_r)

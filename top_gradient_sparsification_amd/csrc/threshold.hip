@@ -6,17 +6,19 @@
 // lets through, run with error feedback.
 //
 // Two launches, no global atomics:
-//   k_thr_pass  each workgroup streams its contiguous chunk once: acc =
-//               residual + grad, residual <- acc (non-temporal), qualifying
-//               entries (key(acc) >= key(lambda)) are counted and the first
+//   k_thr_pass  each workgroup streams its contiguous chunk once (two tiles
+//               in flight): acc = residual + grad; qualifying entries
+//               (key(acc) >= key(lambda)) are counted and the first
 //               `stash_cap` of them are kept, in index order, in the
-//               workgroup's stash; the count goes to cnt[wg].
+//               workgroup's stash; residual <- +0 for those, acc for every
+//               other entry (non-temporal); the count goes to cnt[wg].
 //   k_thr_emit  each workgroup adds up the counts of the workgroups before it
-//               (its output offset), copies its stash to the output while the
-//               position is below `capacity` and zeroes those residual entries.
-//               A workgroup whose stash overflowed rescans its chunk of acc
-//               (now in residual) instead.  The last workgroup writes the
-//               total count.
+//               (its output offset) and copies its stash to the output while
+//               the position is below `capacity`; stashed entries past it get
+//               acc back in the residual.  A workgroup whose stash overflowed
+//               and whose later entries are still below `capacity` rescans
+//               its chunk of acc (in residual) for them.  The last workgroup
+//               writes the total count.
 // The output is in ascending index order: chunks are contiguous and in
 // workgroup order, and inside a chunk entries are ranked by (tile, wave, lane,
 // component), which is index order.
@@ -155,36 +157,138 @@ __device__ int64_t ordered_walk(const ThrArgs& a, Load load, Put put, u32 (*s_wt
   return running;
 }
 
+// Ranks of one tile's qualifying entries (bit c of qmask: component c of
+// this thread qualifies), in index order: returns the rank of this thread's
+// first one and advances `running` past the tile.  Every thread calls it.
+__device__ __forceinline__ u32 tile_rank(u32 qmask, u32& running, u32 (*s_wt)[kThrWaves], int& par) {
+  const int w = threadIdx.x / kWave;
+  u32 below = 0, wtot = 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const u64 m = ballot((qmask >> c) & 1u);
+    below += lanes_below(m);
+    wtot += (u32)__popcll(m);
+  }
+  if (lane_id() == 0) s_wt[par][w] = wtot;
+  __syncthreads();
+  u32 woff = 0, ttot = 0;
+#pragma unroll
+  for (int ww = 0; ww < kThrWaves; ++ww) {
+    const u32 v = s_wt[par][ww];
+    if (ww < w) woff += v;
+    ttot += v;
+  }
+  const u32 r0 = running + woff + below;
+  running += ttot;
+  par ^= 1;
+  return r0;
+}
+
+// The pass writes +0 to the residual of every qualifying entry that goes to
+// the stash (rank < stash_cap), acc everywhere else: in the usual case
+// (count <= capacity, no overflow) every stashed entry is emitted and the
+// emit pass only copies.  Entries the capacity turns away get acc back.
 __global__ __launch_bounds__(kThrThreads) void k_thr_pass(ThrArgs a) {
   __shared__ u32 s_wt[2][kThrWaves];
   const float* __restrict__ g = a.grad;
   float* __restrict__ r = a.residual;
-  const v4f* __restrict__ gv = (const v4f*)(g + a.head);
-  v4f* __restrict__ rv = (v4f*)(r + a.head);
   Pair* stash = a.stash + (int64_t)blockIdx.x * a.stash_cap;
   const int64_t cap = a.stash_cap;
-  auto load = [&](int64_t i, const int64_t* idx, u32* bits, int nval) {
-    if (i >= 0 && a.vec) {
-      v4f x = __builtin_nontemporal_load(rv + i) + __builtin_nontemporal_load(gv + i);
-      __builtin_nontemporal_store(x, rv + i);
-      bits[0] = __float_as_uint(x.x);
-      bits[1] = __float_as_uint(x.y);
-      bits[2] = __float_as_uint(x.z);
-      bits[3] = __float_as_uint(x.w);
-    } else {
+  const int tid = threadIdx.x;
+  if (!a.vec) {
+    auto load = [&](int64_t, const int64_t* idx, u32* bits, int nval) {
       for (int c = 0; c < nval; ++c) {
         float x = r[idx[c]] + g[idx[c]];
         r[idx[c]] = x;
         bits[c] = __float_as_uint(x);
       }
+    };
+    auto put = [&](int64_t rank, int64_t idx, u32 bits) {
+      if (rank < cap) {
+        stash[rank] = Pair{(int32_t)idx, bits};
+        r[idx] = 0.0f;  // after this thread's own acc store to it
+      }
+    };
+    const int64_t total = ordered_walk(a, load, put, s_wt);
+    if (tid == 0) {
+      a.cnt[blockIdx.x] = (u32)total;
+      if (blockIdx.x == 0) *a.err = 0u;
+    }
+    return;
+  }
+  // vector mode: the partition of ordered_walk (which the emit pass's rescan
+  // uses): head tile (workgroup 0), main tiles of one float4 per thread with
+  // two tiles in flight, tail tile (last workgroup)
+  const int G = gridDim.x;
+  const int64_t per = (a.nv + G - 1) / G;
+  const int64_t ub = std::min<int64_t>(a.nv, (int64_t)blockIdx.x * per);
+  const int64_t ue = std::min<int64_t>(a.nv, ub + per);
+  const int64_t tail0 = a.head + 4 * a.nv;
+  u32 running = 0;
+  int par = 0;
+  auto scalar_tile = [&](int64_t i0, int64_t cnt) {  // entries i0 + tid for tid < cnt (< 4)
+    const bool in = tid < cnt;
+    const int64_t i = i0 + tid;
+    float x = 0.0f;
+    u32 qm = 0;
+    if (in) {
+      x = r[i] + g[i];
+      qm = key_of(x) >= a.klam ? 1u : 0u;
+    }
+    const u32 rk = tile_rank(qm, running, s_wt, par);
+    if (in) {
+      if (qm && rk < cap) {
+        stash[rk] = Pair{(int32_t)i, __float_as_uint(x)};
+        x = 0.0f;
+      }
+      r[i] = x;
     }
   };
-  auto put = [&](int64_t rank, int64_t idx, u32 bits) {
-    if (rank < cap) stash[rank] = Pair{(int32_t)idx, bits};
+  if (blockIdx.x == 0 && a.head > 0) scalar_tile(0, a.head);
+  const v4f* __restrict__ gv = (const v4f*)(g + a.head);
+  v4f* __restrict__ rv = (v4f*)(r + a.head);
+  const int64_t ntiles = (ue - ub + kThrThreads - 1) / kThrThreads;
+  auto load = [&](int64_t t, v4f& gg, v4f& rr) {
+    const int64_t i = ub + t * kThrThreads + tid;
+    if (t < ntiles && i < ue) {
+      gg = __builtin_nontemporal_load(gv + i);
+      rr = __builtin_nontemporal_load(rv + i);
+    }
   };
-  int64_t total = ordered_walk(a, load, put, s_wt);
-  if (threadIdx.x == 0) {
-    a.cnt[blockIdx.x] = (u32)total;
+  auto step = [&](int64_t t, const v4f& gg, const v4f& rr) {
+    const int64_t i = ub + t * kThrThreads + tid;
+    const bool in = i < ue;
+    v4f acc = rr + gg;
+    u32 qm = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qm |= (in && key_of(acc[c]) >= a.klam ? 1u : 0u) << c;
+    u32 rk = tile_rank(qm, running, s_wt, par);
+    if (in) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if ((qm >> c) & 1u) {
+          if (rk < cap) {
+            stash[rk] = Pair{(int32_t)(a.head + 4 * i + c), __float_as_uint(acc[c])};
+            acc[c] = 0.0f;
+          }
+          ++rk;
+        }
+      __builtin_nontemporal_store(acc, rv + i);
+    }
+  };
+  v4f ga, ra, gb, rb;
+  load(0, ga, ra);
+  load(1, gb, rb);
+  for (int64_t t = 0; t < ntiles; t += 2) {
+    step(t, ga, ra);
+    load(t + 2, ga, ra);
+    if (t + 1 >= ntiles) break;
+    step(t + 1, gb, rb);
+    load(t + 3, gb, rb);
+  }
+  if (blockIdx.x == G - 1 && tail0 < a.n) scalar_tile(tail0, a.n - tail0);
+  if (tid == 0) {
+    a.cnt[blockIdx.x] = running;
     if (blockIdx.x == 0) *a.err = 0u;
   }
 }
@@ -201,19 +305,28 @@ __global__ __launch_bounds__(kThrThreads) void k_thr_emit(ThrArgs a) {
   const int64_t prefix = prefix_u;
   const int64_t mine = a.cnt[b];
   if (b == gridDim.x - 1 && tid == 0) *a.d_count = prefix + mine;
-  if (prefix >= a.capacity || mine == 0) return;
-  const int64_t take = std::min<int64_t>(mine, a.capacity - prefix);
-  if (mine <= a.stash_cap) {
-    const Pair* stash = a.stash + (int64_t)b * a.stash_cap;
-    for (int64_t j = tid; j < take; j += kThrThreads) {
-      Pair e = stash[j];
+  if (mine == 0) return;
+  const int64_t take = std::max<int64_t>(0, std::min<int64_t>(mine, a.capacity - prefix));
+  // stashed entries (ranks below stash_cap; their residual is +0): emitted
+  // below `take`, given acc back above it
+  const int64_t stashed = std::min<int64_t>(mine, a.stash_cap);
+  const Pair* stash = a.stash + (int64_t)b * a.stash_cap;
+  float* rw = a.residual;
+  for (int64_t j = tid; j < stashed; j += kThrThreads) {
+    const Pair e = stash[j];
+    if (j < take) {
       a.out_idx[prefix + j] = e.idx;
       a.out_val[prefix + j] = __uint_as_float(e.bits);
-      if (e.idx >= 0 && (int64_t)e.idx < a.n) a.residual[e.idx] = 0.0f;
+    } else {
+      rw[e.idx] = __uint_as_float(e.bits);
     }
-    return;
   }
-  // the stash overflowed: rescan acc (held in residual) in index order
+  if (take <= a.stash_cap) return;
+  // the stash overflowed and entries past it are to be emitted: rescan acc
+  // (held in residual) in index order.  Stashed entries now hold +0, which
+  // qualifies only when lambda is 0: then every entry qualifies and the
+  // rescan's ranks are the pass's; otherwise the rescan sees only the
+  // entries past the stash, so their ranks start at stash_cap.
   const float* r = a.residual;
   const v4f* rv = (const v4f*)(r + a.head);
   auto load = [&](int64_t i, const int64_t* idx, u32* bits, int nval) {
@@ -227,9 +340,10 @@ __global__ __launch_bounds__(kThrThreads) void k_thr_emit(ThrArgs a) {
       for (int c = 0; c < nval; ++c) bits[c] = __float_as_uint(r[idx[c]]);
     }
   };
-  float* rw = a.residual;
-  auto put = [&](int64_t rank, int64_t idx, u32 bits) {
-    if (rank < take) {
+  const int64_t shift = a.klam == 0u ? 0 : a.stash_cap;
+  auto put = [&](int64_t rank0, int64_t idx, u32 bits) {
+    const int64_t rank = rank0 + shift;
+    if (rank >= a.stash_cap && rank < take) {
       a.out_idx[prefix + rank] = (int32_t)idx;
       a.out_val[prefix + rank] = __uint_as_float(bits);
       rw[idx] = 0.0f;

@@ -423,3 +423,32 @@ def test_guided_is_the_default_for_large_k(tgs_gpu):
         ei, ev = oracle.topk_ef_step(grad, r_cpu, k)
         assert_topk_equal((host(idx), host(val), host(r_gpu)), (ei, ev, r_cpu), "step %d" % step)
     assert _guided(ws) == (3, 0)
+
+
+@pytest.mark.parametrize("dist", ["normal", "ties", "special", "mixture"])
+def test_small_vector_kernel(tgs_gpu, dist):
+    """n <= 2^18 and k <= 256 run in one launch: each workgroup of 8192
+    entries selects its own top k, the last to finish selects among those
+    lists.  Sizes at the workgroup boundaries, k at both ends, ties across
+    workgroups (the lower index wins) and unaligned slices."""
+    rng = np.random.default_rng(59 + len(dist))
+    for n in (1, 2, 8191, 8192, 8193, 100_003, 262_144):
+        grad, res = make(dist, n, rng)
+        for k in (1, 7, 255, 256):
+            if k > n:
+                continue
+            assert_topk_equal(gpu_topk(tgs_gpu, grad, res, k), oracle_topk(grad, res, k), "n=%d k=%d %s" % (n, k, dist))
+    # every entry equal: the k lowest indices, all from workgroup 0
+    grad = np.full(50_000, 0.75, np.float32)
+    res = np.zeros_like(grad)
+    assert_topk_equal(gpu_topk(tgs_gpu, grad, res, 256), oracle_topk(grad, res, 256), "all equal")
+    # unaligned slice
+    n, off = 30_001, 3
+    grad, res = make(dist, n, rng)
+    gb = torch.zeros(n + 8, dtype=torch.float32, device="cuda")
+    rb = torch.zeros(n + 8, dtype=torch.float32, device="cuda")
+    gb[1:1 + n] = gpu(grad)
+    rb[off:off + n] = gpu(res)
+    got = topk_dev(tgs_gpu, gb[1:1 + n], rb[off:off + n], 100)
+    assert_topk_equal(got, oracle_topk(grad, res, 100), "unaligned")
+    assert np.all(host(rb[:off]) == 0) and np.all(host(rb[off + n:]) == 0)

@@ -94,6 +94,10 @@ constexpr int kMaxGenWG = 256;  // workgroups of either general-path launch
 constexpr int kLsdDigits = 512;  // digits of an LSD pass at most (9 bits)
 
 // reasons a plan did not hold (StepCtl::why)
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallPer = 8192;            // entries per workgroup of k_small (8 per thread)
+constexpr int64_t kSmallMaxN = 1 << 18;    // k_small: n <= this (at most 32 workgroups) ...
+constexpr int64_t kSmallMaxK = 256;        // ... and k <= this
 constexpr u32 kNoGuide = 0xFFFFFFFFu;  // guided accumulate pass: keep no candidates
 constexpr u32 kBktMax = 8192;     // buckets of the guided ranking at most
 constexpr u32 kBktCap = 1024;     // entries one bucket may hold
@@ -154,7 +158,8 @@ struct StepCtl {
   u32 rescans;    // workgroup shares re-read because their list was incomplete (never reset)
   u32 guided_used;    // guided general-path calls that selected from the copied candidates (never reset)
   u32 guided_missed;  // guided calls whose guess or regions did not hold: acc read again (never reset)
-  u32 pad1[56];
+  u32 small_done;     // k_small arrivals; its last workgroup leaves it zero
+  u32 pad1[55];
   StepSet set[2];
   Plan plan;
   // guided accumulate pass (standalone general path): k_guess adds its sample
@@ -179,7 +184,7 @@ struct GenState {
 
 struct TopkLayout {
   size_t ctl, gstate, gcnt, lsd_cnt, lsd_pre, lsd_tot, bufA, bufB, cand, hist_rows, guide_cnt, bkt_cnt, bkt_cur, bkt_buf,
-      pub, rcnt, slots, ovf, total;
+      small, pub, rcnt, slots, ovf, total;
   u32 cand_cap;
 };
 
@@ -218,6 +223,7 @@ static TopkLayout topk_layout(int64_t n, int64_t k) {
   L.bkt_cnt = take(sizeof(u32) * kBktMax);
   L.bkt_cur = take(sizeof(u32) * kBktMax);
   L.bkt_buf = take(sizeof(u64) * (size_t)kMaxGenWG * (kGenThreads / kWave) * L.cand_cap);
+  L.small = take(sizeof(u64) * (size_t)(kSmallMaxN / kSmallPer) * kSmallMaxK);
   L.pub = take(sizeof(u32) * ((size_t)kPlanCap + kMaxStepBlocks));
   L.rcnt = take(sizeof(u32) * (size_t)kMaxStepBlocks * (kMaxBuckets / 2));
   L.slots = take(sizeof(Pair) * (size_t)kMaxBuckets * kSlotTotal);
@@ -1326,6 +1332,210 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_guided(GuidedArgs a) {
 }
 
 __global__ __launch_bounds__(kGenThreads) void k_general(GenArgs a) { general_path<kGenThreads, 16, true, 9, true>(a); }
+
+// ------------------------------------------------------------- k_small ----
+// Small vectors (n <= 2^18, k <= 256) in one launch with no grid barrier:
+// workgroup b takes entries [8192 b, 8192 (b+1)): acc = residual + grad,
+// written back at device scope, keys kept in LDS; it selects its own top
+// min(k, len) by a three-level radix select in LDS and writes them, in index
+// order, to its candidate list.  The last workgroup to arrive selects the
+// top k of the lists (in workgroup order, so in index order: ties go to the
+// lower index as everywhere), sorts them by (key desc, index asc) and emits
+// them.  Any entry of the global top k is in its own workgroup's top k.
+struct SmallArgs {
+  const float* grad;
+  float* residual;
+  int64_t n, k;
+  int32_t* out_idx;
+  float* out_val;
+  StepCtl* ctl;
+  u64* cand;  // [gridDim.x][kSmallMaxK]
+};
+
+// Radix select in LDS of the need-th largest key among `len` entries, whose
+// key is key_at(i) (i < len, 8 per thread at i = tid + j NT).  Returns the
+// selection rule: every key >= t_lo, plus the first r keys equal to t_eq.
+template <int NT, class KeyAt>
+__device__ __forceinline__ void lds_select(KeyAt key_at, u32 len, u32 need, u32* s_hist, u32* s_scan, u32* s_found,
+                                           u32& t_lo, u32& t_eq, u32& r) {
+  const int tid = threadIdx.x;
+  const int shifts[3] = {20, 9, 0};
+  const int widths[3] = {11, 11, 9};
+  u32 prefix = 0;
+  t_lo = 0;
+  t_eq = 0;
+  r = 0;
+  for (int L = 0; L < 3; ++L) {
+    const int sh = shifts[L], wd = widths[L];
+    const int nbins = 1 << wd;
+    for (int i = tid; i < 2048; i += NT) s_hist[i] = 0;
+    __syncthreads();
+    for (u32 i = tid; i < len; i += NT) {
+      const u32 key = key_at(i);
+      if ((key >> (sh + wd)) == prefix) atomicAdd(&s_hist[(key >> sh) & (u32)(nbins - 1)], 1u);
+    }
+    __syncthreads();
+    // thread t owns bins [nbins - cpt (t+1), nbins - cpt t), from the top
+    const int cpt = nbins / NT > 0 ? nbins / NT : 1;
+    const int top = nbins - cpt * tid;
+    u32 own = 0;
+    if (top > 0)
+      for (int d = top - 1; d >= std::max(0, top - cpt); --d) own += s_hist[d];
+    u32 tot;
+    const u32 above = block_exclusive_sum<NT>(own, s_scan, tot);
+    if (top > 0 && above < need && above + own >= need) {
+      u32 run = above;
+      for (int d = top - 1; d >= std::max(0, top - cpt); --d) {
+        const u32 h = s_hist[d];
+        if (run + h >= need) {
+          s_found[0] = (u32)d;
+          s_found[1] = run;
+          s_found[2] = h;
+          break;
+        }
+        run += h;
+      }
+    }
+    __syncthreads();
+    const u32 d = s_found[0];
+    need -= s_found[1];
+    const u32 h = s_found[2];
+    prefix = (prefix << wd) | d;
+    __syncthreads();  // s_found is rewritten by the next level
+    if (need == h) {  // the whole digit range is taken
+      t_lo = prefix << sh;
+      return;
+    }
+    if (L == 2) {
+      t_lo = prefix + 1;
+      t_eq = prefix;
+      r = need;
+    }
+  }
+}
+
+// Ordered compaction: entries i < len (pair_at(i), key of its bits) in index
+// order i = j NT + tid; the selected ones (key >= t_lo, or among the first r
+// equal to t_eq) go to place(pos, pair) with pos their rank among them.
+template <int NT, int ROWS, class PairAt, class Place>
+__device__ __forceinline__ void lds_compact(PairAt pair_at, u32 len, u32 t_lo, u32 t_eq, u32 r, u32 (*s_wc)[NT / kWave][2],
+                                            Place place) {
+  constexpr int NW = NT / kWave;
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  u32 gt_seen = 0, eq_seen = 0;
+  for (int j = 0; j < ROWS; ++j) {
+    const u32 i = (u32)(j * NT + tid);
+    const bool in = i < len;
+    const u64 pv = in ? pair_at(i) : 0ull;
+    const u32 key = key_of_bits((u32)(pv >> 32));
+    const bool g = in && key >= t_lo, e = in && r > 0 && key == t_eq;
+    const u64 bg = ballot(g), be = ballot(e);
+    const int par = j & 1;
+    if (lane == 0) {
+      s_wc[par][w][0] = (u32)__popcll(bg);
+      s_wc[par][w][1] = (u32)__popcll(be);
+    }
+    __syncthreads();
+    u32 og = 0, oe = 0, tg = 0, te = 0;
+#pragma unroll
+    for (int q = 0; q < NW; ++q) {
+      const u32 cg = s_wc[par][q][0], ce = s_wc[par][q][1];
+      og += q < w ? cg : 0u;
+      oe += q < w ? ce : 0u;
+      tg += cg;
+      te += ce;
+    }
+    const u32 gb = gt_seen + og + lanes_below(bg), eb = eq_seen + oe + lanes_below(be);
+    if (g || (e && eb < r)) place(gb + std::min(eb, r), pv);
+    gt_seen += tg;
+    eq_seen += te;
+  }
+}
+
+__global__ __launch_bounds__(kSmallThreads) void k_small(SmallArgs a) {
+  constexpr int NT = kSmallThreads, NW = NT / kWave, EPT = kSmallPer / NT;
+  constexpr int MAXC = (int)(kSmallMaxN / kSmallPer * kSmallMaxK);  // candidates at most
+  __shared__ u32 s_bits[kSmallPer];
+  __shared__ u64 s_cand[MAXC];
+  __shared__ u64 s_sel[kSmallMaxK];
+  __shared__ u32 s_hist[2048];
+  __shared__ u32 s_scan[NW + 1];
+  __shared__ u32 s_found[4];
+  __shared__ u32 s_wc[2][NW][2];
+  __shared__ u32 s_last;
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x, G = gridDim.x;
+  const int64_t cb = (int64_t)b * kSmallPer;
+  const u32 len = (u32)std::min<int64_t>(kSmallPer, a.n - cb);
+  const u32 kk = (u32)std::min<int64_t>(a.k, len);
+  if (b == 0 && tid == 0) a.ctl->err = 0u;
+  {
+    float gq[EPT], rq[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const u32 i = (u32)(j * NT + tid);
+      const int64_t e = cb + (i < len ? i : 0u);
+      gq[j] = a.grad[e];
+      rq[j] = a.residual[e];
+    }
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const u32 i = (u32)(j * NT + tid);
+      if (i < len) {
+        const float acc = rq[j] + gq[j];
+        st_agent_f32(a.residual + cb + i, acc);
+        s_bits[i] = __float_as_uint(acc);
+      }
+    }
+  }
+  __syncthreads();
+  u32 t_lo, t_eq, r;
+  lds_select<NT>([&](u32 i) { return key_of_bits(s_bits[i]); }, len, kk, s_hist, s_scan, s_found, t_lo, t_eq, r);
+  u64* const mine = a.cand + (size_t)b * kSmallMaxK;
+  lds_compact<NT, EPT>([&](u32 i) { return pack_pair(Pair{(int32_t)(cb + i), s_bits[i]}); }, len, t_lo, t_eq, r, s_wc,
+                       [&](u32 pos, u64 pv) { st_agent64(mine + pos, pv); });
+  wait_all_memory();  // acc and the list have completed at device scope
+  __syncthreads();
+  if (tid == 0) s_last = add_agent_acqrel(&a.ctl->small_done, 1u) == (u32)G - 1u ? 1u : 0u;
+  __syncthreads();
+  if (!s_last) return;
+  if (tid < kWave) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  __syncthreads();
+  // every list but the last holds k entries
+  const u32 k = (u32)a.k;
+  const u32 M = (u32)(G - 1) * k + (u32)std::min<int64_t>(a.k, a.n - (int64_t)(G - 1) * kSmallPer);
+  for (u32 q = tid; q < M; q += NT) s_cand[q] = ld_agent64(a.cand + (size_t)(q / k) * kSmallMaxK + q % k);
+  __syncthreads();
+  lds_select<NT>([&](u32 i) { return key_of_bits((u32)(s_cand[i] >> 32)); }, M, k, s_hist, s_scan, s_found, t_lo, t_eq,
+                 r);
+  for (int i = tid; i < kSmallMaxK; i += NT) s_sel[i] = pack_pair(pair_sentinel());
+  __syncthreads();
+  lds_compact<NT, MAXC / NT>([&](u32 i) { return s_cand[i]; }, M, t_lo, t_eq, r, s_wc,
+                             [&](u32 pos, u64 pv) { s_sel[pos] = pv; });
+  __syncthreads();
+  // bitonic sort of the (at most 256) selected by (key desc, index asc);
+  // the padding sorts last
+  for (u32 k2 = 2; k2 <= (u32)kSmallMaxK; k2 <<= 1)
+    for (u32 jj = k2 >> 1; jj > 0; jj >>= 1) {
+      if (tid < kSmallMaxK / 2) {
+        const u32 t2 = (u32)tid, i = 2 * t2 - (t2 & (jj - 1)), l = i + jj;
+        const u64 pi = s_sel[i], pl = s_sel[l];
+        const bool up = (i & k2) == 0;
+        if ((pair_rank(unpack_pair(pi)) > pair_rank(unpack_pair(pl))) == up) {
+          s_sel[i] = pl;
+          s_sel[l] = pi;
+        }
+      }
+      __syncthreads();
+    }
+  for (u32 i = tid; i < k; i += NT) {
+    const Pair e = unpack_pair(s_sel[i]);
+    a.out_idx[i] = e.idx;
+    a.out_val[i] = __uint_as_float(e.bits);
+    st_agent_f32(a.residual + e.idx, 0.0f);
+  }
+  if (tid == 0) st_agent(&a.ctl->small_done, 0u);
+}
 
 // ------------------------------------------------------------- k_step ----
 struct StepArgs {
@@ -2472,6 +2682,26 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
   ga.bar.gen = &gs->bar_gen[0][0];
   ga.bar.abort = &gs->bar_abort;
   ga.bar.err = &ctl->err;
+
+  if (path != 1 && path < 7 && k >= 1 && k <= kSmallMaxK && n <= kSmallMaxN) {
+    SmallArgs m{};
+    m.grad = grad;
+    m.residual = residual;
+    m.n = n;
+    m.k = k;
+    m.out_idx = out_idx;
+    m.out_val = out_val;
+    m.ctl = ctl;
+    m.cand = (u64*)(ws + L.small);
+    hipEvent_t e0, e1;
+    take_profile_events(&e0, &e1);
+    if (e0) (void)hipEventRecord(e0, stream);
+    hipLaunchKernelGGL(k_small, dim3((unsigned)((n + kSmallPer - 1) / kSmallPer)), dim3(kSmallThreads), 0, stream, m);
+    if (e1) (void)hipEventRecord(e1, stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(TGS_EHIP, "topk_ef_step: launch failed: %s", hipGetErrorString(e));
+    return TGS_OK;
+  }
 
   StepArgs sa{};
   int G = 0;

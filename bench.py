@@ -36,7 +36,7 @@ kernel of it) against its algorithmic bytes:
     topk_n138M_0.1%                     138M VGG-16-sized mixture, whole vector,
                                         k = 138,000 (residual after 2 steps)
     topk_segments_n138M_0.1%            the same vector as 32 log-uniform
-                                        segments, one call per segment,
+                                        segments in one layer-wise call,
                                         k_s = floor(0.001 size_s)
     topk_n1.5e9_0.1%                    1.5e9 mixture (0.5% Laplace(0, 0.05)),
                                         k = 1,500,000 (residual after 2 steps)
@@ -107,12 +107,8 @@ def run_other(args):
         elif kind == "segments":
             sizes = workloads.segments_log_uniform(n)
             offs = np.concatenate([[0], np.cumsum(sizes)])
-            runs = [tgs.TopkStep(int(sz), workloads.k_for_density(int(sz), par), dev) for sz in sizes]
-
-            def one(g):
-                for j, run in enumerate(runs):
-                    a, b = int(offs[j]), int(offs[j + 1])
-                    run(g[a:b], resid[a:b])
+            seg = tgs.TopkSegments(offs, [workloads.k_for_density(int(sz), par) for sz in sizes], dev)
+            one = lambda g: seg(g, resid)
         else:
             run = tgs.TopkStep(n, workloads.k_for_density(n, par), dev)
             one = lambda g: run(g, resid)

@@ -15,6 +15,10 @@
  *   [HT]    same listing, entry "Rethinking gradient sparsification as total
  *           error minimization": hard-threshold sparsifier (k set by a constant
  *           threshold) with error feedback.
+ *   [LAYER] fugumt page for arXiv 2502.07634, related-paper entry "L-GreCo:
+ *           Layerwise-Adaptive Gradient Compression for Efficient and
+ *           Accurate Deep Learning": compression applied layer by layer, each
+ *           layer with its own degree.
  *   [GTOPK] nubint review "A Distributed Synchronous SGD Algorithm with Global
  *           Top-k Sparsification for Low Bandwidth Networks", ABSTRACT and
  *           Method: global top-k of the largest |values| over P workers by an
@@ -32,9 +36,10 @@
  *   - `workspace` is caller-owned device memory of at least the size the
  *     matching *_workspace_bytes() query returns.  One workspace serves one
  *     call at a time; calls that share a workspace must be ordered (same
- *     stream).  Its first 8 KB carry synchronisation counters from one call
- *     to the next (every call leaves them at zero): a new workspace must be
- *     zero-filled, and the caller must not write to it between calls.  Any
+ *     stream).  Its first 32 KB carry state from one call to the next
+ *     (synchronisation counters that every call leaves at zero, route
+ *     counters): a new workspace must be zero-filled, and the caller must
+ *     not write to it between calls.  Any
  *     of the three operations may use a workspace after any other.  The rest
  *     is scratch.
  *   - Magnitude order: key(x) = bits(x) & 0x7FFFFFFF as an unsigned integer.
@@ -85,6 +90,30 @@ size_t tgs_topk_workspace_bytes(int64_t n, int64_t k);
 tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64_t n, int64_t k,
                             int32_t* out_idx, float* out_val, void* workspace,
                             size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace tgs_topk_ef_step_segmented needs for this segment table
+   (HOST arrays, as below).  0 if the table is invalid. */
+size_t tgs_topk_segmented_workspace_bytes(int32_t nseg, const int64_t* offsets, const int64_t* ks);
+
+/*
+ * Layer-wise error-feedback top-k ([LAYER] with [EF], [CONV]): the vector
+ * grad/residual [offsets[nseg]] is cut into nseg segments (layers) and each
+ * gets the top-k step of tgs_topk_ef_step with its own k, in one call.
+ *   offsets   HOST int64 [nseg + 1]: segment s is [offsets[s], offsets[s+1]);
+ *             offsets[0] == 0, nondecreasing, offsets[nseg] <= 2^31 - 1.
+ *   ks        HOST int64 [nseg]: 0 <= ks[s] <= the segment's length.
+ *   out_idx / out_val  [sum of ks]: segment s's pairs start at
+ *             sum(ks[0..s)), in the order tgs_topk_ef_step gives them, with
+ *             indices relative to the segment's start.
+ * Segments of at most 2^18 entries with k <= 256 run together, up to 64 per
+ * launch of one kernel; every other segment takes its own step.  The
+ * results are those of one tgs_topk_ef_step call per segment.  Pointer and
+ * overlap rules as tgs_topk_ef_step, over the whole vector and sum(ks).
+ */
+tgs_status tgs_topk_ef_step_segmented(const float* grad, float* residual, int32_t nseg,
+                                      const int64_t* offsets, const int64_t* ks, int32_t* out_idx,
+                                      float* out_val, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
 
 /* Bytes of workspace tgs_threshold_ef_step needs for this n (0 if invalid). */
 size_t tgs_threshold_workspace_bytes(int64_t n);

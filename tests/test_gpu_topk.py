@@ -242,6 +242,19 @@ def test_vgg16_sized_segments(tgs_gpu):
         i, v, _ = topk_dev(tgs_gpu, g_d[s0:s0 + sz], r_d[s0:s0 + sz], k)
         outs.append((i, v))
     r_after = host(r_d)
+    # the same 32 segments in one layer-wise call, on fresh copies
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    ks_all = [workloads.k_for_density(int(sz), 0.001) for sz in sizes]
+    g2, r2 = gpu(grad), gpu(res)
+    ws2 = torch.zeros(tgs_gpu.topk_segmented_workspace_bytes(offsets, ks_all), dtype=torch.uint8, device="cuda")
+    si, sv = tgs_gpu.topk_ef_step_segmented(g2, r2, offsets, ks_all, ws=ws2)
+    tgs_gpu.check_device_error(ws2)
+    si, sv, sr = host(si), host(sv), host(r2)
+    del g2, r2, ws2
+    assert np.array_equal(bits(sr), bits(r_after)), "segmented residual"
+    koffs = np.concatenate([[0], np.cumsum(ks_all)])
+    for j, (gi, gv) in enumerate(outs):
+        assert np.array_equal(si[koffs[j]:koffs[j + 1]], gi) and np.array_equal(bits(sv[koffs[j]:koffs[j + 1]]), bits(gv))
     for (s0, sz), (gi, gv) in zip(zip(starts, sizes), outs):
         k = workloads.k_for_density(int(sz), 0.001)
         r = res[s0:s0 + sz].copy()
@@ -452,3 +465,59 @@ def test_small_vector_kernel(tgs_gpu, dist):
     got = topk_dev(tgs_gpu, gb[1:1 + n], rb[off:off + n], 100)
     assert_topk_equal(got, oracle_topk(grad, res, 100), "unaligned")
     assert np.all(host(rb[:off]) == 0) and np.all(host(rb[off + n:]) == 0)
+
+
+def _oracle_segments(grad, res, offsets, ks):
+    """Per-slice oracle steps: (concatenated idx, concatenated val, residual)."""
+    r = res.copy()
+    ii, vv = [], []
+    for s in range(len(ks)):
+        a, b = int(offsets[s]), int(offsets[s + 1])
+        rs = r[a:b].copy()
+        i, v = oracle.topk_ef_step(grad[a:b], rs, int(ks[s]))
+        r[a:b] = rs
+        ii.append(i)
+        vv.append(v)
+    return np.concatenate(ii).astype(np.int32), np.concatenate(vv).astype(np.float32), r
+
+
+def _segmented_dev(tgs_gpu, grad, res, offsets, ks):
+    g, r = gpu(grad), gpu(res)
+    ws = torch.zeros(tgs_gpu.topk_segmented_workspace_bytes(offsets, ks), dtype=torch.uint8, device="cuda")
+    idx, val = tgs_gpu.topk_ef_step_segmented(g, r, offsets, ks, ws=ws)
+    tgs_gpu.check_device_error(ws)
+    return host(idx), host(val), host(r)
+
+
+@pytest.mark.parametrize("dist", ["mixture", "ties", "special"])
+def test_segmented_step(tgs_gpu, dist):
+    """One layer-wise call: small segments (batched in one kernel launch,
+    k = 0 and k = length among them), segments just above the small limit,
+    fast-path and large-k segments, an empty segment; every segment's pairs
+    and residual as the oracle's step on that slice."""
+    rng = np.random.default_rng(61 + len(dist))
+    sizes = [1, 5, 1000, 8192, 8193, 0, 77, 100_003, 262_144, 262_145, 300_000, 600_000, 4_300_001, 3]
+    ks = [1, 0, 1, 256, 8, 0, 77, 100, 256, 262, 300, 600, 60_000, 3]
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    grad, res = make(dist, int(offsets[-1]), rng)
+    got = _segmented_dev(tgs_gpu, grad, res, offsets, ks)
+    assert_topk_equal(got, _oracle_segments(grad, res, offsets, ks), dist)
+
+
+def test_segmented_many_small_segments(tgs_gpu):
+    """More small segments than one launch takes (64): several launches of
+    the batched kernel, chained EF steps on one workspace."""
+    rng = np.random.default_rng(67)
+    sizes = rng.integers(1, 20_000, 150)
+    ks = np.minimum(sizes, rng.integers(0, 257, 150))
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    n = int(offsets[-1])
+    r_gpu = torch.zeros(n, dtype=torch.float32, device="cuda")
+    r_cpu = np.zeros(n, np.float32)
+    ws = torch.zeros(tgs_gpu.topk_segmented_workspace_bytes(offsets, ks), dtype=torch.uint8, device="cuda")
+    for step in range(2):
+        grad = rng.standard_normal(n).astype(np.float32)
+        idx, val = tgs_gpu.topk_ef_step_segmented(gpu(grad), r_gpu, offsets, ks, ws=ws)
+        tgs_gpu.check_device_error(ws)
+        ei, ev, r_cpu = _oracle_segments(grad, r_cpu, offsets, ks)
+        assert_topk_equal((host(idx), host(val), host(r_gpu)), (ei, ev, r_cpu), "step %d" % step)

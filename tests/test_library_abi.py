@@ -115,3 +115,32 @@ def test_product_path_has_no_oracle_or_cpu_fallback():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "liboracle" not in text, f
+
+
+def test_segmented_table_checks_before_any_launch(lib):
+    """The layer-wise step validates its host segment table (and the
+    workspace size) before it enqueues anything: fake device pointers are
+    never touched."""
+    import numpy as np
+    import top_gradient_sparsification_amd as tgs
+    assert tgs.topk_segmented_workspace_bytes([0, 10, 300_000, 300_100], [1, 300, 0]) > 0
+    assert tgs.topk_segmented_workspace_bytes([0], []) > 0
+    for offs, ks in (([0, 10, 5], [1, 1]),          # offsets decrease
+                     ([1, 10], [1]),                 # offsets[0] != 0
+                     ([0, 10], [11]),                # k above the segment length
+                     ([0, 10], [-1]),
+                     ([0, 2**31], [1])):             # beyond int32 indices
+        assert tgs.topk_segmented_workspace_bytes(offs, ks) == 0, (offs, ks)
+        o = np.asarray(offs, np.int64)
+        k = np.asarray(ks, np.int64)
+        st = lib.tgs_topk_ef_step_segmented(ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000), k.size,
+                                            o.ctypes.data, k.ctypes.data, ctypes.c_void_p(0x300000),
+                                            ctypes.c_void_p(0x400000), ctypes.c_void_p(0x500000), 1 << 30, None)
+        assert st == -1, (offs, ks)
+    o = np.asarray([0, 1000, 400_000], np.int64)
+    k = np.asarray([3, 400], np.int64)
+    need = tgs.topk_segmented_workspace_bytes(o, k)
+    st = lib.tgs_topk_ef_step_segmented(ctypes.c_void_p(0x10000000), ctypes.c_void_p(0x20000000), 2, o.ctypes.data,
+                                        k.ctypes.data, ctypes.c_void_p(0x30000000), ctypes.c_void_p(0x40000000),
+                                        ctypes.c_void_p(0x50000000), need - 1, None)
+    assert st == -2

@@ -25,6 +25,7 @@ import ctypes
 import os
 import threading
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -73,6 +74,10 @@ def _load():
         lib.tgs_topk_workspace_bytes.restype = sz
         lib.tgs_topk_ef_step.argtypes = [vp, vp, i64, i64, vp, vp, vp, sz, vp]
         lib.tgs_topk_ef_step.restype = i32
+        lib.tgs_topk_segmented_workspace_bytes.argtypes = [i32, vp, vp]
+        lib.tgs_topk_segmented_workspace_bytes.restype = sz
+        lib.tgs_topk_ef_step_segmented.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]
+        lib.tgs_topk_ef_step_segmented.restype = i32
         lib.tgs_threshold_workspace_bytes.argtypes = [i64]
         lib.tgs_threshold_workspace_bytes.restype = sz
         lib.tgs_threshold_ef_step.argtypes = [vp, vp, i64, ctypes.c_float, vp, vp, i64, vp, vp, sz, vp]
@@ -218,6 +223,88 @@ class TopkStep:
         if status:
             _check(status, "tgs_topk_ef_step")
         return self.out_idx, self.out_val
+
+
+def _segment_table(offsets, ks):
+    """(nseg, int64 offsets[nseg+1], int64 ks[nseg]) as contiguous host arrays."""
+    offs = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
+    kk = np.ascontiguousarray(np.asarray(ks, dtype=np.int64))
+    if offs.ndim != 1 or kk.ndim != 1 or offs.size != kk.size + 1:
+        raise ValueError("offsets must have one entry more than ks")
+    return int(kk.size), offs, kk
+
+
+def topk_segmented_workspace_bytes(offsets, ks) -> int:
+    nseg, offs, kk = _segment_table(offsets, ks)
+    return int(_load().tgs_topk_segmented_workspace_bytes(nseg, offs.ctypes.data, kk.ctypes.data))
+
+
+def topk_ef_step_segmented(grad: torch.Tensor, residual: torch.Tensor, offsets, ks, out_idx=None, out_val=None,
+                           ws: torch.Tensor | None = None):
+    """Layer-wise error-feedback top-k: segment s = [offsets[s], offsets[s+1])
+    of ``grad``/``residual`` gets the top-k step with k = ks[s], in one call.
+
+    Returns ``(idx int32[sum ks], val float32[sum ks])``: segment s's pairs
+    start at ``sum(ks[:s])``, with indices relative to the segment's start."""
+    _require(grad, torch.float32, "grad")
+    _require(residual, torch.float32, "residual")
+    nseg, offs, kk = _segment_table(offsets, ks)
+    n = grad.numel()
+    if residual.numel() != n or residual.device != grad.device:
+        raise ValueError("grad and residual must have the same length and device")
+    if nseg and int(offs[-1]) != n:
+        raise ValueError("offsets[-1] must equal the vector length")
+    total = int(kk.sum()) if nseg else 0
+    dev = grad.device
+    if out_idx is None:
+        out_idx = torch.empty(total, dtype=torch.int32, device=dev)
+    if out_val is None:
+        out_val = torch.empty(total, dtype=torch.float32, device=dev)
+    _require(out_idx, torch.int32, "out_idx")
+    _require(out_val, torch.float32, "out_val")
+    if out_idx.numel() < total or out_val.numel() < total:
+        raise ValueError("outputs hold fewer than sum(ks) entries")
+    lib = _load()
+    need = lib.tgs_topk_segmented_workspace_bytes(nseg, offs.ctypes.data, kk.ctypes.data)
+    if need == 0:
+        raise ValueError("invalid segment table")
+    if ws is None:
+        ws = workspace("topk", need, dev)
+    st = lib.tgs_topk_ef_step_segmented(_ptr(grad), _ptr(residual), nseg, offs.ctypes.data, kk.ctypes.data,
+                                        _ptr(out_idx), _ptr(out_val), ws.data_ptr(), ws.numel(), _stream_handle(dev))
+    _check(st, "tgs_topk_ef_step_segmented")
+    return out_idx[:total], out_val[:total]
+
+
+class TopkSegments:
+    """A prepared layer-wise top-k step (fixed segment table) for repeated
+    calls: holds the host table, the outputs, the workspace and the stream."""
+
+    def __init__(self, offsets, ks, device="cuda", stream=None):
+        lib = _load()
+        self.nseg, self.offsets, self.ks = _segment_table(offsets, ks)
+        self.n = int(self.offsets[-1]) if self.nseg else 0
+        self.total = int(self.ks.sum()) if self.nseg else 0
+        self.device = torch.device(device)
+        need = lib.tgs_topk_segmented_workspace_bytes(self.nseg, self.offsets.ctypes.data, self.ks.ctypes.data)
+        if need == 0:
+            raise ValueError("invalid segment table")
+        self.ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
+        self.out_idx = torch.empty(max(self.total, 1), dtype=torch.int32, device=self.device)
+        self.out_val = torch.empty(max(self.total, 1), dtype=torch.float32, device=self.device)
+        self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
+        self._fn = lib.tgs_topk_ef_step_segmented
+        self._args = (self.nseg, self.offsets.ctypes.data, self.ks.ctypes.data, self.out_idx.data_ptr(),
+                      self.out_val.data_ptr(), self.ws.data_ptr(), self.ws.numel(), self.stream.cuda_stream)
+
+    def __call__(self, grad: torch.Tensor, residual: torch.Tensor):
+        if grad.numel() != self.n or residual.numel() != self.n:
+            raise ValueError("this step is prepared for n=%d" % self.n)
+        ns, op, kp, oi, ov, wp, wn, st = self._args
+        status = self._fn(grad.data_ptr(), residual.data_ptr(), ns, op, kp, oi, ov, wp, wn, st)
+        if status:
+            _check(status, "tgs_topk_ef_step_segmented")
+        return self.out_idx[:self.total], self.out_val[:self.total]
 
 
 def threshold_workspace_bytes(n: int) -> int:

@@ -98,6 +98,7 @@ constexpr int kSmallThreads = 1024;
 constexpr int kSmallPer = 8192;            // entries per workgroup of k_small (8 per thread)
 constexpr int64_t kSmallMaxN = 1 << 18;    // k_small: n <= this (at most 32 workgroups) ...
 constexpr int64_t kSmallMaxK = 256;        // ... and k <= this
+constexpr int kSmallMaxSeg = 64;           // segments one k_small launch takes
 constexpr u32 kNoGuide = 0xFFFFFFFFu;  // guided accumulate pass: keep no candidates
 constexpr u32 kBktMax = 8192;     // buckets of the guided ranking at most
 constexpr u32 kBktCap = 1024;     // entries one bucket may hold
@@ -158,10 +159,11 @@ struct StepCtl {
   u32 rescans;    // workgroup shares re-read because their list was incomplete (never reset)
   u32 guided_used;    // guided general-path calls that selected from the copied candidates (never reset)
   u32 guided_missed;  // guided calls whose guess or regions did not hold: acc read again (never reset)
-  u32 small_done;     // k_small arrivals; its last workgroup leaves it zero
+  u32 small_done;     // (unused)
   u32 pad1[55];
   StepSet set[2];
   Plan plan;
+  u32 seg_done[64];  // k_small arrivals per segment of a launch; each segment's last workgroup leaves it zero
   // guided accumulate pass (standalone general path): k_guess adds its sample
   // histogram into guide_hist; its last workgroup picks guide_bin and leaves
   // guide_hist, guide_done and guide_ovf zero for the accumulate pass
@@ -1334,22 +1336,35 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_guided(GuidedArgs a) {
 __global__ __launch_bounds__(kGenThreads) void k_general(GenArgs a) { general_path<kGenThreads, 16, true, 9, true>(a); }
 
 // ------------------------------------------------------------- k_small ----
-// Small vectors (n <= 2^18, k <= 256) in one launch with no grid barrier:
-// workgroup b takes entries [8192 b, 8192 (b+1)): acc = residual + grad,
-// written back at device scope, keys kept in LDS; it selects its own top
-// min(k, len) by a three-level radix select in LDS and writes them, in index
-// order, to its candidate list.  The last workgroup to arrive selects the
-// top k of the lists (in workgroup order, so in index order: ties go to the
-// lower index as everywhere), sorts them by (key desc, index asc) and emits
-// them.  Any entry of the global top k is in its own workgroup's top k.
+// Small vectors (n <= 2^18, k <= 256) in one launch with no grid barrier,
+// up to 64 of them (the segments of one vector, layer by layer) per launch.
+// Workgroup b belongs to the last segment whose first workgroup is <= b and
+// takes that segment's entries [8192 b', 8192 (b'+1)) (b' = b minus the
+// segment's first workgroup): acc = residual + grad, written back at device
+// scope, keys kept in LDS; it selects its own top min(k, len) by a
+// three-level radix select in LDS and writes them, in index order, to its
+// candidate list.  The segment's last workgroup to arrive selects the top k
+// of its lists (in workgroup order, so in index order: ties go to the lower
+// index as everywhere), sorts them by (key desc, index asc) and emits them.
+// Any entry of the segment's top k is in its own workgroup's top k.  With
+// k = 0 a segment only writes acc.
+struct SmallSeg {
+  int64_t start;  // first entry (from grad / residual)
+  u32 len;        // entries, <= kSmallMaxN
+  u32 k;          // <= min(kSmallMaxK, len)
+  u32 out_off;    // its pairs start at out_idx + out_off; indices relative to `start`
+  u32 wg0;        // its first workgroup
+};
 struct SmallArgs {
   const float* grad;
   float* residual;
-  int64_t n, k;
   int32_t* out_idx;
   float* out_val;
-  StepCtl* ctl;
+  u32* err;
+  u32* done;  // [nseg] arrival counters, zero on entry, left zero
   u64* cand;  // [gridDim.x][kSmallMaxK]
+  int nseg;
+  SmallSeg seg[kSmallMaxSeg];
 };
 
 // Radix select in LDS of the need-th largest key among `len` entries, whose
@@ -1464,30 +1479,39 @@ __global__ __launch_bounds__(kSmallThreads) void k_small(SmallArgs a) {
   __shared__ u32 s_wc[2][NW][2];
   __shared__ u32 s_last;
   const int tid = threadIdx.x;
-  const int b = blockIdx.x, G = gridDim.x;
-  const int64_t cb = (int64_t)b * kSmallPer;
-  const u32 len = (u32)std::min<int64_t>(kSmallPer, a.n - cb);
-  const u32 kk = (u32)std::min<int64_t>(a.k, len);
-  if (b == 0 && tid == 0) a.ctl->err = 0u;
+  const u32 b = blockIdx.x;
+  int sg = 0;  // this workgroup's segment (the same in every thread)
+  for (int q = 1; q < a.nseg; ++q)
+    if (a.seg[q].wg0 <= b) sg = q;
+  const SmallSeg S = a.seg[sg];
+  const u32 bl = b - S.wg0;                          // workgroup within the segment
+  const u32 G = (S.len + kSmallPer - 1) / kSmallPer;  // the segment's workgroups
+  const u32 cb = bl * kSmallPer;                     // relative to the segment
+  const u32 len = std::min<u32>(kSmallPer, S.len - cb);
+  const u32 kk = std::min<u32>(S.k, len);
+  const float* __restrict__ g = a.grad + S.start;
+  float* __restrict__ res = a.residual + S.start;
+  if (b == 0 && tid == 0) *a.err = 0u;
   {
     float gq[EPT], rq[EPT];
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
       const u32 i = (u32)(j * NT + tid);
-      const int64_t e = cb + (i < len ? i : 0u);
-      gq[j] = a.grad[e];
-      rq[j] = a.residual[e];
+      const u32 e = cb + (i < len ? i : 0u);
+      gq[j] = g[e];
+      rq[j] = res[e];
     }
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
       const u32 i = (u32)(j * NT + tid);
       if (i < len) {
         const float acc = rq[j] + gq[j];
-        st_agent_f32(a.residual + cb + i, acc);
+        st_agent_f32(res + cb + i, acc);
         s_bits[i] = __float_as_uint(acc);
       }
     }
   }
+  if (S.k == 0) return;
   __syncthreads();
   u32 t_lo, t_eq, r;
   lds_select<NT>([&](u32 i) { return key_of_bits(s_bits[i]); }, len, kk, s_hist, s_scan, s_found, t_lo, t_eq, r);
@@ -1496,15 +1520,16 @@ __global__ __launch_bounds__(kSmallThreads) void k_small(SmallArgs a) {
                        [&](u32 pos, u64 pv) { st_agent64(mine + pos, pv); });
   wait_all_memory();  // acc and the list have completed at device scope
   __syncthreads();
-  if (tid == 0) s_last = add_agent_acqrel(&a.ctl->small_done, 1u) == (u32)G - 1u ? 1u : 0u;
+  if (tid == 0) s_last = add_agent_acqrel(&a.done[sg], 1u) == G - 1u ? 1u : 0u;
   __syncthreads();
   if (!s_last) return;
   if (tid < kWave) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   __syncthreads();
-  // every list but the last holds k entries
-  const u32 k = (u32)a.k;
-  const u32 M = (u32)(G - 1) * k + (u32)std::min<int64_t>(a.k, a.n - (int64_t)(G - 1) * kSmallPer);
-  for (u32 q = tid; q < M; q += NT) s_cand[q] = ld_agent64(a.cand + (size_t)(q / k) * kSmallMaxK + q % k);
+  // every list of the segment but its last holds k entries
+  const u32 k = S.k;
+  const u32 M = (G - 1) * k + std::min<u32>(k, S.len - (G - 1) * kSmallPer);
+  const u64* const lists = a.cand + (size_t)S.wg0 * kSmallMaxK;
+  for (u32 q = tid; q < M; q += NT) s_cand[q] = ld_agent64(lists + (size_t)(q / k) * kSmallMaxK + q % k);
   __syncthreads();
   lds_select<NT>([&](u32 i) { return key_of_bits((u32)(s_cand[i] >> 32)); }, M, k, s_hist, s_scan, s_found, t_lo, t_eq,
                  r);
@@ -1528,13 +1553,15 @@ __global__ __launch_bounds__(kSmallThreads) void k_small(SmallArgs a) {
       }
       __syncthreads();
     }
+  int32_t* const oi = a.out_idx + S.out_off;
+  float* const ov = a.out_val + S.out_off;
   for (u32 i = tid; i < k; i += NT) {
     const Pair e = unpack_pair(s_sel[i]);
-    a.out_idx[i] = e.idx;
-    a.out_val[i] = __uint_as_float(e.bits);
-    st_agent_f32(a.residual + e.idx, 0.0f);
+    oi[i] = e.idx;
+    ov[i] = __uint_as_float(e.bits);
+    st_agent_f32(res + e.idx, 0.0f);
   }
-  if (tid == 0) st_agent(&a.ctl->small_done, 0u);
+  if (tid == 0) st_agent(&a.done[sg], 0u);
 }
 
 // ------------------------------------------------------------- k_step ----
@@ -2687,12 +2714,13 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
     SmallArgs m{};
     m.grad = grad;
     m.residual = residual;
-    m.n = n;
-    m.k = k;
     m.out_idx = out_idx;
     m.out_val = out_val;
-    m.ctl = ctl;
+    m.err = &ctl->err;
+    m.done = ctl->seg_done;
     m.cand = (u64*)(ws + L.small);
+    m.nseg = 1;
+    m.seg[0] = SmallSeg{0, (u32)n, (u32)k, 0u, 0u};
     hipEvent_t e0, e1;
     take_profile_events(&e0, &e1);
     if (e0) (void)hipEventRecord(e0, stream);
@@ -2833,5 +2861,129 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
   if (ev1) (void)hipEventRecord(ev1, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TGS_EHIP, "topk_ef_step: launch failed: %s", hipGetErrorString(e));
+  return TGS_OK;
+}
+
+// ======================================================== segmented host ==
+namespace {
+
+bool small_segment(int64_t len, int64_t k) { return len <= kSmallMaxN && k <= kSmallMaxK; }
+
+// Checks the segment table; false (with the reason) if it is not valid.
+bool segments_valid(int32_t nseg, const int64_t* offsets, const int64_t* ks, const char** why) {
+  if (nseg < 0) return *why = "nseg < 0", false;
+  if (nseg > 0 && (!offsets || !ks)) return *why = "null offsets/ks", false;
+  if (nseg == 0) return true;
+  if (offsets[0] != 0) return *why = "offsets[0] != 0", false;
+  int64_t ksum = 0;
+  for (int32_t s = 0; s < nseg; ++s) {
+    const int64_t len = offsets[s + 1] - offsets[s];
+    if (len < 0) return *why = "offsets decrease", false;
+    if (ks[s] < 0 || ks[s] > len) return *why = "ks[s] outside [0, segment length]", false;
+    ksum += ks[s];
+  }
+  if (offsets[nseg] > INT32_MAX || ksum > INT32_MAX) return *why = "total length or total k above 2^31-1", false;
+  return true;
+}
+
+// Workspace: a top-k workspace for the largest non-small segment (its header
+// also serves the small-segment launches), then the candidate lists of the
+// small segments' workgroups.
+struct SegLayout {
+  size_t big, lists, total;
+};
+
+SegLayout seg_layout(int32_t nseg, const int64_t* offsets, const int64_t* ks) {
+  SegLayout L{};
+  L.big = kWorkspaceHeader;
+  int64_t wgs = 0;
+  for (int32_t s = 0; s < nseg; ++s) {
+    const int64_t len = offsets[s + 1] - offsets[s];
+    if (len == 0) continue;
+    if (small_segment(len, ks[s])) wgs += (len + kSmallPer - 1) / kSmallPer;
+    else L.big = std::max(L.big, topk_layout(len, ks[s]).total);
+  }
+  L.big = align256(L.big);
+  L.lists = L.big;
+  L.total = L.lists + sizeof(u64) * (size_t)wgs * kSmallMaxK;
+  return L;
+}
+
+}  // namespace
+
+extern "C" size_t tgs_topk_segmented_workspace_bytes(int32_t nseg, const int64_t* offsets, const int64_t* ks) {
+  const char* why = nullptr;
+  if (!segments_valid(nseg, offsets, ks, &why)) return 0;
+  return seg_layout(nseg, offsets, ks).total;
+}
+
+extern "C" tgs_status tgs_topk_ef_step_segmented(const float* grad, float* residual, int32_t nseg,
+                                                 const int64_t* offsets, const int64_t* ks, int32_t* out_idx,
+                                                 float* out_val, void* workspace, size_t workspace_bytes,
+                                                 hipStream_t stream) {
+  const char* why = nullptr;
+  if (!segments_valid(nseg, offsets, ks, &why)) return fail(TGS_EINVAL, "topk_ef_step_segmented: %s", why);
+  if (!workspace) return fail(TGS_EINVAL, "topk_ef_step_segmented: null workspace");
+  if (nseg == 0) return TGS_OK;
+  const int64_t n = offsets[nseg];
+  int64_t ksum = 0;
+  for (int32_t s = 0; s < nseg; ++s) ksum += ks[s];
+  if (n > 0 && (!grad || !residual)) return fail(TGS_EINVAL, "topk_ef_step_segmented: null grad/residual");
+  if (ksum > 0 && (!out_idx || !out_val)) return fail(TGS_EINVAL, "topk_ef_step_segmented: null output pointer");
+  for (const void* p : {(const void*)grad, (const void*)residual, (const void*)out_idx, (const void*)out_val})
+    if (((uintptr_t)p & 3u) != 0) return fail(TGS_EINVAL, "topk_ef_step_segmented: pointer not 4-byte aligned");
+  const size_t nb4 = (size_t)n * 4, kb4 = (size_t)ksum * 4;
+  if (overlaps(grad, nb4, residual, nb4) || overlaps(grad, nb4, out_idx, kb4) || overlaps(grad, nb4, out_val, kb4) ||
+      overlaps(residual, nb4, out_idx, kb4) || overlaps(residual, nb4, out_val, kb4) ||
+      overlaps(out_idx, kb4, out_val, kb4))
+    return fail(TGS_EINVAL, "topk_ef_step_segmented: overlapping buffers");
+  const SegLayout L = seg_layout(nseg, offsets, ks);
+  if (workspace_bytes < L.total)
+    return fail(TGS_EWORKSPACE, "topk_ef_step_segmented: workspace %zu bytes, need %zu", workspace_bytes, L.total);
+  char* ws = (char*)workspace;
+  StepCtl* ctl = (StepCtl*)ws;
+  // the small segments, up to kSmallMaxSeg per launch
+  SmallArgs m{};
+  m.grad = grad;
+  m.residual = residual;
+  m.out_idx = out_idx;
+  m.out_val = out_val;
+  m.err = &ctl->err;
+  m.done = ctl->seg_done;
+  u64* lists = (u64*)(ws + L.lists);
+  u32 wg = 0;
+  auto flush = [&]() {
+    if (m.nseg == 0) return;
+    m.cand = lists;
+    hipLaunchKernelGGL(k_small, dim3(wg), dim3(kSmallThreads), 0, stream, m);
+    lists += (size_t)wg * kSmallMaxK;
+    m.nseg = 0;
+    wg = 0;
+  };
+  int64_t koff = 0;
+  for (int32_t s = 0; s < nseg; ++s) {
+    const int64_t len = offsets[s + 1] - offsets[s];
+    if (len > 0 && small_segment(len, ks[s])) {
+      m.seg[m.nseg++] = SmallSeg{offsets[s], (u32)len, (u32)ks[s], (u32)koff, wg};
+      wg += (u32)((len + kSmallPer - 1) / kSmallPer);
+      if (m.nseg == kSmallMaxSeg) flush();
+    }
+    koff += ks[s];
+  }
+  flush();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TGS_EHIP, "topk_ef_step_segmented: launch failed: %s", hipGetErrorString(e));
+  // the others, one step each on the shared top-k workspace
+  koff = 0;
+  for (int32_t s = 0; s < nseg; ++s) {
+    const int64_t len = offsets[s + 1] - offsets[s];
+    if (len > 0 && !small_segment(len, ks[s])) {
+      const tgs_status st = tgs_topk_ef_step(grad + offsets[s], residual + offsets[s], len, ks[s],
+                                             ks[s] ? out_idx + koff : nullptr, ks[s] ? out_val + koff : nullptr,
+                                             workspace, L.big, stream);
+      if (st != TGS_OK) return st;
+    }
+    koff += ks[s];
+  }
   return TGS_OK;
 }

@@ -18,7 +18,9 @@
 //              k_gt_select  one workgroup per merge: radix select of the k-th
 //                           key over 11/11/9-bit digits, then an ordered
 //                           compaction that keeps every key above it and the
-//                           lowest-index ties, written back to slot s.
+//                           lowest-index ties, written back to slot s (for
+//                           2k <= 65,536 the merge's keys stay in registers:
+//                           k_gt_select_reg).
 //   final    slot 0 sorted by (key desc, index asc) with the same run sort and
 //            merge passes; the mask binary-searches every input index in the
 //            index-sorted slot 0.
@@ -296,6 +298,128 @@ __global__ __launch_bounds__(kSelThreads) void k_gt_select(SelectArgs a) {
   }
 }
 
+// The same selection with M's keys loaded once into registers: thread t
+// holds entries j NT + t (j < EPT; coalesced rows, every load in flight at
+// once).  The three histogram levels run on the registers, and the ordered
+// compaction walks the rows in order (index order is (row, thread) order)
+// with a ballot and per-wave counts per row; only the selected pairs are
+// read again to be written out.  For 2k <= EPT NT.
+template <int EPT>
+__global__ __launch_bounds__(kSelThreads) void k_gt_select_reg(SelectArgs a) {
+  constexpr int NT = kSelThreads;
+  __shared__ u32 s_hist[2048];
+  __shared__ u32 s_scan[NT / kWave + 1];
+  __shared__ u32 s_found[3];
+  const int tid = threadIdx.x;
+  const int64_t m = blockIdx.x;
+  const u32 len = (u32)(2 * a.k);
+  const Pair* __restrict__ M = a.M + m * (int64_t)len;
+  Pair* __restrict__ out = a.slots + (m * a.stride) * a.k;
+  // a hole or a place past the end gets key 0xFFFFFFFF, above every real
+  // key: no histogram level counts it (its top bits never match the prefix)
+  // and, compared as signed, it is below every threshold
+  // (16 rows of loads in flight at a time: all EPT at once would need two
+  // registers per row on top of the keys)
+  static_assert(EPT % 16 == 0, "rows come in groups of 16");
+  u32 key[EPT];
+#pragma unroll
+  for (int c = 0; c < EPT; c += 16) {
+#pragma unroll
+    for (int j = c; j < c + 16; ++j) {
+      const u32 i = (u32)(j * NT + tid);
+      const Pair e = M[i < len ? i : 0u];
+      key[j] = i < len && e.idx >= 0 ? key_of_bits(e.bits) : 0xFFFFFFFFu;
+    }
+    asm volatile("" ::: "memory");
+  }
+  const int shifts[3] = {20, 9, 0};
+  const int widths[3] = {11, 11, 9};
+  u32 prefix = 0;
+  u32 need = (u32)a.k;
+  u32 t_lo = 0, t_eq = 0, r = 0;
+  for (int L = 0; L < 3; ++L) {
+    const int sh = shifts[L], wd = widths[L];
+    const u32 nbins = 1u << wd;
+    for (int i = tid; i < 2048; i += NT) s_hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < EPT; ++j)
+      if ((key[j] >> (sh + wd)) == prefix) atomicAdd(&s_hist[(key[j] >> sh) & (nbins - 1)], 1u);
+    __syncthreads();
+    const int cpt = std::max(1, (int)nbins / NT);
+    const int top = (int)nbins - cpt * tid;
+    u32 own = 0;
+    if (top > 0)
+      for (int d = top - 1; d >= std::max(0, top - cpt); --d) own += s_hist[d];
+    u32 tot;
+    const u32 above = block_exclusive_sum<NT>(own, s_scan, tot);
+    if (tid == 0) s_found[0] = 0xFFFFFFFFu;
+    __syncthreads();
+    if (top > 0 && above < need && above + own >= need) {
+      u32 run = above;
+      for (int d = top - 1; d >= std::max(0, top - cpt); --d) {
+        const u32 h = s_hist[d];
+        if (run + h >= need) {
+          s_found[0] = (u32)d;
+          s_found[1] = run;
+          s_found[2] = h;
+          break;
+        }
+        run += h;
+      }
+    }
+    __syncthreads();
+    const u32 d = s_found[0];
+    if (d == 0xFFFFFFFFu) return;  // fewer than k live entries: impossible for valid rows
+    need -= s_found[1];
+    const u32 h = s_found[2];
+    prefix = (prefix << wd) | d;
+    __syncthreads();  // s_found is rewritten by the next level
+    if (need == h) {
+      t_lo = prefix << sh;
+      break;
+    }
+    if (L == 2) {
+      t_lo = prefix + 1;
+      t_eq = prefix;
+      r = need;
+    }
+  }
+  // ordered compaction: every key >= t_lo and the first r equal to t_eq,
+  // row by row
+  __shared__ u32 s_wc[2][NT / kWave][2];
+  const int lane = lane_id(), w = tid / kWave;
+  u32 gt_seen = 0, eq_seen = 0;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const bool g = (int)key[j] >= (int)t_lo;
+    const bool q = r > 0 && key[j] == t_eq;
+    const u64 bg = ballot(g), be = ballot(q);
+    if (lane == 0) {
+      s_wc[j & 1][w][0] = (u32)__popcll(bg);
+      s_wc[j & 1][w][1] = (u32)__popcll(be);
+    }
+    __syncthreads();
+    u32 og = 0, oe = 0, tg = 0, te = 0;
+#pragma unroll
+    for (int v = 0; v < NT / kWave; ++v) {
+      const u32 cg = s_wc[j & 1][v][0], ce = s_wc[j & 1][v][1];
+      og += v < w ? cg : 0u;
+      oe += v < w ? ce : 0u;
+      tg += cg;
+      te += ce;
+    }
+    const u32 gb = gt_seen + og + lanes_below(bg), eb = eq_seen + oe + lanes_below(be);
+    if (g || (q && eb < r)) {
+      const u32 pos = gb + std::min(eb, r);
+      if (pos < (u32)a.k) out[pos] = M[(u32)(j * NT + tid)];
+    }
+    gt_seen += tg;
+    eq_seen += te;
+    asm volatile("" ::: "memory");  // keep each row's reload in its row
+  }
+}
+
 __global__ void k_gt_emit(const Pair* __restrict__ g, int64_t k, int32_t* out_idx, float* out_val) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < k) {
@@ -396,7 +520,12 @@ extern "C" tgs_status tgs_gtopk_merge(const int32_t* idx, const float* val, int3
     const int64_t ublocks = (ua.threads_per_merge * nm + kMergeThreads - 1) / kMergeThreads;
     hipLaunchKernelGGL(k_gt_union, dim3((unsigned)ublocks), dim3(kMergeThreads), 0, stream, ua);
     SelectArgs sa{slots, M, k, stride};
-    hipLaunchKernelGGL(k_gt_select, dim3((unsigned)nm), dim3(kSelThreads), 0, stream, sa);
+    const int64_t ept = (2 * k + kSelThreads - 1) / kSelThreads;
+    if (ept <= 16) hipLaunchKernelGGL(k_gt_select_reg<16>, dim3((unsigned)nm), dim3(kSelThreads), 0, stream, sa);
+    else if (ept <= 32) hipLaunchKernelGGL(k_gt_select_reg<32>, dim3((unsigned)nm), dim3(kSelThreads), 0, stream, sa);
+    else if (ept <= 48) hipLaunchKernelGGL(k_gt_select_reg<48>, dim3((unsigned)nm), dim3(kSelThreads), 0, stream, sa);
+    else if (ept <= 64) hipLaunchKernelGGL(k_gt_select_reg<64>, dim3((unsigned)nm), dim3(kSelThreads), 0, stream, sa);
+    else hipLaunchKernelGGL(k_gt_select, dim3((unsigned)nm), dim3(kSelThreads), 0, stream, sa);
   }
   Pair* f0 = (Pair*)(ws + L.f0);
   Pair* f1 = (Pair*)(ws + L.f1);

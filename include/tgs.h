@@ -190,7 +190,7 @@ const char* tgs_last_error(void);
  *                       9 = guided general path (the accumulate pass copies
  *                       out the candidates of a sampled first-level bin)
  *                       where the fast path would otherwise run.
- *                       The guided path needs n >= 2^22, grad and residual
+ *                       The guided path needs n >= 2^18, grad and residual
  *                       equally aligned modulo 16 bytes and k > 0; otherwise
  *                       7-9 run the plain general path.
  *   TGS_OPT_MAIN_GRID   0 = automatic, else the number of workgroups of the

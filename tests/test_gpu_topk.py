@@ -521,3 +521,15 @@ def test_segmented_many_small_segments(tgs_gpu):
         tgs_gpu.check_device_error(ws)
         ei, ev, r_cpu = _oracle_segments(grad, r_cpu, offsets, ks)
         assert_topk_equal((host(idx), host(val), host(r_gpu)), (ei, ev, r_cpu), "step %d" % step)
+
+
+@pytest.mark.parametrize("n,k", [(300_001, 300), (583_306, 583), (600_000, 60_000), (1_000_003, 100_000)])
+def test_guided_mid_sizes(tgs_gpu, n, k):
+    """Vectors between 2^18 and a few million entries, where the one-launch
+    step does not apply, take the guided route with fewer accumulate
+    workgroups than general-path workgroups."""
+    rng = np.random.default_rng(n % 1000 + k)
+    grad, res = make("mixture", n, rng)
+    got, (used, missed) = _guided_step(tgs_gpu, gpu(grad), gpu(res), k)
+    assert_topk_equal(got, oracle_topk(grad, res, k), "n=%d k=%d" % (n, k))
+    assert (used, missed) == (1, 0)

@@ -109,7 +109,7 @@ constexpr int kGuessBlocks = 64;
 constexpr int kGuessUnroll = 8;  // sample chunks per wave, all loads in flight at once
 constexpr int kGuessChunk = 4 * kWave;  // entries per sample chunk: one float4 per lane
 constexpr int64_t kGuessMaxChunks = (int64_t)kGuessBlocks * (kGuessThreads / kWave) * kGuessUnroll;
-constexpr int64_t kGuideMinN = (int64_t)1 << 22;  // smaller vectors take the plain accumulate pass
+constexpr int64_t kGuideMinN = (int64_t)1 << 18;  // smaller vectors take the plain accumulate pass
 constexpr u32 kWhyPlan = 1u, kWhyBucket = 4u, kWhyFew = 8u, kWhyRegion = 16u, kWhyList = 32u, kWhyWait = 64u;
 
 // ------------------------------------------------------------- state ----
@@ -298,11 +298,12 @@ struct GenArgs {
   u32 cand_cap;
   u32 acc_rows;          // rows of acc_hist (standalone path)
   const u32* acc_hist;   // [acc_rows][2048] first-level histograms from the accumulate pass
-  // guided accumulate pass (guided != 0; then acc_rows == the grid): the
-  // entries of first-level bins >= *guide_bin streamed by workgroup b, in no
-  // particular order, fill the regions of its waves as one region of
-  // guide_cnt[b] pairs
+  // guided accumulate pass (guided != 0; then acc_rows <= the grid): the
+  // entries of first-level bins >= *guide_bin streamed by its workgroup b, in
+  // no particular order, fill the regions of this kernel's workgroup b's
+  // waves as one region of guide_cnt[b] pairs
   u32 guided;
+  u32 guide_stride;  // pairs between consecutive workgroups' regions
   const u32* guide_bin;
   const u32* guide_ovf;
   const u32* guide_cnt;
@@ -798,11 +799,11 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
         const u32 gb = *a.guide_bin;
         bool ranked = false;
         if (gb != kNoGuide && gb <= d && *a.guide_ovf == 0u) {
-          const u32 cntb = a.guide_cnt[b];
+          const u32 cntb = (u32)b < a.acc_rows ? a.guide_cnt[b] : 0u;  // the accumulate pass may have fewer workgroups
           const u32 part = (cntb + NW - 1) / NW;
           const u32 lo = std::min(cntb, (u32)w * part), hi = std::min(cntb, lo + part);
           const u64* const wave_reg = creg;
-          creg = opaque_ptr(a.cand + (size_t)b * NW * a.cand_cap + lo);
+          creg = opaque_ptr(a.cand + (size_t)b * a.guide_stride + lo);
           ccount = hi - lo;
           const int st = bucket_rank(d, (u32)(n_above + h));
           if (st < 0) return;
@@ -2805,7 +2806,7 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
     // The guided accumulate pass copies the candidates out while it streams,
     // so k_general need not read acc again: it takes one region per
     // workgroup of k_general, in index order.
-    const bool guided = vec && k > 0 && path != 1 && n >= kGuideMinN && G1 == G2;
+    const bool guided = vec && k > 0 && path != 1 && n >= kGuideMinN && G1 <= G2;
     if (guided) {
       const int64_t want = (int64_t)std::ceil(1024.0 * (double)n / (double)k);  // ~1024 expected above the k-th key
       int64_t chunks = (want + kGuessChunk - 1) / kGuessChunk;
@@ -2818,7 +2819,10 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
       const double f = (double)(chunks * kGuessChunk) / (double)n;
       const double c = (double)k * f;
       q.c_req = path == 7 ? 1u : (u32)std::min(4.0e9, std::ceil(c + 6.0 * std::sqrt(c) + 8.0));
-      const double room = (double)G1 * (kGenThreads / kWave) * L.cand_cap;
+      // the candidate room of all k_general waves, split over the G1
+      // accumulate workgroups
+      const u32 stride = (u32)((int64_t)G2 * (kGenThreads / kWave) * L.cand_cap / G1);
+      const double room = (double)G1 * stride;
       q.s_max = (u32)std::min(4.0e9, std::floor(0.6 * room * f));
       q.ctl = ctl;
       const int gq = (int)std::min<int64_t>(kGuessBlocks, (chunks + (kGuessThreads / kWave) * kGuessUnroll - 1) /
@@ -2838,9 +2842,10 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
       g.guide_ovf = &ctl->guide_ovf;
       g.guide_cnt = (u32*)(ws + L.guide_cnt);
       g.cand = ga.cand;
-      g.cap = path == 8 ? 1u : (u32)(kGenThreads / kWave) * L.cand_cap;
+      g.cap = path == 8 ? 1u : stride;
       hipLaunchKernelGGL(k_acc_guided, dim3(G1), dim3(kAccThreads), 0, stream, g);
       ga.guided = 1;
+      ga.guide_stride = stride;
       ga.guide_bin = &ctl->guide_bin;
       ga.guide_ovf = &ctl->guide_ovf;
       ga.guide_cnt = g.guide_cnt;

@@ -192,11 +192,11 @@ def parse():
 # the 256 MiB copy of --copy-calibration.  Valid only for the k_step
 # source they were taken on: `source_sha256` is the hash of csrc/topk.hip then.
 MEASURED_TRAFFIC = {
-    "source_sha256": "39ff11c688e371a00df89f7b20012b251a45c526a67a5c54457ca4915c721543",
-    # FETCH_SIZE 103,060.8 KiB x (262,144 / 131,083.5: the copy's true read over its counter)
-    "fetch_bytes": 211049963,
-    # WRITE_SIZE 102,287.7 KiB x 1.0 (the copy's counter read exactly 262,144 KiB)
-    "write_bytes": 104742640,
+    "source_sha256": "8d3c973cdb0df26144f36725711cdfd44d66c04723353e567e69e084fbbc1af0",
+    # FETCH_SIZE 103,059.4 KiB x (262,144 / 131,083.5: the copy's true read over its counter)
+    "fetch_bytes": 211047147,
+    # WRITE_SIZE 102,287.0 KiB x 1.0 (the copy's counter read exactly 262,144 KiB)
+    "write_bytes": 104741936,
 }
 
 

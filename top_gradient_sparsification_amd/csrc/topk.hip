@@ -1294,9 +1294,11 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_guided(GuidedArgs a) {
       rr = __builtin_nontemporal_load(rv + i);
     }
   };
-  auto process = [&](int64_t t, const v4f& gg, const v4f& rr) {
+  // a row's candidates are placed after the loads of the row two ahead
+  // are out, so the LDS atomic of the placement does not hold them back
+  auto process = [&](int64_t t, const v4f& gg, const v4f& rr, u32& m4, u32* bq) {
     const int64_t i = t * NT + tid;
-    u32 m4 = 0, bq[4] = {0u, 0u, 0u, 0u};
+    m4 = 0;
     if (i < a.nv) {
       const v4f acc = rr + gg;
       __builtin_nontemporal_store(acc, rv + i);
@@ -1308,18 +1310,20 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_guided(GuidedArgs a) {
         m4 |= (guide && bin >= gbin ? 1u : 0u) << e;
       }
     }
-    if (guide) place(m4, a.head + 4 * i, bq);
   };
   v4f ga, ra, gb, rb;
+  u32 m4, bq[4] = {0u, 0u, 0u, 0u};
   int64_t t = blockIdx.x;
   load(t, ga, ra);
   load(t + G, gb, rb);
   for (; t < nrows; t += 2 * G) {
-    process(t, ga, ra);
+    process(t, ga, ra, m4, bq);
     load(t + 2 * G, ga, ra);
+    if (guide) place(m4, a.head + 4 * (t * NT + tid), bq);
     if (t + G >= nrows) break;
-    process(t + G, gb, rb);
+    process(t + G, gb, rb, m4, bq);
     load(t + 3 * G, gb, rb);
+    if (guide) place(m4, a.head + 4 * ((t + G) * NT + tid), bq);
   }
   if (blockIdx.x == gridDim.x - 1 && tid < kWave) {
     const int64_t i = a.head + 4 * a.nv + tid;

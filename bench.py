@@ -192,11 +192,11 @@ def parse():
 # the 256 MiB copy of --copy-calibration.  Valid only for the k_step
 # source they were taken on: `source_sha256` is the hash of csrc/topk.hip then.
 MEASURED_TRAFFIC = {
-    "source_sha256": "8d3c973cdb0df26144f36725711cdfd44d66c04723353e567e69e084fbbc1af0",
-    # FETCH_SIZE 103,059.4 KiB x (262,144 / 131,083.5: the copy's true read over its counter)
-    "fetch_bytes": 211047147,
-    # WRITE_SIZE 102,287.0 KiB x 1.0 (the copy's counter read exactly 262,144 KiB)
-    "write_bytes": 104741936,
+    "source_sha256": "98e195917f823db0f4d19ab7b86cf4b242c76beb678364db3955c32b8b4692ca",
+    # FETCH_SIZE 103,058.9 KiB x (262,144 / 131,083.5: the copy's true read over its counter)
+    "fetch_bytes": 211046059,
+    # WRITE_SIZE 102,288.4 KiB x 1.0 (the copy's counter read exactly 262,144 KiB)
+    "write_bytes": 104743280,
 }
 
 

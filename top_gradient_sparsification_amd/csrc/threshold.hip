@@ -30,7 +30,7 @@
 
 namespace tgs {
 
-constexpr int kThrThreads = 256;
+constexpr int kThrThreads = 1024;
 constexpr int kThrWaves = kThrThreads / kWave;
 constexpr int kThrMaxBlocks = 2048;
 

@@ -8,12 +8,14 @@ positions, residual carried over from earlier error-feedback steps.
 
 A step is one tgs_topk_ef_step call: acc = residual + grad, top-k of |acc|
 with the lower-index tie rule, (int32, fp32) pairs out, residual written back.
-Four residual buffers and sixteen gradients (drawn on the GPU from the same
-seeded mixture) rotate: consecutive steps never touch the same buffers, so no
-step finds its inputs in the 256 MB Infinity Cache and every timed step streams
-them from HBM, and each residual buffer meets all sixteen gradients before one
-repeats.  The W warm-up steps give every residual buffer its error-feedback
-history (W = 20 -> 5 steps each).
+Sixteen gradients are drawn on the GPU from the seeded mixture.  A set-up
+phase, outside the timing and independent of --warmup, gives each of up to 64
+residual buffers its error-feedback history: 5 prior EF steps at the same
+density, starting from 0.  Timed step i uses residual buffer i (mod 64) and
+gradient i (mod 16), so up to 64 timed steps each measure exactly the sixth
+EF step, and consecutive steps never touch the same buffers: no step finds
+its inputs in the 256 MB Infinity Cache.  The W warm-up steps run on scratch
+copies of the residuals.
 
 Prints one JSON line.  `roofline` covers the dominant kernel, k_step (the
 whole fused step, one launch: 12n + 8k algorithmic bytes per launch), timed
@@ -21,7 +23,7 @@ with HIP events on the stream it is launched on, recorded around spans of 8
 back-to-back launches: the average launch period, gaps between launches
 included, without an event pair around every launch (which adds a few
 microseconds of its own); `cpu_baseline` is the plain C oracle on one host core
-on the same workload.
+on the same workload (its residual history built by the oracle itself).
 
     python bench.py --workload NAME [--steps K]
 
@@ -52,6 +54,8 @@ import json
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -136,7 +140,7 @@ def run_other(args):
         restore()
         call()
     torch.cuda.synchronize()
-    K = max(1, args.steps if args.steps != 500 else (20 if n < 1_000_000_000 else 5))
+    K = max(1, args.steps if args.steps != 64 else (20 if n < 1_000_000_000 else 5))
     times = []
     print("bench: timing %d calls" % K, file=sys.stderr, flush=True)
     for _ in range(K):
@@ -177,8 +181,8 @@ def run_other(args):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="topk_n25.6M_0.1%", choices=sorted(OTHER) + ["topk_n25.6M_0.1%"])
     ap.add_argument("--copy-calibration", action="store_true",
@@ -211,6 +215,40 @@ def traffic_per_launch():
     return MEASURED_TRAFFIC["fetch_bytes"] + MEASURED_TRAFFIC["write_bytes"]
 
 
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return os.uname().machine
+
+
+def cpu_baseline(k):
+    """The C oracle on one host core, on the headline workload: a residual
+    built by 5 oracle EF steps from 0, then step 6 timed 3 times (median)."""
+    import oracle
+    from top_gradient_sparsification_amd import workloads
+    print("bench: cpu baseline (oracle, 1 core): 5 history steps, then 3 timed", file=sys.stderr, flush=True)
+    res = np.zeros(N, np.float32)
+    for p in range(5):
+        oracle.topk_ef_step(workloads.grad_resnet50(p + 1, variant=100), res, k)
+    g = workloads.grad_resnet50(6, variant=100)
+    times = []
+    for _ in range(3):
+        rr = res.copy()
+        c0 = time.perf_counter()
+        oracle.topk_ef_step(g, rr, k)
+        times.append(time.perf_counter() - c0)
+    tc = sorted(times)[1]
+    ncpu = os.cpu_count()
+    return {"value": N / tc, "unit": "elements/s", "cores": 1, "kind": "oracle",
+            "sample": "the full n=25.6M, k=25,600 step 6 (residual from 5 oracle EF steps), median of 3 calls, "
+                      "%.2f s per call; oracle: 1 of %s cores (%s)" % (tc, ncpu, _cpu_model()),
+            "host_cores": ncpu, "cpu_model": _cpu_model()}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -221,7 +259,6 @@ def main():
     if args.workload != "topk_n25.6M_0.1%":
         run_other(args)
         return
-    import numpy as np
     import torch
     import top_gradient_sparsification_amd as tgs
     from top_gradient_sparsification_amd import workloads
@@ -229,7 +266,9 @@ def main():
     assert torch.cuda.is_available(), "no GPU visible"
     dev = torch.device("cuda:0")
     k = workloads.k_for_density(N, DENSITY)
-    sets, pool = 4, 16
+    K = args.steps
+    pool, prior = 16, 5
+    sets = max(1, min(64, K))
     print("bench: generating %d gradients of n=%d" % (pool, N), file=sys.stderr, flush=True)
     grads = [workloads.mixture_gpu(N, 1e-3, 0.01, 0.1, (workloads.CFG_RESNET50, 100, j), device=dev)
              for j in range(pool)]
@@ -244,18 +283,25 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def step(t):
-        run(grads[(t + t // pool) % pool], resid[t % sets])
-
-    print("bench: warmup %d steps" % args.warmup, file=sys.stderr, flush=True)
-    for t in range(args.warmup):
-        step(t)
+    print("bench: set-up: %d residual buffers x %d prior EF steps" % (sets, prior), file=sys.stderr, flush=True)
+    for j in range(sets):
+        for p in range(prior):
+            run(grads[(j + 5 * p) % pool], resid[j])
     torch.cuda.synchronize()
-    tgs.check_device_error(ws)
+    run.check()
+    print("bench: warmup %d steps" % args.warmup, file=sys.stderr, flush=True)
+    scratch = [resid[j % sets].clone() for j in range(min(2, sets))]
+    for t in range(args.warmup):
+        run(grads[t % pool], scratch[t % len(scratch)])
+    torch.cuda.synchronize()
+    run.check()
+    del scratch
     fb0 = int(ws[12:16].view(torch.int32).item())  # calls whose sampled plan did not hold
     rs0 = int(ws[20:24].view(torch.int32).item())  # workgroup shares re-read (incomplete local lists)
 
-    K = args.steps
+    def step(t):
+        run(grads[(t + 3) % pool], resid[t % sets])
+
     span = 8  # launches between two events
     nspan = max(1, K // span)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(nspan + 1)]
@@ -267,12 +313,12 @@ def main():
     for i in range(K):
         if i % span == 0 and i // span < nspan:
             ev[i // span].record(run.stream)
-        step(args.warmup + i)
+        step(i)
         if i + 1 == nspan * span:
             ev[nspan].record(run.stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    tgs.check_device_error(ws)
+    run.check()
     fast = int(ws[8:12].view(torch.int32).item())  # verdict word of the last step
     fallbacks = int(ws[12:16].view(torch.int32).item()) - fb0
     rescans = int(ws[20:24].view(torch.int32).item()) - rs0
@@ -288,20 +334,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
-        print("bench: cpu baseline (oracle, 1 core)", file=sys.stderr, flush=True)
-        g = workloads.grad_resnet50(1, variant=100)
-        r = workloads.grad_resnet50(2, variant=100)  # a nonzero residual of the same shape
-        times = []
-        for _ in range(2):
-            rr = r.copy()
-            c0 = time.perf_counter()
-            oracle.topk_ef_step(g, rr, k)
-            times.append(time.perf_counter() - c0)
-        tc = min(times)
-        cpu = {"value": N / tc, "unit": "elements/s", "cores": 1, "kind": "oracle",
-               "sample": "2 calls of the oracle on the full n=25.6M, k=25,600 step (fastest taken), "
-                         "%.2f s per call, host %s" % (tc, os.uname().machine)}
+        cpu = cpu_baseline(k)
 
     rec = {
         "metric": "gradient elements/sec sparsified (GB/s, % HBM roofline) at n=25.6M, 0.1%",
@@ -319,7 +352,9 @@ def main():
         "config": {"workload": "topk_ef_step n=25,600,000 k=25,600 (0.1%), grad 99% N(0,1e-3) + 1% "
                                "Laplace(0,0.1) (16 seeded GPU draws), residual from prior EF steps, "
                                "inputs resident in HBM",
-                   "n": N, "k": k, "density": DENSITY},
+                   "n": N, "k": k, "density": DENSITY,
+                   "residual": "5 prior EF steps at 0.1%% from 0 (a distinct buffer per timed step for the first %d)"
+                               % sets},
         "gbps_step": gbps_step,
         "roofline_frac_step": gbps_step / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "achieved": gbps_main, "peak": HBM_PEAK_GBPS, "unit": "GB/s",

@@ -36,12 +36,26 @@
  *   - `workspace` is caller-owned device memory of at least the size the
  *     matching *_workspace_bytes() query returns.  One workspace serves one
  *     call at a time; calls that share a workspace must be ordered (same
- *     stream).  Its first 32 KB carry state from one call to the next
- *     (synchronisation counters that every call leaves at zero, route
- *     counters): a new workspace must be zero-filled, and the caller must
- *     not write to it between calls.  Any
- *     of the three operations may use a workspace after any other.  The rest
- *     is scratch.
+ *     stream).  Its first 32 KB (the header) hold the device error word and
+ *     the synchronisation state of the top-k kernels; the rest is scratch.
+ *     A workspace is ready after tgs_workspace_init() (a kernel, so it may
+ *     sit in a captured graph) or after being zero-filled, and every call
+ *     leaves it ready for the next one, on the host's order or replayed
+ *     from a graph: the library keeps no state on the host.  Between calls
+ *     the caller must not write to the header.  Any of the operations may
+ *     use a workspace after any other.
+ *   - Device error word (the header's first word): kernels only set bits in
+ *     it, so it collects every problem since it was last read;
+ *     tgs_check_device_error() reads and clears it.  After a report other
+ *     than bad merge input, run tgs_workspace_init() before the next call.
+ *   - Residency: the top-k kernels that synchronise their workgroups through
+ *     memory (k_step, k_general) size their grid to what fits on the device
+ *     at once and assume every workgroup runs concurrently.  Kernels running
+ *     on other streams at the same time can keep workgroups from starting;
+ *     the waits are bounded, so the call then ends with wrong outputs and the
+ *     wait-timeout bit (0x2) in the device error word, never a hang.  Run
+ *     the top-k step on a device (or stream priority class) it has to itself,
+ *     or check the error word.
  *   - Magnitude order: key(x) = bits(x) & 0x7FFFFFFF as an unsigned integer.
  *     This matches |x| for every non-NaN value, ranks NaN above infinity and
  *     makes -0 and +0 equal.  Among equal keys the lower index comes first.
@@ -66,7 +80,7 @@ typedef int32_t tgs_status;
 #define TGS_EINVAL (-1)     /* bad size, null pointer, overlapping buffers, bad lambda */
 #define TGS_EWORKSPACE (-2) /* workspace smaller than the query returned             */
 #define TGS_EHIP (-3)       /* a HIP launch failed; see tgs_last_error()              */
-#define TGS_EDEVICE (-4)    /* a kernel flagged bad input (tgs_check_device_error)    */
+#define TGS_EDEVICE (-4)    /* a kernel flagged a wait timeout or inconsistent counts */
 
 /* Bytes of workspace tgs_topk_ef_step needs for this (n, k).  0 if the sizes
    are invalid. */
@@ -74,9 +88,10 @@ size_t tgs_topk_workspace_bytes(int64_t n, int64_t k);
 
 /*
  * Error-feedback top-k step ([EF], [CONV]; the selection replaces the full
- * sort that [SORT] identifies as the bottleneck).  For k up to ~48k (and
- * n >= 2^18) it is one kernel launch that reads grad and residual once; other
- * sizes take an exact radix-select path.  Both give the same result.
+ * sort that [SORT] identifies as the bottleneck).  For k up to ~48k and
+ * n >= 2^19 it is one kernel launch that reads grad and residual once;
+ * n <= 2^18 with k <= 256 is one launch too; other sizes take an exact
+ * radix-select path (three launches).  Every route gives the same result.
  *   grad      [n] float32, read only.
  *   residual  [n] float32, in/out: on entry the accumulated error, on exit
  *             acc with the selected entries set to +0.0f.
@@ -155,9 +170,18 @@ tgs_status tgs_gtopk_merge(const int32_t* idx, const float* val, int32_t P, int6
                            int32_t* out_idx, float* out_val, uint8_t* out_mask, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
 
-/* Waits for `stream`, then reads the error word a previous call left in
-   `workspace` (TGS_OK or TGS_EDEVICE).  Works for all three workspaces. */
+/* Waits for `stream`, then reads and clears the device error word of
+   `workspace`: TGS_OK if no kernel flagged a problem since it was last read,
+   TGS_EINVAL if a merge row broke the index precondition, TGS_EDEVICE for a
+   wait that timed out or inconsistent counts.  Works for every workspace.
+   Synchronous: not for use inside graph capture. */
 tgs_status tgs_check_device_error(const void* workspace, hipStream_t stream);
+
+/* Makes `workspace` ready for any operation: zero-fills its header (the first
+   min(workspace_bytes, 32 KB) bytes) with a kernel on `stream`.  Needed once
+   for memory that is not zero-filled (and after a TGS_EDEVICE report); the
+   calls themselves keep the workspace ready. */
+tgs_status tgs_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static text for a status code. */
 const char* tgs_status_string(tgs_status s);
@@ -165,52 +189,6 @@ const char* tgs_status_string(tgs_status s);
 /* Thread-local description of the last failure on the calling thread ("" if
    none). */
 const char* tgs_last_error(void);
-
-/*
- * Test and profiling controls (process-wide; not thread-safe against
- * concurrent calls).
- *   TGS_OPT_TOPK_PATH   0 = automatic, 1 = always the exact general path,
- *                       2 = fast path with a sample plan that cannot hold
- *                       (exercises the on-device fallback),
- *                       3 = fast path whose workgroups keep no local list
- *                       while streaming (every workgroup re-reads its rows),
- *                       4 = fast path whose workgroups keep every entry in
- *                       their local list (it overflows; they re-read),
- *                       5 = fast path whose workgroups may publish only one
- *                       candidate each (the plan fails; on-device fallback),
- *                       6 = fast path with one fixed slot per bucket and
- *                       workgroup (nearly every candidate goes through the
- *                       overflow area),
- *                       7 = guided general path whose guessed bin is the
- *                       highest one sampled (the guess fails; the general
- *                       path reads acc again),
- *                       8 = guided general path whose candidate regions
- *                       hold one pair (they overflow; the general path reads
- *                       acc again),
- *                       9 = guided general path (the accumulate pass copies
- *                       out the candidates of a sampled first-level bin)
- *                       where the fast path would otherwise run.
- *                       The guided path needs n >= 2^18, grad and residual
- *                       equally aligned modulo 16 bytes and k > 0; otherwise
- *                       7-9 run the plain general path.
- *   TGS_OPT_MAIN_GRID   0 = automatic, else the number of workgroups of the
- *                       streaming launch, capped at what can be resident;
- *                       below 65 the exact path runs (results must not
- *                       depend on it).
- */
-#define TGS_OPT_TOPK_PATH 1
-#define TGS_OPT_MAIN_GRID 2
-tgs_status tgs_set_option(int32_t option, int64_t value);
-
-/* One-shot profiling hook: the next tgs_topk_ef_step call records `start`
-   right before its first launch and `stop` right after its last (the whole
-   step); the next tgs_threshold_ef_step call brackets its streaming pass.
-   Both on the call's stream.  Pass null events to clear. */
-tgs_status tgs_profile_next_call(hipEvent_t start, hipEvent_t stop);
-
-/* Milliseconds between two events recorded through tgs_profile_next_call
-   (waits for `stop`).  TGS_EHIP if either has not completed. */
-tgs_status tgs_profile_elapsed_ms(hipEvent_t start, hipEvent_t stop, float* ms);
 
 #ifdef __cplusplus
 }

@@ -15,7 +15,7 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
 def run_both(tgs, idx, val, n):
-    gi, gv, gm = tgs.gtopk_merge(gpu(idx), gpu(val), n)
+    gi, gv, gm = tgs.gtopk_merge(gpu(idx), gpu(val), n, check=True)
     ei, ev, em = oracle.gtopk_merge(idx, val, n)
     return (host(gi), host(gv), host(gm)), (ei, ev, em)
 
@@ -29,7 +29,8 @@ def assert_merge_equal(got, exp, what):
 def test_golden(tgs_gpu):
     g = json.load(open(os.path.join(GOLDEN, "gtopk_tournament.json")))
     for case in g["cases"]:
-        gi, gv, gm = tgs_gpu.gtopk_merge(gpu(np.array(case["idx"], np.int32)), gpu(np.float32(case["val"])), case["n"])
+        gi, gv, gm = tgs_gpu.gtopk_merge(gpu(np.array(case["idx"], np.int32)), gpu(np.float32(case["val"])), case["n"],
+                                         check=True)
         assert host(gi).tolist() == case["gidx"], case["name"]
         assert np.array_equal(bits(host(gv)), bits(case["gval"])), case["name"]
         assert host(gm).tolist() == case["mask"], case["name"]
@@ -87,18 +88,18 @@ def test_identical_supports(tgs_gpu):
     P, k = 32, 1000
     idx = np.tile(np.arange(0, 3 * k, 3, dtype=np.int32), (P, 1))
     val = np.full((P, k), 0.375, np.float32)
-    gi, gv, gm = tgs_gpu.gtopk_merge(gpu(idx), gpu(val), 3 * k)
+    gi, gv, gm = tgs_gpu.gtopk_merge(gpu(idx), gpu(val), 3 * k, check=True)
     assert np.all(host(gv) == np.float32(12.0)) and np.all(host(gm) == 1)
 
 
 def test_bad_rows_raise(tgs_gpu):
     idx = np.array([[1, 1, 2], [3, 4, 5]], np.int32)
     val = np.ones((2, 3), np.float32)
-    with pytest.raises(tgs_gpu.TgsError):
-        tgs_gpu.gtopk_merge(gpu(idx), gpu(val), 10)
+    with pytest.raises(ValueError):
+        tgs_gpu.gtopk_merge(gpu(idx), gpu(val), 10, check=True)
     idx = np.array([[1, 2, 12], [3, 4, 5]], np.int32)
-    with pytest.raises(tgs_gpu.TgsError):
-        tgs_gpu.gtopk_merge(gpu(idx), gpu(val), 10)
-    # a good call afterwards clears the error word
+    with pytest.raises(ValueError):
+        tgs_gpu.gtopk_merge(gpu(idx), gpu(val), 10, check=True)
+    # the check cleared the error word: a good call afterwards reports nothing
     idx = np.array([[1, 2, 7], [3, 4, 5]], np.int32)
-    tgs_gpu.gtopk_merge(gpu(idx), gpu(val), 10)
+    tgs_gpu.gtopk_merge(gpu(idx), gpu(val), 10, check=True)

@@ -1,6 +1,7 @@
 """The C-ABI library on the CPU: it loads, exports every symbol include/tgs.h
 declares, sizes workspaces, and rejects bad arguments before touching the GPU."""
 import ctypes
+import glob
 import os
 import re
 import subprocess
@@ -9,11 +10,12 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "tgs.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 LIB = os.path.join(ROOT, "top_gradient_sparsification_amd", "libtgs.so")
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(tgs_[a-z_0-9]+)\s*\(", text)))
 
@@ -44,7 +46,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_header_compiles_as_c():
-    src = '#include "tgs.h"\nint main(void){ return (int)sizeof(tgs_status); }\n'
+    src = '#include "tgs.h"\n#include "tgs_testing.h"\nint main(void){ return (int)sizeof(tgs_status); }\n'
     proc = subprocess.run(["gcc", "-x", "c", "-std=c99", "-fsyntax-only", "-I", os.path.dirname(HEADER),
                            "-I", "/opt/rocm/include", "-D__HIP_PLATFORM_AMD__", "-"], input=src,
                           capture_output=True, text=True)

@@ -44,7 +44,9 @@ _STATUS_EXC = {TGS_EINVAL: ValueError, TGS_EWORKSPACE: MemoryError}
 
 
 class TgsError(RuntimeError):
-    """Raised for TGS_EHIP and TGS_EDEVICE."""
+    """Raised for TGS_EHIP and TGS_EDEVICE (a bounded wait timed out or
+    counts were inconsistent: the outputs of the calls since the error word was
+    last read are not to be used)."""
 
     def __init__(self, status: int, message: str):
         super().__init__(message)
@@ -88,6 +90,8 @@ def _load():
         lib.tgs_gtopk_merge.restype = i32
         lib.tgs_check_device_error.argtypes = [vp, vp]
         lib.tgs_check_device_error.restype = i32
+        lib.tgs_workspace_init.argtypes = [vp, sz, vp]
+        lib.tgs_workspace_init.restype = i32
         lib.tgs_status_string.argtypes = [i32]
         lib.tgs_status_string.restype = ctypes.c_char_p
         lib.tgs_last_error.argtypes = []
@@ -123,15 +127,27 @@ def _ptr(t) -> int | None:
     return t.data_ptr() if t is not None and t.numel() > 0 else None
 
 
-def _require(t, dtype, name):
+def _full_device(device) -> torch.device:
+    """``device`` with its index filled in ("cuda" -> the current device)."""
+    dev = torch.device(device)
+    if dev.type == "cuda" and dev.index is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
+    return dev
+
+
+def _require(t, dtype, name, device=None, min_numel=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
     if t.dtype != dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
     if not t.is_cuda:
         raise TypeError("%s must be a GPU tensor" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError("%s holds %d entries, needs %d" % (name, t.numel(), min_numel))
 
 
 # --------------------------------------------------------------- workspaces --
@@ -140,9 +156,9 @@ _ws_lock = threading.Lock()
 
 
 def workspace(kind: str, nbytes: int, device) -> torch.Tensor:
-    """A zero-initialised uint8 device buffer of at least ``nbytes``, cached per
-    (device, current stream, kind).  Calls that share it are ordered on that
-    stream."""
+    """A zero-initialised (hence ready) uint8 device buffer of at least
+    ``nbytes``, cached per (device, current stream, kind).  Calls that share it
+    are ordered on that stream."""
     dev = torch.device(device)
     key = (dev.index, _stream_handle(dev), kind)
     with _ws_lock:
@@ -193,17 +209,36 @@ def topk_ef_step(grad: torch.Tensor, residual: torch.Tensor, k: int, out_idx=Non
     return out_idx[:k], out_val[:k]
 
 
+def workspace_init(ws: torch.Tensor, stream=None):
+    """Makes ``ws`` ready for any operation (a kernel zero-fills its header on
+    the current stream): for workspaces not allocated zero-filled, and after a
+    TGS_EDEVICE report."""
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda:
+        raise TypeError("ws must be a GPU tensor")
+    st = stream.cuda_stream if stream is not None else _stream_handle(ws.device)
+    _check(_load().tgs_workspace_init(ws.data_ptr(), ws.numel() * ws.element_size(), st), "tgs_workspace_init")
+
+
+def error_word(ws: torch.Tensor) -> torch.Tensor:
+    """The device error word of workspace ``ws`` as a one-element int32 device
+    tensor (a view: no copy, no wait).  Nonzero means a kernel flagged a
+    problem since the word was last cleared by ``check_device_error``."""
+    return ws[:4].view(torch.int32)
+
+
 class TopkStep:
     """A prepared top-k step for repeated calls on tensors of one shape.
 
     Holds the outputs, the workspace and the stream, so a call costs one C-ABI
-    call plus pointer reads: for training loops that sparsify the same buffer
-    every iteration.  The library still validates every call."""
+    call plus a few attribute checks: for training loops that sparsify the same
+    buffer every iteration.  The library still validates every call.  Calls
+    are asynchronous: ``check()`` (or ``error`` for a device-side flag) reports
+    whether a kernel flagged a problem."""
 
     def __init__(self, n: int, k: int, device="cuda", stream=None):
         lib = _load()
         self.n, self.k = int(n), int(k)
-        self.device = torch.device(device)
+        self.device = _full_device(device)
         need = lib.tgs_topk_workspace_bytes(self.n, self.k)
         if need == 0:
             raise ValueError("invalid sizes n=%d k=%d" % (n, k))
@@ -216,13 +251,25 @@ class TopkStep:
                       self.ws.data_ptr(), self.ws.numel(), self.stream.cuda_stream)
 
     def __call__(self, grad: torch.Tensor, residual: torch.Tensor):
-        if grad.numel() != self.n or residual.numel() != self.n:
-            raise ValueError("this step is prepared for n=%d" % self.n)
+        for t, name in ((grad, "grad"), (residual, "residual")):
+            if (t.dtype != torch.float32 or t.device != self.device or t.numel() != self.n
+                    or not t.is_contiguous()):
+                _require(t, torch.float32, name, self.device)
+                raise ValueError("this step is prepared for n=%d, %s holds %d" % (self.n, name, t.numel()))
         oi, ov, wp, wn, st = self._args
         status = self._fn(grad.data_ptr(), residual.data_ptr(), self.n, self.k, oi, ov, wp, wn, st)
         if status:
             _check(status, "tgs_topk_ef_step")
         return self.out_idx, self.out_val
+
+    @property
+    def error(self) -> torch.Tensor:
+        """The workspace's device error word (int32 device tensor, no wait)."""
+        return error_word(self.ws)
+
+    def check(self):
+        """Waits for the stream and raises if a kernel flagged a problem."""
+        _check(_load().tgs_check_device_error(self.ws.data_ptr(), self.stream.cuda_stream), "tgs_topk_ef_step")
 
 
 def _segment_table(offsets, ks):
@@ -285,7 +332,7 @@ class TopkSegments:
         self.nseg, self.offsets, self.ks = _segment_table(offsets, ks)
         self.n = int(self.offsets[-1]) if self.nseg else 0
         self.total = int(self.ks.sum()) if self.nseg else 0
-        self.device = torch.device(device)
+        self.device = _full_device(device)
         need = lib.tgs_topk_segmented_workspace_bytes(self.nseg, self.offsets.ctypes.data, self.ks.ctypes.data)
         if need == 0:
             raise ValueError("invalid segment table")
@@ -298,13 +345,26 @@ class TopkSegments:
                       self.out_val.data_ptr(), self.ws.data_ptr(), self.ws.numel(), self.stream.cuda_stream)
 
     def __call__(self, grad: torch.Tensor, residual: torch.Tensor):
-        if grad.numel() != self.n or residual.numel() != self.n:
-            raise ValueError("this step is prepared for n=%d" % self.n)
+        for t, name in ((grad, "grad"), (residual, "residual")):
+            if (t.dtype != torch.float32 or t.device != self.device or t.numel() != self.n
+                    or not t.is_contiguous()):
+                _require(t, torch.float32, name, self.device)
+                raise ValueError("this call is prepared for n=%d, %s holds %d" % (self.n, name, t.numel()))
         ns, op, kp, oi, ov, wp, wn, st = self._args
         status = self._fn(grad.data_ptr(), residual.data_ptr(), ns, op, kp, oi, ov, wp, wn, st)
         if status:
             _check(status, "tgs_topk_ef_step_segmented")
         return self.out_idx[:self.total], self.out_val[:self.total]
+
+    @property
+    def error(self) -> torch.Tensor:
+        """The workspace's device error word (int32 device tensor, no wait)."""
+        return error_word(self.ws)
+
+    def check(self):
+        """Waits for the stream and raises if a kernel flagged a problem."""
+        _check(_load().tgs_check_device_error(self.ws.data_ptr(), self.stream.cuda_stream),
+               "tgs_topk_ef_step_segmented")
 
 
 def threshold_workspace_bytes(n: int) -> int:
@@ -327,12 +387,17 @@ def threshold_ef_step(grad: torch.Tensor, residual: torch.Tensor, lam: float, ca
         raise ValueError("grad and residual must have the same length and device")
     dev = grad.device
     capacity = int(capacity)
+    if capacity < 0:
+        raise ValueError("capacity must be >= 0")
     if out_idx is None:
-        out_idx = torch.empty(max(capacity, 0), dtype=torch.int32, device=dev)
+        out_idx = torch.empty(capacity, dtype=torch.int32, device=dev)
     if out_val is None:
-        out_val = torch.empty(max(capacity, 0), dtype=torch.float32, device=dev)
+        out_val = torch.empty(capacity, dtype=torch.float32, device=dev)
     if count is None:
         count = torch.empty(1, dtype=torch.int64, device=dev)
+    _require(out_idx, torch.int32, "out_idx", dev, capacity)
+    _require(out_val, torch.float32, "out_val", dev, capacity)
+    _require(count, torch.int64, "count", dev, 1)
     lib = _load()
     need = lib.tgs_threshold_workspace_bytes(n)
     if need == 0:
@@ -351,12 +416,13 @@ def gtopk_workspace_bytes(P: int, k: int, n: int) -> int:
 
 
 def gtopk_merge(idx: torch.Tensor, val: torch.Tensor, n: int, ws: torch.Tensor | None = None,
-                check: bool = True):
+                check: bool = False):
     """gTop-k tournament of the P rows of ``idx``/``val`` (shape [P, k]).
 
-    Returns ``(gidx int32[k], gval float32[k], mask uint8[P, k])``.  With
-    ``check`` the call waits for the device and raises if a row broke the
-    index precondition (distinct indices inside [0, n))."""
+    Returns ``(gidx int32[k], gval float32[k], mask uint8[P, k])``,
+    asynchronously.  With ``check`` the call also waits for the device and
+    raises ValueError if a row broke the index precondition (distinct indices
+    inside [0, n)); otherwise ``check_device_error(ws)`` reports it later."""
     _require(idx, torch.int32, "idx")
     _require(val, torch.float32, "val")
     if idx.dim() != 2 or idx.shape != val.shape:
@@ -381,7 +447,9 @@ def gtopk_merge(idx: torch.Tensor, val: torch.Tensor, n: int, ws: torch.Tensor |
 
 
 def check_device_error(ws: torch.Tensor):
-    """Waits for the current stream and raises if a kernel flagged bad input."""
+    """Waits for the current stream, then reads and clears the workspace's
+    device error word: raises ValueError for bad merge input, TgsError for a
+    wait timeout or inconsistent counts."""
     lib = _load()
     _check(lib.tgs_check_device_error(ws.data_ptr(), _stream_handle(ws.device)), "tgs_check_device_error")
 
@@ -411,8 +479,9 @@ def profile_elapsed_ms(start_event, stop_event) -> float:
 
 
 __all__ = [
-    "TopkStep", "topk_ef_step", "threshold_ef_step", "gtopk_merge", "topk_workspace_bytes", "threshold_workspace_bytes",
-    "gtopk_workspace_bytes", "check_device_error", "set_option", "profile_next_call", "profile_elapsed_ms",
-    "library", "workspace",
+    "TopkStep", "TopkSegments", "topk_ef_step", "topk_ef_step_segmented", "threshold_ef_step", "gtopk_merge",
+    "topk_workspace_bytes", "topk_segmented_workspace_bytes", "threshold_workspace_bytes",
+    "gtopk_workspace_bytes", "check_device_error", "error_word", "workspace_init", "set_option",
+    "profile_next_call", "profile_elapsed_ms", "library", "workspace",
     "TgsError", "OPT_TOPK_PATH", "OPT_MAIN_GRID", "LIB_PATH",
 ]

@@ -2,11 +2,9 @@
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
-#include <map>
-#include <mutex>
-#include <utility>
 
 #include "tgs_host.h"
+#include "tgs_internal.h"
 
 namespace tgs {
 
@@ -26,13 +24,15 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-static std::atomic<int64_t> g_opt_path{0};
-static std::atomic<int64_t> g_opt_grid{0};
+// Test and profiling controls: per calling thread, so calls on other threads
+// never see them.
+static thread_local int64_t t_opt_path = 0;
+static thread_local int64_t t_opt_grid = 0;
 
 int64_t get_option(int32_t option) {
   switch (option) {
-    case TGS_OPT_TOPK_PATH: return g_opt_path.load();
-    case TGS_OPT_MAIN_GRID: return g_opt_grid.load();
+    case TGS_OPT_TOPK_PATH: return t_opt_path;
+    case TGS_OPT_MAIN_GRID: return t_opt_grid;
     default: return 0;
   }
 }
@@ -48,36 +48,17 @@ int device_cu_count() {
   return v;
 }
 
-// Launch parity per (device, workspace): which of the top-k control block's
-// two counter sets the next fast-path launch on that workspace uses.
-static std::mutex g_parity_mu;
-static std::map<std::pair<int, uintptr_t>, uint32_t> g_parity;
-
-static std::pair<int, uintptr_t> parity_key(const void* workspace) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
-  return {dev, (uintptr_t)workspace};
-}
-
-uint32_t launch_parity(const void* workspace) {
-  std::lock_guard<std::mutex> lk(g_parity_mu);
-  auto it = g_parity.find(parity_key(workspace));
-  return it == g_parity.end() ? 0u : it->second;
-}
-
-void advance_parity(const void* workspace) {
-  std::lock_guard<std::mutex> lk(g_parity_mu);
-  g_parity[parity_key(workspace)] ^= 1u;
-}
-
-static std::mutex g_prof_mu;
-static hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
+static thread_local hipEvent_t t_prof_start = nullptr, t_prof_stop = nullptr;
 
 void take_profile_events(hipEvent_t* start, hipEvent_t* stop) {
-  std::lock_guard<std::mutex> lk(g_prof_mu);
-  *start = g_prof_start;
-  *stop = g_prof_stop;
-  g_prof_start = g_prof_stop = nullptr;
+  *start = t_prof_start;
+  *stop = t_prof_stop;
+  t_prof_start = t_prof_stop = nullptr;
+}
+
+// Zero-fills the workspace header (words [0, nwords)).
+__global__ void k_workspace_init(u32* ws, u32 nwords) {
+  for (u32 i = blockIdx.x * blockDim.x + threadIdx.x; i < nwords; i += gridDim.x * blockDim.x) ws[i] = 0u;
 }
 
 }  // namespace tgs
@@ -101,11 +82,11 @@ extern "C" tgs_status tgs_set_option(int32_t option, int64_t value) {
   switch (option) {
     case TGS_OPT_TOPK_PATH:
       if (value < 0 || value > 9) return fail(TGS_EINVAL, "TGS_OPT_TOPK_PATH takes 0 .. 9");
-      g_opt_path.store(value);
+      t_opt_path = value;
       return TGS_OK;
     case TGS_OPT_MAIN_GRID:
       if (value < 0) return fail(TGS_EINVAL, "TGS_OPT_MAIN_GRID must be >= 0");
-      g_opt_grid.store(value);
+      t_opt_grid = value;
       return TGS_OK;
     default: return fail(TGS_EINVAL, "unknown option %d", (int)option);
   }
@@ -113,9 +94,8 @@ extern "C" tgs_status tgs_set_option(int32_t option, int64_t value) {
 
 extern "C" tgs_status tgs_profile_next_call(hipEvent_t start, hipEvent_t stop) {
   if ((start == nullptr) != (stop == nullptr)) return fail(TGS_EINVAL, "profile events: pass both or neither");
-  std::lock_guard<std::mutex> lk(g_prof_mu);
-  g_prof_start = start;
-  g_prof_stop = stop;
+  t_prof_start = start;
+  t_prof_stop = stop;
   return TGS_OK;
 }
 
@@ -134,6 +114,28 @@ extern "C" tgs_status tgs_check_device_error(const void* workspace, hipStream_t 
   uint32_t word = 0;
   e = hipMemcpy(&word, workspace, sizeof word, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return fail(TGS_EHIP, "check_device_error: %s", hipGetErrorString(e));
-  if (word != 0) return fail(TGS_EDEVICE, "device error word 0x%x (bit0 bad merge input, bit1 grid barrier timeout, bit2 inconsistent counts)", word);
+  if (word == 0) return TGS_OK;
+  // reported once: the word is cleared for the calls that follow
+  const uint32_t zero = 0;
+  e = hipMemcpy((void*)workspace, &zero, sizeof zero, hipMemcpyHostToDevice);
+  if (e != hipSuccess) return fail(TGS_EHIP, "check_device_error: %s", hipGetErrorString(e));
+  if (word == kErrBadMergeInput)
+    return fail(TGS_EINVAL, "device error word 0x%x: a merge row holds an index outside [0, n) or a repeated index",
+                word);
+  return fail(TGS_EDEVICE,
+              "device error word 0x%x (bit0 bad merge input, bit1 wait timed out: the grid was not all resident, "
+              "bit2 inconsistent counts); re-initialise the workspace before its next use",
+              word);
+}
+
+extern "C" tgs_status tgs_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!workspace) return fail(TGS_EINVAL, "workspace_init: null workspace");
+  if (((uintptr_t)workspace & 3u) != 0) return fail(TGS_EINVAL, "workspace_init: workspace not 4-byte aligned");
+  const size_t bytes = workspace_bytes < kWorkspaceHeader ? workspace_bytes : kWorkspaceHeader;
+  const u32 nwords = (u32)(bytes / 4);
+  if (nwords == 0) return TGS_OK;
+  hipLaunchKernelGGL(k_workspace_init, dim3((nwords + 255) / 256), dim3(256), 0, stream, (u32*)workspace, nwords);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TGS_EHIP, "workspace_init: launch failed: %s", hipGetErrorString(e));
   return TGS_OK;
 }

@@ -443,10 +443,6 @@ __global__ void k_gt_mask(const int32_t* __restrict__ idx, int64_t total, const 
   mask[t] = (lo < k && sorted0[lo].idx == x) ? 1 : 0;
 }
 
-__global__ void k_gt_clear_err(u32* err) {
-  if (threadIdx.x == 0 && blockIdx.x == 0) *err = 0u;
-}
-
 __global__ void k_gt_copy(const Pair* __restrict__ src, Pair* __restrict__ dst, int64_t len) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < len) dst[i] = src[i];
@@ -507,7 +503,6 @@ extern "C" tgs_status tgs_gtopk_merge(const int32_t* idx, const float* val, int3
   const int64_t total = (int64_t)P * k;
   const unsigned eb = (unsigned)((total + 255) / 256);
 
-  hipLaunchKernelGGL(k_gt_clear_err, dim3(1), dim3(64), 0, stream, err);
   hipLaunchKernelGGL(k_gt_load_rows, dim3(eb), dim3(256), 0, stream, idx, val, slots, total);
   Pair* sorted = sort_segments<ByIdx>(slots, tmp, k, P, stream);
   if (sorted != slots) hipLaunchKernelGGL(k_gt_copy, dim3(eb), dim3(256), 0, stream, sorted, slots, total);

@@ -1,5 +1,5 @@
 // Host-side helpers of the sparsifier library: error reporting, argument
-// checks, process-wide options and the one-shot profiling hook.
+// checks, the per-thread test options and the one-shot profiling hook.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "tgs.h"
+#include "tgs_testing.h"
 
 namespace tgs {
 
@@ -20,13 +21,6 @@ int64_t get_option(int32_t option);
 
 // Compute units of the current device (cached per device; 0 on failure).
 int device_cu_count();
-
-// Which of the top-k control block's two counter sets the next fast-path
-// launch on `workspace` (current device) uses; advance_parity flips it after a
-// launch went out.  A workspace the library has not seen starts at 0 (both
-// sets of a zero-filled workspace are clean).
-uint32_t launch_parity(const void* workspace);
-void advance_parity(const void* workspace);
 
 // Hands out (and clears) the events set by tgs_profile_next_call; null when
 // none are pending.

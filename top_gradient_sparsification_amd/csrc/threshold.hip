@@ -49,7 +49,6 @@ struct ThrArgs {
   float* out_val;
   int64_t capacity;
   int64_t* d_count;
-  u32* err;      // device error word (cleared by k_thr_pass)
 };
 
 // Walks this workgroup's chunk in index order.  For each tile, `load(i, bits[4],
@@ -210,10 +209,7 @@ __global__ __launch_bounds__(kThrThreads) void k_thr_pass(ThrArgs a) {
       }
     };
     const int64_t total = ordered_walk(a, load, put, s_wt);
-    if (tid == 0) {
-      a.cnt[blockIdx.x] = (u32)total;
-      if (blockIdx.x == 0) *a.err = 0u;
-    }
+    if (tid == 0) a.cnt[blockIdx.x] = (u32)total;
     return;
   }
   // vector mode: the partition of ordered_walk (which the emit pass's rescan
@@ -287,10 +283,7 @@ __global__ __launch_bounds__(kThrThreads) void k_thr_pass(ThrArgs a) {
     load(t + 3, gb, rb);
   }
   if (blockIdx.x == G - 1 && tail0 < a.n) scalar_tile(tail0, a.n - tail0);
-  if (tid == 0) {
-    a.cnt[blockIdx.x] = running;
-    if (blockIdx.x == 0) *a.err = 0u;
-  }
+  if (tid == 0) a.cnt[blockIdx.x] = running;
 }
 
 __global__ __launch_bounds__(kThrThreads) void k_thr_emit(ThrArgs a) {
@@ -431,7 +424,6 @@ extern "C" tgs_status tgs_threshold_ef_step(const float* grad, float* residual, 
     a.out_val = out_val;
     a.capacity = capacity;
     a.d_count = d_count;
-    a.err = (u32*)ws;
     hipEvent_t ev0, ev1;
     take_profile_events(&ev0, &ev1);
     if (ev0) (void)hipEventRecord(ev0, stream);

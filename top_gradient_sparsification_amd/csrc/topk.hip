@@ -35,15 +35,21 @@
 //   finish   finisher f waits for every workgroup, adds up the bucket counts,
 //            checks that the plan held (at least k candidates, every bucket
 //            that holds a rank below k fits in LDS, nothing overflowed),
-//            gathers bucket f, orders it by (key desc, index asc) and writes
-//            the entries of rank < k to the output.  The finisher that holds
-//            rank k-1 publishes its composite key R.
-//   zero     each streaming workgroup sets to +0 the residual of those of its
-//            own candidates whose composite key is <= R.  It wrote their acc
-//            itself, so its own two stores reach memory in order.
-// No residual word is written by two workgroups and everything one
-// workgroup reads from another goes through device-scope atomics, so the
-// fast path needs no cache write-back fences.
+//            gathers bucket f, orders it by (key desc, index asc), writes the
+//            entries of rank < k to the output and stores +0 to their
+//            residual.  Every acc store of every streaming workgroup completed
+//            at device scope before that workgroup arrived, so the zero lands
+//            after the acc it replaces.
+// Everything one workgroup reads from another is written with device-scope
+// stores or atomics and read with device-scope loads, so the fast path needs
+// no cache write-back fences.
+//
+// State between launches: the control block holds two counter sets and a
+// parity word saying which one the next launch uses.  Every workgroup reads
+// the parity when it starts; workgroup 0 clears the other set, and once every
+// workgroup has arrived at the sample phase (so has read the parity) it flips
+// the word.  A launch therefore finds its set clean whatever launched before
+// it, on the host or replayed from a graph, and nothing is kept on the host.
 //
 // When the plan did not hold, residual already holds acc everywhere: the
 // grid fences, meets at a barrier and runs the exact general path below.
@@ -55,6 +61,7 @@
 //   order (ties at the k-th key resolved by index), a stable LSD radix sort of
 //   the k entries by descending key (4 x 8-bit digits), then emit and zero.
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cstring>
 #include <type_traits>
@@ -148,7 +155,7 @@ __device__ __forceinline__ void flag_set(Counter* f, u64 v) {
 }
 
 // Start of every top-k workspace.  Launches alternate between the two
-// counter sets (the host passes the parity); workgroup 0 of each launch
+// counter sets (the parity word says which); workgroup 0 of each launch
 // clears the set the next launch uses, which no one else touches meanwhile.
 struct StepCtl {
   u32 err;        // device error word (offset 0 of every workspace)
@@ -159,7 +166,7 @@ struct StepCtl {
   u32 rescans;    // workgroup shares re-read because their list was incomplete (never reset)
   u32 guided_used;    // guided general-path calls that selected from the copied candidates (never reset)
   u32 guided_missed;  // guided calls whose guess or regions did not hold: acc read again (never reset)
-  u32 small_done;     // (unused)
+  u32 parity;         // counter set the next k_step launch uses (flipped by each launch)
   u32 pad1[55];
   StepSet set[2];
   Plan plan;
@@ -1062,7 +1069,7 @@ __device__ __forceinline__ void general_path(const GenArgs& a) {
 
 // ---------------------------------------------------------- k_acc_pass ----
 // acc = residual + grad written back to residual; the general path then runs
-// on it.  Workgroup 0 clears the general-path state and the error word.
+// on it.  Workgroup 0 clears the general-path state.
 struct AccArgs {
   const float* grad;
   float* residual;
@@ -1071,7 +1078,6 @@ struct AccArgs {
   int64_t nv;    // float4 vectors in the aligned part
   u32* zero_ptr;
   int zero_words;
-  u32* err;
   u32* hist_rows;  // [gridDim.x][2048]: each workgroup's first-level histogram
 };
 
@@ -1081,10 +1087,8 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_pass(AccArgs a) {
   __shared__ u32 s_h[2048];  // first-level histogram of this workgroup's keys (key >> 20)
   const int tid = threadIdx.x;
   for (int i = tid; i < 2048; i += NT) s_h[i] = 0;
-  if (blockIdx.x == 0) {
+  if (blockIdx.x == 0)
     for (int i = tid; i < a.zero_words; i += NT) a.zero_ptr[i] = 0u;
-    if (tid == 0) *a.err = 0u;
-  }
   __syncthreads();
   const float* __restrict__ g = a.grad;
   float* __restrict__ r = a.residual;
@@ -1229,7 +1233,6 @@ struct GuidedArgs {
   int64_t nv;    // float4 vectors in the aligned part
   u32* zero_ptr;
   int zero_words;
-  u32* err;
   u32* hist_rows;      // [gridDim.x][2048]
   const StepCtl* ctl;  // guide_bin
   u32* guide_ovf;      // set when a region overflowed
@@ -1245,10 +1248,8 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_guided(GuidedArgs a) {
   const int tid = threadIdx.x, lane = lane_id();
   for (int i = tid; i < 2048; i += NT) s_h[i] = 0;
   if (tid == 0) s_cnt = 0;
-  if (blockIdx.x == 0) {
+  if (blockIdx.x == 0)
     for (int i = tid; i < a.zero_words; i += NT) a.zero_ptr[i] = 0u;
-    if (tid == 0) *a.err = 0u;
-  }
   const u32 gbin = a.ctl->guide_bin;
   const bool guide = gbin != kNoGuide;  // the same in every thread
   __syncthreads();
@@ -1365,7 +1366,6 @@ struct SmallArgs {
   float* residual;
   int32_t* out_idx;
   float* out_val;
-  u32* err;
   u32* done;  // [nseg] arrival counters, zero on entry, left zero
   u64* cand;  // [gridDim.x][kSmallMaxK]
   int nseg;
@@ -1496,7 +1496,6 @@ __global__ __launch_bounds__(kSmallThreads) void k_small(SmallArgs a) {
   const u32 kk = std::min<u32>(S.k, len);
   const float* __restrict__ g = a.grad + S.start;
   float* __restrict__ res = a.residual + S.start;
-  if (b == 0 && tid == 0) *a.err = 0u;
   {
     float gq[EPT], rq[EPT];
 #pragma unroll
@@ -1586,7 +1585,6 @@ struct StepArgs {
   u32 loc_mode;                  // test hook: 1 = T_loc above every key, 2 = T_loc = 0
   u32 region_cap;                // candidates one workgroup may publish (no limit; less to test)
   u32 slot_log;                  // each workgroup has S = 2^slot_log slots per bucket
-  u32 parity;                    // which counter set this launch uses
   StepCtl* ctl;
   u32* pub;      // [kMaxStepBlocks][kPubCap] keys, then [kMaxStepBlocks] count | floor << 16
   u32* rcnt;     // [kMaxStepBlocks][kMaxBuckets / 2] bucket counts, two u16 per word
@@ -1642,7 +1640,7 @@ __device__ __forceinline__ void publish_plan(StepCtl* ctl, StepSet* cs, u32 vali
 //   is exact when b_T lies at or above every workgroup's floor (all bins
 //   from the highest floor up were published in full); otherwise the keys
 //   are interpolated inside their bins.  The plan is a guess either way.
-__device__ __forceinline__ void step_plan(const StepArgs& a, u32* s_raw, u32* s_scan) {
+__device__ __forceinline__ void step_plan(const StepArgs& a, u32 par, u32* s_raw, u32* s_scan) {
   constexpr int NT = kStepThreads;
   constexpr int NW = kStepWaves;
   constexpr int per = kHistBins / NT;  // 4 bins per thread, top first
@@ -1661,9 +1659,12 @@ __device__ __forceinline__ void step_plan(const StepArgs& a, u32* s_raw, u32* s_
   const int w = tid / kWave;
   const int G = gridDim.x;
   StepCtl* ctl = a.ctl;
-  StepSet* cs = &ctl->set[a.parity];
+  StepSet* cs = &ctl->set[par];
   if (tid == 0) {
     s_ok = phase_wait(&cs->samp_all, G, &ctl->err) ? 1u : 0u;
+    // every workgroup has read the parity (its arrival used it): the next
+    // launch takes the other set, cleared at this launch's start
+    st_agent(&ctl->parity, par ^ 1u);
     s_maxfloor = 0;
     s_kmax = 0;
     s_bT = 0xFFFFFFFFu;
@@ -1876,7 +1877,7 @@ __device__ __forceinline__ void step_plan(const StepArgs& a, u32* s_raw, u32* s_
 
 // Finisher f (workgroups 0..63), once every workgroup has published: the
 // verdict, then bucket f.  Returns false when the plan did not hold.
-__device__ __forceinline__ bool step_finish(const StepArgs& a, u32* s_raw, u32* s_scan) {
+__device__ __forceinline__ bool step_finish(const StepArgs& a, u32 par, u32* s_raw, u32* s_scan) {
   constexpr int NT = kStepThreads;
   constexpr int NW = kStepWaves;
   constexpr int kWords = kMaxBuckets / 2;                // count words per workgroup (two u16)
@@ -1902,7 +1903,7 @@ __device__ __forceinline__ bool step_finish(const StepArgs& a, u32* s_raw, u32* 
   const int G = gridDim.x;
   const u32 slog = a.slot_log, S = 1u << slog;
   StepCtl* ctl = a.ctl;
-  StepSet* cs = &ctl->set[a.parity];
+  StepSet* cs = &ctl->set[par];
   __syncthreads();  // s_raw changes role
   // The plan is final before any workgroup publishes (every streaming
   // workgroup waited for it), so it is read while waiting for the others.
@@ -2122,6 +2123,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
   __shared__ u32 s_npairs;
   __shared__ u32 s_pstate[2];      // plan polling state, by iteration parity
   __shared__ bool s_plan_in_lds;
+  __shared__ u32 s_par;
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int w = tid / kWave;
@@ -2129,7 +2131,10 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
   const int b = blockIdx.x;
   const int M = G - 1, m = b - 1;  // streaming workgroups and this one's rank among them
   StepCtl* ctl = a.ctl;
-  StepSet* cs = &ctl->set[a.parity];
+  // the counter set of this launch: issued first, so waiting for it does not
+  // wait for the data loads behind it
+  u32 par_ld = 0;
+  if (tid == 0) par_ld = ld_agent(&ctl->parity);
   float* __restrict__ r = a.residual;
   const float* __restrict__ g = a.grad;
   const v4f* __restrict__ gv = (const v4f*)(g + a.head);
@@ -2194,15 +2199,15 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
       s_npairs = 0;
       s_plan_in_lds = false;
     }
-    if (b == 0) {  // the exact path's state and the error word start at zero; the
-                   // other counter set is cleared for the next launch
+    if (b == 0)  // the exact path's state starts at zero
       for (int i = tid; i < a.gstate_words; i += NT) st_agent(&a.gstate[i], 0u);
-      if (tid == 0) st_agent(&ctl->err, 0u);
+    if (tid == 0) s_par = par_ld & 1u;
+    __syncthreads();
+    if (b == 0) {  // the other counter set is cleared for the next launch
       constexpr int kSetWords = (int)(sizeof(StepSet) / sizeof(Counter));
-      Counter* other = (Counter*)&ctl->set[a.parity ^ 1u];
+      Counter* other = (Counter*)&ctl->set[s_par ^ 1u];
       if (tid < kSetWords) st_agent64(&other[tid].v, 0u);
     }
-    __syncthreads();
 #pragma unroll
     for (int j = 0; j < kSampleRounds; ++j) {
       if (!sok[j]) continue;
@@ -2229,6 +2234,8 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
     }
     __syncthreads();
   }
+  const u32 par = s_par;
+  StepSet* const cs = &ctl->set[par];
   // Publishes the sample keys of bins >= floor and their count: first those
   // of bins above the floor bin (fewer than pub_want, so they always fit),
   // then those of the floor bin while kPubCap allows.  A workgroup that had
@@ -2276,7 +2283,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
     // ---------------- plan ----------------
     sample_publish();
     sample_arrive();
-    step_plan(a, s_raw, s_scan);
+    step_plan(a, par, s_raw, s_scan);
     __syncthreads();
     if (tid == 0 && phase_arrive(cs->main_grp, &cs->main_all, G)) flag_set(cs->main_go, 1u);
   } else {
@@ -2580,7 +2587,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
   // ---------------- finish ----------------
   u32 verdict;
   if (b < kMaxBuckets) {
-    verdict = step_finish(a, s_raw, s_scan) ? 1u : 2u;
+    verdict = step_finish(a, par, s_raw, s_scan) ? 1u : 2u;
   } else {
     if (tid == 0) s_flag = flag_wait(&cs->verdict_flag[blockIdx.x & 7], &ctl->err);
     __syncthreads();
@@ -2603,20 +2610,35 @@ using namespace tgs;
 
 namespace {
 
-// Workgroups k_step may use on the current device: one per compute unit (its
-// LDS allows no more), never above kMaxStepBlocks.  0 if unknown.
-int step_capacity() {
-  static int cache[64];
+// Workgroups of `kernel` (NT threads) that fit on the current device at once,
+// at most `cap`: resident workgroups per compute unit times the compute units.
+// Cached per device (and kernel, through the caller's cache); 0 if unknown.
+template <class K>
+int resident_capacity(std::atomic<int>* cache, K kernel, int NT, int cap) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cache[dev] == 0) {
+  int v = cache[dev].load();
+  if (v == 0) {
     int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_step, kStepThreads, 0) != hipSuccess) occ = 0;
-    const int cus = device_cu_count();
-    cache[dev] = std::max(0, std::min(kMaxStepBlocks, occ * cus));
-    if (cache[dev] == 0) cache[dev] = -1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, NT, 0) != hipSuccess) occ = 0;
+    v = std::max(0, std::min(cap, occ * device_cu_count()));
+    if (v == 0) v = -1;
+    cache[dev].store(v);
   }
-  return cache[dev] > 0 ? cache[dev] : 0;
+  return v > 0 ? v : 0;
+}
+
+// Workgroups k_step may use: one per compute unit (its LDS allows no more),
+// never above kMaxStepBlocks.
+int step_capacity() {
+  static std::atomic<int> cache[64];
+  return resident_capacity(cache, k_step, kStepThreads, kMaxStepBlocks);
+}
+
+// Workgroups of k_general, every one resident (grid barriers).
+int general_capacity() {
+  static std::atomic<int> cache[64];
+  return resident_capacity(cache, k_general, kGenThreads, kGenBlocks);
 }
 
 // Sampling and sizing of the fast path for (n, k) on G workgroups; false when
@@ -2721,7 +2743,6 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
     m.residual = residual;
     m.out_idx = out_idx;
     m.out_val = out_val;
-    m.err = &ctl->err;
     m.done = ctl->seg_done;
     m.cand = (u64*)(ws + L.small);
     m.nseg = 1;
@@ -2765,7 +2786,6 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
     // every candidate goes to the overflow area)
     sa.slot_log = 0;
     while (path != 6 && ((int64_t)G << (sa.slot_log + 1)) <= kSlotTotal) ++sa.slot_log;
-    sa.parity = launch_parity(workspace);
     sa.ctl = ctl;
     sa.pub = (u32*)(ws + L.pub);
     sa.rcnt = (u32*)(ws + L.rcnt);
@@ -2776,7 +2796,6 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
     sa.gen = ga;
     sa.gen.bar.nwg = (u32)G;
     hipLaunchKernelGGL(k_step, dim3(G), dim3(kStepThreads), 0, stream, sa);
-    if (hipPeekAtLastError() == hipSuccess) advance_parity(workspace);
   } else {
     AccArgs aa{};
     aa.grad = grad;
@@ -2786,7 +2805,6 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
     aa.nv = nv;
     aa.zero_ptr = (u32*)gs;
     aa.zero_words = (int)(sizeof(GenState) / sizeof(u32));
-    aa.err = &ctl->err;
     const int64_t units = vec ? nv : n;
     const int64_t per = (int64_t)kAccThreads * (vec ? 2 : 8);
     int G1 = (int)std::max<int64_t>(1, std::min<int64_t>(kMaxAccBlocks, (units + per - 1) / per));
@@ -2797,15 +2815,8 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
     int G2 = 0;
     if (k > 0) {
       // every workgroup of k_general must be resident at once (grid barriers)
-      static int occ = 0;
-      if (occ == 0) {
-        int o = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, k_general, kGenThreads, 0) != hipSuccess || o < 1) o = 1;
-        occ = o;
-      }
-      const int cus = device_cu_count();
-      if (cus <= 0) return fail(TGS_EHIP, "topk_ef_step: cannot read the compute-unit count");
-      G2 = std::max(1, std::min(kGenBlocks, cus * occ));
+      G2 = general_capacity();
+      if (G2 <= 0) return fail(TGS_EHIP, "topk_ef_step: cannot read the device's resident capacity");
     }
     // The guided accumulate pass copies the candidates out while it streams,
     // so k_general need not read acc again: it takes one region per
@@ -2840,7 +2851,6 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
       g.nv = nv;
       g.zero_ptr = aa.zero_ptr;
       g.zero_words = aa.zero_words;
-      g.err = aa.err;
       g.hist_rows = aa.hist_rows;
       g.ctl = ctl;
       g.guide_ovf = &ctl->guide_ovf;
@@ -2957,7 +2967,6 @@ extern "C" tgs_status tgs_topk_ef_step_segmented(const float* grad, float* resid
   m.residual = residual;
   m.out_idx = out_idx;
   m.out_val = out_val;
-  m.err = &ctl->err;
   m.done = ctl->seg_done;
   u64* lists = (u64*)(ws + L.lists);
   u32 wg = 0;

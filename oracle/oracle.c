@@ -24,6 +24,20 @@
  *           and Method: global top-k of the largest absolute values across P
  *           workers, found by a tournament of O(log P) pairwise rounds; only the
  *           globally selected indices keep their index information.
+ *   [EST]   arxivdaily listing, entry "Near-Optimal Sparse Allreduce for
+ *           Distributed Deep Learning" (Ok-Topk picks the top-k gradients
+ *           through an estimated threshold rather than a sort); fugumt page
+ *           for arXiv 2502.07634, related-paper entry "An Efficient
+ *           Statistical-based Gradient Compression Technique for Distributed
+ *           Training Systems" (SIDCo: threshold sparsification whose threshold
+ *           estimate is as good as DGC's) and its Abstract (DGC scales better
+ *           than top-k, whose sorting costs offset the communication saved).
+ *   [RTOPK] arxivdaily listing, entry "rTop-k: A Statistical Estimation
+ *           Approach to Distributed SGD": a sparsifier that chains top-k and
+ *           random-k, i.e. a random subset of the largest entries.
+ *   [PHILOX] Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers: As Easy
+ *           as 1, 2, 3" (SC'11): the Philox4x32-10 counter-based generator,
+ *           which supplies rTop-k's random draws.
  *
  * Readings where the pages are silent (each listed in the design notes):
  *   - acc = residual + grad, one binary32 add, round-to-nearest-even, no
@@ -39,6 +53,14 @@
  *     slot s + 2^r; coinciding indices have their values added in binary32;
  *     the k largest by (key desc, index asc) survive; a slot with no partner
  *     passes through.
+ *   - threshold estimate: the q-th largest key(acc) over m sampled positions
+ *     (given by the caller, repeats allowed); the hard threshold then keeps
+ *     every entry whose key reaches it.
+ *   - rTop-k: the top r by (key desc, index asc), then the k of them with the
+ *     smallest (u_i, i), u_i = word 0 of Philox4x32-10 at counter
+ *     (i, step low, step high, 0) under key (seed low, seed high): a uniform
+ *     random k-subset.  Emitted in (key desc, index asc) order; every entry
+ *     not emitted, the r - k left out included, keeps acc in the residual.
  */
 #include <stdint.h>
 #include <stdlib.h>
@@ -123,11 +145,22 @@ int oracle_topk_ef_step(const float* grad, float* residual, int64_t n, int64_t k
  * (including qualifying ones past the capacity) keeps residual_i = acc_i.
  * Returns the total number of qualifying entries, or -1 for invalid input.
  */
+int64_t oracle_threshold_ef_step_key(const float* grad, float* residual, int64_t n, uint32_t klam,
+                                     int32_t* out_idx, float* out_val, int64_t capacity);
+
 int64_t oracle_threshold_ef_step(const float* grad, float* residual, int64_t n, float lambda,
                                  int32_t* out_idx, float* out_val, int64_t capacity) {
-  if (n < 0 || n > 0x7FFFFFFF || capacity < 0 || !(lambda >= 0.0f)) return -1;
+  if (!(lambda >= 0.0f)) return -1;
+  return oracle_threshold_ef_step_key(grad, residual, n, mag_key(lambda), out_idx, out_val, capacity);
+}
+
+/* The same step for a threshold given as its magnitude key (any value of
+   bits & 0x7FFFFFFF; a key above infinity's is a NaN payload, which only NaNs
+   of a larger or equal payload reach). */
+int64_t oracle_threshold_ef_step_key(const float* grad, float* residual, int64_t n, uint32_t klam,
+                                     int32_t* out_idx, float* out_val, int64_t capacity) {
+  if (n < 0 || n > 0x7FFFFFFF || capacity < 0 || klam > 0x7FFFFFFFu) return -1;
   unsigned int mode = ieee_enter();
-  uint32_t klam = mag_key(lambda);
   int64_t count = 0;
   for (int64_t i = 0; i < n; ++i) {
     float acc = add_f32(residual[i], grad[i]);
@@ -146,6 +179,140 @@ int64_t oracle_threshold_ef_step(const float* grad, float* residual, int64_t n, 
   }
   ieee_leave(mode);
   return count;
+}
+
+/* ------------------------- threshold estimate ----------------------------- */
+
+static int cmp_u32_desc(const void* a, const void* b) {
+  uint32_t x = *(const uint32_t*)a, y = *(const uint32_t*)b;
+  return (x < y) - (x > y);
+}
+
+/*
+ * Threshold estimate ([EST]): the q-th largest magnitude key among the accs at
+ * m sampled positions.
+ *   key_j   = key(residual[s_j] + grad[s_j]) for j < m (s_j in [0, n); a
+ *             position may repeat and then counts as often as it appears)
+ *   *key_out = the q-th entry of the key_j sorted in descending order
+ * Feeding *key_out to the hard threshold keeps about q/m of the entries.
+ * Reads grad and residual only.  Returns 0, -1 for invalid input (n < 1,
+ * m < 1, q outside [1, m], a position outside [0, n)), -2 if memory runs out.
+ */
+int oracle_threshold_estimate(const float* grad, const float* residual, int64_t n, const int32_t* sample_idx,
+                              int64_t m, int64_t q, uint32_t* key_out) {
+  if (n < 1 || n > 0x7FFFFFFF || m < 1 || q < 1 || q > m) return -1;
+  for (int64_t j = 0; j < m; ++j)
+    if (sample_idx[j] < 0 || (int64_t)sample_idx[j] >= n) return -1;
+  uint32_t* k = (uint32_t*)malloc((size_t)m * sizeof(uint32_t));
+  if (!k) return -2;
+  unsigned int mode = ieee_enter();
+  for (int64_t j = 0; j < m; ++j) {
+    int32_t i = sample_idx[j];
+    k[j] = mag_key(add_f32(residual[i], grad[i]));
+  }
+  qsort(k, (size_t)m, sizeof(uint32_t), cmp_u32_desc);
+  *key_out = k[q - 1];
+  ieee_leave(mode);
+  free(k);
+  return 0;
+}
+
+/* ------------------------------ Philox --------------------------------- */
+
+/*
+ * Philox4x32-10 ([PHILOX]): a 128-bit counter (c0..c3) is put through ten
+ * rounds under a 64-bit key (k0, k1).  A round multiplies c0 and c2 by the
+ * two round multipliers (0xD2511F53, 0xCD9E8D57) to 64-bit products; the new
+ * counter is (high(c2 product) ^ c1 ^ k0, low(c2 product),
+ * high(c0 product) ^ c3 ^ k1, low(c0 product)).  Between rounds the key words
+ * grow by the Weyl constants 0x9E3779B9 and 0xBB67AE85.
+ */
+void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+  uint32_t k0 = key[0], k1 = key[1];
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    uint64_t p0 = (uint64_t)0xD2511F53u * (uint64_t)c0;
+    uint64_t p2 = (uint64_t)0xCD9E8D57u * (uint64_t)c2;
+    uint32_t n0 = (uint32_t)(p2 >> 32) ^ c1 ^ k0;
+    uint32_t n1 = (uint32_t)p2;
+    uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    uint32_t n3 = (uint32_t)p0;
+    c0 = n0;
+    c1 = n1;
+    c2 = n2;
+    c3 = n3;
+  }
+  out[0] = c0;
+  out[1] = c1;
+  out[2] = c2;
+  out[3] = c3;
+}
+
+/* rTop-k's draw for entry i: Philox word 0 at counter (i, step low, step
+   high, 0) under key (seed low, seed high). */
+static uint32_t rtopk_draw(uint64_t seed, uint64_t step, uint32_t i) {
+  uint32_t ctr[4] = {i, (uint32_t)step, (uint32_t)(step >> 32), 0u};
+  uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  uint32_t out[4];
+  oracle_philox4x32_10(ctr, key, out);
+  return out[0];
+}
+
+/* ------------------------------- rTop-k -------------------------------- */
+
+/*
+ * rTop-k step with error feedback ([RTOPK] with [EF]).
+ *   acc_i  = residual_i + grad_i
+ *   R      = the first r indices in (key(acc) desc, index asc) order
+ *   S      = the k members i of R with the smallest (u_i, i), u_i the draw of
+ *            entry i for (seed, step)
+ *   out    = S in (key desc, index asc) order, out_val = acc there (bitwise)
+ *   residual_i = +0.0f for i in S, acc_i otherwise
+ * Returns 0, -1 for invalid sizes (0 <= k <= r <= n), -2 if memory runs out.
+ */
+int oracle_rtopk_ef_step(const float* grad, float* residual, int64_t n, int64_t r, int64_t k, uint64_t seed,
+                         uint64_t step, int32_t* out_idx, float* out_val) {
+  if (n < 0 || n > 0x7FFFFFFF || r < 0 || r > n || k < 0 || k > r) return -1;
+  if (n == 0) return 0;
+  float* acc = (float*)malloc((size_t)n * sizeof(float));
+  uint64_t* order = (uint64_t*)malloc((size_t)n * sizeof(uint64_t));
+  uint64_t* draw = (uint64_t*)malloc((size_t)(r > 0 ? r : 1) * sizeof(uint64_t));
+  unsigned char* picked = (unsigned char*)calloc((size_t)n, 1);
+  if (!acc || !order || !draw || !picked) { free(acc); free(order); free(draw); free(picked); return -2; }
+  unsigned int mode = ieee_enter();
+
+  for (int64_t i = 0; i < n; ++i) acc[i] = add_f32(residual[i], grad[i]);
+  for (int64_t i = 0; i < n; ++i) order[i] = rank_key(mag_key(acc[i]), (uint32_t)i);
+  qsort(order, (size_t)n, sizeof(uint64_t), cmp_u64);
+  /* R = order[0 .. r); the k smallest (u, i) among them */
+  for (int64_t j = 0; j < r; ++j) {
+    uint32_t i = (uint32_t)(order[j] & 0xFFFFFFFFu);
+    draw[j] = ((uint64_t)rtopk_draw(seed, step, i) << 32) | (uint64_t)i;
+  }
+  qsort(draw, (size_t)r, sizeof(uint64_t), cmp_u64);
+  for (int64_t j = 0; j < k; ++j) picked[draw[j] & 0xFFFFFFFFu] = 1;
+  /* emitted in R's order, which is (key desc, index asc) */
+  int64_t e = 0;
+  for (int64_t j = 0; j < r; ++j) {
+    int32_t i = (int32_t)(order[j] & 0xFFFFFFFFu);
+    if (picked[i]) {
+      out_idx[e] = i;
+      out_val[e] = acc[i];
+      e += 1;
+    }
+  }
+  for (int64_t i = 0; i < n; ++i) residual[i] = picked[i] ? 0.0f : acc[i];
+
+  ieee_leave(mode);
+  free(acc);
+  free(order);
+  free(draw);
+  free(picked);
+  return 0;
 }
 
 /* ---------------------------- gTop-k merge -------------------------------- */

@@ -402,3 +402,163 @@ def test_merge_rejects_bad_rows(oracle_lib):
         oracle_lib.gtopk_merge(idx, val, 10)
     with pytest.raises(ValueError):
         oracle_lib.gtopk_merge(np.array([[0, 10]], np.int32), np.ones((1, 2), np.float32), 10)
+
+
+# ------------------------------------------------------ threshold estimate --
+def test_golden_threshold_estimate(oracle_lib):
+    g = json.load(open(os.path.join(GOLDEN, "threshold_estimate.json")))
+    grad, res = f32(g["grad"]), f32(g["residual"])
+    sample = np.array(g["sample"], np.int32)
+    for case in g["cases"]:
+        r = res.copy()
+        assert oracle_lib.threshold_estimate(grad, r, sample, case["q"]) == int(case["key"], 16)
+        idx, val, count, key = oracle_lib.estimated_threshold_ef_step(grad, r, sample, case["q"], 8)
+        assert key == int(case["key"], 16) and count == case["count"]
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_threshold_estimate_count_characterisation(oracle_lib, seed):
+    """Brute force on tiny inputs: the estimate is a sampled key v with
+    #{j : key_j > v} < q <= #{j : key_j >= v} (the q-th largest, counted with
+    repeats), computed with numpy's binary32 add and no sort."""
+    rng = np.random.default_rng(900 + seed)
+    n = int(rng.integers(1, 40))
+    grad = tie_heavy(rng, n) if seed % 2 else rng.standard_normal(n).astype(np.float32)
+    res = tie_heavy(rng, n)
+    m = int(rng.integers(1, 50))
+    sample = rng.integers(0, n, m).astype(np.int32)
+    sk = [int(x) for x in keys((res + grad)[sample])]
+    for q in range(1, m + 1):
+        v = oracle_lib.threshold_estimate(grad, res, sample, q)
+        assert v in sk
+        assert sum(1 for x in sk if x > v) < q <= sum(1 for x in sk if x >= v)
+
+
+def test_threshold_estimate_closed_forms(oracle_lib):
+    n = 1000
+    # all-equal magnitudes: the estimate is that magnitude for every q
+    grad = np.where(np.arange(n) % 3 == 0, -0.375, 0.375).astype(np.float32)
+    sample = np.arange(0, n, 7, dtype=np.int32)
+    for q in (1, 5, sample.size):
+        assert oracle_lib.threshold_estimate(grad, np.zeros(n, np.float32), sample, q) == int(keys(f32(0.375)))
+    # the sampled accs are a permutation of 1..m: the q-th largest is m - q + 1
+    m = 200
+    rng = np.random.default_rng(5)
+    perm = rng.permutation(m) + 1
+    sample = rng.choice(n, m, replace=False).astype(np.int32)
+    grad = rng.standard_normal(n).astype(np.float32)
+    grad[sample] = perm.astype(np.float32)
+    for q in (1, 2, 50, 200):
+        assert oracle_lib.threshold_estimate(grad, np.zeros(n, np.float32), sample, q) == int(keys(f32(m - q + 1)))
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_full_sample_estimate_is_the_topk_threshold(oracle_lib, seed):
+    """Sampling every position with q = k: the hard threshold then keeps
+    exactly the top-k set of the (separately pinned) top-k oracle, plus any
+    ties at the k-th key."""
+    rng = np.random.default_rng(70 + seed)
+    n, k = 5000, 37 + 40 * seed
+    grad = rng.standard_normal(n).astype(np.float32) if seed < 3 else tie_heavy(rng, n)
+    res = rng.standard_normal(n).astype(np.float32)
+    r1, r2 = res.copy(), res.copy()
+    idx, val, count, key = oracle_lib.estimated_threshold_ef_step(grad, r1, np.arange(n, dtype=np.int32), k, n)
+    ti, tv = oracle_lib.topk_ef_step(grad, r2, k)
+    acc = res + grad
+    assert key == int(keys(acc)[ti[-1]])
+    assert count == int(np.sum(keys(acc) >= key)) >= k
+    assert set(ti.tolist()) <= set(idx.tolist())
+    if count == k:
+        assert np.array_equal(np.sort(ti), idx) and np.array_equal(bits(r1), bits(r2))
+
+
+def test_threshold_estimate_special_values_and_rejects(oracle_lib):
+    grad = f32([np.nan, 1.0, -np.inf, 0.5, -0.0])
+    res = np.zeros(5, np.float32)
+    s = np.arange(5, dtype=np.int32)
+    assert oracle_lib.threshold_estimate(grad, res, s, 1) == int(keys(f32(np.nan)))  # NaN above inf
+    assert oracle_lib.threshold_estimate(grad, res, s, 2) == 0x7F800000
+    assert oracle_lib.threshold_estimate(grad, res, s, 5) == 0  # -0 has key 0
+    # a NaN-payload threshold keeps only the NaN
+    idx, val, count, key = oracle_lib.estimated_threshold_ef_step(grad, res.copy(), s, 1, 5)
+    assert count == 1 and idx.tolist() == [0]
+    for q in (0, 6):
+        with pytest.raises(ValueError):
+            oracle_lib.threshold_estimate(grad, res, s, q)
+    with pytest.raises(ValueError):
+        oracle_lib.threshold_estimate(grad, res, np.array([0, 5], np.int32), 1)
+
+
+# ----------------------------------------------------------------- rTop-k --
+def test_golden_philox_known_answers(oracle_lib):
+    g = json.load(open(os.path.join(GOLDEN, "philox_kat.json")))
+    for case in g["cases"]:
+        out = oracle_lib.philox4x32_10([int(x, 16) for x in case["ctr"]], [int(x, 16) for x in case["key"]])
+        assert [int(x) for x in out] == [int(x, 16) for x in case["out"]]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_rtopk_with_r_equal_k_is_topk(oracle_lib, seed):
+    rng = np.random.default_rng(300 + seed)
+    n = 3000
+    grad = rng.standard_normal(n).astype(np.float32) if seed % 2 else tie_heavy(rng, n)
+    res = rng.standard_normal(n).astype(np.float32)
+    for k in (0, 1, 17, 400, n):
+        r1, r2 = res.copy(), res.copy()
+        ri, rv = oracle_lib.rtopk_ef_step(grad, r1, k, k, 1234 + seed, seed)
+        ti, tv = oracle_lib.topk_ef_step(grad, r2, k)
+        assert np.array_equal(ri, ti) and np.array_equal(bits(rv), bits(tv)) and np.array_equal(bits(r1), bits(r2))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_rtopk_picks_the_smallest_draws_of_the_top_r(oracle_lib, seed):
+    """The k emitted entries are the members of the top r (from the pinned
+    top-k oracle) with the smallest (draw, index), the draw being Philox word
+    0 at counter (index, step low, step high, 0) under key (seed low, seed
+    high); in (key desc, index asc) order; residual +0 there, acc elsewhere."""
+    rng = np.random.default_rng(500 + seed)
+    n = 4000
+    grad = rng.standard_normal(n).astype(np.float32) if seed % 2 else tie_heavy(rng, n)
+    res = rng.standard_normal(n).astype(np.float32)
+    r, k = 64 + 50 * seed, 10 + 7 * seed
+    s64, t64 = int(rng.integers(0, 2**63)) * 2 + 1, int(rng.integers(0, 2**40))
+    rr = res.copy()
+    idx, val = oracle_lib.rtopk_ef_step(grad, rr, r, k, s64, t64)
+    top_i, _ = oracle_lib.topk_ef_step(grad, res.copy(), r)
+    key2 = [s64 & 0xFFFFFFFF, s64 >> 32]
+
+    def draw(i):
+        return int(oracle_lib.philox4x32_10([i, t64 & 0xFFFFFFFF, t64 >> 32, 0], key2)[0])
+
+    want = sorted(top_i.tolist(), key=lambda i: (draw(i), i))[:k]
+    assert sorted(idx.tolist()) == sorted(want)
+    pos = {int(i): p for p, i in enumerate(top_i)}
+    assert [pos[int(i)] for i in idx] == sorted(pos[int(i)] for i in idx)  # the top-r list's order
+    acc = res + grad
+    assert np.array_equal(bits(val), bits(acc[idx]))
+    sel = np.zeros(n, bool)
+    sel[idx] = True
+    assert np.all(bits(rr)[sel] == 0) and np.array_equal(bits(rr)[~sel], bits(acc)[~sel])
+
+
+def test_rtopk_subset_is_uniform(oracle_lib):
+    """Over 2000 steps each of the top r = 16 is picked (k = 4) with frequency
+    k / r = 0.25 within 5 standard deviations: the draws select a uniform
+    random subset, not a fixed or index-biased one."""
+    n, r, k, T = 64, 16, 4, 2000
+    grad = (np.arange(n, dtype=np.float32) + 1.0)[::-1].copy()  # top 16 are indices 0..15
+    counts = np.zeros(r)
+    for t in range(T):
+        idx, _ = oracle_lib.rtopk_ef_step(grad, np.zeros(n, np.float32), r, k, 0xC0FFEE, t)
+        assert idx.max() < r
+        counts[idx] += 1
+    p = k / r
+    sd = math.sqrt(p * (1 - p) / T)
+    assert np.all(np.abs(counts / T - p) < 5 * sd), counts / T
+
+
+def test_rtopk_rejects_bad_sizes(oracle_lib):
+    g = np.ones(10, np.float32)
+    for r, k in ((11, 1), (3, 4), (-1, 0), (5, -1)):
+        with pytest.raises(ValueError):
+            oracle_lib.rtopk_ef_step(g, np.zeros(10, np.float32), r, k, 1, 1)

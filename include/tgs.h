@@ -23,6 +23,15 @@
  *           Top-k Sparsification for Low Bandwidth Networks", ABSTRACT and
  *           Method: global top-k of the largest |values| over P workers by an
  *           O(log P)-round tournament; only the selected indices survive.
+ *   [EST]   arxivdaily listing, entry "Near-Optimal Sparse Allreduce for
+ *           Distributed Deep Learning" (top-k picked through an estimated
+ *           threshold rather than a sort); fugumt page for arXiv 2502.07634,
+ *           related-paper entry "An Efficient Statistical-based Gradient
+ *           Compression Technique for Distributed Training Systems"
+ *           (threshold sparsification with an estimated threshold) and its
+ *           Abstract (top-k's sorting costs offset what it saves).
+ *   [RTOPK] arxivdaily listing, entry "rTop-k: A Statistical Estimation
+ *           Approach to Distributed SGD": random-k chained after top-k.
  *
  * Conventions shared by every entry point
  *   - Array arguments are DEVICE pointers owned by the caller; the library
@@ -149,6 +158,62 @@ tgs_status tgs_threshold_ef_step(const float* grad, float* residual, int64_t n, 
                                  int64_t* d_count, void* workspace, size_t workspace_bytes,
                                  hipStream_t stream);
 
+/* Bytes of workspace tgs_threshold_estimate needs for m samples (0 if m is
+   outside [1, 2^24]).  A workspace of the larger of this and
+   tgs_threshold_workspace_bytes(n) serves both calls of an estimated step. */
+size_t tgs_threshold_estimate_workspace_bytes(int64_t m);
+
+/*
+ * Threshold estimate from a sample ([EST]), for the hard-threshold step.
+ *   sample_idx [m] int32, device: positions in [0, n) (repeats allowed), for
+ *             example drawn uniformly by the caller; 1 <= m <= 2^24.
+ *   q         1 <= q <= m: the estimate is the q-th largest of
+ *             key(residual[s_j] + grad[s_j]) over j < m (ties counted), so a
+ *             target density rho takes q = ceil(rho * m).
+ *   d_lambda  device float, out: the float whose bits are that key (>= 0).
+ * grad and residual are only read.  A position outside [0, n) sets the
+ * bad-input bit of the device error word (the estimate is then unspecified).
+ * One launch; intended for m up to ~2^20 (its last workgroup reads the m keys
+ * once more).  The workspace must be 16-byte aligned.
+ */
+tgs_status tgs_threshold_estimate(const float* grad, const float* residual, int64_t n, const int32_t* sample_idx,
+                                  int64_t m, int64_t q, float* d_lambda, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
+/*
+ * tgs_threshold_ef_step with the threshold read on the device ([HT] fed by
+ * [EST]): an entry qualifies when key(acc_i) >= key(*d_lambda), read when the
+ * kernels run (so tgs_threshold_estimate may write it earlier on the same
+ * stream, with no host round trip).  Any bit pattern is accepted: the key of
+ * a negative value is that of its magnitude; a NaN's key is only reached by
+ * NaNs of at least its payload.  Everything else as tgs_threshold_ef_step.
+ */
+tgs_status tgs_threshold_ef_step_dev(const float* grad, float* residual, int64_t n, const float* d_lambda,
+                                     int32_t* out_idx, float* out_val, int64_t capacity, int64_t* d_count,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace tgs_rtopk_ef_step needs (0 if the sizes are invalid). */
+size_t tgs_rtopk_workspace_bytes(int64_t n, int64_t r, int64_t k);
+
+/*
+ * rTop-k step with error feedback ([RTOPK] with [EF]): k entries drawn
+ * uniformly at random from the r of largest |acc|.
+ *   0 <= k <= r <= n.  The top r are the first r by (key(acc) desc, index
+ *   asc), as tgs_topk_ef_step finds them.  Entry i draws u_i = output word 0
+ *   of Philox4x32-10 (Salmon et al., SC'11) at counter (i, step & 0xFFFFFFFF,
+ *   step >> 32, 0) under key (seed & 0xFFFFFFFF, seed >> 32); the k of the top
+ *   r with the smallest (u_i, i) are sent.
+ *   out_idx/out_val [k]: the sent entries in (key desc, index asc) order,
+ *             values bit for bit.
+ *   residual  in/out: +0.0f at the k sent, acc everywhere else (the r - k
+ *             passed over included).
+ * r = k gives tgs_topk_ef_step's result.  One more kernel follows the top-r
+ * step's launches.  Pointer and overlap rules as tgs_topk_ef_step.
+ */
+tgs_status tgs_rtopk_ef_step(const float* grad, float* residual, int64_t n, int64_t r, int64_t k, uint64_t seed,
+                             uint64_t step, int32_t* out_idx, float* out_val, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
 /* Bytes of workspace tgs_gtopk_merge needs (0 if the sizes are invalid). */
 size_t tgs_gtopk_workspace_bytes(int32_t P, int64_t k, int64_t n);
 
@@ -172,7 +237,8 @@ tgs_status tgs_gtopk_merge(const int32_t* idx, const float* val, int32_t P, int6
 
 /* Waits for `stream`, then reads and clears the device error word of
    `workspace`: TGS_OK if no kernel flagged a problem since it was last read,
-   TGS_EINVAL if a merge row broke the index precondition, TGS_EDEVICE for a
+   TGS_EINVAL for an input index outside its range (a merge row's index out
+   of range or repeated, a sample position out of range), TGS_EDEVICE for a
    wait that timed out or inconsistent counts.  Works for every workspace.
    Synchronous: not for use inside graph capture. */
 tgs_status tgs_check_device_error(const void* workspace, hipStream_t stream);

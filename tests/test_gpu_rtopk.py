@@ -1,0 +1,107 @@
+"""GPU parity of the rTop-k step against the CPU oracle (bit for bit: the k
+sent pairs, in order, and the residual), through every route of its top-r
+step (small-vector kernel, single-launch step, guided general path)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _helpers import assert_topk_equal, gpu, host
+from top_gradient_sparsification_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+def make(dist, n, rng):
+    if dist == "normal":
+        return rng.standard_normal(n).astype(np.float32), rng.standard_normal(n).astype(np.float32)
+    if dist == "ties":
+        return (rng.integers(-4, 5, n) * 0.5).astype(np.float32), (rng.integers(-2, 3, n) * 0.25).astype(np.float32)
+    if dist == "mixture":
+        return workloads.mixture(n, 1e-3, 0.01, 0.1, (31, n, 1)), workloads.mixture(n, 1e-3, 0.01, 0.1, (31, n, 2))
+    raise ValueError(dist)
+
+
+def run_gpu(tgs, grad, res, r, k, seed, step):
+    g, rr = gpu(grad), gpu(res)
+    ws = torch.zeros(tgs.rtopk_workspace_bytes(grad.size, r, k), dtype=torch.uint8, device="cuda")
+    idx, val = tgs.rtopk_ef_step(g, rr, r, k, seed, step, ws=ws)
+    tgs.check_device_error(ws)
+    return host(idx), host(val), host(rr)
+
+
+def run_oracle(grad, res, r, k, seed, step):
+    rr = res.copy()
+    i, v = oracle.rtopk_ef_step(grad, rr, r, k, seed, step)
+    return i, v, rr
+
+
+@pytest.mark.parametrize("dist", ["normal", "ties", "mixture"])
+@pytest.mark.parametrize("n,rk", [(1, [(1, 1), (1, 0)]), (5, [(5, 2), (3, 3), (4, 0)]),
+                                  (1000, [(100, 10), (1000, 999), (64, 1)]),
+                                  (70_001, [(256, 100), (5000, 2500), (70_001, 7)]),
+                                  (1_000_003, [(2000, 1000), (30_000, 20_000), (60_000, 1)])])
+def test_sizes(tgs_gpu, dist, n, rk):
+    rng = np.random.default_rng(n + 11)
+    grad, res = make(dist, n, rng)
+    for r, k in rk:
+        for seed, step in ((1, 0), (0xDEADBEEF12345678, 2**40 + 3)):
+            assert_topk_equal(run_gpu(tgs_gpu, grad, res, r, k, seed, step),
+                              run_oracle(grad, res, r, k, seed, step), "%s n=%d r=%d k=%d" % (dist, n, r, k))
+
+
+def test_guided_top_r(tgs_gpu):
+    """r above the single-launch step's limit (guided general path for the
+    top r), a few thousand picked."""
+    rng = np.random.default_rng(5)
+    n = 4_194_304
+    grad, res = make("mixture", n, rng)
+    for r, k in ((120_000, 30_000), (60_000, 59_999)):
+        assert_topk_equal(run_gpu(tgs_gpu, grad, res, r, k, 77, 5), run_oracle(grad, res, r, k, 77, 5),
+                          "r=%d k=%d" % (r, k))
+
+
+def test_small_config_three_chained_steps(tgs_gpu):
+    """n = 1,048,576, N(0, 1) gradients, k = 1,048 (0.1%) of r = 2k, three
+    chained steps (step number in the counter) from a zero residual."""
+    n = 1 << 20
+    k = workloads.k_for_density(n, 0.001)
+    r_gpu = torch.zeros(n, dtype=torch.float32, device="cuda")
+    r_cpu = np.zeros(n, np.float32)
+    for step in (1, 2, 3):
+        g = workloads.grad_small(step)
+        idx, val = tgs_gpu.rtopk_ef_step(gpu(g), r_gpu, 2 * k, k, 2024, step)
+        ei, ev = oracle.rtopk_ef_step(g, r_cpu, 2 * k, k, 2024, step)
+        assert_topk_equal((host(idx), host(val), host(r_gpu)), (ei, ev, r_cpu), "step %d" % step)
+
+
+def test_resnet50_sized_chained(tgs_gpu):
+    """n = 25.6M mixture, k = 25,600 (0.1%) of r = 51,200, three chained steps
+    from a zero residual."""
+    n = 25_600_000
+    k = workloads.k_for_density(n, 0.001)
+    r_gpu = torch.zeros(n, dtype=torch.float32, device="cuda")
+    r_cpu = np.zeros(n, np.float32)
+    for step in (1, 2, 3):
+        g = workloads.grad_resnet50(step, variant=31)
+        idx, val = tgs_gpu.rtopk_ef_step(gpu(g), r_gpu, 2 * k, k, 99, step)
+        ei, ev = oracle.rtopk_ef_step(g, r_cpu, 2 * k, k, 99, step)
+        assert_topk_equal((host(idx), host(val), host(r_gpu)), (ei, ev, r_cpu), "step %d" % step)
+
+
+def test_draws_depend_on_seed_and_step_only(tgs_gpu):
+    rng = np.random.default_rng(9)
+    n = 200_000
+    grad, res = make("normal", n, rng)
+    a = run_gpu(tgs_gpu, grad, res, 4000, 400, 5, 1)
+    b = run_gpu(tgs_gpu, grad, res, 4000, 400, 5, 1)
+    c = run_gpu(tgs_gpu, grad, res, 4000, 400, 5, 2)
+    assert np.array_equal(a[0], b[0]) and not np.array_equal(a[0], c[0])
+
+
+def test_invalid_arguments(tgs_gpu):
+    g = gpu(np.ones(10, np.float32))
+    r = torch.zeros(10, dtype=torch.float32, device="cuda")
+    for rr, kk in ((11, 1), (3, 4), (-1, 0)):
+        with pytest.raises(ValueError):
+            tgs_gpu.rtopk_ef_step(g, r, rr, kk, 1, 1)

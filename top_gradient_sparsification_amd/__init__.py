@@ -15,6 +15,14 @@ Operations (cited by page title and section):
 * ``gtopk_merge``       -- the gTop-k tournament (nubint review "A Distributed
   Synchronous SGD Algorithm with Global Top-k Sparsification for Low Bandwidth
   Networks", ABSTRACT and Method).
+* ``threshold_estimate`` / ``estimated_threshold_ef_step`` -- a threshold
+  estimated from a sample, fed to the hard threshold on the device (arxivdaily
+  listing, entry "Near-Optimal Sparse Allreduce for Distributed Deep
+  Learning"; fugumt page for arXiv 2502.07634, related-paper entry "An
+  Efficient Statistical-based Gradient Compression Technique for Distributed
+  Training Systems").
+* ``rtopk_ef_step``     -- k random entries of the top r (arxivdaily listing,
+  entry "rTop-k: A Statistical Estimation Approach to Distributed SGD").
 
 There is no fallback: if ``libtgs.so`` is missing or cannot be loaded, every
 call raises.
@@ -92,6 +100,17 @@ def _load():
         lib.tgs_check_device_error.restype = i32
         lib.tgs_workspace_init.argtypes = [vp, sz, vp]
         lib.tgs_workspace_init.restype = i32
+        lib.tgs_threshold_estimate_workspace_bytes.argtypes = [i64]
+        lib.tgs_threshold_estimate_workspace_bytes.restype = sz
+        lib.tgs_threshold_estimate.argtypes = [vp, vp, i64, vp, i64, i64, vp, vp, sz, vp]
+        lib.tgs_threshold_estimate.restype = i32
+        lib.tgs_threshold_ef_step_dev.argtypes = [vp, vp, i64, vp, vp, vp, i64, vp, vp, sz, vp]
+        lib.tgs_threshold_ef_step_dev.restype = i32
+        u64 = ctypes.c_uint64
+        lib.tgs_rtopk_workspace_bytes.argtypes = [i64, i64, i64]
+        lib.tgs_rtopk_workspace_bytes.restype = sz
+        lib.tgs_rtopk_ef_step.argtypes = [vp, vp, i64, i64, i64, u64, u64, vp, vp, vp, sz, vp]
+        lib.tgs_rtopk_ef_step.restype = i32
         lib.tgs_status_string.argtypes = [i32]
         lib.tgs_status_string.restype = ctypes.c_char_p
         lib.tgs_last_error.argtypes = []
@@ -411,6 +430,125 @@ def threshold_ef_step(grad: torch.Tensor, residual: torch.Tensor, lam: float, ca
     return out_idx, out_val, count
 
 
+def threshold_estimate_workspace_bytes(m: int) -> int:
+    return int(_load().tgs_threshold_estimate_workspace_bytes(m))
+
+
+def threshold_estimate(grad: torch.Tensor, residual: torch.Tensor, sample_idx: torch.Tensor, q: int,
+                       d_lambda: torch.Tensor | None = None, ws: torch.Tensor | None = None) -> torch.Tensor:
+    """The q-th largest |residual + grad| over the positions ``sample_idx``
+    (int32 device tensor), as a one-element float32 device tensor (no host
+    round trip).  grad and residual are only read."""
+    _require(grad, torch.float32, "grad")
+    dev = grad.device
+    _require(residual, torch.float32, "residual", dev, grad.numel())
+    _require(sample_idx, torch.int32, "sample_idx", dev)
+    n, m = grad.numel(), sample_idx.numel()
+    if residual.numel() != n:
+        raise ValueError("grad and residual must have the same length")
+    if d_lambda is None:
+        d_lambda = torch.empty(1, dtype=torch.float32, device=dev)
+    _require(d_lambda, torch.float32, "d_lambda", dev, 1)
+    lib = _load()
+    need = lib.tgs_threshold_estimate_workspace_bytes(m)
+    if need == 0:
+        raise ValueError("invalid sample count m=%d" % m)
+    if ws is None:
+        ws = workspace("estimate", need, dev)
+    st = lib.tgs_threshold_estimate(_ptr(grad), _ptr(residual), n, _ptr(sample_idx), m, int(q), d_lambda.data_ptr(),
+                                    ws.data_ptr(), ws.numel(), _stream_handle(dev))
+    _check(st, "tgs_threshold_estimate")
+    return d_lambda
+
+
+def threshold_ef_step_dev(grad: torch.Tensor, residual: torch.Tensor, d_lambda: torch.Tensor, capacity: int,
+                          out_idx=None, out_val=None, count=None, ws: torch.Tensor | None = None):
+    """``threshold_ef_step`` with the threshold in device memory (a
+    one-element float32 tensor, read when the kernels run)."""
+    _require(grad, torch.float32, "grad")
+    dev = grad.device
+    _require(residual, torch.float32, "residual", dev)
+    _require(d_lambda, torch.float32, "d_lambda", dev, 1)
+    n = grad.numel()
+    if residual.numel() != n:
+        raise ValueError("grad and residual must have the same length")
+    capacity = int(capacity)
+    if capacity < 0:
+        raise ValueError("capacity must be >= 0")
+    if out_idx is None:
+        out_idx = torch.empty(capacity, dtype=torch.int32, device=dev)
+    if out_val is None:
+        out_val = torch.empty(capacity, dtype=torch.float32, device=dev)
+    if count is None:
+        count = torch.empty(1, dtype=torch.int64, device=dev)
+    _require(out_idx, torch.int32, "out_idx", dev, capacity)
+    _require(out_val, torch.float32, "out_val", dev, capacity)
+    _require(count, torch.int64, "count", dev, 1)
+    lib = _load()
+    need = lib.tgs_threshold_workspace_bytes(n)
+    if need == 0:
+        raise ValueError("invalid size n=%d" % n)
+    if ws is None:
+        ws = workspace("threshold", need, dev)
+    st = lib.tgs_threshold_ef_step_dev(_ptr(grad), _ptr(residual), n, d_lambda.data_ptr(), _ptr(out_idx),
+                                       _ptr(out_val), capacity, count.data_ptr(), ws.data_ptr(), ws.numel(),
+                                       _stream_handle(dev))
+    _check(st, "tgs_threshold_ef_step_dev")
+    return out_idx, out_val, count
+
+
+def estimated_threshold_ef_step(grad: torch.Tensor, residual: torch.Tensor, sample_idx: torch.Tensor, q: int,
+                                capacity: int, out_idx=None, out_val=None, count=None, d_lambda=None,
+                                ws: torch.Tensor | None = None):
+    """The sampled estimate, then the hard-threshold step with it, both on
+    the current stream with no host round trip.  Returns ``(idx, val, count,
+    d_lambda)`` (device tensors).  ``ws``, if given, must be large enough for
+    both calls."""
+    n, m = grad.numel(), sample_idx.numel()
+    if ws is None:
+        need = max(threshold_estimate_workspace_bytes(m), threshold_workspace_bytes(n))
+        ws = workspace("threshold", need, grad.device)
+    d_lambda = threshold_estimate(grad, residual, sample_idx, q, d_lambda=d_lambda, ws=ws)
+    idx, val, cnt = threshold_ef_step_dev(grad, residual, d_lambda, capacity, out_idx=out_idx, out_val=out_val,
+                                          count=count, ws=ws)
+    return idx, val, cnt, d_lambda
+
+
+def rtopk_workspace_bytes(n: int, r: int, k: int) -> int:
+    return int(_load().tgs_rtopk_workspace_bytes(n, r, k))
+
+
+def rtopk_ef_step(grad: torch.Tensor, residual: torch.Tensor, r: int, k: int, seed: int, step: int,
+                  out_idx=None, out_val=None, ws: torch.Tensor | None = None):
+    """One rTop-k step: k entries drawn at random (Philox4x32-10 keyed by
+    ``seed``, counter by entry index and ``step``) from the top r of
+    |residual + grad|.  ``residual`` is updated in place.  Returns ``(idx
+    int32[k], val float32[k])`` in (|acc| desc, index asc) order."""
+    _require(grad, torch.float32, "grad")
+    dev = grad.device
+    _require(residual, torch.float32, "residual", dev)
+    n = grad.numel()
+    if residual.numel() != n:
+        raise ValueError("grad and residual must have the same length")
+    r, k = int(r), int(k)
+    if out_idx is None:
+        out_idx = torch.empty(k, dtype=torch.int32, device=dev)
+    if out_val is None:
+        out_val = torch.empty(k, dtype=torch.float32, device=dev)
+    _require(out_idx, torch.int32, "out_idx", dev, k)
+    _require(out_val, torch.float32, "out_val", dev, k)
+    lib = _load()
+    need = lib.tgs_rtopk_workspace_bytes(n, r, k)
+    if need == 0:
+        raise ValueError("invalid sizes n=%d r=%d k=%d" % (n, r, k))
+    if ws is None:
+        ws = workspace("rtopk", need, dev)
+    st = lib.tgs_rtopk_ef_step(_ptr(grad), _ptr(residual), n, r, k, int(seed) & (2**64 - 1), int(step) & (2**64 - 1),
+                               _ptr(out_idx), _ptr(out_val), ws.data_ptr(), ws.numel(), _stream_handle(dev))
+    _check(st, "tgs_rtopk_ef_step")
+    return out_idx[:k], out_val[:k]
+
+
 def gtopk_workspace_bytes(P: int, k: int, n: int) -> int:
     return int(_load().tgs_gtopk_workspace_bytes(P, k, n))
 
@@ -482,6 +620,8 @@ __all__ = [
     "TopkStep", "TopkSegments", "topk_ef_step", "topk_ef_step_segmented", "threshold_ef_step", "gtopk_merge",
     "topk_workspace_bytes", "topk_segmented_workspace_bytes", "threshold_workspace_bytes",
     "gtopk_workspace_bytes", "check_device_error", "error_word", "workspace_init", "set_option",
+    "threshold_estimate", "threshold_estimate_workspace_bytes", "threshold_ef_step_dev",
+    "estimated_threshold_ef_step", "rtopk_ef_step", "rtopk_workspace_bytes",
     "profile_next_call", "profile_elapsed_ms", "library", "workspace",
     "TgsError", "OPT_TOPK_PATH", "OPT_MAIN_GRID", "LIB_PATH",
 ]

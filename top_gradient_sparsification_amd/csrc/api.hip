@@ -119,11 +119,13 @@ extern "C" tgs_status tgs_check_device_error(const void* workspace, hipStream_t 
   const uint32_t zero = 0;
   e = hipMemcpy((void*)workspace, &zero, sizeof zero, hipMemcpyHostToDevice);
   if (e != hipSuccess) return fail(TGS_EHIP, "check_device_error: %s", hipGetErrorString(e));
-  if (word == kErrBadMergeInput)
-    return fail(TGS_EINVAL, "device error word 0x%x: a merge row holds an index outside [0, n) or a repeated index",
+  if (word == kErrBadInput)
+    return fail(TGS_EINVAL,
+                "device error word 0x%x: an input index outside its range (a merge row's index outside [0, n) or "
+                "repeated, or a sample position outside [0, n))",
                 word);
   return fail(TGS_EDEVICE,
-              "device error word 0x%x (bit0 bad merge input, bit1 wait timed out: the grid was not all resident, "
+              "device error word 0x%x (bit0 bad input index, bit1 wait timed out: the grid was not all resident, "
               "bit2 inconsistent counts); re-initialise the workspace before its next use",
               word);
 }

@@ -149,7 +149,7 @@ __global__ void k_gt_validate(const Pair* __restrict__ rows, int64_t k, int64_t 
   int32_t x = rows[i].idx;
   bool bad = x < 0 || (int64_t)x >= n;
   if (i % k != 0) bad = bad || rows[i - 1].idx == x;
-  if (bad) atomicOr(err, kErrBadMergeInput);
+  if (bad) atomicOr(err, kErrBadInput);
 }
 
 // Union of slot pairs.  Merge m combines A = slots[sa[m]] and B = slots[sa[m] + half]

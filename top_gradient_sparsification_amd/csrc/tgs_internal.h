@@ -26,6 +26,23 @@ constexpr int kWave = 64;
 // workspace can move between operations without clearing it.
 constexpr size_t kWorkspaceHeader = 32768;
 
+// The end of every header: a 2048-bin histogram and an arrival counter that a
+// launch's workgroups add into and its last arrival reads and leaves zero
+// (the top-k guess, the threshold estimate).  Calls on one workspace are
+// ordered, so they can share it.
+struct HeaderHist {
+  u32 hist[2048];
+  u32 done;
+  u32 pad[63];
+};
+constexpr size_t kHeaderHistOffset = kWorkspaceHeader - sizeof(HeaderHist);
+__host__ __device__ inline HeaderHist* header_hist(void* workspace) {
+  return (HeaderHist*)((char*)workspace + kHeaderHistOffset);
+}
+
+// Device error word bits.
+constexpr u32 kErrBadInput = 1u << 0;  // an index outside its range, or a repeated merge index
+
 // ---------------------------------------------------------------- keys ----
 __device__ __forceinline__ u32 key_of_bits(u32 b) { return b & 0x7FFFFFFFu; }
 __device__ __forceinline__ u32 key_of(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
@@ -211,7 +228,6 @@ struct GridBar {
 };
 
 constexpr u32 kErrBarrierTimeout = 1u << 1;
-constexpr u32 kErrBadMergeInput = 1u << 0;
 
 __device__ __forceinline__ bool grid_sync(const GridBar& gb) {
   __shared__ u32 s_ok;

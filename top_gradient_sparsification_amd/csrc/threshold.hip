@@ -42,6 +42,7 @@ struct ThrArgs {
   int64_t nv;    // float4 vectors (0 in scalar mode)
   bool vec;
   u32 klam;
+  const float* lam_dev;  // when set, the threshold is key(*lam_dev) (read on the device) instead of klam
   u32* cnt;      // [G]
   Pair* stash;   // [G][stash_cap]
   int64_t stash_cap;
@@ -187,7 +188,16 @@ __device__ __forceinline__ u32 tile_rank(u32 qmask, u32& running, u32 (*s_wt)[kT
 // the stash (rank < stash_cap), acc everywhere else: in the usual case
 // (count <= capacity, no overflow) every stashed entry is emitted and the
 // emit pass only copies.  Entries the capacity turns away get acc back.
-__global__ __launch_bounds__(kThrThreads) void k_thr_pass(ThrArgs a) {
+// The arguments with the threshold key in place (read from the device when
+// it comes from there).
+__device__ __forceinline__ ThrArgs with_key(const ThrArgs& in) {
+  ThrArgs a = in;
+  if (a.lam_dev) a.klam = __builtin_amdgcn_readfirstlane(__float_as_uint(*a.lam_dev) & 0x7FFFFFFFu);
+  return a;
+}
+
+__global__ __launch_bounds__(kThrThreads) void k_thr_pass(ThrArgs ain) {
+  const ThrArgs a = with_key(ain);
   __shared__ u32 s_wt[2][kThrWaves];
   const float* __restrict__ g = a.grad;
   float* __restrict__ r = a.residual;
@@ -286,7 +296,8 @@ __global__ __launch_bounds__(kThrThreads) void k_thr_pass(ThrArgs a) {
   if (tid == 0) a.cnt[blockIdx.x] = running;
 }
 
-__global__ __launch_bounds__(kThrThreads) void k_thr_emit(ThrArgs a) {
+__global__ __launch_bounds__(kThrThreads) void k_thr_emit(ThrArgs ain) {
+  const ThrArgs a = with_key(ain);
   __shared__ u32 s_wt[2][kThrWaves];
   __shared__ u32 s_scan[kThrWaves + 1];
   const int tid = threadIdx.x;
@@ -380,28 +391,33 @@ extern "C" size_t tgs_threshold_workspace_bytes(int64_t n) {
   return thr_layout(n).total;
 }
 
-extern "C" tgs_status tgs_threshold_ef_step(const float* grad, float* residual, int64_t n, float lambda,
-                                            int32_t* out_idx, float* out_val, int64_t capacity,
-                                            int64_t* d_count, void* workspace, size_t workspace_bytes,
-                                            hipStream_t stream) {
-  if (n < 0 || n > INT32_MAX) return fail(TGS_EINVAL, "threshold_ef_step: n=%lld outside [0, 2^31-1]", (long long)n);
-  if (!(lambda >= 0.0f)) return fail(TGS_EINVAL, "threshold_ef_step: lambda must be >= 0 and not NaN");
-  if (capacity < 0) return fail(TGS_EINVAL, "threshold_ef_step: capacity < 0");
-  if (!d_count || !workspace) return fail(TGS_EINVAL, "threshold_ef_step: null d_count/workspace");
-  if (n > 0 && (!grad || !residual)) return fail(TGS_EINVAL, "threshold_ef_step: null grad/residual");
-  if (capacity > 0 && (!out_idx || !out_val)) return fail(TGS_EINVAL, "threshold_ef_step: null outputs");
-  for (const void* p : {(const void*)grad, (const void*)residual, (const void*)out_idx, (const void*)out_val})
-    if (((uintptr_t)p & 3u) != 0) return fail(TGS_EINVAL, "threshold_ef_step: pointer not 4-byte aligned");
-  if (((uintptr_t)d_count & 7u) != 0) return fail(TGS_EINVAL, "threshold_ef_step: d_count not 8-byte aligned");
+// Validates and launches the threshold step; the threshold is key(lambda),
+// or key(*lam_dev) read on the device when lam_dev is set.
+static tgs_status threshold_launch(const char* what, const float* grad, float* residual, int64_t n, float lambda,
+                                   const float* lam_dev, int32_t* out_idx, float* out_val, int64_t capacity,
+                                   int64_t* d_count, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (n < 0 || n > INT32_MAX) return fail(TGS_EINVAL, "%s: n=%lld outside [0, 2^31-1]", what, (long long)n);
+  if (!lam_dev && !(lambda >= 0.0f)) return fail(TGS_EINVAL, "%s: lambda must be >= 0 and not NaN", what);
+  if (capacity < 0) return fail(TGS_EINVAL, "%s: capacity < 0", what);
+  if (!d_count || !workspace) return fail(TGS_EINVAL, "%s: null d_count/workspace", what);
+  if (n > 0 && (!grad || !residual)) return fail(TGS_EINVAL, "%s: null grad/residual", what);
+  if (capacity > 0 && (!out_idx || !out_val)) return fail(TGS_EINVAL, "%s: null outputs", what);
+  for (const void* p : {(const void*)grad, (const void*)residual, (const void*)out_idx, (const void*)out_val,
+                        (const void*)lam_dev})
+    if (((uintptr_t)p & 3u) != 0) return fail(TGS_EINVAL, "%s: pointer not 4-byte aligned", what);
+  if (((uintptr_t)d_count & 7u) != 0) return fail(TGS_EINVAL, "%s: d_count not 8-byte aligned", what);
   const size_t nb4 = (size_t)n * 4, cb4 = (size_t)capacity * 4;
   if (overlaps(grad, nb4, residual, nb4) || overlaps(grad, nb4, out_idx, cb4) || overlaps(grad, nb4, out_val, cb4) ||
       overlaps(residual, nb4, out_idx, cb4) || overlaps(residual, nb4, out_val, cb4) ||
       overlaps(out_idx, cb4, out_val, cb4) || overlaps(d_count, 8, residual, nb4) ||
       overlaps(d_count, 8, out_idx, cb4) || overlaps(d_count, 8, out_val, cb4) || overlaps(d_count, 8, grad, nb4))
-    return fail(TGS_EINVAL, "threshold_ef_step: overlapping buffers");
+    return fail(TGS_EINVAL, "%s: overlapping buffers", what);
+  if (lam_dev && (overlaps(lam_dev, 4, residual, nb4) || overlaps(lam_dev, 4, out_idx, cb4) ||
+                  overlaps(lam_dev, 4, out_val, cb4) || overlaps(lam_dev, 4, d_count, 8)))
+    return fail(TGS_EINVAL, "%s: d_lambda overlaps an output", what);
   const ThrLayout L = thr_layout(n);
   if (workspace_bytes < L.total)
-    return fail(TGS_EWORKSPACE, "threshold_ef_step: workspace %zu bytes, need %zu", workspace_bytes, L.total);
+    return fail(TGS_EWORKSPACE, "%s: workspace %zu bytes, need %zu", what, workspace_bytes, L.total);
   if (n == 0) {
     hipLaunchKernelGGL(k_store_zero_count, dim3(1), dim3(64), 0, stream, d_count);
   } else {
@@ -416,7 +432,8 @@ extern "C" tgs_status tgs_threshold_ef_step(const float* grad, float* residual, 
       a.head = std::min<int64_t>(head, n);
       a.nv = (n - a.head) / 4;
     }
-    a.klam = __builtin_bit_cast(uint32_t, lambda) & 0x7FFFFFFFu;
+    a.klam = lam_dev ? 0u : (__builtin_bit_cast(uint32_t, lambda) & 0x7FFFFFFFu);
+    a.lam_dev = lam_dev;
     a.cnt = (u32*)(ws + L.cnt);
     a.stash = (Pair*)(ws + L.stash);
     a.stash_cap = L.stash_cap;
@@ -432,6 +449,23 @@ extern "C" tgs_status tgs_threshold_ef_step(const float* grad, float* residual, 
     hipLaunchKernelGGL(k_thr_emit, dim3(L.G), dim3(kThrThreads), 0, stream, a);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(TGS_EHIP, "threshold_ef_step: launch failed: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail(TGS_EHIP, "%s: launch failed: %s", what, hipGetErrorString(e));
   return TGS_OK;
+}
+
+extern "C" tgs_status tgs_threshold_ef_step(const float* grad, float* residual, int64_t n, float lambda,
+                                            int32_t* out_idx, float* out_val, int64_t capacity,
+                                            int64_t* d_count, void* workspace, size_t workspace_bytes,
+                                            hipStream_t stream) {
+  return threshold_launch("threshold_ef_step", grad, residual, n, lambda, nullptr, out_idx, out_val, capacity, d_count,
+                          workspace, workspace_bytes, stream);
+}
+
+extern "C" tgs_status tgs_threshold_ef_step_dev(const float* grad, float* residual, int64_t n, const float* d_lambda,
+                                                int32_t* out_idx, float* out_val, int64_t capacity,
+                                                int64_t* d_count, void* workspace, size_t workspace_bytes,
+                                                hipStream_t stream) {
+  if (!d_lambda) return fail(TGS_EINVAL, "threshold_ef_step_dev: null d_lambda");
+  return threshold_launch("threshold_ef_step_dev", grad, residual, n, 0.0f, d_lambda, out_idx, out_val, capacity,
+                          d_count, workspace, workspace_bytes, stream);
 }

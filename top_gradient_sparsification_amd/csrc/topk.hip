@@ -172,14 +172,12 @@ struct StepCtl {
   Plan plan;
   u32 seg_done[64];  // k_small arrivals per segment of a launch; each segment's last workgroup leaves it zero
   // guided accumulate pass (standalone general path): k_guess adds its sample
-  // histogram into guide_hist; its last workgroup picks guide_bin and leaves
-  // guide_hist, guide_done and guide_ovf zero for the accumulate pass
-  u32 guide_hist[2048];
-  u32 guide_done;
+  // histogram into the header histogram; its last workgroup picks guide_bin
+  // and leaves the histogram, its counter and guide_ovf zero
   u32 guide_bin;  // candidates are the entries of first-level bins >= guide_bin (kNoGuide: none)
   u32 guide_ovf;  // set by the accumulate pass when a workgroup's region overflowed
 };
-static_assert(sizeof(StepCtl) <= kWorkspaceHeader, "control block exceeds the workspace header");
+static_assert(sizeof(StepCtl) <= kHeaderHistOffset, "control block overlaps the header histogram");
 static_assert(kMaxAccBlocks <= kMaxGenWG, "guided regions are the general path's");
 
 // State of the general path (zero when it starts).
@@ -1157,6 +1155,7 @@ struct GuessArgs {
   int64_t chunks, stride;  // chunk c covers float4 [c * stride, c * stride + 64); stride >= 64
   u32 c_req, s_max;
   StepCtl* ctl;
+  HeaderHist* hh;
 };
 
 __global__ __launch_bounds__(kGuessThreads) void k_guess(GuessArgs a) {
@@ -1187,16 +1186,16 @@ __global__ __launch_bounds__(kGuessThreads) void k_guess(GuessArgs a) {
   __syncthreads();
   StepCtl* ctl = a.ctl;
   for (int i = tid; i < 2048; i += NT)
-    if (s_h[i]) add_agent_relaxed(&ctl->guide_hist[i], s_h[i]);
+    if (s_h[i]) add_agent_relaxed(&a.hh->hist[i], s_h[i]);
   wait_all_memory();
   __syncthreads();
-  if (tid == 0) s_last = add_agent_acqrel(&ctl->guide_done, 1u) == gridDim.x - 1 ? 1u : 0u;
+  if (tid == 0) s_last = add_agent_acqrel(&a.hh->done, 1u) == gridDim.x - 1 ? 1u : 0u;
   __syncthreads();
   if (!s_last) return;
   // last workgroup: every other one has added its histogram
   static_assert(NT * 2 == 2048, "two bins per thread");
   const int hi = 2047 - 2 * tid;  // this thread's bins, from the top: hi, hi - 1
-  const u32 h1 = ld_agent(&ctl->guide_hist[hi]), h0 = ld_agent(&ctl->guide_hist[hi - 1]);
+  const u32 h1 = ld_agent(&a.hh->hist[hi]), h0 = ld_agent(&a.hh->hist[hi - 1]);
   u32 tot;
   const u32 above = block_exclusive_sum<NT>(h1 + h0, s_scan, tot);
   if (tid == 0) s_pick = 0u;  // no bin reaches c_req: every bin
@@ -1207,12 +1206,12 @@ __global__ __launch_bounds__(kGuessThreads) void k_guess(GuessArgs a) {
   // sample entries in the bins >= pick
   const u32 mine = (u32)hi >= pick ? h1 : 0u, mine0 = (u32)(hi - 1) >= pick ? h0 : 0u;
   const u32 kept = block_sum<NT>(mine + mine0, s_scan);
-  st_agent(&ctl->guide_hist[hi], 0u);
-  st_agent(&ctl->guide_hist[hi - 1], 0u);
+  st_agent(&a.hh->hist[hi], 0u);
+  st_agent(&a.hh->hist[hi - 1], 0u);
   if (tid == 0) {
     st_agent(&ctl->guide_bin, kept <= a.s_max ? pick : kNoGuide);
     st_agent(&ctl->guide_ovf, 0u);
-    st_agent(&ctl->guide_done, 0u);
+    st_agent(&a.hh->done, 0u);
   }
 }
 
@@ -2840,6 +2839,7 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
       const double room = (double)G1 * stride;
       q.s_max = (u32)std::min(4.0e9, std::floor(0.6 * room * f));
       q.ctl = ctl;
+      q.hh = header_hist(workspace);
       const int gq = (int)std::min<int64_t>(kGuessBlocks, (chunks + (kGuessThreads / kWave) * kGuessUnroll - 1) /
                                                               ((kGuessThreads / kWave) * kGuessUnroll));
       hipLaunchKernelGGL(k_guess, dim3(gq), dim3(kGuessThreads), 0, stream, q);

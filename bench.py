@@ -46,6 +46,14 @@ kernel of it) against its algorithmic bytes:
                                         capacity 30M (residual after 1 step)
     gtopk_P32_k25600                    the merge of 32 sets of 25,600 pairs
                                         (50% from a hot set of 51,200)
+    thrEst_n25.6M_0.1%                  the 25.6M mixture, threshold estimated
+                                        from 2^17 uniform sample positions for
+                                        a 0.1% target (q = 132), then the hard
+                                        threshold with it on the device,
+                                        capacity 2k (residual after 5 steps)
+    rtopk_n25.6M_r0.2%_k0.1%            the 25.6M mixture, rTop-k: k = 25,600
+                                        drawn from the top r = 51,200
+                                        (residual after 5 steps)
 """
 from __future__ import annotations
 
@@ -74,7 +82,22 @@ OTHER = {
     "topk_n1.5e9_0.1%": ("topk", 1_500_000_000, 0.001, (1e-3, 0.005, 0.05), 5, 2),
     "threshold_n1.5e9": ("threshold", 1_500_000_000, 4e-3, (1e-3, 0.005, 0.05), 5, 1),
     "gtopk_P32_k25600": ("gtopk", 25_600_000, 0.0, None, 4, 0),
+    "thrEst_n25.6M_0.1%": ("estimate", 25_600_000, 0.001, (1e-3, 0.01, 0.1), 2, 5),
+    "rtopk_n25.6M_r0.2%_k0.1%": ("rtopk", 25_600_000, 0.001, (1e-3, 0.01, 0.1), 2, 5),
 }
+EST_SAMPLES = 1 << 17
+
+
+def copy_calibration(dev):
+    """A plain copy of 256 MiB, three times: a kernel of known traffic for
+    scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def run_other(args):
@@ -87,6 +110,8 @@ def run_other(args):
     kind, n, par, mix, cfg, prior = OTHER[args.workload]
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
+    if args.copy_calibration:
+        copy_calibration(dev)
     flush = torch.empty(128 << 20, dtype=torch.float32, device=dev) if n < 200_000_000 or kind == "gtopk" else None
     print("bench: preparing %s" % args.workload, file=sys.stderr, flush=True)
     if kind == "gtopk":
@@ -108,6 +133,29 @@ def run_other(args):
             cnt = torch.zeros(1, dtype=torch.int64, device=dev)
             ws = torch.zeros(tgs.threshold_workspace_bytes(n), dtype=torch.uint8, device=dev)
             one = lambda g: tgs.threshold_ef_step(g, resid, par, cap, out_idx=oi, out_val=ov, count=cnt, ws=ws)
+        elif kind == "estimate":
+            import math
+            m = EST_SAMPLES
+            q = math.ceil(par * m)
+            cap = 2 * workloads.k_for_density(n, par)
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(4242)
+            sample = torch.randint(0, n, (m,), generator=gen, device=dev, dtype=torch.int64).to(torch.int32)
+            oi = torch.empty(cap, dtype=torch.int32, device=dev)
+            ov = torch.empty(cap, dtype=torch.float32, device=dev)
+            cnt = torch.zeros(1, dtype=torch.int64, device=dev)
+            lam = torch.zeros(1, dtype=torch.float32, device=dev)
+            ws = torch.zeros(max(tgs.threshold_estimate_workspace_bytes(m), tgs.threshold_workspace_bytes(n)),
+                             dtype=torch.uint8, device=dev)
+            one = lambda g: tgs.estimated_threshold_ef_step(g, resid, sample, q, cap, out_idx=oi, out_val=ov,
+                                                            count=cnt, d_lambda=lam, ws=ws)
+        elif kind == "rtopk":
+            k_r = workloads.k_for_density(n, par)
+            r_r = 2 * k_r
+            oi = torch.empty(k_r, dtype=torch.int32, device=dev)
+            ov = torch.empty(k_r, dtype=torch.float32, device=dev)
+            ws = torch.zeros(tgs.rtopk_workspace_bytes(n, r_r, k_r), dtype=torch.uint8, device=dev)
+            one = lambda g: tgs.rtopk_ef_step(g, resid, r_r, k_r, 0x5EED, 6, out_idx=oi, out_val=ov, ws=ws)
         elif kind == "segments":
             sizes = workloads.segments_log_uniform(n)
             offs = np.concatenate([[0], np.cumsum(sizes)])
@@ -127,14 +175,17 @@ def run_other(args):
 
         call = lambda: one(g_last)
         elems, what = n, "gradient elements"
-        if kind == "threshold":
+        if kind in ("threshold", "estimate"):
+            restore()
             one(g_last)
             torch.cuda.synchronize()
             c = int(cnt.item())
             nbytes = 12.0 * n + 8.0 * min(c, cap) + 8.0
+            if kind == "estimate":
+                nbytes += 12.0 * m  # sample positions, and grad and residual at them
         elif kind == "segments":
             nbytes = 12.0 * n + 8.0 * sum(workloads.k_for_density(int(sz), par) for sz in sizes)
-        else:
+        else:  # top-k and rTop-k: read grad and residual, write residual and k pairs
             nbytes = 12.0 * n + 8.0 * workloads.k_for_density(n, par)
     for _ in range(3):  # warm-up calls
         restore()
@@ -173,8 +224,13 @@ def run_other(args):
                                "between calls" % K},
         "cpu_baseline": None,
     }
-    if kind == "threshold":
+    if kind in ("threshold", "estimate"):
         rec["config"]["count"] = c
+    if kind == "estimate":
+        rec["config"].update({"samples": m, "q": q, "capacity": cap,
+                              "threshold": float(lam.item())})
+    if kind == "rtopk":
+        rec["config"].update({"r": r_r, "k": k_r})
     print(json.dumps(rec))
 
 
@@ -276,12 +332,7 @@ def main():
     run = tgs.TopkStep(N, k, dev)
     ws = run.ws
     if args.copy_calibration:
-        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration(dev)
 
     print("bench: set-up: %d residual buffers x %d prior EF steps" % (sets, prior), file=sys.stderr, flush=True)
     for j in range(sets):

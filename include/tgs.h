@@ -173,8 +173,7 @@ size_t tgs_threshold_estimate_workspace_bytes(int64_t m);
  *   d_lambda  device float, out: the float whose bits are that key (>= 0).
  * grad and residual are only read.  A position outside [0, n) sets the
  * bad-input bit of the device error word (the estimate is then unspecified).
- * One launch; intended for m up to ~2^20 (its last workgroup reads the m keys
- * once more).  The workspace must be 16-byte aligned.
+ * Two launches.  The workspace must be 256-byte aligned.
  */
 tgs_status tgs_threshold_estimate(const float* grad, const float* residual, int64_t n, const int32_t* sample_idx,
                                   int64_t m, int64_t q, float* d_lambda, void* workspace, size_t workspace_bytes,
@@ -207,7 +206,7 @@ size_t tgs_rtopk_workspace_bytes(int64_t n, int64_t r, int64_t k);
  *             values bit for bit.
  *   residual  in/out: +0.0f at the k sent, acc everywhere else (the r - k
  *             passed over included).
- * r = k gives tgs_topk_ef_step's result.  One more kernel follows the top-r
+ * r = k gives tgs_topk_ef_step's result.  Two more kernels follow the top-r
  * step's launches.  Pointer and overlap rules as tgs_topk_ef_step.
  */
 tgs_status tgs_rtopk_ef_step(const float* grad, float* residual, int64_t n, int64_t r, int64_t k, uint64_t seed,

@@ -9,14 +9,15 @@
 //   1. the top-r step (tgs_topk_ef_step with k = r) into workspace buffers:
 //      acc written back, the r largest in (key desc, index asc) order, their
 //      residual set to +0;
-//   2. k_rtopk_pick, one workgroup: entry i draws u_i = word 0 of
-//      Philox4x32-10 (Salmon et al., "Parallel Random Numbers: As Easy as 1,
-//      2, 3", SC'11) at counter (i, step low, step high, 0) under key
-//      (seed low, seed high); the k entries with the smallest (u_i, i) are
-//      kept, found by a radix select over the 64-bit composite u_i << 32 | i
-//      (unique, so no tie rule is needed).  An ordered compaction over the
-//      top-r list writes them in its order, (key desc, index asc); every
-//      entry passed over gets its acc back in the residual.
+//   2. k_rtopk_draw: entry i of the list draws u_i = word 0 of Philox4x32-10
+//      (Salmon et al., "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11)
+//      at counter (i, step low, step high, 0) under key (seed low, seed high);
+//   3. k_rtopk_pick, one workgroup: the k entries with the smallest (u_i, i)
+//      are kept, found by a radix select over the 64-bit composite
+//      u_i << 32 | i (unique, so no tie rule is needed; the index bits are
+//      looked at only when draws tie).  An ordered compaction over the top-r
+//      list writes them in its order, (key desc, index asc); every entry
+//      passed over gets its acc back in the residual.
 #include <algorithm>
 #include <climits>
 
@@ -50,7 +51,7 @@ __device__ __forceinline__ u32 philox_w0(u32 c0, u32 c1, u32 c2, u32 c3, u32 k0,
 struct PickArgs {
   const int32_t* idx;  // [r] the top r, in (key desc, index asc) order
   const float* val;    // [r] their acc
-  u32* draw;           // [r] scratch: u_j
+  u32* draw;           // [r] u_j (written by k_rtopk_draw)
   u32 r, k;
   u32 seed_lo, seed_hi, step_lo, step_hi;
   int32_t* out_idx;    // [k]
@@ -58,22 +59,29 @@ struct PickArgs {
   float* residual;
 };
 
+// u_j for every entry of the top-r list, one per thread.
+__global__ __launch_bounds__(256) void k_rtopk_draw(PickArgs a) {
+  const u32 j = blockIdx.x * 256u + threadIdx.x;
+  if (j < a.r) a.draw[j] = philox_w0((u32)a.idx[j], a.step_lo, a.step_hi, 0u, a.seed_lo, a.seed_hi);
+}
+
+// One workgroup.  The entries are visited in batches of kPickBatch rows of
+// 1024 (entry j = row * 1024 + tid), each batch's loads all in flight before
+// any is used.
+constexpr int kPickBatch = 16;
+
 __global__ __launch_bounds__(kPickThreads) void k_rtopk_pick(PickArgs a) {
-  constexpr int NT = kPickThreads, NW = NT / kWave;
+  constexpr int NT = kPickThreads, NW = NT / kWave, B = kPickBatch;
   __shared__ u32 s_h[2048];
   __shared__ u32 s_scan[NW + 1];
   __shared__ u32 s_out[2];
-  __shared__ u32 s_wc[2][NW];
+  __shared__ u32 s_wc[B][NW];
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const u32 r = a.r, k = a.k;
-  // composite of entry j: draw << 32 | index
-  auto comp = [&](u32 j) -> u64 { return ((u64)a.draw[j] << 32) | (u64)(u32)a.idx[j]; };
-  for (u32 j = tid; j < r; j += NT)
-    a.draw[j] = philox_w0((u32)a.idx[j], a.step_lo, a.step_hi, 0u, a.seed_lo, a.seed_hi);
-  __syncthreads();  // each thread reads back only its own draws before this; others' after it
-  // T = the k-th smallest composite (k >= 1); kept: composite <= T.
-  u64 T = ~0ull;
-  if (k == 0) T = 0;  // nothing kept (checked below)
+  const u32 rows = (r + NT - 1) / NT;
+  // T = the k-th smallest composite u << 32 | index (1 <= k < r); kept:
+  // composite <= T
+  u64 T = 0;
   if (k > 0 && k < r) {
     constexpr int kShift[6] = {53, 42, 32, 21, 10, 0};
     constexpr int kWidth[6] = {11, 11, 10, 11, 11, 10};
@@ -82,12 +90,28 @@ __global__ __launch_bounds__(kPickThreads) void k_rtopk_pick(PickArgs a) {
     for (int L = 0; L < 6; ++L) {
       const int sh = kShift[L], wd = kWidth[L];
       const u32 nb = 1u << wd;
+      const int top = sh + wd;
       for (int i = tid; i < 2048; i += NT) s_h[i] = 0;
       __syncthreads();
-      const int top = sh + wd;  // composites whose bits above `top` equal prefix take part
-      for (u32 j = tid; j < r; j += NT) {
-        const u64 c = comp(j);
-        if (top >= 64 || (c >> top) == prefix) atomicAdd(&s_h[(u32)(c >> sh) & (nb - 1u)], 1u);
+      for (u32 b0 = 0; b0 < rows; b0 += B) {
+        u32 dq[B];
+#pragma unroll
+        for (int e = 0; e < B; ++e) {
+          const u32 j = (b0 + e) * NT + tid;
+          dq[e] = j < r ? a.draw[j] : 0u;
+        }
+#pragma unroll
+        for (int e = 0; e < B; ++e) {
+          const u32 j = (b0 + e) * NT + tid;
+          if (j >= r) continue;
+          if (L < 3) {  // the draw's bits
+            const u64 c = (u64)dq[e] << 32;
+            if (top >= 64 || (c >> top) == prefix) atomicAdd(&s_h[(u32)(c >> sh) & (nb - 1u)], 1u);
+          } else if ((u64)dq[e] == (prefix >> (32 - top))) {  // the draw ties the chosen one: index bits
+            const u64 c = ((u64)dq[e] << 32) | (u64)(u32)a.idx[j];
+            if ((c >> top) == prefix) atomicAdd(&s_h[(u32)(c >> sh) & (nb - 1u)], 1u);
+          }
+        }
       }
       __syncthreads();
       // the smallest digit d whose prefix count reaches need; thread t owns
@@ -112,36 +136,55 @@ __global__ __launch_bounds__(kPickThreads) void k_rtopk_pick(PickArgs a) {
       }
     }
   }
-  // ordered compaction over the top-r list (rank order); entries passed over
-  // get their acc back
+  // ordered compaction over the list (rank order); entries passed over get
+  // their acc back
+  const u32 tu = (u32)(T >> 32);
   u32 seen = 0;
-  const u32 rows = (r + NT - 1) / NT;
-  for (u32 t = 0; t < rows; ++t) {
-    const u32 j = t * NT + tid;
-    const bool in = j < r;
-    const bool keep = in && k > 0 && (k == r || comp(j) <= T);
-    const u64 m = ballot(keep);
-    if (lane == 0) s_wc[t & 1][w] = (u32)__popcll(m);
-    __syncthreads();
-    u32 off = 0, tt = 0;
+  for (u32 b0 = 0; b0 < rows; b0 += B) {
+    u32 dq[B], iq[B], vq[B];
 #pragma unroll
-    for (int q = 0; q < NW; ++q) {
-      const u32 v = s_wc[t & 1][q];
-      off += q < w ? v : 0u;
-      tt += v;
+    for (int e = 0; e < B; ++e) {
+      const u32 j = (b0 + e) * NT + tid;
+      const bool in = j < r;
+      dq[e] = in ? a.draw[j] : 0u;
+      iq[e] = in ? (u32)a.idx[j] : 0u;
+      vq[e] = in ? __float_as_uint(a.val[j]) : 0u;
     }
-    if (keep) {
-      const u32 p = seen + off + lanes_below(m);
-      a.out_idx[p] = a.idx[j];
-      a.out_val[p] = a.val[j];
-    } else if (in) {
-      a.residual[a.idx[j]] = a.val[j];
+    u32 kmask = 0;
+#pragma unroll
+    for (int e = 0; e < B; ++e) {
+      const u32 j = (b0 + e) * NT + tid;
+      const bool keep = j < r && k > 0 && (k == r || dq[e] < tu || (dq[e] == tu && iq[e] <= (u32)T));
+      const u64 m = ballot(keep);
+      if (lane == 0) s_wc[e][w] = (u32)__popcll(m);
+      kmask |= (u32)keep << e;
     }
-    seen += tt;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < B; ++e) {
+      const u32 j = (b0 + e) * NT + tid;
+      u32 off = 0, tt = 0;
+#pragma unroll
+      for (int q = 0; q < NW; ++q) {
+        const u32 c = s_wc[e][q];
+        off += q < w ? c : 0u;
+        tt += c;
+      }
+      const bool keep = (kmask >> e) & 1u;
+      const u64 m = ballot(keep);
+      if (keep) {
+        const u32 p = seen + off + lanes_below(m);
+        a.out_idx[p] = (int32_t)iq[e];
+        a.out_val[p] = __uint_as_float(vq[e]);
+      } else if (j < r) {
+        a.residual[iq[e]] = __uint_as_float(vq[e]);
+      }
+      seen += tt;
+    }
+    __syncthreads();  // s_wc is rewritten by the next batch
   }
 }
 
-// The top-r step's workspace first, then the top r pairs and their draws.
 struct RtopkLayout {
   size_t idx, val, draw, total;
 };
@@ -208,6 +251,7 @@ extern "C" tgs_status tgs_rtopk_ef_step(const float* grad, float* residual, int6
   a.out_idx = out_idx;
   a.out_val = out_val;
   a.residual = residual;
+  hipLaunchKernelGGL(k_rtopk_draw, dim3((unsigned)((r + 255) / 256)), dim3(256), 0, stream, a);
   hipLaunchKernelGGL(k_rtopk_pick, dim3(1), dim3(kPickThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TGS_EHIP, "rtopk_ef_step: launch failed: %s", hipGetErrorString(e));

@@ -36,6 +36,8 @@ struct HeaderHist {
   u32 pad[63];
 };
 constexpr size_t kHeaderHistOffset = kWorkspaceHeader - sizeof(HeaderHist);
+// The 128 bytes before it: the threshold estimate's selection state.
+constexpr size_t kEstStateOffset = kHeaderHistOffset - 128;
 __host__ __device__ inline HeaderHist* header_hist(void* workspace) {
   return (HeaderHist*)((char*)workspace + kHeaderHistOffset);
 }

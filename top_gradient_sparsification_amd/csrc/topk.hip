@@ -177,7 +177,7 @@ struct StepCtl {
   u32 guide_bin;  // candidates are the entries of first-level bins >= guide_bin (kNoGuide: none)
   u32 guide_ovf;  // set by the accumulate pass when a workgroup's region overflowed
 };
-static_assert(sizeof(StepCtl) <= kHeaderHistOffset, "control block overlaps the header histogram");
+static_assert(sizeof(StepCtl) <= kEstStateOffset, "control block overlaps the header's shared state");
 static_assert(kMaxAccBlocks <= kMaxGenWG, "guided regions are the general path's");
 
 // State of the general path (zero when it starts).

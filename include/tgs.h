@@ -115,6 +115,23 @@ tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64_t n, int64
                             int32_t* out_idx, float* out_val, void* workspace,
                             size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * tgs_topk_ef_step for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same step, with no workspace argument.  Its workspace is a device array of
+ * TGS_NOALLOC_WORKSPACE_BYTES inside the library, one per GPU, held until the
+ * process ends; sizes whose tgs_topk_workspace_bytes(n, k) exceed it are
+ * rejected with TGS_EINVAL.  The call allocates nothing: on a device's first
+ * call it looks up that device's copy of the array and zero-fills its header
+ * with a kernel on `stream`.  All calls on one GPU share the array (it keeps
+ * the last call's contents), so calls that overlap in time on one GPU race:
+ * order them on one stream.  Its device error word is not reachable; callers
+ * that need it use tgs_topk_ef_step.
+ */
+#define TGS_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+tgs_status tgs_topk_ef_step_noalloc(const float* grad, float* residual, int64_t n, int64_t k, int32_t* out_idx,
+                                    float* out_val, hipStream_t stream);
+
 /* Bytes of workspace tgs_topk_ef_step_segmented needs for this segment table
    (HOST arrays, as below).  0 if the table is invalid. */
 size_t tgs_topk_segmented_workspace_bytes(int32_t nseg, const int64_t* offsets, const int64_t* ks);

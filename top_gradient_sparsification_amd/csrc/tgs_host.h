@@ -19,6 +19,11 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb);
 
 int64_t get_option(int32_t option);
 
+// The argument checks of the top-k step (sizes, null and misaligned pointers,
+// overlapping buffers); `what` names the entry point in the message.
+tgs_status topk_check_args(const char* what, const float* grad, const float* residual, int64_t n, int64_t k,
+                           const int32_t* out_idx, const float* out_val);
+
 // Compute units of the current device (cached per device; 0 on failure).
 int device_cu_count();
 

@@ -2682,21 +2682,32 @@ extern "C" size_t tgs_topk_workspace_bytes(int64_t n, int64_t k) {
   return topk_layout(n, k).total;
 }
 
-extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64_t n, int64_t k,
-                                       int32_t* out_idx, float* out_val, void* workspace,
-                                       size_t workspace_bytes, hipStream_t stream) {
-  if (n < 0 || n > INT32_MAX) return fail(TGS_EINVAL, "topk_ef_step: n=%lld outside [0, 2^31-1]", (long long)n);
-  if (k < 0 || k > n) return fail(TGS_EINVAL, "topk_ef_step: k=%lld outside [0, n=%lld]", (long long)k, (long long)n);
-  if (n > 0 && (!grad || !residual)) return fail(TGS_EINVAL, "topk_ef_step: null grad/residual");
-  if (k > 0 && (!out_idx || !out_val)) return fail(TGS_EINVAL, "topk_ef_step: null output pointer");
-  if (!workspace) return fail(TGS_EINVAL, "topk_ef_step: null workspace");
+namespace tgs {
+
+tgs_status topk_check_args(const char* what, const float* grad, const float* residual, int64_t n, int64_t k,
+                           const int32_t* out_idx, const float* out_val) {
+  if (n < 0 || n > INT32_MAX) return fail(TGS_EINVAL, "%s: n=%lld outside [0, 2^31-1]", what, (long long)n);
+  if (k < 0 || k > n) return fail(TGS_EINVAL, "%s: k=%lld outside [0, n=%lld]", what, (long long)k, (long long)n);
+  if (n > 0 && (!grad || !residual)) return fail(TGS_EINVAL, "%s: null grad/residual", what);
+  if (k > 0 && (!out_idx || !out_val)) return fail(TGS_EINVAL, "%s: null output pointer", what);
   for (const void* p : {(const void*)grad, (const void*)residual, (const void*)out_idx, (const void*)out_val})
-    if (((uintptr_t)p & 3u) != 0) return fail(TGS_EINVAL, "topk_ef_step: pointer not 4-byte aligned");
+    if (((uintptr_t)p & 3u) != 0) return fail(TGS_EINVAL, "%s: pointer not 4-byte aligned", what);
   const size_t nb4 = (size_t)n * 4, kb4 = (size_t)k * 4;
   if (overlaps(grad, nb4, residual, nb4) || overlaps(grad, nb4, out_idx, kb4) ||
       overlaps(grad, nb4, out_val, kb4) || overlaps(residual, nb4, out_idx, kb4) ||
       overlaps(residual, nb4, out_val, kb4) || overlaps(out_idx, kb4, out_val, kb4))
-    return fail(TGS_EINVAL, "topk_ef_step: overlapping buffers");
+    return fail(TGS_EINVAL, "%s: overlapping buffers", what);
+  return TGS_OK;
+}
+
+}  // namespace tgs
+
+extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64_t n, int64_t k,
+                                       int32_t* out_idx, float* out_val, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+  const tgs_status chk = topk_check_args("topk_ef_step", grad, residual, n, k, out_idx, out_val);
+  if (chk != TGS_OK) return chk;
+  if (!workspace) return fail(TGS_EINVAL, "topk_ef_step: null workspace");
   const TopkLayout L = topk_layout(n, k);
   if (workspace_bytes < L.total)
     return fail(TGS_EWORKSPACE, "topk_ef_step: workspace %zu bytes, need %zu", workspace_bytes, L.total);

@@ -19,14 +19,13 @@
 //            T_guess (about 1.4k entries expected above it) and up to 64
 //            bucket boundaries between T_guess and the top.  It publishes
 //            the plan while the others stream.
-//   stream   acc = residual + grad, one pass over rows of 1024 float4, two
-//            rows at a time.  About three quarters of the row pairs are dealt
-//            out statically, the rest are handed out at run time from eight
-//            counters (so workgroups that started late or run slow take
-//            fewer).  Every acc goes back to residual as a whole float4
-//            (non-temporal; partial lines would cost far more), and entries
-//            with key >= T_loc are also appended to an LDS list.  Nothing
-//            waits for the plan here.
+//   stream   acc = residual + grad, one pass over rows of 1024 float4, dealt
+//            round-robin (streaming workgroup m takes rows m, m + M, ...),
+//            two rows in flight per workgroup.  Every acc goes back to
+//            residual as a whole float4 (non-temporal; partial lines would
+//            cost far more), and entries with key >= T_loc are also appended
+//            to an LDS list.  Nothing waits for the plan here: wave 0 polls
+//            its flag once per row and loads it into LDS once published.
 //   publish  at the end of its share a workgroup reads the plan, keeps the
 //            list entries with key >= T_guess (the candidates), groups them
 //            by bucket and publishes them and their per-bucket counts with
@@ -89,7 +88,6 @@ constexpr int kOvfCap = 4096;                       // candidates one workgroup 
 constexpr int kFinishCap = 4096;                    // bucket entries a finisher orders in LDS
 constexpr int kSubBins = 2048;
 constexpr int kRawWords = 28672;                    // 112 KB of LDS shared by the phases
-constexpr int kMaxPairs = 256;                      // row pairs one workgroup remembers (for a re-read)
 constexpr int64_t kFastMinN = (int64_t)kMaxStepBlocks * kStepWaves * kSampleRounds * kSampleChunk;  // 2^19
 constexpr u32 kSpinLimit = 1u << 18;
 // plain pass + standalone general path
@@ -142,7 +140,6 @@ struct StepSet {
   Counter samp_grp[8], samp_all;  // sample phase arrivals (workgroup 0 polls samp_all)
   Counter main_grp[8], main_all;  // streaming workgroups published
   Counter main_go[8];             // 1 once main_all is complete
-  Counter rows_grp[8];            // row pairs handed out per group of streaming workgroups
   Counter plan_flag[8];           // 1 once the plan is published
   Counter verdict_flag[8];        // 1 = the plan held, 2 = run the exact path
   Counter bad;                    // low word: OR of kWhy* failures seen by the streaming workgroups
@@ -2117,10 +2114,6 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
   __shared__ u32 s_boff[kMaxBuckets];
   __shared__ u32 s_hdr[3];
   __shared__ u32 s_nlist, s_ovf, s_npub, s_novf, s_flag, s_floor, s_tlocbin;
-  __shared__ int64_t s_next[2];        // next row pair (double-buffered), -1 when none is left
-  __shared__ u32 s_pairs[kMaxPairs];  // row pairs this workgroup streamed
-  __shared__ u32 s_npairs;
-  __shared__ u32 s_pstate[2];      // plan polling state, by iteration parity
   __shared__ bool s_plan_in_lds;
   __shared__ u32 s_par;
   const int tid = threadIdx.x;
@@ -2138,20 +2131,13 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
   const float* __restrict__ g = a.grad;
   const v4f* __restrict__ gv = (const v4f*)(g + a.head);
   v4f* __restrict__ rv = (v4f*)(r + a.head);
-  // Aligned mode streams rows of NT float4, two at a time: pair p is rows
-  // 2p and 2p + 1.  Streaming workgroup m takes pair m first, then pairs
-  // handed out at run time (see next_pair), so workgroups on busier parts of
-  // the chip take fewer; the grid still sweeps the arrays front to back.
-  // Scalar mode streams tiles of NT * 8 elements, tile t to workgroup t % M.
+  // Aligned mode streams rows of NT float4: streaming workgroup m takes rows
+  // m, m + M, ... (measured against run-time hand-out of the last quarter of
+  // the rows in pairs: 66.1 against 66.4 us at n = 25.6M; the hand-out's
+  // barrier per pair costs more than the balance gains).  Scalar mode streams
+  // tiles of NT * 8 elements, tile t to workgroup t % M.
   constexpr int64_t TE = (int64_t)NT * 8;
   const int64_t nrows = a.vec ? (a.nv + NT - 1) / NT : (a.n + TE - 1) / TE;
-  const int64_t npairs = (nrows + 1) / 2;
-  const int ng = phase_groups(G);
-  // aligned mode: rows [0, R0) are dealt statically, one at a time: streaming
-  // workgroup m takes rows m, m + M, ...; the pairs of rows after them, about
-  // a quarter, are handed out at run time
-  const int64_t S = std::min<int64_t>(npairs, std::max<int64_t>(1, (npairs * 3 / 4) / M) * M);
-  const int64_t R0 = std::min<int64_t>(nrows, 2 * S);
 
   // sample loads first, then the first two rows, all in flight together
   float sg[kSampleRounds], sr[kSampleRounds];
@@ -2174,8 +2160,8 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
     }
   };
   if (b > 0 && a.vec) {
-    if ((int64_t)m < R0) load_row(m, ag, ar);
-    if ((int64_t)m + M < R0) load_row((int64_t)m + M, bg, br);
+    if ((int64_t)m < nrows) load_row(m, ag, ar);
+    if ((int64_t)m + M < nrows) load_row((int64_t)m + M, bg, br);
   }
 
   // ---------------- sample ----------------
@@ -2195,7 +2181,6 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
       s_ovf = 0;
       s_npub = 0;
       s_novf = 0;
-      s_npairs = 0;
       s_plan_in_lds = false;
     }
     if (b == 0)  // the exact path's state starts at zero
@@ -2358,110 +2343,57 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
       }
     };
     if (a.vec) {
-      // Rows [0, R0) are dealt statically (no barriers).  Pairs [S, npairs)
-      // (rows from R0 = 2S on), about a quarter, are handed out
-      // at run time: group x (= b % ng) hands out S + x, S + x + ng, ...
-      // from its counter.  Thread 0 asks for the next pair one iteration
-      // ahead; when its group has none left it looks at every group's
-      // counter and asks the one with the most left.
-      u32 xs = (u32)(b % ng);
-      u64 pend = 0;
-      bool more = npairs > S;
-      auto group_total = [&](u32 x) -> u64 {
-        const int64_t d = npairs - S - (int64_t)x;
-        return d > 0 ? (u64)((d + ng - 1) / ng) : 0u;
-      };
-      auto next_pair = [&]() -> int64_t {  // thread 0: completes the request in flight
-        if (!more) return -1;
-        int64_t p = S + (int64_t)xs + (int64_t)ng * (int64_t)pend;
-        for (int attempt = 0; p >= npairs && attempt < 16; ++attempt) {
-          u64 c[8];
-#pragma unroll
-          for (int x = 0; x < 8; ++x) c[x] = x < ng ? ld_agent64(&cs->rows_grp[x].v) : 0u;
-          u64 best_left = 0;
-          int best = -1;
-          for (int x = 0; x < ng; ++x) {
-            const u64 tot = group_total((u32)x);
-            const u64 left = tot > c[x] ? tot - c[x] : 0u;
-            if (left > best_left) {
-              best_left = left;
-              best = x;
-            }
+      // The plan is usually published while the rows stream: lane 0 of
+      // wave 0 polls its flag once per row (the answer is looked at a row
+      // later), and once it is seen, wave 0's lanes load the plan (state 1)
+      // and write it to LDS a row later (state 2), when the loads are back.
+      u32 st0 = 0;  // wave 0: 0 plan not seen, 1 loading, 2 in LDS
+      u64 pf = 0;   // lane 0 of wave 0: the flag poll in flight
+      u32 pw = 0, ph = 0;
+      auto poll_plan = [&]() {  // wave 0, every lane
+        if (st0 == 0) {
+          u32 seen = 0;
+          if (lane == 0) {
+            if (pf != 0) seen = 1;
+            else pf = ld_agent64(&cs->plan_flag[blockIdx.x & 7].v);
           }
-          if (best < 0) break;
-          xs = (u32)best;
-          pend = add_agent64(&cs->rows_grp[xs].v, 1u);
-          p = S + (int64_t)xs + (int64_t)ng * (int64_t)pend;
+          if (__builtin_amdgcn_readfirstlane(seen)) {
+            st0 = 1;
+            pw = ld_agent(&ctl->plan.lo[lane]);
+            if (lane < 3) ph = ld_agent(lane == 0 ? &ctl->plan.t_guess : lane == 1 ? &ctl->plan.nbuckets : &ctl->plan.valid);
+          }
+        } else if (st0 == 1) {
+          st0 = 2;
+          s_lo[lane] = pw;
+          if (lane < 3) s_hdr[lane] = ph;
         }
-        if (p >= npairs) {
-          more = false;
-          return -1;
-        }
-        return p;
       };
-      // static rows m, m + M, ...: buffer A holds one, B the next, and the
-      // load of the row after goes out before a buffer is processed (two
-      // rows of a workgroup in flight: more would cost the memory system)
-      if ((int64_t)m < R0) vec_row(m, ag, ar);
+      // rows m, m + M, ...: buffer A holds one, B the next, and the load of
+      // the row after goes out before a buffer is processed (two rows of a
+      // workgroup in flight: more would cost the memory system)
+      if ((int64_t)m < nrows) vec_row(m, ag, ar);
       sample_publish();
       bool arrived = false;
-      for (int64_t t = (int64_t)m + M; t < R0; t += 2 * (int64_t)M) {
-        if (t + M < R0) load_row(t + M, ag, ar);
+      for (int64_t t = (int64_t)m + M; t < nrows; t += 2 * (int64_t)M) {
+        if (t + M < nrows) load_row(t + M, ag, ar);
         vec_row(t, bg, br);
         if (!arrived) {
           sample_arrive();
           arrived = true;
         }
-        if (t + M >= R0) break;
-        if (t + 2 * (int64_t)M < R0) load_row(t + 2 * (int64_t)M, bg, br);
+        if (w == 0) poll_plan();
+        if (t + M >= nrows) break;
+        if (t + 2 * (int64_t)M < nrows) load_row(t + 2 * (int64_t)M, bg, br);
         vec_row(t + M, ag, ar);
+        if (w == 0) poll_plan();
       }
       if (!arrived) sample_arrive();
-      // The plan is usually published while the dynamic pairs stream: thread
-      // 0 polls its flag once per pair (state 1 = seen), and the iteration
-      // after, threads 0..66 load it into LDS (state 2 = in LDS).  The state
-      // is double-buffered by iteration parity like s_next.
-      if (tid == 0) {
-        if (more) pend = add_agent64(&cs->rows_grp[xs].v, 1u);
-        s_pstate[0] = 0;
-      }
-      for (int it = 0;; ++it) {
-        if (tid == 0) s_next[it & 1] = next_pair();
-        __syncthreads();
-        const int64_t p = s_next[it & 1];
-        const u32 pst = s_pstate[it & 1];
-        if (p < 0) {
-          s_plan_in_lds = pst == 2u;
-          break;
+      if (w == 0) {
+        if (st0 == 1) {  // loaded during the last row: to LDS
+          s_lo[lane] = pw;
+          if (lane < 3) s_hdr[lane] = ph;
         }
-        u64 pf = 0;
-        if (tid == 0) {
-          if (more) pend = add_agent64(&cs->rows_grp[xs].v, 1u);  // the one after
-          if (pst == 0) pf = ld_agent64(&cs->plan_flag[blockIdx.x & 7].v);
-          if (s_npairs < (u32)kMaxPairs) s_pairs[s_npairs] = (u32)p;
-          ++s_npairs;
-        }
-        u32 pw = 0;
-        if (pst == 1u && tid < kMaxBuckets + 3)
-          pw = ld_agent(tid < kMaxBuckets ? &ctl->plan.lo[tid] : tid == kMaxBuckets ? &ctl->plan.t_guess
-                                                               : tid == kMaxBuckets + 1 ? &ctl->plan.nbuckets
-                                                                                        : &ctl->plan.valid);
-        v4f gg[2], rr[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int64_t i = (2 * p + u) * NT + tid;
-          if (i < a.nv) {
-            gg[u] = __builtin_nontemporal_load(gv + i);
-            rr[u] = __builtin_nontemporal_load(rv + i);
-          }
-        }
-        vec_row(2 * p, gg[0], rr[0]);
-        vec_row(2 * p + 1, gg[1], rr[1]);
-        if (pst == 1u && tid < kMaxBuckets + 3) {
-          if (tid < kMaxBuckets) s_lo[tid] = pw;
-          else s_hdr[tid - kMaxBuckets] = pw;
-        }
-        if (tid == 0) s_pstate[(it + 1) & 1] = pst == 0u ? (pf != 0 ? 1u : 0u) : 2u;
+        if (lane == 0) s_plan_in_lds = st0 >= 1;
       }
       if (m == 0 && tid < a.head) keep_scalar(tid);
       if (m == M - 1)
@@ -2535,10 +2467,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
         auto rescan_rows = [&](int64_t t, int64_t nr) {
           rescan(a.head + 4 * t * NT, a.head + 4 * std::min<int64_t>(a.nv, (t + nr) * NT));
         };
-        for (int64_t t = m; t < R0; t += M) rescan_rows(t, 1);
-        const u32 np = std::min(s_npairs, (u32)kMaxPairs);
-        for (u32 q = 0; q < np; ++q) rescan_rows(2 * (int64_t)s_pairs[q], 2);
-        if (s_npairs > (u32)kMaxPairs) atomicOr(&s_ovf, 1u);  // rows not remembered: cannot re-read
+        for (int64_t t = m; t < nrows; t += M) rescan_rows(t, 1);
       } else {
         for (int64_t t = m; t < nrows; t += M) rescan(t * TE, std::min<int64_t>(a.n, (t + 1) * TE));
       }

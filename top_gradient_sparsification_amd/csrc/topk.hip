@@ -62,6 +62,7 @@
 #include <algorithm>
 #include <atomic>
 #include <climits>
+#include <cstddef>
 #include <cstring>
 #include <type_traits>
 
@@ -138,12 +139,13 @@ struct alignas(128) Counter {  // one cache line each
 // everything else that goes there.
 struct StepSet {
   Counter samp_grp[8], samp_all;  // sample phase arrivals (workgroup 0 polls samp_all)
-  Counter main_grp[8], main_all;  // streaming workgroups published
-  Counter main_go[8];             // 1 once main_all is complete
+  Counter main_grp[8], main_all;  // streaming workgroups published (the finishers poll main_all)
   Counter plan_flag[8];           // 1 once the plan is published
   Counter verdict_flag[8];        // 1 = the plan held, 2 = run the exact path
   Counter bad;                    // low word: OR of kWhy* failures seen by the streaming workgroups
+  alignas(128) u32 tot[kMaxBuckets];  // candidates per bucket over all workgroups (device adds)
 };
+constexpr int kSetCounters = (int)(offsetof(StepSet, tot) / sizeof(Counter));
 
 // Thread 0 only: sets all 8 copies of a replicated flag (no wait).
 __device__ __forceinline__ void flag_set(Counter* f, u64 v) {
@@ -229,7 +231,7 @@ static TopkLayout topk_layout(int64_t n, int64_t k) {
   L.bkt_buf = take(sizeof(u64) * (size_t)kMaxGenWG * (kGenThreads / kWave) * L.cand_cap);
   L.small = take(sizeof(u64) * (size_t)(kSmallMaxN / kSmallPer) * kSmallMaxK);
   L.pub = take(sizeof(u32) * ((size_t)kPlanCap + kMaxStepBlocks));
-  L.rcnt = take(sizeof(u32) * (size_t)kMaxStepBlocks * (kMaxBuckets / 2));
+  L.rcnt = take(sizeof(u16) * (size_t)kMaxStepBlocks * kMaxBuckets);
   L.slots = take(sizeof(Pair) * (size_t)kMaxBuckets * kSlotTotal);
   L.ovf = take(sizeof(Pair) * (size_t)kMaxStepBlocks * kOvfCap);
   L.total = off;
@@ -1583,7 +1585,7 @@ struct StepArgs {
   u32 slot_log;                  // each workgroup has S = 2^slot_log slots per bucket
   StepCtl* ctl;
   u32* pub;      // [kMaxStepBlocks][kPubCap] keys, then [kMaxStepBlocks] count | floor << 16
-  u32* rcnt;     // [kMaxStepBlocks][kMaxBuckets / 2] bucket counts, two u16 per word
+  u16* cnt_t;    // [kMaxBuckets][kMaxStepBlocks] workgroup b's candidates of bucket j at j * 256 + b
   u64* slots;    // [kMaxBuckets][G][S] candidates (packed pairs): bucket j's first S of workgroup b
   u64* ovf;      // [kMaxStepBlocks][kOvfCap] the rest of workgroup b's candidates, by bucket
   u32* gstate;   // the general path's state, cleared by workgroup 0
@@ -1875,22 +1877,15 @@ __device__ __forceinline__ void step_plan(const StepArgs& a, u32 par, u32* s_raw
 // verdict, then bucket f.  Returns false when the plan did not hold.
 __device__ __forceinline__ bool step_finish(const StepArgs& a, u32 par, u32* s_raw, u32* s_scan) {
   constexpr int NT = kStepThreads;
-  constexpr int NW = kStepWaves;
-  constexpr int kWords = kMaxBuckets / 2;                // count words per workgroup (two u16)
-  constexpr int kIters = kMaxStepBlocks * kWords / NT;   // count words per thread (all in one column)
   constexpr int kSlotIters = kSlotTotal / NT;            // slots per thread
   Pair* s_a = (Pair*)s_raw;                      // [kFinishCap] the bucket, as gathered
   Pair* s_b = (Pair*)(s_raw + 2 * kFinishCap);   // [kFinishCap] grouped by key sub-range
   u32* s_sub_cnt = s_raw + 4 * kFinishCap;       // [kSubBins]
   u32* s_sub_off = s_sub_cnt + kSubBins;         // [kSubBins]
-  u32* s_part = s_sub_off + kSubBins;            // [NW][kMaxBuckets] partial bucket totals
-  u32* s_cf = s_part + NW * kMaxBuckets;         // [kMaxStepBlocks] bucket f's count per workgroup
-  static_assert(4 * kFinishCap + 2 * kSubBins + NW * kMaxBuckets + kMaxStepBlocks <= kRawWords, "LDS");
-  static_assert(NT % kWords == 0, "a thread's count words share one column");
+  static_assert(4 * kFinishCap + 2 * kSubBins <= kRawWords, "LDS");
   __shared__ u32 s_plo[kMaxBuckets];
   __shared__ u32 s_phdr[3];
-  __shared__ u32 s_kmin, s_kmax, s_ok, s_wait, s_seen;
-  __shared__ u32 s_rpre[kMaxStepBlocks];  // where workgroup b's entries of bucket f start in s_a
+  __shared__ u32 s_kmin, s_kmax, s_ok, s_wait, s_seen, s_n;
   __shared__ int64_t s_start, s_mytot;
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -1909,63 +1904,87 @@ __device__ __forceinline__ bool step_finish(const StepArgs& a, u32 par, u32* s_r
   if (tid == kMaxBuckets + 2) s_phdr[2] = ld_agent(&ctl->plan.valid);
   for (int i = tid; i < kSubBins; i += NT) s_sub_cnt[i] = 0;
   if (tid == 0) {
-    s_wait = flag_wait(&cs->main_go[blockIdx.x & 7], &ctl->err) != 0 ? 1u : 0u;
+    s_wait = phase_wait(&cs->main_all, G, &ctl->err) ? 1u : 0u;  // every streaming workgroup published
     s_kmin = 0xFFFFFFFFu;
     s_kmax = 0;
+    s_n = 0;
   }
   __syncthreads();
-  // One round trip: the count matrix (G rows of 32 words, two u16 counts
-  // each; row 0, the planner, publishes nothing) and bucket f's slots.
+  // One round trip: bucket f's slots and the count of each slot's workgroup
+  // (the bucket's column of the count table), the bucket totals (wave 0,
+  // lane j = bucket j) and the failure word.
   const int nslots = G << slog;  // <= kSlotTotal
   u64 sv[kSlotIters];
+  u32 cw[kSlotIters];
+  u32 tj = 0;
   {
     const u64* mine = a.slots + ((int64_t)f << slog) * G;
-    u32 xw[kIters];
+    const u16* col = a.cnt_t + f * kMaxStepBlocks;
+    // Unconditional loads (an index out of range reads row 1's first slot
+    // instead), so all of them are in flight at once: a load under a branch
+    // would be waited for on its own.
 #pragma unroll
-    for (int it = 0; it < kIters; ++it) {
-      const int wd = tid + it * NT;
-      xw[it] = (wd >= kWords && wd < G * kWords) ? ld_agent(&a.rcnt[wd]) : 0u;
+    for (int q = 0; q < kSlotIters; ++q) {
+      const int i = tid + q * NT;
+      const int ic = i < nslots && (i >> slog) >= 1 ? i : (int)S;  // row 0 (the planner) publishes nothing
+      sv[q] = ld_agent64(mine + ic);
+      cw[q] = ld_agent_u16(col + (ic >> slog));
     }
 #pragma unroll
     for (int q = 0; q < kSlotIters; ++q) {
       const int i = tid + q * NT;
-      sv[q] = i < nslots ? ld_agent64(mine + i) : 0u;
+      if (!(i < nslots && (i >> slog) >= 1)) cw[q] = 0u;
     }
+    if (w == 0) tj = ld_agent(&cs->tot[lane]);
     if (tid == 0) s_seen = ld_agent((const u32*)&cs->bad.v);
-    // Thread tid holds column c = tid % 32 (buckets 2c, 2c + 1) of rows
-    // tid / 32 + 32 it.  Its sums, plus those of lane +- 32 (same column),
-    // then of the 16 waves, give the bucket totals; the threads of column
-    // f / 2 keep bucket f's count of each row.
-    const int c = tid % kWords;
-    u32 lo = 0, hi = 0;
+  }
+  // Gather the slots below their workgroup's count into s_a, in any order
+  // (the sort below ranks by key and index): one LDS append per wave and
+  // slot round.  Entries past a workgroup's S slots (rare) come from its
+  // overflow area, which holds its candidates past S grouped by bucket.
+  u32 gmin = 0xFFFFFFFFu, gmax = 0;
+  auto take_entry = [&](const Pair& p, u32 at) {
+    if (at < (u32)kFinishCap) s_a[at] = p;
+    const u32 kk = key_of_bits(p.bits);
+    gmin = std::min(gmin, kk);
+    gmax = std::max(gmax, kk);
+  };
 #pragma unroll
-    for (int it = 0; it < kIters; ++it) {
-      lo += xw[it] & 0xFFFFu;
-      hi += xw[it] >> 16;
-    }
-    lo += __shfl_xor(lo, kWords);
-    hi += __shfl_xor(hi, kWords);
-    if (lane < kWords) {
-      s_part[w * kMaxBuckets + 2 * c] = lo;
-      s_part[w * kMaxBuckets + 2 * c + 1] = hi;
-    }
-    if (c == (f >> 1)) {
+  for (int q = 0; q < kSlotIters; ++q) {
+    const int i = tid + q * NT;
+    const bool keep = ((u32)i & (S - 1u)) < cw[q];
+    const u64 bm = ballot(keep);
+    if (bm == 0) continue;  // wave-uniform
+    u32 base = 0;
+    if (lane == 0) base = atomicAdd(&s_n, (u32)__popcll(bm));
+    base = __builtin_amdgcn_readfirstlane(base);
+    if (keep) take_entry(unpack_pair(sv[q]), base + lanes_below(bm));
+  }
 #pragma unroll
-      for (int it = 0; it < kIters; ++it) s_cf[tid / kWords + it * (NT / kWords)] = (f & 1) ? xw[it] >> 16 : xw[it] & 0xFFFFu;
+  for (int q = 0; q < kSlotIters; ++q) {
+    const int i = tid + q * NT;
+    if (((u32)i & (S - 1u)) == 0u && cw[q] > S) {  // workgroup i >> slog overflowed in bucket f
+      const int row = i >> slog;
+      u32 off = 0;  // its overflow entries of buckets 0..f-1
+      for (int j = 0; j < f; ++j) {
+        const u32 cj = ld_agent_u16(a.cnt_t + j * kMaxStepBlocks + row);
+        off += cj > S ? cj - S : 0u;
+      }
+      const u64* src = a.ovf + (int64_t)row * kOvfCap + off;
+      const u32 extra = cw[q] - S;
+      const u32 at = atomicAdd(&s_n, extra);
+      for (u32 e = 0; e < extra; ++e) take_entry(unpack_pair(ld_agent64(src + e)), at + e);
     }
   }
-  __syncthreads();
-  {  // where each workgroup's entries of bucket f go: exclusive prefix over the rows
-    const u32 cnt = tid < kMaxStepBlocks ? s_cf[tid] : 0u;  // rows >= G hold 0
-    u32 tot;
-    const u32 ex = block_exclusive_sum<NT>(cnt, s_scan, tot);
-    if (tid < kMaxStepBlocks) s_rpre[tid] = ex;
+  gmin = wave_min(gmin);
+  gmax = wave_max(gmax);
+  if (lane == 0) {
+    atomicMin(&s_kmin, gmin);
+    atomicMax(&s_kmax, gmax);
   }
-  // verdict and bucket offsets in wave 0 (lane i = bucket i)
+  // verdict and bucket offsets in wave 0 (lane j = bucket j)
   if (w == 0) {
-    u32 t = 0;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) t += s_part[ww * kMaxBuckets + lane];
+    const u32 t = tj;
     const u32 nb = s_phdr[1];
     bool plan_ok = s_wait && s_phdr[2] == 1u && nb >= 1 && nb <= (u32)kMaxBuckets;
     if (plan_ok) {
@@ -2001,49 +2020,11 @@ __device__ __forceinline__ bool step_finish(const StepArgs& a, u32 par, u32* s_r
   if (!s_ok) return false;
   const int64_t mystart = s_start, mytot = s_mytot;
   if (mytot == 0 || mystart >= a.k) return true;  // no rank below k here
-  const int m = (int)mytot;  // <= kFinishCap (verdict)
-  {  // gather: the slots in hand, then (rarely) entries past a workgroup's S slots
-    u32 kmin = 0xFFFFFFFFu, kmax = 0;
-    auto take_entry = [&](const Pair& p, u32 at) {
-      s_a[at] = p;
-      const u32 kk = key_of_bits(p.bits);
-      kmin = std::min(kmin, kk);
-      kmax = std::max(kmax, kk);
-    };
-    u32 cq[kSlotIters], pq[kSlotIters];  // all LDS reads first, then the writes
-#pragma unroll
-    for (int q = 0; q < kSlotIters; ++q) {
-      const int row = std::min((tid + q * NT) >> slog, kMaxStepBlocks - 1);
-      cq[q] = s_cf[row];
-      pq[q] = s_rpre[row];
-    }
-#pragma unroll
-    for (int q = 0; q < kSlotIters; ++q) {
-      const int i = tid + q * NT;
-      const u32 sl = (u32)i & (S - 1u);
-      if (i < nslots && sl < cq[q]) take_entry(unpack_pair(sv[q]), pq[q] + sl);
-    }
-    if (tid < G) {
-      const u32 cnt = s_cf[tid];
-      if (cnt > S) {  // workgroup tid put entries of bucket f in its overflow area
-        u32 off = 0;  // its overflow entries of buckets 0..f-1 (its counts, read again)
-        for (int j = 0; j < f; ++j) {
-          const u32 x = ld_agent(&a.rcnt[tid * kWords + (j >> 1)]);
-          const u32 cj = (j & 1) ? x >> 16 : x & 0xFFFFu;
-          off += cj > S ? cj - S : 0u;
-        }
-        const u64* src = a.ovf + (int64_t)tid * kOvfCap + off;
-        for (u32 sl = S; sl < cnt; ++sl) take_entry(unpack_pair(ld_agent64(src + (sl - S))), s_rpre[tid] + sl);
-      }
-    }
-    kmin = wave_min(kmin);
-    kmax = wave_max(kmax);
-    if (lane == 0) {
-      atomicMin(&s_kmin, kmin);
-      atomicMax(&s_kmax, kmax);
-    }
+  if ((int64_t)s_n != mytot) {  // the column and the total disagree: cannot happen
+    if (tid == 0) atomicOr(&ctl->err, 1u << 2);
+    return true;
   }
-  __syncthreads();
+  const int m = (int)mytot;  // <= kFinishCap (verdict)
   // Split [kmin, kmax] into kSubBins equal key sub-ranges numbered from the
   // top and group the entries by sub-range (counting sort); inside a
   // sub-range an entry's place is the number of its entries that rank before
@@ -2188,9 +2169,9 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
     if (tid == 0) s_par = par_ld & 1u;
     __syncthreads();
     if (b == 0) {  // the other counter set is cleared for the next launch
-      constexpr int kSetWords = (int)(sizeof(StepSet) / sizeof(Counter));
-      Counter* other = (Counter*)&ctl->set[s_par ^ 1u];
-      if (tid < kSetWords) st_agent64(&other[tid].v, 0u);
+      StepSet* other = &ctl->set[s_par ^ 1u];
+      if (tid < kSetCounters) st_agent64(&((Counter*)other)[tid].v, 0u);
+      if (tid >= 128 && tid < 128 + kMaxBuckets) st_agent(&other->tot[tid - 128], 0u);
     }
 #pragma unroll
     for (int j = 0; j < kSampleRounds; ++j) {
@@ -2269,7 +2250,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
     sample_arrive();
     step_plan(a, par, s_raw, s_scan);
     __syncthreads();
-    if (tid == 0 && phase_arrive(cs->main_grp, &cs->main_all, G)) flag_set(cs->main_go, 1u);
+    if (tid == 0) phase_arrive(cs->main_grp, &cs->main_all, G);
   } else {
     // ---------------- stream ----------------
     const u32 tloc = a.loc_mode == 1u ? 0x7FFFFFFFu : a.loc_mode == 2u ? 0u : s_tlocbin << kHistShift;
@@ -2496,11 +2477,14 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
         const u32 t = s_ovt[q];
         st_agent64(dst + s_boff[t >> 16] + (t & 0xFFFFu), pack_pair(s_ovl[q]));
       }
-      if (tid < kMaxBuckets / 2)
-        st_agent(&a.rcnt[b * (kMaxBuckets / 2) + tid], s_bcnt[2 * tid] | (s_bcnt[2 * tid + 1] << 16));
+      if (tid < kMaxBuckets) {  // this workgroup's count of bucket tid, and the bucket's total
+        const u32 c = s_bcnt[tid];
+        st_agent_u16(&a.cnt_t[tid * kMaxStepBlocks + b], (u16)c);
+        if (c) (void)add_agent_relaxed(&cs->tot[tid], c);
+      }
     } else {
       // cannot publish: the plan fails
-      if (tid < kMaxBuckets / 2) st_agent(&a.rcnt[b * (kMaxBuckets / 2) + tid], 0u);
+      if (tid < kMaxBuckets) st_agent_u16(&a.cnt_t[tid * kMaxStepBlocks + b], 0);
       if (tid == 0) or_agent((u32*)&cs->bad.v, fail);
     }
     // Every store of this workgroup -- acc included -- has completed at
@@ -2509,7 +2493,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a) {
     // entries of residual, stores that must land after the acc stores.
     wait_all_memory();
     __syncthreads();
-    if (tid == 0 && phase_arrive(cs->main_grp, &cs->main_all, G)) flag_set(cs->main_go, 1u);
+    if (tid == 0) phase_arrive(cs->main_grp, &cs->main_all, G);
   }
 
   // ---------------- finish ----------------
@@ -2727,7 +2711,7 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
     while (path != 6 && ((int64_t)G << (sa.slot_log + 1)) <= kSlotTotal) ++sa.slot_log;
     sa.ctl = ctl;
     sa.pub = (u32*)(ws + L.pub);
-    sa.rcnt = (u32*)(ws + L.rcnt);
+    sa.cnt_t = (u16*)(ws + L.rcnt);
     sa.slots = (u64*)(ws + L.slots);
     sa.ovf = (u64*)(ws + L.ovf);
     sa.gstate = (u32*)gs;

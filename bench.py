@@ -252,11 +252,11 @@ def parse():
 # the 256 MiB copy of --copy-calibration.  Valid only for the k_step
 # source they were taken on: `source_sha256` is the hash of csrc/topk.hip then.
 MEASURED_TRAFFIC = {
-    "source_sha256": "98e195917f823db0f4d19ab7b86cf4b242c76beb678364db3955c32b8b4692ca",
-    # FETCH_SIZE 103,058.9 KiB x (262,144 / 131,083.5: the copy's true read over its counter)
-    "fetch_bytes": 211046059,
-    # WRITE_SIZE 102,288.4 KiB x 1.0 (the copy's counter read exactly 262,144 KiB)
-    "write_bytes": 104743280,
+    "source_sha256": "1e9344826a1cfe0781276b765dffe873623cba5774448a45cf418213bc99b000",
+    # FETCH_SIZE 102,920.8 KiB x (262,144 / 131,083.5: the copy's true read over its counter)
+    "fetch_bytes": 210763306,
+    # WRITE_SIZE 102,792.8 KiB x 1.0 (the copy's counter read exactly 262,144 KiB)
+    "write_bytes": 105259827,
 }
 
 

@@ -74,8 +74,8 @@ def test_ties_at_lambda_and_special_values(tgs_gpu):
 
 
 def test_stash_overflow_rescan(tgs_gpu):
-    """lambda = 0: every entry qualifies, so every workgroup's stash overflows
-    and the emit pass rescans acc in index order."""
+    """lambda = 0: every entry qualifies, so every wave's stash overflows and
+    the emit pass rescans acc in index order."""
     rng = np.random.default_rng(3)
     n = 2_000_000
     grad = rng.standard_normal(n).astype(np.float32)
@@ -84,14 +84,15 @@ def test_stash_overflow_rescan(tgs_gpu):
         assert_thr_equal(gpu_thr(tgs_gpu, grad, res, 0.0, cap), oracle_thr(grad, res, 0.0, cap), "cap=%d" % cap)
 
 
-@pytest.mark.parametrize("layout", ["dense", "clustered"])
+@pytest.mark.parametrize("layout", ["dense", "clustered", "round_edge"])
 def test_stash_overflow_positive_lambda(tgs_gpu, layout):
-    """lambda > 0 with more qualifying entries than a stash holds: every
-    workgroup (dense: 38% of N(0,1) has |x| >= 0.5) or only those over one
-    index range (clustered) overflow.  The pass has already set the stashed
-    entries' residual to +0, so the rescan must skip them and number the
-    rest from the stash's end, and stashed entries past the capacity must get
-    acc back."""
+    """lambda > 0 with more qualifying entries than a stash holds: every wave
+    (dense: 38% of N(0,1) has |x| >= 0.5) or only the waves whose rows fall in
+    one index range (clustered; round_edge: a range across the boundary of the
+    first two rounds of 4096 rows of 256 entries) overflow.  The pass has
+    already set the stashed entries' residual to +0, so the rescan must skip
+    them and number the rest from the stash's end, and stashed entries past
+    the capacity must get acc back."""
     rng = np.random.default_rng(4)
     n = 2_000_003
     grad = rng.standard_normal(n).astype(np.float32)
@@ -99,6 +100,8 @@ def test_stash_overflow_positive_lambda(tgs_gpu, layout):
     lam = 0.5 if layout == "dense" else 4.0
     if layout == "clustered":
         grad[700_000:760_000] = rng.uniform(5.0, 6.0, 60_000).astype(np.float32)
+    if layout == "round_edge":
+        grad[1_000_000:1_100_000] = rng.uniform(5.0, 6.0, 100_000).astype(np.float32)
     exp_all = oracle_thr(grad, res, lam, n)
     c = exp_all[2]
     for cap in (n, c, c - 1, c // 3, 7, 0):

@@ -5,23 +5,31 @@
 // top-k, where the number of entries sent is whatever a constant threshold
 // lets through, run with error feedback.
 //
-// Two launches, no global atomics:
-//   k_thr_pass  each workgroup streams its contiguous chunk once (two tiles
-//               in flight): acc = residual + grad; qualifying entries
-//               (key(acc) >= key(lambda)) are counted and the first
-//               `stash_cap` of them are kept, in index order, in the
-//               workgroup's stash; residual <- +0 for those, acc for every
-//               other entry (non-temporal); the count goes to cnt[wg].
-//   k_thr_emit  each workgroup adds up the counts of the workgroups before it
-//               (its output offset) and copies its stash to the output while
-//               the position is below `capacity`; stashed entries past it get
-//               acc back in the residual.  A workgroup whose stash overflowed
-//               and whose later entries are still below `capacity` rescans
-//               its chunk of acc (in residual) for them.  The last workgroup
-//               writes the total count.
-// The output is in ascending index order: chunks are contiguous and in
-// workgroup order, and inside a chunk entries are ranked by (tile, wave, lane,
-// component), which is index order.
+// Two launches:
+//   k_thr_pass  one block of 256 float4 slots (1024 entries) per 256-thread
+//               workgroup, a grid of one workgroup per block: the hardware
+//               hands blocks out in order, so the stretch of memory the chip
+//               streams at any moment stays short (a persistent grid whose
+//               workgroups walk their own rows drifts apart over a long
+//               vector and streams slower).  acc = residual + grad;
+//               qualifying entries (key(acc) >= key(lambda)) are ranked in
+//               index order inside the block (ballots and one block scan of
+//               the wave counts), the first `cap` go to the block's stash,
+//               residual <- +0 for those and acc for every other entry
+//               (non-temporal), and the count goes to cnt[block].
+//   k_thr_emit  one workgroup per group of 1024 blocks, numbered by a ticket
+//               in the order they start.  The group's offset in the output
+//               comes from a scan with decoupled look-back (each group
+//               publishes its total, then its inclusive prefix, and sums its
+//               predecessors' words back to the nearest prefix).  Stashed
+//               entries are copied while their position is below `capacity`
+//               and get acc back past it.  A block whose entries outran its
+//               stash and still have positions below the capacity is scanned
+//               again (acc is in residual) by one wave, with the pass's ranks.
+//               The last group writes the count.
+// The output is in ascending index order: blocks are in index order, and
+// inside a block entries are ranked by (wave, lane, component), which is
+// index order (the head before the first slot, the tail after the last).
 #include <algorithm>
 #include <climits>
 
@@ -30,164 +38,37 @@
 
 namespace tgs {
 
-constexpr int kThrThreads = 1024;
-constexpr int kThrWaves = kThrThreads / kWave;
-constexpr int kThrMaxBlocks = 2048;
+constexpr int kPassThreads = 256;               // one float4 slot per thread
+constexpr int kPassWaves = kPassThreads / kWave;
+constexpr u32 kBlockCap = 32;                    // stash slots per block: 1/32 of its entries
+constexpr int kEmitThreads = 1024;               // one block per thread
+constexpr int kEmitWaves = kEmitThreads / kWave;
+constexpr u64 kFlagTotal = 1ull << 62;   // a group's word: its own total is known
+constexpr u64 kFlagPrefix = 2ull << 62;  // a group's word: the total up to and including it is known
+constexpr u32 kLookbackSpins = 1u << 22;
 
 struct ThrArgs {
   const float* grad;
   float* residual;
   int64_t n;
-  int64_t head;  // scalar elements before the 16-byte aligned part (vector mode)
-  int64_t nv;    // float4 vectors (0 in scalar mode)
-  bool vec;
+  int64_t head;     // entries before the first float4 slot (vector mode; 0 in scalar mode)
+  int64_t nv;       // float4 slots (vector mode: 16-byte aligned; scalar mode: floor(n / 4) groups of 4)
+  int64_t tail0;    // first entry after the slots: head + 4 nv
+  int64_t nblocks;  // blocks of 256 slots (at least 1 when n > 0: block 0 holds the head, the last the tail)
+  int64_t ngroups;  // emit groups of kEmitThreads blocks
   u32 klam;
   const float* lam_dev;  // when set, the threshold is key(*lam_dev) (read on the device) instead of klam
-  u32* cnt;      // [G]
-  Pair* stash;   // [G][stash_cap]
-  int64_t stash_cap;
+  u32* cnt;         // [nblocks]
+  Pair* stash;      // [nblocks][kBlockCap]
+  u64* status;      // [ngroups] look-back words
+  u32* ticket;      // emit groups started
+  u32* err;         // device error word
   int32_t* out_idx;
   float* out_val;
   int64_t capacity;
   int64_t* d_count;
 };
 
-// Walks this workgroup's chunk in index order.  For each tile, `load(i, bits[4],
-// idx[4], nval)` fills up to 4 values of thread slot i; qualifying entries get
-// consecutive ranks starting at `rank0`, and `put(rank, idx, bits)` is called
-// for each.  Returns the number of qualifying entries in the chunk.
-template <class Load, class Put>
-__device__ int64_t ordered_walk(const ThrArgs& a, Load load, Put put, u32 (*s_wt)[kThrWaves]) {
-  const int tid = threadIdx.x;
-  const int w = tid / kWave;
-  const int G = gridDim.x;
-  int64_t running = 0;
-  int par = 0;
-  // chunk in "slots": a slot is one float4 (vector mode) or one float (scalar)
-  const int64_t units = a.vec ? a.nv : a.n;
-  const int64_t per = (units + G - 1) / G;
-  const int64_t ub = std::min<int64_t>(units, (int64_t)blockIdx.x * per);
-  const int64_t ue = std::min<int64_t>(units, ub + per);
-  // vector mode: head elements belong to workgroup 0 (before its chunk) and the
-  // tail to the last workgroup (after its chunk); both run as one extra tile.
-  const bool has_head = a.vec && blockIdx.x == 0 && a.head > 0;
-  const bool has_tail = a.vec && blockIdx.x == G - 1 && a.head + 4 * a.nv < a.n;
-  const int64_t tail0 = a.head + 4 * a.nv;
-  const int64_t ntiles_main = (ue - ub + kThrThreads - 1) / kThrThreads;
-  const int64_t tail_tiles = has_tail ? (a.n - tail0 + 4 * kThrThreads - 1) / (4 * kThrThreads) : 0;
-  const int64_t ntiles = (has_head ? 1 : 0) + ntiles_main + tail_tiles;
-  for (int64_t t = 0; t < ntiles; ++t) {
-    u32 bits[4] = {0, 0, 0, 0};
-    int64_t idx[4] = {0, 0, 0, 0};
-    int nval = 0;
-    int64_t tt = t;
-    int kind = 1;  // 0 head, 1 main, 2 tail
-    if (has_head) {
-      if (tt == 0) kind = 0;
-      else tt -= 1;
-    }
-    if (kind == 1 && tt >= ntiles_main) {
-      kind = 2;
-      tt -= ntiles_main;
-    }
-    if (kind == 0) {
-      if (tid < a.head) {
-        idx[0] = tid;
-        nval = 1;
-        load(-1, idx, bits, nval);
-      }
-    } else if (kind == 1) {
-      int64_t i = ub + tt * kThrThreads + tid;
-      if (i < ue) {
-        if (a.vec) {
-          int64_t e = a.head + 4 * i;
-          idx[0] = e;
-          idx[1] = e + 1;
-          idx[2] = e + 2;
-          idx[3] = e + 3;
-          nval = 4;
-        } else {
-          idx[0] = i;
-          nval = 1;
-        }
-        load(i, idx, bits, nval);
-      }
-    } else {
-      // tail: up to 4 scalar elements per thread, in index order
-      int64_t base = tail0 + tt * 4 * kThrThreads + 4 * (int64_t)tid;
-      for (int c = 0; c < 4; ++c)
-        if (base + c < a.n) {
-          idx[c] = base + c;
-          nval = c + 1;
-        }
-      if (nval) load(-2, idx, bits, nval);
-    }
-    bool q[4];
-    u32 mine = 0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      q[c] = c < nval && key_of_bits(bits[c]) >= a.klam;
-      mine += q[c];
-    }
-    u32 below = 0, wtot = 0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      u64 m = ballot(q[c]);
-      below += lanes_below(m);
-      wtot += (u32)__popcll(m);
-    }
-    if (lane_id() == 0) s_wt[par][w] = wtot;
-    __syncthreads();
-    u32 woff = 0, ttot = 0;
-#pragma unroll
-    for (int ww = 0; ww < kThrWaves; ++ww) {
-      u32 v = s_wt[par][ww];
-      if (ww < w) woff += v;
-      ttot += v;
-    }
-    if (mine) {
-      int64_t r = running + woff + below;
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (q[c]) put(r++, idx[c], bits[c]);
-    }
-    running += ttot;
-    par ^= 1;
-  }
-  return running;
-}
-
-// Ranks of one tile's qualifying entries (bit c of qmask: component c of
-// this thread qualifies), in index order: returns the rank of this thread's
-// first one and advances `running` past the tile.  Every thread calls it.
-__device__ __forceinline__ u32 tile_rank(u32 qmask, u32& running, u32 (*s_wt)[kThrWaves], int& par) {
-  const int w = threadIdx.x / kWave;
-  u32 below = 0, wtot = 0;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const u64 m = ballot((qmask >> c) & 1u);
-    below += lanes_below(m);
-    wtot += (u32)__popcll(m);
-  }
-  if (lane_id() == 0) s_wt[par][w] = wtot;
-  __syncthreads();
-  u32 woff = 0, ttot = 0;
-#pragma unroll
-  for (int ww = 0; ww < kThrWaves; ++ww) {
-    const u32 v = s_wt[par][ww];
-    if (ww < w) woff += v;
-    ttot += v;
-  }
-  const u32 r0 = running + woff + below;
-  running += ttot;
-  par ^= 1;
-  return r0;
-}
-
-// The pass writes +0 to the residual of every qualifying entry that goes to
-// the stash (rank < stash_cap), acc everywhere else: in the usual case
-// (count <= capacity, no overflow) every stashed entry is emitted and the
-// emit pass only copies.  Entries the capacity turns away get acc back.
 // The arguments with the threshold key in place (read from the device when
 // it comes from there).
 __device__ __forceinline__ ThrArgs with_key(const ThrArgs& in) {
@@ -196,164 +77,297 @@ __device__ __forceinline__ ThrArgs with_key(const ThrArgs& in) {
   return a;
 }
 
-__global__ __launch_bounds__(kThrThreads) void k_thr_pass(ThrArgs ain) {
-  const ThrArgs a = with_key(ain);
-  __shared__ u32 s_wt[2][kThrWaves];
-  const float* __restrict__ g = a.grad;
-  float* __restrict__ r = a.residual;
-  Pair* stash = a.stash + (int64_t)blockIdx.x * a.stash_cap;
-  const int64_t cap = a.stash_cap;
-  const int tid = threadIdx.x;
-  if (!a.vec) {
-    auto load = [&](int64_t, const int64_t* idx, u32* bits, int nval) {
-      for (int c = 0; c < nval; ++c) {
-        float x = r[idx[c]] + g[idx[c]];
-        r[idx[c]] = x;
-        bits[c] = __float_as_uint(x);
-      }
-    };
-    auto put = [&](int64_t rank, int64_t idx, u32 bits) {
-      if (rank < cap) {
-        stash[rank] = Pair{(int32_t)idx, bits};
-        r[idx] = 0.0f;  // after this thread's own acc store to it
-      }
-    };
-    const int64_t total = ordered_walk(a, load, put, s_wt);
-    if (tid == 0) a.cnt[blockIdx.x] = (u32)total;
-    return;
+// Slot i: 4 consecutive entries, as one float4 (vector mode) or four floats
+// (scalar mode, grad and residual not equally aligned).
+template <bool VEC>
+__device__ __forceinline__ v4f load_slot(const float* p, const ThrArgs& a, int64_t i) {
+  if (VEC) return __builtin_nontemporal_load((const v4f*)(p + a.head) + i);
+  const float* q = p + 4 * i;
+  return v4f{q[0], q[1], q[2], q[3]};
+}
+template <bool VEC>
+__device__ __forceinline__ void store_slot(float* p, const ThrArgs& a, int64_t i, v4f v) {
+  if (VEC) {
+    __builtin_nontemporal_store(v, (v4f*)(p + a.head) + i);
+  } else {
+    float* q = p + 4 * i;
+    q[0] = v.x;
+    q[1] = v.y;
+    q[2] = v.z;
+    q[3] = v.w;
   }
-  // vector mode: the partition of ordered_walk (which the emit pass's rescan
-  // uses): head tile (workgroup 0), main tiles of one float4 per thread with
-  // two tiles in flight, tail tile (last workgroup)
-  const int G = gridDim.x;
-  const int64_t per = (a.nv + G - 1) / G;
-  const int64_t ub = std::min<int64_t>(a.nv, (int64_t)blockIdx.x * per);
-  const int64_t ue = std::min<int64_t>(a.nv, ub + per);
-  const int64_t tail0 = a.head + 4 * a.nv;
-  u32 running = 0;
-  int par = 0;
-  auto scalar_tile = [&](int64_t i0, int64_t cnt) {  // entries i0 + tid for tid < cnt (< 4)
-    const bool in = tid < cnt;
-    const int64_t i = i0 + tid;
-    float x = 0.0f;
-    u32 qm = 0;
-    if (in) {
-      x = r[i] + g[i];
-      qm = key_of(x) >= a.klam ? 1u : 0u;
-    }
-    const u32 rk = tile_rank(qm, running, s_wt, par);
-    if (in) {
-      if (qm && rk < cap) {
-        stash[rk] = Pair{(int32_t)i, __float_as_uint(x)};
-        x = 0.0f;
-      }
-      r[i] = x;
-    }
-  };
-  if (blockIdx.x == 0 && a.head > 0) scalar_tile(0, a.head);
-  const v4f* __restrict__ gv = (const v4f*)(g + a.head);
-  v4f* __restrict__ rv = (v4f*)(r + a.head);
-  const int64_t ntiles = (ue - ub + kThrThreads - 1) / kThrThreads;
-  auto load = [&](int64_t t, v4f& gg, v4f& rr) {
-    const int64_t i = ub + t * kThrThreads + tid;
-    if (t < ntiles && i < ue) {
-      gg = __builtin_nontemporal_load(gv + i);
-      rr = __builtin_nontemporal_load(rv + i);
-    }
-  };
-  auto step = [&](int64_t t, const v4f& gg, const v4f& rr) {
-    const int64_t i = ub + t * kThrThreads + tid;
-    const bool in = i < ue;
-    v4f acc = rr + gg;
-    u32 qm = 0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) qm |= (in && key_of(acc[c]) >= a.klam ? 1u : 0u) << c;
-    u32 rk = tile_rank(qm, running, s_wt, par);
-    if (in) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if ((qm >> c) & 1u) {
-          if (rk < cap) {
-            stash[rk] = Pair{(int32_t)(a.head + 4 * i + c), __float_as_uint(acc[c])};
-            acc[c] = 0.0f;
-          }
-          ++rk;
-        }
-      __builtin_nontemporal_store(acc, rv + i);
-    }
-  };
-  v4f ga, ra, gb, rb;
-  load(0, ga, ra);
-  load(1, gb, rb);
-  for (int64_t t = 0; t < ntiles; t += 2) {
-    step(t, ga, ra);
-    load(t + 2, ga, ra);
-    if (t + 1 >= ntiles) break;
-    step(t + 1, gb, rb);
-    load(t + 3, gb, rb);
-  }
-  if (blockIdx.x == G - 1 && tail0 < a.n) scalar_tile(tail0, a.n - tail0);
-  if (tid == 0) a.cnt[blockIdx.x] = running;
 }
 
-__global__ __launch_bounds__(kThrThreads) void k_thr_emit(ThrArgs ain) {
+// Rank inside the wave of this lane's first qualifying component (bit c of
+// qm: component c qualifies), lanes in order and components in order inside
+// a lane; `tot` gets the wave's count.  Every lane of the wave calls it.
+__device__ __forceinline__ u32 wave_rank4(u32 qm, u32& tot) {
+  u32 below = 0;
+  tot = 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const u64 m = ballot((qm >> c) & 1u);
+    below += lanes_below(m);
+    tot += (u32)__popcll(m);
+  }
+  return below;
+}
+
+// One wave's part of block b, in index order: the head (wave 0 of block 0),
+// the wave's 64 slots (this lane's: `slot`, present when `in`), the tail (the
+// last wave of the last block).
+struct WavePart {
+  bool has_head, has_tail;
+  int64_t slot;  // this lane's slot
+  bool in;       // the slot exists
+};
+
+__device__ __forceinline__ WavePart wave_part(const ThrArgs& a, int64_t b, int w) {
+  WavePart p;
+  p.has_head = b == 0 && w == 0 && a.head > 0;
+  p.has_tail = b == a.nblocks - 1 && w == kPassWaves - 1 && a.tail0 < a.n;
+  p.slot = b * kPassThreads + w * kWave + lane_id();
+  p.in = p.slot < a.nv;
+  return p;
+}
+
+// The pass.
+template <bool VEC>
+__global__ __launch_bounds__(kPassThreads) void k_thr_pass(ThrArgs ain) {
   const ThrArgs a = with_key(ain);
-  __shared__ u32 s_wt[2][kThrWaves];
-  __shared__ u32 s_scan[kThrWaves + 1];
+  __shared__ u32 s_w[kPassWaves];
+  const float* __restrict__ g = a.grad;
+  float* __restrict__ r = a.residual;
   const int tid = threadIdx.x;
-  const int b = blockIdx.x;
-  u32 before = 0;
-  for (int i = tid; i < b; i += kThrThreads) before += a.cnt[i];
-  u32 prefix_u;
-  block_exclusive_sum<kThrThreads>(before, s_scan, prefix_u);
-  const int64_t prefix = prefix_u;
-  const int64_t mine = a.cnt[b];
-  if (b == gridDim.x - 1 && tid == 0) *a.d_count = prefix + mine;
-  if (mine == 0) return;
-  const int64_t take = std::max<int64_t>(0, std::min<int64_t>(mine, a.capacity - prefix));
-  // stashed entries (ranks below stash_cap; their residual is +0): emitted
-  // below `take`, given acc back above it
-  const int64_t stashed = std::min<int64_t>(mine, a.stash_cap);
-  const Pair* stash = a.stash + (int64_t)b * a.stash_cap;
-  float* rw = a.residual;
-  for (int64_t j = tid; j < stashed; j += kThrThreads) {
-    const Pair e = stash[j];
-    if (j < take) {
-      a.out_idx[prefix + j] = e.idx;
-      a.out_val[prefix + j] = __uint_as_float(e.bits);
-    } else {
-      rw[e.idx] = __uint_as_float(e.bits);
+  const int w = tid / kWave;
+  const int lane = lane_id();
+  const int64_t b = blockIdx.x;
+  // the look-back words and the ticket of the emit launch that follows
+  if (tid == 0 && b < a.ngroups) st_agent64(a.status + b, 0ull);
+  if (tid == 0 && b == 0) st_agent(a.ticket, 0u);
+  const WavePart p = wave_part(a, b, w);
+  v4f gg = {0, 0, 0, 0}, rr = gg;
+  if (p.in) {
+    gg = load_slot<VEC>(g, a, p.slot);
+    rr = load_slot<VEC>(r, a, p.slot);
+  }
+  // head / tail: up to 3 single entries, lane c holding entry i0 + c
+  float xh = 0.0f, xt = 0.0f;
+  bool qh = false, qt = false;
+  if (p.has_head && lane < a.head) {
+    xh = r[lane] + g[lane];
+    qh = key_of(xh) >= a.klam;
+  }
+  if (p.has_tail && lane < a.n - a.tail0) {
+    xt = r[a.tail0 + lane] + g[a.tail0 + lane];
+    qt = key_of(xt) >= a.klam;
+  }
+  v4f acc = rr + gg;
+  u32 qm = 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) qm |= (p.in && key_of(acc[c]) >= a.klam ? 1u : 0u) << c;
+  const u64 mh = ballot(qh), mt = ballot(qt);
+  u32 mtot;
+  const u32 mbelow = wave_rank4(qm, mtot);
+  const u32 hcnt = (u32)__popcll(mh);
+  const u32 wtot = hcnt + mtot + (u32)__popcll(mt);
+  if (lane == 0) s_w[w] = wtot;
+  __syncthreads();
+  u32 woff = 0, btot = 0;
+#pragma unroll
+  for (int i = 0; i < kPassWaves; ++i) {
+    const u32 v = s_w[i];
+    woff += i < w ? v : 0u;
+    btot += v;
+  }
+  Pair* __restrict__ stash = a.stash + b * kBlockCap;
+  if (qh) {
+    const u32 s = woff + lanes_below(mh);
+    if (s < kBlockCap) {
+      stash[s] = Pair{(int32_t)lane, __float_as_uint(xh)};
+      xh = 0.0f;
     }
   }
-  if (take <= a.stash_cap) return;
-  // the stash overflowed and entries past it are to be emitted: rescan acc
-  // (held in residual) in index order.  Stashed entries now hold +0, which
-  // qualifies only when lambda is 0: then every entry qualifies and the
-  // rescan's ranks are the pass's; otherwise the rescan sees only the
-  // entries past the stash, so their ranks start at stash_cap.
-  const float* r = a.residual;
-  const v4f* rv = (const v4f*)(r + a.head);
-  auto load = [&](int64_t i, const int64_t* idx, u32* bits, int nval) {
-    if (i >= 0 && a.vec) {
-      v4f x = rv[i];
-      bits[0] = __float_as_uint(x.x);
-      bits[1] = __float_as_uint(x.y);
-      bits[2] = __float_as_uint(x.z);
-      bits[3] = __float_as_uint(x.w);
-    } else {
-      for (int c = 0; c < nval; ++c) bits[c] = __float_as_uint(r[idx[c]]);
+  if (qm) {
+    u32 s = woff + hcnt + mbelow;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if ((qm >> c) & 1u) {
+        if (s < kBlockCap) {
+          stash[s] = Pair{(int32_t)(a.head + 4 * p.slot + c), __float_as_uint(acc[c])};
+          acc[c] = 0.0f;
+        }
+        ++s;
+      }
+  }
+  if (qt) {
+    const u32 s = woff + hcnt + mtot + lanes_below(mt);
+    if (s < kBlockCap) {
+      stash[s] = Pair{(int32_t)(a.tail0 + lane), __float_as_uint(xt)};
+      xt = 0.0f;
+    }
+  }
+  if (p.in) store_slot<VEC>(r, a, p.slot, acc);
+  if (p.has_head && lane < a.head) r[lane] = xh;
+  if (p.has_tail && lane < a.n - a.tail0) r[a.tail0 + lane] = xt;
+  if (tid == 0) a.cnt[b] = btot;
+}
+
+// Block b scanned again by one wave (every lane calls it), its four wave
+// parts in order: its qualifying entries past the first `nst` (the stashed
+// ones, whose residual the pass set to +0) go to the output at o + their
+// rank in the block while below the capacity, and their residual becomes
+// +0.  The stashed entries still qualify when the threshold key is 0
+// (key(+0) = 0), so the ranks are the pass's; otherwise the scan sees only
+// the others, numbered from nst.
+template <bool VEC>
+__device__ void rescan_block(const ThrArgs& a, int64_t b, int64_t o, u32 nst) {
+  float* r = a.residual;
+  const int lane = lane_id();
+  const u32 shift = a.klam == 0u ? 0u : nst;
+  u32 run = 0;
+  auto put = [&](u32 rank, int64_t idx, float x) {
+    const int64_t e = (int64_t)rank + shift;
+    if (e >= nst && o + e < a.capacity) {
+      a.out_idx[o + e] = (int32_t)idx;
+      a.out_val[o + e] = x;
+      r[idx] = 0.0f;
     }
   };
-  const int64_t shift = a.klam == 0u ? 0 : a.stash_cap;
-  auto put = [&](int64_t rank0, int64_t idx, u32 bits) {
-    const int64_t rank = rank0 + shift;
-    if (rank >= a.stash_cap && rank < take) {
-      a.out_idx[prefix + rank] = (int32_t)idx;
-      a.out_val[prefix + rank] = __uint_as_float(bits);
-      rw[idx] = 0.0f;
-    }
+  auto single = [&](int64_t i0, int64_t cnt) {
+    const bool in = lane < cnt;
+    const float x = in ? r[i0 + lane] : 0.0f;
+    const bool q = in && key_of(x) >= a.klam;
+    const u64 m = ballot(q);
+    if (q) put(run + lanes_below(m), i0 + lane, x);
+    run += (u32)__popcll(m);
   };
-  ordered_walk(a, load, put, s_wt);
+  v4f x[kPassWaves];
+  WavePart p[kPassWaves];
+#pragma unroll
+  for (int w = 0; w < kPassWaves; ++w) {
+    p[w] = wave_part(a, b, w);
+    x[w] = p[w].in ? load_slot<VEC>(r, a, p[w].slot) : v4f{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int w = 0; w < kPassWaves; ++w) {
+    if (p[w].has_head) single(0, a.head);
+    u32 qm = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qm |= (p[w].in && key_of(x[w][c]) >= a.klam ? 1u : 0u) << c;
+    u32 tot;
+    u32 s = run + wave_rank4(qm, tot);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if ((qm >> c) & 1u) put(s++, a.head + 4 * p[w].slot + c, x[w][c]);
+    run += tot;
+    if (p[w].has_tail) single(a.tail0, a.n - a.tail0);
+  }
+}
+
+// Decoupled look-back for group e (wave 0, every lane): the sum of the totals
+// of groups 0 .. e-1.  Every group publishes its total before it looks back,
+// and a group's ticket is taken after its predecessors', so the waits end;
+// the spin is bounded all the same (error bit kErrBarrierTimeout).
+__device__ u32 look_back(const ThrArgs& a, int64_t e) {
+  const int lane = lane_id();
+  u32 sum = 0;
+  int64_t k = e - 1;  // the nearest group not yet summed
+  while (k >= 0) {
+    const int64_t j = k - lane;
+    u64 v = j >= 0 ? ld_agent64(a.status + j) : kFlagPrefix;
+    u32 spins = 0;
+    while (ballot((v >> 62) == 0)) {
+      if (++spins > kLookbackSpins) {
+        if (lane == 0) or_agent(a.err, kErrBarrierTimeout);
+        return sum;
+      }
+      if ((v >> 62) == 0) v = ld_agent64(a.status + j);
+    }
+    const u64 pm = ballot((v >> 62) == 2);
+    const int stop = pm ? __builtin_ctzll(pm) : kWave - 1;  // lanes 0 .. stop are summed
+    sum += wave_sum(lane <= stop ? (u32)v : 0u);
+    if (pm) break;
+    k -= kWave;
+  }
+  return sum;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kEmitThreads) void k_thr_emit(ThrArgs ain) {
+  const ThrArgs a = with_key(ain);
+  __shared__ u32 s_scan[kEmitWaves + 1];
+  __shared__ u32 s_off[kEmitThreads];       // a block's first position in the group's output
+  __shared__ u32 s_soff[kEmitThreads + 1];  // a block's first stashed entry among the group's
+  __shared__ u32 s_e, s_before;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  if (tid == 0) s_e = add_agent_relaxed(a.ticket, 1u);
+  __syncthreads();
+  const int64_t e = s_e;
+  const int64_t x = e * kEmitThreads + tid;  // this thread's block
+  const u32 c = x < a.nblocks ? a.cnt[x] : 0u;
+  const u32 nst = std::min(c, kBlockCap);
+  u32 gtot, stot;
+  const u32 off = block_exclusive_sum<kEmitThreads>(c, s_scan, gtot);
+  const u32 soff = block_exclusive_sum<kEmitThreads>(nst, s_scan, stot);
+  s_off[tid] = off;
+  s_soff[tid] = soff;
+  if (tid == 0) s_soff[kEmitThreads] = stot;
+  if (tid < kWave) {
+    if (lane == 0) st_agent64(a.status + e, (e == 0 ? kFlagPrefix : kFlagTotal) | gtot);
+    const u32 before = e == 0 ? 0u : look_back(a, e);
+    if (lane == 0) {
+      if (e > 0) st_agent64(a.status + e, kFlagPrefix | (u64)(before + gtot));
+      s_before = before;
+      if (e == a.ngroups - 1) *a.d_count = (int64_t)before + gtot;
+    }
+  }
+  __syncthreads();
+  const int64_t P = s_before;
+  // stashed entries, flattened: entry q of the group is entry q - soff[j] of
+  // the group's block j, where soff[j] <= q < soff[j + 1]; four per thread at
+  // a time, so that their loads are in flight together
+  constexpr int U = 4;
+  for (u32 q0 = tid; q0 < stot; q0 += U * kEmitThreads) {
+    Pair pr[U];
+    int64_t pos[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const u32 q = q0 + u * kEmitThreads;
+      pos[u] = -1;
+      if (q < stot) {
+        int lo = 0, hi = kEmitThreads;  // s_soff[lo] <= q < s_soff[hi]
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (s_soff[mid] <= q) lo = mid;
+          else hi = mid;
+        }
+        const u32 j = q - s_soff[lo];
+        pr[u] = a.stash[(e * kEmitThreads + lo) * kBlockCap + j];
+        pos[u] = P + s_off[lo] + j;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (pos[u] < 0) continue;
+      if (pos[u] < a.capacity) {
+        a.out_idx[pos[u]] = pr[u].idx;
+        a.out_val[pos[u]] = __uint_as_float(pr[u].bits);
+      } else {
+        a.residual[pr[u].idx] = __uint_as_float(pr[u].bits);
+      }
+    }
+  }
+  // blocks whose entries outran the stash with positions still below the
+  // capacity: each wave scans its own lanes' blocks in turn
+  const int64_t o = P + off;
+  u64 m = ballot(c > nst && o + nst < a.capacity);
+  while (m) {
+    const int L = __builtin_ctzll(m);
+    m &= m - 1;
+    rescan_block<VEC>(a, __shfl(x, L), __shfl(o, L), __shfl(nst, L));
+  }
 }
 
 __global__ void k_store_zero_count(int64_t* d_count) {
@@ -361,24 +375,23 @@ __global__ void k_store_zero_count(int64_t* d_count) {
 }
 
 struct ThrLayout {
-  int G;
-  int64_t stash_cap;
-  size_t cnt, stash, total;
+  int64_t nblocks, ngroups;
+  size_t ticket, cnt, status, stash, total;
 };
 
+// Sized for floor(n / 4) slots, as many as either mode has: a launch's own
+// block count is at most L.nblocks.
 static ThrLayout thr_layout(int64_t n) {
   ThrLayout L{};
-  int64_t units = (n + 3) / 4;
-  int64_t want = (units + kThrThreads - 1) / kThrThreads;
-  L.G = (int)std::max<int64_t>(1, std::min<int64_t>(kThrMaxBlocks, want));
-  // one workgroup covers at most ceil(n / G) + 3 elements (head/tail shifts);
-  // the stash keeps up to 1/64 of them (at least 256)
-  int64_t per = (n + L.G - 1) / L.G + 8;
-  L.stash_cap = std::max<int64_t>(256, (per + 63) / 64);
-  L.cnt = kWorkspaceHeader;  // after the header whose first word is the error word
-  size_t cnt_bytes = (((size_t)L.G * 4) + 255) & ~(size_t)255;
-  L.stash = L.cnt + cnt_bytes;
-  L.total = L.stash + (size_t)L.G * (size_t)L.stash_cap * sizeof(Pair);
+  const int64_t nv = n / 4;
+  L.nblocks = std::max<int64_t>(1, (nv + kPassThreads - 1) / kPassThreads);
+  L.ngroups = (L.nblocks + kEmitThreads - 1) / kEmitThreads;
+  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  L.ticket = kWorkspaceHeader;  // after the header whose first word is the error word
+  L.cnt = L.ticket + 256;
+  L.status = L.cnt + up((size_t)L.nblocks * 4);
+  L.stash = L.status + up((size_t)L.ngroups * 8);
+  L.total = L.stash + (size_t)L.nblocks * kBlockCap * sizeof(Pair);
   return L;
 }
 
@@ -426,17 +439,22 @@ static tgs_status threshold_launch(const char* what, const float* grad, float* r
     a.grad = grad;
     a.residual = residual;
     a.n = n;
-    a.vec = (((uintptr_t)grad) & 15u) == (((uintptr_t)residual) & 15u);
-    if (a.vec) {
+    const bool vec = (((uintptr_t)grad) & 15u) == (((uintptr_t)residual) & 15u);
+    if (vec) {
       int64_t head = (int64_t)(((16u - (((uintptr_t)residual) & 15u)) & 15u) / 4u);
       a.head = std::min<int64_t>(head, n);
-      a.nv = (n - a.head) / 4;
     }
+    a.nv = (n - a.head) / 4;
+    a.tail0 = a.head + 4 * a.nv;
+    a.nblocks = std::max<int64_t>(1, (a.nv + kPassThreads - 1) / kPassThreads);
+    a.ngroups = (a.nblocks + kEmitThreads - 1) / kEmitThreads;
     a.klam = lam_dev ? 0u : (__builtin_bit_cast(uint32_t, lambda) & 0x7FFFFFFFu);
     a.lam_dev = lam_dev;
     a.cnt = (u32*)(ws + L.cnt);
     a.stash = (Pair*)(ws + L.stash);
-    a.stash_cap = L.stash_cap;
+    a.status = (u64*)(ws + L.status);
+    a.ticket = (u32*)(ws + L.ticket);
+    a.err = (u32*)ws;
     a.out_idx = out_idx;
     a.out_val = out_val;
     a.capacity = capacity;
@@ -444,9 +462,15 @@ static tgs_status threshold_launch(const char* what, const float* grad, float* r
     hipEvent_t ev0, ev1;
     take_profile_events(&ev0, &ev1);
     if (ev0) (void)hipEventRecord(ev0, stream);
-    hipLaunchKernelGGL(k_thr_pass, dim3(L.G), dim3(kThrThreads), 0, stream, a);
+    if (vec)
+      hipLaunchKernelGGL(k_thr_pass<true>, dim3(a.nblocks), dim3(kPassThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL(k_thr_pass<false>, dim3(a.nblocks), dim3(kPassThreads), 0, stream, a);
     if (ev1) (void)hipEventRecord(ev1, stream);
-    hipLaunchKernelGGL(k_thr_emit, dim3(L.G), dim3(kThrThreads), 0, stream, a);
+    if (vec)
+      hipLaunchKernelGGL(k_thr_emit<true>, dim3(a.ngroups), dim3(kEmitThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL(k_thr_emit<false>, dim3(a.ngroups), dim3(kEmitThreads), 0, stream, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TGS_EHIP, "%s: launch failed: %s", what, hipGetErrorString(e));

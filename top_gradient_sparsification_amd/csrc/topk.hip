@@ -173,8 +173,9 @@ struct StepCtl {
   // guided accumulate pass (standalone general path): k_guess adds its sample
   // histogram into the header histogram; its last workgroup picks guide_bin
   // and leaves the histogram, its counter and guide_ovf zero
-  u32 guide_bin;  // candidates are the entries of first-level bins >= guide_bin (kNoGuide: none)
-  u32 guide_ovf;  // set by the accumulate pass when a workgroup's region overflowed
+  u32 guide_bin;   // candidates are the entries of first-level bins >= guide_bin (kNoGuide: none)
+  u32 guide_ovf;   // set by the accumulate pass when a workgroup's region overflowed
+  u32 acc_ticket;  // row pairs handed out by the accumulate pass (k_guess sets it to zero)
 };
 static_assert(sizeof(StepCtl) <= kEstStateOffset, "control block overlaps the header's shared state");
 static_assert(kMaxAccBlocks <= kMaxGenWG, "guided regions are the general path's");
@@ -1210,6 +1211,7 @@ __global__ __launch_bounds__(kGuessThreads) void k_guess(GuessArgs a) {
   if (tid == 0) {
     st_agent(&ctl->guide_bin, kept <= a.s_max ? pick : kNoGuide);
     st_agent(&ctl->guide_ovf, 0u);
+    st_agent(&ctl->acc_ticket, 0u);
     st_agent(&a.hh->done, 0u);
   }
 }
@@ -1217,12 +1219,18 @@ __global__ __launch_bounds__(kGuessThreads) void k_guess(GuessArgs a) {
 // ------------------------------------------------------- k_acc_guided ----
 // The accumulate pass of the standalone general path, given the guessed bin:
 // acc = residual + grad written back to residual and the first-level
-// histogram of each workgroup, as k_acc_pass does (rows of NT float4 dealt
-// round-robin, two in flight), and the candidates -- every entry of the bins
-// >= the guessed bin -- copied into one region per workgroup, in no
-// particular order: a wave reserves room for a row's candidates with one LDS
-// atomic and places them by a DPP scan over its lanes, so waves never wait
-// for each other.  k_general ranks them by (key desc, index asc) itself.
+// histogram of each workgroup, as k_acc_pass does (rows of NT float4, two in
+// flight), and the candidates -- every entry of the bins >= the guessed bin
+// -- copied into one region per workgroup, in no particular order: a wave
+// reserves room for a row's candidates with one LDS atomic and places them by
+// a DPP scan over its lanes, so waves never wait for each other.  k_general
+// ranks them by (key desc, index asc) itself.
+//
+// With DYN false row t goes to workgroup t mod G.  With DYN true (long
+// vectors) rows go out in pairs: workgroup b takes pair b and then the pairs
+// a ticket hands out (G + the ticket's count), one pair ahead: the
+// workgroups then stay on one short stretch of memory however their speeds
+// differ, where a fixed deal lets the slower ones fall behind and finish last.
 struct GuidedArgs {
   const float* grad;
   float* residual;
@@ -1237,12 +1245,15 @@ struct GuidedArgs {
   u32* guide_cnt;      // [gridDim.x] candidates each workgroup found (above cap: its region overflowed)
   u64* cand;           // workgroup b's region: cand + b * cap
   u32 cap;
+  u32* ticket;         // zero at the start (DYN)
 };
 
+template <bool DYN>
 __global__ __launch_bounds__(kAccThreads) void k_acc_guided(GuidedArgs a) {
   constexpr int NT = kAccThreads;
   __shared__ u32 s_h[2048];
   __shared__ u32 s_cnt;
+  __shared__ int64_t s_next;
   const int tid = threadIdx.x, lane = lane_id();
   for (int i = tid; i < 2048; i += NT) s_h[i] = 0;
   if (tid == 0) s_cnt = 0;
@@ -1250,6 +1261,12 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_guided(GuidedArgs a) {
     for (int i = tid; i < a.zero_words; i += NT) a.zero_ptr[i] = 0u;
   const u32 gbin = a.ctl->guide_bin;
   const bool guide = gbin != kNoGuide;  // the same in every thread
+  const int64_t nrows = (a.nv + NT - 1) / NT, npairs = (nrows + 1) / 2, G = gridDim.x;
+  int64_t nn = 0;  // thread 0 (DYN): the pair after the next one
+  if (DYN && tid == 0) {
+    s_next = G + (int64_t)add_agent_relaxed(a.ticket, 1u);
+    nn = G + (int64_t)add_agent_relaxed(a.ticket, 1u);
+  }
   __syncthreads();
   u64* const reg = a.cand + (size_t)blockIdx.x * a.cap;
   // this lane's kept entries i0 + j (bit j of m4) go to the region; every
@@ -1285,7 +1302,6 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_guided(GuidedArgs a) {
   if (blockIdx.x == 0 && tid < kWave) scalar(tid, tid < a.head);
   const v4f* __restrict__ gv = (const v4f*)(g + a.head);
   v4f* __restrict__ rv = (v4f*)(r + a.head);
-  const int64_t nrows = (a.nv + NT - 1) / NT, G = gridDim.x;
   auto load = [&](int64_t t, v4f& gg, v4f& rr) {
     const int64_t i = t * NT + tid;
     if (t < nrows && i < a.nv) {
@@ -1298,7 +1314,7 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_guided(GuidedArgs a) {
   auto process = [&](int64_t t, const v4f& gg, const v4f& rr, u32& m4, u32* bq) {
     const int64_t i = t * NT + tid;
     m4 = 0;
-    if (i < a.nv) {
+    if (t < nrows && i < a.nv) {
       const v4f acc = rr + gg;
       __builtin_nontemporal_store(acc, rv + i);
 #pragma unroll
@@ -1310,19 +1326,36 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_guided(GuidedArgs a) {
       }
     }
   };
+  // unit u: rows 2u and 2u + 1 (DYN), or rows u and u + G (units u = b,
+  // b + 2G, ...)
+  auto row0 = [&](int64_t u) { return DYN ? 2 * u : u; };
+  auto row1 = [&](int64_t u) { return DYN ? 2 * u + 1 : u + G; };
+  const int64_t nunits = DYN ? npairs : nrows;
   v4f ga, ra, gb, rb;
   u32 m4, bq[4] = {0u, 0u, 0u, 0u};
-  int64_t t = blockIdx.x;
-  load(t, ga, ra);
-  load(t + G, gb, rb);
-  for (; t < nrows; t += 2 * G) {
-    process(t, ga, ra, m4, bq);
-    load(t + 2 * G, ga, ra);
-    if (guide) place(m4, a.head + 4 * (t * NT + tid), bq);
-    if (t + G >= nrows) break;
-    process(t + G, gb, rb, m4, bq);
-    load(t + 3 * G, gb, rb);
-    if (guide) place(m4, a.head + 4 * ((t + G) * NT + tid), bq);
+  int64_t u = blockIdx.x;                    // this unit
+  int64_t un = DYN ? s_next : u + 2 * G;     // the next one
+  load(row0(u), ga, ra);
+  load(row1(u), gb, rb);
+  while (u < nunits) {
+    process(row0(u), ga, ra, m4, bq);
+    load(row0(un), ga, ra);
+    if (guide) place(m4, a.head + 4 * (row0(u) * NT + tid), bq);
+    process(row1(u), gb, rb, m4, bq);
+    load(row1(un), gb, rb);
+    if (guide) place(m4, a.head + 4 * (row1(u) * NT + tid), bq);
+    u = un;
+    if (DYN) {
+      __syncthreads();  // every thread has read s_next
+      if (tid == 0) {
+        s_next = nn;
+        if (nn < npairs) nn = G + (int64_t)add_agent_relaxed(a.ticket, 1u);
+      }
+      __syncthreads();
+      un = s_next;
+    } else {
+      un = u + 2 * G;
+    }
   }
   if (blockIdx.x == gridDim.x - 1 && tid < kWave) {
     const int64_t i = a.head + 4 * a.nv + tid;
@@ -2781,7 +2814,13 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
       g.guide_cnt = (u32*)(ws + L.guide_cnt);
       g.cand = ga.cand;
       g.cap = path == 8 ? 1u : stride;
-      hipLaunchKernelGGL(k_acc_guided, dim3(G1), dim3(kAccThreads), 0, stream, g);
+      g.ticket = &ctl->acc_ticket;
+      // the ticket's hand-out pays from about 32 rows per workgroup on
+      const int64_t rows = (nv + kAccThreads - 1) / kAccThreads;
+      if (rows >= 32 * (int64_t)G1)
+        hipLaunchKernelGGL(k_acc_guided<true>, dim3(G1), dim3(kAccThreads), 0, stream, g);
+      else
+        hipLaunchKernelGGL(k_acc_guided<false>, dim3(G1), dim3(kAccThreads), 0, stream, g);
       ga.guided = 1;
       ga.guide_stride = stride;
       ga.guide_bin = &ctl->guide_bin;

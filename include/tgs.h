@@ -246,6 +246,9 @@ size_t tgs_gtopk_workspace_bytes(int32_t P, int64_t k, int64_t n);
  *   out_mask [P][k] uint8: 1 where idx[p][j] is one of out_idx, else 0.
  * Rows that break the index precondition set a device error word; check it
  * with tgs_check_device_error (the outputs are then unspecified).
+ * k is at most 2^26 and P k at most 2^31 - 1; the workspace must be 16-byte
+ * aligned.  Each call starts by zero-filling the part of the workspace it
+ * keeps its tables and counters in, so it assumes nothing of that part.
  */
 tgs_status tgs_gtopk_merge(const int32_t* idx, const float* val, int32_t P, int64_t k, int64_t n,
                            int32_t* out_idx, float* out_val, uint8_t* out_mask, void* workspace,

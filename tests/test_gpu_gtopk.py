@@ -68,6 +68,47 @@ def test_ties_and_cancellation(tgs_gpu):
     assert_merge_equal(got, exp, "ties")
 
 
+@pytest.mark.parametrize("k", [10000, 20000, 40000])
+def test_mid_k_three_workers(tgs_gpu, k):
+    """P = 3: round 0 merges rows 0 and 1, row 2 waits a round; k spans the
+    select's one-LDS-list and streaming sizes."""
+    rng = np.random.default_rng(k + 3)
+    n = 4 * k
+    idx, val = random_sets(rng, 3, k, n, 2 * k)
+    got, exp = run_both(tgs_gpu, idx, val, n)
+    assert_merge_equal(got, exp, "P=3 k=%d" % k)
+
+
+def test_ties_large_k(tgs_gpu):
+    """k = 40,000 on a coarse value grid: the k-th key is held by thousands of
+    entries, so the lowest indices decide."""
+    rng = np.random.default_rng(40)
+    P, k, n = 4, 40000, 200000
+    idx, _ = random_sets(rng, P, k, n, 60000)
+    val = (rng.integers(-3, 4, (P, k)) * 0.5).astype(np.float32)
+    val[val == 0] = 0.5
+    got, exp = run_both(tgs_gpu, idx, val, n)
+    assert_merge_equal(got, exp, "ties k=40000")
+
+
+def test_nan_and_inf_values(tgs_gpu):
+    """NaN (bit patterns 0x7FFFFFFF, 0xFFFFFFFF, 0x7FC00000, 0xFFC00001) and
+    +-inf on indices no other row holds (so they are never added): NaN keys
+    rank above inf, inf above every finite key."""
+    rng = np.random.default_rng(77)
+    P, k, n = 5, 3000, 50000
+    idx, val = random_sets(rng, P, k, n, 4000)
+    specials = np.array([0x7FFFFFFF, 0xFFFFFFFF, 0x7FC00000, 0xFFC00001, 0x7F800000, 0xFF800000],
+                        np.uint32).view(np.float32)
+    counts = np.bincount(idx.ravel(), minlength=n)
+    for p in range(P):
+        own = np.nonzero(counts[idx[p]] == 1)[0]
+        pos = rng.choice(own, 3 * specials.size, replace=False)
+        val[p, pos] = np.tile(specials, 3)
+    got, exp = run_both(tgs_gpu, idx, val, n)
+    assert_merge_equal(got, exp, "nan/inf")
+
+
 def test_full_config(tgs_gpu):
     """P = 32 workers, k = 25,600 pairs over [0, 25.6M), half of each row from
     a shared hot set of 51,200: 5 rounds."""

@@ -6,24 +6,34 @@
 // O(log P) pairwise rounds; only the indices that survive keep their index
 // information, and each worker learns which of its own entries survived.
 //
-// Every slot is held as k (index, bits) pairs sorted by index, which turns the
-// per-round union into a merge:
-//   rows     each worker's row copied to its slot, sorted by index (LDS
-//            bitonic runs of 2048, then merge-path passes); repeated or
-//            out-of-range indices set the device error word.
-//   round r  for every slot s with a partner s + 2^r:
-//              k_gt_union   merge-path merge of the two slots by index; a
-//                           shared index keeps the A entry with value a + b
-//                           (one binary32 add) and the B entry becomes a hole;
-//              k_gt_select  one workgroup per merge: radix select of the k-th
-//                           key over 11/11/9-bit digits, then an ordered
-//                           compaction that keeps every key above it and the
-//                           lowest-index ties, written back to slot s (for
-//                           2k <= 65,536 the merge's keys stay in registers:
-//                           k_gt_select_reg).
-//   final    slot 0 sorted by (key desc, index asc) with the same run sort and
-//            merge passes; the mask binary-searches every input index in the
-//            index-sorted slot 0.
+// A merge needs the union by index of two k-sets and the k best of it.  The
+// union is a hash join in LDS: the indices are hashed into NP parts, and one
+// workgroup per (merge, part) builds a table of the A side's entries of its
+// part and looks the B side's entries of its part up in it.  No set is ever
+// sorted by index and no table lives in memory:
+//   k_gt_clear  zero-fills the histograms and counters of the call.
+//   round r, for every merge m (slot s = m 2^(r+1) absorbs s + 2^r):
+//     k_gt_join   workgroup (m, part): the A entries of its part into an LDS
+//                 table; each B entry of its part found there adds its value
+//                 to that entry (one binary32 add), the others are appended
+//                 to the merge's union W; then the A entries are appended.
+//                 The union's keys are counted into the merge's histogram of
+//                 key >> 20, and the last workgroup of the merge to arrive
+//                 finds the bin b1 that holds the k-th key.
+//     k_gt_keep   every entry of W above bin b1 is appended to the merge's
+//                 output, the entries of bin b1 are listed as candidates, and
+//                 the last workgroup of the merge to arrive finds the k-th
+//                 key T and the largest index I kept at T among them and
+//                 appends the candidates with key > T, or key = T and index
+//                 <= I (ties keep the lowest indices).
+//   k_gt_final  the mask, as a join of each row against the final set (and
+//               the rows' precondition check: a repeated index within a
+//               row, or one outside [0, n), sets the error word), and runs
+//               of 4096 of the final set sorted by (key desc, index asc);
+//   k_gt_merge  passes merge the runs; the last one writes the outputs.
+// Slots without a partner keep their data where it is until they are merged:
+// a slot's data is its row until it has been a merge's destination, then
+// that merge's output.
 #include <algorithm>
 #include <climits>
 #include <vector>
@@ -33,435 +43,782 @@
 
 namespace tgs {
 
-constexpr int kRun = 2048;          // LDS-sorted run length
-constexpr int kRunThreads = 1024;
-constexpr int kMergeThreads = 256;
-constexpr int kMergeSpan = 16;      // outputs per thread in a merge pass
-constexpr int kSelThreads = 1024;
+constexpr int kGtThreads = 1024;
+constexpr int kGtWaves = kGtThreads / kWave;
+constexpr int kGtBins = 2048;      // first-level bins: key >> 20
+constexpr int kSelList = 8192;     // candidates the select holds in LDS
+constexpr int kSortTile = 4096;    // entries one workgroup sorts or merges
+constexpr int kSortPer = kSortTile / kGtThreads;
+constexpr int kGtBatch = 16;       // loads in flight per thread in the scans
+constexpr u32 kLogSlots = 13;      // places of one part's LDS table
+constexpr u32 kSlots = 1u << kLogSlots;
+constexpr int64_t kPartLoad = kSlots / 2;  // entries a part holds on average at most
+constexpr int64_t kGtMaxK = (int64_t)1 << 20;
 
-struct ByIdx {
-  __device__ static u64 key(const Pair& p) { return (u64)(u32)p.idx; }
+typedef u32 v4u __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32 gt_bin(u32 bits) { return key_of_bits(bits) >> 20; }
+
+// Multiplicative (Fibonacci) hashing of an index: the top logNP bits pick
+// the part, the next kLogSlots bits the first place of the probe sequence
+// inside the part's table (which wraps around).
+struct HashPart {
+  u32 part, slot;
 };
-struct ByRank {
-  __device__ static u64 key(const Pair& p) { return pair_rank(p); }
+__device__ __forceinline__ HashPart gt_hash(int32_t idx, u32 logNP) {
+  const u32 h = (u32)idx * 0x9E3779B1u;
+  return HashPart{logNP ? h >> (32u - logNP) : 0u, (h >> (32u - logNP - kLogSlots)) & (kSlots - 1u)};
+}
+
+// An LDS table of one part: key[h] = index + 1 (0: empty), val[h] = the
+// entry's value bits.
+// Inserts (idx, bits); false if idx is there already or the table is full.
+__device__ bool lds_insert(u32* key, u32* val, u32 h, int32_t idx, u32 bits) {
+  const u32 want = (u32)idx + 1u;
+  u32 old = 0u, probe = 0u;
+  do {  // one exit: an empty place taken, the index found, or every place tried
+    old = atomicCAS(&key[h], 0u, want);
+    if (old != 0u && old != want) h = (h + 1u) & (kSlots - 1u);
+  } while (old != 0u && old != want && ++probe < kSlots);
+  if (old != 0u) return false;
+  if (val) val[h] = bits;
+  return true;
+}
+// The place of idx, or -1.
+__device__ int lds_find(const u32* key, u32 h, int32_t idx) {
+  const u32 want = (u32)idx + 1u;
+  u32 kk = 0u, probe = 0u;
+  do {
+    kk = key[h];
+    if (kk != 0u && kk != want) h = (h + 1u) & (kSlots - 1u);
+  } while (kk != 0u && kk != want && ++probe < kSlots);
+  return kk == want ? (int)h : -1;
+}
+
+// Adds the workgroup's LDS histogram to a merge's histogram in memory.
+__device__ __forceinline__ void flush_hist(const u32* s_h, u32* H) {
+  for (int i = threadIdx.x; i < kGtBins; i += blockDim.x)
+    if (s_h[i]) (void)add_agent_relaxed(&H[i], s_h[i]);
+}
+
+// Appends the entries whose `keep` is set (one per thread) to dst at the
+// places a counter hands out (one device add per workgroup), in no
+// particular order; returns this thread's place (or -1).  Every thread
+// calls it.  s_w holds kGtWaves words, s_base one.
+__device__ int64_t wg_append(bool keep, u32* counter, u32* s_w, u32* s_base) {
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  const u64 bal = ballot(keep);
+  if (lane == 0) s_w[w] = (u32)__popcll(bal);
+  __syncthreads();
+  u32 woff = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kGtWaves; ++i) {
+    const u32 v = s_w[i];
+    woff += i < w ? v : 0u;
+    tot += v;
+  }
+  if (tid == 0) *s_base = tot ? add_agent_relaxed(counter, tot) : 0u;
+  __syncthreads();
+  const int64_t pos = keep ? (int64_t)(*s_base + woff + lanes_below(bal)) : -1;
+  __syncthreads();  // s_w and s_base are free again
+  return pos;
+}
+
+// The same for cnt entries of each thread: returns the place of this
+// thread's first.  s_scan holds kGtWaves + 1 words.
+__device__ int64_t wg_append_n(u32 cnt, u32* counter, u32* s_scan, u32* s_base) {
+  u32 tot;
+  const u32 before = block_exclusive_sum<kGtThreads>(cnt, s_scan, tot);
+  if (threadIdx.x == 0) *s_base = tot ? add_agent_relaxed(counter, tot) : 0u;
+  __syncthreads();
+  const int64_t pos = (int64_t)*s_base + before;
+  __syncthreads();
+  return pos;
+}
+
+// Compacts this part's entries among n entries (got by get(j)) into LDS,
+// kStagePer per thread at a time, and hands each batch to use(count) with
+// the batch in s_stage[0 .. count); every thread calls it (barriers).
+constexpr int kStagePer = 8;
+constexpr int kStageCap = kStagePer * kGtThreads;
+template <class Get, class Use>
+__device__ void stage_part(int64_t n, u32 logNP, u32 g, Pair* s_stage, u32* s_n, Get get, Use use) {
+  const int tid = threadIdx.x, lane = lane_id();
+  // the next batch's loads are in flight while this one is staged and used
+  Pair e[kStagePer], nx[kStagePer];
+  auto load = [&](int64_t j0, Pair (&x)[kStagePer]) {
+#pragma unroll
+    for (int u = 0; u < kStagePer; ++u) {
+      const int64_t j = j0 + (int64_t)u * kGtThreads + tid;
+      x[u] = j < n ? get(j) : pair_sentinel();
+    }
+  };
+  load(0, nx);
+  for (int64_t j0 = 0; j0 < n; j0 += kStageCap) {
+#pragma unroll
+    for (int u = 0; u < kStagePer; ++u) e[u] = nx[u];
+    if (j0 + kStageCap < n) load(j0 + kStageCap, nx);
+    if (tid == 0) *s_n = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kStagePer; ++u) {
+      const int64_t j = j0 + (int64_t)u * kGtThreads + tid;
+      const bool own = j < n && gt_hash(e[u].idx, logNP).part == g;
+      const u64 bal = ballot(own);
+      if (!bal) continue;
+      u32 base = 0;
+      if (lane == 0) base = atomicAdd(s_n, (u32)__popcll(bal));
+      base = __builtin_amdgcn_readfirstlane(base);
+      if (own) s_stage[base + lanes_below(bal)] = e[u];
+    }
+    __syncthreads();
+    use(*s_n);
+    __syncthreads();
+  }
+}
+
+// -------------------------------------------------------------- k_gt_clear ----
+__global__ void k_gt_clear(v4u* p, int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) p[i] = v4u{0u, 0u, 0u, 0u};
+}
+
+// Merges of round r, and the first output slot of round r (outputs are kept
+// round after round).
+__host__ __device__ inline int64_t gt_merges(int64_t P, int r) {
+  const int64_t half = (int64_t)1 << r;
+  return P > half ? (P - half + 2 * half - 1) / (2 * half) : 0;
+}
+__host__ __device__ inline int64_t gt_out_base(int64_t P, int r) {
+  int64_t o = 0;
+  for (int q = 0; q < r; ++q) o += gt_merges(P, q);
+  return o;
+}
+
+// Where slot s's data is before round r: the output of the last round before
+// r it was a destination in, else its row (idx, val).
+struct SlotData {
+  const Pair* pairs;   // (null: the row)
+  const int32_t* idx;
+  const float* val;
+};
+__device__ SlotData slot_data(int64_t P, int64_t k, int r, int64_t s, const Pair* out, const int32_t* idx,
+                              const float* val) {
+  for (int q = r - 1; q >= 0; --q)
+    if (s % ((int64_t)2 << q) == 0 && s + ((int64_t)1 << q) < P)
+      return SlotData{out + (gt_out_base(P, q) + (s >> (q + 1))) * k, nullptr, nullptr};
+  return SlotData{nullptr, idx + s * k, val + s * k};
+}
+__device__ __forceinline__ Pair slot_entry(const SlotData& d, int64_t j) {
+  return d.pairs ? d.pairs[j] : Pair{d.idx[j], __float_as_uint(d.val[j])};
+}
+
+// --------------------------------------------------------------- selection ----
+// The k-th best live entry of a merge by (key desc, index asc) is found in
+// two steps.  From the merge's histogram of key >> 20 (complete once every
+// probing workgroup has added to it), the bin b1 that holds it and `need`,
+// its rank inside the bin.  Then, among the bin's entries (the candidates,
+// which k_gt_keep lists), radix levels over the rest of the key and, among
+// the entries whose key is T, the k-th key, over the index: T and I, the
+// largest index kept at T (ties keep the lowest indices).
+struct BinShared {  // the histogram levels
+  u32 h[kGtBins];
+  u32 scan[kGtWaves + 1];
+  u32 pick, before, count;
+};
+struct SelShared : BinShared {  // and the candidates
+  Pair list[kSelList];
 };
 
-template <class Cmp>
-__device__ void lds_bitonic(Pair* a, int N) {
-  for (int size = 2; size <= N; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < (N >> 1); i += blockDim.x) {
-        int lo = 2 * i - (i & (stride - 1));
-        int hi = lo + stride;
-        bool up = (lo & size) == 0;
-        Pair x = a[lo], y = a[hi];
-        u64 kx = Cmp::key(x), ky = Cmp::key(y);
-        if (up ? (kx > ky) : (kx < ky)) {
-          a[lo] = y;
-          a[hi] = x;
-        }
+// Bins 0..nb-1 (nb = 1024 or 2048) in s.h; the bin where the count from the
+// top (desc) or the bottom (asc) reaches `need`, the count before it and the
+// bin's own count land in s.pick, s.before, s.count.  Every thread calls it.
+__device__ void pick_level(BinShared& s, int nb, u32 need, bool desc) {
+  const int tid = threadIdx.x;
+  const int per = nb / kGtThreads;  // 1 or 2
+  u32 c[2] = {0u, 0u};
+  int bin[2] = {0, 0};
+  u32 own = 0;
+  for (int u = 0; u < per; ++u) {
+    const int o = tid * per + u;  // order position
+    bin[u] = desc ? nb - 1 - o : o;
+    c[u] = s.h[bin[u]];
+    own += c[u];
+  }
+  u32 tot;
+  const u32 before = block_exclusive_sum<kGtThreads>(own, s.scan, tot);
+  if (tid == 0) {
+    s.pick = 0xFFFFFFFFu;
+    s.before = 0;
+    s.count = 0;
+  }
+  __syncthreads();
+  if (before < need && before + own >= need) {
+    u32 run = before;
+    for (int u = 0; u < per; ++u) {
+      if (run + c[u] >= need) {
+        s.pick = (u32)bin[u];
+        s.before = run;
+        s.count = c[u];
+        break;
       }
-      __syncthreads();
+      run += c[u];
+    }
+  }
+  __syncthreads();
+}
+
+// First step, one workgroup: b1 and need into sel[0], sel[1] (b1 = 2^32 - 1
+// when the merge has fewer than k live entries, which only rows that break
+// the preconditions can cause).  Leaves H zero.
+__device__ void select_bin(BinShared& s, int64_t k, u32* H, u32* sel, u32* err) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kGtBins; i += kGtThreads) {
+    s.h[i] = ld_agent(&H[i]);
+    st_agent(&H[i], 0u);
+  }
+  __syncthreads();
+  pick_level(s, kGtBins, (u32)k, true);
+  if (tid == 0) {
+    if (s.pick == 0xFFFFFFFFu) atomicOr(err, kErrBadInput);
+    st_agent(&sel[0], s.pick);
+    st_agent(&sel[1], (u32)k - s.before);
+  }
+}
+
+// Second step, one workgroup, over the nc candidates of clist (read with
+// device-scope loads): T and I with the rank `need` inside bin b1.
+__device__ void select_in_bin(SelShared& s, const Pair* clist, u32 nc, u32 b1, u32 need, u32& T, u32& I) {
+  const int tid = threadIdx.x;
+  const bool in_lds = nc <= (u32)kSelList;
+  if (in_lds) {
+    for (u32 i0 = tid; i0 < nc; i0 += (u32)kGtBatch * kGtThreads) {
+      Pair e[kGtBatch];
+#pragma unroll
+      for (int u = 0; u < kGtBatch; ++u) {
+        const u32 i = i0 + (u32)u * kGtThreads;
+        if (i < nc) e[u] = unpack_pair(ld_agent64((const u64*)(clist + i)));
+      }
+#pragma unroll
+      for (int u = 0; u < kGtBatch; ++u) {
+        const u32 i = i0 + (u32)u * kGtThreads;
+        if (i < nc) s.list[i] = e[u];
+      }
+    }
+    __syncthreads();
+  }
+  // calls f(e) for every candidate that passes pred(e); every thread calls it
+  auto for_cands = [&](auto pred, auto f) {
+    if (in_lds) {
+      for (u32 i = tid; i < nc; i += kGtThreads) {
+        const Pair e = s.list[i];
+        if (pred(e)) f(e);
+      }
+    } else {
+      for (u32 i = tid; i < nc; i += kGtThreads) {
+        const Pair e = unpack_pair(ld_agent64((const u64*)(clist + i)));
+        if (pred(e)) f(e);
+      }
+    }
+  };
+  auto level = [&](int nb, u32 nd, bool desc, auto pred, auto digit) {
+    for (int i = tid; i < nb; i += kGtThreads) s.h[i] = 0;
+    __syncthreads();
+    for_cands(pred, [&](const Pair& e) { atomicAdd(&s.h[digit(e)], 1u); });
+    __syncthreads();
+    pick_level(s, nb, nd, desc);
+  };
+  // key bits 19..10, then 9..0 (from the top)
+  level(1024, need, true, [](const Pair&) { return true; },
+        [](const Pair& e) { return (key_of_bits(e.bits) >> 10) & 1023u; });
+  const u32 d1 = s.pick;
+  need -= s.before;
+  const u32 p2 = (b1 << 10) | (d1 & 1023u);
+  level(1024, need, true, [p2](const Pair& e) { return (key_of_bits(e.bits) >> 10) == p2; },
+        [](const Pair& e) { return key_of_bits(e.bits) & 1023u; });
+  T = (p2 << 10) | (s.pick & 1023u);
+  need -= s.before;
+  I = 0x7FFFFFFFu;
+  if (need < s.count) {
+    // ties at T: the need lowest indices, over index bits 30..20, 19..10, 9..0
+    const u32 t = T;
+    level(2048, need, false, [t](const Pair& e) { return key_of_bits(e.bits) == t; },
+          [](const Pair& e) { return ((u32)e.idx >> 20) & 2047u; });
+    const u32 i1 = s.pick & 2047u;
+    need -= s.before;
+    level(1024, need, false, [t, i1](const Pair& e) { return key_of_bits(e.bits) == t && ((u32)e.idx >> 20) == i1; },
+          [](const Pair& e) { return ((u32)e.idx >> 10) & 1023u; });
+    const u32 i2 = (i1 << 10) | (s.pick & 1023u);
+    need -= s.before;
+    level(1024, need, false, [t, i2](const Pair& e) { return key_of_bits(e.bits) == t && ((u32)e.idx >> 10) == i2; },
+          [](const Pair& e) { return (u32)e.idx & 1023u; });
+    I = (i2 << 10) | (s.pick & 1023u);
+  }
+}
+
+// --------------------------------------------------------------- k_gt_join ----
+struct JoinArgs {
+  int32_t P;
+  int r;
+  int64_t k;
+  u32 logNP;
+  const int32_t* idx;  // the rows
+  const float* val;
+  const Pair* out;     // merge outputs of the earlier rounds, round by round
+  Pair* W;             // the round's unions, 2k places per merge
+  u32* wcnt;           // union lengths (32 words apart)
+  u32* hist;           // histograms, kGtBins per merge
+  u32* arrive;         // arrival counters (32 words apart)
+  u32* sel;            // [2] per merge: b1, need
+  u32* err;
+};
+
+__global__ __launch_bounds__(kGtThreads) void k_gt_join(JoinArgs a) {
+  __shared__ u32 s_key[kSlots];
+  __shared__ u32 s_val[kSlots];
+  __shared__ Pair s_stage[kStageCap];
+  __shared__ BinShared s;
+  __shared__ u32 s_base, s_last, s_n;
+  const int tid = threadIdx.x;
+  const u32 NP = 1u << a.logNP;
+  const int64_t m = blockIdx.x / NP;
+  const u32 g = blockIdx.x % NP;
+  const int64_t half = (int64_t)1 << a.r;
+  const int64_t sa = m * 2 * half;  // A slot; B is sa + half
+  const SlotData A = slot_data(a.P, a.k, a.r, sa, a.out, a.idx, a.val);
+  const SlotData B = slot_data(a.P, a.k, a.r, sa + half, a.out, a.idx, a.val);
+  for (u32 i = tid; i < kSlots; i += kGtThreads) s_key[i] = 0u;
+  for (int i = tid; i < kGtBins; i += kGtThreads) s.h[i] = 0u;
+  __syncthreads();
+  // the A entries of this part into the table (a repeated index is the
+  // rows' fault: the final check reports it)
+  stage_part(a.k, a.logNP, g, s_stage, &s_n, [&](int64_t j) { return slot_entry(A, j); }, [&](u32 n) {
+    for (u32 i = tid; i < n; i += kGtThreads) {
+      const Pair e = s_stage[i];
+      if (!lds_insert(s_key, s_val, gt_hash(e.idx, a.logNP).slot, e.idx, e.bits)) atomicOr(a.err, kErrBadInput);
+    }
+  });
+  Pair* W = a.W + m * 2 * a.k;
+  u32* wcnt = a.wcnt + m * 32;
+  // the B entries of this part: found, added to the A entry; else appended
+  stage_part(a.k, a.logNP, g, s_stage, &s_n, [&](int64_t j) { return slot_entry(B, j); }, [&](u32 n) {
+    u32 app = 0, napp = 0;  // bit q: staged entry tid + q 1024 is appended
+#pragma unroll
+    for (int q = 0; q < kStagePer; ++q) {
+      const u32 i = tid + (u32)q * kGtThreads;
+      if (i >= n) continue;
+      const Pair e = s_stage[i];
+      const int h = lds_find(s_key, gt_hash(e.idx, a.logNP).slot, e.idx);
+      if (h >= 0) {
+        s_val[h] = __float_as_uint(__uint_as_float(s_val[h]) + __uint_as_float(e.bits));
+      } else {
+        app |= 1u << q;
+        ++napp;
+        atomicAdd(&s.h[gt_bin(e.bits)], 1u);
+      }
+    }
+    int64_t pos = wg_append_n(napp, wcnt, s.scan, &s_base);
+#pragma unroll
+    for (int q = 0; q < kStagePer; ++q)
+      if ((app >> q) & 1u) W[pos++] = s_stage[tid + (u32)q * kGtThreads];
+  });
+  // the A entries of this part (every B entry has been looked up): slots
+  // tid + i 1024
+  {
+    constexpr int kPer = kSlots / kGtThreads;
+    u32 nk = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) nk += s_key[i * kGtThreads + tid] != 0u ? 1u : 0u;
+    int64_t pos = wg_append_n(nk, wcnt, s.scan, &s_base);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const u32 h = i * kGtThreads + tid;
+      const u32 kk = s_key[h];
+      if (!kk) continue;
+      const Pair e{(int32_t)(kk - 1u), s_val[h]};
+      atomicAdd(&s.h[gt_bin(e.bits)], 1u);
+      W[pos++] = e;
+    }
+  }
+  __syncthreads();
+  flush_hist(s.h, a.hist + m * kGtBins);
+  // the last workgroup of the merge to arrive picks the first-level bin: it
+  // needs only the histogram, whose adds are complete before each workgroup
+  // arrives
+  wait_all_memory();
+  __syncthreads();
+  if (tid == 0) s_last = add_agent_relaxed(&a.arrive[m * 32], 1u) == NP - 1u ? 1u : 0u;
+  __syncthreads();
+  if (!s_last) return;
+  select_bin(s, a.k, a.hist + m * kGtBins, a.sel + 2 * m, a.err);
+  if (tid == 0) st_agent(&a.arrive[m * 32], 0u);
+}
+
+// --------------------------------------------------------------- k_gt_keep ----
+struct KeepArgs {
+  int64_t k;
+  const Pair* W;       // the round's unions
+  u32* wcnt;           // their lengths (read, then zeroed by the last workgroup)
+  const u32* sel;      // b1, need
+  u32* cnt;            // output append counters (32 words apart)
+  u32* ccnt;           // candidate counters (32 words apart)
+  u32* karrive;        // arrival counters (32 words apart)
+  Pair* cand;          // candidate lists, 2k per merge
+  Pair* out;           // this round's outputs, k per merge
+  u32* err;
+};
+
+constexpr int kKeepPer = 2;  // union places per thread of k_gt_keep
+constexpr int kKeepSpan = kKeepPer * kGtThreads;
+
+__global__ __launch_bounds__(kGtThreads) __attribute__((amdgpu_waves_per_eu(8))) void k_gt_keep(KeepArgs a) {
+  __shared__ SelShared s;
+  __shared__ u32 s_w[kGtWaves];
+  __shared__ u32 s_base, s_last;
+  const int tid = threadIdx.x;
+  const int64_t len = 2 * a.k;
+  const int64_t cpm = (len + kKeepSpan - 1) / kKeepSpan;
+  const int64_t m = blockIdx.x / cpm;
+  const int64_t c = blockIdx.x % cpm;
+  const int64_t n = a.wcnt[m * 32];  // the union's length
+  const u32 b1 = a.sel[2 * m];
+  const bool b1ok = b1 != 0xFFFFFFFFu;
+  Pair* out = a.out + m * a.k;
+  u32* cnt = a.cnt + m * 32;
+  Pair* clist = a.cand + m * len;
+  auto put = [&](bool keep, const Pair& e) {
+    const int64_t pos = wg_append(keep, cnt, s_w, &s_base);
+    if (keep) {
+      if (pos < a.k) out[pos] = e;
+      else atomicOr(a.err, kErrBadInput);
+    }
+  };
+  Pair e[kKeepPer];
+#pragma unroll
+  for (int u = 0; u < kKeepPer; ++u) {
+    const int64_t q = c * kKeepSpan + u * kGtThreads + tid;
+    e[u] = q < n ? a.W[m * len + q] : pair_sentinel();
+  }
+  u32 kp = 0, cd = 0, nk = 0, nc0 = 0;  // bit u: e[u] is kept / a candidate
+#pragma unroll
+  for (int u = 0; u < kKeepPer; ++u) {
+    const bool live = e[u].idx >= 0;
+    const u32 bin = gt_bin(e[u].bits);
+    if (live && b1ok && bin > b1) {
+      kp |= 1u << u;
+      ++nk;
+    } else if (live && (bin == b1 || !b1ok)) {
+      cd |= 1u << u;
+      ++nc0;
+    }
+  }
+  {
+    int64_t pos = wg_append_n(nk, cnt, s.scan, &s_base);
+#pragma unroll
+    for (int u = 0; u < kKeepPer; ++u)
+      if ((kp >> u) & 1u) {
+        if (pos < a.k) out[pos] = e[u];
+        else atomicOr(a.err, kErrBadInput);
+        ++pos;
+      }
+    // candidates: stored at device scope for the selecting workgroup
+    int64_t cp = wg_append_n(nc0, a.ccnt + m * 32, s.scan, &s_base);
+#pragma unroll
+    for (int u = 0; u < kKeepPer; ++u)
+      if ((cd >> u) & 1u) st_agent64((u64*)(clist + cp++), pack_pair(e[u]));
+  }
+  // the last workgroup of the merge to arrive resolves the candidates
+  wait_all_memory();
+  __syncthreads();
+  if (tid == 0) s_last = add_agent_relaxed(&a.karrive[m * 32], 1u) == (u32)(cpm - 1) ? 1u : 0u;
+  __syncthreads();
+  if (!s_last) return;
+  const u32 nc = ld_agent(&a.ccnt[m * 32]);
+  u32 T = 0u, I = 0x7FFFFFFFu;  // (no b1: every candidate is kept as far as room allows)
+  if (b1ok) select_in_bin(s, clist, nc, b1, a.sel[2 * m + 1], T, I);
+  const bool lds = b1ok && nc <= (u32)kSelList;
+  for (u32 i0 = 0; i0 < nc; i0 += kGtThreads) {
+    const u32 i = i0 + tid;
+    Pair ce = pair_sentinel();
+    if (i < nc) ce = lds ? s.list[i] : unpack_pair(ld_agent64((const u64*)(clist + i)));
+    const u32 key = key_of_bits(ce.bits);
+    put(i < nc && (key > T || (key == T && (u32)ce.idx <= I)), ce);
+  }
+  if (tid == 0) {
+    st_agent(&a.karrive[m * 32], 0u);
+    st_agent(&a.ccnt[m * 32], 0u);
+    st_agent(&a.cnt[m * 32], 0u);
+    st_agent(&a.wcnt[m * 32], 0u);
+  }
+}
+
+// -------------------------------------------------------------- final ----
+// Rank key of a pair: ascending order is (key desc, index asc); the sign
+// rides in bit 0 (never decides: (key, index) is unique).
+__device__ __forceinline__ u64 rank64(const Pair& e) {
+  const u32 key = key_of_bits(e.bits);
+  return ((u64)(0x7FFFFFFFu - key) << 32) | ((u64)((u32)e.idx & 0x7FFFFFFFu) << 1) | (u64)(e.bits >> 31);
+}
+__device__ __forceinline__ Pair unrank64(u64 r) {
+  const u32 key = 0x7FFFFFFFu - (u32)(r >> 32);
+  return Pair{(int32_t)(((u32)r >> 1) & 0x7FFFFFFFu), key | (((u32)r & 1u) << 31)};
+}
+
+__device__ __forceinline__ u64 shfl_xor64(u64 v, int m) {
+  const int lo = __shfl_xor((int)(u32)v, m), hi = __shfl_xor((int)(u32)(v >> 32), m);
+  return ((u64)(u32)hi << 32) | (u64)(u32)lo;
+}
+
+// LDS place of sort element e: one pad word after every 4, so that the 64
+// lanes of a wave, 4 elements apart, fall on different banks.
+__device__ __forceinline__ u32 sort_slot(u32 e) { return e + (e >> 2); }
+constexpr int kSortLds = kSortTile + kSortTile / 4;
+
+// Bitonic sort of 4096 keys, ascending; thread t holds elements 4t .. 4t + 3
+// in x.  Partners at distance 1 and 2 are in the same thread, 4 .. 128 in
+// the same wave (lane shuffles), 256 and above in other waves (LDS).
+__device__ void block_sort4096(u64 (&x)[kSortPer], u64* lds) {
+  const int tid = threadIdx.x;
+  // fully unrolled: every stage's distance is a constant, so the partners
+  // inside a thread are plain registers and the lane masks immediates
+#pragma unroll
+  for (u32 size = 2; size <= (u32)kSortTile; size <<= 1) {
+#pragma unroll
+    for (u32 d = size >> 1; d > 0; d >>= 1) {
+      u64 y[kSortPer];
+      if (d >= 4u * kWave) {
+#pragma unroll
+        for (int c = 0; c < kSortPer; ++c) lds[sort_slot(kSortPer * tid + c)] = x[c];
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < kSortPer; ++c) y[c] = lds[sort_slot((kSortPer * tid + c) ^ d)];
+        __syncthreads();
+      } else if (d >= (u32)kSortPer) {
+#pragma unroll
+        for (int c = 0; c < kSortPer; ++c) y[c] = shfl_xor64(x[c], (int)(d / kSortPer));
+      } else {
+#pragma unroll
+        for (int c = 0; c < kSortPer; ++c) y[c] = x[c ^ d];
+      }
+#pragma unroll
+      for (int c = 0; c < kSortPer; ++c) {
+        const u32 e = (u32)(kSortPer * tid + c);
+        const bool asc = (e & size) == 0, lower = (e & d) == 0;
+        x[c] = (asc == lower) ? (x[c] < y[c] ? x[c] : y[c]) : (x[c] < y[c] ? y[c] : x[c]);
+      }
     }
   }
 }
 
-// Sorts every run of kRun entries of every segment in place.
-template <class Cmp>
-__global__ __launch_bounds__(kRunThreads) void k_run_sort(Pair* data, int64_t seg_len, int64_t runs_per_seg) {
-  __shared__ Pair s[kRun];
-  const int64_t seg = blockIdx.x / runs_per_seg;
-  const int64_t run = blockIdx.x % runs_per_seg;
-  const int64_t b0 = run * kRun;
-  const int len = (int)std::min<int64_t>(kRun, seg_len - b0);
-  Pair* p = data + seg * seg_len + b0;
-  for (int i = threadIdx.x; i < kRun; i += kRunThreads) s[i] = i < len ? p[i] : pair_sentinel();
-  __syncthreads();
-  lds_bitonic<Cmp>(s, kRun);
-  for (int i = threadIdx.x; i < len; i += kRunThreads) p[i] = s[i];
+// P = 1: the single row, as pairs.
+__global__ void k_gt_pack_row(const int32_t* __restrict__ idx, const float* __restrict__ val, int64_t k,
+                              Pair* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < k) out[i] = Pair{idx[i], __float_as_uint(val[i])};
 }
 
-// Merge-path split of output position o between sorted A[0,la) and B[0,lb):
-// the number of A entries among the first o outputs (A first on equal keys).
-template <class Cmp>
-__device__ __forceinline__ int64_t merge_split(const Pair* A, int64_t la, const Pair* B, int64_t lb, int64_t o) {
+struct FinalArgs {
+  const int32_t* idx;  // the rows
+  int32_t P;
+  int64_t k, n;
+  u32 logNP;
+  uint8_t* mask;
+  const Pair* F;       // the final set, k pairs in no order
+  int64_t nruns;       // workgroups that sort runs; the others make the mask
+  u64* runs;           // sorted runs (more than one run)
+  int32_t* out_idx;    // (one run)
+  float* out_val;
+  u32* err;
+};
+
+// Workgroups 0 .. nruns-1 sort runs of the final set; workgroup (p, part)
+// after them joins row p's entries of its part against the final set's (the
+// mask) and checks them: in [0, n), and no index twice in the row.
+__global__ __launch_bounds__(kGtThreads) void k_gt_final(FinalArgs a) {
+  __shared__ u64 s_lds[kSlots];  // the two tables, or the sort's LDS
+  __shared__ Pair s_stage[kStageCap];
+  __shared__ u32 s_n;
+  static_assert(kSortLds <= (int)kSlots, "the sort fits in the tables' LDS");
+  u32* s_key = (u32*)s_lds;      // the final set's part
+  u32* s_row = s_key + kSlots;   // the row's part (the repeat check)
+  u64* s = s_lds;
+  const int tid = threadIdx.x;
+  if ((int64_t)blockIdx.x < a.nruns) {
+    const int64_t base = (int64_t)blockIdx.x * kSortTile;
+    u64 x[kSortPer];
+#pragma unroll
+    for (int c = 0; c < kSortPer; ++c) {
+      const int64_t i = base + kSortPer * tid + c;
+      x[c] = i < a.k ? rank64(a.F[i]) : ~0ull;
+    }
+    block_sort4096(x, s);
+    const bool one = a.k <= kSortTile;
+#pragma unroll
+    for (int c = 0; c < kSortPer; ++c) {
+      const int64_t i = base + kSortPer * tid + c;
+      if (i >= a.k) continue;
+      if (one) {
+        const Pair e = unrank64(x[c]);
+        a.out_idx[i] = e.idx;
+        a.out_val[i] = __uint_as_float(e.bits);
+      } else {
+        a.runs[i] = x[c];
+      }
+    }
+    return;
+  }
+  const u32 NP = 1u << a.logNP;
+  const int64_t b = (int64_t)blockIdx.x - a.nruns;
+  const int64_t p = b / NP;
+  const u32 g = (u32)(b % NP);
+  for (u32 i = tid; i < kSlots; i += kGtThreads) {
+    s_key[i] = 0u;
+    s_row[i] = 0u;
+  }
+  __syncthreads();
+  // the final set's indices of this part
+  stage_part(a.k, a.logNP, g, s_stage, &s_n, [&](int64_t j) { return Pair{a.F[j].idx, 0u}; }, [&](u32 n) {
+    for (u32 i = tid; i < n; i += kGtThreads) {
+      const int32_t x = s_stage[i].idx;
+      (void)lds_insert(s_key, nullptr, gt_hash(x, a.logNP).slot, x, 0u);
+    }
+  });
+  // row p's entries of this part (staged with their place in the row)
+  const int32_t* row = a.idx + p * a.k;
+  uint8_t* mrow = a.mask + p * a.k;
+  stage_part(a.k, a.logNP, g, s_stage, &s_n, [&](int64_t j) { return Pair{row[j], (u32)j}; }, [&](u32 n) {
+    for (u32 i = tid; i < n; i += kGtThreads) {
+      const Pair e = s_stage[i];
+      const u32 h = gt_hash(e.idx, a.logNP).slot;
+      const bool bad = e.idx < 0 || (int64_t)e.idx >= a.n || !lds_insert(s_row, nullptr, h, e.idx, 0u);
+      if (bad) atomicOr(a.err, kErrBadInput);
+      mrow[e.bits] = (e.idx >= 0 && lds_find(s_key, h, e.idx) >= 0) ? 1 : 0;
+    }
+  });
+}
+
+// Number of A entries among the first o outputs of the merge of sorted
+// A[0, la) and B[0, lb) (A first on equal keys); one wave, every lane.
+__device__ int64_t wave_merge_split(const u64* A, int64_t la, const u64* B, int64_t lb, int64_t o) {
+  const int lane = lane_id();
   int64_t lo = std::max<int64_t>(0, o - lb), hi = std::min<int64_t>(o, la);
-  while (lo < hi) {
-    int64_t mid = (lo + hi) >> 1;
-    if (Cmp::key(A[mid]) <= Cmp::key(B[o - mid - 1])) lo = mid + 1;
-    else hi = mid;
+  // the answer is lo + #{i in [lo, hi) : A[i] <= B[o - i - 1]} (true for a prefix)
+  while (hi > lo) {
+    const int64_t step = (hi - lo + kWave - 1) / kWave;
+    const int64_t i = lo + step * lane;
+    const bool t = i < hi && A[i] <= B[o - i - 1];
+    const u32 cnt = (u32)__popcll(ballot(t));
+    if (step == 1) return lo + cnt;
+    if (cnt == 0) return lo;
+    const int64_t nlo = lo + step * (cnt - 1) + 1;
+    hi = std::min<int64_t>(hi, lo + step * cnt);
+    lo = nlo;
   }
   return lo;
 }
 
-// Merges adjacent sorted runs of length L (inside segments of seg_len).
-template <class Cmp>
-__global__ __launch_bounds__(kMergeThreads) void k_merge_pass(const Pair* __restrict__ src, Pair* __restrict__ dst,
-                                                              int64_t seg_len, int64_t nseg, int64_t L,
-                                                              int64_t threads_per_seg) {
-  const int64_t gt = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
-  const int64_t seg = gt / threads_per_seg;
-  if (seg >= nseg) return;
-  const int64_t o0 = (gt % threads_per_seg) * kMergeSpan;  // output position in the segment
-  if (o0 >= seg_len) return;
-  const int64_t pair0 = (o0 / (2 * L)) * (2 * L);
-  const int64_t la = std::max<int64_t>(0, std::min<int64_t>(L, seg_len - pair0));
-  const int64_t lb = std::max<int64_t>(0, std::min<int64_t>(L, seg_len - pair0 - L));
-  const Pair* A = src + seg * seg_len + pair0;
-  const Pair* B = A + la;
-  Pair* out = dst + seg * seg_len + pair0;
-  const int64_t o = o0 - pair0;
-  const int64_t oend = std::min<int64_t>(o + kMergeSpan, la + lb);
-  int64_t i = merge_split<Cmp>(A, la, B, lb, o);
-  int64_t j = o - i;
-  for (int64_t q = o; q < oend; ++q) {
-    bool takeA = j >= lb || (i < la && Cmp::key(A[i]) <= Cmp::key(B[j]));
-    out[q] = takeA ? A[i++] : B[j++];
-  }
-}
-
-// Host: sorts nseg segments of seg_len entries (in `a`, using `b` as scratch);
-// returns the buffer that holds the result.
-template <class Cmp>
-static Pair* sort_segments(Pair* a, Pair* b, int64_t seg_len, int64_t nseg, hipStream_t st) {
-  if (seg_len <= 1 || nseg == 0) return a;
-  const int64_t runs = (seg_len + kRun - 1) / kRun;
-  hipLaunchKernelGGL(k_run_sort<Cmp>, dim3((unsigned)(runs * nseg)), dim3(kRunThreads), 0, st, a, seg_len, runs);
-  const int64_t tps = (seg_len + kMergeSpan - 1) / kMergeSpan;
-  const int64_t blocks = (tps * nseg + kMergeThreads - 1) / kMergeThreads;
-  for (int64_t L = kRun; L < seg_len; L *= 2) {
-    hipLaunchKernelGGL(k_merge_pass<Cmp>, dim3((unsigned)blocks), dim3(kMergeThreads), 0, st, a, b, seg_len, nseg, L, tps);
-    std::swap(a, b);
-  }
-  return a;
-}
-
-__global__ void k_gt_load_rows(const int32_t* __restrict__ idx, const float* __restrict__ val, Pair* __restrict__ out,
-                               int64_t total) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < total) out[i] = Pair{idx[i], __float_as_uint(val[i])};
-}
-
-// Rows sorted by index: flags a repeated index or one outside [0, n).
-__global__ void k_gt_validate(const Pair* __restrict__ rows, int64_t k, int64_t total, int64_t n, u32* err) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= total) return;
-  int32_t x = rows[i].idx;
-  bool bad = x < 0 || (int64_t)x >= n;
-  if (i % k != 0) bad = bad || rows[i - 1].idx == x;
-  if (bad) atomicOr(err, kErrBadInput);
-}
-
-// Union of slot pairs.  Merge m combines A = slots[sa[m]] and B = slots[sa[m] + half]
-// (k entries each, sorted by index) into M[m] (2k entries): entries in merge
-// order, a B entry whose index A also holds becomes a hole (idx -1) and that A
-// entry carries a + b.
-struct UnionArgs {
-  Pair* slots;
-  Pair* M;
-  int64_t k;
-  int64_t half;         // 2^r
-  int64_t stride;       // 2^(r+1)
-  int64_t threads_per_merge;
-  int64_t nm;           // merges in this round
+struct MergeArgs {
+  const u64* src;
+  u64* dst;            // (not the last pass)
+  int64_t k, L;        // runs of L become runs of 2L
+  bool last;           // write the outputs
+  int32_t* out_idx;
+  float* out_val;
 };
 
-__global__ __launch_bounds__(kMergeThreads) void k_gt_union(UnionArgs a) {
-  const int64_t gt = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
-  const int64_t m = gt / a.threads_per_merge;
-  const int64_t o = (gt % a.threads_per_merge) * kMergeSpan;
-  const int64_t two_k = 2 * a.k;
-  if (m >= a.nm || o >= two_k) return;
-  const Pair* A = a.slots + (m * a.stride) * a.k;
-  const Pair* B = a.slots + (m * a.stride + a.half) * a.k;
-  Pair* out = a.M + m * two_k;
-  const int64_t la = a.k, lb = a.k;
-  const int64_t oend = std::min<int64_t>(o + kMergeSpan, two_k);
-  int64_t i = merge_split<ByIdx>(A, la, B, lb, o);
-  int64_t j = o - i;
-  for (int64_t q = o; q < oend; ++q) {
-    bool takeA = j >= lb || (i < la && (u32)A[i].idx <= (u32)B[j].idx);
-    if (takeA) {
-      Pair e = A[i++];
-      if (j < lb && B[j].idx == e.idx) e.bits = __float_as_uint(__uint_as_float(e.bits) + __uint_as_float(B[j].bits));
-      out[q] = e;
-    } else {
-      Pair e = B[j++];
-      if (i > 0 && A[i - 1].idx == e.idx) e = pair_sentinel();
-      out[q] = e;
-    }
+__global__ __launch_bounds__(kGtThreads) void k_gt_merge(MergeArgs a) {
+  __shared__ u64 s[kSortTile];
+  __shared__ int64_t s_cut[2];
+  const int tid = threadIdx.x, w = tid / kWave;
+  const int64_t t0 = (int64_t)blockIdx.x * kSortTile;  // first output
+  const int64_t pb = (t0 / (2 * a.L)) * (2 * a.L);     // the pair of runs
+  const int64_t la = std::min<int64_t>(a.L, a.k - pb);
+  const int64_t lb = std::max<int64_t>(0, std::min<int64_t>(a.L, a.k - pb - a.L));
+  const u64* A = a.src + pb;
+  const u64* B = A + la;
+  const int64_t o0 = t0 - pb, o1 = std::min<int64_t>(o0 + kSortTile, la + lb);
+  if (w < 2) {
+    const int64_t cut = wave_merge_split(A, la, B, lb, w == 0 ? o0 : o1);
+    if (lane_id() == 0) s_cut[w] = cut;
   }
-}
-
-// One workgroup per merge: keeps the k best of M[m] (holes excluded) in index
-// order, written to slots[m * stride].
-struct SelectArgs {
-  Pair* slots;
-  const Pair* M;
-  int64_t k;
-  int64_t stride;
-};
-
-__global__ __launch_bounds__(kSelThreads) void k_gt_select(SelectArgs a) {
-  constexpr int NT = kSelThreads;
-  __shared__ u32 s_hist[2048];
-  __shared__ u32 s_scan[NT / kWave + 1];
-  __shared__ u32 s_found[3];
-  const int tid = threadIdx.x;
-  const int64_t m = blockIdx.x;
-  const int64_t len = 2 * a.k;
-  const Pair* M = a.M + m * len;
-  Pair* out = a.slots + (m * a.stride) * a.k;
-  const int shifts[3] = {20, 9, 0};
-  const int widths[3] = {11, 11, 9};
-  u32 prefix = 0;
-  int64_t need = a.k;
-  int64_t t_strict = -1;
-  u32 t_eq = 0;
-  int64_t r = 0;
-  for (int L = 0; L < 3; ++L) {
-    const int sh = shifts[L], wd = widths[L];
-    const u32 nbins = 1u << wd;
-    for (int i = tid; i < 2048; i += NT) s_hist[i] = 0;
-    __syncthreads();
-    for (int64_t i = tid; i < len; i += NT) {
-      Pair e = M[i];
-      u32 key = key_of_bits(e.bits);
-      if (e.idx >= 0 && (key >> (sh + wd)) == prefix) atomicAdd(&s_hist[(key >> sh) & (nbins - 1)], 1u);
-    }
-    __syncthreads();
-    const int cpt = std::max(1, (int)nbins / NT);
-    const int top = (int)nbins - cpt * tid;
-    u32 own = 0;
-    if (top > 0)
-      for (int d = top - 1; d >= std::max(0, top - cpt); --d) own += s_hist[d];
-    u32 tot;
-    u32 above = block_exclusive_sum<NT>(own, s_scan, tot);
-    if (tid == 0) s_found[0] = 0xFFFFFFFFu;
-    __syncthreads();
-    if (top > 0 && (int64_t)above < need && (int64_t)(above + own) >= need) {
-      u32 run = above;
-      for (int d = top - 1; d >= std::max(0, top - cpt); --d) {
-        u32 h = s_hist[d];
-        if ((int64_t)(run + h) >= need) {
-          s_found[0] = (u32)d;
-          s_found[1] = run;
-          s_found[2] = h;
-          break;
-        }
-        run += h;
-      }
-    }
-    __syncthreads();
-    const u32 d = s_found[0];
-    if (d == 0xFFFFFFFFu) return;  // fewer than k live entries: impossible for valid rows
-    need -= (int64_t)s_found[1];
-    const int64_t h = s_found[2];
-    prefix = (prefix << wd) | d;
-    if (need == h) {
-      t_strict = (int64_t)((u64)prefix << sh) - 1;
-      r = 0;
-      break;
-    }
-    if (L == 2) {
-      t_strict = prefix;
-      t_eq = prefix;
-      r = need;
-    }
-    __syncthreads();
-  }
-  // ordered compaction over contiguous per-thread ranges
-  const int64_t span = (len + NT - 1) / NT;
-  const int64_t lo = std::min<int64_t>(len, tid * span), hi = std::min<int64_t>(len, lo + span);
-  u32 gt = 0, eq = 0;
-  for (int64_t i = lo; i < hi; ++i) {
-    Pair e = M[i];
-    u32 key = key_of_bits(e.bits);
-    bool live = e.idx >= 0;
-    gt += live && (int64_t)key > t_strict;
-    eq += live && r > 0 && key == t_eq;
-  }
-  u32 gt_tot, eq_tot;
-  u32 gt_ex = block_exclusive_sum<NT>(gt, s_scan, gt_tot);
-  u32 eq_ex = block_exclusive_sum<NT>(eq, s_scan, eq_tot);
-  int64_t pos = (int64_t)gt_ex + std::min<int64_t>((int64_t)eq_ex, r);
-  int64_t eq_seen = eq_ex;
-  for (int64_t i = lo; i < hi; ++i) {
-    Pair e = M[i];
-    u32 key = key_of_bits(e.bits);
-    bool live = e.idx >= 0;
-    bool g = live && (int64_t)key > t_strict;
-    bool q = live && r > 0 && key == t_eq;
-    bool sel = g || (q && eq_seen < r);
-    eq_seen += q;
-    if (sel && pos < a.k) out[pos++] = e;
-  }
-}
-
-// The same selection with M's keys loaded once into registers: thread t
-// holds entries j NT + t (j < EPT; coalesced rows, every load in flight at
-// once).  The three histogram levels run on the registers, and the ordered
-// compaction walks the rows in order (index order is (row, thread) order)
-// with a ballot and per-wave counts per row; only the selected pairs are
-// read again to be written out.  For 2k <= EPT NT.
-template <int EPT>
-__global__ __launch_bounds__(kSelThreads) void k_gt_select_reg(SelectArgs a) {
-  constexpr int NT = kSelThreads;
-  __shared__ u32 s_hist[2048];
-  __shared__ u32 s_scan[NT / kWave + 1];
-  __shared__ u32 s_found[3];
-  const int tid = threadIdx.x;
-  const int64_t m = blockIdx.x;
-  const u32 len = (u32)(2 * a.k);
-  const Pair* __restrict__ M = a.M + m * (int64_t)len;
-  Pair* __restrict__ out = a.slots + (m * a.stride) * a.k;
-  // a hole or a place past the end gets key 0xFFFFFFFF, above every real
-  // key: no histogram level counts it (its top bits never match the prefix)
-  // and, compared as signed, it is below every threshold
-  // (16 rows of loads in flight at a time: all EPT at once would need two
-  // registers per row on top of the keys)
-  static_assert(EPT % 16 == 0, "rows come in groups of 16");
-  u32 key[EPT];
-#pragma unroll
-  for (int c = 0; c < EPT; c += 16) {
-#pragma unroll
-    for (int j = c; j < c + 16; ++j) {
-      const u32 i = (u32)(j * NT + tid);
-      const Pair e = M[i < len ? i : 0u];
-      key[j] = i < len && e.idx >= 0 ? key_of_bits(e.bits) : 0xFFFFFFFFu;
-    }
-    asm volatile("" ::: "memory");
-  }
-  const int shifts[3] = {20, 9, 0};
-  const int widths[3] = {11, 11, 9};
-  u32 prefix = 0;
-  u32 need = (u32)a.k;
-  u32 t_lo = 0, t_eq = 0, r = 0;
-  for (int L = 0; L < 3; ++L) {
-    const int sh = shifts[L], wd = widths[L];
-    const u32 nbins = 1u << wd;
-    for (int i = tid; i < 2048; i += NT) s_hist[i] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < EPT; ++j)
-      if ((key[j] >> (sh + wd)) == prefix) atomicAdd(&s_hist[(key[j] >> sh) & (nbins - 1)], 1u);
-    __syncthreads();
-    const int cpt = std::max(1, (int)nbins / NT);
-    const int top = (int)nbins - cpt * tid;
-    u32 own = 0;
-    if (top > 0)
-      for (int d = top - 1; d >= std::max(0, top - cpt); --d) own += s_hist[d];
-    u32 tot;
-    const u32 above = block_exclusive_sum<NT>(own, s_scan, tot);
-    if (tid == 0) s_found[0] = 0xFFFFFFFFu;
-    __syncthreads();
-    if (top > 0 && above < need && above + own >= need) {
-      u32 run = above;
-      for (int d = top - 1; d >= std::max(0, top - cpt); --d) {
-        const u32 h = s_hist[d];
-        if (run + h >= need) {
-          s_found[0] = (u32)d;
-          s_found[1] = run;
-          s_found[2] = h;
-          break;
-        }
-        run += h;
-      }
-    }
-    __syncthreads();
-    const u32 d = s_found[0];
-    if (d == 0xFFFFFFFFu) return;  // fewer than k live entries: impossible for valid rows
-    need -= s_found[1];
-    const u32 h = s_found[2];
-    prefix = (prefix << wd) | d;
-    __syncthreads();  // s_found is rewritten by the next level
-    if (need == h) {
-      t_lo = prefix << sh;
-      break;
-    }
-    if (L == 2) {
-      t_lo = prefix + 1;
-      t_eq = prefix;
-      r = need;
-    }
-  }
-  // ordered compaction: every key >= t_lo and the first r equal to t_eq,
-  // row by row
-  __shared__ u32 s_wc[2][NT / kWave][2];
-  const int lane = lane_id(), w = tid / kWave;
-  u32 gt_seen = 0, eq_seen = 0;
-#pragma unroll
-  for (int j = 0; j < EPT; ++j) {
-    const bool g = (int)key[j] >= (int)t_lo;
-    const bool q = r > 0 && key[j] == t_eq;
-    const u64 bg = ballot(g), be = ballot(q);
-    if (lane == 0) {
-      s_wc[j & 1][w][0] = (u32)__popcll(bg);
-      s_wc[j & 1][w][1] = (u32)__popcll(be);
-    }
-    __syncthreads();
-    u32 og = 0, oe = 0, tg = 0, te = 0;
-#pragma unroll
-    for (int v = 0; v < NT / kWave; ++v) {
-      const u32 cg = s_wc[j & 1][v][0], ce = s_wc[j & 1][v][1];
-      og += v < w ? cg : 0u;
-      oe += v < w ? ce : 0u;
-      tg += cg;
-      te += ce;
-    }
-    const u32 gb = gt_seen + og + lanes_below(bg), eb = eq_seen + oe + lanes_below(be);
-    if (g || (q && eb < r)) {
-      const u32 pos = gb + std::min(eb, r);
-      if (pos < (u32)a.k) out[pos] = M[(u32)(j * NT + tid)];
-    }
-    gt_seen += tg;
-    eq_seen += te;
-    asm volatile("" ::: "memory");  // keep each row's reload in its row
-  }
-}
-
-__global__ void k_gt_emit(const Pair* __restrict__ g, int64_t k, int32_t* out_idx, float* out_val) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < k) {
-    out_idx[i] = g[i].idx;
-    out_val[i] = __uint_as_float(g[i].bits);
-  }
-}
-
-// mask[t] = 1 when idx[t] is among the k indices of `sorted0` (sorted by index).
-__global__ void k_gt_mask(const int32_t* __restrict__ idx, int64_t total, const Pair* __restrict__ sorted0, int64_t k,
-                          uint8_t* __restrict__ mask) {
-  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= total) return;
-  int32_t x = idx[t];
-  int64_t lo = 0, hi = k;
+  __syncthreads();
+  const int64_t i0 = s_cut[0], i1 = s_cut[1];
+  const int64_t j0 = o0 - i0, j1 = o1 - i1;
+  const int na = (int)(i1 - i0), nb = (int)(j1 - j0);
+  for (int i = tid; i < na; i += kGtThreads) s[i] = A[i0 + i];
+  for (int i = tid; i < nb; i += kGtThreads) s[na + i] = B[j0 + i];
+  __syncthreads();
+  const u64* sA = s;
+  const u64* sB = s + na;
+  const int d = kSortPer * tid;
+  const int nout = na + nb;
+  if (d >= nout) return;
+  int lo = std::max(0, d - nb), hi = std::min(d, na);
   while (lo < hi) {
-    int64_t mid = (lo + hi) >> 1;
-    if (sorted0[mid].idx < x) lo = mid + 1;
+    const int mid = (lo + hi) >> 1;
+    if (sA[mid] <= sB[d - mid - 1]) lo = mid + 1;
     else hi = mid;
   }
-  mask[t] = (lo < k && sorted0[lo].idx == x) ? 1 : 0;
+  int i = lo, j = d - lo;
+  for (int u = 0; u < kSortPer && d + u < nout; ++u) {
+    const bool takeA = j >= nb || (i < na && sA[i] <= sB[j]);
+    const u64 v = takeA ? sA[i++] : sB[j++];
+    const int64_t o = pb + o0 + d + u;
+    if (a.last) {
+      const Pair e = unrank64(v);
+      a.out_idx[o] = e.idx;
+      a.out_val[o] = __uint_as_float(e.bits);
+    } else {
+      a.dst[o] = v;
+    }
+  }
 }
 
-__global__ void k_gt_copy(const Pair* __restrict__ src, Pair* __restrict__ dst, int64_t len) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < len) dst[i] = src[i];
+// ------------------------------------------------------------------ layout ----
+static int gt_rounds(int64_t P) {
+  int R = 0;
+  while (((int64_t)1 << R) < P) ++R;
+  return R;
 }
 
 struct GtLayout {
-  size_t slots, tmp, M, f0, f1, total;
+  int R;
+  int64_t nmax;  // merges of round 0 (the most of any round), at least 1
+  u32 logNP;     // hash parts: 2^logNP
+  size_t hist, arrive, wcnt, cnt, ccnt, karrive, clear_end;  // zero-filled at the start of a call
+  size_t sel, W, cand, out, runs[2], total;
 };
 
 static GtLayout gt_layout(int64_t P, int64_t k) {
   GtLayout L{};
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  size_t pk = sizeof(Pair) * (size_t)P * (size_t)std::max<int64_t>(k, 1);
-  L.slots = kWorkspaceHeader;  // after the header whose first word is the error word
-  L.tmp = L.slots + al(pk);
-  L.M = L.tmp + al(pk);
-  L.f0 = L.M + al(pk);  // (P/2) merges x 2k entries <= P*k
-  L.f1 = L.f0 + al(sizeof(Pair) * (size_t)std::max<int64_t>(k, 1));
-  L.total = L.f1 + al(sizeof(Pair) * (size_t)std::max<int64_t>(k, 1));
+  const int64_t kk = std::max<int64_t>(k, 1);
+  L.R = gt_rounds(P);
+  L.nmax = std::max<int64_t>(1, gt_merges(P, 0));
+  u32 lp = 0;
+  while (((int64_t)kPartLoad << lp) < kk) ++lp;
+  L.logNP = lp;
+  size_t o = kWorkspaceHeader;  // after the header whose first word is the error word
+  L.hist = o;
+  o += al(4 * (size_t)kGtBins * (size_t)L.nmax);
+  for (size_t* f : {&L.arrive, &L.wcnt, &L.cnt, &L.ccnt, &L.karrive}) {
+    *f = o;
+    o += al(128 * (size_t)L.nmax);
+  }
+  L.clear_end = o;
+  L.sel = o;
+  o += al(8 * (size_t)L.nmax);
+  L.W = o;
+  o += al(sizeof(Pair) * 2 * (size_t)kk * (size_t)L.nmax);
+  L.cand = o;
+  o += al(sizeof(Pair) * 2 * (size_t)kk * (size_t)L.nmax);
+  L.out = o;
+  o += al(sizeof(Pair) * (size_t)kk * (size_t)P);
+  for (int i = 0; i < 2; ++i) {
+    L.runs[i] = o;
+    o += al(8 * (size_t)kk);
+  }
+  L.total = o;
   return L;
 }
 
@@ -470,7 +827,7 @@ static GtLayout gt_layout(int64_t P, int64_t k) {
 using namespace tgs;
 
 extern "C" size_t tgs_gtopk_workspace_bytes(int32_t P, int64_t k, int64_t n) {
-  if (P < 1 || k < 0 || n < 0 || n > INT32_MAX || k > n) return 0;
+  if (P < 1 || k < 0 || n < 0 || n > INT32_MAX || k > n || k > kGtMaxK || (int64_t)P * k > INT32_MAX) return 0;
   return gt_layout(P, k).total;
 }
 
@@ -480,12 +837,14 @@ extern "C" tgs_status tgs_gtopk_merge(const int32_t* idx, const float* val, int3
   if (P < 1) return fail(TGS_EINVAL, "gtopk_merge: P=%d < 1", (int)P);
   if (n < 0 || n > INT32_MAX) return fail(TGS_EINVAL, "gtopk_merge: n=%lld outside [0, 2^31-1]", (long long)n);
   if (k < 0 || k > n) return fail(TGS_EINVAL, "gtopk_merge: k=%lld outside [0, n]", (long long)k);
+  if (k > kGtMaxK) return fail(TGS_EINVAL, "gtopk_merge: k=%lld above 2^20", (long long)k);
   if ((int64_t)P * k > INT32_MAX) return fail(TGS_EINVAL, "gtopk_merge: P*k too large");
   if (!workspace) return fail(TGS_EINVAL, "gtopk_merge: null workspace");
   if (k > 0 && (!idx || !val || !out_idx || !out_val || !out_mask))
     return fail(TGS_EINVAL, "gtopk_merge: null array pointer");
   for (const void* p : {(const void*)idx, (const void*)val, (const void*)out_idx, (const void*)out_val})
     if (((uintptr_t)p & 3u) != 0) return fail(TGS_EINVAL, "gtopk_merge: pointer not 4-byte aligned");
+  if (((uintptr_t)workspace & 15u) != 0) return fail(TGS_EINVAL, "gtopk_merge: workspace not 16-byte aligned");
   const size_t pk4 = (size_t)P * (size_t)k * 4, k4 = (size_t)k * 4, pk1 = (size_t)P * (size_t)k;
   if (overlaps(out_idx, k4, out_val, k4) || overlaps(out_idx, k4, out_mask, pk1) || overlaps(out_val, k4, out_mask, pk1) ||
       overlaps(idx, pk4, out_idx, k4) || overlaps(idx, pk4, out_val, k4) || overlaps(idx, pk4, out_mask, pk1) ||
@@ -497,38 +856,81 @@ extern "C" tgs_status tgs_gtopk_merge(const int32_t* idx, const float* val, int3
   if (k == 0) return TGS_OK;
   char* ws = (char*)workspace;
   u32* err = (u32*)ws;
-  Pair* slots = (Pair*)(ws + L.slots);
-  Pair* tmp = (Pair*)(ws + L.tmp);
-  Pair* M = (Pair*)(ws + L.M);
-  const int64_t total = (int64_t)P * k;
-  const unsigned eb = (unsigned)((total + 255) / 256);
-
-  hipLaunchKernelGGL(k_gt_load_rows, dim3(eb), dim3(256), 0, stream, idx, val, slots, total);
-  Pair* sorted = sort_segments<ByIdx>(slots, tmp, k, P, stream);
-  if (sorted != slots) hipLaunchKernelGGL(k_gt_copy, dim3(eb), dim3(256), 0, stream, sorted, slots, total);
-  hipLaunchKernelGGL(k_gt_validate, dim3(eb), dim3(256), 0, stream, slots, k, total, n, err);
-
-  for (int64_t half = 1; half < P; half *= 2) {
-    const int64_t stride = 2 * half;
-    const int64_t nm = (P - half + stride - 1) / stride;  // slots s = m*stride with s + half < P
-    UnionArgs ua{slots, M, k, half, stride, (2 * k + kMergeSpan - 1) / kMergeSpan, nm};
-    const int64_t ublocks = (ua.threads_per_merge * nm + kMergeThreads - 1) / kMergeThreads;
-    hipLaunchKernelGGL(k_gt_union, dim3((unsigned)ublocks), dim3(kMergeThreads), 0, stream, ua);
-    SelectArgs sa{slots, M, k, stride};
-    const int64_t ept = (2 * k + kSelThreads - 1) / kSelThreads;
-    if (ept <= 16) hipLaunchKernelGGL(k_gt_select_reg<16>, dim3((unsigned)nm), dim3(kSelThreads), 0, stream, sa);
-    else if (ept <= 32) hipLaunchKernelGGL(k_gt_select_reg<32>, dim3((unsigned)nm), dim3(kSelThreads), 0, stream, sa);
-    else if (ept <= 48) hipLaunchKernelGGL(k_gt_select_reg<48>, dim3((unsigned)nm), dim3(kSelThreads), 0, stream, sa);
-    else if (ept <= 64) hipLaunchKernelGGL(k_gt_select_reg<64>, dim3((unsigned)nm), dim3(kSelThreads), 0, stream, sa);
-    else hipLaunchKernelGGL(k_gt_select, dim3((unsigned)nm), dim3(kSelThreads), 0, stream, sa);
+  const int R = L.R;
+  const int64_t NP = (int64_t)1 << L.logNP;
+  {
+    const int64_t n16 = (int64_t)(L.clear_end - L.hist) / 16;
+    const int blocks = (int)std::min<int64_t>(1024, (n16 + 255) / 256);
+    hipLaunchKernelGGL(k_gt_clear, dim3(blocks), dim3(256), 0, stream, (v4u*)(ws + L.hist), n16);
   }
-  Pair* f0 = (Pair*)(ws + L.f0);
-  Pair* f1 = (Pair*)(ws + L.f1);
-  const unsigned kb = (unsigned)((k + 255) / 256);
-  hipLaunchKernelGGL(k_gt_copy, dim3(kb), dim3(256), 0, stream, slots, f0, k);
-  Pair* g = sort_segments<ByRank>(f0, f1, k, 1, stream);
-  hipLaunchKernelGGL(k_gt_emit, dim3(kb), dim3(256), 0, stream, g, k, out_idx, out_val);
-  hipLaunchKernelGGL(k_gt_mask, dim3(eb), dim3(256), 0, stream, idx, total, slots, k, out_mask);
+  Pair* outs = (Pair*)(ws + L.out);
+  for (int r = 0; r < R; ++r) {
+    const int64_t nm = gt_merges(P, r);
+    JoinArgs ja{};
+    ja.P = P;
+    ja.r = r;
+    ja.k = k;
+    ja.logNP = L.logNP;
+    ja.idx = idx;
+    ja.val = val;
+    ja.out = outs;
+    ja.W = (Pair*)(ws + L.W);
+    ja.wcnt = (u32*)(ws + L.wcnt);
+    ja.hist = (u32*)(ws + L.hist);
+    ja.arrive = (u32*)(ws + L.arrive);
+    ja.sel = (u32*)(ws + L.sel);
+    ja.err = err;
+    hipLaunchKernelGGL(k_gt_join, dim3((unsigned)(nm * NP)), dim3(kGtThreads), 0, stream, ja);
+    KeepArgs ka{};
+    ka.k = k;
+    ka.W = ja.W;
+    ka.wcnt = ja.wcnt;
+    ka.sel = ja.sel;
+    ka.cnt = (u32*)(ws + L.cnt);
+    ka.ccnt = (u32*)(ws + L.ccnt);
+    ka.karrive = (u32*)(ws + L.karrive);
+    ka.cand = (Pair*)(ws + L.cand);
+    ka.out = outs + gt_out_base(P, r) * k;
+    ka.err = err;
+    const int64_t cpm = (2 * k + kKeepSpan - 1) / kKeepSpan;
+    hipLaunchKernelGGL(k_gt_keep, dim3((unsigned)(cpm * nm)), dim3(kGtThreads), 0, stream, ka);
+  }
+  {
+    const int64_t nruns = (k + kSortTile - 1) / kSortTile;
+    FinalArgs fa{};
+    fa.idx = idx;
+    fa.P = P;
+    fa.k = k;
+    fa.n = n;
+    fa.logNP = L.logNP;
+    fa.mask = out_mask;
+    // the final set: the last round's output, or the single row (P = 1)
+    fa.F = R > 0 ? outs + gt_out_base(P, R - 1) * k : nullptr;
+    if (R == 0) {
+      // (P = 1) the row is the final set: copy it into the output area
+      hipLaunchKernelGGL(k_gt_pack_row, dim3((unsigned)((k + 255) / 256)), dim3(256), 0, stream, idx, val, k, outs);
+      fa.F = outs;
+    }
+    fa.nruns = nruns;
+    fa.runs = (u64*)(ws + L.runs[0]);
+    fa.out_idx = out_idx;
+    fa.out_val = out_val;
+    fa.err = err;
+    hipLaunchKernelGGL(k_gt_final, dim3((unsigned)(nruns + (int64_t)P * NP)), dim3(kGtThreads), 0, stream, fa);
+    int cur = 0;
+    for (int64_t Lr = kSortTile; Lr < k; Lr *= 2) {
+      MergeArgs ma{};
+      ma.src = (const u64*)(ws + L.runs[cur]);
+      ma.dst = (u64*)(ws + L.runs[1 - cur]);
+      ma.k = k;
+      ma.L = Lr;
+      ma.last = 2 * Lr >= k;
+      ma.out_idx = out_idx;
+      ma.out_val = out_val;
+      hipLaunchKernelGGL(k_gt_merge, dim3((unsigned)nruns), dim3(kGtThreads), 0, stream, ma);
+      cur = 1 - cur;
+    }
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TGS_EHIP, "gtopk_merge: launch failed: %s", hipGetErrorString(e));
   return TGS_OK;

@@ -252,11 +252,11 @@ def parse():
 # the 256 MiB copy of --copy-calibration.  Valid only for the k_step
 # source they were taken on: `source_sha256` is the hash of csrc/topk.hip then.
 MEASURED_TRAFFIC = {
-    "source_sha256": "1e9344826a1cfe0781276b765dffe873623cba5774448a45cf418213bc99b000",
-    # FETCH_SIZE 102,920.8 KiB x (262,144 / 131,083.5: the copy's true read over its counter)
-    "fetch_bytes": 210763306,
-    # WRITE_SIZE 102,792.8 KiB x 1.0 (the copy's counter read exactly 262,144 KiB)
-    "write_bytes": 105259827,
+    "source_sha256": "aa49cc2a6b39fcc8674d6f3df99b8635fbb96b60fca8cab515d9ae5fedcd1e27",
+    # FETCH_SIZE 102,916.5 KiB x (262,144 / 131,083.5: the copy's true read over its counter)
+    "fetch_bytes": 210754565,
+    # WRITE_SIZE 102,793.0 KiB x 1.0 (the copy's counter read exactly 262,144 KiB)
+    "write_bytes": 105260048,
 }
 
 

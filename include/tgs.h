@@ -63,8 +63,8 @@
  *     on other streams at the same time can keep workgroups from starting;
  *     the waits are bounded, so the call then ends with wrong outputs and the
  *     wait-timeout bit (0x2) in the device error word, never a hang.  Run
- *     the top-k step on a device (or stream priority class) it has to itself,
- *     or check the error word.
+ *     the top-k step while no other kernel occupies the device, or check
+ *     the error word.
  *   - Magnitude order: key(x) = bits(x) & 0x7FFFFFFF as an unsigned integer.
  *     This matches |x| for every non-NaN value, ranks NaN above infinity and
  *     makes -0 and +0 equal.  Among equal keys the lower index comes first.
@@ -246,7 +246,7 @@ size_t tgs_gtopk_workspace_bytes(int32_t P, int64_t k, int64_t n);
  *   out_mask [P][k] uint8: 1 where idx[p][j] is one of out_idx, else 0.
  * Rows that break the index precondition set a device error word; check it
  * with tgs_check_device_error (the outputs are then unspecified).
- * k is at most 2^26 and P k at most 2^31 - 1; the workspace must be 16-byte
+ * k is at most 2^20 and P k at most 2^31 - 1; the workspace must be 16-byte
  * aligned.  Each call starts by zero-filling the part of the workspace it
  * keeps its tables and counters in, so it assumes nothing of that part.
  */

@@ -9,31 +9,38 @@
 // A merge needs the union by index of two k-sets and the k best of it.  The
 // union is a hash join in LDS: the indices are hashed into NP parts, and one
 // workgroup per (merge, part) builds a table of the A side's entries of its
-// part and looks the B side's entries of its part up in it.  No set is ever
-// sorted by index and no table lives in memory:
-//   k_gt_clear  zero-fills the histograms and counters of the call.
+// part and looks the B side's entries of its part up in it.  Every set is
+// kept grouped by part (a directory gives each part's place and length), so a
+// workgroup reads its own part and nothing else.  No set is ever sorted by
+// index and no table lives in memory:
+//   k_gt_rcount    counts each row's entries per part, per chunk of 4096 (and
+//                  zero-fills the call's histograms and counters);
+//   k_gt_rscatter  copies each row grouped by part, every entry with its
+//                  place in the row, and writes the rows' directories.
 //   round r, for every merge m (slot s = m 2^(r+1) absorbs s + 2^r):
 //     k_gt_join   workgroup (m, part): the A entries of its part into an LDS
 //                 table; each B entry of its part found there adds its value
-//                 to that entry (one binary32 add), the others are appended
-//                 to the merge's union W; then the A entries are appended.
+//                 to that entry (one binary32 add), the others go to the
+//                 part's region of the merge's union W; then the A entries.
 //                 The union's keys are counted into the merge's histogram of
 //                 key >> 20, and the last workgroup of the merge to arrive
 //                 finds the bin b1 that holds the k-th key.
-//     k_gt_keep   every entry of W above bin b1 is appended to the merge's
-//                 output, the entries of bin b1 are listed as candidates, and
-//                 the last workgroup of the merge to arrive finds the k-th
-//                 key T and the largest index I kept at T among them and
-//                 appends the candidates with key > T, or key = T and index
-//                 <= I (ties keep the lowest indices).
-//   k_gt_final  the mask, as a join of each row against the final set (and
-//               the rows' precondition check: a repeated index within a
-//               row, or one outside [0, n), sets the error word), and runs
-//               of 4096 of the final set sorted by (key desc, index asc);
+//     k_gt_keep   workgroup (m, part): every entry of its part of W above bin
+//                 b1 goes to the same part of slot s's output, the entries of
+//                 bin b1 are listed as candidates, and the last workgroup of
+//                 the merge to arrive finds the k-th key T and the largest
+//                 index I kept at T among them, places the candidates with
+//                 key > T, or key = T and index <= I (ties keep the lowest
+//                 indices), each in its part, and writes the directory.
+//   k_gt_final  the mask, as a join of each row's part against the final
+//               set's (and the rows' precondition check: a repeated index
+//               within a row, or one outside [0, n), sets the error word),
+//               and runs of 4096 of the final set sorted by (key desc, index
+//               asc);
 //   k_gt_merge  passes merge the runs; the last one writes the outputs.
 // Slots without a partner keep their data where it is until they are merged:
-// a slot's data is its row until it has been a merge's destination, then
-// that merge's output.
+// a slot's data is its grouped row until it has been a merge's destination,
+// then its output region, which each later merge into it rewrites.
 #include <algorithm>
 #include <climits>
 #include <vector>
@@ -52,8 +59,12 @@ constexpr int kSortPer = kSortTile / kGtThreads;
 constexpr int kGtBatch = 16;       // loads in flight per thread in the scans
 constexpr u32 kLogSlots = 13;      // places of one part's LDS table
 constexpr u32 kSlots = 1u << kLogSlots;
-constexpr int64_t kPartLoad = kSlots / 2;  // entries a part holds on average at most
+constexpr int64_t kPartLoad = 2048;  // entries of one set a part holds on average at most
 constexpr int64_t kGtMaxK = (int64_t)1 << 20;
+constexpr u32 kMaxParts = 512;     // parts at k = kGtMaxK
+constexpr int kRowPer = 4;
+constexpr int kRowChunk = kRowPer * kGtThreads;  // row entries per workgroup of the row kernels
+constexpr int kJoinPer = 8;        // part entries per thread in flight in k_gt_join
 
 typedef u32 v4u __attribute__((ext_vector_type(4)));
 
@@ -69,6 +80,12 @@ __device__ __forceinline__ HashPart gt_hash(int32_t idx, u32 logNP) {
   const u32 h = (u32)idx * 0x9E3779B1u;
   return HashPart{logNP ? h >> (32u - logNP) : 0u, (h >> (32u - logNP - kLogSlots)) & (kSlots - 1u)};
 }
+
+// Where one part of a set lies (entries [start, start + count) of the set's
+// region) and how many entries it has.
+struct PartDir {
+  u32 start, count;
+};
 
 // An LDS table of one part: key[h] = index + 1 (0: empty), val[h] = the
 // entry's value bits.
@@ -101,31 +118,9 @@ __device__ __forceinline__ void flush_hist(const u32* s_h, u32* H) {
     if (s_h[i]) (void)add_agent_relaxed(&H[i], s_h[i]);
 }
 
-// Appends the entries whose `keep` is set (one per thread) to dst at the
-// places a counter hands out (one device add per workgroup), in no
-// particular order; returns this thread's place (or -1).  Every thread
-// calls it.  s_w holds kGtWaves words, s_base one.
-__device__ int64_t wg_append(bool keep, u32* counter, u32* s_w, u32* s_base) {
-  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
-  const u64 bal = ballot(keep);
-  if (lane == 0) s_w[w] = (u32)__popcll(bal);
-  __syncthreads();
-  u32 woff = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < kGtWaves; ++i) {
-    const u32 v = s_w[i];
-    woff += i < w ? v : 0u;
-    tot += v;
-  }
-  if (tid == 0) *s_base = tot ? add_agent_relaxed(counter, tot) : 0u;
-  __syncthreads();
-  const int64_t pos = keep ? (int64_t)(*s_base + woff + lanes_below(bal)) : -1;
-  __syncthreads();  // s_w and s_base are free again
-  return pos;
-}
-
-// The same for cnt entries of each thread: returns the place of this
-// thread's first.  s_scan holds kGtWaves + 1 words.
+// Appends cnt entries of each thread at places a counter in memory hands out
+// (one device add per workgroup): returns the place of this thread's first.
+// s_scan holds kGtWaves + 1 words.  Every thread calls it.
 __device__ int64_t wg_append_n(u32 cnt, u32* counter, u32* s_scan, u32* s_base) {
   u32 tot;
   const u32 before = block_exclusive_sum<kGtThreads>(cnt, s_scan, tot);
@@ -136,81 +131,129 @@ __device__ int64_t wg_append_n(u32 cnt, u32* counter, u32* s_scan, u32* s_base) 
   return pos;
 }
 
-// Compacts this part's entries among n entries (got by get(j)) into LDS,
-// kStagePer per thread at a time, and hands each batch to use(count) with
-// the batch in s_stage[0 .. count); every thread calls it (barriers).
-constexpr int kStagePer = 8;
-constexpr int kStageCap = kStagePer * kGtThreads;
-template <class Get, class Use>
-__device__ void stage_part(int64_t n, u32 logNP, u32 g, Pair* s_stage, u32* s_n, Get get, Use use) {
-  const int tid = threadIdx.x, lane = lane_id();
-  // the next batch's loads are in flight while this one is staged and used
-  Pair e[kStagePer], nx[kStagePer];
-  auto load = [&](int64_t j0, Pair (&x)[kStagePer]) {
+// The wave's lanes with `keep` set take the next places of an LDS counter (one
+// LDS add per wave): returns this lane's place (meaningless without keep).
+// Every lane of the wave calls it.
+__device__ __forceinline__ u32 wave_take(bool keep, u32* s_n) {
+  const u64 bal = ballot(keep);
+  u32 base = 0;
+  if (bal) {
+    if (lane_id() == 0) base = atomicAdd(s_n, (u32)__popcll(bal));
+    base = __builtin_amdgcn_readfirstlane(base);
+  }
+  return base + lanes_below(bal);
+}
+
+// ---------------------------------------------------------- the rows ----
+struct RowArgs {
+  const int32_t* idx;  // the rows [P][k]
+  const float* val;
+  int64_t k, cpr;      // chunks of kRowChunk per row
+  u32 logNP;
+  u32* rcnt;           // [P][cpr][NP] entries per (row, chunk, part)
+  PartDir* rdir;       // [P][NP] each row's parts in its grouped copy
+  Pair* prow;          // [P][k] the rows grouped by part
+  u32* ppos;           // [P][k] each grouped entry's place in its row
+  v4u* clear;          // zero-filled by k_gt_rcount: the call's counters
+  int64_t nclear;      // (16-byte words)
+};
+
+// Workgroup (p, c) counts chunk c of row p per part; the grid also
+// zero-fills the histograms and counters of the rounds.
+__global__ __launch_bounds__(kGtThreads) void k_gt_rcount(RowArgs a) {
+  __shared__ u32 s_c[kMaxParts];
+  const int tid = threadIdx.x;
+  for (int64_t i = (int64_t)blockIdx.x * kGtThreads + tid; i < a.nclear; i += (int64_t)gridDim.x * kGtThreads)
+    a.clear[i] = v4u{0u, 0u, 0u, 0u};
+  const u32 NP = 1u << a.logNP;
+  const int64_t p = blockIdx.x / a.cpr, c = blockIdx.x % a.cpr;
+  const int32_t* row = a.idx + p * a.k;
+  int32_t ix[kRowPer];
 #pragma unroll
-    for (int u = 0; u < kStagePer; ++u) {
-      const int64_t j = j0 + (int64_t)u * kGtThreads + tid;
-      x[u] = j < n ? get(j) : pair_sentinel();
+  for (int u = 0; u < kRowPer; ++u) {
+    const int64_t j = c * kRowChunk + u * kGtThreads + tid;
+    ix[u] = j < a.k ? row[j] : 0;
+  }
+  for (u32 i = tid; i < NP; i += kGtThreads) s_c[i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kRowPer; ++u) {
+    const int64_t j = c * kRowChunk + u * kGtThreads + tid;
+    if (j < a.k) atomicAdd(&s_c[gt_hash(ix[u], a.logNP).part], 1u);
+  }
+  __syncthreads();
+  for (u32 i = tid; i < NP; i += kGtThreads) a.rcnt[(p * a.cpr + c) * NP + i] = s_c[i];
+}
+
+// Workgroup (p, c) places chunk c of row p: part g of the row starts after
+// the row's entries of parts below g, and the chunk's entries of part g after
+// those of the chunks before it.  Inside a chunk's share of a part the order
+// is whatever the LDS adds give (no result depends on it).
+__global__ __launch_bounds__(kGtThreads) void k_gt_rscatter(RowArgs a) {
+  __shared__ u32 s_c[kMaxParts], s_off[kMaxParts];
+  __shared__ u32 s_scan[kGtWaves + 1];
+  const int tid = threadIdx.x;
+  const u32 NP = 1u << a.logNP;
+  const int64_t p = blockIdx.x / a.cpr, c = blockIdx.x % a.cpr;
+  const int32_t* row = a.idx + p * a.k;
+  const float* vrow = a.val + p * a.k;
+  int32_t ix[kRowPer];
+  u32 vb[kRowPer];
+#pragma unroll
+  for (int u = 0; u < kRowPer; ++u) {
+    const int64_t j = c * kRowChunk + u * kGtThreads + tid;
+    ix[u] = j < a.k ? row[j] : 0;
+    vb[u] = j < a.k ? __float_as_uint(vrow[j]) : 0u;
+  }
+  u32 tot = 0, below = 0;
+  for (u32 g = tid; g < NP; g += kGtThreads) {  // (NP <= kGtThreads: one part per thread)
+    const u32* rc = a.rcnt + p * a.cpr * NP + g;
+    for (int64_t q = 0; q < a.cpr; ++q) {
+      const u32 v = rc[q * NP];
+      tot += v;
+      below += q < c ? v : 0u;
     }
-  };
-  load(0, nx);
-  for (int64_t j0 = 0; j0 < n; j0 += kStageCap) {
+  }
+  u32 all;
+  const u32 start = block_exclusive_sum<kGtThreads>(tot, s_scan, all);
+  if ((u32)tid < NP) {
+    s_off[tid] = start + below;
+    s_c[tid] = 0u;
+    if (c == 0) a.rdir[p * NP + tid] = PartDir{start, tot};
+  }
+  __syncthreads();
+  Pair* prow = a.prow + p * a.k;
+  u32* ppos = a.ppos + p * a.k;
 #pragma unroll
-    for (int u = 0; u < kStagePer; ++u) e[u] = nx[u];
-    if (j0 + kStageCap < n) load(j0 + kStageCap, nx);
-    if (tid == 0) *s_n = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < kStagePer; ++u) {
-      const int64_t j = j0 + (int64_t)u * kGtThreads + tid;
-      const bool own = j < n && gt_hash(e[u].idx, logNP).part == g;
-      const u64 bal = ballot(own);
-      if (!bal) continue;
-      u32 base = 0;
-      if (lane == 0) base = atomicAdd(s_n, (u32)__popcll(bal));
-      base = __builtin_amdgcn_readfirstlane(base);
-      if (own) s_stage[base + lanes_below(bal)] = e[u];
+  for (int u = 0; u < kRowPer; ++u) {
+    const int64_t j = c * kRowChunk + u * kGtThreads + tid;
+    if (j < a.k) {
+      const u32 g = gt_hash(ix[u], a.logNP).part;
+      const u32 pos = s_off[g] + atomicAdd(&s_c[g], 1u);
+      prow[pos] = Pair{ix[u], vb[u]};
+      ppos[pos] = (u32)j;
     }
-    __syncthreads();
-    use(*s_n);
-    __syncthreads();
   }
 }
 
-// -------------------------------------------------------------- k_gt_clear ----
-__global__ void k_gt_clear(v4u* p, int64_t n16) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) p[i] = v4u{0u, 0u, 0u, 0u};
-}
-
-// Merges of round r, and the first output slot of round r (outputs are kept
-// round after round).
+// Merges of round r: slot s = m 2^(r+1) absorbs s + 2^r while that slot exists.
 __host__ __device__ inline int64_t gt_merges(int64_t P, int r) {
   const int64_t half = (int64_t)1 << r;
   return P > half ? (P - half + 2 * half - 1) / (2 * half) : 0;
 }
-__host__ __device__ inline int64_t gt_out_base(int64_t P, int r) {
-  int64_t o = 0;
-  for (int q = 0; q < r; ++q) o += gt_merges(P, q);
-  return o;
-}
 
-// Where slot s's data is before round r: the output of the last round before
-// r it was a destination in, else its row (idx, val).
+// Where slot s's data is before round r: its output region if it was a
+// merge's destination in a round before r, else its grouped row.
 struct SlotData {
-  const Pair* pairs;   // (null: the row)
-  const int32_t* idx;
-  const float* val;
+  const Pair* pairs;
+  const PartDir* dir;
 };
-__device__ SlotData slot_data(int64_t P, int64_t k, int r, int64_t s, const Pair* out, const int32_t* idx,
-                              const float* val) {
+__device__ SlotData slot_data(int64_t P, int64_t k, u32 NP, int r, int64_t s, const Pair* out, const PartDir* odir,
+                              const Pair* prow, const PartDir* rdir) {
   for (int q = r - 1; q >= 0; --q)
     if (s % ((int64_t)2 << q) == 0 && s + ((int64_t)1 << q) < P)
-      return SlotData{out + (gt_out_base(P, q) + (s >> (q + 1))) * k, nullptr, nullptr};
-  return SlotData{nullptr, idx + s * k, val + s * k};
-}
-__device__ __forceinline__ Pair slot_entry(const SlotData& d, int64_t j) {
-  return d.pairs ? d.pairs[j] : Pair{d.idx[j], __float_as_uint(d.val[j])};
+      return SlotData{out + (s >> 1) * 2 * k, odir + (s >> 1) * NP};
+  return SlotData{prow + s * k, rdir + s * NP};
 }
 
 // --------------------------------------------------------------- selection ----
@@ -362,11 +405,12 @@ struct JoinArgs {
   int r;
   int64_t k;
   u32 logNP;
-  const int32_t* idx;  // the rows
-  const float* val;
-  const Pair* out;     // merge outputs of the earlier rounds, round by round
+  const Pair* prow;    // the grouped rows and their directories
+  const PartDir* rdir;
+  const Pair* out;     // the slots' output regions (2k places each) and directories
+  const PartDir* odir;
   Pair* W;             // the round's unions, 2k places per merge
-  u32* wcnt;           // union lengths (32 words apart)
+  PartDir* wdir;       // [merge][NP] each part's place and length in W
   u32* hist;           // histograms, kGtBins per merge
   u32* arrive;         // arrival counters (32 words apart)
   u32* sel;            // [2] per merge: b1, need
@@ -376,71 +420,101 @@ struct JoinArgs {
 __global__ __launch_bounds__(kGtThreads) void k_gt_join(JoinArgs a) {
   __shared__ u32 s_key[kSlots];
   __shared__ u32 s_val[kSlots];
-  __shared__ Pair s_stage[kStageCap];
   __shared__ BinShared s;
-  __shared__ u32 s_base, s_last, s_n;
+  __shared__ PartDir s_da, s_db;
+  __shared__ u32 s_ws, s_n, s_last;
   const int tid = threadIdx.x;
   const u32 NP = 1u << a.logNP;
   const int64_t m = blockIdx.x / NP;
   const u32 g = blockIdx.x % NP;
   const int64_t half = (int64_t)1 << a.r;
   const int64_t sa = m * 2 * half;  // A slot; B is sa + half
-  const SlotData A = slot_data(a.P, a.k, a.r, sa, a.out, a.idx, a.val);
-  const SlotData B = slot_data(a.P, a.k, a.r, sa + half, a.out, a.idx, a.val);
+  const SlotData A = slot_data(a.P, a.k, NP, a.r, sa, a.out, a.odir, a.prow, a.rdir);
+  const SlotData B = slot_data(a.P, a.k, NP, a.r, sa + half, a.out, a.odir, a.prow, a.rdir);
+  // this part's region of W: after those of the parts below it, each as
+  // large as the two sides' entries of its part
+  {
+    u32 cap = 0;
+    PartDir da{0u, 0u}, db{0u, 0u};
+    if ((u32)tid < NP) {
+      da = A.dir[tid];
+      db = B.dir[tid];
+      cap = da.count + db.count;
+    }
+    u32 all;
+    const u32 ws = block_exclusive_sum<kGtThreads>(cap, s.scan, all);
+    if ((u32)tid == g) {
+      s_da = da;
+      s_db = db;
+      s_ws = ws;
+      s_n = 0u;
+    }
+  }
   for (u32 i = tid; i < kSlots; i += kGtThreads) s_key[i] = 0u;
   for (int i = tid; i < kGtBins; i += kGtThreads) s.h[i] = 0u;
   __syncthreads();
+  const PartDir da = s_da, db = s_db;
   // the A entries of this part into the table (a repeated index is the
-  // rows' fault: the final check reports it)
-  stage_part(a.k, a.logNP, g, s_stage, &s_n, [&](int64_t j) { return slot_entry(A, j); }, [&](u32 n) {
-    for (u32 i = tid; i < n; i += kGtThreads) {
-      const Pair e = s_stage[i];
-      if (!lds_insert(s_key, s_val, gt_hash(e.idx, a.logNP).slot, e.idx, e.bits)) atomicOr(a.err, kErrBadInput);
-    }
-  });
-  Pair* W = a.W + m * 2 * a.k;
-  u32* wcnt = a.wcnt + m * 32;
-  // the B entries of this part: found, added to the A entry; else appended
-  stage_part(a.k, a.logNP, g, s_stage, &s_n, [&](int64_t j) { return slot_entry(B, j); }, [&](u32 n) {
-    u32 app = 0, napp = 0;  // bit q: staged entry tid + q 1024 is appended
+  // rows' fault, a full table a part far above its expected load: both are
+  // reported as bad input)
+  for (u32 i0 = 0; i0 < da.count; i0 += (u32)kJoinPer * kGtThreads) {
+    Pair e[kJoinPer];
 #pragma unroll
-    for (int q = 0; q < kStagePer; ++q) {
-      const u32 i = tid + (u32)q * kGtThreads;
-      if (i >= n) continue;
-      const Pair e = s_stage[i];
-      const int h = lds_find(s_key, gt_hash(e.idx, a.logNP).slot, e.idx);
-      if (h >= 0) {
-        s_val[h] = __float_as_uint(__uint_as_float(s_val[h]) + __uint_as_float(e.bits));
-      } else {
-        app |= 1u << q;
-        ++napp;
-        atomicAdd(&s.h[gt_bin(e.bits)], 1u);
+    for (int u = 0; u < kJoinPer; ++u) {
+      const u32 i = i0 + (u32)u * kGtThreads + tid;
+      e[u] = i < da.count ? A.pairs[da.start + i] : pair_sentinel();
+    }
+#pragma unroll
+    for (int u = 0; u < kJoinPer; ++u) {
+      const u32 i = i0 + (u32)u * kGtThreads + tid;
+      if (i < da.count && !lds_insert(s_key, s_val, gt_hash(e[u].idx, a.logNP).slot, e[u].idx, e[u].bits))
+        atomicOr(a.err, kErrBadInput);
+    }
+  }
+  __syncthreads();
+  Pair* W = a.W + m * 2 * a.k + s_ws;
+  // the B entries of this part: found, added to the A entry; else to W
+  for (u32 i0 = 0; i0 < db.count; i0 += (u32)kJoinPer * kGtThreads) {
+    Pair e[kJoinPer];
+#pragma unroll
+    for (int u = 0; u < kJoinPer; ++u) {
+      const u32 i = i0 + (u32)u * kGtThreads + tid;
+      e[u] = i < db.count ? B.pairs[db.start + i] : pair_sentinel();
+    }
+#pragma unroll
+    for (int u = 0; u < kJoinPer; ++u) {
+      const u32 i = i0 + (u32)u * kGtThreads + tid;
+      bool app = false;
+      if (i < db.count) {
+        const int h = lds_find(s_key, gt_hash(e[u].idx, a.logNP).slot, e[u].idx);
+        if (h >= 0) {
+          s_val[h] = __float_as_uint(__uint_as_float(s_val[h]) + __uint_as_float(e[u].bits));
+        } else {
+          app = true;
+          atomicAdd(&s.h[gt_bin(e[u].bits)], 1u);
+        }
       }
+      const u32 pos = wave_take(app, &s_n);
+      if (app) W[pos] = e[u];
     }
-    int64_t pos = wg_append_n(napp, wcnt, s.scan, &s_base);
-#pragma unroll
-    for (int q = 0; q < kStagePer; ++q)
-      if ((app >> q) & 1u) W[pos++] = s_stage[tid + (u32)q * kGtThreads];
-  });
+  }
+  __syncthreads();
   // the A entries of this part (every B entry has been looked up): slots
   // tid + i 1024
   {
     constexpr int kPer = kSlots / kGtThreads;
-    u32 nk = 0;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) nk += s_key[i * kGtThreads + tid] != 0u ? 1u : 0u;
-    int64_t pos = wg_append_n(nk, wcnt, s.scan, &s_base);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const u32 h = i * kGtThreads + tid;
       const u32 kk = s_key[h];
-      if (!kk) continue;
       const Pair e{(int32_t)(kk - 1u), s_val[h]};
-      atomicAdd(&s.h[gt_bin(e.bits)], 1u);
-      W[pos++] = e;
+      if (kk) atomicAdd(&s.h[gt_bin(e.bits)], 1u);
+      const u32 pos = wave_take(kk != 0u, &s_n);
+      if (kk) W[pos] = e;
     }
   }
   __syncthreads();
+  if (tid == 0) a.wdir[m * NP + g] = PartDir{s_ws, s_n};
   flush_hist(s.h, a.hist + m * kGtBins);
   // the last workgroup of the merge to arrive picks the first-level bin: it
   // needs only the histogram, whose adds are complete before each workgroup
@@ -456,101 +530,119 @@ __global__ __launch_bounds__(kGtThreads) void k_gt_join(JoinArgs a) {
 
 // --------------------------------------------------------------- k_gt_keep ----
 struct KeepArgs {
+  int r;
   int64_t k;
+  u32 logNP;
   const Pair* W;       // the round's unions
-  u32* wcnt;           // their lengths (read, then zeroed by the last workgroup)
+  const PartDir* wdir;
   const u32* sel;      // b1, need
-  u32* cnt;            // output append counters (32 words apart)
   u32* ccnt;           // candidate counters (32 words apart)
   u32* karrive;        // arrival counters (32 words apart)
+  u32* kabove;         // [merge][NP] entries above b1 each part keeps
   Pair* cand;          // candidate lists, 2k per merge
-  Pair* out;           // this round's outputs, k per merge
+  Pair* out;           // the slots' output regions, 2k places each
+  PartDir* odir;       // and their directories
   u32* err;
 };
 
-constexpr int kKeepPer = 2;  // union places per thread of k_gt_keep
+constexpr int kKeepPer = 2;  // union places per thread and pass of k_gt_keep
 constexpr int kKeepSpan = kKeepPer * kGtThreads;
 
 __global__ __launch_bounds__(kGtThreads) __attribute__((amdgpu_waves_per_eu(8))) void k_gt_keep(KeepArgs a) {
   __shared__ SelShared s;
-  __shared__ u32 s_w[kGtWaves];
-  __shared__ u32 s_base, s_last;
+  __shared__ u32 s_at[kMaxParts], s_kc[kMaxParts], s_ab[kMaxParts];
+  __shared__ u32 s_base, s_last, s_n, s_placed, s_above;
   const int tid = threadIdx.x;
+  const u32 NP = 1u << a.logNP;
+  const int64_t m = blockIdx.x / NP;
+  const u32 g = blockIdx.x % NP;
   const int64_t len = 2 * a.k;
-  const int64_t cpm = (len + kKeepSpan - 1) / kKeepSpan;
-  const int64_t m = blockIdx.x / cpm;
-  const int64_t c = blockIdx.x % cpm;
-  const int64_t n = a.wcnt[m * 32];  // the union's length
+  const int64_t slot = m << (a.r + 1);
+  Pair* O = a.out + (slot >> 1) * len;
+  const PartDir wd = a.wdir[m * NP + g];
   const u32 b1 = a.sel[2 * m];
   const bool b1ok = b1 != 0xFFFFFFFFu;
-  Pair* out = a.out + m * a.k;
-  u32* cnt = a.cnt + m * 32;
   Pair* clist = a.cand + m * len;
-  auto put = [&](bool keep, const Pair& e) {
-    const int64_t pos = wg_append(keep, cnt, s_w, &s_base);
-    if (keep) {
-      if (pos < a.k) out[pos] = e;
-      else atomicOr(a.err, kErrBadInput);
+  const Pair* W = a.W + m * len + wd.start;
+  if (tid == 0) s_n = 0u;
+  __syncthreads();
+  for (u32 i0 = 0; i0 < wd.count; i0 += (u32)kKeepSpan) {
+    Pair e[kKeepPer];
+#pragma unroll
+    for (int u = 0; u < kKeepPer; ++u) {
+      const u32 q = i0 + (u32)u * kGtThreads + tid;
+      e[u] = q < wd.count ? W[q] : pair_sentinel();
     }
-  };
-  Pair e[kKeepPer];
+    u32 cd = 0, nc0 = 0;  // bit u: e[u] is a candidate
 #pragma unroll
-  for (int u = 0; u < kKeepPer; ++u) {
-    const int64_t q = c * kKeepSpan + u * kGtThreads + tid;
-    e[u] = q < n ? a.W[m * len + q] : pair_sentinel();
-  }
-  u32 kp = 0, cd = 0, nk = 0, nc0 = 0;  // bit u: e[u] is kept / a candidate
-#pragma unroll
-  for (int u = 0; u < kKeepPer; ++u) {
-    const bool live = e[u].idx >= 0;
-    const u32 bin = gt_bin(e[u].bits);
-    if (live && b1ok && bin > b1) {
-      kp |= 1u << u;
-      ++nk;
-    } else if (live && (bin == b1 || !b1ok)) {
-      cd |= 1u << u;
-      ++nc0;
-    }
-  }
-  {
-    int64_t pos = wg_append_n(nk, cnt, s.scan, &s_base);
-#pragma unroll
-    for (int u = 0; u < kKeepPer; ++u)
-      if ((kp >> u) & 1u) {
-        if (pos < a.k) out[pos] = e[u];
-        else atomicOr(a.err, kErrBadInput);
-        ++pos;
+    for (int u = 0; u < kKeepPer; ++u) {
+      const bool live = i0 + (u32)u * kGtThreads + tid < wd.count;
+      const u32 bin = gt_bin(e[u].bits);
+      const bool keep = live && b1ok && bin > b1;
+      if (live && !keep && (bin == b1 || !b1ok)) {
+        cd |= 1u << u;
+        ++nc0;
       }
+      const u32 pos = wave_take(keep, &s_n);
+      if (keep) O[wd.start + pos] = e[u];
+    }
     // candidates: stored at device scope for the selecting workgroup
     int64_t cp = wg_append_n(nc0, a.ccnt + m * 32, s.scan, &s_base);
 #pragma unroll
     for (int u = 0; u < kKeepPer; ++u)
       if ((cd >> u) & 1u) st_agent64((u64*)(clist + cp++), pack_pair(e[u]));
   }
+  __syncthreads();
+  if (tid == 0) st_agent(&a.kabove[m * NP + g], s_n);
   // the last workgroup of the merge to arrive resolves the candidates
   wait_all_memory();
   __syncthreads();
-  if (tid == 0) s_last = add_agent_relaxed(&a.karrive[m * 32], 1u) == (u32)(cpm - 1) ? 1u : 0u;
+  if (tid == 0) s_last = add_agent_relaxed(&a.karrive[m * 32], 1u) == NP - 1u ? 1u : 0u;
   __syncthreads();
   if (!s_last) return;
   const u32 nc = ld_agent(&a.ccnt[m * 32]);
   u32 T = 0u, I = 0x7FFFFFFFu;  // (no b1: every candidate is kept as far as room allows)
   if (b1ok) select_in_bin(s, clist, nc, b1, a.sel[2 * m + 1], T, I);
+  // each part's candidates go after its entries above b1
+  u32 ab = 0;
+  if ((u32)tid < NP) {
+    ab = ld_agent(&a.kabove[m * NP + tid]);
+    s_ab[tid] = ab;
+    s_at[tid] = a.wdir[m * NP + tid].start + ab;
+    s_kc[tid] = 0u;
+  }
+  {
+    u32 all;
+    (void)block_exclusive_sum<kGtThreads>(ab, s.scan, all);
+    if (tid == 0) {
+      s_above = all;
+      s_placed = 0u;
+    }
+  }
+  __syncthreads();
   const bool lds = b1ok && nc <= (u32)kSelList;
+  const int64_t room = a.k - (int64_t)s_above;  // (k entries at most, whatever the input)
   for (u32 i0 = 0; i0 < nc; i0 += kGtThreads) {
     const u32 i = i0 + tid;
     Pair ce = pair_sentinel();
     if (i < nc) ce = lds ? s.list[i] : unpack_pair(ld_agent64((const u64*)(clist + i)));
     const u32 key = key_of_bits(ce.bits);
-    put(i < nc && (key > T || (key == T && (u32)ce.idx <= I)), ce);
+    const bool pass = i < nc && (key > T || (key == T && (u32)ce.idx <= I));
+    const u32 q = wave_take(pass, &s_placed);
+    if (pass && (int64_t)q < room) {
+      const u32 gp = gt_hash(ce.idx, a.logNP).part;
+      O[s_at[gp] + atomicAdd(&s_kc[gp], 1u)] = ce;
+    }
   }
+  __syncthreads();
+  if ((u32)tid < NP)
+    a.odir[(slot >> 1) * NP + tid] = PartDir{s_at[tid] - s_ab[tid], s_ab[tid] + s_kc[tid]};
   if (tid == 0) {
     st_agent(&a.karrive[m * 32], 0u);
     st_agent(&a.ccnt[m * 32], 0u);
-    st_agent(&a.cnt[m * 32], 0u);
-    st_agent(&a.wcnt[m * 32], 0u);
   }
 }
+
 
 // -------------------------------------------------------------- final ----
 // Rank key of a pair: ascending order is (key desc, index asc); the sign
@@ -610,20 +702,16 @@ __device__ void block_sort4096(u64 (&x)[kSortPer], u64* lds) {
   }
 }
 
-// P = 1: the single row, as pairs.
-__global__ void k_gt_pack_row(const int32_t* __restrict__ idx, const float* __restrict__ val, int64_t k,
-                              Pair* __restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < k) out[i] = Pair{idx[i], __float_as_uint(val[i])};
-}
-
 struct FinalArgs {
-  const int32_t* idx;  // the rows
   int32_t P;
   int64_t k, n;
   u32 logNP;
   uint8_t* mask;
-  const Pair* F;       // the final set, k pairs in no order
+  const Pair* F;       // the final set, grouped by part
+  const PartDir* fdir;
+  const Pair* prow;    // the grouped rows, their places in the rows and directories
+  const u32* ppos;
+  const PartDir* rdir;
   int64_t nruns;       // workgroups that sort runs; the others make the mask
   u64* runs;           // sorted runs (more than one run)
   int32_t* out_idx;    // (one run)
@@ -636,20 +724,42 @@ struct FinalArgs {
 // mask) and checks them: in [0, n), and no index twice in the row.
 __global__ __launch_bounds__(kGtThreads) void k_gt_final(FinalArgs a) {
   __shared__ u64 s_lds[kSlots];  // the two tables, or the sort's LDS
-  __shared__ Pair s_stage[kStageCap];
-  __shared__ u32 s_n;
+  __shared__ u32 s_pre[kMaxParts], s_fst[kMaxParts];
+  __shared__ u32 s_scan[kGtWaves + 1];
   static_assert(kSortLds <= (int)kSlots, "the sort fits in the tables' LDS");
   u32* s_key = (u32*)s_lds;      // the final set's part
   u32* s_row = s_key + kSlots;   // the row's part (the repeat check)
   u64* s = s_lds;
   const int tid = threadIdx.x;
+  const u32 NP = 1u << a.logNP;
   if ((int64_t)blockIdx.x < a.nruns) {
+    // entry i of the final set, counted part after part
+    u32 cnt = 0;
+    if ((u32)tid < NP) {
+      const PartDir d = a.fdir[tid];
+      cnt = d.count;
+      s_fst[tid] = d.start;
+    }
+    u32 total;
+    const u32 pre = block_exclusive_sum<kGtThreads>(cnt, s_scan, total);
+    if ((u32)tid < NP) s_pre[tid] = pre;
+    __syncthreads();
+    const int64_t have = std::min<int64_t>(a.k, total);  // (k, unless the rows broke the preconditions)
     const int64_t base = (int64_t)blockIdx.x * kSortTile;
     u64 x[kSortPer];
 #pragma unroll
     for (int c = 0; c < kSortPer; ++c) {
       const int64_t i = base + kSortPer * tid + c;
-      x[c] = i < a.k ? rank64(a.F[i]) : ~0ull;
+      x[c] = ~0ull;
+      if (i < have) {
+        u32 lo = 0, hi = NP;  // the last part whose first entry is at or below i
+        while (hi - lo > 1) {
+          const u32 mid = (lo + hi) >> 1;
+          if ((int64_t)s_pre[mid] <= i) lo = mid;
+          else hi = mid;
+        }
+        x[c] = rank64(a.F[s_fst[lo] + (u32)(i - s_pre[lo])]);
+      }
     }
     block_sort4096(x, s);
     const bool one = a.k <= kSortTile;
@@ -667,34 +777,57 @@ __global__ __launch_bounds__(kGtThreads) void k_gt_final(FinalArgs a) {
     }
     return;
   }
-  const u32 NP = 1u << a.logNP;
   const int64_t b = (int64_t)blockIdx.x - a.nruns;
   const int64_t p = b / NP;
   const u32 g = (u32)(b % NP);
+  const PartDir fd = a.fdir[g];
+  const PartDir rd = a.rdir[p * NP + g];
   for (u32 i = tid; i < kSlots; i += kGtThreads) {
     s_key[i] = 0u;
     s_row[i] = 0u;
   }
   __syncthreads();
-  // the final set's indices of this part
-  stage_part(a.k, a.logNP, g, s_stage, &s_n, [&](int64_t j) { return Pair{a.F[j].idx, 0u}; }, [&](u32 n) {
-    for (u32 i = tid; i < n; i += kGtThreads) {
-      const int32_t x = s_stage[i].idx;
-      (void)lds_insert(s_key, nullptr, gt_hash(x, a.logNP).slot, x, 0u);
+  // the final set's indices of this part (a table that cannot hold them all:
+  // a part far above its expected load, reported as bad input)
+  for (u32 i0 = 0; i0 < fd.count; i0 += (u32)kJoinPer * kGtThreads) {
+    int32_t x[kJoinPer];
+#pragma unroll
+    for (int u = 0; u < kJoinPer; ++u) {
+      const u32 i = i0 + (u32)u * kGtThreads + tid;
+      x[u] = i < fd.count ? a.F[fd.start + i].idx : 0;
     }
-  });
-  // row p's entries of this part (staged with their place in the row)
-  const int32_t* row = a.idx + p * a.k;
+#pragma unroll
+    for (int u = 0; u < kJoinPer; ++u) {
+      const u32 i = i0 + (u32)u * kGtThreads + tid;
+      if (i < fd.count && !lds_insert(s_key, nullptr, gt_hash(x[u], a.logNP).slot, x[u], 0u) &&
+          lds_find(s_key, gt_hash(x[u], a.logNP).slot, x[u]) < 0)
+        atomicOr(a.err, kErrBadInput);
+    }
+  }
+  __syncthreads();
+  // row p's entries of this part, with their places in the row
+  const Pair* prow = a.prow + p * a.k + rd.start;
+  const u32* ppos = a.ppos + p * a.k + rd.start;
   uint8_t* mrow = a.mask + p * a.k;
-  stage_part(a.k, a.logNP, g, s_stage, &s_n, [&](int64_t j) { return Pair{row[j], (u32)j}; }, [&](u32 n) {
-    for (u32 i = tid; i < n; i += kGtThreads) {
-      const Pair e = s_stage[i];
-      const u32 h = gt_hash(e.idx, a.logNP).slot;
-      const bool bad = e.idx < 0 || (int64_t)e.idx >= a.n || !lds_insert(s_row, nullptr, h, e.idx, 0u);
-      if (bad) atomicOr(a.err, kErrBadInput);
-      mrow[e.bits] = (e.idx >= 0 && lds_find(s_key, h, e.idx) >= 0) ? 1 : 0;
+  for (u32 i0 = 0; i0 < rd.count; i0 += (u32)kJoinPer * kGtThreads) {
+    int32_t x[kJoinPer];
+    u32 j[kJoinPer];
+#pragma unroll
+    for (int u = 0; u < kJoinPer; ++u) {
+      const u32 i = i0 + (u32)u * kGtThreads + tid;
+      x[u] = i < rd.count ? prow[i].idx : 0;
+      j[u] = i < rd.count ? ppos[i] : 0u;
     }
-  });
+#pragma unroll
+    for (int u = 0; u < kJoinPer; ++u) {
+      const u32 i = i0 + (u32)u * kGtThreads + tid;
+      if (i >= rd.count) continue;
+      const u32 h = gt_hash(x[u], a.logNP).slot;
+      const bool bad = x[u] < 0 || (int64_t)x[u] >= a.n || !lds_insert(s_row, nullptr, h, x[u], 0u);
+      if (bad) atomicOr(a.err, kErrBadInput);
+      mrow[j[u]] = (x[u] >= 0 && lds_find(s_key, h, x[u]) >= 0) ? 1 : 0;
+    }
+  }
 }
 
 // Number of A entries among the first o outputs of the merge of sorted
@@ -783,10 +916,11 @@ static int gt_rounds(int64_t P) {
 
 struct GtLayout {
   int R;
-  int64_t nmax;  // merges of round 0 (the most of any round), at least 1
+  int64_t nmax;  // merges of round 0 (the most of any round; also the output regions), at least 1
   u32 logNP;     // hash parts: 2^logNP
-  size_t hist, arrive, wcnt, cnt, ccnt, karrive, clear_end;  // zero-filled at the start of a call
-  size_t sel, W, cand, out, runs[2], total;
+  int64_t cpr;   // row chunks of the row kernels
+  size_t hist, arrive, ccnt, karrive, clear_end;  // zero-filled at the start of a call
+  size_t sel, rcnt, rdir, prow, ppos, wdir, kabove, odir, W, cand, out, runs[2], total;
 };
 
 static GtLayout gt_layout(int64_t P, int64_t k) {
@@ -798,26 +932,33 @@ static GtLayout gt_layout(int64_t P, int64_t k) {
   u32 lp = 0;
   while (((int64_t)kPartLoad << lp) < kk) ++lp;
   L.logNP = lp;
+  const size_t NP = (size_t)1 << lp;
+  L.cpr = (kk + kRowChunk - 1) / kRowChunk;
   size_t o = kWorkspaceHeader;  // after the header whose first word is the error word
   L.hist = o;
   o += al(4 * (size_t)kGtBins * (size_t)L.nmax);
-  for (size_t* f : {&L.arrive, &L.wcnt, &L.cnt, &L.ccnt, &L.karrive}) {
+  for (size_t* f : {&L.arrive, &L.ccnt, &L.karrive}) {
     *f = o;
     o += al(128 * (size_t)L.nmax);
   }
   L.clear_end = o;
-  L.sel = o;
-  o += al(8 * (size_t)L.nmax);
-  L.W = o;
-  o += al(sizeof(Pair) * 2 * (size_t)kk * (size_t)L.nmax);
-  L.cand = o;
-  o += al(sizeof(Pair) * 2 * (size_t)kk * (size_t)L.nmax);
-  L.out = o;
-  o += al(sizeof(Pair) * (size_t)kk * (size_t)P);
-  for (int i = 0; i < 2; ++i) {
-    L.runs[i] = o;
-    o += al(8 * (size_t)kk);
-  }
+  auto take = [&](size_t& f, size_t bytes) {
+    f = o;
+    o += al(bytes);
+  };
+  take(L.sel, 8 * (size_t)L.nmax);
+  take(L.rcnt, 4 * (size_t)P * (size_t)L.cpr * NP);
+  take(L.rdir, sizeof(PartDir) * (size_t)P * NP);
+  take(L.prow, sizeof(Pair) * (size_t)P * (size_t)kk);
+  take(L.ppos, 4 * (size_t)P * (size_t)kk);
+  take(L.wdir, sizeof(PartDir) * (size_t)L.nmax * NP);
+  take(L.kabove, 4 * (size_t)L.nmax * NP);
+  take(L.odir, sizeof(PartDir) * (size_t)L.nmax * NP);
+  take(L.W, sizeof(Pair) * 2 * (size_t)kk * (size_t)L.nmax);
+  take(L.cand, sizeof(Pair) * 2 * (size_t)kk * (size_t)L.nmax);
+  take(L.out, sizeof(Pair) * 2 * (size_t)kk * (size_t)L.nmax);
+  take(L.runs[0], 8 * (size_t)kk);
+  take(L.runs[1], 8 * (size_t)kk);
   L.total = o;
   return L;
 }
@@ -858,12 +999,27 @@ extern "C" tgs_status tgs_gtopk_merge(const int32_t* idx, const float* val, int3
   u32* err = (u32*)ws;
   const int R = L.R;
   const int64_t NP = (int64_t)1 << L.logNP;
-  {
-    const int64_t n16 = (int64_t)(L.clear_end - L.hist) / 16;
-    const int blocks = (int)std::min<int64_t>(1024, (n16 + 255) / 256);
-    hipLaunchKernelGGL(k_gt_clear, dim3(blocks), dim3(256), 0, stream, (v4u*)(ws + L.hist), n16);
-  }
+  const Pair* prow = (const Pair*)(ws + L.prow);
+  const PartDir* rdir = (const PartDir*)(ws + L.rdir);
   Pair* outs = (Pair*)(ws + L.out);
+  PartDir* odir = (PartDir*)(ws + L.odir);
+  {
+    RowArgs ra{};
+    ra.idx = idx;
+    ra.val = val;
+    ra.k = k;
+    ra.cpr = L.cpr;
+    ra.logNP = L.logNP;
+    ra.rcnt = (u32*)(ws + L.rcnt);
+    ra.rdir = (PartDir*)(ws + L.rdir);
+    ra.prow = (Pair*)(ws + L.prow);
+    ra.ppos = (u32*)(ws + L.ppos);
+    ra.clear = (v4u*)(ws + L.hist);
+    ra.nclear = (int64_t)(L.clear_end - L.hist) / 16;
+    const unsigned grid = (unsigned)((int64_t)P * L.cpr);
+    hipLaunchKernelGGL(k_gt_rcount, dim3(grid), dim3(kGtThreads), 0, stream, ra);
+    hipLaunchKernelGGL(k_gt_rscatter, dim3(grid), dim3(kGtThreads), 0, stream, ra);
+  }
   for (int r = 0; r < R; ++r) {
     const int64_t nm = gt_merges(P, r);
     JoinArgs ja{};
@@ -871,46 +1027,47 @@ extern "C" tgs_status tgs_gtopk_merge(const int32_t* idx, const float* val, int3
     ja.r = r;
     ja.k = k;
     ja.logNP = L.logNP;
-    ja.idx = idx;
-    ja.val = val;
+    ja.prow = prow;
+    ja.rdir = rdir;
     ja.out = outs;
+    ja.odir = odir;
     ja.W = (Pair*)(ws + L.W);
-    ja.wcnt = (u32*)(ws + L.wcnt);
+    ja.wdir = (PartDir*)(ws + L.wdir);
     ja.hist = (u32*)(ws + L.hist);
     ja.arrive = (u32*)(ws + L.arrive);
     ja.sel = (u32*)(ws + L.sel);
     ja.err = err;
     hipLaunchKernelGGL(k_gt_join, dim3((unsigned)(nm * NP)), dim3(kGtThreads), 0, stream, ja);
     KeepArgs ka{};
+    ka.r = r;
     ka.k = k;
+    ka.logNP = L.logNP;
     ka.W = ja.W;
-    ka.wcnt = ja.wcnt;
+    ka.wdir = ja.wdir;
     ka.sel = ja.sel;
-    ka.cnt = (u32*)(ws + L.cnt);
     ka.ccnt = (u32*)(ws + L.ccnt);
     ka.karrive = (u32*)(ws + L.karrive);
+    ka.kabove = (u32*)(ws + L.kabove);
     ka.cand = (Pair*)(ws + L.cand);
-    ka.out = outs + gt_out_base(P, r) * k;
+    ka.out = outs;
+    ka.odir = odir;
     ka.err = err;
-    const int64_t cpm = (2 * k + kKeepSpan - 1) / kKeepSpan;
-    hipLaunchKernelGGL(k_gt_keep, dim3((unsigned)(cpm * nm)), dim3(kGtThreads), 0, stream, ka);
+    hipLaunchKernelGGL(k_gt_keep, dim3((unsigned)(nm * NP)), dim3(kGtThreads), 0, stream, ka);
   }
   {
     const int64_t nruns = (k + kSortTile - 1) / kSortTile;
     FinalArgs fa{};
-    fa.idx = idx;
     fa.P = P;
     fa.k = k;
     fa.n = n;
     fa.logNP = L.logNP;
     fa.mask = out_mask;
-    // the final set: the last round's output, or the single row (P = 1)
-    fa.F = R > 0 ? outs + gt_out_base(P, R - 1) * k : nullptr;
-    if (R == 0) {
-      // (P = 1) the row is the final set: copy it into the output area
-      hipLaunchKernelGGL(k_gt_pack_row, dim3((unsigned)((k + 255) / 256)), dim3(256), 0, stream, idx, val, k, outs);
-      fa.F = outs;
-    }
+    // the final set: slot 0's output region, or (P = 1) its grouped row
+    fa.F = R > 0 ? outs : prow;
+    fa.fdir = R > 0 ? odir : rdir;
+    fa.prow = prow;
+    fa.ppos = (const u32*)(ws + L.ppos);
+    fa.rdir = rdir;
     fa.nruns = nruns;
     fa.runs = (u64*)(ws + L.runs[0]);
     fa.out_idx = out_idx;

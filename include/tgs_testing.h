@@ -39,7 +39,12 @@ extern "C" {
  *                       acc again),
  *                       9 = guided general path (the accumulate pass copies
  *                       out the candidates of a sampled first-level bin)
- *                       where the fast path would otherwise run.
+ *                       where the fast path would otherwise run,
+ *                       10 = layer-wise calls: every segment of the batched
+ *                       path selects exactly from acc (as when its sampled
+ *                       guess does not hold),
+ *                       11 = layer-wise calls without the batched path (the
+ *                       small-segment kernel and one step per segment).
  *                       The guided path needs n >= 2^18, grad and residual
  *                       equally aligned modulo 16 bytes and k > 0; otherwise
  *                       7-9 run the plain general path.

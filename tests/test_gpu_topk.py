@@ -546,6 +546,41 @@ def test_segmented_many_small_segments(tgs_gpu):
         assert_topk_equal((host(idx), host(val), host(r_gpu)), (ei, ev, r_cpu), "step %d" % step)
 
 
+def _mid_exact(ws):
+    """Segments of the batched layer-wise path that selected exactly from acc."""
+    return int(host(ws[36:40].view(torch.int32))[0])
+
+
+@pytest.mark.parametrize("path", [0, 10, 11])
+def test_segmented_batched_routes(tgs_gpu, path):
+    """Segments of at most 2^23 entries with k <= 4096 take the batched path
+    (a sampled guess per segment, one streaming pass over all of them, one
+    selecting workgroup per segment).  By default the guesses hold on the
+    mixture, and only the dense segment (k = 4096 of 16,385) and the all-zero
+    one (every key ties) select exactly from acc; path 10 forces every
+    segment to, path 11 turns the batched path off.  Sizes cover a whole
+    segment read into LDS (<= 8192 entries), the sampled guess, k = 0, k
+    above the batched limit and odd offsets; every segment's pairs and
+    residual as the oracle's step on that slice."""
+    tgs_gpu.set_option(tgs_gpu.OPT_TOPK_PATH, path)
+    rng = np.random.default_rng(71)
+    sizes = [16_384, 16_385, 20_000, 3, 100_000, 50_000, 583_306, 9_000, 1_112_885, 300_000, 2_701_282, 4_200_001]
+    ks = [16, 4096, 1, 2, 100, 10, 583, 0, 1112, 5000, 2701, 2000]
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    grad, res = make("mixture", int(offsets[-1]), rng)
+    z0, z1 = int(offsets[5]), int(offsets[6])
+    grad[z0:z1] = 0.0
+    res[z0:z1] = 0.0
+    g, r = gpu(grad), gpu(res)
+    ws = torch.zeros(tgs_gpu.topk_segmented_workspace_bytes(offsets, ks), dtype=torch.uint8, device="cuda")
+    idx, val = tgs_gpu.topk_ef_step_segmented(g, r, offsets, ks, ws=ws)
+    tgs_gpu.check_device_error(ws)
+    got = (host(idx), host(val), host(r))
+    assert_topk_equal(got, _oracle_segments(grad, res, offsets, ks), "path %d" % path)
+    batched = sum(1 for n_, k_ in zip(sizes, ks) if n_ <= 1 << 23 and 0 < k_ <= 4096)
+    assert _mid_exact(ws) == {0: 2, 10: batched, 11: 0}[path]
+
+
 @pytest.mark.parametrize("n,k", [(300_001, 300), (583_306, 583), (600_000, 60_000), (1_000_003, 100_000)])
 def test_guided_mid_sizes(tgs_gpu, n, k):
     """Vectors between 2^18 and a few million entries, where the one-launch

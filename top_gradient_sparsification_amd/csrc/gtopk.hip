@@ -54,8 +54,6 @@ constexpr int kGtThreads = 1024;
 constexpr int kGtWaves = kGtThreads / kWave;
 constexpr int kGtBins = 2048;      // first-level bins: key >> 20
 constexpr int kSelList = 8192;     // candidates the select holds in LDS
-constexpr int kSortTile = 4096;    // entries one workgroup sorts or merges
-constexpr int kSortPer = kSortTile / kGtThreads;
 constexpr int kGtBatch = 16;       // loads in flight per thread in the scans
 constexpr u32 kLogSlots = 13;      // places of one part's LDS table
 constexpr u32 kSlots = 1u << kLogSlots;
@@ -205,15 +203,35 @@ __global__ __launch_bounds__(kGtThreads) void k_gt_rscatter(RowArgs a) {
     ix[u] = j < a.k ? row[j] : 0;
     vb[u] = j < a.k ? __float_as_uint(vrow[j]) : 0u;
   }
-  u32 tot = 0, below = 0;
-  for (u32 g = tid; g < NP; g += kGtThreads) {  // (NP <= kGtThreads: one part per thread)
-    const u32* rc = a.rcnt + p * a.cpr * NP + g;
-    for (int64_t q = 0; q < a.cpr; ++q) {
-      const u32 v = rc[q * NP];
-      tot += v;
-      below += q < c ? v : 0u;
+  // the row's counts, every (chunk, part) word loaded by its own thread:
+  // per part the row's total and the earlier chunks' sum
+  for (u32 g = tid; g < NP; g += kGtThreads) {
+    s_c[g] = 0u;
+    s_off[g] = 0u;
+  }
+  __syncthreads();
+  {
+    const u32* rc = a.rcnt + p * a.cpr * NP;
+    const int64_t nw = a.cpr * NP;
+    for (int64_t i0 = 0; i0 < nw; i0 += (int64_t)kGtBatch * kGtThreads) {
+      u32 v[kGtBatch];
+#pragma unroll
+      for (int u = 0; u < kGtBatch; ++u) {
+        const int64_t i = i0 + (int64_t)u * kGtThreads + tid;
+        v[u] = i < nw ? rc[i] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < kGtBatch; ++u) {
+        const int64_t i = i0 + (int64_t)u * kGtThreads + tid;
+        if (v[u]) {
+          atomicAdd(&s_c[i % NP], v[u]);
+          if (i / NP < c) atomicAdd(&s_off[i % NP], v[u]);
+        }
+      }
     }
   }
+  __syncthreads();
+  const u32 tot = (u32)tid < NP ? s_c[tid] : 0u, below = (u32)tid < NP ? s_off[tid] : 0u;
   u32 all;
   const u32 start = block_exclusive_sum<kGtThreads>(tot, s_scan, all);
   if ((u32)tid < NP) {
@@ -454,6 +472,14 @@ __global__ __launch_bounds__(kGtThreads) void k_gt_join(JoinArgs a) {
   for (int i = tid; i < kGtBins; i += kGtThreads) s.h[i] = 0u;
   __syncthreads();
   const PartDir da = s_da, db = s_db;
+  // the first batch of B entries is loaded with the A entries, so that its
+  // loads are in flight while the table is built
+  Pair eb[kJoinPer];
+#pragma unroll
+  for (int u = 0; u < kJoinPer; ++u) {
+    const u32 i = (u32)u * kGtThreads + tid;
+    eb[u] = i < db.count ? B.pairs[db.start + i] : pair_sentinel();
+  }
   // the A entries of this part into the table (a repeated index is the
   // rows' fault, a full table a part far above its expected load: both are
   // reported as bad input)
@@ -479,7 +505,7 @@ __global__ __launch_bounds__(kGtThreads) void k_gt_join(JoinArgs a) {
 #pragma unroll
     for (int u = 0; u < kJoinPer; ++u) {
       const u32 i = i0 + (u32)u * kGtThreads + tid;
-      e[u] = i < db.count ? B.pairs[db.start + i] : pair_sentinel();
+      e[u] = i0 == 0 ? eb[u] : i < db.count ? B.pairs[db.start + i] : pair_sentinel();
     }
 #pragma unroll
     for (int u = 0; u < kJoinPer; ++u) {
@@ -645,63 +671,6 @@ __global__ __launch_bounds__(kGtThreads) __attribute__((amdgpu_waves_per_eu(8)))
 
 
 // -------------------------------------------------------------- final ----
-// Rank key of a pair: ascending order is (key desc, index asc); the sign
-// rides in bit 0 (never decides: (key, index) is unique).
-__device__ __forceinline__ u64 rank64(const Pair& e) {
-  const u32 key = key_of_bits(e.bits);
-  return ((u64)(0x7FFFFFFFu - key) << 32) | ((u64)((u32)e.idx & 0x7FFFFFFFu) << 1) | (u64)(e.bits >> 31);
-}
-__device__ __forceinline__ Pair unrank64(u64 r) {
-  const u32 key = 0x7FFFFFFFu - (u32)(r >> 32);
-  return Pair{(int32_t)(((u32)r >> 1) & 0x7FFFFFFFu), key | (((u32)r & 1u) << 31)};
-}
-
-__device__ __forceinline__ u64 shfl_xor64(u64 v, int m) {
-  const int lo = __shfl_xor((int)(u32)v, m), hi = __shfl_xor((int)(u32)(v >> 32), m);
-  return ((u64)(u32)hi << 32) | (u64)(u32)lo;
-}
-
-// LDS place of sort element e: one pad word after every 4, so that the 64
-// lanes of a wave, 4 elements apart, fall on different banks.
-__device__ __forceinline__ u32 sort_slot(u32 e) { return e + (e >> 2); }
-constexpr int kSortLds = kSortTile + kSortTile / 4;
-
-// Bitonic sort of 4096 keys, ascending; thread t holds elements 4t .. 4t + 3
-// in x.  Partners at distance 1 and 2 are in the same thread, 4 .. 128 in
-// the same wave (lane shuffles), 256 and above in other waves (LDS).
-__device__ void block_sort4096(u64 (&x)[kSortPer], u64* lds) {
-  const int tid = threadIdx.x;
-  // fully unrolled: every stage's distance is a constant, so the partners
-  // inside a thread are plain registers and the lane masks immediates
-#pragma unroll
-  for (u32 size = 2; size <= (u32)kSortTile; size <<= 1) {
-#pragma unroll
-    for (u32 d = size >> 1; d > 0; d >>= 1) {
-      u64 y[kSortPer];
-      if (d >= 4u * kWave) {
-#pragma unroll
-        for (int c = 0; c < kSortPer; ++c) lds[sort_slot(kSortPer * tid + c)] = x[c];
-        __syncthreads();
-#pragma unroll
-        for (int c = 0; c < kSortPer; ++c) y[c] = lds[sort_slot((kSortPer * tid + c) ^ d)];
-        __syncthreads();
-      } else if (d >= (u32)kSortPer) {
-#pragma unroll
-        for (int c = 0; c < kSortPer; ++c) y[c] = shfl_xor64(x[c], (int)(d / kSortPer));
-      } else {
-#pragma unroll
-        for (int c = 0; c < kSortPer; ++c) y[c] = x[c ^ d];
-      }
-#pragma unroll
-      for (int c = 0; c < kSortPer; ++c) {
-        const u32 e = (u32)(kSortPer * tid + c);
-        const bool asc = (e & size) == 0, lower = (e & d) == 0;
-        x[c] = (asc == lower) ? (x[c] < y[c] ? x[c] : y[c]) : (x[c] < y[c] ? y[c] : x[c]);
-      }
-    }
-  }
-}
-
 struct FinalArgs {
   int32_t P;
   int64_t k, n;

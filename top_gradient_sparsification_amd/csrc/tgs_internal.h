@@ -10,6 +10,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "tgs.h"
 
 namespace tgs {
@@ -278,6 +280,183 @@ __device__ __forceinline__ bool grid_sync(const GridBar& gb) {
   if (threadIdx.x < kWave) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   __syncthreads();
   return s_ok != 0;
+}
+
+// Rank inside the wave of this lane's first qualifying component (bit c of
+// qm: component c qualifies), lanes in order and components in order inside
+// a lane; `tot` gets the wave's count.  Every lane of the wave calls it.
+__device__ __forceinline__ u32 wave_rank4(u32 qm, u32& tot) {
+  u32 below = 0;
+  tot = 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const u64 m = ballot((qm >> c) & 1u);
+    below += lanes_below(m);
+    tot += (u32)__popcll(m);
+  }
+  return below;
+}
+
+// ------------------------------------------------ LDS select / sort ----
+// Radix select in LDS of the need-th largest key among `len` entries, whose
+// key is key_at(i) (i < len, 8 per thread at i = tid + j NT).  Returns the
+// selection rule: every key >= t_lo, plus the first r keys equal to t_eq.
+template <int NT, class KeyAt>
+__device__ __forceinline__ void lds_select(KeyAt key_at, u32 len, u32 need, u32* s_hist, u32* s_scan, u32* s_found,
+                                           u32& t_lo, u32& t_eq, u32& r) {
+  const int tid = threadIdx.x;
+  const int shifts[3] = {20, 9, 0};
+  const int widths[3] = {11, 11, 9};
+  u32 prefix = 0;
+  t_lo = 0;
+  t_eq = 0;
+  r = 0;
+  for (int L = 0; L < 3; ++L) {
+    const int sh = shifts[L], wd = widths[L];
+    const int nbins = 1 << wd;
+    for (int i = tid; i < 2048; i += NT) s_hist[i] = 0;
+    __syncthreads();
+    for (u32 i = tid; i < len; i += NT) {
+      const u32 key = key_at(i);
+      if ((key >> (sh + wd)) == prefix) atomicAdd(&s_hist[(key >> sh) & (u32)(nbins - 1)], 1u);
+    }
+    __syncthreads();
+    // thread t owns bins [nbins - cpt (t+1), nbins - cpt t), from the top
+    const int cpt = nbins / NT > 0 ? nbins / NT : 1;
+    const int top = nbins - cpt * tid;
+    u32 own = 0;
+    if (top > 0)
+      for (int d = top - 1; d >= std::max(0, top - cpt); --d) own += s_hist[d];
+    u32 tot;
+    const u32 above = block_exclusive_sum<NT>(own, s_scan, tot);
+    if (top > 0 && above < need && above + own >= need) {
+      u32 run = above;
+      for (int d = top - 1; d >= std::max(0, top - cpt); --d) {
+        const u32 h = s_hist[d];
+        if (run + h >= need) {
+          s_found[0] = (u32)d;
+          s_found[1] = run;
+          s_found[2] = h;
+          break;
+        }
+        run += h;
+      }
+    }
+    __syncthreads();
+    const u32 d = s_found[0];
+    need -= s_found[1];
+    const u32 h = s_found[2];
+    prefix = (prefix << wd) | d;
+    __syncthreads();  // s_found is rewritten by the next level
+    if (need == h) {  // the whole digit range is taken
+      t_lo = prefix << sh;
+      return;
+    }
+    if (L == 2) {
+      t_lo = prefix + 1;
+      t_eq = prefix;
+      r = need;
+    }
+  }
+}
+
+// Ordered compaction: entries i < len (pair_at(i), key of its bits) in index
+// order i = j NT + tid; the selected ones (key >= t_lo, or among the first r
+// equal to t_eq) go to place(pos, pair) with pos their rank among them.
+template <int NT, int ROWS, class PairAt, class Place>
+__device__ __forceinline__ void lds_compact(PairAt pair_at, u32 len, u32 t_lo, u32 t_eq, u32 r, u32 (*s_wc)[NT / kWave][2],
+                                            Place place) {
+  constexpr int NW = NT / kWave;
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  u32 gt_seen = 0, eq_seen = 0;
+  for (int j = 0; j < ROWS; ++j) {
+    const u32 i = (u32)(j * NT + tid);
+    const bool in = i < len;
+    const u64 pv = in ? pair_at(i) : 0ull;
+    const u32 key = key_of_bits((u32)(pv >> 32));
+    const bool g = in && key >= t_lo, e = in && r > 0 && key == t_eq;
+    const u64 bg = ballot(g), be = ballot(e);
+    const int par = j & 1;
+    if (lane == 0) {
+      s_wc[par][w][0] = (u32)__popcll(bg);
+      s_wc[par][w][1] = (u32)__popcll(be);
+    }
+    __syncthreads();
+    u32 og = 0, oe = 0, tg = 0, te = 0;
+#pragma unroll
+    for (int q = 0; q < NW; ++q) {
+      const u32 cg = s_wc[par][q][0], ce = s_wc[par][q][1];
+      og += q < w ? cg : 0u;
+      oe += q < w ? ce : 0u;
+      tg += cg;
+      te += ce;
+    }
+    const u32 gb = gt_seen + og + lanes_below(bg), eb = eq_seen + oe + lanes_below(be);
+    if (g || (e && eb < r)) place(gb + std::min(eb, r), pv);
+    gt_seen += tg;
+    eq_seen += te;
+  }
+}
+
+// Bitonic sort of kSortTile 64-bit keys by one workgroup of kSortThreads.
+constexpr int kSortTile = 4096;
+constexpr int kSortThreads = 1024;
+constexpr int kSortPer = kSortTile / kSortThreads;
+// Rank key of a pair: ascending order is (key desc, index asc); the sign
+// rides in bit 0 (never decides: (key, index) is unique).
+__device__ __forceinline__ u64 rank64(const Pair& e) {
+  const u32 key = key_of_bits(e.bits);
+  return ((u64)(0x7FFFFFFFu - key) << 32) | ((u64)((u32)e.idx & 0x7FFFFFFFu) << 1) | (u64)(e.bits >> 31);
+}
+__device__ __forceinline__ Pair unrank64(u64 r) {
+  const u32 key = 0x7FFFFFFFu - (u32)(r >> 32);
+  return Pair{(int32_t)(((u32)r >> 1) & 0x7FFFFFFFu), key | (((u32)r & 1u) << 31)};
+}
+
+__device__ __forceinline__ u64 shfl_xor64(u64 v, int m) {
+  const int lo = __shfl_xor((int)(u32)v, m), hi = __shfl_xor((int)(u32)(v >> 32), m);
+  return ((u64)(u32)hi << 32) | (u64)(u32)lo;
+}
+
+// LDS place of sort element e: one pad word after every 4, so that the 64
+// lanes of a wave, 4 elements apart, fall on different banks.
+__device__ __forceinline__ u32 sort_slot(u32 e) { return e + (e >> 2); }
+constexpr int kSortLds = kSortTile + kSortTile / 4;
+
+// Bitonic sort of 4096 keys, ascending; thread t holds elements 4t .. 4t + 3
+// in x.  Partners at distance 1 and 2 are in the same thread, 4 .. 128 in
+// the same wave (lane shuffles), 256 and above in other waves (LDS).
+__device__ inline void block_sort4096(u64 (&x)[kSortPer], u64* lds) {
+  const int tid = threadIdx.x;
+  // fully unrolled: every stage's distance is a constant, so the partners
+  // inside a thread are plain registers and the lane masks immediates
+#pragma unroll
+  for (u32 size = 2; size <= (u32)kSortTile; size <<= 1) {
+#pragma unroll
+    for (u32 d = size >> 1; d > 0; d >>= 1) {
+      u64 y[kSortPer];
+      if (d >= 4u * kWave) {
+#pragma unroll
+        for (int c = 0; c < kSortPer; ++c) lds[sort_slot(kSortPer * tid + c)] = x[c];
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < kSortPer; ++c) y[c] = lds[sort_slot((kSortPer * tid + c) ^ d)];
+        __syncthreads();
+      } else if (d >= (u32)kSortPer) {
+#pragma unroll
+        for (int c = 0; c < kSortPer; ++c) y[c] = shfl_xor64(x[c], (int)(d / kSortPer));
+      } else {
+#pragma unroll
+        for (int c = 0; c < kSortPer; ++c) y[c] = x[c ^ d];
+      }
+#pragma unroll
+      for (int c = 0; c < kSortPer; ++c) {
+        const u32 e = (u32)(kSortPer * tid + c);
+        const bool asc = (e & size) == 0, lower = (e & d) == 0;
+        x[c] = (asc == lower) ? (x[c] < y[c] ? x[c] : y[c]) : (x[c] < y[c] ? y[c] : x[c]);
+      }
+    }
+  }
 }
 
 }  // namespace tgs

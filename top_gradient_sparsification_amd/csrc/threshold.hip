@@ -98,21 +98,6 @@ __device__ __forceinline__ void store_slot(float* p, const ThrArgs& a, int64_t i
   }
 }
 
-// Rank inside the wave of this lane's first qualifying component (bit c of
-// qm: component c qualifies), lanes in order and components in order inside
-// a lane; `tot` gets the wave's count.  Every lane of the wave calls it.
-__device__ __forceinline__ u32 wave_rank4(u32 qm, u32& tot) {
-  u32 below = 0;
-  tot = 0;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const u64 m = ballot((qm >> c) & 1u);
-    below += lanes_below(m);
-    tot += (u32)__popcll(m);
-  }
-  return below;
-}
-
 // One wave's part of block b, in index order: the head (wave 0 of block 0),
 // the wave's 64 slots (this lane's: `slot`, present when `in`), the tail (the
 // last wave of the last block).

@@ -65,9 +65,11 @@
 #include <cstddef>
 #include <cstring>
 #include <type_traits>
+#include <vector>
 
 #include "tgs_host.h"
 #include "tgs_internal.h"
+#include "tgs_midseg.h"
 
 namespace tgs {
 
@@ -166,10 +168,11 @@ struct StepCtl {
   u32 guided_used;    // guided general-path calls that selected from the copied candidates (never reset)
   u32 guided_missed;  // guided calls whose guess or regions did not hold: acc read again (never reset)
   u32 parity;         // counter set the next k_step launch uses (flipped by each launch)
-  u32 pad1[55];
+  u32 mid_exact;      // batched layer-wise segments selected exactly from acc (never reset)
+  u32 pad1[54];
   StepSet set[2];
   Plan plan;
-  u32 seg_done[64];  // k_small arrivals per segment of a launch; each segment's last workgroup leaves it zero
+  u32 seg_done[64];  // arrivals per segment of a k_small or k_mid_guess launch; each segment's last workgroup leaves it zero
   // guided accumulate pass (standalone general path): k_guess adds its sample
   // histogram into the header histogram; its last workgroup picks guide_bin
   // and leaves the histogram, its counter and guide_ovf zero
@@ -178,6 +181,7 @@ struct StepCtl {
   u32 acc_ticket;  // row pairs handed out by the accumulate pass (k_guess sets it to zero)
 };
 static_assert(sizeof(StepCtl) <= kEstStateOffset, "control block overlaps the header's shared state");
+static_assert(offsetof(StepCtl, mid_exact) == 36, "the tests read the route counters at fixed offsets");
 static_assert(kMaxAccBlocks <= kMaxGenWG, "guided regions are the general path's");
 
 // State of the general path (zero when it starts).
@@ -1072,7 +1076,7 @@ struct AccArgs {
   const float* grad;
   float* residual;
   int64_t n;
-  int64_t head;  // scalar elements before the 16-byte aligned part
+  int64_t head;  // scalar elements before the aligned part (< 64)
   int64_t nv;    // float4 vectors in the aligned part
   u32* zero_ptr;
   int zero_words;
@@ -1235,7 +1239,7 @@ struct GuidedArgs {
   const float* grad;
   float* residual;
   int64_t n;
-  int64_t head;  // scalar entries before the 16-byte aligned part
+  int64_t head;  // scalar entries before the aligned part (< 64)
   int64_t nv;    // float4 vectors in the aligned part
   u32* zero_ptr;
   int zero_words;
@@ -1402,106 +1406,6 @@ struct SmallArgs {
   int nseg;
   SmallSeg seg[kSmallMaxSeg];
 };
-
-// Radix select in LDS of the need-th largest key among `len` entries, whose
-// key is key_at(i) (i < len, 8 per thread at i = tid + j NT).  Returns the
-// selection rule: every key >= t_lo, plus the first r keys equal to t_eq.
-template <int NT, class KeyAt>
-__device__ __forceinline__ void lds_select(KeyAt key_at, u32 len, u32 need, u32* s_hist, u32* s_scan, u32* s_found,
-                                           u32& t_lo, u32& t_eq, u32& r) {
-  const int tid = threadIdx.x;
-  const int shifts[3] = {20, 9, 0};
-  const int widths[3] = {11, 11, 9};
-  u32 prefix = 0;
-  t_lo = 0;
-  t_eq = 0;
-  r = 0;
-  for (int L = 0; L < 3; ++L) {
-    const int sh = shifts[L], wd = widths[L];
-    const int nbins = 1 << wd;
-    for (int i = tid; i < 2048; i += NT) s_hist[i] = 0;
-    __syncthreads();
-    for (u32 i = tid; i < len; i += NT) {
-      const u32 key = key_at(i);
-      if ((key >> (sh + wd)) == prefix) atomicAdd(&s_hist[(key >> sh) & (u32)(nbins - 1)], 1u);
-    }
-    __syncthreads();
-    // thread t owns bins [nbins - cpt (t+1), nbins - cpt t), from the top
-    const int cpt = nbins / NT > 0 ? nbins / NT : 1;
-    const int top = nbins - cpt * tid;
-    u32 own = 0;
-    if (top > 0)
-      for (int d = top - 1; d >= std::max(0, top - cpt); --d) own += s_hist[d];
-    u32 tot;
-    const u32 above = block_exclusive_sum<NT>(own, s_scan, tot);
-    if (top > 0 && above < need && above + own >= need) {
-      u32 run = above;
-      for (int d = top - 1; d >= std::max(0, top - cpt); --d) {
-        const u32 h = s_hist[d];
-        if (run + h >= need) {
-          s_found[0] = (u32)d;
-          s_found[1] = run;
-          s_found[2] = h;
-          break;
-        }
-        run += h;
-      }
-    }
-    __syncthreads();
-    const u32 d = s_found[0];
-    need -= s_found[1];
-    const u32 h = s_found[2];
-    prefix = (prefix << wd) | d;
-    __syncthreads();  // s_found is rewritten by the next level
-    if (need == h) {  // the whole digit range is taken
-      t_lo = prefix << sh;
-      return;
-    }
-    if (L == 2) {
-      t_lo = prefix + 1;
-      t_eq = prefix;
-      r = need;
-    }
-  }
-}
-
-// Ordered compaction: entries i < len (pair_at(i), key of its bits) in index
-// order i = j NT + tid; the selected ones (key >= t_lo, or among the first r
-// equal to t_eq) go to place(pos, pair) with pos their rank among them.
-template <int NT, int ROWS, class PairAt, class Place>
-__device__ __forceinline__ void lds_compact(PairAt pair_at, u32 len, u32 t_lo, u32 t_eq, u32 r, u32 (*s_wc)[NT / kWave][2],
-                                            Place place) {
-  constexpr int NW = NT / kWave;
-  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
-  u32 gt_seen = 0, eq_seen = 0;
-  for (int j = 0; j < ROWS; ++j) {
-    const u32 i = (u32)(j * NT + tid);
-    const bool in = i < len;
-    const u64 pv = in ? pair_at(i) : 0ull;
-    const u32 key = key_of_bits((u32)(pv >> 32));
-    const bool g = in && key >= t_lo, e = in && r > 0 && key == t_eq;
-    const u64 bg = ballot(g), be = ballot(e);
-    const int par = j & 1;
-    if (lane == 0) {
-      s_wc[par][w][0] = (u32)__popcll(bg);
-      s_wc[par][w][1] = (u32)__popcll(be);
-    }
-    __syncthreads();
-    u32 og = 0, oe = 0, tg = 0, te = 0;
-#pragma unroll
-    for (int q = 0; q < NW; ++q) {
-      const u32 cg = s_wc[par][q][0], ce = s_wc[par][q][1];
-      og += q < w ? cg : 0u;
-      oe += q < w ? ce : 0u;
-      tg += cg;
-      te += ce;
-    }
-    const u32 gb = gt_seen + og + lanes_below(bg), eb = eq_seen + oe + lanes_below(be);
-    if (g || (e && eb < r)) place(gb + std::min(eb, r), pv);
-    gt_seen += tg;
-    eq_seen += te;
-  }
-}
 
 __global__ __launch_bounds__(kSmallThreads) void k_small(SmallArgs a) {
   constexpr int NT = kSmallThreads, NW = NT / kWave, EPT = kSmallPer / NT;
@@ -2665,9 +2569,14 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
   const int path = (int)get_option(TGS_OPT_TOPK_PATH);
   const int64_t gopt = get_option(TGS_OPT_MAIN_GRID);
   const bool vec = (((uintptr_t)grad) & 15u) == (((uintptr_t)residual) & 15u);
+  // vector mode: up to 63 scalar entries first, so that the float4 part of
+  // residual starts on a 256-byte boundary and every wave's store of 64
+  // float4 covers whole cache lines (a vector cut at any offset, such as a
+  // layer of a layer-wise call, would otherwise store partial lines, which
+  // device-scope stores pay for dearly)
   int64_t head = 0, nv = 0;
   if (vec) {
-    head = std::min<int64_t>(n, (int64_t)(((16u - (((uintptr_t)residual) & 15u)) & 15u) / 4u));
+    head = std::min<int64_t>(n, (int64_t)(((256u - (((uintptr_t)residual) & 255u)) & 255u) / 4u));
     nv = (n - head) / 4;
   }
 
@@ -2868,26 +2777,37 @@ bool segments_valid(int32_t nseg, const int64_t* offsets, const int64_t* ks, con
   return true;
 }
 
-// Workspace: a top-k workspace for the largest non-small segment (its header
-// also serves the small-segment launches), then the candidate lists of the
-// small segments' workgroups.
+// A segment for the batched layer-wise path (grad and residual equally
+// aligned modulo 16 bytes, at most 2^23 entries, k <= 4096).
+bool mid_segment(int64_t len, int64_t k) {
+  u32 a = 0, b = 0, c = 0;
+  return len > 0 && mid_plan(len, k, &a, &b, &c);
+}
+
+// Workspace: a top-k workspace for the largest segment that may take a step
+// of its own (its header also serves the other launches), then the candidate
+// lists of the small segments' workgroups, then the batched path's region
+// (sized for every batched segment; whether it is used depends on the
+// pointers' alignment, so both are provided).
 struct SegLayout {
-  size_t big, lists, total;
+  size_t big, lists, mid, total;
 };
 
 SegLayout seg_layout(int32_t nseg, const int64_t* offsets, const int64_t* ks) {
   SegLayout L{};
   L.big = kWorkspaceHeader;
-  int64_t wgs = 0;
+  int64_t wgs = 0, blocks = 0;
   for (int32_t s = 0; s < nseg; ++s) {
     const int64_t len = offsets[s + 1] - offsets[s];
     if (len == 0) continue;
+    if (mid_segment(len, ks[s])) blocks += len / 1024 + 2;
     if (small_segment(len, ks[s])) wgs += (len + kSmallPer - 1) / kSmallPer;
     else L.big = std::max(L.big, topk_layout(len, ks[s]).total);
   }
   L.big = align256(L.big);
   L.lists = L.big;
-  L.total = L.lists + sizeof(u64) * (size_t)wgs * kSmallMaxK;
+  L.mid = align256(L.lists + sizeof(u64) * (size_t)wgs * kSmallMaxK);
+  L.total = L.mid + (blocks ? mid_workspace_bytes(blocks) : 0);
   return L;
 }
 
@@ -2924,6 +2844,28 @@ extern "C" tgs_status tgs_topk_ef_step_segmented(const float* grad, float* resid
     return fail(TGS_EWORKSPACE, "topk_ef_step_segmented: workspace %zu bytes, need %zu", workspace_bytes, L.total);
   char* ws = (char*)workspace;
   StepCtl* ctl = (StepCtl*)ws;
+  // grad and residual equally aligned: the segments of at most 2^23 entries
+  // with k <= 4096 take the batched path; the others (and every segment
+  // otherwise) as below
+  const bool vec = (((uintptr_t)grad) & 15u) == (((uintptr_t)residual) & 15u);
+  auto batched = [&](int32_t s) {
+    const int64_t len = offsets[s + 1] - offsets[s];
+    return vec && get_option(TGS_OPT_TOPK_PATH) != 11 && mid_segment(len, ks[s]);
+  };
+  {
+    std::vector<MidSegSpec> mids;
+    int64_t ko = 0;
+    for (int32_t s = 0; s < nseg; ++s) {
+      if (batched(s)) mids.push_back(MidSegSpec{offsets[s], offsets[s + 1] - offsets[s], ks[s], ko});
+      ko += ks[s];
+    }
+    if (!mids.empty()) {
+      const tgs_status st =
+          mid_launch(grad, residual, out_idx, out_val, (int)mids.size(), mids.data(), &ctl->mid_exact, ctl->seg_done,
+                     ws + L.mid, stream);
+      if (st != TGS_OK) return st;
+    }
+  }
   // the small segments, up to kSmallMaxSeg per launch
   SmallArgs m{};
   m.grad = grad;
@@ -2944,7 +2886,7 @@ extern "C" tgs_status tgs_topk_ef_step_segmented(const float* grad, float* resid
   int64_t koff = 0;
   for (int32_t s = 0; s < nseg; ++s) {
     const int64_t len = offsets[s + 1] - offsets[s];
-    if (len > 0 && small_segment(len, ks[s])) {
+    if (len > 0 && !batched(s) && small_segment(len, ks[s])) {
       m.seg[m.nseg++] = SmallSeg{offsets[s], (u32)len, (u32)ks[s], (u32)koff, wg};
       wg += (u32)((len + kSmallPer - 1) / kSmallPer);
       if (m.nseg == kSmallMaxSeg) flush();
@@ -2958,7 +2900,7 @@ extern "C" tgs_status tgs_topk_ef_step_segmented(const float* grad, float* resid
   koff = 0;
   for (int32_t s = 0; s < nseg; ++s) {
     const int64_t len = offsets[s + 1] - offsets[s];
-    if (len > 0 && !small_segment(len, ks[s])) {
+    if (len > 0 && !batched(s) && !small_segment(len, ks[s])) {
       const tgs_status st = tgs_topk_ef_step(grad + offsets[s], residual + offsets[s], len, ks[s],
                                              ks[s] ? out_idx + koff : nullptr, ks[s] ? out_val + koff : nullptr,
                                              workspace, L.big, stream);

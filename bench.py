@@ -20,9 +20,11 @@ copies of the residuals.
 Prints one JSON line.  `roofline` covers the dominant kernel, k_step (the
 whole fused step, one launch: 12n + 8k algorithmic bytes per launch), timed
 with HIP events on the stream it is launched on, recorded around spans of 8
-back-to-back launches: the average launch period, gaps between launches
-included, without an event pair around every launch (which adds a few
-microseconds of its own); `cpu_baseline` is the plain C oracle on one host core
+back-to-back launches from the second timed launch on (the first one also
+waits for the host to issue it onto the idle GPU): the average launch period,
+gaps between launches included, without an event pair around every launch
+(which adds a few microseconds of its own); `cpu_baseline` is the plain C
+oracle on one host core
 on the same workload (its residual history built by the oracle itself).
 
     python bench.py --workload NAME [--steps K]
@@ -353,20 +355,28 @@ def main():
     def step(t):
         run(grads[(t + 3) % pool], resid[t % sets])
 
-    span = 8  # launches between two events
-    nspan = max(1, K // span)
+    # The launch period: events on the launch stream around spans of 8
+    # back-to-back launches.  The spans start after launch 0, so that the
+    # stream already holds queued work: launch 0 also waits for the host to
+    # issue it after the idle GPU, which is no part of a launch's duration.
+    span = 8
+    nspan = (K - 1) // span
+    first = 1
+    if nspan < 1:  # (fewer than 9 steps: one span over all of them)
+        span, nspan, first = K, 1, 0
+    marks = {first - 1 + j * span: j for j in range(nspan + 1)}  # event j goes right after launch `mark`
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(nspan + 1)]
     for e in ev:  # torch creates the HIP event on its first record
         e.record(run.stream)
     print("bench: timing %d steps" % K, file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    if -1 in marks:
+        ev[marks[-1]].record(run.stream)
     for i in range(K):
-        if i % span == 0 and i // span < nspan:
-            ev[i // span].record(run.stream)
         step(i)
-        if i + 1 == nspan * span:
-            ev[nspan].record(run.stream)
+        if i in marks:
+            ev[marks[i]].record(run.stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     run.check()
@@ -412,7 +422,8 @@ def main():
                      "frac": gbps_main / HBM_PEAK_GBPS, "traffic": traffic,
                      "kernel": "k_step", "bytes_per_launch": bytes_step,
                      "avg_launch_us": main_avg_ms * 1e3, "median_launch_us": main_ms[len(main_ms) // 2] * 1e3,
-                     "launches_timed": nspan * span, "timing": "HIP events around spans of %d launches" % span},
+                     "launches_timed": nspan * span,
+                     "timing": "HIP events around spans of %d back-to-back launches, from launch %d" % (span, first)},
         "cpu_baseline": cpu,
         "last_step_fast_path": bool(fast == 1),
         "timed_steps_on_exact_fallback": fallbacks,

@@ -44,7 +44,13 @@ extern "C" {
  *                       path selects exactly from acc (as when its sampled
  *                       guess does not hold),
  *                       11 = layer-wise calls without the batched path (the
- *                       small-segment kernel and one step per segment).
+ *                       small-segment kernel and one step per segment),
+ *                       12 = bucketed ranking (k >= 32768 beyond the
+ *                       one-launch step) whose accumulate workgroups may
+ *                       stage one candidate each: they overflow and the
+ *                       general path selects from acc,
+ *                       13 = no bucketed ranking: the guided general path
+ *                       ranks the copied candidates itself.
  *                       The guided path needs n >= 2^18, grad and residual
  *                       equally aligned modulo 16 bytes and k > 0; otherwise
  *                       7-9 run the plain general path.

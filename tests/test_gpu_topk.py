@@ -444,9 +444,17 @@ def test_guided_general_path_misaligned(tgs_gpu, off):
     assert np.all(host(rb[:off]) == 0) and np.all(host(rb[off + n:]) == 0)
 
 
-def test_guided_is_the_default_for_large_k(tgs_gpu):
-    """k above what the one-launch step buckets: the guided general path runs
-    by default, over 3 chained EF steps sharing one workspace."""
+def _bucketed(ws):
+    """(used, missed) counters of the bucketed ranking in a top-k workspace."""
+    w = host(ws[:64].view(torch.int32))
+    return int(w[13]), int(w[14])
+
+
+def test_bucketed_is_the_default_for_large_k(tgs_gpu):
+    """k above what the one-launch step buckets: the bucketed ranking (the
+    accumulate pass files the candidates into sampled key buckets, one
+    workgroup orders each bucket) runs by default, over 3 chained EF steps
+    sharing one workspace."""
     rng = np.random.default_rng(53)
     n, k = 6_000_000, 120_000
     r_gpu = torch.zeros(n, dtype=torch.float32, device="cuda")
@@ -458,7 +466,47 @@ def test_guided_is_the_default_for_large_k(tgs_gpu):
         tgs_gpu.check_device_error(ws)
         ei, ev = oracle.topk_ef_step(grad, r_cpu, k)
         assert_topk_equal((host(idx), host(val), host(r_gpu)), (ei, ev, r_cpu), "step %d" % step)
-    assert _guided(ws) == (3, 0)
+    assert _bucketed(ws) == (3, 0) and _guided(ws) == (0, 0)
+
+
+@pytest.mark.parametrize("dist", ["normal", "mixture", "ties", "special"])
+def test_bucketed_ranking(tgs_gpu, dist):
+    """The bucketed ranking at several sizes and k (k >= 32768): it holds on
+    the smooth distributions; on the tie-heavy grid and the special values
+    (NaN, +-inf, +-0, subnormals) a bucket may exceed what one workgroup
+    orders, and the general path then selects from acc.  Either way the
+    oracle's result."""
+    rng = np.random.default_rng(83 + len(dist))
+    for n, k in ((300_001, 40_000), (4_200_007, 60_000), (6_000_000, 300_000)):
+        grad, res = make(dist, n, rng)
+        ws = torch.zeros(tgs_gpu.topk_workspace_bytes(n, k), dtype=torch.uint8, device="cuda")
+        r = gpu(res)
+        idx, val = tgs_gpu.topk_ef_step(gpu(grad), r, k, ws=ws)
+        tgs_gpu.check_device_error(ws)
+        assert_topk_equal((host(idx), host(val), host(r)), oracle_topk(grad, res, k), "%s n=%d k=%d" % (dist, n, k))
+        used, missed = _bucketed(ws)
+        assert used + missed == 1
+        if dist in ("normal", "mixture"):
+            assert used == 1, "%s n=%d k=%d: the bucketed ranking should hold" % (dist, n, k)
+
+
+@pytest.mark.parametrize("path", [12, 13])
+def test_bucketed_ranking_off_and_overflow(tgs_gpu, path):
+    """Path 12: the accumulate workgroups may stage one candidate each, so
+    they overflow and the general path selects from acc; path 13: the
+    bucketed ranking off (the guided general path ranks the copied
+    candidates)."""
+    tgs_gpu.set_option(tgs_gpu.OPT_TOPK_PATH, path)
+    rng = np.random.default_rng(89 + path)
+    n, k = 4_200_007, 100_000
+    grad, res = make("mixture", n, rng)
+    ws = torch.zeros(tgs_gpu.topk_workspace_bytes(n, k), dtype=torch.uint8, device="cuda")
+    r = gpu(res)
+    idx, val = tgs_gpu.topk_ef_step(gpu(grad), r, k, ws=ws)
+    tgs_gpu.check_device_error(ws)
+    assert_topk_equal((host(idx), host(val), host(r)), oracle_topk(grad, res, k), "path %d" % path)
+    assert _bucketed(ws) == ({12: (0, 1), 13: (0, 0)}[path])
+    assert _guided(ws) == ({12: (0, 0), 13: (1, 0)}[path])
 
 
 @pytest.mark.parametrize("dist", ["normal", "ties", "special", "mixture"])
@@ -588,6 +636,10 @@ def test_guided_mid_sizes(tgs_gpu, n, k):
     workgroups than general-path workgroups."""
     rng = np.random.default_rng(n % 1000 + k)
     grad, res = make("mixture", n, rng)
-    got, (used, missed) = _guided_step(tgs_gpu, gpu(grad), gpu(res), k)
-    assert_topk_equal(got, oracle_topk(grad, res, k), "n=%d k=%d" % (n, k))
-    assert (used, missed) == (1, 0)
+    ws = torch.zeros(tgs_gpu.topk_workspace_bytes(n, k), dtype=torch.uint8, device="cuda")
+    r = gpu(res)
+    idx, val = tgs_gpu.topk_ef_step(gpu(grad), r, k, ws=ws)
+    tgs_gpu.check_device_error(ws)
+    assert_topk_equal((host(idx), host(val), host(r)), oracle_topk(grad, res, k), "n=%d k=%d" % (n, k))
+    # k from 32768 on: the bucketed ranking; below it the guided ranking
+    assert (_bucketed(ws) if k >= 32768 else _guided(ws)) == (1, 0)

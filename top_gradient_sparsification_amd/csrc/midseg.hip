@@ -46,6 +46,7 @@
 #include "tgs_host.h"
 #include "tgs_internal.h"
 #include "tgs_midseg.h"
+#include "tgs_rank.h"
 
 namespace tgs {
 
@@ -57,9 +58,8 @@ constexpr u32 kGuessRows = 4;       // sampled rows per workgroup of k_mid_guess
 constexpr int kMidPassThreads = 256;
 constexpr int kMidPassWaves = kMidPassThreads / kWave;
 constexpr u32 kMidBlockCap = 64;    // stash places per block
-constexpr int kMidList = 8192;      // candidates one select workgroup holds (LDS)
+constexpr int kMidList = kRankList;  // candidates one select workgroup holds (LDS)
 constexpr u32 kMidDirect = kMidList;  // segments read whole by the select workgroup
-constexpr int kRankBins = 2048;     // sub-ranges of the key span when ordering
 constexpr int kMidHistBins = 4096;  // sample histogram: key >> 19
 constexpr u32 kMidNoGuess = 0xFFFFFFFFu;  // no stashing (the whole segment is read, or k = 0)
 constexpr int kMidStream = 16;      // loads in flight per thread in the exact route
@@ -263,88 +263,8 @@ __global__ __launch_bounds__(kMidPassThreads) void k_mid_pass(MidArgs a) {
 }
 
 // ----------------------------------------------------------- k_mid_select ----
-// Shared memory of the select workgroup.
-struct SelLds {
-  u64 list[kMidList];  // the candidates: packed pairs, in index order
-  u64 tmp[kMidList];   // the same, grouped by sub-range of the key span
-  u32 cnt[kRankBins];  // entries per sub-range (and the radix histogram of the exact route)
-  u32 start[kRankBins];
-  u32 cur[kRankBins];
-  u32 scan[kMidWaves + 1];
-  u32 found[4];
-  u32 wc[2][kMidWaves][2];
-  u32 kmin, kmax, flag;
-};
-
-// Orders the n candidates of s.list (k <= n <= kMidList) by (key desc, index
-// asc) and emits the first k: a counting sort over kRankBins equal
-// sub-ranges of the candidates' key span (the largest keys first), which
-// keeps only the sub-ranges that start below rank k, then each entry's rank
-// inside its sub-range by counting the entries of the sub-range before it.
-// Every thread calls it.
-__device__ void rank_emit(SelLds& s, u32 n, u32 k, float* r, int32_t* oi, float* ov) {
-  constexpr int NT = kMidThreads;
-  const int tid = threadIdx.x;
-  u32 mn = 0xFFFFFFFFu, mx = 0u;
-  for (u32 i = tid; i < n; i += NT) {
-    const u32 key = key_of_bits((u32)(s.list[i] >> 32));
-    mn = std::min(mn, key);
-    mx = std::max(mx, key);
-  }
-  mn = wave_min(mn);
-  mx = wave_max(mx);
-  if (tid == 0) {
-    s.kmin = 0xFFFFFFFFu;
-    s.kmax = 0u;
-  }
-  for (int i = tid; i < kRankBins; i += NT) {
-    s.cnt[i] = 0u;
-    s.cur[i] = 0u;
-  }
-  __syncthreads();
-  if (lane_id() == 0) {
-    atomicMin(&s.kmin, mn);
-    atomicMax(&s.kmax, mx);
-  }
-  __syncthreads();
-  const u32 kmax = s.kmax, span = s.kmax - s.kmin;
-  auto sub = [&](u32 key) { return span ? (u32)(((u64)(kmax - key) * (u64)(kRankBins - 1)) / span) : 0u; };
-  for (u32 i = tid; i < n; i += NT) atomicAdd(&s.cnt[sub(key_of_bits((u32)(s.list[i] >> 32)))], 1u);
-  __syncthreads();
-  static_assert(kRankBins == 2 * NT, "two sub-ranges per thread");
-  const u32 c0 = s.cnt[2 * tid], c1 = s.cnt[2 * tid + 1];
-  u32 tot;
-  const u32 b0 = block_exclusive_sum<NT>(c0 + c1, s.scan, tot);
-  s.start[2 * tid] = b0;
-  s.start[2 * tid + 1] = b0 + c0;
-  // the sub-ranges that start below k hold the first E entries
-  u32 E;
-  (void)block_exclusive_sum<NT>((b0 < k ? c0 : 0u) + (b0 + c0 < k ? c1 : 0u), s.scan, E);
-  for (u32 i = tid; i < n; i += NT) {
-    const u64 pv = s.list[i];
-    const u32 sb = sub(key_of_bits((u32)(pv >> 32)));
-    const u32 a = s.start[sb];
-    if (a < k) s.tmp[a + atomicAdd(&s.cur[sb], 1u)] = pv;
-  }
-  __syncthreads();
-  auto rkey = [](u64 pv) {
-    return ((u64)(0x7FFFFFFFu - key_of_bits((u32)(pv >> 32))) << 32) | (u64)(u32)pv;
-  };
-  for (u32 p = tid; p < E; p += NT) {
-    const u64 pv = s.tmp[p];
-    const u64 me = rkey(pv);
-    const u32 sb = sub(key_of_bits((u32)(pv >> 32)));
-    const u32 a = s.start[sb], c = s.cnt[sb];
-    u32 rank = a;
-    for (u32 q = a; q < a + c; ++q) rank += rkey(s.tmp[q]) < me ? 1u : 0u;
-    if (rank < k) {
-      const Pair e = unpack_pair(pv);
-      oi[rank] = e.idx;
-      ov[rank] = __uint_as_float(e.bits);
-      r[e.idx] = 0.0f;
-    }
-  }
-}
+// Shared memory of the select workgroup: RankLds (list, sorting scratch).
+using SelLds = RankLds;
 
 // Exact route, streaming acc (len entries at r) from memory: the rule that
 // selects the top `need` (every key >= t_lo, plus the first rr keys equal to

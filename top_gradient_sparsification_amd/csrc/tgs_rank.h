@@ -1,0 +1,97 @@
+// Ordering of up to 8192 (index, value) pairs by one workgroup of 1024
+// threads: (key desc, index asc), the first k emitted.  Used by the batched
+// layer-wise path and by the bucketed ranking of the top-k step.
+#pragma once
+
+#include "tgs_internal.h"
+
+namespace tgs {
+
+constexpr int kRankThreads = 1024;
+constexpr int kRankList = 8192;   // entries one workgroup orders (LDS)
+constexpr int kRankBins = 2048;   // sub-ranges of the key span
+
+// Shared memory of a ranking workgroup.
+struct RankLds {
+  u64 list[kRankList];  // the entries: packed pairs
+  u64 tmp[kRankList];   // the same, grouped by sub-range of the key span
+  u32 cnt[kRankBins];  // entries per sub-range (and the radix histogram of the exact route)
+  u32 start[kRankBins];
+  u32 cur[kRankBins];
+  u32 scan[kRankThreads / kWave + 1];
+  u32 found[4];
+  u32 wc[2][kRankThreads / kWave][2];
+  u32 kmin, kmax, flag;
+};
+
+// Orders the n entries of s.list (k <= n <= kRankList) by (key desc, index
+// asc) and emits the first k: a counting sort over kRankBins equal
+// sub-ranges of the candidates' key span (the largest keys first), which
+// keeps only the sub-ranges that start below rank k, then each entry's rank
+// inside its sub-range by counting the entries of the sub-range before it;
+// the emitted entries' residual becomes +0.  Every thread calls it.
+__device__ inline void rank_emit(RankLds& s, u32 n, u32 k, float* r, int32_t* oi, float* ov) {
+  constexpr int NT = kRankThreads;
+  const int tid = threadIdx.x;
+  u32 mn = 0xFFFFFFFFu, mx = 0u;
+  for (u32 i = tid; i < n; i += NT) {
+    const u32 key = key_of_bits((u32)(s.list[i] >> 32));
+    mn = std::min(mn, key);
+    mx = std::max(mx, key);
+  }
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  if (tid == 0) {
+    s.kmin = 0xFFFFFFFFu;
+    s.kmax = 0u;
+  }
+  for (int i = tid; i < kRankBins; i += NT) {
+    s.cnt[i] = 0u;
+    s.cur[i] = 0u;
+  }
+  __syncthreads();
+  if (lane_id() == 0) {
+    atomicMin(&s.kmin, mn);
+    atomicMax(&s.kmax, mx);
+  }
+  __syncthreads();
+  const u32 kmax = s.kmax, span = s.kmax - s.kmin;
+  auto sub = [&](u32 key) { return span ? (u32)(((u64)(kmax - key) * (u64)(kRankBins - 1)) / span) : 0u; };
+  for (u32 i = tid; i < n; i += NT) atomicAdd(&s.cnt[sub(key_of_bits((u32)(s.list[i] >> 32)))], 1u);
+  __syncthreads();
+  static_assert(kRankBins == 2 * NT, "two sub-ranges per thread");
+  const u32 c0 = s.cnt[2 * tid], c1 = s.cnt[2 * tid + 1];
+  u32 tot;
+  const u32 b0 = block_exclusive_sum<NT>(c0 + c1, s.scan, tot);
+  s.start[2 * tid] = b0;
+  s.start[2 * tid + 1] = b0 + c0;
+  // the sub-ranges that start below k hold the first E entries
+  u32 E;
+  (void)block_exclusive_sum<NT>((b0 < k ? c0 : 0u) + (b0 + c0 < k ? c1 : 0u), s.scan, E);
+  for (u32 i = tid; i < n; i += NT) {
+    const u64 pv = s.list[i];
+    const u32 sb = sub(key_of_bits((u32)(pv >> 32)));
+    const u32 a = s.start[sb];
+    if (a < k) s.tmp[a + atomicAdd(&s.cur[sb], 1u)] = pv;
+  }
+  __syncthreads();
+  auto rkey = [](u64 pv) {
+    return ((u64)(0x7FFFFFFFu - key_of_bits((u32)(pv >> 32))) << 32) | (u64)(u32)pv;
+  };
+  for (u32 p = tid; p < E; p += NT) {
+    const u64 pv = s.tmp[p];
+    const u64 me = rkey(pv);
+    const u32 sb = sub(key_of_bits((u32)(pv >> 32)));
+    const u32 a = s.start[sb], c = s.cnt[sb];
+    u32 rank = a;
+    for (u32 q = a; q < a + c; ++q) rank += rkey(s.tmp[q]) < me ? 1u : 0u;
+    if (rank < k) {
+      const Pair e = unpack_pair(pv);
+      oi[rank] = e.idx;
+      ov[rank] = __uint_as_float(e.bits);
+      r[e.idx] = 0.0f;
+    }
+  }
+}
+
+}  // namespace tgs

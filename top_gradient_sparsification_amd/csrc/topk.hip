@@ -70,6 +70,7 @@
 #include "tgs_host.h"
 #include "tgs_internal.h"
 #include "tgs_midseg.h"
+#include "tgs_rank.h"
 
 namespace tgs {
 
@@ -118,6 +119,10 @@ constexpr int kGuessUnroll = 8;  // sample chunks per wave, all loads in flight 
 constexpr int kGuessChunk = 4 * kWave;  // entries per sample chunk: one float4 per lane
 constexpr int64_t kGuessMaxChunks = (int64_t)kGuessBlocks * (kGuessThreads / kWave) * kGuessUnroll;
 constexpr int64_t kGuideMinN = (int64_t)1 << 18;  // smaller vectors take the plain accumulate pass
+constexpr int kRkBuckets = 1024;   // buckets of the bucketed ranking at most (one ranking workgroup each)
+constexpr int64_t kRkMinK = 32768; // the bucketed ranking serves k from this on
+constexpr int kRkStage = 12288;    // candidates one accumulate workgroup stages in LDS (its region)
+static_assert(kRkBuckets <= kRankThreads, "one bucket total per ranking thread");
 constexpr u32 kWhyPlan = 1u, kWhyBucket = 4u, kWhyFew = 8u, kWhyRegion = 16u, kWhyList = 32u, kWhyWait = 64u;
 
 // ------------------------------------------------------------- state ----
@@ -169,7 +174,12 @@ struct StepCtl {
   u32 guided_missed;  // guided calls whose guess or regions did not hold: acc read again (never reset)
   u32 parity;         // counter set the next k_step launch uses (flipped by each launch)
   u32 mid_exact;      // batched layer-wise segments selected exactly from acc (never reset)
-  u32 pad1[54];
+  u32 rk_count;       // bucketed ranking: buckets of this call (0: none), set by k_guess
+  u32 rk_ok;          // 1 once the bucketed ranking has emitted the step (k_general then exits)
+  u32 rk_ovf;         // set when a workgroup's slots of a bucket overflowed
+  u32 rk_used;        // calls whose bucketed ranking held (never reset)
+  u32 rk_missed;      // calls whose bucketed ranking did not hold: k_general ran (never reset)
+  u32 pad1[49];
   StepSet set[2];
   Plan plan;
   u32 seg_done[64];  // arrivals per segment of a k_small or k_mid_guess launch; each segment's last workgroup leaves it zero
@@ -181,7 +191,8 @@ struct StepCtl {
   u32 acc_ticket;  // row pairs handed out by the accumulate pass (k_guess sets it to zero)
 };
 static_assert(sizeof(StepCtl) <= kEstStateOffset, "control block overlaps the header's shared state");
-static_assert(offsetof(StepCtl, mid_exact) == 36, "the tests read the route counters at fixed offsets");
+static_assert(offsetof(StepCtl, mid_exact) == 36 && offsetof(StepCtl, rk_used) == 52,
+              "the tests read the route counters at fixed offsets");
 static_assert(kMaxAccBlocks <= kMaxGenWG, "guided regions are the general path's");
 
 // State of the general path (zero when it starts).
@@ -195,9 +206,27 @@ struct GenState {
 
 struct TopkLayout {
   size_t ctl, gstate, gcnt, lsd_cnt, lsd_pre, lsd_tot, bufA, bufB, cand, hist_rows, guide_cnt, bkt_cnt, bkt_cur, bkt_buf,
-      small, pub, rcnt, slots, ovf, total;
+      small, pub, rcnt, slots, ovf, rk_tab, rk_tot, rk_cnt, rk_slots, total;
   u32 cand_cap;
+  int64_t rk_entries;  // candidate places of the bucketed ranking (0: not provided)
+  u32 rk_target;       // entries per bucket the bucketed ranking aims at
 };
+
+// The bucketed ranking's sizes for (n, k): the accumulate workgroups (as
+// the host launches them) and the entries per bucket aimed at: about 240
+// buckets for the ~1.5 k candidates, so that the ranking workgroups (one per
+// compute unit: each holds 152 KB of LDS) run in one wave, 256 to 3000 each.
+struct RkSizes {
+  int G1;
+  u32 target;
+};
+static RkSizes rk_sizes(int64_t n, int64_t k) {
+  RkSizes z{};
+  const int64_t units = n / 4, per = (int64_t)kAccThreads * 2;
+  z.G1 = (int)std::max<int64_t>(1, std::min<int64_t>(kMaxAccBlocks, (units + per - 1) / per));
+  z.target = (u32)std::min<int64_t>(3000, std::max<int64_t>(256, (3 * k + 479) / 480));
+  return z;
+}
 
 // Pairs one candidate region (one wave of the standalone general path) holds:
 // room for 4 k spread evenly, plus slack.  The guided accumulate pass fills
@@ -211,7 +240,6 @@ static u32 cand_region_cap(int64_t k) {
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 static TopkLayout topk_layout(int64_t n, int64_t k) {
-  (void)n;
   TopkLayout L{};
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -239,6 +267,15 @@ static TopkLayout topk_layout(int64_t n, int64_t k) {
   L.rcnt = take(sizeof(u16) * (size_t)kMaxStepBlocks * kMaxBuckets);
   L.slots = take(sizeof(Pair) * (size_t)kMaxBuckets * kSlotTotal);
   L.ovf = take(sizeof(Pair) * (size_t)kMaxStepBlocks * kOvfCap);
+  if (k >= kRkMinK && n >= kGuideMinN) {
+    const RkSizes z = rk_sizes(n, k);
+    L.rk_target = z.target;
+    L.rk_entries = (int64_t)z.G1 * kRkStage;
+    L.rk_tab = take(sizeof(u32) * 2048);
+    L.rk_tot = take(sizeof(u32) * kRkBuckets);
+    L.rk_cnt = take(sizeof(u32) * (size_t)kRkBuckets * kMaxAccBlocks);
+    L.rk_slots = take(sizeof(u64) * (size_t)L.rk_entries);
+  }
   L.total = off;
   return L;
 }
@@ -1160,6 +1197,11 @@ struct GuessArgs {
   u32 c_req, s_max;
   StepCtl* ctl;
   HeaderHist* hh;
+  // bucketed ranking (rk_tab set): the bucket table, the bucket totals (left
+  // zero here) and the sample entries one bucket should hold
+  u32* rk_tab;
+  u32* rk_tot;
+  float rk_samples;
 };
 
 __global__ __launch_bounds__(kGuessThreads) void k_guess(GuessArgs a) {
@@ -1212,6 +1254,32 @@ __global__ __launch_bounds__(kGuessThreads) void k_guess(GuessArgs a) {
   const u32 kept = block_sum<NT>(mine + mine0, s_scan);
   st_agent(&a.hh->hist[hi], 0u);
   st_agent(&a.hh->hist[hi - 1], 0u);
+  if (a.rk_tab) {
+    // The bucketed ranking's buckets, numbered from the top: bin j >= pick is
+    // cut into s_j equal sub-ranges of its 2^20 keys, s_j the sample entries
+    // of the bin over those one bucket should hold, rounded up; a bin without
+    // sample entries joins the bucket just above it (bucket 0 for the top
+    // bins).  rk_tab[j] = first bucket of bin j << 16 | s_j.  More than
+    // kRkBuckets buckets: twice the entries per bucket, again.
+    float per = a.rk_samples;
+    u32 s1 = 0, s0 = 0, nb = 0;
+    for (int tries = 0; tries < 12; ++tries, per *= 2.0f) {
+      s1 = (u32)hi >= pick && h1 ? (u32)ceilf((float)h1 / per) : 0u;
+      s0 = (u32)(hi - 1) >= pick && h0 ? (u32)ceilf((float)h0 / per) : 0u;
+      nb = block_sum<NT>(s1 + s0, s_scan);
+      if (nb <= (u32)kRkBuckets) break;
+    }
+    u32 all;
+    const u32 base = block_exclusive_sum<NT>(s1 + s0, s_scan, all);
+    a.rk_tab[hi] = base << 16 | s1;
+    a.rk_tab[hi - 1] = (base + s1) << 16 | s0;
+    for (int i = tid; i < kRkBuckets; i += NT) a.rk_tot[i] = 0u;
+    if (tid == 0) {
+      ctl->rk_count = nb <= (u32)kRkBuckets ? std::max(nb, 1u) : 0u;
+      ctl->rk_ok = 0u;
+      ctl->rk_ovf = 0u;
+    }
+  }
   if (tid == 0) {
     st_agent(&ctl->guide_bin, kept <= a.s_max ? pick : kNoGuide);
     st_agent(&ctl->guide_ovf, 0u);
@@ -1235,6 +1303,13 @@ __global__ __launch_bounds__(kGuessThreads) void k_guess(GuessArgs a) {
 // a ticket hands out (G + the ticket's count), one pair ahead: the
 // workgroups then stay on one short stretch of memory however their speeds
 // differ, where a fixed deal lets the slower ones fall behind and finish last.
+//
+// With BKT (the bucketed ranking) the candidates are staged in LDS instead
+// (the same wave-wise placement) and, at the end, written to the
+// workgroup's own region grouped by bucket (k_guess's table: a bin's entries
+// split into equal key sub-ranges), with each bucket's place and count in
+// the region; the counts are added into the buckets' totals.  More
+// candidates than the stage holds flag the overflow.
 struct GuidedArgs {
   const float* grad;
   float* residual;
@@ -1250,12 +1325,30 @@ struct GuidedArgs {
   u64* cand;           // workgroup b's region: cand + b * cap
   u32 cap;
   u32* ticket;         // zero at the start (DYN)
+  // BKT
+  const u32* rk_tab;   // [2048] first bucket of bin j << 16 | its buckets
+  const u32* rk_count; // buckets
+  u32* rk_cnt;         // [bucket][gridDim.x] place in the region << 16 | entries
+  u32* rk_tot;         // [bucket] entries over all workgroups (zero on entry)
+  u64* rk_reg;         // [gridDim.x][kRkStage] packed pairs, grouped by bucket
+  u32* rk_ovf;
+  u32 rk_cap;          // candidates staged at most (kRkStage; less to test)
 };
 
-template <bool DYN>
+// Bucket of a candidate key under the bucketed ranking's table.
+__device__ __forceinline__ u32 rk_bucket(const u32* tab, u32 key) {
+  const u32 t = tab[key >> 20], base = t >> 16, sj = t & 0xFFFFu;
+  return sj ? base + (u32)(((u64)(0xFFFFFu - (key & 0xFFFFFu)) * sj) >> 20) : (base ? base - 1u : 0u);
+}
+
+template <bool DYN, bool BKT>
 __global__ __launch_bounds__(kAccThreads) void k_acc_guided(GuidedArgs a) {
   constexpr int NT = kAccThreads;
   __shared__ u32 s_h[2048];
+  __shared__ u32 s_tab[BKT ? 2048 : 1];
+  __shared__ u32 s_bc[BKT ? kRkBuckets : 1];
+  __shared__ u64 s_stage[BKT ? kRkStage : 1];
+  __shared__ u32 s_scan[BKT ? kAccThreads / kWave + 1 : 1];
   __shared__ u32 s_cnt;
   __shared__ int64_t s_next;
   const int tid = threadIdx.x, lane = lane_id();
@@ -1264,7 +1357,12 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_guided(GuidedArgs a) {
   if (blockIdx.x == 0)
     for (int i = tid; i < a.zero_words; i += NT) a.zero_ptr[i] = 0u;
   const u32 gbin = a.ctl->guide_bin;
-  const bool guide = gbin != kNoGuide;  // the same in every thread
+  const u32 nbk = BKT ? *a.rk_count : 0u;
+  const bool guide = gbin != kNoGuide && (!BKT || nbk > 0);  // the same in every thread
+  if (BKT) {
+    for (int i = tid; i < 2048; i += NT) s_tab[i] = a.rk_tab[i];
+    for (int i = tid; i < kRkBuckets; i += NT) s_bc[i] = 0u;
+  }
   const int64_t nrows = (a.nv + NT - 1) / NT, npairs = (nrows + 1) / 2, G = gridDim.x;
   int64_t nn = 0;  // thread 0 (DYN): the pair after the next one
   if (DYN && tid == 0) {
@@ -1273,8 +1371,8 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_guided(GuidedArgs a) {
   }
   __syncthreads();
   u64* const reg = a.cand + (size_t)blockIdx.x * a.cap;
-  // this lane's kept entries i0 + j (bit j of m4) go to the region; every
-  // lane of the wave calls it
+  // this lane's kept entries i0 + j (bit j of m4) go to the region (BKT: to
+  // their bucket's slots); every lane of the wave calls it
   auto place = [&](u32 m4, int64_t i0, const u32* bq) {
     const u32 c = (u32)__popc(m4);
     if (ballot(c != 0u) == 0u) return;
@@ -1285,7 +1383,12 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_guided(GuidedArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       if ((m4 >> j) & 1u) {
-        if (pos < a.cap) reg[pos] = pack_pair(Pair{(int32_t)(i0 + j), bq[j]});
+        const u64 pv = pack_pair(Pair{(int32_t)(i0 + j), bq[j]});
+        if (BKT) {
+          if (pos < a.rk_cap) s_stage[pos] = pv;
+        } else if (pos < a.cap) {
+          reg[pos] = pv;
+        }
         ++pos;
       }
   };
@@ -1367,14 +1470,111 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_guided(GuidedArgs a) {
   }
   __syncthreads();
   for (int i = tid; i < 2048; i += NT) a.hist_rows[(size_t)blockIdx.x * 2048 + i] = s_h[i];
-  if (tid == 0) {
+  if (BKT) {
+    // the staged candidates to the region, grouped by bucket
+    const u32 ns = s_cnt;
+    if (ns > a.rk_cap) {
+      if (tid == 0) atomicOr(a.rk_ovf, 1u);
+    } else if (guide) {
+      for (u32 i = tid; i < ns; i += NT) atomicAdd(&s_bc[rk_bucket(s_tab, key_of_bits((u32)(s_stage[i] >> 32)))], 1u);
+      __syncthreads();
+      static_assert(kRkBuckets == NT, "one bucket per thread");
+      const u32 c = (u32)tid < nbk ? s_bc[tid] : 0u;
+      u32 all;
+      const u32 off = block_exclusive_sum<NT>(c, s_scan, all);
+      if ((u32)tid < nbk) {
+        a.rk_cnt[(size_t)tid * gridDim.x + blockIdx.x] = off << 16 | c;
+        if (c) (void)add_agent_relaxed(&a.rk_tot[tid], c);
+        s_bc[tid] = off;  // now the bucket's next place
+      }
+      __syncthreads();
+      u64* const rg = a.rk_reg + (size_t)blockIdx.x * kRkStage;
+      for (u32 i = tid; i < ns; i += NT) {
+        const u64 pv = s_stage[i];
+        rg[atomicAdd(&s_bc[rk_bucket(s_tab, key_of_bits((u32)(pv >> 32)))], 1u)] = pv;
+      }
+    }
+  } else if (tid == 0) {
     const u32 cnt = s_cnt;
     a.guide_cnt[blockIdx.x] = cnt;
     if (cnt > a.cap) atomicOr(a.guide_ovf, 1u);
   }
 }
 
-__global__ __launch_bounds__(kGenThreads) void k_general(GenArgs a) { general_path<kGenThreads, 16, true, 9, true>(a); }
+// ------------------------------------------------------------- k_rank ----
+// The bucketed ranking: workgroup w orders buckets w, w + G, ...  Every
+// workgroup reads the bucket totals and decides alike whether the route
+// held: no accumulate workgroup's stage overflowed, the buckets hold at least
+// k entries (then every entry at or above the k-th key is among them, the
+// guessed bin being at or below the k-th key's bin) and none holds more than
+// one workgroup orders.  Then bucket b's entries take the places after those
+// of the buckets above it: the workgroup gathers them from every accumulate
+// workgroup's region, orders them by (key desc, index asc) and emits the
+// ones whose place is below k, setting their residual to +0.  When the route
+// did not hold nothing is written and k_general, which runs next, selects
+// from acc instead.
+struct RankArgs {
+  StepCtl* ctl;        // rk_count, rk_ovf; rk_ok is set when the route held
+  const u32* tot;      // [bucket]
+  const u32* cnt;      // [bucket][G1] place << 16 | entries
+  const u64* reg;      // [G1][kRkStage]
+  u32 G1;
+  int64_t k;
+  int32_t* out_idx;
+  float* out_val;
+  float* residual;
+};
+
+__global__ __launch_bounds__(kRankThreads) void k_rank(RankArgs a) {
+  __shared__ RankLds s;
+  __shared__ u32 s_pre[kRkBuckets];
+  __shared__ u32 s_max;
+  const int tid = threadIdx.x;
+  const u32 B = a.ctl->rk_count;
+  const u32 v = (u32)tid < B ? a.tot[tid] : 0u;
+  if (tid == 0) s_max = 0u;
+  u32 sum;
+  s_pre[tid] = block_exclusive_sum<kRankThreads>(v, s.scan, sum);
+  const u32 mx = wave_max(v);
+  if (lane_id() == 0) atomicMax(&s_max, mx);
+  __syncthreads();
+  const bool ok = B > 0 && a.ctl->rk_ovf == 0u && (int64_t)sum >= a.k && s_max <= (u32)kRankList;
+  if (blockIdx.x == 0 && tid == 0) {
+    if (ok) a.ctl->rk_ok = 1u;
+    atomicAdd(ok ? &a.ctl->rk_used : &a.ctl->rk_missed, 1u);
+  }
+  if (!ok) return;
+  // buckets b = blockIdx.x, + gridDim.x, ...
+  for (u32 b = blockIdx.x; b < B; b += gridDim.x) {
+    const u32 start = s_pre[b];
+    if ((int64_t)start >= a.k) break;  // (so does every later bucket)
+    const u32 nb = a.tot[b];
+    const u32 kk = (u32)std::min<int64_t>(nb, a.k - start);
+    // bucket b's entries from the accumulate workgroups' regions (thread w:
+    // those of workgroup w), in any order: the ordering needs none
+    const u32 oc = (u32)tid < a.G1 ? a.cnt[(size_t)b * a.G1 + tid] : 0u;
+    const u32 c = oc & 0xFFFFu;
+    u32 tot;
+    const u32 at = block_exclusive_sum<kRankThreads>(c, s.scan, tot);
+    const u64* sl = a.reg + (size_t)tid * kRkStage + (oc >> 16);
+    for (u32 e0 = 0; e0 < c; e0 += 8) {
+      u64 e[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) e[j] = e0 + j < c ? sl[e0 + j] : 0ull;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (e0 + j < c) s.list[at + e0 + j] = e[j];
+    }
+    __syncthreads();
+    rank_emit(s, nb, kk, a.residual, a.out_idx + start, a.out_val + start);
+    __syncthreads();  // s is reused by the next bucket
+  }
+}
+
+__global__ __launch_bounds__(kGenThreads) void k_general(GenArgs a, const u32* rk_ok) {
+  if (rk_ok && *rk_ok) return;  // the bucketed ranking has emitted the step
+  general_path<kGenThreads, 16, true, 9, true>(a);
+}
 
 // ------------------------------------------------------------- k_small ----
 // Small vectors (n <= 2^18, k <= 256) in one launch with no grid barrier,
@@ -2687,6 +2887,10 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
     // so k_general need not read acc again: it takes one region per
     // workgroup of k_general, in index order.
     const bool guided = vec && k > 0 && path != 1 && n >= kGuideMinN && G1 <= G2;
+    // the bucketed ranking (the default from kRkMinK on; path 12: a stage of
+    // one candidate, so that it overflows; path 13: never)
+    const RkSizes rz = rk_sizes(n, k);
+    const bool bucketed = guided && L.rk_entries > 0 && (path == 0 || path == 12) && G1 <= rz.G1;
     if (guided) {
       const int64_t want = (int64_t)std::ceil(1024.0 * (double)n / (double)k);  // ~1024 expected above the k-th key
       int64_t chunks = (want + kGuessChunk - 1) / kGuessChunk;
@@ -2703,9 +2907,14 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
       // accumulate workgroups
       const u32 stride = (u32)((int64_t)G2 * (kGenThreads / kWave) * L.cand_cap / G1);
       const double room = (double)G1 * stride;
-      q.s_max = (u32)std::min(4.0e9, std::floor(0.6 * room * f));
+      q.s_max = bucketed ? 0xFFFFFFFFu : (u32)std::min(4.0e9, std::floor(0.6 * room * f));
       q.ctl = ctl;
       q.hh = header_hist(workspace);
+      if (bucketed) {
+        q.rk_tab = (u32*)(ws + L.rk_tab);
+        q.rk_tot = (u32*)(ws + L.rk_tot);
+        q.rk_samples = (float)std::max(1e-3, f * (double)L.rk_target);
+      }
       const int gq = (int)std::min<int64_t>(kGuessBlocks, (chunks + (kGuessThreads / kWave) * kGuessUnroll - 1) /
                                                               ((kGuessThreads / kWave) * kGuessUnroll));
       hipLaunchKernelGGL(k_guess, dim3(gq), dim3(kGuessThreads), 0, stream, q);
@@ -2726,10 +2935,45 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
       g.ticket = &ctl->acc_ticket;
       // the ticket's hand-out pays from about 32 rows per workgroup on
       const int64_t rows = (nv + kAccThreads - 1) / kAccThreads;
-      if (rows >= 32 * (int64_t)G1)
-        hipLaunchKernelGGL(k_acc_guided<true>, dim3(G1), dim3(kAccThreads), 0, stream, g);
+      const bool dyn = rows >= 32 * (int64_t)G1;
+      if (bucketed) {
+        g.rk_tab = q.rk_tab;
+        g.rk_count = &ctl->rk_count;
+        g.rk_cnt = (u32*)(ws + L.rk_cnt);
+        g.rk_tot = q.rk_tot;
+        g.rk_reg = (u64*)(ws + L.rk_slots);
+        g.rk_ovf = &ctl->rk_ovf;
+        g.rk_cap = path == 12 ? 1u : (u32)kRkStage;
+        if (dyn)
+          hipLaunchKernelGGL((k_acc_guided<true, true>), dim3(G1), dim3(kAccThreads), 0, stream, g);
+        else
+          hipLaunchKernelGGL((k_acc_guided<false, true>), dim3(G1), dim3(kAccThreads), 0, stream, g);
+        RankArgs ra{};
+        ra.ctl = ctl;
+        ra.tot = g.rk_tot;
+        ra.cnt = g.rk_cnt;
+        ra.reg = g.rk_reg;
+        ra.G1 = (u32)G1;
+        ra.k = k;
+        ra.out_idx = out_idx;
+        ra.out_val = out_val;
+        ra.residual = residual;
+        // one ranking workgroup per compute unit (each holds ~156 KB of LDS)
+        const int gr = std::max(1, std::min(kRkBuckets, device_cu_count()));
+        hipLaunchKernelGGL(k_rank, dim3(gr), dim3(kRankThreads), 0, stream, ra);
+        // if the ranking did not hold, k_general selects from acc (its
+        // first-level histogram rows are the accumulate pass's)
+        ga.bar.nwg = (u32)G2;
+        hipLaunchKernelGGL(k_general, dim3(G2), dim3(kGenThreads), 0, stream, ga, (const u32*)&ctl->rk_ok);
+        if (ev1) (void)hipEventRecord(ev1, stream);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return fail(TGS_EHIP, "topk_ef_step: launch failed: %s", hipGetErrorString(e));
+        return TGS_OK;
+      }
+      if (dyn)
+        hipLaunchKernelGGL((k_acc_guided<true, false>), dim3(G1), dim3(kAccThreads), 0, stream, g);
       else
-        hipLaunchKernelGGL(k_acc_guided<false>, dim3(G1), dim3(kAccThreads), 0, stream, g);
+        hipLaunchKernelGGL((k_acc_guided<false, false>), dim3(G1), dim3(kAccThreads), 0, stream, g);
       ga.guided = 1;
       ga.guide_stride = stride;
       ga.guide_bin = &ctl->guide_bin;
@@ -2746,7 +2990,7 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
     }
     if (k > 0) {
       ga.bar.nwg = (u32)G2;
-      hipLaunchKernelGGL(k_general, dim3(G2), dim3(kGenThreads), 0, stream, ga);
+      hipLaunchKernelGGL(k_general, dim3(G2), dim3(kGenThreads), 0, stream, ga, (const u32*)nullptr);
     }
   }
   if (ev1) (void)hipEventRecord(ev1, stream);

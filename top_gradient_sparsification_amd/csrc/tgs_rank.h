@@ -21,29 +21,53 @@ struct RankLds {
   u32 scan[kRankThreads / kWave + 1];
   u32 found[4];
   u32 wc[2][kRankThreads / kWave][2];
-  u32 kmin, kmax, flag;
+  u64 kmin, kmax;  // rank keys' span
+  u32 flag;
 };
 
 // Orders the n entries of s.list (k <= n <= kRankList) by (key desc, index
 // asc) and emits the first k: a counting sort over kRankBins equal
-// sub-ranges of the candidates' key span (the largest keys first), which
-// keeps only the sub-ranges that start below rank k, then each entry's rank
-// inside its sub-range by counting the entries of the sub-range before it;
+// sub-ranges of the span of the rank keys ((0x7FFFFFFF - key) << 32 |
+// index), which keeps only the sub-ranges that start below rank k, then each
+// entry's rank inside its sub-range by counting the entries of the sub-range
+// before it;
 // the emitted entries' residual becomes +0.  Every thread calls it.
+// 64-bit minimum and maximum over the wave (every lane gets them).
+__device__ __forceinline__ u64 wave_min64(u64 v) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) {
+    const u64 o = ((u64)(u32)__shfl_xor((int)(u32)(v >> 32), m) << 32) | (u64)(u32)__shfl_xor((int)(u32)v, m);
+    v = o < v ? o : v;
+  }
+  return v;
+}
+__device__ __forceinline__ u64 wave_max64(u64 v) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) {
+    const u64 o = ((u64)(u32)__shfl_xor((int)(u32)(v >> 32), m) << 32) | (u64)(u32)__shfl_xor((int)(u32)v, m);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
 __device__ inline void rank_emit(RankLds& s, u32 n, u32 k, float* r, int32_t* oi, float* ov) {
   constexpr int NT = kRankThreads;
   const int tid = threadIdx.x;
-  u32 mn = 0xFFFFFFFFu, mx = 0u;
+  // the rank order of an entry: (key desc, index asc), unique
+  auto rkey = [](u64 pv) {
+    return ((u64)(0x7FFFFFFFu - key_of_bits((u32)(pv >> 32))) << 32) | (u64)(u32)pv;
+  };
+  u64 mn = ~0ull, mx = 0ull;
   for (u32 i = tid; i < n; i += NT) {
-    const u32 key = key_of_bits((u32)(s.list[i] >> 32));
-    mn = std::min(mn, key);
-    mx = std::max(mx, key);
+    const u64 c = rkey(s.list[i]);
+    mn = c < mn ? c : mn;
+    mx = c > mx ? c : mx;
   }
-  mn = wave_min(mn);
-  mx = wave_max(mx);
+  mn = wave_min64(mn);
+  mx = wave_max64(mx);
   if (tid == 0) {
-    s.kmin = 0xFFFFFFFFu;
-    s.kmax = 0u;
+    s.kmin = ~0ull;
+    s.kmax = 0ull;
   }
   for (int i = tid; i < kRankBins; i += NT) {
     s.cnt[i] = 0u;
@@ -55,9 +79,12 @@ __device__ inline void rank_emit(RankLds& s, u32 n, u32 k, float* r, int32_t* oi
     atomicMax(&s.kmax, mx);
   }
   __syncthreads();
-  const u32 kmax = s.kmax, span = s.kmax - s.kmin;
-  auto sub = [&](u32 key) { return span ? (u32)(((u64)(kmax - key) * (u64)(kRankBins - 1)) / span) : 0u; };
-  for (u32 i = tid; i < n; i += NT) atomicAdd(&s.cnt[sub(key_of_bits((u32)(s.list[i] >> 32)))], 1u);
+  // sub-range of a rank key: monotone in it, so that the sub-ranges are
+  // consecutive stretches of the order (and equal keys spread by index)
+  const u64 cmin = s.kmin, span = s.kmax - s.kmin;
+  const double scale = span ? (double)(kRankBins - 1) / (double)span : 0.0;
+  auto sub = [&](u64 c) { return std::min<u32>((u32)((double)(c - cmin) * scale), (u32)(kRankBins - 1)); };
+  for (u32 i = tid; i < n; i += NT) atomicAdd(&s.cnt[sub(rkey(s.list[i]))], 1u);
   __syncthreads();
   static_assert(kRankBins == 2 * NT, "two sub-ranges per thread");
   const u32 c0 = s.cnt[2 * tid], c1 = s.cnt[2 * tid + 1];
@@ -70,18 +97,15 @@ __device__ inline void rank_emit(RankLds& s, u32 n, u32 k, float* r, int32_t* oi
   (void)block_exclusive_sum<NT>((b0 < k ? c0 : 0u) + (b0 + c0 < k ? c1 : 0u), s.scan, E);
   for (u32 i = tid; i < n; i += NT) {
     const u64 pv = s.list[i];
-    const u32 sb = sub(key_of_bits((u32)(pv >> 32)));
+    const u32 sb = sub(rkey(pv));
     const u32 a = s.start[sb];
     if (a < k) s.tmp[a + atomicAdd(&s.cur[sb], 1u)] = pv;
   }
   __syncthreads();
-  auto rkey = [](u64 pv) {
-    return ((u64)(0x7FFFFFFFu - key_of_bits((u32)(pv >> 32))) << 32) | (u64)(u32)pv;
-  };
   for (u32 p = tid; p < E; p += NT) {
     const u64 pv = s.tmp[p];
     const u64 me = rkey(pv);
-    const u32 sb = sub(key_of_bits((u32)(pv >> 32)));
+    const u32 sb = sub(me);
     const u32 a = s.start[sb], c = s.cnt[sb];
     u32 rank = a;
     for (u32 q = a; q < a + c; ++q) rank += rkey(s.tmp[q]) < me ? 1u : 0u;

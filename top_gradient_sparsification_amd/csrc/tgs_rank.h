@@ -30,8 +30,10 @@ struct RankLds {
 // sub-ranges of the span of the rank keys ((0x7FFFFFFF - key) << 32 |
 // index), which keeps only the sub-ranges that start below rank k, then each
 // entry's rank inside its sub-range by counting the entries of the sub-range
-// before it;
-// the emitted entries' residual becomes +0.  Every thread calls it.
+// before it; the emitted entries' residual becomes +0.  With np > 1 only the
+// entries of sub-ranges [part kRankBins / np, (part + 1) kRankBins / np) are
+// emitted (np workgroups that order the same entries then emit them all
+// between them).  Every thread calls it.
 // 64-bit minimum and maximum over the wave (every lane gets them).
 __device__ __forceinline__ u64 wave_min64(u64 v) {
 #pragma unroll
@@ -50,7 +52,8 @@ __device__ __forceinline__ u64 wave_max64(u64 v) {
   return v;
 }
 
-__device__ inline void rank_emit(RankLds& s, u32 n, u32 k, float* r, int32_t* oi, float* ov) {
+__device__ inline void rank_emit(RankLds& s, u32 n, u32 k, float* r, int32_t* oi, float* ov, u32 part = 0,
+                                 u32 np = 1) {
   constexpr int NT = kRankThreads;
   const int tid = threadIdx.x;
   // the rank order of an entry: (key desc, index asc), unique
@@ -102,7 +105,10 @@ __device__ inline void rank_emit(RankLds& s, u32 n, u32 k, float* r, int32_t* oi
     if (a < k) s.tmp[a + atomicAdd(&s.cur[sb], 1u)] = pv;
   }
   __syncthreads();
-  for (u32 p = tid; p < E; p += NT) {
+  // this workgroup's share of the places [0, E): whole sub-ranges
+  const u32 lo = part == 0 ? 0u : std::min(E, s.start[part * kRankBins / np]);
+  const u32 hi = part + 1 >= np ? E : std::min(E, s.start[(part + 1) * kRankBins / np]);
+  for (u32 p = lo + tid; p < hi; p += NT) {
     const u64 pv = s.tmp[p];
     const u64 me = rkey(pv);
     const u32 sb = sub(me);

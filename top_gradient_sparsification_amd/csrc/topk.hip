@@ -122,6 +122,8 @@ constexpr int64_t kGuideMinN = (int64_t)1 << 18;  // smaller vectors take the pl
 constexpr int kRkBuckets = 1024;   // buckets of the bucketed ranking at most (one ranking workgroup each)
 constexpr int64_t kRkMinK = 32768; // the bucketed ranking serves k from this on
 constexpr int kRkStage = 12288;    // candidates one accumulate workgroup stages in LDS (its region)
+constexpr u32 kRkPart = 3072;      // a bucket above this many entries is shared by several ranking workgroups
+constexpr u32 kRkMaxParts = 4;     // ... at most this many
 static_assert(kRkBuckets <= kRankThreads, "one bucket total per ranking thread");
 constexpr u32 kWhyPlan = 1u, kWhyBucket = 4u, kWhyFew = 8u, kWhyRegion = 16u, kWhyList = 32u, kWhyWait = 64u;
 
@@ -1182,14 +1184,16 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_pass(AccArgs a) {
 // ------------------------------------------------------------- k_guess ----
 // Guess of the first-level bin that holds the k-th key, from a sample of
 // chunks of 256 consecutive entries (one float4 per lane) spread over the
-// 16-byte aligned part of the vector.  The guessed bin
-// is the highest one whose bins and those above it hold at least c_req sample
-// entries, c_req being the expected sample count above the k-th key plus six
-// standard deviations of its Poisson noise: the whole vector then holds at
-// least k entries in those bins except with negligible probability.  A guess
-// whose bins would hold more than s_max sample entries (more candidates than
-// the regions can take) is dropped.  The guess shapes only how much work the
-// later passes do; whether it held is checked against the exact histogram.
+// 16-byte aligned part of the vector.  The guessed bin is the highest one
+// whose bins and those above it hold at least c_req sample entries, c_req
+// being the expected sample count above the k-th key plus six standard
+// deviations of its Poisson noise: the whole vector then holds at least k
+// entries in those bins except with negligible probability.  A guess whose
+// bins would hold more than s_max sample entries (more candidates than the
+// regions can take) is dropped.  For the bucketed ranking (rk_tab set) the
+// last workgroup also builds the bucket table.  The guess shapes only how
+// much work the later passes do; whether it held is checked against exact
+// counts.
 struct GuessArgs {
   const v4f* grad;      // the aligned parts (grad + head, residual + head)
   const v4f* residual;
@@ -1218,9 +1222,11 @@ __global__ __launch_bounds__(kGuessThreads) void k_guess(GuessArgs a) {
 #pragma unroll
   for (int u = 0; u < kGuessUnroll; ++u) {
     const int64_t c = c0 + u * W;
-    const int64_t i = (c < a.chunks ? c : 0) * a.stride + lane;
-    gq[u] = __builtin_nontemporal_load(a.grad + i);
-    rq[u] = __builtin_nontemporal_load(a.residual + i);
+    if (c < a.chunks) {
+      const int64_t i = c * a.stride + lane;
+      gq[u] = __builtin_nontemporal_load(a.grad + i);
+      rq[u] = __builtin_nontemporal_load(a.residual + i);
+    }
   }
 #pragma unroll
   for (int u = 0; u < kGuessUnroll; ++u)
@@ -1238,10 +1244,14 @@ __global__ __launch_bounds__(kGuessThreads) void k_guess(GuessArgs a) {
   if (tid == 0) s_last = add_agent_acqrel(&a.hh->done, 1u) == gridDim.x - 1 ? 1u : 0u;
   __syncthreads();
   if (!s_last) return;
-  // last workgroup: every other one has added its histogram
+  // last workgroup: every other one has added its histogram (read coalesced
+  // into LDS: strided device-scope loads would each fetch a line for a few
+  // words)
   static_assert(NT * 2 == 2048, "two bins per thread");
+  for (int i = tid; i < 2048; i += NT) s_h[i] = ld_agent(&a.hh->hist[i]);
+  __syncthreads();
   const int hi = 2047 - 2 * tid;  // this thread's bins, from the top: hi, hi - 1
-  const u32 h1 = ld_agent(&a.hh->hist[hi]), h0 = ld_agent(&a.hh->hist[hi - 1]);
+  const u32 h1 = s_h[hi], h0 = s_h[hi - 1];
   u32 tot;
   const u32 above = block_exclusive_sum<NT>(h1 + h0, s_scan, tot);
   if (tid == 0) s_pick = 0u;  // no bin reaches c_req: every bin
@@ -1252,8 +1262,6 @@ __global__ __launch_bounds__(kGuessThreads) void k_guess(GuessArgs a) {
   // sample entries in the bins >= pick
   const u32 mine = (u32)hi >= pick ? h1 : 0u, mine0 = (u32)(hi - 1) >= pick ? h0 : 0u;
   const u32 kept = block_sum<NT>(mine + mine0, s_scan);
-  st_agent(&a.hh->hist[hi], 0u);
-  st_agent(&a.hh->hist[hi - 1], 0u);
   if (a.rk_tab) {
     // The bucketed ranking's buckets, numbered from the top: bin j >= pick is
     // cut into s_j equal sub-ranges of its 2^20 keys, s_j the sample entries
@@ -1280,6 +1288,8 @@ __global__ __launch_bounds__(kGuessThreads) void k_guess(GuessArgs a) {
       ctl->rk_ovf = 0u;
     }
   }
+  // the histogram left zero (coalesced, after the workgroup's last barrier)
+  for (int i = tid; i < 2048; i += NT) st_agent(&a.hh->hist[i], 0u);
   if (tid == 0) {
     st_agent(&ctl->guide_bin, kept <= a.s_max ? pick : kNoGuide);
     st_agent(&ctl->guide_ovf, 0u);
@@ -1298,11 +1308,14 @@ __global__ __launch_bounds__(kGuessThreads) void k_guess(GuessArgs a) {
 // a DPP scan over its lanes, so waves never wait for each other.  k_general
 // ranks them by (key desc, index asc) itself.
 //
-// With DYN false row t goes to workgroup t mod G.  With DYN true (long
-// vectors) rows go out in pairs: workgroup b takes pair b and then the pairs
-// a ticket hands out (G + the ticket's count), one pair ahead: the
-// workgroups then stay on one short stretch of memory however their speeds
-// differ, where a fixed deal lets the slower ones fall behind and finish last.
+// Rows go out in pairs.  With DYN true (long vectors) workgroup b takes
+// pair b and then the pairs a ticket hands out (G + the ticket's count), one
+// pair ahead: the workgroups then stay on one short stretch of memory however
+// their speeds differ, where a fixed deal lets the slower ones fall behind and
+// finish last.  With DYN false the first nstatic pairs of each workgroup are
+// dealt (b, b + G, ...) and only the last few come from the ticket, which
+// then evens out the workgroups' finish (the dies' speeds differ by several
+// percent) without queueing on its atomic.
 //
 // With BKT (the bucketed ranking) the candidates are staged in LDS instead
 // (the same wave-wise placement) and, at the end, written to the
@@ -1324,7 +1337,8 @@ struct GuidedArgs {
   u32* guide_cnt;      // [gridDim.x] candidates each workgroup found (above cap: its region overflowed)
   u64* cand;           // workgroup b's region: cand + b * cap
   u32 cap;
-  u32* ticket;         // zero at the start (DYN)
+  u32* ticket;         // zero at the start
+  int64_t nstatic;     // row pairs each workgroup is dealt before it takes them from the ticket (>= 1)
   // BKT
   const u32* rk_tab;   // [2048] first bucket of bin j << 16 | its buckets
   const u32* rk_count; // buckets
@@ -1335,7 +1349,7 @@ struct GuidedArgs {
   u32 rk_cap;          // candidates staged at most (kRkStage; less to test)
 };
 
-// Bucket of a candidate key under the bucketed ranking's table.
+// Bucket of a candidate key under the bucketed ranking's table (k_guess).
 __device__ __forceinline__ u32 rk_bucket(const u32* tab, u32 key) {
   const u32 t = tab[key >> 20], base = t >> 16, sj = t & 0xFFFFu;
   return sj ? base + (u32)(((u64)(0xFFFFFu - (key & 0xFFFFFu)) * sj) >> 20) : (base ? base - 1u : 0u);
@@ -1364,10 +1378,19 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_guided(GuidedArgs a) {
     for (int i = tid; i < kRkBuckets; i += NT) s_bc[i] = 0u;
   }
   const int64_t nrows = (a.nv + NT - 1) / NT, npairs = (nrows + 1) / 2, G = gridDim.x;
-  int64_t nn = 0;  // thread 0 (DYN): the pair after the next one
-  if (DYN && tid == 0) {
-    s_next = G + (int64_t)add_agent_relaxed(a.ticket, 1u);
-    nn = G + (int64_t)add_agent_relaxed(a.ticket, 1u);
+  // Row pair j of this workgroup: b + j G while j < nstatic, then the next
+  // one the ticket hands out (pairs nstatic G, nstatic G + 1, ...), so the
+  // workgroups that stream faster take more of the last pairs.  Thread 0
+  // fetches one pair ahead.
+  const int64_t S = a.nstatic;
+  int64_t jn = 1, nn = 0;  // thread 0: the next pair's number j, and the pair after the next one
+  auto fetch = [&]() -> int64_t {
+    const int64_t j = jn++;
+    return j < S ? (int64_t)blockIdx.x + j * G : S * G + (int64_t)add_agent_relaxed(a.ticket, 1u);
+  };
+  if (tid == 0) {
+    s_next = fetch();
+    nn = fetch();
   }
   __syncthreads();
   u64* const reg = a.cand + (size_t)blockIdx.x * a.cap;
@@ -1423,7 +1446,17 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_guided(GuidedArgs a) {
     m4 = 0;
     if (t < nrows && i < a.nv) {
       const v4f acc = rr + gg;
-      __builtin_nontemporal_store(acc, rv + i);
+      // Without DYN (below about 2^25 entries, a residual of at most 128
+      // MiB) the stores allocate in the caches: the residual then stays in
+      // the 256 MB Infinity Cache, and the selected entries' scattered +0
+      // stores that follow merge into cached lines instead of each costing
+      // a read-modify-write of HBM (2% of 25.6M entries: 28 -> 21 us of
+      // ranking).  A longer vector streams with the non-temporal hint: its
+      // residual would only push out lines still to be read.
+      if (DYN)
+        __builtin_nontemporal_store(acc, rv + i);
+      else
+        rv[i] = acc;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         bq[e] = __float_as_uint(acc[e]);
@@ -1433,15 +1466,14 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_guided(GuidedArgs a) {
       }
     }
   };
-  // unit u: rows 2u and 2u + 1 (DYN), or rows u and u + G (units u = b,
-  // b + 2G, ...)
-  auto row0 = [&](int64_t u) { return DYN ? 2 * u : u; };
-  auto row1 = [&](int64_t u) { return DYN ? 2 * u + 1 : u + G; };
-  const int64_t nunits = DYN ? npairs : nrows;
+  // unit u: rows 2u and 2u + 1
+  auto row0 = [&](int64_t u) { return 2 * u; };
+  auto row1 = [&](int64_t u) { return 2 * u + 1; };
+  const int64_t nunits = npairs;
   v4f ga, ra, gb, rb;
   u32 m4, bq[4] = {0u, 0u, 0u, 0u};
-  int64_t u = blockIdx.x;                    // this unit
-  int64_t un = DYN ? s_next : u + 2 * G;     // the next one
+  int64_t u = blockIdx.x;  // this unit
+  int64_t un = s_next;     // the next one
   load(row0(u), ga, ra);
   load(row1(u), gb, rb);
   while (u < nunits) {
@@ -1452,17 +1484,13 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_guided(GuidedArgs a) {
     load(row1(un), gb, rb);
     if (guide) place(m4, a.head + 4 * (row1(u) * NT + tid), bq);
     u = un;
-    if (DYN) {
-      __syncthreads();  // every thread has read s_next
-      if (tid == 0) {
-        s_next = nn;
-        if (nn < npairs) nn = G + (int64_t)add_agent_relaxed(a.ticket, 1u);
-      }
-      __syncthreads();
-      un = s_next;
-    } else {
-      un = u + 2 * G;
+    __syncthreads();  // every thread has read s_next
+    if (tid == 0) {
+      s_next = nn;
+      if (nn < npairs) nn = fetch();
     }
+    __syncthreads();
+    un = s_next;
   }
   if (blockIdx.x == gridDim.x - 1 && tid < kWave) {
     const int64_t i = a.head + 4 * a.nv + tid;
@@ -1528,7 +1556,7 @@ struct RankArgs {
 __global__ __launch_bounds__(kRankThreads) void k_rank(RankArgs a) {
   __shared__ RankLds s;
   __shared__ u32 s_pre[kRkBuckets];
-  __shared__ u32 s_max;
+  __shared__ u32 s_max, s_item;
   const int tid = threadIdx.x;
   const u32 B = a.ctl->rk_count;
   const u32 v = (u32)tid < B ? a.tot[tid] : 0u;
@@ -1544,10 +1572,21 @@ __global__ __launch_bounds__(kRankThreads) void k_rank(RankArgs a) {
     atomicAdd(ok ? &a.ctl->rk_used : &a.ctl->rk_missed, 1u);
   }
   if (!ok) return;
-  // buckets b = blockIdx.x, + gridDim.x, ...
-  for (u32 b = blockIdx.x; b < B; b += gridDim.x) {
+  // Work items, bucket after bucket: a bucket of more than kRkPart entries
+  // is shared by several workgroups (at most kRkMaxParts), each of which
+  // gathers and orders the whole bucket but emits only its share of it, so
+  // that one large bucket does not leave its workgroup storing long after
+  // the others.  Thread b holds bucket b's items [ip, ip + parts).  Items
+  // it = blockIdx.x, + gridDim.x, ...
+  const u32 parts = (u32)tid < B ? std::min<u32>(kRkMaxParts, std::max<u32>(1u, (v + kRkPart - 1) / kRkPart)) : 0u;
+  u32 nitems;
+  const u32 ip = block_exclusive_sum<kRankThreads>(parts, s.scan, nitems);
+  for (u32 it = blockIdx.x; it < nitems; it += gridDim.x) {
+    if (ip <= it && it < ip + parts) s_item = (u32)tid << 8 | (it - ip) << 4 | parts;
+    __syncthreads();
+    const u32 b = s_item >> 8, part = (s_item >> 4) & 15u, np = s_item & 15u;
     const u32 start = s_pre[b];
-    if ((int64_t)start >= a.k) break;  // (so does every later bucket)
+    if ((int64_t)start >= a.k) break;  // (so does every later item)
     const u32 nb = a.tot[b];
     const u32 kk = (u32)std::min<int64_t>(nb, a.k - start);
     // bucket b's entries from the accumulate workgroups' regions (thread w:
@@ -1566,8 +1605,8 @@ __global__ __launch_bounds__(kRankThreads) void k_rank(RankArgs a) {
         if (e0 + j < c) s.list[at + e0 + j] = e[j];
     }
     __syncthreads();
-    rank_emit(s, nb, kk, a.residual, a.out_idx + start, a.out_val + start);
-    __syncthreads();  // s is reused by the next bucket
+    rank_emit(s, nb, kk, a.residual, a.out_idx + start, a.out_val + start, part, np);
+    __syncthreads();  // s and s_item are reused by the next item
   }
 }
 
@@ -2915,8 +2954,9 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
         q.rk_tot = (u32*)(ws + L.rk_tot);
         q.rk_samples = (float)std::max(1e-3, f * (double)L.rk_target);
       }
-      const int gq = (int)std::min<int64_t>(kGuessBlocks, (chunks + (kGuessThreads / kWave) * kGuessUnroll - 1) /
-                                                              ((kGuessThreads / kWave) * kGuessUnroll));
+      // one chunk per wave where the workgroups allow: a compute unit
+      // fetches only so fast, and the sample's loads are all the work
+      const int gq = (int)std::min<int64_t>(kGuessBlocks, (chunks + kGuessThreads / kWave - 1) / (kGuessThreads / kWave));
       hipLaunchKernelGGL(k_guess, dim3(gq), dim3(kGuessThreads), 0, stream, q);
       GuidedArgs g{};
       g.grad = grad;
@@ -2936,6 +2976,11 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
       // the ticket's hand-out pays from about 32 rows per workgroup on
       const int64_t rows = (nv + kAccThreads - 1) / kAccThreads;
       const bool dyn = rows >= 32 * (int64_t)G1;
+      // A long vector takes every pair after the first from the ticket; a
+      // shorter one deals all but about the last two pairs of each
+      // workgroup, so the ticket's atomic is rare enough not to queue.
+      const int64_t pairs = (rows + 1) / 2;
+      g.nstatic = dyn ? 1 : std::max<int64_t>(1, pairs / G1 - 2);
       if (bucketed) {
         g.rk_tab = q.rk_tab;
         g.rk_count = &ctl->rk_count;

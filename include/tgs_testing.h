@@ -50,7 +50,10 @@ extern "C" {
  *                       stage one candidate each: they overflow and the
  *                       general path selects from acc,
  *                       13 = no bucketed ranking: the guided general path
- *                       ranks the copied candidates itself.
+ *                       ranks the copied candidates itself,
+ *                       14 = rTop-k: the pick's last workgroup selects over
+ *                       the candidates in device memory instead of LDS (the
+ *                       top-r step runs as with 0).
  *                       The guided path needs n >= 2^18, grad and residual
  *                       equally aligned modulo 16 bytes and k > 0; otherwise
  *                       7-9 run the plain general path.

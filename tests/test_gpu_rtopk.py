@@ -61,6 +61,23 @@ def test_guided_top_r(tgs_gpu):
                           "r=%d k=%d" % (r, k))
 
 
+@pytest.mark.parametrize("path", [0, 14])
+def test_pick_routes(tgs_gpu, path):
+    """A large top r (bucketed ranking) with hundreds of candidates at the
+    pick's cut, the cut selected in LDS (0) or over the candidates in device
+    memory (14); also k = 1, k = r - 1 and k = r."""
+    rng = np.random.default_rng(9)
+    n = 4_194_304
+    grad, res = make("mixture", n, rng)
+    try:
+        tgs_gpu.set_option(tgs_gpu.OPT_TOPK_PATH, path)
+        for r, k in ((1_000_000, 400_000), (70_000, 1), (70_000, 69_999), (5_000, 5_000)):
+            assert_topk_equal(run_gpu(tgs_gpu, grad, res, r, k, 3, 9), run_oracle(grad, res, r, k, 3, 9),
+                              "path=%d r=%d k=%d" % (path, r, k))
+    finally:
+        tgs_gpu.set_option(tgs_gpu.OPT_TOPK_PATH, 0)
+
+
 def test_small_config_three_chained_steps(tgs_gpu):
     """n = 1,048,576, N(0, 1) gradients, k = 1,048 (0.1%) of r = 2k, three
     chained steps (step number in the counter) from a zero residual."""

@@ -104,7 +104,7 @@ def test_invalid_arguments_fail_before_any_launch(lib):
                              vp(0xC00000), vp(0xB00000), 1 << 30, None)
     assert st == -1
     assert lib.tgs_status_string(-2).startswith(b"TGS_EWORKSPACE")
-    assert lib.tgs_set_option(1, 14) == -1
+    assert lib.tgs_set_option(1, 15) == -1
     assert lib.tgs_set_option(99, 0) == -1
 
 

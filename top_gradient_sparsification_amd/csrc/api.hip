@@ -81,7 +81,7 @@ extern "C" const char* tgs_last_error(void) { return t_last_error; }
 extern "C" tgs_status tgs_set_option(int32_t option, int64_t value) {
   switch (option) {
     case TGS_OPT_TOPK_PATH:
-      if (value < 0 || value > 13) return fail(TGS_EINVAL, "TGS_OPT_TOPK_PATH takes 0 .. 13");
+      if (value < 0 || value > 14) return fail(TGS_EINVAL, "TGS_OPT_TOPK_PATH takes 0 .. 14");
       t_opt_path = value;
       return TGS_OK;
     case TGS_OPT_MAIN_GRID:

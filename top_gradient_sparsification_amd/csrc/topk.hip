@@ -2805,7 +2805,8 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
   StepCtl* ctl = (StepCtl*)(ws + L.ctl);
   GenState* gs = (GenState*)(ws + L.gstate);
 
-  const int path = (int)get_option(TGS_OPT_TOPK_PATH);
+  int path = (int)get_option(TGS_OPT_TOPK_PATH);
+  if (path == 14) path = 0;  // (an option of rTop-k's pick)
   const int64_t gopt = get_option(TGS_OPT_MAIN_GRID);
   const bool vec = (((uintptr_t)grad) & 15u) == (((uintptr_t)residual) & 15u);
   // vector mode: up to 63 scalar entries first, so that the float4 part of

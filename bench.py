@@ -254,11 +254,11 @@ def parse():
 # the 256 MiB copy of --copy-calibration.  Valid only for the k_step
 # source they were taken on: `source_sha256` is the hash of csrc/topk.hip then.
 MEASURED_TRAFFIC = {
-    "source_sha256": "6ed5e7adf71d1df7c3fea4fcb90bfadbe44943a3b9042027a966de24e27037af",
-    # FETCH_SIZE 102,915.9 KiB x (262,144 / 131,085.9: the copy's true read over its counter)
-    "fetch_bytes": 210749467,
-    # WRITE_SIZE 102,793.2 KiB x 1.0 (the copy's counter read exactly 262,144 KiB)
-    "write_bytes": 105260256,
+    "source_sha256": "802de778c28a4df5773939c9a6d8e81af948db2508601d435c82dca56d96b37c",
+    # FETCH_SIZE 102,916.2 KiB x (262,144 / 131,083.5: the copy's true read over its counter)
+    "fetch_bytes": 210753925,
+    # WRITE_SIZE 102,793.3 KiB x 1.0 (the copy's counter read exactly 262,144 KiB)
+    "write_bytes": 105260352,
 }
 
 

@@ -30,11 +30,15 @@ on the same workload (its residual history built by the oracle itself).
     python bench.py --workload NAME [--steps K]
 
 times one of the other workloads instead (names below; no cpu_baseline).
-Before every timed call the residual is restored from a copy holding its
-error-feedback history and, for vectors below 200M entries, a 512 MiB buffer
-is written to push the inputs out of the Infinity Cache; an event pair on the
-call's stream times each call.  `roofline` then covers the whole call (every
-kernel of it) against its algorithmic bytes:
+The timed calls run back to back in spans of 4 between HIP events, as the
+headline's launches do, on the workload's gradients and 4 copies of its
+residual (each holding its error-feedback history) in turn, so that no call
+finds its inputs in the 256 MB Infinity Cache; the line reports the median
+span's time per call.  From 200M entries on (no cache holds the vectors)
+each call is timed by an event pair of its own, on one gradient with the
+residual restored before it; so is the merge, whose inputs (7.6 MB) would
+stay cached whatever the rotation, after a 512 MiB buffer is written.  `roofline` then covers the
+whole call (every kernel of it) against its algorithmic bytes:
     topk_n25.6M_2%, topk_n25.6M_0.02%   the 25.6M mixture at k = 512,000 / 5,120
                                         (residual after 5 steps at that density)
     topk_n138M_0.1%                     138M VGG-16-sized mixture, whole vector,
@@ -110,18 +114,18 @@ def run_other(args):
     from top_gradient_sparsification_amd import workloads
 
     kind, n, par, mix, cfg, prior = OTHER[args.workload]
+    big = False  # (large vectors: timed call by call)
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     if args.copy_calibration:
         copy_calibration(dev)
-    flush = torch.empty(128 << 20, dtype=torch.float32, device=dev) if n < 200_000_000 or kind == "gtopk" else None
+    flush = torch.empty(128 << 20, dtype=torch.float32, device=dev) if kind == "gtopk" else None
     print("bench: preparing %s" % args.workload, file=sys.stderr, flush=True)
     if kind == "gtopk":
         P, k = 32, 25_600
         gi, gv = workloads.gtopk_sets(P=P, k=k, n=n, hot=51_200)
         ti, tv = torch.from_numpy(gi).to(dev), torch.from_numpy(gv).to(dev)
         ws = torch.zeros(tgs.gtopk_workspace_bytes(P, k, n), dtype=torch.uint8, device=dev)
-        restore = lambda: None
         call = lambda: tgs.gtopk_merge(ti, tv, n, ws=ws, check=False)
         nbytes, elems, what = 8.0 * P * k + 8.0 * k + P * k, P * k, "pairs merged"
     else:
@@ -134,7 +138,7 @@ def run_other(args):
             ov = torch.empty(cap, dtype=torch.float32, device=dev)
             cnt = torch.zeros(1, dtype=torch.int64, device=dev)
             ws = torch.zeros(tgs.threshold_workspace_bytes(n), dtype=torch.uint8, device=dev)
-            one = lambda g: tgs.threshold_ef_step(g, resid, par, cap, out_idx=oi, out_val=ov, count=cnt, ws=ws)
+            one = lambda g, r: tgs.threshold_ef_step(g, r, par, cap, out_idx=oi, out_val=ov, count=cnt, ws=ws)
         elif kind == "estimate":
             import math
             m = EST_SAMPLES
@@ -149,37 +153,53 @@ def run_other(args):
             lam = torch.zeros(1, dtype=torch.float32, device=dev)
             ws = torch.zeros(max(tgs.threshold_estimate_workspace_bytes(m), tgs.threshold_workspace_bytes(n)),
                              dtype=torch.uint8, device=dev)
-            one = lambda g: tgs.estimated_threshold_ef_step(g, resid, sample, q, cap, out_idx=oi, out_val=ov,
-                                                            count=cnt, d_lambda=lam, ws=ws)
+            one = lambda g, r: tgs.estimated_threshold_ef_step(g, r, sample, q, cap, out_idx=oi, out_val=ov,
+                                                               count=cnt, d_lambda=lam, ws=ws)
         elif kind == "rtopk":
             k_r = workloads.k_for_density(n, par)
             r_r = 2 * k_r
             oi = torch.empty(k_r, dtype=torch.int32, device=dev)
             ov = torch.empty(k_r, dtype=torch.float32, device=dev)
             ws = torch.zeros(tgs.rtopk_workspace_bytes(n, r_r, k_r), dtype=torch.uint8, device=dev)
-            one = lambda g: tgs.rtopk_ef_step(g, resid, r_r, k_r, 0x5EED, 6, out_idx=oi, out_val=ov, ws=ws)
+            one = lambda g, r: tgs.rtopk_ef_step(g, r, r_r, k_r, 0x5EED, 6, out_idx=oi, out_val=ov, ws=ws)
         elif kind == "segments":
             sizes = workloads.segments_log_uniform(n)
             offs = np.concatenate([[0], np.cumsum(sizes)])
             seg = tgs.TopkSegments(offs, [workloads.k_for_density(int(sz), par) for sz in sizes], dev)
-            one = lambda g: seg(g, resid)
+            one = lambda g, r: seg(g, r)
         else:
             run = tgs.TopkStep(n, workloads.k_for_density(n, par), dev)
-            one = lambda g: run(g, resid)
+            one = lambda g, r: run(g, r)
         for j in range(prior):  # the residual's error-feedback history
-            one(grads[j])
+            one(grads[j], resid)
+        # Below 200M entries the timed calls take the gradients and R copies
+        # of the residual in turn, so that between two uses of a buffer the
+        # other calls move well over the 256 MB Infinity Cache through it.
+        # Larger vectors (no cache holds them) are timed call by call on one
+        # gradient and the residual restored before each call: cycling
+        # through tens of GB of buffers adds address-translation misses a
+        # training loop does not have, and feeding one gradient again and
+        # again would leave the residual far from an error-feedback state.
+        big = n >= 200_000_000
+        if big:
+            del grads[:prior]
+        else:
+            while len(grads) < 4:
+                grads.append(workloads.mixture_gpu(n, sigma, p_out, b_out, (cfg, 200, len(grads)), device=dev))
+        R = 1 if big else 4
+        resids = [resid] + [resid.clone() for _ in range(R - 1)]
+        state = {"i": 0}
+
+        def call():
+            i = state["i"]
+            state["i"] = i + 1
+            one(grads[i % len(grads)], resids[i % R])
+
         pristine = resid.clone()
-        g_last = grads[prior]
-        del grads[:prior]
-
-        def restore():
-            resid.copy_(pristine)
-
-        call = lambda: one(g_last)
+        restore = lambda: resid.copy_(pristine)
         elems, what = n, "gradient elements"
         if kind in ("threshold", "estimate"):
-            restore()
-            one(g_last)
+            one(grads[-1], resid)  # (a large vector's residual is restored before every timed call)
             torch.cuda.synchronize()
             c = int(cnt.item())
             nbytes = 12.0 * n + 8.0 * min(c, cap) + 8.0
@@ -189,23 +209,56 @@ def run_other(args):
             nbytes = 12.0 * n + 8.0 * sum(workloads.k_for_density(int(sz), par) for sz in sizes)
         else:  # top-k and rTop-k: read grad and residual, write residual and k pairs
             nbytes = 12.0 * n + 8.0 * workloads.k_for_density(n, par)
-    for _ in range(3):  # warm-up calls
-        restore()
-        call()
-    torch.cuda.synchronize()
     K = max(1, args.steps if args.steps != 64 else (20 if n < 1_000_000_000 else 5))
     times = []
     print("bench: timing %d calls" % K, file=sys.stderr, flush=True)
-    for _ in range(K):
-        restore()
-        if flush is not None:
-            flush.fill_(1.0)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        call()
-        e1.record(stream)
+    if kind == "gtopk" or big:
+        # an event pair around each call: the merge's inputs (7.6 MB: no
+        # rotation of buffers could keep them out of the cache) pushed out
+        # before it; a large vector's residual restored before it
+        for _ in range(3):  # warm-up calls
+            if big:
+                restore()
+            call()
         torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1))
+        for _ in range(K):
+            if big:
+                restore()
+            else:
+                flush.fill_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        timing = "HIP event pair per call (median of %d); %s between calls" % (
+            K, "the residual restored" if big else "the cache flushed")
+    else:
+        # spans of back-to-back calls, as for the headline: events after call
+        # 0 (which also waits for the host to issue it onto the idle GPU) and
+        # after every `span` calls; the median span's time per call
+        for _ in range(3):  # warm-up calls
+            call()
+        torch.cuda.synchronize()
+        span = 4 if K >= 8 else K
+        nspan = max(1, K // span)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(nspan + 1)]
+        for e in ev:
+            e.record(stream)
+        torch.cuda.synchronize()
+        call()
+        ev[0].record(stream)
+        for j in range(nspan):
+            for _ in range(span):
+                call()
+            ev[j + 1].record(stream)
+        torch.cuda.synchronize()
+        times = [ev[j].elapsed_time(ev[j + 1]) / span for j in range(nspan)]
+        K = nspan * span
+        timing = ("HIP events around %d spans of %d back-to-back calls (after one untimed call), the "
+                  "median span's time per call; the calls take %d residual copies and %d gradients in turn"
+                  % (nspan, span, R, len(grads)))
     times.sort()
     med = times[len(times) // 2]
     gbps = nbytes / (med * 1e-3) / 1e9
@@ -222,8 +275,7 @@ def run_other(args):
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": gbps / HBM_PEAK_GBPS, "traffic": None, "kernel": "whole call (all its kernels)",
                      "bytes_per_launch": nbytes,
-                     "timing": "HIP event pair per call (median of %d); residual restored and the cache flushed "
-                               "between calls" % K},
+                     "timing": timing},
         "cpu_baseline": None,
     }
     if kind in ("threshold", "estimate"):
@@ -254,11 +306,11 @@ def parse():
 # the 256 MiB copy of --copy-calibration.  Valid only for the k_step
 # source they were taken on: `source_sha256` is the hash of csrc/topk.hip then.
 MEASURED_TRAFFIC = {
-    "source_sha256": "802de778c28a4df5773939c9a6d8e81af948db2508601d435c82dca56d96b37c",
-    # FETCH_SIZE 102,916.2 KiB x (262,144 / 131,083.5: the copy's true read over its counter)
-    "fetch_bytes": 210753925,
-    # WRITE_SIZE 102,793.3 KiB x 1.0 (the copy's counter read exactly 262,144 KiB)
-    "write_bytes": 105260352,
+    "source_sha256": "b23148033f5bbda264bda6b660f5de41a19a5e594fbd2ee65cca4d2421415d9b",
+    # FETCH_SIZE 102,915.4 KiB x (262,144 / 131,083.5: the copy's true read over its counter)
+    "fetch_bytes": 210752325,
+    # WRITE_SIZE 102,793.1 KiB x 1.0 (the copy's counter read exactly 262,144 KiB)
+    "write_bytes": 105260176,
 }
 
 

@@ -178,7 +178,7 @@ struct StepCtl {
   u32 mid_exact;      // batched layer-wise segments selected exactly from acc (never reset)
   u32 rk_count;       // bucketed ranking: buckets of this call (0: none), set by k_guess
   u32 rk_ok;          // 1 once the bucketed ranking has emitted the step (k_general then exits)
-  u32 rk_ovf;         // set when a workgroup's slots of a bucket overflowed
+  u32 rk_ovf;         // set when an accumulate workgroup's stage of candidates overflowed
   u32 rk_used;        // calls whose bucketed ranking held (never reset)
   u32 rk_missed;      // calls whose bucketed ranking did not hold: k_general ran (never reset)
   u32 pad1[49];
@@ -1446,17 +1446,10 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_guided(GuidedArgs a) {
     m4 = 0;
     if (t < nrows && i < a.nv) {
       const v4f acc = rr + gg;
-      // Without DYN (below about 2^25 entries, a residual of at most 128
-      // MiB) the stores allocate in the caches: the residual then stays in
-      // the 256 MB Infinity Cache, and the selected entries' scattered +0
-      // stores that follow merge into cached lines instead of each costing
-      // a read-modify-write of HBM (2% of 25.6M entries: 28 -> 21 us of
-      // ranking).  A longer vector streams with the non-temporal hint: its
-      // residual would only push out lines still to be read.
-      if (DYN)
-        __builtin_nontemporal_store(acc, rv + i);
-      else
-        rv[i] = acc;
+      // (non-temporal: stores that allocate in the caches leave the next
+      // call a residual's worth of dirty lines to write back, which costs
+      // more than the ranking's scattered +0 stores gain from them)
+      __builtin_nontemporal_store(acc, rv + i);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         bq[e] = __float_as_uint(acc[e]);

@@ -36,7 +36,7 @@
 //               set's (and the rows' precondition check: a repeated index
 //               within a row, or one outside [0, n), sets the error word),
 //               and runs of 4096 of the final set sorted by (key desc, index
-//               asc);
+//               asc) with a counting sort in LDS;
 //   k_gt_merge  passes merge the runs; the last one writes the outputs.
 // Slots without a partner keep their data where it is until they are merged:
 // a slot's data is its grouped row until it has been a merge's destination,
@@ -60,6 +60,14 @@ constexpr u32 kSlots = 1u << kLogSlots;
 constexpr int64_t kPartLoad = 2048;  // entries of one set a part holds on average at most
 constexpr int64_t kGtMaxK = (int64_t)1 << 20;
 constexpr u32 kMaxParts = 512;     // parts at k = kGtMaxK
+// The final set is sorted in runs of kRunTile (one workgroup each, a counting
+// sort over kRunBins sub-ranges in LDS), which merge passes then join.  (Runs
+// of 8192 over 1024 sub-ranges, one merge pass fewer, were slower: the
+// final set's keys crowd just above its least, and the count inside a
+// sub-range grows with the square of its size.)
+constexpr int kRunPer = 4;
+constexpr int kRunTile = kRunPer * kSortThreads;
+constexpr int kRunBins = 2048;
 constexpr int kRowPer = 4;
 constexpr int kRowChunk = kRowPer * kGtThreads;  // row entries per workgroup of the row kernels
 constexpr int kJoinPer = 8;        // part entries per thread in flight in k_gt_join
@@ -692,10 +700,11 @@ struct FinalArgs {
 // after them joins row p's entries of its part against the final set's (the
 // mask) and checks them: in [0, n), and no index twice in the row.
 __global__ __launch_bounds__(kGtThreads) void k_gt_final(FinalArgs a) {
+  constexpr int kLds = block_sort_lds(kRunPer, kRunBins);
+  static_assert(kLds <= (int)kSlots, "the sort fits in the two tables' LDS");
   __shared__ u64 s_lds[kSlots];  // the two tables, or the sort's LDS
   __shared__ u32 s_pre[kMaxParts], s_fst[kMaxParts];
   __shared__ u32 s_scan[kGtWaves + 1];
-  static_assert(kSortLds <= (int)kSlots, "the sort fits in the tables' LDS");
   u32* s_key = (u32*)s_lds;      // the final set's part
   u32* s_row = s_key + kSlots;   // the row's part (the repeat check)
   u64* s = s_lds;
@@ -714,11 +723,11 @@ __global__ __launch_bounds__(kGtThreads) void k_gt_final(FinalArgs a) {
     if ((u32)tid < NP) s_pre[tid] = pre;
     __syncthreads();
     const int64_t have = std::min<int64_t>(a.k, total);  // (k, unless the rows broke the preconditions)
-    const int64_t base = (int64_t)blockIdx.x * kSortTile;
-    u64 x[kSortPer];
+    const int64_t base = (int64_t)blockIdx.x * kRunTile;
+    u64 x[kRunPer];
 #pragma unroll
-    for (int c = 0; c < kSortPer; ++c) {
-      const int64_t i = base + kSortPer * tid + c;
+    for (int c = 0; c < kRunPer; ++c) {
+      const int64_t i = base + kRunPer * tid + c;
       x[c] = ~0ull;
       if (i < have) {
         u32 lo = 0, hi = NP;  // the last part whose first entry is at or below i
@@ -730,11 +739,11 @@ __global__ __launch_bounds__(kGtThreads) void k_gt_final(FinalArgs a) {
         x[c] = rank64(a.F[s_fst[lo] + (u32)(i - s_pre[lo])]);
       }
     }
-    block_sort4096(x, s);
-    const bool one = a.k <= kSortTile;
+    block_sort<kRunPer, kRunBins>(x, s);
+    const bool one = a.k <= kRunTile;
 #pragma unroll
-    for (int c = 0; c < kSortPer; ++c) {
-      const int64_t i = base + kSortPer * tid + c;
+    for (int c = 0; c < kRunPer; ++c) {
+      const int64_t i = base + kRunPer * tid + c;
       if (i >= a.k) continue;
       if (one) {
         const Pair e = unrank64(x[c]);
@@ -1024,7 +1033,8 @@ extern "C" tgs_status tgs_gtopk_merge(const int32_t* idx, const float* val, int3
     hipLaunchKernelGGL(k_gt_keep, dim3((unsigned)(nm * NP)), dim3(kGtThreads), 0, stream, ka);
   }
   {
-    const int64_t nruns = (k + kSortTile - 1) / kSortTile;
+    const int64_t nruns = (k + kRunTile - 1) / kRunTile;      // sorted runs
+    const int64_t ntiles = (k + kSortTile - 1) / kSortTile;   // merge workgroups
     FinalArgs fa{};
     fa.P = P;
     fa.k = k;
@@ -1044,7 +1054,7 @@ extern "C" tgs_status tgs_gtopk_merge(const int32_t* idx, const float* val, int3
     fa.err = err;
     hipLaunchKernelGGL(k_gt_final, dim3((unsigned)(nruns + (int64_t)P * NP)), dim3(kGtThreads), 0, stream, fa);
     int cur = 0;
-    for (int64_t Lr = kSortTile; Lr < k; Lr *= 2) {
+    for (int64_t Lr = kRunTile; Lr < k; Lr *= 2) {
       MergeArgs ma{};
       ma.src = (const u64*)(ws + L.runs[cur]);
       ma.dst = (u64*)(ws + L.runs[1 - cur]);
@@ -1053,7 +1063,7 @@ extern "C" tgs_status tgs_gtopk_merge(const int32_t* idx, const float* val, int3
       ma.last = 2 * Lr >= k;
       ma.out_idx = out_idx;
       ma.out_val = out_val;
-      hipLaunchKernelGGL(k_gt_merge, dim3((unsigned)nruns), dim3(kGtThreads), 0, stream, ma);
+      hipLaunchKernelGGL(k_gt_merge, dim3((unsigned)ntiles), dim3(kGtThreads), 0, stream, ma);
       cur = 1 - cur;
     }
   }

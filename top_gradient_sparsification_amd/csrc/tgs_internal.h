@@ -398,7 +398,8 @@ __device__ __forceinline__ void lds_compact(PairAt pair_at, u32 len, u32 t_lo, u
   }
 }
 
-// Bitonic sort of kSortTile 64-bit keys by one workgroup of kSortThreads.
+// Sorted runs of 64-bit keys by one workgroup of kSortThreads; merges of
+// them kSortTile outputs to a workgroup.
 constexpr int kSortTile = 4096;
 constexpr int kSortThreads = 1024;
 constexpr int kSortPer = kSortTile / kSortThreads;
@@ -413,50 +414,110 @@ __device__ __forceinline__ Pair unrank64(u64 r) {
   return Pair{(int32_t)(((u32)r >> 1) & 0x7FFFFFFFu), key | (((u32)r & 1u) << 31)};
 }
 
-__device__ __forceinline__ u64 shfl_xor64(u64 v, int m) {
-  const int lo = __shfl_xor((int)(u32)v, m), hi = __shfl_xor((int)(u32)(v >> 32), m);
-  return ((u64)(u32)hi << 32) | (u64)(u32)lo;
+// 64-bit minimum and maximum over the wave (every lane gets them).
+__device__ __forceinline__ u64 wave_min64(u64 v) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) {
+    const u64 o = ((u64)(u32)__shfl_xor((int)(u32)(v >> 32), m) << 32) | (u64)(u32)__shfl_xor((int)(u32)v, m);
+    v = o < v ? o : v;
+  }
+  return v;
+}
+__device__ __forceinline__ u64 wave_max64(u64 v) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) {
+    const u64 o = ((u64)(u32)__shfl_xor((int)(u32)(v >> 32), m) << 32) | (u64)(u32)__shfl_xor((int)(u32)v, m);
+    v = o > v ? o : v;
+  }
+  return v;
 }
 
-// LDS place of sort element e: one pad word after every 4, so that the 64
-// lanes of a wave, 4 elements apart, fall on different banks.
-__device__ __forceinline__ u32 sort_slot(u32 e) { return e + (e >> 2); }
-constexpr int kSortLds = kSortTile + kSortTile / 4;
+// LDS of block_sort<PER, BINS>, in u64 words: the keys grouped by
+// sub-range, then two tables of BINS counters.
+constexpr int block_sort_lds(int per, int bins) { return per * kSortThreads + bins; }
 
-// Bitonic sort of 4096 keys, ascending; thread t holds elements 4t .. 4t + 3
-// in x.  Partners at distance 1 and 2 are in the same thread, 4 .. 128 in
-// the same wave (lane shuffles), 256 and above in other waves (LDS).
-__device__ inline void block_sort4096(u64 (&x)[kSortPer], u64* lds) {
+// Sorts PER * kSortThreads keys ascending; thread t holds elements PER t ..
+// PER t + PER - 1 in x, and the sorted ones there after the call.  Keys equal
+// to ~0 (padding) must sit at the tail and stay there.  A counting sort of
+// the other keys over BINS equal sub-ranges of their span, then each key's
+// place inside its sub-range by counting the keys there below it (a few to
+// a sub-range, where a bitonic network over 4096 keys takes 78
+// compare-and-exchange stages; equal keys keep the order in which they were
+// grouped).  Every thread calls it.
+template <int PER, int BINS>
+__device__ inline void block_sort(u64 (&x)[PER], u64* lds) {
+  constexpr int NT = kSortThreads, B = BINS, TILE = PER * NT, BPT = B / NT;
+  static_assert(BPT * NT == B && (BPT == 1 || BPT == 2), "one or two sub-ranges per thread");
+  __shared__ u64 s_lo, s_hi;
+  __shared__ u32 s_scan[NT / kWave + 1];
+  u64* keys = lds;                     // [TILE]
+  u32* cnt = (u32*)(lds + TILE);       // [B]: counts, then fill cursors (sub-range ends)
+  u32* start = cnt + B;                // [B]
   const int tid = threadIdx.x;
-  // fully unrolled: every stage's distance is a constant, so the partners
-  // inside a thread are plain registers and the lane masks immediates
+  u64 lo = ~0ull, hi = 0ull;
 #pragma unroll
-  for (u32 size = 2; size <= (u32)kSortTile; size <<= 1) {
-#pragma unroll
-    for (u32 d = size >> 1; d > 0; d >>= 1) {
-      u64 y[kSortPer];
-      if (d >= 4u * kWave) {
-#pragma unroll
-        for (int c = 0; c < kSortPer; ++c) lds[sort_slot(kSortPer * tid + c)] = x[c];
-        __syncthreads();
-#pragma unroll
-        for (int c = 0; c < kSortPer; ++c) y[c] = lds[sort_slot((kSortPer * tid + c) ^ d)];
-        __syncthreads();
-      } else if (d >= (u32)kSortPer) {
-#pragma unroll
-        for (int c = 0; c < kSortPer; ++c) y[c] = shfl_xor64(x[c], (int)(d / kSortPer));
-      } else {
-#pragma unroll
-        for (int c = 0; c < kSortPer; ++c) y[c] = x[c ^ d];
-      }
-#pragma unroll
-      for (int c = 0; c < kSortPer; ++c) {
-        const u32 e = (u32)(kSortPer * tid + c);
-        const bool asc = (e & size) == 0, lower = (e & d) == 0;
-        x[c] = (asc == lower) ? (x[c] < y[c] ? x[c] : y[c]) : (x[c] < y[c] ? y[c] : x[c]);
-      }
+  for (int c = 0; c < PER; ++c)
+    if (x[c] != ~0ull) {
+      lo = x[c] < lo ? x[c] : lo;
+      hi = x[c] > hi ? x[c] : hi;
     }
+  lo = wave_min64(lo);
+  hi = wave_max64(hi);
+  if (tid == 0) {
+    s_lo = ~0ull;
+    s_hi = 0ull;
   }
+  for (int i = tid; i < B; i += NT) cnt[i] = 0u;
+  __syncthreads();
+  if (lane_id() == 0) {
+    atomicMin(&s_lo, lo);
+    atomicMax(&s_hi, hi);
+  }
+  __syncthreads();
+  const u64 base = s_lo;
+  const double scale = s_hi > s_lo ? (double)(B - 1) / (double)(s_hi - s_lo) : 0.0;
+  u32 sb[PER];
+#pragma unroll
+  for (int c = 0; c < PER; ++c) {
+    sb[c] = std::min<u32>((u32)((double)(x[c] - base) * scale), (u32)(B - 1));  // monotone in the key
+    if (x[c] != ~0ull) atomicAdd(&cnt[sb[c]], 1u);
+  }
+  __syncthreads();
+  const u32 c0 = cnt[BPT * tid], c1 = BPT == 2 ? cnt[BPT * tid + 1] : 0u;
+  u32 all;
+  const u32 b0 = block_exclusive_sum<NT>(c0 + c1, s_scan, all);
+  start[BPT * tid] = b0;
+  cnt[BPT * tid] = b0;
+  if (BPT == 2) {
+    start[BPT * tid + 1] = b0 + c0;
+    cnt[BPT * tid + 1] = b0 + c0;
+  }
+  __syncthreads();
+  u32 at[PER];  // each key's slot in its sub-range's group
+#pragma unroll
+  for (int c = 0; c < PER; ++c)
+    if (x[c] != ~0ull) {
+      at[c] = atomicAdd(&cnt[sb[c]], 1u);
+      keys[at[c]] = x[c];
+    }
+  __syncthreads();
+  u32 place[PER];
+#pragma unroll
+  for (int c = 0; c < PER; ++c) {
+    place[c] = (u32)(PER * tid + c);  // padding keeps its place
+    if (x[c] == ~0ull) continue;
+    const u32 a = start[sb[c]], e = cnt[sb[c]];
+    u32 r = a;
+    for (u32 q = a; q < e; ++q) r += (keys[q] < x[c] || (keys[q] == x[c] && q < at[c])) ? 1u : 0u;
+    place[c] = r;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < PER; ++c) keys[place[c]] = x[c];
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < PER; ++c) x[c] = keys[PER * tid + c];
+  __syncthreads();  // (the caller may reuse lds)
 }
 
 }  // namespace tgs

@@ -34,24 +34,6 @@ struct RankLds {
 // entries of sub-ranges [part kRankBins / np, (part + 1) kRankBins / np) are
 // emitted (np workgroups that order the same entries then emit them all
 // between them).  Every thread calls it.
-// 64-bit minimum and maximum over the wave (every lane gets them).
-__device__ __forceinline__ u64 wave_min64(u64 v) {
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) {
-    const u64 o = ((u64)(u32)__shfl_xor((int)(u32)(v >> 32), m) << 32) | (u64)(u32)__shfl_xor((int)(u32)v, m);
-    v = o < v ? o : v;
-  }
-  return v;
-}
-__device__ __forceinline__ u64 wave_max64(u64 v) {
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) {
-    const u64 o = ((u64)(u32)__shfl_xor((int)(u32)(v >> 32), m) << 32) | (u64)(u32)__shfl_xor((int)(u32)v, m);
-    v = o > v ? o : v;
-  }
-  return v;
-}
-
 __device__ inline void rank_emit(RankLds& s, u32 n, u32 k, float* r, int32_t* oi, float* ov, u32 part = 0,
                                  u32 np = 1) {
   constexpr int NT = kRankThreads;

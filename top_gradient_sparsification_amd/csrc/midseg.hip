@@ -256,7 +256,14 @@ __global__ __launch_bounds__(kMidPassThreads) void k_mid_pass(MidArgs a) {
     const u32 s = woff + hcnt + mtot + lanes_below(mt);
     if (s < kMidBlockCap) stash[s] = Pair{(int32_t)(tail0 + lane), __float_as_uint(xt)};
   }
-  if (in) __builtin_nontemporal_store(acc, (v4f*)(r + S.head) + slot);
+  if (in) {
+    // the wave's 1 KB as whole lines (the body starts on a 256-byte
+    // boundary), written through at device scope: the launch's end then has
+    // no dirty lines of it to write back
+    const u64 w0 = (u64)(slot - lane);  // the same in every lane: a scalar for the buffer's base
+    const int64_t s0 = (int64_t)((u64)__builtin_amdgcn_readfirstlane((u32)(w0 >> 32)) << 32 | __builtin_amdgcn_readfirstlane((u32)w0));
+    st_agent_v4_nt((v4f*)(r + S.head) + s0, (u32)kWave * 16u, (u32)(slot - s0) * 16u, acc);
+  }
   if (has_head && (u32)lane < S.head) r[lane] = xh;
   if (has_tail && (u32)lane < S.len - tail0) r[tail0 + lane] = xt;
   if (tid == 0) a.cnt[b] = btot;

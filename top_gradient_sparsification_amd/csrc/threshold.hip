@@ -67,6 +67,7 @@ struct ThrArgs {
   float* out_val;
   int64_t capacity;
   int64_t* d_count;
+  bool wt;          // vector mode, slots on 256-byte boundaries: store them written through at device scope
 };
 
 // The arguments with the threshold key in place (read from the device when
@@ -85,10 +86,20 @@ __device__ __forceinline__ v4f load_slot(const float* p, const ThrArgs& a, int64
   const float* q = p + 4 * i;
   return v4f{q[0], q[1], q[2], q[3]};
 }
+// Slot i of a wave whose first slot is i0 (i = i0 + lane).  With `wt` the
+// wave's 1 KB goes out as whole lines written through at device scope, which
+// leaves the launch's end no dirty lines to write back (on slots that cut
+// lines the device-scope stores would cost more than they save).
 template <bool VEC>
-__device__ __forceinline__ void store_slot(float* p, const ThrArgs& a, int64_t i, v4f v) {
+__device__ __forceinline__ void store_slot(float* p, const ThrArgs& a, int64_t i, int64_t i0, v4f v) {
   if (VEC) {
-    __builtin_nontemporal_store(v, (v4f*)(p + a.head) + i);
+    if (a.wt) {
+      const u64 w0 = (u64)i0;  // the same in every lane: made a scalar for the buffer's base
+      const int64_t s0 = (int64_t)((u64)__builtin_amdgcn_readfirstlane((u32)(w0 >> 32)) << 32 | __builtin_amdgcn_readfirstlane((u32)w0));
+      st_agent_v4_nt((v4f*)(p + a.head) + s0, (u32)kWave * 16u, (u32)(i - s0) * 16u, v);
+    } else {
+      __builtin_nontemporal_store(v, (v4f*)(p + a.head) + i);
+    }
   } else {
     float* q = p + 4 * i;
     q[0] = v.x;
@@ -192,7 +203,7 @@ __global__ __launch_bounds__(kPassThreads) void k_thr_pass(ThrArgs ain) {
       xt = 0.0f;
     }
   }
-  if (p.in) store_slot<VEC>(r, a, p.slot, acc);
+  if (p.in) store_slot<VEC>(r, a, p.slot, p.slot - lane, acc);
   if (p.has_head && lane < a.head) r[lane] = xh;
   if (p.has_tail && lane < a.n - a.tail0) r[a.tail0 + lane] = xt;
   if (tid == 0) a.cnt[b] = btot;
@@ -428,6 +439,7 @@ static tgs_status threshold_launch(const char* what, const float* grad, float* r
     if (vec) {
       int64_t head = (int64_t)(((16u - (((uintptr_t)residual) & 15u)) & 15u) / 4u);
       a.head = std::min<int64_t>(head, n);
+      a.wt = (((uintptr_t)(residual + a.head)) & 255u) == 0;
     }
     a.nv = (n - a.head) / 4;
     a.tail0 = a.head + 4 * a.nv;

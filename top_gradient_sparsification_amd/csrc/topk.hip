@@ -1446,10 +1446,14 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_guided(GuidedArgs a) {
     m4 = 0;
     if (t < nrows && i < a.nv) {
       const v4f acc = rr + gg;
-      // (non-temporal: stores that allocate in the caches leave the next
-      // call a residual's worth of dirty lines to write back, which costs
-      // more than the ranking's scattered +0 stores gain from them)
-      __builtin_nontemporal_store(acc, rv + i);
+      // (written through at device scope with the streaming hint: stores
+      // that allocate in the caches leave the next call a residual's worth
+      // of dirty lines to write back, which costs more than the ranking's
+      // scattered +0 stores gain from them, and the write-through ones also
+      // leave this launch's end less to write back than the hint alone;
+      // the aligned part starts on a 256-byte boundary, so a wave's stores
+      // cover whole lines)
+      st_agent_v4_nt(rv + t * NT, (u32)NT * 16u, (u32)tid * 16u, acc);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         bq[e] = __float_as_uint(acc[e]);

@@ -11,6 +11,8 @@ constexpr int kRankThreads = 1024;
 constexpr int kRankList = 8192;   // entries one workgroup orders (LDS)
 constexpr int kRankBins = 2048;   // sub-ranges of the key span
 
+__device__ __forceinline__ u32 umin(u32 x, u32 y) { return x < y ? x : y; }
+
 // Shared memory of a ranking workgroup.
 struct RankLds {
   u64 list[kRankList];  // the entries: packed pairs
@@ -33,7 +35,8 @@ struct RankLds {
 // before it; the emitted entries' residual becomes +0.  With np > 1 only the
 // entries of sub-ranges [part kRankBins / np, (part + 1) kRankBins / np) are
 // emitted (np workgroups that order the same entries then emit them all
-// between them).  Every thread calls it.
+// between them).  Entries whose key is at or above `sure` keep the residual
+// they have (+0 already).  Every thread calls it.
 __device__ inline void rank_emit(RankLds& s, u32 n, u32 k, float* r, int32_t* oi, float* ov, u32 part = 0,
                                  u32 np = 1) {
   constexpr int NT = kRankThreads;
@@ -87,9 +90,11 @@ __device__ inline void rank_emit(RankLds& s, u32 n, u32 k, float* r, int32_t* oi
     if (a < k) s.tmp[a + atomicAdd(&s.cur[sb], 1u)] = pv;
   }
   __syncthreads();
-  // this workgroup's share of the places [0, E): whole sub-ranges
-  const u32 lo = part == 0 ? 0u : std::min(E, s.start[part * kRankBins / np]);
-  const u32 hi = part + 1 >= np ? E : std::min(E, s.start[(part + 1) * kRankBins / np]);
+  // this workgroup's share of the places [0, E): whole sub-ranges (minima
+  // taken by value: std::min's references to E and to an LDS word would keep
+  // E in scratch memory, which every launch then has to set up)
+  const u32 lo = part == 0 ? 0u : umin(E, (u32)s.start[part * kRankBins / np]);
+  const u32 hi = part + 1 >= np ? E : umin(E, (u32)s.start[(part + 1) * kRankBins / np]);
   for (u32 p = lo + tid; p < hi; p += NT) {
     const u64 pv = s.tmp[p];
     const u64 me = rkey(pv);

@@ -91,6 +91,18 @@ def test_ties_large_k(tgs_gpu):
     assert_merge_equal(got, exp, "ties k=40000")
 
 
+@pytest.mark.parametrize("P,k", [(2, 300_001), (3, 1 << 20)])
+def test_large_k(tgs_gpu, P, k):
+    """k far past one sorted run of the final set: 74 runs and seven merge
+    passes with a ragged last run (k = 300,001), and the largest k the call
+    takes (2^20: 256 runs, eight passes), with the hash parts at their most."""
+    rng = np.random.default_rng(7 + P)
+    n = 4 * k
+    idx, val = random_sets(rng, P, k, n, 2 * k)
+    got, exp = run_both(tgs_gpu, idx, val, n)
+    assert_merge_equal(got, exp, "P=%d k=%d" % (P, k))
+
+
 def test_nan_and_inf_values(tgs_gpu):
     """NaN (bit patterns 0x7FFFFFFF, 0xFFFFFFFF, 0x7FC00000, 0xFFC00001) and
     +-inf on indices no other row holds (so they are never added): NaN keys

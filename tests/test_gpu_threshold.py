@@ -109,14 +109,18 @@ def test_stash_overflow_positive_lambda(tgs_gpu, layout):
                          "%s cap=%d" % (layout, cap))
 
 
-@pytest.mark.parametrize("off_g,off_r", [(1, 1), (3, 3), (0, 2)])
+@pytest.mark.parametrize("off_g,off_r", [(1, 1), (3, 3), (0, 2), (63, 63)])
 def test_misaligned(tgs_gpu, off_g, off_r):
+    """Offsets of 1 and 3 entries: a scalar head, slots off the 256-byte
+    grid (stored with the streaming hint alone); 0 and 2: grad and residual
+    unequally aligned (scalar slots); 63: a one-entry head after which the
+    slots start on a 256-byte boundary (written through at device scope)."""
     rng = np.random.default_rng(10 + off_g + off_r)
     n = 500_001
     grad = rng.standard_normal(n).astype(np.float32)
     res = rng.standard_normal(n).astype(np.float32)
-    gb = torch.zeros(n + 8, dtype=torch.float32, device="cuda")
-    rb = torch.zeros(n + 8, dtype=torch.float32, device="cuda")
+    gb = torch.zeros(n + 64, dtype=torch.float32, device="cuda")
+    rb = torch.zeros(n + 64, dtype=torch.float32, device="cuda")
     gb[off_g:off_g + n] = gpu(grad)
     rb[off_r:off_r + n] = gpu(res)
     r = rb[off_r:off_r + n]

@@ -306,11 +306,11 @@ def parse():
 # the 256 MiB copy of --copy-calibration.  Valid only for the k_step
 # source they were taken on: `source_sha256` is the hash of csrc/topk.hip then.
 MEASURED_TRAFFIC = {
-    "source_sha256": "52c9ba168fee5a968e21690e723be89efca18f625858d864e04a4159b8238d7d",
-    # FETCH_SIZE 102,916.9 KiB x (262,144 / 131,083.5: the copy's true read over its counter)
-    "fetch_bytes": 210755397,
-    # WRITE_SIZE 102,793.6 KiB x 1.0 (the copy's counter read exactly 262,144 KiB)
-    "write_bytes": 105260656,
+    "source_sha256": "aeb2bfbf489b3fcd6919f9f5db39dc3087a5bce6baca4ae76e6c0879b582149a",
+    # FETCH_SIZE 102,909.6 KiB x (262,144 / 131,083.5: the copy's true read over its counter)
+    "fetch_bytes": 210740358,
+    # WRITE_SIZE 102,793.0 KiB x 1.0 (the copy's counter read exactly 262,144 KiB)
+    "write_bytes": 105260000,
 }
 
 

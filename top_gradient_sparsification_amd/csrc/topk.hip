@@ -53,8 +53,9 @@
 // When the plan did not hold, residual already holds acc everywhere: the
 // grid fences, meets at a barrier and runs the exact general path below.
 //
-// General path (grid barriers; the fast path's fallback, and a launch of its
-// own, k_general, where the fast path does not apply):
+// General path (grid barriers; the fallback of the fast path and of the
+// bucketed ranking, inside their launches, and a launch of its own,
+// k_general, where neither applies):
 //   radix select of the k-th key over 11/11/9-bit digits, counts per
 //   workgroup, ordered compaction of the selected entries in ascending index
 //   order (ties at the k-th key resolved by index), a stable LSD radix sort of
@@ -177,10 +178,10 @@ struct StepCtl {
   u32 parity;         // counter set the next k_step launch uses (flipped by each launch)
   u32 mid_exact;      // batched layer-wise segments selected exactly from acc (never reset)
   u32 rk_count;       // bucketed ranking: buckets of this call (0: none), set by k_guess
-  u32 rk_ok;          // 1 once the bucketed ranking has emitted the step (k_general then exits)
+  u32 rk_ok;          // 1 once the bucketed ranking has emitted the step
   u32 rk_ovf;         // set when an accumulate workgroup's stage of candidates overflowed
   u32 rk_used;        // calls whose bucketed ranking held (never reset)
-  u32 rk_missed;      // calls whose bucketed ranking did not hold: k_general ran (never reset)
+  u32 rk_missed;      // calls whose bucketed ranking did not hold: the general path ran (never reset)
   u32 pad1[49];
   StepSet set[2];
   Plan plan;
@@ -362,6 +363,12 @@ struct GenArgs {
   u64* bkt_buf;  // the candidates, grouped by bucket in bucket order
 };
 
+// LDS words the general path's tables take when the caller lends them.
+template <int NT, int DB>
+constexpr int general_lds_words() {
+  return 2048 + (NT / kWave) * (1 << DB) + 2 * (1 << DB);
+}
+
 // Sum over the block of one value per thread.
 template <int NT>
 __device__ __forceinline__ u32 block_sum(u32 v, u32* lds) {
@@ -375,15 +382,21 @@ __device__ __forceinline__ u32 block_sum(u32 v, u32* lds) {
 // rows of NT entries each pass keeps in flight per tile (kPipe: the next
 // tile's loads go out before a tile is processed).  acc is read from
 // residual, which every participant must be able to see.
-template <int NT, int V, bool kPipe, int DB, bool kCand>
-__device__ __forceinline__ void general_path(const GenArgs& a) {
+template <int NT, int V, bool kPipe, int DB, bool kCand, bool kExt = false>
+__device__ __forceinline__ void general_path(const GenArgs& a, u32* ext = nullptr) {
   constexpr int NW = NT / kWave;
   constexpr int ND = 1 << DB;  // digits of one LSD pass
   static_assert(ND <= kLsdDigits && ND <= 2048, "LSD digit tables");
-  __shared__ u32 s_hist[2048];
-  __shared__ u32 s_wcnt[NW][ND];
-  __shared__ u32 s_base[ND];
-  __shared__ u32 s_run[ND];
+  // the tables in LDS of their own, or (kExt) in the caller's LDS from `ext`
+  // on (general_lds_words<NT, DB>() words the caller does not use meanwhile)
+  __shared__ u32 own_hist[kExt ? 1 : 2048];
+  __shared__ u32 own_wcnt[kExt ? 1 : NW][kExt ? 1 : ND];
+  __shared__ u32 own_base[kExt ? 1 : ND];
+  __shared__ u32 own_run[kExt ? 1 : ND];
+  u32* const s_hist = kExt ? ext : own_hist;
+  u32 (*const s_wcnt)[ND] = reinterpret_cast<u32 (*)[ND]>(kExt ? ext + 2048 : &own_wcnt[0][0]);
+  u32* const s_base = kExt ? ext + 2048 + NW * ND : own_base;
+  u32* const s_run = kExt ? ext + 2048 + NW * ND + ND : own_run;
   __shared__ u32 s_scan[NW + 1];
   __shared__ u32 s_found[4];
   const int tid = threadIdx.x;
@@ -1212,7 +1225,7 @@ __global__ __launch_bounds__(kGuessThreads) void k_guess(GuessArgs a) {
   constexpr int NT = kGuessThreads, NW = NT / kWave;
   __shared__ u32 s_h[2048];
   __shared__ u32 s_scan[NW + 1];
-  __shared__ u32 s_last, s_pick;
+  __shared__ u32 s_last, s_pick, s_kept;
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   for (int i = tid; i < 2048; i += NT) s_h[i] = 0;
   __syncthreads();
@@ -1249,19 +1262,23 @@ __global__ __launch_bounds__(kGuessThreads) void k_guess(GuessArgs a) {
   // words)
   static_assert(NT * 2 == 2048, "two bins per thread");
   for (int i = tid; i < 2048; i += NT) s_h[i] = ld_agent(&a.hh->hist[i]);
+  if (tid == 0) {
+    s_pick = 0u;           // no bin reaches c_req: every bin ...
+    s_kept = 0xFFFFFFFFu;  // ... and every sample entry kept
+  }
   __syncthreads();
   const int hi = 2047 - 2 * tid;  // this thread's bins, from the top: hi, hi - 1
   const u32 h1 = s_h[hi], h0 = s_h[hi - 1];
   u32 tot;
   const u32 above = block_exclusive_sum<NT>(h1 + h0, s_scan, tot);
-  if (tid == 0) s_pick = 0u;  // no bin reaches c_req: every bin
+  if (above < a.c_req && above + h1 + h0 >= a.c_req) {
+    // the pick, and the sample entries in the bins at or above it
+    const bool top = above + h1 >= a.c_req;
+    s_pick = top ? (u32)hi : (u32)(hi - 1);
+    s_kept = top ? above + h1 : above + h1 + h0;
+  }
   __syncthreads();
-  if (above < a.c_req && above + h1 + h0 >= a.c_req) s_pick = above + h1 >= a.c_req ? (u32)hi : (u32)(hi - 1);
-  __syncthreads();
-  const u32 pick = s_pick;
-  // sample entries in the bins >= pick
-  const u32 mine = (u32)hi >= pick ? h1 : 0u, mine0 = (u32)(hi - 1) >= pick ? h0 : 0u;
-  const u32 kept = block_sum<NT>(mine + mine0, s_scan);
+  const u32 pick = s_pick, kept = s_kept == 0xFFFFFFFFu ? tot : s_kept;
   if (a.rk_tab) {
     // The bucketed ranking's buckets, numbered from the top: bin j >= pick is
     // cut into s_j equal sub-ranges of its 2^20 keys, s_j the sample entries
@@ -1270,15 +1287,21 @@ __global__ __launch_bounds__(kGuessThreads) void k_guess(GuessArgs a) {
     // bins).  rk_tab[j] = first bucket of bin j << 16 | s_j.  More than
     // kRkBuckets buckets: twice the entries per bucket, again.
     float per = a.rk_samples;
-    u32 s1 = 0, s0 = 0, nb = 0;
-    for (int tries = 0; tries < 12; ++tries, per *= 2.0f) {
+    auto cut = [&](u32& s1, u32& s0) {
       s1 = (u32)hi >= pick && h1 ? (u32)ceilf((float)h1 / per) : 0u;
       s0 = (u32)(hi - 1) >= pick && h0 ? (u32)ceilf((float)h0 / per) : 0u;
-      nb = block_sum<NT>(s1 + s0, s_scan);
-      if (nb <= (u32)kRkBuckets) break;
+    };
+    u32 s1, s0, nb;
+    cut(s1, s0);
+    u32 base = block_exclusive_sum<NT>(s1 + s0, s_scan, nb);
+    if (nb > (u32)kRkBuckets) {  // (the same in every thread)
+      for (int tries = 1; tries < 12 && nb > (u32)kRkBuckets; ++tries) {
+        per *= 2.0f;
+        cut(s1, s0);
+        nb = block_sum<NT>(s1 + s0, s_scan);
+      }
+      base = block_exclusive_sum<NT>(s1 + s0, s_scan, nb);
     }
-    u32 all;
-    const u32 base = block_exclusive_sum<NT>(s1 + s0, s_scan, all);
     a.rk_tab[hi] = base << 16 | s1;
     a.rk_tab[hi - 1] = (base + s1) << 16 | s0;
     for (int i = tid; i < kRkBuckets; i += NT) a.rk_tot[i] = 0u;
@@ -1536,8 +1559,8 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_guided(GuidedArgs a) {
 // of the buckets above it: the workgroup gathers them from every accumulate
 // workgroup's region, orders them by (key desc, index asc) and emits the
 // ones whose place is below k, setting their residual to +0.  When the route
-// did not hold nothing is written and k_general, which runs next, selects
-// from acc instead.
+// did not hold, the general path selects from acc in the same launch (every
+// workgroup of the grid is resident; the ranking's LDS holds its tables).
 struct RankArgs {
   StepCtl* ctl;        // rk_count, rk_ovf; rk_ok is set when the route held
   const u32* tot;      // [bucket]
@@ -1548,6 +1571,7 @@ struct RankArgs {
   int32_t* out_idx;
   float* out_val;
   float* residual;
+  GenArgs gen;         // the general path's (bar.nwg: this grid, at most kMaxGenWG)
 };
 
 __global__ __launch_bounds__(kRankThreads) void k_rank(RankArgs a) {
@@ -1568,7 +1592,12 @@ __global__ __launch_bounds__(kRankThreads) void k_rank(RankArgs a) {
     if (ok) a.ctl->rk_ok = 1u;
     atomicAdd(ok ? &a.ctl->rk_used : &a.ctl->rk_missed, 1u);
   }
-  if (!ok) return;
+  if (!ok) {
+    // (the same verdict in every workgroup, so all of them take part)
+    static_assert(general_lds_words<kRankThreads, 8>() * sizeof(u32) <= sizeof(s.list), "the tables fit the list");
+    general_path<kRankThreads, 4, true, 8, false, true>(a.gen, (u32*)s.list);
+    return;
+  }
   // Work items, bucket after bucket: a bucket of more than kRkPart entries
   // is shared by several workgroups (at most kRkMaxParts), each of which
   // gathers and orders the whole bucket but emits only its share of it, so
@@ -1607,10 +1636,7 @@ __global__ __launch_bounds__(kRankThreads) void k_rank(RankArgs a) {
   }
 }
 
-__global__ __launch_bounds__(kGenThreads) void k_general(GenArgs a, const u32* rk_ok) {
-  if (rk_ok && *rk_ok) return;  // the bucketed ranking has emitted the step
-  general_path<kGenThreads, 16, true, 9, true>(a);
-}
+__global__ __launch_bounds__(kGenThreads) void k_general(GenArgs a) { general_path<kGenThreads, 16, true, 9, true>(a); }
 
 // ------------------------------------------------------------- k_small ----
 // Small vectors (n <= 2^18, k <= 256) in one launch with no grid barrier,
@@ -3005,13 +3031,12 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
         ra.out_idx = out_idx;
         ra.out_val = out_val;
         ra.residual = residual;
-        // one ranking workgroup per compute unit (each holds ~156 KB of LDS)
-        const int gr = std::max(1, std::min(kRkBuckets, device_cu_count()));
+        // one ranking workgroup per compute unit (each holds ~156 KB of LDS),
+        // and no more than the general path's tables are sized for
+        const int gr = std::max(1, std::min({kRkBuckets, kMaxGenWG, device_cu_count()}));
+        ra.gen = ga;
+        ra.gen.bar.nwg = (u32)gr;
         hipLaunchKernelGGL(k_rank, dim3(gr), dim3(kRankThreads), 0, stream, ra);
-        // if the ranking did not hold, k_general selects from acc (its
-        // first-level histogram rows are the accumulate pass's)
-        ga.bar.nwg = (u32)G2;
-        hipLaunchKernelGGL(k_general, dim3(G2), dim3(kGenThreads), 0, stream, ga, (const u32*)&ctl->rk_ok);
         if (ev1) (void)hipEventRecord(ev1, stream);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return fail(TGS_EHIP, "topk_ef_step: launch failed: %s", hipGetErrorString(e));
@@ -3037,7 +3062,7 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
     }
     if (k > 0) {
       ga.bar.nwg = (u32)G2;
-      hipLaunchKernelGGL(k_general, dim3(G2), dim3(kGenThreads), 0, stream, ga, (const u32*)nullptr);
+      hipLaunchKernelGGL(k_general, dim3(G2), dim3(kGenThreads), 0, stream, ga);
     }
   }
   if (ev1) (void)hipEventRecord(ev1, stream);

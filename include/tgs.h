@@ -58,7 +58,7 @@
  *     tgs_check_device_error() reads and clears it.  After a report other
  *     than bad merge input, run tgs_workspace_init() before the next call.
  *   - Residency: the top-k kernels that synchronise their workgroups through
- *     memory (k_step, k_general) size their grid to what fits on the device
+ *     memory (k_step, k_rank, k_general) size their grid to what fits on the device
  *     at once and assume every workgroup runs concurrently.  Kernels running
  *     on other streams at the same time can keep workgroups from starting;
  *     the waits are bounded, so the call then ends with wrong outputs and the

@@ -58,7 +58,8 @@ constexpr u32 kGuessRows = 4;       // sampled rows per workgroup of k_mid_guess
 constexpr int kMidPassThreads = 256;
 constexpr int kMidPassWaves = kMidPassThreads / kWave;
 constexpr u32 kMidBlockCap = 64;    // stash places per block
-constexpr int kMidList = kRankList;  // candidates one select workgroup holds (LDS)
+constexpr int kMidList = 8192;  // candidates one select workgroup holds (LDS)
+static_assert(kMidList <= kRankList, "the ranking's list holds them");
 constexpr u32 kMidDirect = kMidList;  // segments read whole by the select workgroup
 constexpr int kMidHistBins = 4096;  // sample histogram: key >> 19
 constexpr u32 kMidNoGuess = 0xFFFFFFFFu;  // no stashing (the whole segment is read, or k = 0)

@@ -8,15 +8,18 @@
 namespace tgs {
 
 constexpr int kRankThreads = 1024;
-constexpr int kRankList = 8192;   // entries one workgroup orders (LDS)
+constexpr int kRankList = 12288;  // entries one workgroup orders (LDS)
 constexpr int kRankBins = 2048;   // sub-ranges of the key span
 
 __device__ __forceinline__ u32 umin(u32 x, u32 y) { return x < y ? x : y; }
 
+static_assert(kRankList <= 65536, "places fit 16 bits");
+
 // Shared memory of a ranking workgroup.
 struct RankLds {
   u64 list[kRankList];  // the entries: packed pairs
-  u64 tmp[kRankList];   // the same, grouped by sub-range of the key span
+  u16 tmp[kRankList];   // their places in list, grouped by sub-range of the key span
+                        // (places, not copies: the room goes to a longer list)
   u32 cnt[kRankBins];  // entries per sub-range (and the radix histogram of the exact route)
   u32 start[kRankBins];
   u32 cur[kRankBins];
@@ -87,7 +90,7 @@ __device__ inline void rank_emit(RankLds& s, u32 n, u32 k, float* r, int32_t* oi
     const u64 pv = s.list[i];
     const u32 sb = sub(rkey(pv));
     const u32 a = s.start[sb];
-    if (a < k) s.tmp[a + atomicAdd(&s.cur[sb], 1u)] = pv;
+    if (a < k) s.tmp[a + atomicAdd(&s.cur[sb], 1u)] = (u16)i;
   }
   __syncthreads();
   // this workgroup's share of the places [0, E): whole sub-ranges (minima
@@ -96,12 +99,12 @@ __device__ inline void rank_emit(RankLds& s, u32 n, u32 k, float* r, int32_t* oi
   const u32 lo = part == 0 ? 0u : umin(E, (u32)s.start[part * kRankBins / np]);
   const u32 hi = part + 1 >= np ? E : umin(E, (u32)s.start[(part + 1) * kRankBins / np]);
   for (u32 p = lo + tid; p < hi; p += NT) {
-    const u64 pv = s.tmp[p];
+    const u64 pv = s.list[s.tmp[p]];
     const u64 me = rkey(pv);
     const u32 sb = sub(me);
     const u32 a = s.start[sb], c = s.cnt[sb];
     u32 rank = a;
-    for (u32 q = a; q < a + c; ++q) rank += rkey(s.tmp[q]) < me ? 1u : 0u;
+    for (u32 q = a; q < a + c; ++q) rank += rkey(s.list[s.tmp[q]]) < me ? 1u : 0u;
     if (rank < k) {
       const Pair e = unpack_pair(pv);
       oi[rank] = e.idx;

@@ -3031,7 +3031,7 @@ extern "C" tgs_status tgs_topk_ef_step(const float* grad, float* residual, int64
         ra.out_idx = out_idx;
         ra.out_val = out_val;
         ra.residual = residual;
-        // one ranking workgroup per compute unit (each holds ~156 KB of LDS),
+        // one ranking workgroup per compute unit (each holds ~148 KB of LDS),
         // and no more than the general path's tables are sized for
         const int gr = std::max(1, std::min({kRkBuckets, kMaxGenWG, device_cu_count()}));
         ra.gen = ga;

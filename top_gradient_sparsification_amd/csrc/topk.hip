@@ -1447,7 +1447,7 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_guided(GuidedArgs a) {
       r[i] = acc;
       bq[0] = __float_as_uint(acc);
       const u32 bin = key_of_bits(bq[0]) >> 20;
-      atomicAdd(&s_h[bin], 1u);
+      if (!BKT) atomicAdd(&s_h[bin], 1u);
       m = guide && bin >= gbin ? 1u : 0u;
     }
     if (guide) place(m, i, bq);
@@ -1481,7 +1481,7 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_guided(GuidedArgs a) {
       for (int e = 0; e < 4; ++e) {
         bq[e] = __float_as_uint(acc[e]);
         const u32 bin = key_of_bits(bq[e]) >> 20;
-        atomicAdd(&s_h[bin], 1u);
+        if (!BKT) atomicAdd(&s_h[bin], 1u);
         m4 |= (guide && bin >= gbin ? 1u : 0u) << e;
       }
     }
@@ -1517,7 +1517,10 @@ __global__ __launch_bounds__(kAccThreads) void k_acc_guided(GuidedArgs a) {
     scalar(i, i < a.n);
   }
   __syncthreads();
-  for (int i = tid; i < 2048; i += NT) a.hist_rows[(size_t)blockIdx.x * 2048 + i] = s_h[i];
+  // (the first-level histogram rows are k_general's; the bucketed ranking's
+  // fallback reads acc itself)
+  if (!BKT)
+    for (int i = tid; i < 2048; i += NT) a.hist_rows[(size_t)blockIdx.x * 2048 + i] = s_h[i];
   if (BKT) {
     // the staged candidates to the region, grouped by bucket
     const u32 ns = s_cnt;

@@ -306,11 +306,11 @@ def parse():
 # the 256 MiB copy of --copy-calibration.  Valid only for the k_step
 # source they were taken on: `source_sha256` is the hash of csrc/topk.hip then.
 MEASURED_TRAFFIC = {
-    "source_sha256": "d548c53cfdf265d7ff953ed19af4f1f755b4135247b251c8e06cab5e6db9a050",
-    # FETCH_SIZE 102,909.5 KiB x (262,144 / 131,083.5: the copy's true read over its counter)
-    "fetch_bytes": 210740166,
-    # WRITE_SIZE 102,793.3 KiB x 1.0 (the copy's counter read exactly 262,144 KiB)
-    "write_bytes": 105260336,
+    "source_sha256": "677f5c5a3c3e2274901fe7f1d4dc090446a8d9553d74efa05d0e949d940581e5",
+    # FETCH_SIZE 102,909.7 KiB x (262,144 / 131,083.5: the copy's true read over its counter)
+    "fetch_bytes": 210740614,
+    # WRITE_SIZE 102,792.9 KiB x 1.0 (the copy's counter read exactly 262,144 KiB)
+    "write_bytes": 105259920,
 }
 
 

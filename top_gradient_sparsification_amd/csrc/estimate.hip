@@ -10,7 +10,7 @@
 // sampled positions, and the hard threshold keeps every entry that reaches it.
 //
 // Two launches, no grid-wide wait:
-//   k_est_keys    workgroup b takes samples [512 b, 512 (b + 1)): the
+//   k_est_keys    workgroup b takes samples [1024 b, 1024 (b + 1)): the
 //                 positions (coalesced), then acc = residual + grad at each
 //                 (gathers), its magnitude key to keys[j] and to a 2048-bin LDS
 //                 histogram of key >> 20, whose nonzero bins are added into
@@ -36,7 +36,8 @@ namespace tgs {
 // k_est_keys: small workgroups, so that the random gathers of even a modest
 // sample come from every compute unit at once (they are latency-bound)
 constexpr int kKeyThreads = 256;
-constexpr int kKeyPer = 2;                          // samples per thread
+constexpr int kKeyPer = 4;                          // samples per thread (2: 2 us slower, the
+                                                    // workgroups' histogram adds contending more)
 constexpr int kKeyChunk = kKeyThreads * kKeyPer;    // samples per workgroup
 // k_est_select: coalesced reads of the keys
 constexpr int kEstThreads = 1024;

@@ -469,6 +469,26 @@ def test_bucketed_is_the_default_for_large_k(tgs_gpu):
     assert _bucketed(ws) == (3, 0) and _guided(ws) == (0, 0)
 
 
+def test_bucketed_ranking_over_chained_steps(tgs_gpu):
+    """Twenty chained EF steps at 2% on one residual with fresh gradients:
+    every step bit for bit against the oracle.  As the residual piles up
+    just below the last threshold the buckets near the k-th key grow; the
+    ranking's list still holds them, so nearly every call keeps to the
+    bucketed route rather than the general path."""
+    n, k = 4_000_000, 80_000
+    r_gpu = torch.zeros(n, dtype=torch.float32, device="cuda")
+    r_cpu = np.zeros(n, np.float32)
+    ws = torch.zeros(tgs_gpu.topk_workspace_bytes(n, k), dtype=torch.uint8, device="cuda")
+    for step in range(20):
+        grad = workloads.mixture(n, 1e-3, 0.01, 0.1, (97, step, 1))
+        idx, val = tgs_gpu.topk_ef_step(gpu(grad), r_gpu, k, ws=ws)
+        tgs_gpu.check_device_error(ws)
+        ei, ev = oracle.topk_ef_step(grad, r_cpu, k)
+        assert_topk_equal((host(idx), host(val), host(r_gpu)), (ei, ev, r_cpu), "step %d" % step)
+    used, missed = _bucketed(ws)
+    assert used + missed == 20 and used >= 18, (used, missed)
+
+
 @pytest.mark.parametrize("dist", ["normal", "mixture", "ties", "special"])
 def test_bucketed_ranking(tgs_gpu, dist):
     """The bucketed ranking at several sizes and k (k >= 32768): it holds on

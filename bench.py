@@ -362,7 +362,7 @@ def cpu_baseline(k):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the per-worker step shards as independent units; see the design notes). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)

@@ -363,7 +363,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
-              "(the per-worker step shards as independent units; see the design notes). "
+              "(under data parallelism each GPU runs the step on its own gradient and residual, "
+              "so N GPUs give N times this figure). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if args.workload != "topk_n25.6M_0.1%":

@@ -39,7 +39,7 @@
  *           as 1, 2, 3" (SC'11): the Philox4x32-10 counter-based generator,
  *           which supplies rTop-k's random draws.
  *
- * Readings where the pages are silent (each listed in the design notes):
+ * Readings where the pages are silent:
  *   - acc = residual + grad, one binary32 add, round-to-nearest-even, no
  *     fused multiply-add, subnormals kept (the x86 MXCSR FTZ and DAZ bits are
  *     cleared for the duration of every call).
